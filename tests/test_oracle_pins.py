@@ -1,0 +1,390 @@
+"""Pin the fp64 oracle (oracle/attention.py) to things other than itself.
+
+Each pin is chosen so a plausible mistake in the oracle fails at least one:
+  * scalar brute force with math.fsum on tiny inputs (vectorisation / axis errors);
+  * closed forms: L=1, identical keys, a dominant key, V = ones (rows sum to 1);
+  * one-hot V per KV head (which KV head each query head reads);
+  * torch's scaled_dot_product_attention in float64 (an independent library routine),
+    for MHA, for GQA (enable_gqa) and for explicitly up-projected MLA;
+  * absorbed MLA == explicit MLA (associativity);
+  * MLA with identity up-projections and no RoPE == MQA (cross-pins the two paths);
+  * split-KV merge of any partition (including empty chunks) == unsplit result.
+The planted-mistake tests at the end re-run some pins against a deliberately
+broken copy of an oracle step and check that the pin then fails.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.attention as OA
+from oracle.attention import (combine_ref, gqa_decode_ref, mla_absorbed_ref,
+                              mla_explicit_ref)
+
+RNG = np.random.default_rng(1234)
+
+
+def rand(*shape, rng=RNG):
+    return rng.standard_normal(shape)
+
+
+# ----------------------------------------------------------------------------
+# brute force
+# ----------------------------------------------------------------------------
+
+def brute_gqa(q, k, v, seq_lens, scale):
+    """Scalar loops with exact-ish summation; independent of numpy vector ops."""
+    B, Hq, D = q.shape
+    Hkv = k.shape[2]
+    g = Hq // Hkv
+    out = np.zeros((B, Hq, D))
+    lse = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        L = int(seq_lens[b])
+        for h in range(Hq):
+            kv = h // g
+            if L == 0:
+                continue
+            s = [scale * math.fsum(float(q[b, h, i]) * float(k[b, j, kv, i]) for i in range(D))
+                 for j in range(L)]
+            m = max(s)
+            e = [math.exp(x - m) for x in s]
+            z = math.fsum(e)
+            lse[b, h] = m + math.log(z)
+            for i in range(D):
+                out[b, h, i] = math.fsum(e[j] / z * float(v[b, j, kv, i]) for j in range(L))
+    return out, lse
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (4, 2), (8, 2), (8, 1), (6, 3), (3, 1)])
+@pytest.mark.parametrize("L", [1, 2, 5, 8])
+def test_gqa_brute_force(Hq, Hkv, L):
+    rng = np.random.default_rng([Hq, Hkv, L])
+    B, D = 2, 5
+    q = rand(B, Hq, D, rng=rng)
+    k = rand(B, 8, Hkv, D, rng=rng)
+    v = rand(B, 8, Hkv, D, rng=rng)
+    lens = np.array([L, max(1, L - 1)])
+    o, l = gqa_decode_ref(q, k, v, lens, 0.7)
+    ob, lb = brute_gqa(q, k, v, lens, 0.7)
+    np.testing.assert_allclose(o, ob, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(l, lb, rtol=1e-13, atol=1e-13)
+
+
+def brute_mla(q_nope, q_rope, cache, seq_lens, w_uk, w_uv, scale, d_c):
+    """Scalar loops of the literal (up-projected) MLA formula."""
+    B, H, dn = q_nope.shape
+    dr = q_rope.shape[2]
+    dv = w_uv.shape[2]
+    out = np.zeros((B, H, dv))
+    lse = np.full((B, H), -np.inf)
+    for b in range(B):
+        L = int(seq_lens[b])
+        for h in range(H):
+            s = []
+            for j in range(L):
+                kc = [math.fsum(cache[b, j, c] * w_uk[h, c, e] for c in range(d_c)) for e in range(dn)]
+                dot = math.fsum([q_nope[b, h, e] * kc[e] for e in range(dn)] +
+                                [q_rope[b, h, r] * cache[b, j, d_c + r] for r in range(dr)])
+                s.append(scale * dot)
+            m = max(s)
+            e_ = [math.exp(x - m) for x in s]
+            z = math.fsum(e_)
+            lse[b, h] = m + math.log(z)
+            for e in range(dv):
+                vcol = [math.fsum(cache[b, j, c] * w_uv[h, c, e] for c in range(d_c)) for j in range(L)]
+                out[b, h, e] = math.fsum(e_[j] / z * vcol[j] for j in range(L))
+    return out, lse
+
+
+@pytest.mark.parametrize("H,d_c,d_r,L", [(1, 4, 0, 1), (2, 4, 2, 3), (4, 8, 2, 8), (2, 8, 0, 5)])
+def test_mla_brute_force(H, d_c, d_r, L):
+    rng = np.random.default_rng([H, d_c, d_r, L, 7])
+    B, dn, dv = 2, 3, 4
+    qn, qr = rand(B, H, dn, rng=rng), rand(B, H, d_r, rng=rng)
+    cache = rand(B, 8, d_c + d_r, rng=rng)
+    wuk, wuv = rand(H, d_c, dn, rng=rng), rand(H, d_c, dv, rng=rng)
+    lens = np.array([L, 1])
+    sc = 1.0 / math.sqrt(dn + d_r)
+    ob, lb = brute_mla(qn, qr, cache, lens, wuk, wuv, sc, d_c)
+    for fn in (mla_absorbed_ref, mla_explicit_ref):
+        o, l = fn(qn, qr, cache, lens, wuk, wuv, sc, kv_lora_rank=d_c)
+        np.testing.assert_allclose(o, ob, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(l, lb, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# closed forms and invariants
+# ----------------------------------------------------------------------------
+
+def test_L1_returns_the_single_value_row():
+    q, k, v = rand(3, 4, 8), rand(3, 2, 2, 8), rand(3, 2, 2, 8)
+    o, l = gqa_decode_ref(q, k, v, [1, 1, 1], 0.5)
+    for b in range(3):
+        for h in range(4):
+            np.testing.assert_allclose(o[b, h], v[b, 0, h // 2], rtol=0, atol=1e-15)
+            assert l[b, h] == pytest.approx(0.5 * float(q[b, h] @ k[b, 0, h // 2]), abs=1e-14)
+
+
+def test_identical_keys_give_mean_of_values():
+    B, L, D = 2, 7, 16
+    q = rand(B, 2, D)
+    krow = rand(B, 1, 1, D)
+    k = np.repeat(krow, L, axis=1)
+    v = rand(B, L, 1, D)
+    o, l = gqa_decode_ref(q, k, v, [L, L], 0.25)
+    for b in range(B):
+        for h in range(2):
+            np.testing.assert_allclose(o[b, h], v[b, :, 0].mean(axis=0), atol=1e-14)
+            s = 0.25 * float(q[b, h] @ krow[b, 0, 0])
+            assert l[b, h] == pytest.approx(s + math.log(L), abs=1e-13)
+
+
+def test_dominant_key_selects_its_value():
+    D, L = 8, 6
+    q = np.zeros((1, 1, D)); q[0, 0, 0] = 1.0
+    k = np.zeros((1, L, 1, D)); k[0, 3, 0, 0] = 50.0
+    v = rand(1, L, 1, D)
+    o, l = gqa_decode_ref(q, k, v, [L], 1.0)
+    # the other five weights are each exp(-50) relative to the dominant one
+    np.testing.assert_allclose(o[0, 0], v[0, 3, 0], rtol=0, atol=10 * L * math.exp(-50))
+    assert l[0, 0] == pytest.approx(50.0 + math.log(1 + 5 * math.exp(-50)), abs=1e-14)
+
+
+def test_softmax_rows_sum_to_one_and_weights_in_unit_interval():
+    B, Hq, Hkv, D, L = 2, 4, 2, 8, 8
+    q, k = rand(B, Hq, D), rand(B, L, Hkv, D) * 3
+    ones = np.ones((B, L, Hkv, D))
+    o, _ = gqa_decode_ref(q, k, ones, [L, 5], 0.9)
+    np.testing.assert_allclose(o, 1.0, rtol=0, atol=1e-14)
+    # one-hot V per token exposes each softmax weight p_j as an output element
+    eye = np.zeros((B, L, Hkv, D))
+    for j in range(L):
+        eye[:, j, :, j] = 1.0
+    p, lse = gqa_decode_ref(q, k, eye, [L, 5], 0.9)
+    assert (p >= 0).all() and (p <= 1).all()
+    np.testing.assert_allclose(p.sum(axis=2), 1.0, atol=1e-14)
+    assert np.all(p[1, :, 5:] == 0)      # tokens past the length get no weight
+    # and each weight equals exp(s_j - lse)
+    for b, Lb in enumerate([L, 5]):
+        for h in range(Hq):
+            s = 0.9 * k[b, :Lb, h // 2] @ q[b, h]
+            np.testing.assert_allclose(p[b, h, :Lb], np.exp(s - lse[b, h]), atol=1e-14)
+
+
+def test_token_permutation_invariance():
+    B, Hq, Hkv, D, L = 1, 4, 1, 8, 8
+    q, k, v = rand(B, Hq, D), rand(B, L, Hkv, D), rand(B, L, Hkv, D)
+    perm = RNG.permutation(L)
+    o1, l1 = gqa_decode_ref(q, k, v, [L], 0.3)
+    o2, l2 = gqa_decode_ref(q, k[:, perm], v[:, perm], [L], 0.3)
+    np.testing.assert_allclose(o1, o2, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, atol=1e-14)
+
+
+def test_empty_sequence():
+    q, k, v = rand(2, 4, 8), rand(2, 3, 2, 8), rand(2, 3, 2, 8)
+    o, l = gqa_decode_ref(q, k, v, [0, 3], 0.5)
+    assert np.all(o[0] == 0) and np.all(np.isneginf(l[0]))
+    assert np.all(np.isfinite(l[1]))
+
+
+def head_mapping_expected(Hq, Hkv):
+    """V rows one-hot on the KV-head index: output of head h must be e_{h // g}."""
+    g = Hq // Hkv
+    exp = np.zeros((Hq, max(Hkv, 2)))
+    for h in range(Hq):
+        exp[h, h // g] = 1.0
+    return exp
+
+
+def check_head_mapping(fn, Hq, Hkv):
+    D, L = max(Hkv, 2), 5
+    q, k = rand(1, Hq, D), rand(1, L, Hkv, D)
+    v = np.zeros((1, L, Hkv, D))
+    for kv in range(Hkv):
+        v[0, :, kv, kv] = 1.0
+    o, _ = fn(q, k, v, [L], 0.5)
+    np.testing.assert_allclose(o[0], head_mapping_expected(Hq, Hkv), atol=1e-14)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (32, 8), (8, 8), (8, 1), (6, 3)])
+def test_head_mapping_one_hot(Hq, Hkv):
+    # 8 query heads, 2 KV heads: heads 0-3 read KV 0, heads 4-7 read KV 1
+    # (kakack.github.io section 4; shippingwang.com section 7.3)
+    check_head_mapping(gqa_decode_ref, Hq, Hkv)
+
+
+# ----------------------------------------------------------------------------
+# torch SDPA in float64 (library routine)
+# ----------------------------------------------------------------------------
+
+def sdpa(q, k, v, scale, gqa=False):
+    """q [Hq, D], k/v [L, Hkv, D] -> [Hq, Dv] via torch float64 SDPA."""
+    tq = torch.from_numpy(np.ascontiguousarray(q))[None, :, None, :]
+    tk = torch.from_numpy(np.ascontiguousarray(k.transpose(1, 0, 2)))[None]
+    tv = torch.from_numpy(np.ascontiguousarray(v.transpose(1, 0, 2)))[None]
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale, enable_gqa=gqa)
+    return o[0, :, 0, :].numpy()
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(4, 4, 64), (32, 8, 128), (8, 1, 32), (12, 4, 16)])
+def test_gqa_vs_torch_sdpa(Hq, Hkv, D):
+    B, L = 3, 37
+    q, k, v = rand(B, Hq, D), rand(B, L, Hkv, D), rand(B, L, Hkv, D)
+    lens = [37, 1, 20]
+    sc = 1 / math.sqrt(D)
+    o, _ = gqa_decode_ref(q, k, v, lens, sc)
+    for b, Lb in enumerate(lens):
+        ot = sdpa(q[b], k[b, :Lb], v[b, :Lb], sc, gqa=Hq != Hkv)
+        np.testing.assert_allclose(o[b], ot, rtol=1e-12, atol=1e-13)
+
+
+def test_mla_explicit_vs_torch_sdpa_full_dims():
+    # DeepSeek-V3 per-head dimensions: d_c 512, rope 64, nope 128, v 128
+    H, L, d_c, d_r, dn, dv = 4, 24, 512, 64, 128, 128
+    qn, qr = rand(1, H, dn), rand(1, H, d_r)
+    cache = rand(1, L, d_c + d_r)
+    wuk, wuv = rand(H, d_c, dn) / math.sqrt(512), rand(H, d_c, dv) / math.sqrt(512)
+    sc = 1 / math.sqrt(192)
+    o, _ = mla_explicit_ref(qn, qr, cache, [L], wuk, wuv, sc)
+    tc = torch.from_numpy(cache[0])
+    for h in range(H):
+        kc = tc[:, :d_c] @ torch.from_numpy(wuk[h])                  # [L, 128]
+        kfull = torch.cat([kc, tc[:, d_c:]], dim=1)                   # [L, 192]
+        vfull = tc[:, :d_c] @ torch.from_numpy(wuv[h])                # [L, 128]
+        qfull = torch.cat([torch.from_numpy(qn[0, h]), torch.from_numpy(qr[0, h])])
+        ot = torch.nn.functional.scaled_dot_product_attention(
+            qfull[None, None, None], kfull[None, None], vfull[None, None], scale=sc)
+        np.testing.assert_allclose(o[0, h], ot[0, 0, 0].numpy(), rtol=1e-12, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------
+# MLA associativity and the MQA special case
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("H", [1, 2, 4])
+@pytest.mark.parametrize("d_c", [4, 8])
+@pytest.mark.parametrize("d_r", [0, 2])
+def test_mla_absorbed_equals_explicit_tiny(H, d_c, d_r):
+    rng = np.random.default_rng([H, d_c, d_r])
+    B, Lmax, dn, dv = 2, 8, 3, 5
+    qn, qr = rand(B, H, dn, rng=rng), rand(B, H, d_r, rng=rng)
+    cache = rand(B, Lmax, d_c + d_r, rng=rng)
+    wuk, wuv = rand(H, d_c, dn, rng=rng), rand(H, d_c, dv, rng=rng)
+    lens = [8, 3]
+    sc = 1 / math.sqrt(dn + d_r)
+    oa, la = mla_absorbed_ref(qn, qr, cache, lens, wuk, wuv, sc, kv_lora_rank=d_c)
+    oe, le = mla_explicit_ref(qn, qr, cache, lens, wuk, wuv, sc, kv_lora_rank=d_c)
+    np.testing.assert_allclose(oa, oe, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(la, le, rtol=1e-12, atol=1e-12)
+
+
+def test_mla_absorbed_equals_explicit_full_rows():
+    H, L = 4, 16
+    qn, qr = rand(2, H, 128), rand(2, H, 64)
+    cache = rand(2, L, 576)
+    wuk, wuv = rand(H, 512, 128) / math.sqrt(512), rand(H, 512, 128) / math.sqrt(512)
+    sc = 1 / math.sqrt(192)
+    oa, la = mla_absorbed_ref(qn, qr, cache, [16, 9], wuk, wuv, sc)
+    oe, le = mla_explicit_ref(qn, qr, cache, [16, 9], wuk, wuv, sc)
+    np.testing.assert_allclose(oa, oe, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(la, le, rtol=1e-12, atol=1e-12)
+
+
+def test_mla_with_identity_projections_is_mqa():
+    # GQA/MQA is MLA whose up-projections are 0/1 selection matrices
+    # (arganzheng.life section 4.7): identity W_UK = W_UV, no RoPE, K = V = C.
+    B, H, d, L = 2, 4, 8, 6
+    qn, qr = rand(B, H, d), np.zeros((B, H, 0))
+    cache = rand(B, L, d)
+    eye = np.broadcast_to(np.eye(d), (H, d, d)).copy()
+    o1, l1 = mla_absorbed_ref(qn, qr, cache, [6, 2], eye, eye, 0.4, kv_lora_rank=d)
+    kv = cache[:, :, None, :]
+    o2, l2 = gqa_decode_ref(qn, kv, kv, [6, 2], 0.4)
+    np.testing.assert_allclose(o1, o2, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# split-KV combine
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cuts", [[0, 8], [0, 3, 8], [0, 0, 5, 5, 8], [0, 1, 2, 3, 4, 5, 6, 7, 8],
+                                  [0, 8, 8]])
+def test_combine_any_partition_equals_unsplit(cuts):
+    B, Hq, Hkv, D, L = 2, 4, 2, 8, 8
+    q, k, v = rand(B, Hq, D), rand(B, L, Hkv, D), rand(B, L, Hkv, D)
+    o, l = gqa_decode_ref(q, k, v, [L, L], 0.35)
+    po, pl = [], []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        oo, ll = gqa_decode_ref(q, k[:, a:b], v[:, a:b], [b - a, b - a], 0.35)
+        po.append(oo)
+        pl.append(ll)
+    oc, lc = combine_ref(np.stack(po), np.stack(pl))
+    np.testing.assert_allclose(oc, o, atol=1e-13)
+    np.testing.assert_allclose(lc, l, atol=1e-13)
+
+
+def test_combine_all_empty_and_nan_in_empty_split():
+    po = np.full((3, 2, 4), np.nan)
+    pl = np.full((3, 2), -np.inf)
+    o, l = combine_ref(po, pl)
+    assert np.all(o == 0) and np.all(np.isneginf(l))
+    # an empty split's (garbage) output never leaks into the result
+    po2 = rand(2, 2, 4)
+    po2[1] = np.nan
+    pl2 = np.stack([rand(2), np.full(2, -np.inf)])
+    o2, l2 = combine_ref(po2, pl2)
+    np.testing.assert_allclose(o2, po2[0], atol=0)
+    np.testing.assert_allclose(l2, pl2[0], atol=0)
+
+
+# ----------------------------------------------------------------------------
+# planted mistakes: the pins above must catch a broken oracle
+# ----------------------------------------------------------------------------
+
+def test_planted_interleaved_head_mapping_is_caught(monkeypatch):
+    monkeypatch.setattr(OA, "kv_head_of", lambda h, nq, nkv: h % nkv)
+    with pytest.raises(AssertionError):
+        check_head_mapping(OA.gqa_decode_ref, 8, 2)
+
+
+def test_planted_wrong_mla_scale_is_caught(monkeypatch):
+    real = OA.mla_absorbed_ref
+
+    def wrong(qn, qr, cache, lens, wuk, wuv, scale, kv_lora_rank=512):
+        return real(qn, qr, cache, lens, wuk, wuv, 1 / math.sqrt(576), kv_lora_rank)
+
+    H, L = 2, 6
+    qn, qr, cache = rand(1, H, 128), rand(1, H, 64), rand(1, L, 576)
+    wuk, wuv = rand(H, 512, 128) / 22.6, rand(H, 512, 128) / 22.6
+    oe, _ = mla_explicit_ref(qn, qr, cache, [L], wuk, wuv, 1 / math.sqrt(192))
+    ow, _ = wrong(qn, qr, cache, [L], wuk, wuv, 1 / math.sqrt(192))
+    with pytest.raises(AssertionError):
+        np.testing.assert_allclose(ow, oe, rtol=1e-12, atol=1e-12)
+
+
+def test_planted_transposed_wuk_is_caught():
+    # absorbing with W_UK[h] used the wrong way round breaks associativity
+    H, d_c, dn, L = 2, 6, 6, 5
+    qn, qr, cache = rand(1, H, dn), rand(1, H, 2), rand(1, L, d_c + 2)
+    wuk, wuv = rand(H, d_c, dn), rand(H, d_c, 3)
+    sc = 0.3
+    oe, _ = mla_explicit_ref(qn, qr, cache, [L], wuk, wuv, sc, kv_lora_rank=d_c)
+    ow, _ = mla_absorbed_ref(qn, qr, cache, [L], wuk.transpose(0, 2, 1), wuv, sc, kv_lora_rank=d_c)
+    with pytest.raises(AssertionError):
+        np.testing.assert_allclose(ow, oe, rtol=1e-9, atol=1e-9)
+
+
+def test_planted_dropped_empty_split_guard_is_caught():
+    # merging that multiplies an empty split's NaN output by its zero weight
+    po = rand(2, 1, 4)
+    po[1] = np.nan
+    pl = np.stack([rand(1), np.full(1, -np.inf)])
+    w = np.exp(pl - pl.max(axis=0))
+    naive = np.einsum("sb,sbd->bd", w / w.sum(axis=0), po)
+    assert np.isnan(naive).any()
+    o, _ = combine_ref(po, pl)
+    assert np.isfinite(o).all()

@@ -1,0 +1,299 @@
+"""Seeded synthetic inputs for single-token decode attention over a KV cache.
+
+This module holds no attention arithmetic: it only draws random numbers,
+rounds them to bfloat16 and lays them out. Both the CPU oracle tests and the
+GPU path take their inputs from here, so both see identical bits.
+
+Shapes follow the models the pages analyse:
+  * Llama-3-8B GQA (32 query heads / 8 KV heads, d_head 128) -- "Attention
+    variants and KV cache" (arganzheng.life), section 1.1 model baseline;
+  * Llama-2-7B MHA (32 heads, d_head 128) -- AIFAQ page, per-token element
+    counts for LlaMA-2-7B; kakack.github.io KV-cache page, section 5;
+  * DeepSeek-V3 MLA (128 heads, kv_lora_rank 512, rope 64, nope 128, v 128)
+    -- arganzheng.life section 4.2 config.json; jianzhnie.github.io MLA page,
+    section 3 (actual parameter configuration).
+
+Seeding recipe (every stream is numpy PCG64 via ``default_rng``):
+  * per-sequence lengths:       default_rng([seed, cfg, 0]) .integers(lo, hi, endpoint=True)
+  * queries (q, or q_nope then q_rope): default_rng([seed, cfg, 1])
+  * cache of sequence b (K then V, or latent rows [c_kv | k_rope]):
+                                default_rng([seed, cfg, 2, b])
+  * W_UK:                       default_rng([seed, cfg, 3])
+  * W_UV:                       default_rng([seed, cfg, 4])
+Normals are drawn in float32 and rounded to bfloat16 with round-to-nearest-even.
+W_UK / W_UV are N(0, 1/512): variance 1/512, i.e. standard deviation 1/sqrt(512).
+
+A padded cache has layout [B, L_max, H_kv, D] (GQA) or [B, L_max, 576] (MLA);
+rows at or past a sequence's length are filled with ``pad_value`` (NaN in
+parity runs, so that any read past the end of a sequence poisons the output).
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+from typing import Optional, Sequence
+
+import numpy as np
+
+BASE_SEED = 0
+
+BF16_NAN_BITS = np.uint16(0x7FC0)
+
+
+# ----------------------------------------------------------------------------
+# bfloat16 helpers (storage only: bf16 values are kept as uint16 bit patterns)
+# ----------------------------------------------------------------------------
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """float32 array -> bfloat16 bit patterns (uint16), round-to-nearest-even.
+
+    Inputs here are finite normals, so no NaN special-casing is needed.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    b = x.view(np.uint32)
+    r = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> exactly equal float32 values."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _normal(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return x
+
+
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+# ----------------------------------------------------------------------------
+# workload descriptions
+# ----------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class GQAShape:
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    # either a fixed length for every sequence, or an inclusive uniform range
+    seq_len: Optional[int] = None
+    seq_len_range: Optional[tuple] = None
+    dtype: str = "bf16"  # "bf16" or "f32"
+    name: str = "gqa"
+
+
+@dataclass(frozen=True)
+class MLAShape:
+    batch: int
+    num_heads: int = 128
+    seq_len: Optional[int] = None
+    seq_len_range: Optional[tuple] = None
+    kv_lora_rank: int = 512
+    qk_rope_dim: int = 64
+    qk_nope_dim: int = 128
+    v_head_dim: int = 128
+    name: str = "mla"
+
+
+# The five workloads: a tiny fp32 GQA case, Llama-3-8B GQA, DeepSeek-V3 MLA,
+# long-context MLA and ragged Llama-2-7B-shaped MHA.
+CONFIGS = {
+    1: GQAShape(1, 4, 2, 64, seq_len=128, dtype="f32", name="gqa-tiny-f32-b1-h4-kv2-d64-l128"),
+    2: GQAShape(32, 32, 8, 128, seq_len=4096, name="llama3-8b-gqa-b32-l4096"),
+    3: MLAShape(64, 128, seq_len=4096, name="deepseek-v3-mla-b64-l4096"),
+    4: MLAShape(4, 128, seq_len_range=(16384, 32768), name="deepseek-v3-mla-longctx-b4-l16k-32k"),
+    5: GQAShape(64, 32, 32, 128, seq_len_range=(1, 8192), name="llama2-7b-mha-ragged-b64-l1-8192"),
+}
+
+
+def draw_seq_lens(batch: int, seq_len=None, seq_len_range=None, cfg: int = 0,
+                  seed: int = BASE_SEED) -> np.ndarray:
+    if seq_len is not None:
+        return np.full(batch, int(seq_len), dtype=np.int32)
+    lo, hi = seq_len_range
+    rng = np.random.default_rng([seed, cfg, 0])
+    return rng.integers(lo, hi, size=batch, endpoint=True).astype(np.int32)
+
+
+# ----------------------------------------------------------------------------
+# GQA / MQA / MHA
+# ----------------------------------------------------------------------------
+
+@dataclass
+class GQAInputs:
+    """Host copies of one GQA decode problem.
+
+    q: [B, Hq, D]; k, v: [B, L_max, Hkv, D]. For dtype "bf16" arrays hold
+    uint16 bit patterns, for "f32" they hold float32 values.
+    """
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    seq_lens: np.ndarray
+    dtype: str
+    scale: float
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def shape(self):
+        B, Hq, D = self.q.shape
+        return B, Hq, self.k.shape[2], D, self.k.shape[1]
+
+    def as_f64(self, name: str) -> np.ndarray:
+        a = getattr(self, name)
+        if self.dtype == "bf16":
+            return bf16_to_f32(a).astype(np.float64)
+        return a.astype(np.float64)
+
+
+def _store(x_f32: np.ndarray, dtype: str) -> np.ndarray:
+    return bf16_round(x_f32) if dtype == "bf16" else np.ascontiguousarray(x_f32, np.float32)
+
+
+def _pad_fill(dtype: str, pad_value: float):
+    if dtype == "bf16":
+        if np.isnan(pad_value):
+            return BF16_NAN_BITS
+        return bf16_round(np.array([pad_value], np.float32))[0]
+    return np.float32(pad_value)
+
+
+def make_gqa(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+             seq_lens: Sequence[int], dtype: str = "bf16", cfg: int = 0,
+             seed: int = BASE_SEED, max_seq_len: Optional[int] = None,
+             pad_value: float = 0.0, only_seqs: Optional[Sequence[int]] = None) -> GQAInputs:
+    """Draw q, K, V ~ N(0, 1) for a GQA decode step.
+
+    ``only_seqs`` restricts cache generation to the listed sequences (other
+    sequences stay filled with ``pad_value``); their bits are identical to a
+    full generation because each sequence owns its own random stream.
+    """
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    assert seq_lens.shape == (batch,)
+    L_max = int(max_seq_len if max_seq_len is not None else max(1, int(seq_lens.max(initial=0))))
+    assert int(seq_lens.max(initial=0)) <= L_max
+    B, Hq, Hkv, D = batch, num_q_heads, num_kv_heads, head_dim
+    rq = np.random.default_rng([seed, cfg, 1])
+    q = _store(_normal(rq, (B, Hq, D)), dtype)
+    store_dt = np.uint16 if dtype == "bf16" else np.float32
+    k = np.empty((B, L_max, Hkv, D), dtype=store_dt)
+    v = np.empty((B, L_max, Hkv, D), dtype=store_dt)
+    fill = _pad_fill(dtype, pad_value)
+
+    def one(b):
+        L = int(seq_lens[b])
+        k[b, L:] = fill
+        v[b, L:] = fill
+        if only_seqs is not None and b not in only_seqs:
+            k[b, :L] = fill
+            v[b, :L] = fill
+            return
+        r = np.random.default_rng([seed, cfg, 2, b])
+        k[b, :L] = _store(_normal(r, (L, Hkv, D)), dtype)
+        v[b, :L] = _store(_normal(r, (L, Hkv, D)), dtype)
+
+    if B > 1 and int(seq_lens.sum()) * Hkv * D > (1 << 22):
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(one, range(B)))
+    else:
+        for b in range(B):
+            one(b)
+    scale = 1.0 / float(np.sqrt(D))
+    return GQAInputs(q, k, v, seq_lens, dtype, scale,
+                     meta=dict(cfg=cfg, seed=seed, pad_value=pad_value))
+
+
+def make_gqa_config(cfg: int, seed: int = BASE_SEED, pad_value: float = 0.0,
+                    only_seqs=None, batch: Optional[int] = None) -> GQAInputs:
+    s = CONFIGS[cfg]
+    assert isinstance(s, GQAShape)
+    B = s.batch if batch is None else batch
+    lens = draw_seq_lens(s.batch, s.seq_len, s.seq_len_range, cfg, seed)[:B]
+    L_max = s.seq_len if s.seq_len is not None else s.seq_len_range[1]
+    return make_gqa(B, s.num_q_heads, s.num_kv_heads, s.head_dim, lens, s.dtype,
+                    cfg=cfg, seed=seed, max_seq_len=L_max, pad_value=pad_value,
+                    only_seqs=only_seqs)
+
+
+# ----------------------------------------------------------------------------
+# absorbed MLA
+# ----------------------------------------------------------------------------
+
+@dataclass
+class MLAInputs:
+    """Host copies (bf16 bit patterns) of one absorbed-MLA decode problem.
+
+    q_nope [B,H,d_nope], q_rope [B,H,d_rope], cache [B,L_max,d_c+d_rope]
+    (row = [c_kv | k_rope]), w_uk and w_uv [H, d_c, d_nope] / [H, d_c, d_v].
+    """
+    q_nope: np.ndarray
+    q_rope: np.ndarray
+    cache: np.ndarray
+    w_uk: np.ndarray
+    w_uv: np.ndarray
+    seq_lens: np.ndarray
+    scale: float
+    meta: dict = field(default_factory=dict)
+
+    def as_f64(self, name: str) -> np.ndarray:
+        return bf16_to_f32(getattr(self, name)).astype(np.float64)
+
+
+def make_mla(batch: int, num_heads: int, seq_lens: Sequence[int], cfg: int = 0,
+             seed: int = BASE_SEED, max_seq_len: Optional[int] = None,
+             kv_lora_rank: int = 512, qk_rope_dim: int = 64, qk_nope_dim: int = 128,
+             v_head_dim: int = 128, pad_value: float = 0.0,
+             only_seqs: Optional[Sequence[int]] = None) -> MLAInputs:
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    assert seq_lens.shape == (batch,)
+    L_max = int(max_seq_len if max_seq_len is not None else max(1, int(seq_lens.max(initial=0))))
+    B, H = batch, num_heads
+    row = kv_lora_rank + qk_rope_dim
+    rq = np.random.default_rng([seed, cfg, 1])
+    q_nope = bf16_round(_normal(rq, (B, H, qk_nope_dim)))
+    q_rope = bf16_round(_normal(rq, (B, H, qk_rope_dim)))
+    cache = np.empty((B, L_max, row), dtype=np.uint16)
+    fill = _pad_fill("bf16", pad_value)
+
+    def one(b):
+        L = int(seq_lens[b])
+        cache[b, L:] = fill
+        if only_seqs is not None and b not in only_seqs:
+            cache[b, :L] = fill
+            return
+        r = np.random.default_rng([seed, cfg, 2, b])
+        cache[b, :L] = bf16_round(_normal(r, (L, row)))
+
+    if B > 1 and int(seq_lens.sum()) * row > (1 << 22):
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(one, range(B)))
+    else:
+        for b in range(B):
+            one(b)
+    std = 1.0 / float(np.sqrt(kv_lora_rank))
+    w_uk = bf16_round(_normal(np.random.default_rng([seed, cfg, 3]), (H, kv_lora_rank, qk_nope_dim), std))
+    w_uv = bf16_round(_normal(np.random.default_rng([seed, cfg, 4]), (H, kv_lora_rank, v_head_dim), std))
+    scale = 1.0 / float(np.sqrt(qk_nope_dim + qk_rope_dim))
+    return MLAInputs(q_nope, q_rope, cache, w_uk, w_uv, seq_lens, scale,
+                     meta=dict(cfg=cfg, seed=seed, pad_value=pad_value))
+
+
+def make_mla_config(cfg: int, seed: int = BASE_SEED, pad_value: float = 0.0,
+                    only_seqs=None, batch: Optional[int] = None) -> MLAInputs:
+    s = CONFIGS[cfg]
+    assert isinstance(s, MLAShape)
+    B = s.batch if batch is None else batch
+    lens = draw_seq_lens(s.batch, s.seq_len, s.seq_len_range, cfg, seed)[:B]
+    L_max = s.seq_len if s.seq_len is not None else s.seq_len_range[1]
+    return make_mla(B, s.num_heads, lens, cfg=cfg, seed=seed, max_seq_len=L_max,
+                    kv_lora_rank=s.kv_lora_rank, qk_rope_dim=s.qk_rope_dim,
+                    qk_nope_dim=s.qk_nope_dim, v_head_dim=s.v_head_dim,
+                    pad_value=pad_value, only_seqs=only_seqs)
