@@ -1,0 +1,341 @@
+"""Decode attention over a KV cache on AMD MI355X: Python binding.
+
+A thin ctypes layer over libdecode_attn.so (see include/decode_attn.h). It
+only marshals arguments: it reads tensor pointers, shapes and strides,
+allocates outputs and workspace through PyTorch's caching allocator and passes
+the current HIP stream. Every step of the computation runs in the library's
+HIP kernels; there is no fallback. If the library is missing, every call
+raises.
+
+    out, lse = gqa_decode(q, k_cache, v_cache, seq_lens)
+    out, lse = mla_decode_absorbed(q_nope, q_rope, kv_cache, w_uk, w_uv, seq_lens)
+    out, lse = splitkv_combine(partial_out, partial_lse)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libdecode_attn.so")
+
+DA_OK = 0
+DA_DTYPE_F32 = 0
+DA_DTYPE_BF16 = 1
+
+
+class GqaParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("q_stride_b", ctypes.c_int64),
+        ("q_stride_h", ctypes.c_int64),
+        ("kv_stride_b", ctypes.c_int64),
+        ("kv_stride_t", ctypes.c_int64),
+        ("kv_stride_h", ctypes.c_int64),
+        ("num_splits", ctypes.c_int32),
+    ]
+
+
+class MlaParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("kv_lora_rank", ctypes.c_int32),
+        ("qk_rope_dim", ctypes.c_int32),
+        ("qk_nope_dim", ctypes.c_int32),
+        ("v_head_dim", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("cache_stride_b", ctypes.c_int64),
+        ("cache_stride_t", ctypes.c_int64),
+        ("num_splits", ctypes.c_int32),
+    ]
+
+
+_vp = ctypes.c_void_p
+_SIGNATURES = {
+    "da_gqa_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(GqaParams)]),
+    "da_gqa_decode_num_splits": (ctypes.c_int32, [ctypes.POINTER(GqaParams)]),
+    "da_gqa_decode_split_pass": (ctypes.c_int, [ctypes.POINTER(GqaParams), _vp, _vp, _vp, _vp, _vp,
+                                                _vp, _vp]),
+    "da_gqa_decode": (ctypes.c_int, [ctypes.POINTER(GqaParams), _vp, _vp, _vp, _vp, _vp, _vp,
+                                     _vp, ctypes.c_size_t, _vp]),
+    "da_mla_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MlaParams)]),
+    "da_mla_decode_num_splits": (ctypes.c_int32, [ctypes.POINTER(MlaParams)]),
+    "da_mla_decode_absorbed": (ctypes.c_int, [ctypes.POINTER(MlaParams), _vp, _vp, _vp, _vp, _vp,
+                                              _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "da_splitkv_combine": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]),
+    "da_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "da_version": (ctypes.c_int32, []),
+    "da_gqa_params_size": (ctypes.c_size_t, []),
+    "da_mla_params_size": (ctypes.c_size_t, []),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded on first use). Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise LibraryMissing(
+            f"{LIB_PATH} is not built; run `python -m decode_attention_kv_bf16_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    if L.da_gqa_params_size() != ctypes.sizeof(GqaParams) or \
+            L.da_mla_params_size() != ctypes.sizeof(MlaParams):
+        raise RuntimeError("libdecode_attn.so parameter structs do not match this binding")
+    _lib = L
+    return L
+
+
+def loaded_library_path() -> Optional[str]:
+    return LIB_PATH if _lib is not None else None
+
+
+class DecodeAttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        msg = lib().da_status_string(status).decode()
+        super().__init__(f"{what}: {msg} (status {status})")
+        self.status = status
+
+
+def _check(status: int, what: str):
+    if status != DA_OK:
+        raise DecodeAttnError(status, what)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _require_cuda(name: str, t: torch.Tensor):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+# ----------------------------------------------------------------------------
+# GQA / MQA / MHA
+# ----------------------------------------------------------------------------
+
+def gqa_params(q: torch.Tensor, k_cache: torch.Tensor, softmax_scale: Optional[float] = None,
+               num_splits: int = 0) -> GqaParams:
+    B, Hq, D = q.shape
+    Bk, L_max, Hkv, Dk = k_cache.shape
+    if Bk != B or Dk != D:
+        raise ValueError(f"q {tuple(q.shape)} and cache {tuple(k_cache.shape)} disagree")
+    if q.dtype == torch.bfloat16:
+        dt = DA_DTYPE_BF16
+    elif q.dtype == torch.float32:
+        dt = DA_DTYPE_F32
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if q.stride(2) != 1 or k_cache.stride(3) != 1:
+        raise ValueError("the head_dim axis must be contiguous")
+    p = GqaParams()
+    p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim, p.max_seq_len = B, Hq, Hkv, D, L_max
+    p.dtype = dt
+    p.softmax_scale = (1.0 / math.sqrt(D)) if softmax_scale is None else float(softmax_scale)
+    p.q_stride_b, p.q_stride_h = q.stride(0), q.stride(1)
+    p.kv_stride_b, p.kv_stride_t, p.kv_stride_h = k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)
+    p.num_splits = int(num_splits)
+    return p
+
+
+def gqa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+               seq_lens: Optional[torch.Tensor] = None, softmax_scale: Optional[float] = None,
+               num_splits: int = 0, out: Optional[torch.Tensor] = None,
+               lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """GQA/MQA/MHA decode of one new token per sequence.
+
+    q [B, Hq, D]; k_cache, v_cache [B, L_max, Hkv, D] (same dtype, bf16 or fp32,
+    same strides); seq_lens [B] int32 on the GPU (None: all L_max).
+    Returns out [B, Hq, D] float32 and lse [B, Hq] float32 (natural log).
+    """
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _require_cuda(name, t)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q, k_cache and v_cache must share a dtype")
+    if v_cache.shape != k_cache.shape or v_cache.stride() != k_cache.stride():
+        raise ValueError("v_cache must have the shape and strides of k_cache")
+    if seq_lens is not None:
+        _require_cuda("seq_lens", seq_lens)
+        if seq_lens.dtype != torch.int32 or seq_lens.shape != (q.shape[0],) or not seq_lens.is_contiguous():
+            raise ValueError("seq_lens must be a contiguous int32 tensor of shape [B]")
+    p = gqa_params(q, k_cache, softmax_scale, num_splits)
+    L = lib()
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ws_bytes = L.da_gqa_decode_workspace_size(ctypes.byref(p))
+    ws = _workspace(ws_bytes, q.device)
+    st = L.da_gqa_decode(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                         _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream_handle())
+    _check(st, "da_gqa_decode")
+    return out, lse
+
+
+def gqa_decode_split_pass(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          seq_lens: Optional[torch.Tensor] = None,
+                          softmax_scale: Optional[float] = None, num_splits: int = 0,
+                          part_out: Optional[torch.Tensor] = None,
+                          part_lse: Optional[torch.Tensor] = None):
+    """The split pass alone: returns per-split (part_out [S,B,Hq,D], part_lse [S,B,Hq]).
+    splitkv_combine() of these equals gqa_decode()."""
+    p = gqa_params(q, k_cache, softmax_scale, num_splits)
+    L = lib()
+    S = int(L.da_gqa_decode_num_splits(ctypes.byref(p)))
+    B, Hq, D = q.shape
+    if part_out is None:
+        part_out = torch.empty((S, B, Hq, D), dtype=torch.float32, device=q.device)
+    if part_lse is None:
+        part_lse = torch.empty((S, B, Hq), dtype=torch.float32, device=q.device)
+    st = L.da_gqa_decode_split_pass(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(seq_lens), _ptr(part_out), _ptr(part_lse),
+                                    _stream_handle())
+    _check(st, "da_gqa_decode_split_pass")
+    return part_out, part_lse
+
+
+def gqa_num_splits(q: torch.Tensor, k_cache: torch.Tensor, num_splits: int = 0) -> int:
+    p = gqa_params(q, k_cache, None, num_splits)
+    return int(lib().da_gqa_decode_num_splits(ctypes.byref(p)))
+
+
+# ----------------------------------------------------------------------------
+# absorbed MLA
+# ----------------------------------------------------------------------------
+
+def mla_params(q_nope: torch.Tensor, kv_cache: torch.Tensor, w_uv: torch.Tensor,
+               q_rope: torch.Tensor, softmax_scale: Optional[float] = None,
+               num_splits: int = 0) -> MlaParams:
+    B, H, d_nope = q_nope.shape
+    Bc, L_max, row = kv_cache.shape
+    d_rope = q_rope.shape[2]
+    d_c = row - d_rope
+    if Bc != B:
+        raise ValueError("q_nope and kv_cache disagree on the batch size")
+    if kv_cache.stride(2) != 1:
+        raise ValueError("kv_cache rows must be contiguous")
+    p = MlaParams()
+    p.batch, p.num_heads, p.kv_lora_rank, p.qk_rope_dim = B, H, d_c, d_rope
+    p.qk_nope_dim, p.v_head_dim, p.max_seq_len = d_nope, w_uv.shape[2], L_max
+    p.softmax_scale = (1.0 / math.sqrt(d_nope + d_rope)) if softmax_scale is None else float(softmax_scale)
+    p.cache_stride_b, p.cache_stride_t = kv_cache.stride(0), kv_cache.stride(1)
+    p.num_splits = int(num_splits)
+    return p
+
+
+def mla_decode_absorbed(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_cache: torch.Tensor,
+                        w_uk: torch.Tensor, w_uv: torch.Tensor,
+                        seq_lens: Optional[torch.Tensor] = None,
+                        softmax_scale: Optional[float] = None, num_splits: int = 0,
+                        out: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """DeepSeek-style absorbed MLA decode of one new token per sequence.
+
+    q_nope [B,H,128], q_rope [B,H,64], kv_cache [B,L_max,576] (row = [c_kv | k_rope]),
+    w_uk, w_uv [H,512,128] -- all bf16; seq_lens [B] int32 on the GPU or None.
+    Returns out [B,H,128] float32 and lse [B,H] float32.
+    """
+    for name, t in (("q_nope", q_nope), ("q_rope", q_rope), ("kv_cache", kv_cache),
+                    ("w_uk", w_uk), ("w_uv", w_uv)):
+        _require_cuda(name, t)
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+    for name, t in (("q_nope", q_nope), ("q_rope", q_rope), ("w_uk", w_uk), ("w_uv", w_uv)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, H, _ = q_nope.shape
+    if q_rope.shape[:2] != (B, H) or w_uk.shape[0] != H or w_uv.shape[0] != H:
+        raise ValueError("head counts disagree")
+    if w_uk.shape[1] != kv_cache.shape[2] - q_rope.shape[2] or w_uk.shape[2] != q_nope.shape[2]:
+        raise ValueError("w_uk must be [H, d_c, d_nope]")
+    if w_uv.shape[1] != w_uk.shape[1]:
+        raise ValueError("w_uv must be [H, d_c, d_v]")
+    if seq_lens is not None:
+        _require_cuda("seq_lens", seq_lens)
+        if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,) or not seq_lens.is_contiguous():
+            raise ValueError("seq_lens must be a contiguous int32 tensor of shape [B]")
+    p = mla_params(q_nope, kv_cache, w_uv, q_rope, softmax_scale, num_splits)
+    L = lib()
+    if out is None:
+        out = torch.empty((B, H, w_uv.shape[2]), dtype=torch.float32, device=q_nope.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q_nope.device)
+    ws_bytes = L.da_mla_decode_workspace_size(ctypes.byref(p))
+    ws = _workspace(ws_bytes, q_nope.device)
+    st = L.da_mla_decode_absorbed(ctypes.byref(p), _ptr(q_nope), _ptr(q_rope), _ptr(kv_cache),
+                                  _ptr(seq_lens), _ptr(w_uk), _ptr(w_uv), _ptr(out), _ptr(lse),
+                                  _ptr(ws), ws_bytes, _stream_handle())
+    _check(st, "da_mla_decode_absorbed")
+    return out, lse
+
+
+def mla_num_splits(q_nope, q_rope, kv_cache, w_uv, num_splits: int = 0) -> int:
+    p = mla_params(q_nope, kv_cache, w_uv, q_rope, None, num_splits)
+    return int(lib().da_mla_decode_num_splits(ctypes.byref(p)))
+
+
+# ----------------------------------------------------------------------------
+# split-KV merge
+# ----------------------------------------------------------------------------
+
+def splitkv_combine(partial_out: torch.Tensor, partial_lse: torch.Tensor,
+                    out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Merge split partials: partial_out [S,B,H,D], partial_lse [S,B,H] (float32)."""
+    _require_cuda("partial_out", partial_out)
+    _require_cuda("partial_lse", partial_lse)
+    if partial_out.dtype != torch.float32 or partial_lse.dtype != torch.float32:
+        raise ValueError("partials must be float32")
+    if not partial_out.is_contiguous() or not partial_lse.is_contiguous():
+        raise ValueError("partials must be contiguous")
+    S, B, H, D = partial_out.shape
+    if partial_lse.shape != (S, B, H):
+        raise ValueError("partial_lse must be [S, B, H]")
+    if out is None:
+        out = torch.empty((B, H, D), dtype=torch.float32, device=partial_out.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=partial_out.device)
+    st = lib().da_splitkv_combine(S, B, H, D, _ptr(partial_out), _ptr(partial_lse), _ptr(out),
+                                  _ptr(lse), _stream_handle())
+    _check(st, "da_splitkv_combine")
+    return out, lse
+
+
+__all__ = ["gqa_decode", "mla_decode_absorbed", "splitkv_combine", "gqa_num_splits",
+           "mla_num_splits", "lib", "LIB_PATH", "GqaParams", "MlaParams", "DecodeAttnError",
+           "LibraryMissing"]

@@ -1,0 +1,350 @@
+// C ABI of libdecode_attn.so: argument checks, split planning, workspace
+// layout and kernel dispatch. Every check runs on the host before any launch.
+#include <math.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "da_internal.h"
+#include "decode_attn.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+// Compute units of the current device (cached); 256 (a full MI355X) when no
+// device can be queried, so that host-only queries still answer.
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  g_cu_count[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------------------
+// GQA
+// ---------------------------------------------------------------------------
+
+// Largest divisor of the group size that is at most 8: the number of query
+// heads one workgroup serves from one pass over a KV head.
+int gqa_heads_per_block(int group) {
+  for (int gh = 8; gh >= 1; --gh)
+    if (group % gh == 0) return gh;
+  return 1;
+}
+
+da_status_t check_gqa_params(const da_gqa_params_t* p) {
+  if (!p) return DA_ERR_INVALID_ARGUMENT;
+  if (p->batch < 1 || p->batch > 65535 || p->num_q_heads < 1 || p->num_kv_heads < 1 ||
+      p->max_seq_len < 1 || p->head_dim < 1 || p->num_splits < 0)
+    return DA_ERR_INVALID_ARGUMENT;
+  if (p->num_q_heads % p->num_kv_heads != 0) return DA_ERR_INVALID_ARGUMENT;
+  if (p->num_q_heads > 65535) return DA_ERR_INVALID_ARGUMENT;
+  if (p->dtype != DA_DTYPE_F32 && p->dtype != DA_DTYPE_BF16) return DA_ERR_INVALID_ARGUMENT;
+  if (!isfinite(p->softmax_scale)) return DA_ERR_INVALID_ARGUMENT;
+  if (p->head_dim != 64 && p->head_dim != 128) return DA_ERR_UNSUPPORTED;
+  const int64_t esz = p->dtype == DA_DTYPE_BF16 ? 2 : 4;
+  const int64_t strides[5] = {p->q_stride_b, p->q_stride_h, p->kv_stride_b, p->kv_stride_t,
+                              p->kv_stride_h};
+  for (int64_t s : strides)
+    if (s < 0 || (s * esz) % 16 != 0) return DA_ERR_INVALID_ARGUMENT;
+  return DA_OK;
+}
+
+struct GqaPlan {
+  int splits, chunk, heads_per_block;
+  size_t part_out_bytes, part_lse_bytes, workspace;
+};
+
+GqaPlan plan_gqa(const da_gqa_params_t* p) {
+  GqaPlan pl{};
+  const int group = p->num_q_heads / p->num_kv_heads;
+  pl.heads_per_block = gqa_heads_per_block(group);
+  const int64_t units = (int64_t)p->batch * p->num_kv_heads * (group / pl.heads_per_block);
+  int64_t s;
+  if (p->num_splits > 0) {
+    s = p->num_splits;
+  } else {
+    // Enough 4-wave workgroups for ~4 per CU, and no split longer than 1024
+    // rows (bounds the tail when lengths are ragged), but no split shorter
+    // than 256 rows unless the sequence itself is shorter.
+    const int64_t target = 4LL * device_cu_count();
+    s = ceil_div(target, units);
+    s = s > ceil_div(p->max_seq_len, 1024) ? s : ceil_div(p->max_seq_len, 1024);
+    const int64_t s_max = ceil_div(p->max_seq_len, 256);
+    s = s < s_max ? s : s_max;
+  }
+  if (s > p->max_seq_len) s = p->max_seq_len;
+  if (s < 1) s = 1;
+  pl.chunk = (int)ceil_div(p->max_seq_len, s);
+  pl.splits = (int)ceil_div(p->max_seq_len, pl.chunk);  // drop splits that would be empty
+  if (pl.splits > 1) {
+    const size_t rows = (size_t)p->batch * p->num_q_heads;
+    pl.part_out_bytes = round_up((size_t)pl.splits * rows * p->head_dim * sizeof(float), 256);
+    pl.part_lse_bytes = round_up((size_t)pl.splits * rows * sizeof(float), 256);
+    pl.workspace = pl.part_out_bytes + pl.part_lse_bytes;
+  }
+  return pl;
+}
+
+// ---------------------------------------------------------------------------
+// MLA
+// ---------------------------------------------------------------------------
+
+constexpr int kMlaDc = 512, kMlaRope = 64, kMlaNope = 128, kMlaV = 128;
+
+da_status_t check_mla_params(const da_mla_params_t* p) {
+  if (!p) return DA_ERR_INVALID_ARGUMENT;
+  if (p->batch < 1 || p->batch > 65535 || p->num_heads < 1 || p->max_seq_len < 1 ||
+      p->num_splits < 0 || p->kv_lora_rank < 1 || p->qk_rope_dim < 0 || p->qk_nope_dim < 1 ||
+      p->v_head_dim < 1)
+    return DA_ERR_INVALID_ARGUMENT;
+  if (!isfinite(p->softmax_scale)) return DA_ERR_INVALID_ARGUMENT;
+  if (p->kv_lora_rank != kMlaDc || p->qk_rope_dim != kMlaRope || p->qk_nope_dim != kMlaNope ||
+      p->v_head_dim != kMlaV)
+    return DA_ERR_UNSUPPORTED;
+  if (p->num_heads % 16 != 0 || p->num_heads > 128) return DA_ERR_UNSUPPORTED;
+  if (p->cache_stride_b < 0 || p->cache_stride_t < kMlaDc + kMlaRope ||
+      (p->cache_stride_b * 2) % 16 != 0 || (p->cache_stride_t * 2) % 16 != 0)
+    return DA_ERR_INVALID_ARGUMENT;
+  return DA_OK;
+}
+
+struct MlaPlan {
+  int splits, chunk;
+  size_t q_hat_bytes, part_out_bytes, part_lse_bytes, workspace;
+};
+
+MlaPlan plan_mla(const da_mla_params_t* p) {
+  MlaPlan pl{};
+  int64_t s;
+  if (p->num_splits > 0) {
+    s = p->num_splits;
+  } else {
+    // One workgroup (all heads of one sequence) per CU; splits no shorter
+    // than 128 rows.
+    s = ceil_div(device_cu_count(), p->batch);
+    const int64_t s_max = ceil_div(p->max_seq_len, 128);
+    s = s < s_max ? s : s_max;
+  }
+  if (s > p->max_seq_len) s = p->max_seq_len;
+  if (s < 1) s = 1;
+  pl.chunk = (int)ceil_div(p->max_seq_len, s);
+  pl.splits = (int)ceil_div(p->max_seq_len, pl.chunk);
+  const size_t rows = (size_t)p->batch * p->num_heads;
+  pl.q_hat_bytes = round_up(rows * (kMlaDc + kMlaRope) * 2, 256);
+  pl.part_out_bytes = round_up((size_t)pl.splits * rows * kMlaDc * sizeof(float), 256);
+  pl.part_lse_bytes = round_up((size_t)pl.splits * rows * sizeof(float), 256);
+  pl.workspace = pl.q_hat_bytes + pl.part_out_bytes + pl.part_lse_bytes;
+  return pl;
+}
+
+da_status_t from_hip(hipError_t e) { return e == hipSuccess ? DA_OK : DA_ERR_HIP; }
+
+}  // namespace
+
+namespace {
+
+da_status_t check_gqa_buffers(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* seq_lens, const float* out, const float* lse) {
+  if (!q || !k_cache || !v_cache || !out) return DA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return DA_ERR_INVALID_ARGUMENT;
+  if ((seq_lens && (reinterpret_cast<uintptr_t>(seq_lens) & 3u)) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return DA_ERR_INVALID_ARGUMENT;
+  return DA_OK;
+}
+
+da::GqaArgs gqa_args(const da_gqa_params_t* p, const GqaPlan& pl, const void* q,
+                     const void* k_cache, const void* v_cache, const int32_t* seq_lens) {
+  da::GqaArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.seq_lens = seq_lens;
+  a.q_sb = p->q_stride_b;
+  a.q_sh = p->q_stride_h;
+  a.kv_sb = p->kv_stride_b;
+  a.kv_st = p->kv_stride_t;
+  a.kv_sh = p->kv_stride_h;
+  a.batch = p->batch;
+  a.num_q_heads = p->num_q_heads;
+  a.num_kv_heads = p->num_kv_heads;
+  a.group = p->num_q_heads / p->num_kv_heads;
+  a.heads_per_block = pl.heads_per_block;
+  a.max_seq_len = p->max_seq_len;
+  a.num_splits = pl.splits;
+  a.chunk = pl.chunk;
+  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  return a;
+}
+
+}  // namespace
+
+
+extern "C" {
+
+size_t da_gqa_decode_workspace_size(const da_gqa_params_t* p) {
+  if (check_gqa_params(p) != DA_OK) return 0;
+  return plan_gqa(p).workspace;
+}
+
+int32_t da_gqa_decode_num_splits(const da_gqa_params_t* p) {
+  if (check_gqa_params(p) != DA_OK) return 0;
+  return plan_gqa(p).splits;
+}
+
+da_status_t da_gqa_decode_split_pass(const da_gqa_params_t* p, const void* q,
+                                     const void* k_cache, const void* v_cache,
+                                     const int32_t* seq_lens, float* part_out, float* part_lse,
+                                     void* hip_stream) {
+  da_status_t st = check_gqa_params(p);
+  if (st != DA_OK) return st;
+  st = check_gqa_buffers(q, k_cache, v_cache, seq_lens, part_out, part_lse);
+  if (st != DA_OK) return st;
+  if (!part_lse) return DA_ERR_INVALID_ARGUMENT;
+  const GqaPlan pl = plan_gqa(p);
+  da::GqaArgs a = gqa_args(p, pl, q, k_cache, v_cache, seq_lens);
+  if (pl.splits == 1) {
+    a.out = part_out;
+    a.lse = part_lse;
+  } else {
+    a.part_out = part_out;
+    a.part_lse = part_lse;
+  }
+  return from_hip(da::launch_gqa_decode(a, p->dtype == DA_DTYPE_BF16 ? 1 : 0, p->head_dim,
+                                        static_cast<hipStream_t>(hip_stream)));
+}
+
+da_status_t da_gqa_decode(const da_gqa_params_t* p, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* seq_lens, float* out, float* lse,
+                          void* workspace, size_t workspace_bytes, void* hip_stream) {
+  da_status_t st = check_gqa_params(p);
+  if (st != DA_OK) return st;
+  st = check_gqa_buffers(q, k_cache, v_cache, seq_lens, out, lse);
+  if (st != DA_OK) return st;
+  const GqaPlan pl = plan_gqa(p);
+  if (pl.workspace > 0) {
+    if (!workspace || workspace_bytes < pl.workspace) return DA_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned16(workspace)) return DA_ERR_INVALID_ARGUMENT;
+  }
+  da::GqaArgs a = gqa_args(p, pl, q, k_cache, v_cache, seq_lens);
+  a.out = out;
+  a.lse = lse;
+  if (pl.splits > 1) {
+    a.part_out = reinterpret_cast<float*>(workspace);
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.part_out_bytes);
+  }
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  hipError_t e = da::launch_gqa_decode(a, p->dtype == DA_DTYPE_BF16 ? 1 : 0, p->head_dim, stream);
+  if (e != hipSuccess) return DA_ERR_HIP;
+  if (pl.splits > 1) {
+    e = da::launch_splitkv_combine(pl.splits, p->batch * p->num_q_heads, p->head_dim, a.part_out,
+                                   a.part_lse, out, lse, stream);
+  }
+  return from_hip(e);
+}
+
+size_t da_mla_decode_workspace_size(const da_mla_params_t* p) {
+  if (check_mla_params(p) != DA_OK) return 0;
+  return plan_mla(p).workspace;
+}
+
+int32_t da_mla_decode_num_splits(const da_mla_params_t* p) {
+  if (check_mla_params(p) != DA_OK) return 0;
+  return plan_mla(p).splits;
+}
+
+da_status_t da_mla_decode_absorbed(const da_mla_params_t* p, const void* q_nope,
+                                   const void* q_rope, const void* kv_cache,
+                                   const int32_t* seq_lens, const void* w_uk, const void* w_uv,
+                                   float* out, float* lse, void* workspace,
+                                   size_t workspace_bytes, void* hip_stream) {
+  const da_status_t st = check_mla_params(p);
+  if (st != DA_OK) return st;
+  if (!q_nope || !q_rope || !kv_cache || !w_uk || !w_uv || !out) return DA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(kv_cache) || !aligned16(w_uk) ||
+      !aligned16(w_uv) || !aligned16(out))
+    return DA_ERR_INVALID_ARGUMENT;
+  if ((seq_lens && (reinterpret_cast<uintptr_t>(seq_lens) & 3u)) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return DA_ERR_INVALID_ARGUMENT;
+  const MlaPlan pl = plan_mla(p);
+  if (!workspace || workspace_bytes < pl.workspace) return DA_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(workspace)) return DA_ERR_INVALID_ARGUMENT;
+  char* ws = static_cast<char*>(workspace);
+  da::MlaArgs a{};
+  a.q_nope = static_cast<const uint16_t*>(q_nope);
+  a.q_rope = static_cast<const uint16_t*>(q_rope);
+  a.cache = static_cast<const uint16_t*>(kv_cache);
+  a.seq_lens = seq_lens;
+  a.w_uk = static_cast<const uint16_t*>(w_uk);
+  a.w_uv = static_cast<const uint16_t*>(w_uv);
+  a.out = out;
+  a.lse = lse;
+  a.q_hat = reinterpret_cast<uint16_t*>(ws);
+  a.part_out = reinterpret_cast<float*>(ws + pl.q_hat_bytes);
+  a.part_lse = reinterpret_cast<float*>(ws + pl.q_hat_bytes + pl.part_out_bytes);
+  a.cache_sb = p->cache_stride_b;
+  a.cache_st = p->cache_stride_t;
+  a.batch = p->batch;
+  a.num_heads = p->num_heads;
+  a.max_seq_len = p->max_seq_len;
+  a.num_splits = pl.splits;
+  a.chunk = pl.chunk;
+  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  const hipError_t e = da::launch_mla_decode(a, static_cast<hipStream_t>(hip_stream));
+  if (e == hipErrorNotSupported) return DA_ERR_UNSUPPORTED;
+  return from_hip(e);
+}
+
+da_status_t da_splitkv_combine(int32_t num_splits, int32_t batch, int32_t num_heads,
+                               int32_t head_dim, const float* partial_out,
+                               const float* partial_lse, float* out, float* lse,
+                               void* hip_stream) {
+  if (num_splits < 1 || batch < 1 || num_heads < 1 || head_dim < 4 || head_dim % 4 != 0 ||
+      head_dim > 1024)
+    return DA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)batch * num_heads > INT32_MAX) return DA_ERR_INVALID_ARGUMENT;
+  if (!partial_out || !partial_lse || !out) return DA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(partial_out) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(partial_lse) & 3u) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return DA_ERR_INVALID_ARGUMENT;
+  return from_hip(da::launch_splitkv_combine(num_splits, batch * num_heads, head_dim, partial_out,
+                                             partial_lse, out, lse,
+                                             static_cast<hipStream_t>(hip_stream)));
+}
+
+const char* da_status_string(da_status_t s) {
+  switch (s) {
+    case DA_OK: return "ok";
+    case DA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case DA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case DA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t da_version(void) { return 100; }
+
+size_t da_gqa_params_size(void) { return sizeof(da_gqa_params_t); }
+size_t da_mla_params_size(void) { return sizeof(da_mla_params_t); }
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// Host-side interfaces between the C ABI layer (api.hip) and the kernel
+// launchers. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace da {
+
+// One GQA decode launch (split-KV pass). Everything the kernel reads.
+struct GqaArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* seq_lens;   // may be null: every sequence has max_seq_len rows
+  float* out;                // [B, Hq, D] final output (used when num_splits == 1)
+  float* lse;                // [B, Hq] or null
+  float* part_out;           // [S, B, Hq, D] split partials (num_splits > 1)
+  float* part_lse;           // [S, B, Hq]
+  int64_t q_sb, q_sh;        // element strides
+  int64_t kv_sb, kv_st, kv_sh;
+  int32_t batch, num_q_heads, num_kv_heads, group;   // group = Hq / Hkv
+  int32_t heads_per_block;   // query heads one workgroup serves (divides group)
+  int32_t max_seq_len, num_splits, chunk;            // chunk = tokens per split
+  float scale_log2;          // softmax_scale * log2(e)
+};
+
+// dtype: 0 = f32, 1 = bf16 (matches da_dtype_t).
+hipError_t launch_gqa_decode(const GqaArgs& a, int dtype, int head_dim, hipStream_t stream);
+
+// Log-sum-exp merge of split partials: rows = B * H.
+hipError_t launch_splitkv_combine(int32_t num_splits, int32_t rows, int32_t head_dim,
+                                  const float* part_out, const float* part_lse,
+                                  float* out, float* lse, hipStream_t stream);
+
+// Absorbed-MLA decode: three launches (query absorption, split-KV latent
+// attention, merge + W_UV up-projection).
+struct MlaArgs {
+  const uint16_t* q_nope;    // [B, H, 128]
+  const uint16_t* q_rope;    // [B, H, 64]
+  const uint16_t* cache;     // row stride cache_st, batch stride cache_sb
+  const int32_t* seq_lens;
+  const uint16_t* w_uk;      // [H, 512, 128]
+  const uint16_t* w_uv;      // [H, 512, 128]
+  float* out;                // [B, H, 128]
+  float* lse;                // [B, H] or null
+  uint16_t* q_hat;           // workspace [B, H, 576] bf16: [q~ | q_rope]
+  float* part_out;           // workspace [S, B, H, 512]
+  float* part_lse;           // workspace [S, B, H]
+  int64_t cache_sb, cache_st;
+  int32_t batch, num_heads, max_seq_len, num_splits, chunk;
+  float scale_log2;
+};
+
+hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream);
+
+}  // namespace da

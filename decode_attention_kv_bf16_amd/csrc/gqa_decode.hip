@@ -1,0 +1,269 @@
+// GQA / MQA / MHA single-token decode, split-KV pass, for gfx950.
+//
+// What it computes: for each sequence b and query head h,
+//   s_j = scale * q[b,h,:] . k[b, j, h / g, :],  p = softmax_j(s),  o = sum_j p_j v[b, j, h / g, :]
+// over the cached rows j of one split of the sequence ("Attention variants and
+// KV cache", arganzheng.life, sections 3.2-3.3 for the grouping; section 5.2
+// for splitting decode attention along the sequence). Query head h reads KV
+// head h / g directly from the cache, with no expanded copy (shippingwang.com
+// chapter 7, section 7.3).
+//
+// Work decomposition (MI355X: 256 CUs, wave64):
+//   grid  = (split, KV head x head sub-group, batch); block = 4 waves.
+//   A workgroup serves GH query heads that share one KV head, so each K/V byte
+//   is fetched from HBM once and used GH times from registers.
+//   A cache row of D elements is spread over D/8 consecutive lanes (8 elements,
+//   16 or 32 bytes per lane), so one wave-wide load covers 4 (D=128) or 8 (D=64)
+//   whole rows: fully used 64-byte segments on every load instruction.
+//   Each group of lanes that owns a row keeps its own online-softmax state
+//   (running max m, sum l, accumulator) in registers; the per-row dot product
+//   is reduced across the D/8 lanes with DPP row moves. States are merged
+//   across the lanes of a wave at the end (cross-lane shuffles), then across
+//   the 4 waves through LDS.
+//   Scores live in the base-2 domain: q is pre-multiplied by scale*log2(e) so
+//   each softmax weight is one v_exp_f32.
+#include "da_device.h"
+#include "da_internal.h"
+
+namespace da {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kEPL = 8;  // elements of a cache row owned by one lane
+
+template <typename T>
+struct Row8;
+
+template <>
+struct Row8<uint16_t> {  // bfloat16 stored as bit patterns
+  struct Raw {
+    uint4 w;
+  };
+  static __device__ __forceinline__ Raw load(const uint16_t* p) {
+    return {*reinterpret_cast<const uint4*>(p)};
+  }
+  static __device__ __forceinline__ Raw zero() { return {make_uint4(0u, 0u, 0u, 0u)}; }
+  static __device__ __forceinline__ void cvt(const Raw& r, float* f) { unpack_bf16x8(r.w, f); }
+};
+
+template <>
+struct Row8<float> {
+  struct Raw {
+    float4 a, b;
+  };
+  static __device__ __forceinline__ Raw load(const float* p) {
+    return {reinterpret_cast<const float4*>(p)[0], reinterpret_cast<const float4*>(p)[1]};
+  }
+  static __device__ __forceinline__ Raw zero() {
+    return {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+  }
+  static __device__ __forceinline__ void cvt(const Raw& r, float* f) {
+    f[0] = r.a.x; f[1] = r.a.y; f[2] = r.a.z; f[3] = r.a.w;
+    f[4] = r.b.x; f[5] = r.b.y; f[6] = r.b.z; f[7] = r.b.w;
+  }
+};
+
+template <typename T, int D, int GH>
+__global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaArgs a) {
+  constexpr int LPT = D / kEPL;   // lanes per cache row
+  constexpr int RPW = 64 / LPT;   // rows covered by one wave-wide load
+  constexpr int U = 16 / RPW;     // rows per lane per step
+  constexpr int TOK = RPW * U;    // tokens per wave per step (16)
+  using R = Row8<T>;
+
+  const int split = blockIdx.x;
+  const int b = blockIdx.z;
+  const int n_sub = a.group / GH;
+  const int kvh = blockIdx.y / n_sub;
+  const int h0 = kvh * a.group + (blockIdx.y % n_sub) * GH;
+  const int L = a.seq_lens ? a.seq_lens[b] : a.max_seq_len;
+  const int t_begin = split * a.chunk;
+  const int t_end = min(L, t_begin + a.chunk);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int row = lane / LPT;
+  const int col = lane % LPT;
+  const bool direct = a.num_splits == 1;
+  const int64_t rows = (int64_t)a.batch * a.num_q_heads;
+  const int64_t r0 = (int64_t)b * a.num_q_heads + h0;
+
+  if (t_begin >= t_end) {  // this split holds no rows of the sequence
+    if (direct) {
+      for (int i = threadIdx.x; i < GH * D; i += kThreads) a.out[r0 * D + i] = 0.f;
+      if (threadIdx.x < GH && a.lse) a.lse[r0 + threadIdx.x] = kNegInf;
+    } else if (threadIdx.x < GH) {
+      a.part_lse[split * rows + r0 + threadIdx.x] = kNegInf;
+    }
+    return;
+  }
+
+  float qf[GH][kEPL];
+  {
+    const T* qp = reinterpret_cast<const T*>(a.q) + b * a.q_sb + col * kEPL;
+#pragma unroll
+    for (int i = 0; i < GH; ++i) {
+      R::cvt(R::load(qp + (int64_t)(h0 + i) * a.q_sh), qf[i]);
+#pragma unroll
+      for (int e = 0; e < kEPL; ++e) qf[i][e] *= a.scale_log2;
+    }
+  }
+
+  float m[GH], l[GH], acc[GH][kEPL];
+#pragma unroll
+  for (int i = 0; i < GH; ++i) {
+    m[i] = kNegInf;
+    l[i] = 0.f;
+#pragma unroll
+    for (int e = 0; e < kEPL; ++e) acc[i][e] = 0.f;
+  }
+
+  const T* kp = reinterpret_cast<const T*>(a.k) + b * a.kv_sb + kvh * a.kv_sh + col * kEPL;
+  const T* vp = reinterpret_cast<const T*>(a.v) + b * a.kv_sb + kvh * a.kv_sh + col * kEPL;
+
+  for (int base = t_begin + wave * TOK; base < t_end; base += kWaves * TOK) {
+    typename R::Raw kw[U], vw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = base + u * RPW + row;
+      if (t < t_end) {
+        kw[u] = R::load(kp + (int64_t)t * a.kv_st);
+        vw[u] = R::load(vp + (int64_t)t * a.kv_st);
+      } else {
+        kw[u] = R::zero();
+        vw[u] = R::zero();
+      }
+    }
+    float s[GH][U];
+    float vf[U][kEPL];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kf[kEPL];
+      R::cvt(kw[u], kf);
+      R::cvt(vw[u], vf[u]);
+      const bool valid = base + u * RPW + row < t_end;
+#pragma unroll
+      for (int i = 0; i < GH; ++i) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < kEPL; ++e) d = fmaf(qf[i][e], kf[e], d);
+        d = group_sum<LPT>(d);
+        s[i][u] = valid ? d : kNegInf;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < GH; ++i) {
+      float mx = m[i];
+#pragma unroll
+      for (int u = 0; u < U; ++u) mx = fmaxf(mx, s[i][u]);
+      const float mu = (mx == kNegInf) ? 0.f : mx;
+      const float alpha = exp2_hw(m[i] - mu);
+      l[i] *= alpha;
+#pragma unroll
+      for (int e = 0; e < kEPL; ++e) acc[i][e] *= alpha;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float p = exp2_hw(s[i][u] - mu);
+        l[i] += p;
+#pragma unroll
+        for (int e = 0; e < kEPL; ++e) acc[i][e] = fmaf(p, vf[u][e], acc[i][e]);
+      }
+      m[i] = mx;
+    }
+  }
+
+  // Merge the row groups of this wave: lanes with the same `col`.
+#pragma unroll
+  for (int off = LPT; off < 64; off <<= 1) {
+#pragma unroll
+    for (int i = 0; i < GH; ++i) {
+      const float mo = __shfl_xor(m[i], off);
+      const float lo = __shfl_xor(l[i], off);
+      const MergeFactors f = merge_factors(m[i], mo);
+      l[i] = l[i] * f.a + lo * f.b;
+#pragma unroll
+      for (int e = 0; e < kEPL; ++e) acc[i][e] = acc[i][e] * f.a + __shfl_xor(acc[i][e], off) * f.b;
+      m[i] = f.m;
+    }
+  }
+
+  // Merge the waves through LDS and write the result.
+  __shared__ float sm_m[kWaves][GH];
+  __shared__ float sm_l[kWaves][GH];
+  __shared__ float sm_acc[kWaves][GH][D];
+  if (row == 0) {
+#pragma unroll
+    for (int i = 0; i < GH; ++i) {
+#pragma unroll
+      for (int e = 0; e < kEPL; ++e) sm_acc[wave][i][col * kEPL + e] = acc[i][e];
+      if (col == 0) {
+        sm_m[wave][i] = m[i];
+        sm_l[wave][i] = l[i];
+      }
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < GH * D; idx += kThreads) {
+    const int i = idx / D;
+    const int d = idx % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][i]);
+    const float mu = (M == kNegInf) ? 0.f : M;
+    float lsum = 0.f, o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = exp2_hw(sm_m[w][i] - mu);
+      lsum += sm_l[w][i] * f;
+      o += sm_acc[w][i][d] * f;
+    }
+    // lsum >= 1: the row holding the running max contributes 2^0.
+    o = o / lsum;
+    const float lse_v = (M + log2_hw(lsum)) * kLn2;
+    const int64_t r = r0 + i;
+    if (direct) {
+      a.out[r * D + d] = o;
+      if (d == 0 && a.lse) a.lse[r] = lse_v;
+    } else {
+      a.part_out[(split * rows + r) * D + d] = o;
+      if (d == 0) a.part_lse[split * rows + r] = lse_v;
+    }
+  }
+}
+
+template <typename T, int D, int GH>
+hipError_t launch_t(const GqaArgs& a, hipStream_t st) {
+  const dim3 grid(a.num_splits, a.num_kv_heads * (a.group / GH), a.batch);
+  hipLaunchKernelGGL((gqa_decode_kernel<T, D, GH>), grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_gh(const GqaArgs& a, hipStream_t st) {
+  switch (a.heads_per_block) {
+    case 1: return launch_t<T, D, 1>(a, st);
+    case 2: return launch_t<T, D, 2>(a, st);
+    case 3: return launch_t<T, D, 3>(a, st);
+    case 4: return launch_t<T, D, 4>(a, st);
+    case 5: return launch_t<T, D, 5>(a, st);
+    case 6: return launch_t<T, D, 6>(a, st);
+    case 7: return launch_t<T, D, 7>(a, st);
+    case 8: return launch_t<T, D, 8>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gqa_decode(const GqaArgs& a, int dtype, int head_dim, hipStream_t st) {
+  if (dtype == 1) {
+    if (head_dim == 128) return launch_gh<uint16_t, 128>(a, st);
+    if (head_dim == 64) return launch_gh<uint16_t, 64>(a, st);
+  } else if (dtype == 0) {
+    if (head_dim == 128) return launch_gh<float, 128>(a, st);
+    if (head_dim == 64) return launch_gh<float, 64>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace da

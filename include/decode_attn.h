@@ -1,0 +1,225 @@
+/*
+ * decode_attn.h -- C ABI of libdecode_attn.so: single-token decode attention
+ * over a KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * Two operations, both one layer and one new query token per sequence:
+ *
+ *  1. GQA / MQA / MHA decode. g = Hq / Hkv query heads share one cached K/V
+ *     head; query head h reads KV head h / g (integer division), read in place
+ *     with no copy of the cache. Semantics: "Attention variants and KV cache"
+ *     (arganzheng.life), sections 3.1-3.3; kakack.github.io KV-cache page,
+ *     section 4 (UnifiedAttention, with its Hq % Hkv == 0 requirement);
+ *     shippingwang.com chapter 7, section 7.3 (the q_head // g mapping).
+ *
+ *  2. DeepSeek-style MLA decode with matrix absorption. Per head,
+ *     q~ = q_nope W_UK^T (512-d); all heads attend one shared cached row
+ *     [c_kv (512) ; k_rope (64)] with scale 1/sqrt(192); the first 512 columns
+ *     of that row are the value; the 512-d result is multiplied by W_UV.
+ *     arganzheng.life sections 4.2, 4.5 and 4.6; jianzhnie.github.io
+ *     "Multi-head Latent Attention", sections 2 and 4.
+ *
+ *  Plus the split-KV merge (flash-decoding: split the cache along the
+ *  sequence, softmax per split, merge the normalisers; arganzheng.life
+ *  section 5.2).
+ *
+ * Conventions shared by every entry point
+ *  - All pointers to tensors are DEVICE pointers on the current HIP device;
+ *    the caller allocates and owns every buffer, including workspace. The
+ *    library never allocates or frees device memory and keeps no state
+ *    between calls apart from cached device properties.
+ *  - Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the null
+ *    stream). Outputs are valid once that stream has been synchronised.
+ *    Calls are thread-safe. Calls that share a workspace buffer race unless
+ *    they are ordered on one stream.
+ *  - lse is the natural-log log-sum-exp of the scaled scores,
+ *    lse = log(sum_j exp(s_j)); a sequence of length 0 yields out = 0 and
+ *    lse = -inf.
+ *  - Strides are in elements. The innermost (head_dim / row) axis must be
+ *    contiguous; every pointer must be 16-byte aligned and every stride a
+ *    multiple of 16 bytes.
+ *  - Arguments are checked on the host before anything is launched; a bad
+ *    argument returns a non-zero status synchronously and launches nothing.
+ *    Device-resident seq_lens are not read on the host (that would need a
+ *    synchronising copy); the caller guarantees 0 <= seq_lens[b] <= max_seq_len.
+ *    A launch failure returns DA_ERR_HIP. No C++ exception crosses this ABI.
+ *  - The cache holds the current token already: all seq_lens[b] rows are
+ *    attended and no causal mask applies at decode (kakack.github.io
+ *    section 2.2; arganzheng.life section 2.2).
+ */
+#ifndef DECODE_ATTN_H
+#define DECODE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define DA_EXPORT __attribute__((visibility("default")))
+#else
+#define DA_EXPORT
+#endif
+
+typedef enum {
+  DA_OK = 0,
+  DA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, stride or alignment */
+  DA_ERR_UNSUPPORTED = 2,        /* valid but not implemented (e.g. head_dim 96) */
+  DA_ERR_WORKSPACE_TOO_SMALL = 3,
+  DA_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
+} da_status_t;
+
+typedef enum {
+  DA_DTYPE_F32 = 0,
+  DA_DTYPE_BF16 = 1
+} da_dtype_t;
+
+/* ------------------------------------------------------------------------ */
+/* GQA / MQA / MHA decode                                                    */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int32_t batch;           /* B >= 1 */
+  int32_t num_q_heads;     /* Hq >= 1, a multiple of num_kv_heads */
+  int32_t num_kv_heads;    /* Hkv >= 1 */
+  int32_t head_dim;        /* D: 64 or 128 */
+  int32_t max_seq_len;     /* L_max >= 1: rows allocated per sequence */
+  da_dtype_t dtype;        /* element type of q, k_cache and v_cache */
+  float softmax_scale;     /* usually 1/sqrt(head_dim) */
+  int64_t q_stride_b;      /* q[b, h, d] at q + b*q_stride_b + h*q_stride_h + d */
+  int64_t q_stride_h;
+  int64_t kv_stride_b;     /* k[b, t, kh, d] at k + b*kv_stride_b + t*kv_stride_t + kh*kv_stride_h + d */
+  int64_t kv_stride_t;     /* default layout [B, L_max, Hkv, D]: */
+  int64_t kv_stride_h;     /*   kv_stride_b = L_max*Hkv*D, kv_stride_t = Hkv*D, kv_stride_h = D */
+  int32_t num_splits;      /* S >= 1 forces a split count; 0 lets the library choose */
+} da_gqa_params_t;
+
+/* Bytes of workspace da_gqa_decode needs for these parameters (0 when the
+ * planned split count is 1). Returns 0 for invalid parameters as well. */
+DA_EXPORT size_t da_gqa_decode_workspace_size(const da_gqa_params_t* params);
+
+/* Split count da_gqa_decode will use for these parameters (>= 1), or 0 for
+ * invalid parameters. */
+DA_EXPORT int32_t da_gqa_decode_num_splits(const da_gqa_params_t* params);
+
+/*
+ * out[b, h, :] = sum_j p_j v[b, j, h/g, :] with p = softmax_j(scale * q[b,h,:] . k[b, j, h/g, :]),
+ * j over [0, seq_lens[b]).
+ *   q        [B, Hq, D] (strides q_stride_b, q_stride_h), dtype
+ *   k_cache  [B, L_max, Hkv, D] (kv strides), dtype
+ *   v_cache  same shape and strides as k_cache, dtype
+ *   seq_lens [B] int32, device; NULL means every sequence has max_seq_len rows
+ *   out      [B, Hq, D] float32, contiguous
+ *   lse      [B, Hq] float32, contiguous; may be NULL
+ *   workspace  device buffer of at least da_gqa_decode_workspace_size() bytes
+ *              (may be NULL when that size is 0); its contents are scratch.
+ * Rows past seq_lens[b] are never read, so they may hold anything.
+ */
+DA_EXPORT da_status_t da_gqa_decode(const da_gqa_params_t* params,
+                          const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* seq_lens,
+                          float* out, float* lse,
+                          void* workspace, size_t workspace_bytes,
+                          void* hip_stream);
+
+/*
+ * The split pass of da_gqa_decode on its own (flash-decoding: each split of a
+ * sequence is normalised locally; arganzheng.life section 5.2). With
+ * S = da_gqa_decode_num_splits(params), it writes for every split s:
+ *   part_out [S, B, Hq, D] float32: that split's normalised output o_s
+ *   part_lse [S, B, Hq] float32:    that split's lse_s (-inf if it holds no rows)
+ * Feeding them to da_splitkv_combine gives exactly what da_gqa_decode returns.
+ * When S == 1 the partials are already the final out and lse.
+ * Needs no workspace. Other arguments as for da_gqa_decode.
+ */
+DA_EXPORT da_status_t da_gqa_decode_split_pass(const da_gqa_params_t* params,
+                                               const void* q, const void* k_cache,
+                                               const void* v_cache, const int32_t* seq_lens,
+                                               float* part_out, float* part_lse,
+                                               void* hip_stream);
+
+/* ------------------------------------------------------------------------ */
+/* Absorbed MLA decode (one shared latent KV head)                           */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int32_t batch;           /* B >= 1 */
+  int32_t num_heads;       /* n_h: a multiple of 16, at most 128 */
+  int32_t kv_lora_rank;    /* d_c: must be 512 */
+  int32_t qk_rope_dim;     /* d_rope: must be 64 */
+  int32_t qk_nope_dim;     /* d_nope: must be 128 */
+  int32_t v_head_dim;      /* d_v: must be 128 */
+  int32_t max_seq_len;     /* L_max >= 1 */
+  float softmax_scale;     /* 1/sqrt(qk_nope_dim + qk_rope_dim) = 1/sqrt(192) for DeepSeek-V3 */
+  int64_t cache_stride_b;  /* row [b, t] at kv_cache + b*cache_stride_b + t*cache_stride_t */
+  int64_t cache_stride_t;  /* default layout [B, L_max, 576]: 576*L_max and 576 */
+  int32_t num_splits;      /* S >= 1 forces a split count; 0 lets the library choose */
+} da_mla_params_t;
+
+/* Bytes of workspace da_mla_decode_absorbed needs (never 0 for valid
+ * parameters: it holds the absorbed queries and the split partials). */
+DA_EXPORT size_t da_mla_decode_workspace_size(const da_mla_params_t* params);
+
+/* Split count da_mla_decode_absorbed will use (>= 1), or 0 if invalid. */
+DA_EXPORT int32_t da_mla_decode_num_splits(const da_mla_params_t* params);
+
+/*
+ *   q_nope   [B, H, d_nope] bf16, contiguous
+ *   q_rope   [B, H, d_rope] bf16, contiguous (RoPE already applied)
+ *   kv_cache [B, L_max, d_c + d_rope] bf16; row = [c_kv | k_rope], k_rope already rotated
+ *   seq_lens [B] int32, device; NULL means max_seq_len for every sequence
+ *   w_uk     [H, d_c, d_nope] bf16, contiguous: per-head slice, k^C_{j,h} = c_kv_j W_UK[h]
+ *   w_uv     [H, d_c, d_v] bf16, contiguous:    per-head slice, v^C_{j,h} = c_kv_j W_UV[h]
+ *   out      [B, H, d_v] float32, contiguous
+ *   lse      [B, H] float32, contiguous; may be NULL
+ * Numerics: q~ and the softmax weights are rounded to bf16 before the matrix
+ * cores; every accumulation is float32.
+ */
+DA_EXPORT da_status_t da_mla_decode_absorbed(const da_mla_params_t* params,
+                                   const void* q_nope, const void* q_rope,
+                                   const void* kv_cache, const int32_t* seq_lens,
+                                   const void* w_uk, const void* w_uv,
+                                   float* out, float* lse,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* hip_stream);
+
+/* ------------------------------------------------------------------------ */
+/* Split-KV merge                                                            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * lse[r] = log(sum_s exp(partial_lse[s, r])),
+ * out[r, :] = sum_s exp(partial_lse[s, r] - lse[r]) * partial_out[s, r, :]
+ * for every row r = (b, h). A split with partial_lse = -inf is empty: its
+ * partial_out row is never read. All splits empty gives out = 0, lse = -inf.
+ *   partial_out [S, B, H, head_dim] float32, contiguous
+ *   partial_lse [S, B, H] float32, contiguous
+ *   out [B, H, head_dim] float32; lse [B, H] float32 (may be NULL)
+ * head_dim must be a multiple of 4 and at most 1024.
+ */
+DA_EXPORT da_status_t da_splitkv_combine(int32_t num_splits, int32_t batch, int32_t num_heads,
+                               int32_t head_dim,
+                               const float* partial_out, const float* partial_lse,
+                               float* out, float* lse, void* hip_stream);
+
+/* ------------------------------------------------------------------------ */
+/* Miscellany                                                                */
+/* ------------------------------------------------------------------------ */
+
+/* Static, never NULL. */
+DA_EXPORT const char* da_status_string(da_status_t status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+DA_EXPORT int32_t da_version(void);
+
+/* sizeof(da_gqa_params_t) and sizeof(da_mla_params_t) as compiled, so that
+ * bindings can check their struct mirrors. */
+DA_EXPORT size_t da_gqa_params_size(void);
+DA_EXPORT size_t da_mla_params_size(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DECODE_ATTN_H */

@@ -1,0 +1,69 @@
+"""Helpers for the GPU parity tests: host arrays -> device tensors, and the
+comparison bar.
+
+The bar for floating-point outputs (bf16 inputs, fp32 accumulation):
+  * output: per row (b, h), max_d |o - o_ref| / max_d |o_ref| <= 1e-2;
+  * lse:    max |lse - lse_ref| <= 1e-3 (absolute, natural log).
+Rows whose reference is empty (lse_ref = -inf) must come back exactly
+out = 0 and lse = -inf.
+"""
+import sys
+
+import numpy as np
+import torch
+
+OUT_RTOL = 1e-2
+LSE_ATOL = 1e-3
+
+
+def announce(msg: str):
+    """Print (and flush) which case is about to run on the GPU."""
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def bf16_tensor(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.to(device).view(torch.bfloat16)
+
+
+def f32_tensor(x: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+
+
+def gqa_to_device(inp):
+    conv = bf16_tensor if inp.dtype == "bf16" else f32_tensor
+    return (conv(inp.q), conv(inp.k), conv(inp.v),
+            torch.from_numpy(inp.seq_lens.astype(np.int32)).cuda())
+
+
+def mla_to_device(inp):
+    return (bf16_tensor(inp.q_nope), bf16_tensor(inp.q_rope), bf16_tensor(inp.cache),
+            bf16_tensor(inp.w_uk), bf16_tensor(inp.w_uv),
+            torch.from_numpy(inp.seq_lens.astype(np.int32)).cuda())
+
+
+def row_rel_err(out: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    err = np.abs(out.astype(np.float64) - ref).max(axis=-1)
+    scale = np.abs(ref).max(axis=-1)
+    return err / np.maximum(scale, 1e-30)
+
+
+def assert_parity(out, lse, ref_out, ref_lse, out_rtol=OUT_RTOL, lse_atol=LSE_ATOL, what=""):
+    """out/lse: numpy (from the GPU); ref_*: float64 oracle results."""
+    out = np.asarray(out, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    empty = np.isneginf(ref_lse)
+    if empty.any():
+        assert np.all(np.isneginf(lse[empty])), f"{what}: empty rows must give lse=-inf"
+        assert np.all(out[empty] == 0), f"{what}: empty rows must give out=0"
+    full = ~empty
+    if not full.any():
+        return 0.0, 0.0
+    assert np.isfinite(out[full]).all(), f"{what}: non-finite outputs"
+    assert np.isfinite(lse[full]).all(), f"{what}: non-finite lse"
+    rel = row_rel_err(out[full], ref_out[full])
+    lerr = np.abs(lse[full] - ref_lse[full])
+    assert rel.max() <= out_rtol, f"{what}: max row-relative output error {rel.max():.3e} > {out_rtol}"
+    assert lerr.max() <= lse_atol, f"{what}: max lse error {lerr.max():.3e} > {lse_atol}"
+    return float(rel.max()), float(lerr.max())

@@ -1,0 +1,173 @@
+"""The C ABI on the host: the library loads, exports every declared symbol,
+its structs match the binding, planning answers, and bad arguments are
+rejected on the host before anything is launched.
+
+Argument-rejection cases pass fake (never dereferenced) pointers, so they are
+skipped on a machine with a GPU, where the GPU tests cover the same errors
+with real buffers.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import decode_attention_kv_bf16_amd as da
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "decode_attn.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(da.LIB_PATH), reason="library not built")
+cpu_only = pytest.mark.skipif(torch.cuda.is_available(), reason="fake-pointer checks run on CPU only")
+
+
+def declared_symbols():
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"DA_EXPORT\s+[\w\s\*]+?\b(da_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    syms = declared_symbols()
+    for name in ("da_gqa_decode", "da_mla_decode_absorbed", "da_splitkv_combine",
+                 "da_gqa_decode_workspace_size", "da_mla_decode_workspace_size",
+                 "da_status_string"):
+        assert name in syms
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(da.LIB_PATH)
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+    # and the binding knows all of them
+    assert set(declared_symbols()) == set(da._SIGNATURES)
+
+
+@needs_lib
+def test_struct_mirrors_and_version():
+    L = da.lib()
+    assert L.da_gqa_params_size() == ctypes.sizeof(da.GqaParams) == 80
+    assert L.da_mla_params_size() == ctypes.sizeof(da.MlaParams)
+    assert L.da_version() >= 100
+    for s, txt in [(0, b"ok"), (1, b"invalid argument"), (2, b"unsupported configuration"),
+                   (3, b"workspace too small"), (4, b"HIP runtime error"), (99, b"unknown status")]:
+        assert L.da_status_string(s) == txt
+
+
+def gqa(B=32, Hq=32, Hkv=8, D=128, L=4096, dtype=da.DA_DTYPE_BF16, splits=0):
+    p = da.GqaParams()
+    p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim, p.max_seq_len = B, Hq, Hkv, D, L
+    p.dtype = dtype
+    p.softmax_scale = D ** -0.5
+    p.q_stride_b, p.q_stride_h = Hq * D, D
+    p.kv_stride_b, p.kv_stride_t, p.kv_stride_h = L * Hkv * D, Hkv * D, D
+    p.num_splits = splits
+    return p
+
+
+def mla(B=64, H=128, L=4096, splits=0):
+    p = da.MlaParams()
+    p.batch, p.num_heads, p.kv_lora_rank, p.qk_rope_dim = B, H, 512, 64
+    p.qk_nope_dim, p.v_head_dim, p.max_seq_len = 128, 128, L
+    p.softmax_scale = 192 ** -0.5
+    p.cache_stride_b, p.cache_stride_t = L * 576, 576
+    p.num_splits = splits
+    return p
+
+
+@needs_lib
+@cpu_only
+def test_split_planning_without_a_device():
+    # with no device the planner assumes a full MI355X (256 CUs)
+    L = da.lib()
+    n = lambda p: L.da_gqa_decode_num_splits(ctypes.byref(p))
+    ws = lambda p: L.da_gqa_decode_workspace_size(ctypes.byref(p))
+    assert n(gqa()) == 4                                   # Llama-3-8B: 256 (b, kv) pairs x 4
+    assert ws(gqa()) == 4 * 32 * 32 * 128 * 4 + 4 * 32 * 32 * 4
+    assert n(gqa(64, 32, 32, 128, 8192)) == 8              # ragged MHA: no split > 1024 rows
+    assert n(gqa(1, 4, 2, 64, 128, da.DA_DTYPE_F32)) == 1  # tiny: one split, no workspace
+    assert ws(gqa(1, 4, 2, 64, 128, da.DA_DTYPE_F32)) == 0
+    assert n(gqa(splits=7)) == 7
+    assert n(gqa(L=5, splits=9)) == 5                      # never more splits than rows
+    m = lambda p: L.da_mla_decode_num_splits(ctypes.byref(p))
+    assert m(mla()) == 4                                   # DeepSeek-V3 B=64: 256 workgroups
+    assert m(mla(4, 128, 32768)) == 64
+    assert L.da_mla_decode_workspace_size(ctypes.byref(mla())) >= 64 * 128 * 576 * 2
+
+
+FAKE = ctypes.c_void_p(0x10000)       # 16-byte aligned, never dereferenced
+FAKE_MIS = ctypes.c_void_p(0x10002)   # misaligned
+
+
+def call_gqa(p, q=FAKE, k=FAKE, v=FAKE, sl=None, out=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 40):
+    return da.lib().da_gqa_decode(ctypes.byref(p) if p is not None else None, q, k, v, sl, out,
+                                  lse, ws, ws_bytes, None)
+
+
+@needs_lib
+@cpu_only
+@pytest.mark.parametrize("mutate,code", [
+    (lambda p: setattr(p, "num_kv_heads", 3), 1),       # 32 % 3 != 0: the pages' assert
+    (lambda p: setattr(p, "head_dim", 96), 2),
+    (lambda p: setattr(p, "head_dim", 0), 1),
+    (lambda p: setattr(p, "batch", 0), 1),
+    (lambda p: setattr(p, "max_seq_len", 0), 1),
+    (lambda p: setattr(p, "num_splits", -1), 1),
+    (lambda p: setattr(p, "dtype", 7), 1),
+    (lambda p: setattr(p, "kv_stride_t", 1028), 1),      # not a multiple of 16 bytes
+    (lambda p: setattr(p, "q_stride_h", -128), 1),
+    (lambda p: setattr(p, "softmax_scale", float("nan")), 1),
+])
+def test_gqa_rejects_bad_parameters(mutate, code):
+    p = gqa()
+    mutate(p)
+    assert call_gqa(p) == code
+    assert da.lib().da_gqa_decode_workspace_size(ctypes.byref(p)) == 0
+
+
+@needs_lib
+@cpu_only
+def test_gqa_rejects_bad_pointers_and_workspace():
+    p = gqa()
+    assert call_gqa(None) == 1
+    assert call_gqa(p, q=None) == 1
+    assert call_gqa(p, out=None) == 1
+    assert call_gqa(p, k=FAKE_MIS) == 1
+    assert call_gqa(p, sl=ctypes.c_void_p(0x10001)) == 1
+    assert call_gqa(p, ws=None) == 3
+    assert call_gqa(p, ws_bytes=100) == 3
+    assert call_gqa(p, ws=FAKE_MIS) == 1
+
+
+@needs_lib
+@cpu_only
+def test_mla_and_combine_reject_bad_parameters():
+    L = da.lib()
+
+    def call_mla(p, ws_bytes=1 << 40, ptr=FAKE):
+        return L.da_mla_decode_absorbed(ctypes.byref(p), ptr, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                                        None, FAKE, ws_bytes, None)
+    for field, val, code in [("kv_lora_rank", 256, 2), ("qk_rope_dim", 32, 2), ("num_heads", 24, 2),
+                             ("num_heads", 256, 2), ("batch", 0, 1), ("cache_stride_t", 512, 1),
+                             ("max_seq_len", -1, 1)]:
+        p = mla()
+        setattr(p, field, val)
+        assert call_mla(p) == code, field
+    assert call_mla(mla(), ws_bytes=10) == 3
+    assert call_mla(mla(), ptr=FAKE_MIS) == 1
+    assert call_mla(mla(), ptr=None) == 1
+    comb = L.da_splitkv_combine
+    assert comb(0, 1, 1, 128, FAKE, FAKE, FAKE, None, None) == 1
+    assert comb(2, 1, 1, 126, FAKE, FAKE, FAKE, None, None) == 1
+    assert comb(2, 1, 1, 2048, FAKE, FAKE, FAKE, None, None) == 1
+    assert comb(2, 1, 1, 128, None, FAKE, FAKE, None, None) == 1
+    assert comb(2, 1, 1, 128, FAKE_MIS, FAKE, FAKE, None, None) == 1
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(da, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(da, "_lib", None)
+    with pytest.raises(da.LibraryMissing):
+        da.lib()
