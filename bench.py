@@ -1,0 +1,335 @@
+#!/usr/bin/env python3
+"""Benchmark of single-token decode attention on one MI355X.
+
+One step is one pass of the whole hot path on synthetic inputs:
+  * GQA decode, Llama-3-8B shape: batch 32, 32 query / 8 KV heads, d_head 128,
+    every sequence at 4096 cached rows, bf16 (split pass + log-sum-exp merge);
+  * absorbed-MLA decode, DeepSeek-V3 shape: batch 64, 128 heads, latent cache
+    [64, 4096, 576] bf16, W_UK / W_UV [128, 512, 128] (query absorption,
+    split-KV latent attention, merge + W_UV projection).
+Inputs are resident in HBM before timing starts. Each step reads the next of
+several copies of the caches, so that no step finds the previous step's cache
+in the 256 MB last-level (Infinity) cache.
+
+Prints ONE JSON line on stdout. `value` is algorithmic bytes per step (cache
+rows once, queries, weights, outputs) over the step time, in GB/s; the
+`roofline` object covers the dominant kernel, timed with HIP events recorded on
+the stream its launches go to; `cpu_baseline` times the fp64 CPU oracle on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn KV GB/s & TFLOP/s per layer-step; % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+MALL_GUARD_BYTES = 1 << 30     # rotate through >= 1 GiB of distinct cache copies
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# algorithmic traffic and work (what the method must move / compute)
+# ----------------------------------------------------------------------------
+
+def gqa_alg(B, Hq, Hkv, D, total_rows, elem=2):
+    """Bytes: every cached K and V row once, q, fp32 out + lse. FLOPs: 2 per
+    dimension for q.k and for p.v, per query head and cached row."""
+    cache = total_rows * 2 * Hkv * D * elem
+    q = B * Hq * D * elem
+    out = B * Hq * (D + 1) * 4
+    return dict(cache=cache, q=q, out=out, total=cache + q + out, flops=4 * Hq * D * total_rows)
+
+
+def mla_alg(B, H, total_rows, d_c=512, d_r=64, d_n=128, d_v=128):
+    """Bytes: every cached latent row (576 bf16) once, W_UK and W_UV once,
+    q_nope/q_rope, fp32 out + lse. FLOPs: per cached row 2*H*(576 + 512), plus
+    the two per-head projections 2*B*H*d_c*(d_n + d_v)."""
+    cache = total_rows * (d_c + d_r) * 2
+    weights = 2 * H * d_c * 128 * 2
+    q = B * H * (d_n + d_r) * 2
+    out = B * H * (d_v + 1) * 4
+    attn_flops = H * 2 * ((d_c + d_r) + d_c) * total_rows
+    proj_flops = 2 * B * H * d_c * (d_n + d_v)
+    return dict(cache=cache, weights=weights, q=q, out=out, total=cache + weights + q + out,
+                flops=attn_flops + proj_flops, attn_flops=attn_flops)
+
+
+# ----------------------------------------------------------------------------
+# GPU part
+# ----------------------------------------------------------------------------
+
+def to_dev_bf16(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def setup_gqa(cfg):
+    import torch
+    import workloads as W
+    import decode_attention_kv_bf16_amd as da
+    inp = W.make_gqa_config(cfg)
+    q = to_dev_bf16(inp.q)
+    k0, v0 = to_dev_bf16(inp.k), to_dev_bf16(inp.v)
+    sl = torch.from_numpy(inp.seq_lens).cuda()
+    fp = k0.numel() * 2 * 2
+    n_copies = max(1, math.ceil(MALL_GUARD_BYTES / fp)) if fp < MALL_GUARD_BYTES else 1
+    copies = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(n_copies - 1)]
+    S = da.gqa_num_splits(q, k0)
+    B, Hq, D = q.shape
+    part_out = torch.empty((S, B, Hq, D), dtype=torch.float32, device="cuda")
+    part_lse = torch.empty((S, B, Hq), dtype=torch.float32, device="cuda")
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    calls = []
+    for kk, vv in copies:
+        def split_pass(kk=kk, vv=vv):
+            da.gqa_decode_split_pass(q, kk, vv, sl, inp.scale, part_out=part_out, part_lse=part_lse)
+
+        def combine():
+            if S > 1:
+                da.splitkv_combine(part_out, part_lse, out=out, lse=lse)
+        calls.append([("gqa_split_pass", split_pass), ("gqa_combine", combine)])
+    alg = gqa_alg(B, Hq, k0.shape[2], D, int(inp.seq_lens.sum()))
+    info = dict(batch=B, q_heads=Hq, kv_heads=int(k0.shape[2]), head_dim=D,
+                seq_len=int(inp.seq_lens.max()), splits=S, cache_copies=len(copies))
+    return calls, alg, info, inp
+
+
+def setup_mla(cfg):
+    import torch
+    import workloads as W
+    import decode_attention_kv_bf16_amd as da
+    inp = W.make_mla_config(cfg)
+    qn, qr = to_dev_bf16(inp.q_nope), to_dev_bf16(inp.q_rope)
+    wuk, wuv = to_dev_bf16(inp.w_uk), to_dev_bf16(inp.w_uv)
+    c0 = to_dev_bf16(inp.cache)
+    sl = torch.from_numpy(inp.seq_lens).cuda()
+    fp = c0.numel() * 2
+    n_copies = max(1, math.ceil(MALL_GUARD_BYTES / fp)) if fp < MALL_GUARD_BYTES else 1
+    caches = [c0] + [c0.clone() for _ in range(n_copies - 1)]
+    calls = []
+    S = None
+    for c in caches:
+        absorb, attend, merge, _, _, bufs = da.mla_stages(qn, qr, c, wuk, wuv, sl, inp.scale)
+        S = bufs["part_out"].shape[0]
+        calls.append([("mla_absorb", absorb), ("mla_attend", attend), ("mla_merge_project", merge)])
+    B, H, _ = qn.shape
+    alg = mla_alg(B, H, int(inp.seq_lens.sum()))
+    info = dict(batch=B, heads=H, seq_len=int(inp.seq_lens.max()),
+                total_rows=int(inp.seq_lens.sum()), splits=S, cache_copies=len(caches))
+    return calls, alg, info, inp
+
+
+def kernel_source_hash(name):
+    """sha256 of the HIP source that holds a kernel (to tie profiles to code)."""
+    src = {"gqa_split_pass": "gqa_decode.hip", "mla_attend": "mla_decode.hip"}.get(name)
+    if src is None:
+        return None
+    with open(os.path.join(ROOT, "decode_attention_kv_bf16_amd", "csrc", src), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(name, launches_alg_bytes):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; otherwise None."""
+    path = os.path.join(PROFILE_DIR, "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(name)
+    if not rec or rec.get("source_sha256") != kernel_source_hash(name):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def run_gpu(args):
+    import torch
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    import decode_attention_kv_bf16_amd as da
+    da.lib()
+    plans = []
+    if args.workload in ("step", "gqa"):
+        plans.append(("gqa", setup_gqa(2)))
+    if args.workload in ("step", "mla"):
+        plans.append(("mla", setup_mla(3)))
+    if args.workload == "mla-long":
+        plans.append(("mla", setup_mla(4)))
+    if args.workload == "gqa-ragged":
+        plans.append(("gqa", setup_gqa(5)))
+    n_rot = max(len(p[1][0]) for p in plans)
+
+    def step_calls(i):
+        seq = []
+        for _, (calls, _, _, _) in plans:
+            seq.extend(calls[i % len(calls)])
+        return seq
+
+    names = [n for n, _ in step_calls(0)]
+    log(f"kernels per step: {names}; rotating {n_rot} input copies")
+    for i in range(args.warmup):
+        for _, fn in step_calls(i):
+            fn()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, events between launches on the launch stream
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        e = ev[i]
+        e[0].record(stream)
+        for j, (_, fn) in enumerate(step_calls(args.warmup + i)):
+            fn()
+            e[j + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    per_kernel = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+                  for j, n in enumerate(names)}
+    ev_step_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][-1]) for i in range(args.steps)]))
+
+    total_bytes = sum(p[1][1]["total"] for p in plans)
+    total_flops = sum(p[1][1]["flops"] for p in plans)
+    value = total_bytes / (ms_per_step * 1e-3) / 1e9
+    tflops = total_flops / (ms_per_step * 1e-3) / 1e12
+
+    # dominant kernel and its roofline
+    dom = max(per_kernel, key=per_kernel.get)
+    kind, (calls, alg, info, _) = next(p for p in plans
+                                       if any(dom == n for n, _ in p[1][0][0]))
+    if dom == "gqa_split_pass":
+        dom_bytes = alg["cache"] + alg["q"]
+    elif dom == "mla_attend":
+        dom_bytes = alg["cache"]
+    else:
+        dom_bytes = alg["total"]
+    dom_ms = per_kernel[dom]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(dom, dom_bytes),
+                "alg_bytes_per_launch": int(dom_bytes), "avg_launch_us": round(dom_ms * 1e3, 2)}
+
+    paths = {}
+    for kind, (calls, alg, info, _) in plans:
+        ks = [n for n, _ in calls[0]]
+        t_ms = sum(per_kernel[n] for n in ks)
+        entry = dict(info)
+        entry.update(kernels_us={n: round(per_kernel[n] * 1e3, 2) for n in ks},
+                     time_us=round(t_ms * 1e3, 2), alg_bytes=int(alg["total"]),
+                     alg_gbs=round(alg["total"] / (t_ms * 1e-3) / 1e9, 1),
+                     cache_gbs=round(alg["cache"] / (t_ms * 1e-3) / 1e9, 1),
+                     tflops=round(alg["flops"] / (t_ms * 1e-3) / 1e12, 2),
+                     hbm_frac=round(alg["total"] / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+        if kind == "mla":
+            entry["mfma_frac"] = round(alg["flops"] / (t_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+        paths[kind] = entry
+
+    prop = torch.cuda.get_device_properties(0)
+    res = dict(metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=args.steps,
+               warmup=args.warmup, ms_per_step=round(ms_per_step, 4), higher_is_better=True,
+               scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
+               config=dict(workload=workload_name(args.workload), parallelism="single-gpu"),
+               tflops=round(tflops, 2), event_ms_per_step=round(ev_step_ms, 4),
+               roofline=roofline, paths=paths,
+               device=dict(name=prop.name, cus=prop.multi_processor_count,
+                           arch=getattr(prop, "gcnArchName", "")))
+    return res, plans
+
+
+def workload_name(w):
+    return {"step": "llama3-8b-gqa-b32-l4096 + deepseek-v3-mla-b64-l4096",
+            "gqa": "llama3-8b-gqa-b32-l4096", "mla": "deepseek-v3-mla-b64-l4096",
+            "mla-long": "deepseek-v3-mla-longctx-b4-l16k-32k",
+            "gqa-ragged": "llama2-7b-mha-ragged-b64-l1-8192"}[w]
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on a bounded sample of the same workload
+# ----------------------------------------------------------------------------
+
+def cpu_baseline(plans, budget_s):
+    from oracle.attention import gqa_decode_ref, mla_absorbed_ref
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    done_bytes, spent, samples = 0, 0.0, []
+    per_kind_budget = budget_s / max(1, len(plans))
+    for kind, (calls, alg, info, inp) in plans:
+        t_kind, n = 0.0, 0
+        B = len(inp.seq_lens)
+        while t_kind < per_kind_budget and n < B:
+            b = n
+            if kind == "gqa":
+                f = (lambda a: W.bf16_to_f32(a).astype(np.float64))
+                L = int(inp.seq_lens[b])
+                args = (f(inp.q[b:b + 1]), f(inp.k[b:b + 1, :L]), f(inp.v[b:b + 1, :L]),
+                        inp.seq_lens[b:b + 1], inp.scale)
+                t = time.perf_counter()
+                gqa_decode_ref(*args)
+                dt = time.perf_counter() - t
+                a1 = gqa_alg(1, inp.q.shape[1], inp.k.shape[2], inp.q.shape[2], L)
+            else:
+                f = (lambda a: W.bf16_to_f32(a).astype(np.float64))
+                L = int(inp.seq_lens[b])
+                args = (f(inp.q_nope[b:b + 1]), f(inp.q_rope[b:b + 1]), f(inp.cache[b:b + 1, :L]),
+                        inp.seq_lens[b:b + 1], f(inp.w_uk), f(inp.w_uv), inp.scale)
+                t = time.perf_counter()
+                mla_absorbed_ref(*args)
+                dt = time.perf_counter() - t
+                a1 = mla_alg(1, inp.q_nope.shape[1], L)
+            t_kind += dt
+            done_bytes += a1["total"]
+            n += 1
+        spent += t_kind
+        samples.append(f"{kind}: {n} of {B} sequences")
+    return dict(value=round(done_bytes / spent / 1e9, 4), unit="GB/s", cores=int(threads),
+                kind="oracle", sample="; ".join(samples) + f"; {spent:.1f} s of oracle time",
+                seconds=round(spent, 2))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="step",
+                    choices=["step", "gqa", "mla", "mla-long", "gqa-ragged"])
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle time for the CPU baseline (0 disables)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(this library has no multi-GPU path).", file=sys.stderr)
+        raise SystemExit(2)
+    res, plans = run_gpu(args)
+    if args.cpu_budget > 0:
+        res["cpu_baseline"] = cpu_baseline(plans, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -74,6 +74,11 @@ _SIGNATURES = {
     "da_mla_decode_num_splits": (ctypes.c_int32, [ctypes.POINTER(MlaParams)]),
     "da_mla_decode_absorbed": (ctypes.c_int, [ctypes.POINTER(MlaParams), _vp, _vp, _vp, _vp, _vp,
                                               _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "da_mla_absorb_query": (ctypes.c_int, [ctypes.POINTER(MlaParams), _vp, _vp, _vp, _vp, _vp]),
+    "da_mla_attend_split_pass": (ctypes.c_int, [ctypes.POINTER(MlaParams), _vp, _vp, _vp, _vp,
+                                                _vp, _vp]),
+    "da_mla_merge_project": (ctypes.c_int, [ctypes.POINTER(MlaParams), _vp, _vp, _vp, _vp, _vp,
+                                            _vp]),
     "da_splitkv_combine": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]),
     "da_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -302,6 +307,41 @@ def mla_decode_absorbed(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_cache: to
                                   _ptr(ws), ws_bytes, _stream_handle())
     _check(st, "da_mla_decode_absorbed")
     return out, lse
+
+
+def mla_stages(q_nope, q_rope, kv_cache, w_uk, w_uv, seq_lens=None, softmax_scale=None,
+               num_splits: int = 0):
+    """The three stages of mla_decode_absorbed as separate callables sharing
+    buffers: returns (absorb, attend, merge, out, lse, buffers). Calling
+    absorb(); attend(); merge() in order on one stream fills out and lse exactly
+    as mla_decode_absorbed does."""
+    p = mla_params(q_nope, kv_cache, w_uv, q_rope, softmax_scale, num_splits)
+    L = lib()
+    S = int(L.da_mla_decode_num_splits(ctypes.byref(p)))
+    B, H, _ = q_nope.shape
+    d_c = kv_cache.shape[2] - q_rope.shape[2]
+    dev = q_nope.device
+    q_hat = torch.empty((B, H, kv_cache.shape[2]), dtype=torch.bfloat16, device=dev)
+    part_out = torch.empty((S, B, H, d_c), dtype=torch.bfloat16, device=dev)
+    part_lse = torch.empty((S, B, H), dtype=torch.float32, device=dev)
+    out = torch.empty((B, H, w_uv.shape[2]), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+
+    def absorb():
+        _check(L.da_mla_absorb_query(ctypes.byref(p), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk),
+                                     _ptr(q_hat), _stream_handle()), "da_mla_absorb_query")
+
+    def attend():
+        _check(L.da_mla_attend_split_pass(ctypes.byref(p), _ptr(q_hat), _ptr(kv_cache),
+                                          _ptr(seq_lens), _ptr(part_out), _ptr(part_lse),
+                                          _stream_handle()), "da_mla_attend_split_pass")
+
+    def merge():
+        _check(L.da_mla_merge_project(ctypes.byref(p), _ptr(part_out), _ptr(part_lse), _ptr(w_uv),
+                                      _ptr(out), _ptr(lse), _stream_handle()),
+               "da_mla_merge_project")
+
+    return absorb, attend, merge, out, lse, dict(q_hat=q_hat, part_out=part_out, part_lse=part_lse)
 
 
 def mla_num_splits(q_nope, q_rope, kv_cache, w_uv, num_splits: int = 0) -> int:

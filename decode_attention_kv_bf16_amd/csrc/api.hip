@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <initializer_list>
 
 #include "da_internal.h"
 #include "decode_attn.h"
@@ -147,7 +148,7 @@ MlaPlan plan_mla(const da_mla_params_t* p) {
   pl.splits = (int)ceil_div(p->max_seq_len, pl.chunk);
   const size_t rows = (size_t)p->batch * p->num_heads;
   pl.q_hat_bytes = round_up(rows * (kMlaDc + kMlaRope) * 2, 256);
-  pl.part_out_bytes = round_up((size_t)pl.splits * rows * kMlaDc * sizeof(float), 256);
+  pl.part_out_bytes = round_up((size_t)pl.splits * rows * kMlaDc * 2, 256);  // bf16
   pl.part_lse_bytes = round_up((size_t)pl.splits * rows * sizeof(float), 256);
   pl.workspace = pl.q_hat_bytes + pl.part_out_bytes + pl.part_lse_bytes;
   return pl;
@@ -168,6 +169,28 @@ da_status_t check_gqa_buffers(const void* q, const void* k_cache, const void* v_
       (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
     return DA_ERR_INVALID_ARGUMENT;
   return DA_OK;
+}
+
+inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Every pointer non-null and 16-byte aligned.
+da_status_t check_ptrs16(std::initializer_list<const void*> ptrs) {
+  for (const void* q : ptrs)
+    if (!q || !aligned16(q)) return DA_ERR_INVALID_ARGUMENT;
+  return DA_OK;
+}
+
+da::MlaArgs mla_args(const da_mla_params_t* p, const MlaPlan& pl) {
+  da::MlaArgs a{};
+  a.cache_sb = p->cache_stride_b;
+  a.cache_st = p->cache_stride_t;
+  a.batch = p->batch;
+  a.num_heads = p->num_heads;
+  a.max_seq_len = p->max_seq_len;
+  a.num_splits = pl.splits;
+  a.chunk = pl.chunk;
+  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  return a;
 }
 
 da::GqaArgs gqa_args(const da_gqa_params_t* p, const GqaPlan& pl, const void* q,
@@ -275,20 +298,16 @@ da_status_t da_mla_decode_absorbed(const da_mla_params_t* p, const void* q_nope,
                                    const int32_t* seq_lens, const void* w_uk, const void* w_uv,
                                    float* out, float* lse, void* workspace,
                                    size_t workspace_bytes, void* hip_stream) {
-  const da_status_t st = check_mla_params(p);
+  da_status_t st = check_mla_params(p);
   if (st != DA_OK) return st;
-  if (!q_nope || !q_rope || !kv_cache || !w_uk || !w_uv || !out) return DA_ERR_INVALID_ARGUMENT;
-  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(kv_cache) || !aligned16(w_uk) ||
-      !aligned16(w_uv) || !aligned16(out))
-    return DA_ERR_INVALID_ARGUMENT;
-  if ((seq_lens && (reinterpret_cast<uintptr_t>(seq_lens) & 3u)) ||
-      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
-    return DA_ERR_INVALID_ARGUMENT;
+  st = check_ptrs16({q_nope, q_rope, kv_cache, w_uk, w_uv, out});
+  if (st != DA_OK) return st;
+  if (!aligned4(seq_lens) || !aligned4(lse)) return DA_ERR_INVALID_ARGUMENT;
   const MlaPlan pl = plan_mla(p);
   if (!workspace || workspace_bytes < pl.workspace) return DA_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned16(workspace)) return DA_ERR_INVALID_ARGUMENT;
   char* ws = static_cast<char*>(workspace);
-  da::MlaArgs a{};
+  da::MlaArgs a = mla_args(p, pl);
   a.q_nope = static_cast<const uint16_t*>(q_nope);
   a.q_rope = static_cast<const uint16_t*>(q_rope);
   a.cache = static_cast<const uint16_t*>(kv_cache);
@@ -298,19 +317,57 @@ da_status_t da_mla_decode_absorbed(const da_mla_params_t* p, const void* q_nope,
   a.out = out;
   a.lse = lse;
   a.q_hat = reinterpret_cast<uint16_t*>(ws);
-  a.part_out = reinterpret_cast<float*>(ws + pl.q_hat_bytes);
+  a.part_out = reinterpret_cast<uint16_t*>(ws + pl.q_hat_bytes);
   a.part_lse = reinterpret_cast<float*>(ws + pl.q_hat_bytes + pl.part_out_bytes);
-  a.cache_sb = p->cache_stride_b;
-  a.cache_st = p->cache_stride_t;
-  a.batch = p->batch;
-  a.num_heads = p->num_heads;
-  a.max_seq_len = p->max_seq_len;
-  a.num_splits = pl.splits;
-  a.chunk = pl.chunk;
-  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
-  const hipError_t e = da::launch_mla_decode(a, static_cast<hipStream_t>(hip_stream));
-  if (e == hipErrorNotSupported) return DA_ERR_UNSUPPORTED;
-  return from_hip(e);
+  return from_hip(da::launch_mla_decode(a, static_cast<hipStream_t>(hip_stream)));
+}
+
+da_status_t da_mla_absorb_query(const da_mla_params_t* p, const void* q_nope, const void* q_rope,
+                                const void* w_uk, void* q_hat, void* hip_stream) {
+  da_status_t st = check_mla_params(p);
+  if (st != DA_OK) return st;
+  st = check_ptrs16({q_nope, q_rope, w_uk, q_hat});
+  if (st != DA_OK) return st;
+  da::MlaArgs a = mla_args(p, plan_mla(p));
+  a.q_nope = static_cast<const uint16_t*>(q_nope);
+  a.q_rope = static_cast<const uint16_t*>(q_rope);
+  a.w_uk = static_cast<const uint16_t*>(w_uk);
+  a.q_hat = static_cast<uint16_t*>(q_hat);
+  return from_hip(da::launch_mla_absorb(a, static_cast<hipStream_t>(hip_stream)));
+}
+
+da_status_t da_mla_attend_split_pass(const da_mla_params_t* p, const void* q_hat,
+                                     const void* kv_cache, const int32_t* seq_lens,
+                                     void* part_out, float* part_lse, void* hip_stream) {
+  da_status_t st = check_mla_params(p);
+  if (st != DA_OK) return st;
+  st = check_ptrs16({q_hat, kv_cache, part_out, part_lse});
+  if (st != DA_OK) return st;
+  if (!aligned4(seq_lens)) return DA_ERR_INVALID_ARGUMENT;
+  da::MlaArgs a = mla_args(p, plan_mla(p));
+  a.q_hat = static_cast<uint16_t*>(const_cast<void*>(q_hat));
+  a.cache = static_cast<const uint16_t*>(kv_cache);
+  a.seq_lens = seq_lens;
+  a.part_out = static_cast<uint16_t*>(part_out);
+  a.part_lse = part_lse;
+  return from_hip(da::launch_mla_attend(a, static_cast<hipStream_t>(hip_stream)));
+}
+
+da_status_t da_mla_merge_project(const da_mla_params_t* p, const void* part_out,
+                                 const float* part_lse, const void* w_uv, float* out, float* lse,
+                                 void* hip_stream) {
+  da_status_t st = check_mla_params(p);
+  if (st != DA_OK) return st;
+  st = check_ptrs16({part_out, w_uv, out});
+  if (st != DA_OK) return st;
+  if (!part_lse || !aligned4(part_lse) || !aligned4(lse)) return DA_ERR_INVALID_ARGUMENT;
+  da::MlaArgs a = mla_args(p, plan_mla(p));
+  a.part_out = static_cast<uint16_t*>(const_cast<void*>(part_out));
+  a.part_lse = const_cast<float*>(part_lse);
+  a.w_uv = static_cast<const uint16_t*>(w_uv);
+  a.out = out;
+  a.lse = lse;
+  return from_hip(da::launch_mla_merge_project(a, static_cast<hipStream_t>(hip_stream)));
 }
 
 da_status_t da_splitkv_combine(int32_t num_splits, int32_t batch, int32_t num_heads,

@@ -57,8 +57,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two floats -> packed bf16 pair (low half = lo) with the hardware
+// round-to-nearest-even conversion (v_cvt_pk_bf16_f32).
+typedef float da_f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 da_bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(da_f32x2_t{lo, hi}, da_bf16x2_t));
 }
 
 // Merge two online-softmax states (m, l, acc) kept in the base-2 domain:

@@ -45,14 +45,17 @@ struct MlaArgs {
   const uint16_t* w_uv;      // [H, 512, 128]
   float* out;                // [B, H, 128]
   float* lse;                // [B, H] or null
-  uint16_t* q_hat;           // workspace [B, H, 576] bf16: [q~ | q_rope]
-  float* part_out;           // workspace [S, B, H, 512]
-  float* part_lse;           // workspace [S, B, H]
+  uint16_t* q_hat;           // [B, H, 576] bf16: [q~ | q_rope]
+  uint16_t* part_out;        // [S, B, H, 512] bf16: each split's normalised o~_s
+  float* part_lse;           // [S, B, H]
   int64_t cache_sb, cache_st;
   int32_t batch, num_heads, max_seq_len, num_splits, chunk;
   float scale_log2;
 };
 
-hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream);
+hipError_t launch_mla_absorb(const MlaArgs& a, hipStream_t stream);
+hipError_t launch_mla_attend(const MlaArgs& a, hipStream_t stream);
+hipError_t launch_mla_merge_project(const MlaArgs& a, hipStream_t stream);
+hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream);  // all three
 
 }  // namespace da

@@ -1,6 +1,526 @@
-// Absorbed-MLA decode (placeholder until the kernels land).
+// DeepSeek-style absorbed-MLA decode for gfx950 (CDNA4): three launches.
+//
+// The method ("Attention variants and KV cache", arganzheng.life, sections
+// 4.5-4.6; jianzhnie.github.io "Multi-head Latent Attention", section 4):
+//   q~_h = q_nope_h W_UK,h^T (512), q^_h = [q~_h ; q_rope_h] (576),
+//   s_j  = q^_h . row_j / sqrt(192) with row_j = [c_kv_j ; k_rope_j] shared by all heads,
+//   o~_h = sum_j softmax(s)_j c_kv_j (the value is the first 512 columns of the same row),
+//   o_h  = o~_h W_UV,h.
+// After absorption every head attends the same 576-wide row, so decode is one
+// dense contraction per sequence: S^T = C Q^^T ([T x 576] x [576 x H]) and
+// O^T += C[:, :512]^T P^T, which runs on the matrix cores.
+//
+// Kernels
+//  1. mla_absorb_kernel   q^ = [q_nope W_UK^T | q_rope] (bf16) for all (b, h).
+//  2. mla_attend_kernel   one workgroup per (split, sequence); for 128 heads,
+//     4 waves of 32 heads each (one wave per SIMD, accumulators in AGPRs).
+//     32-row latent tiles are copied HBM -> LDS by the load-to-LDS path
+//     (global_load_lds_dwordx4, no register staging), double-buffered; each
+//     tile is read from LDS as the A operand of S^T (row-major 16-byte reads)
+//     and, transposed by ds_read_b64_tr_b16, as the A operand of O^T. Each
+//     head's softmax reference max is fixed by its first tile, so the
+//     accumulators are never rescaled in the loop (see kRefHeadroom). Each
+//     split writes its normalised o~_s (bf16) and lse_s.
+//  3. mla_merge_project_kernel  merges the splits by log-sum-exp and multiplies
+//     by W_UV,h on the matrix cores (W_UV,h staged in LDS, read transposed).
+#include "da_device.h"
 #include "da_internal.h"
 
 namespace da {
-hipError_t launch_mla_decode(const MlaArgs&, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+#define LDS __attribute__((address_space(3)))
+
+constexpr int kDc = 512;            // latent (value) width
+constexpr int kRowE = 576;          // cached row: c_kv (512) | k_rope (64)
+constexpr int kRowB = kRowE * 2;    // 1152 bytes
+constexpr int kChunks = kRowB / 16; // 72 16-byte chunks per row
+constexpr int kTok = 32;            // rows per tile
+constexpr int kTileB = kTok * kRowB;          // 36864 bytes, a multiple of 1 KiB
+constexpr int kTileDma = kTileB / 1024;       // wave-wide 1 KiB copies per tile (36)
+// A head's reference max is fixed by its first tile; later scores may exceed
+// it by up to 2^64 (fp32 and bf16 share an exponent range up to 2^127, so the
+// weights and sums stay finite). A tile that exceeds it by more restarts the
+// split with a raised reference instead of rescaling the accumulators, which
+// live in AGPRs where arithmetic cannot touch them.
+constexpr float kRefHeadroom = 64.0f;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read: within each 16-lane group, lane j names an 8-byte
+// piece (row j/4, piece j%4) of a 4x16 bf16 block; lane i gets column i.
+__device__ __forceinline__ i16x4_t lds_read_tr(const LDS uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4_t*)p);
+}
+
+__device__ __forceinline__ bf16x8_t join_tr(i16x4_t lo, i16x4_t hi) {
+  i16x4_t v[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ void load_to_lds16(const void* src, LDS uint8_t* dst_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (LDS void*)dst_wave_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  return pack_bf16x2(lo, hi);
+}
+
+// XOR swizzle of the 16-byte chunk index inside a tile row. Chosen so that
+// (a) 16 consecutive rows read at one logical chunk (S^T operand) and
+// (b) 4 consecutive rows read at two adjacent chunks (transposed O^T operand)
+// both touch distinct LDS banks. Only the low 3 bits of the chunk change, so a
+// chunk stays inside its row (72 chunks = 9 groups of 8).
+__device__ __forceinline__ int row_swizzle(int row) {
+  return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+// ---------------------------------------------------------------------------
+// 1. query absorption
+// ---------------------------------------------------------------------------
+// grid (8 slices of 64 latent columns, H); one wave. Computes the transpose
+// q~^T[c, b] = sum_e W_UK[h, c, e] q_nope[b, h, e] so that each lane ends up
+// with 4 consecutive latent columns of one batch row (one 8-byte store).
+// Both operands are read in their stored layout (e contiguous).
+constexpr int kAbsorbBatch = 64;   // batch rows per pass (4 blocks of 16)
+
+__global__ __launch_bounds__(64) void mla_absorb_kernel(MlaArgs a) {
+  const int slice = blockIdx.x;
+  const int h = blockIdx.y;
+  const int H = a.num_heads;
+  const int B = a.batch;
+  const int lane = threadIdx.x;
+  const int q4 = lane >> 4, l16 = lane & 15;
+  const int c0 = 64 * slice;
+
+  bf16x8_t wa[4][4];   // A: W_UK[h, c0 + 16cb + l16, 32ks + 8q4 .. +8]
+  const uint16_t* wp = a.w_uk + ((int64_t)h * kDc + c0 + l16) * 128 + 8 * q4;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      wa[cb][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(wp + cb * 16 * 128 + 32 * ks));
+
+  for (int b0 = 0; b0 < B; b0 += kAbsorbBatch) {
+    bf16x8_t qb[4][4];  // B: q_nope[b0 + 16bb + l16, h, 32ks + 8q4 .. +8]
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+      const int b = b0 + 16 * bb + l16;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (b < B) v = *reinterpret_cast<const uint4*>(a.q_nope + ((int64_t)b * H + h) * 128 + 32 * ks + 8 * q4);
+        qb[bb][ks] = as_bf16x8(v);
+      }
+    }
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+      const int b = b0 + 16 * bb + l16;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x32(wa[cb][ks], qb[bb][ks], acc);
+        // lane holds q~[b][c0 + 16cb + 4q4 + i], i = 0..3
+        if (b < B) {
+          uint2 v;
+          v.x = cvt_bf16x2(acc[0], acc[1]);
+          v.y = cvt_bf16x2(acc[2], acc[3]);
+          *reinterpret_cast<uint2*>(a.q_hat + ((int64_t)b * H + h) * kRowE + c0 + 16 * cb + 4 * q4) = v;
+        }
+      }
+    }
+  }
+  if (slice == 0) {  // append q_rope (already rotated) unchanged
+    for (int i = lane; i < B * 8; i += 64) {
+      const int b = i >> 3, ch = i & 7;
+      *reinterpret_cast<uint4*>(a.q_hat + ((int64_t)b * H + h) * kRowE + kDc + 8 * ch) =
+          *reinterpret_cast<const uint4*>(a.q_rope + ((int64_t)b * H + h) * 64 + 8 * ch);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. split-KV latent attention
+// ---------------------------------------------------------------------------
+// grid (split, sequence); NW waves, each owning HB blocks of 16 heads
+// (H = 16 * NW * HB; 128 heads: 4 waves x 32 heads, one wave per SIMD, so a
+// wave may hold its 256 accumulator registers plus the 144 registers of its
+// absorbed queries). Every wave reads each 32-row tile from LDS once and
+// feeds both of its head blocks from that read.
+template <int NW, int HB>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_attend_kernel(MlaArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kTileB];
+  LDS uint8_t* lds = (LDS uint8_t*)smem;
+
+  constexpr int H = NW * 16 * HB;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int q4 = lane >> 4, l16 = lane & 15;
+  const int split = blockIdx.x;
+  const int b = blockIdx.y;
+  const int L = a.seq_lens ? a.seq_lens[b] : a.max_seq_len;
+  const int t_begin = split * a.chunk;
+  const int t_end = min(L, t_begin + a.chunk);
+  const int64_t rows = (int64_t)a.batch * H;
+
+  if (t_begin >= t_end) {
+    for (int i = tid; i < H; i += NW * 64) a.part_lse[split * rows + (int64_t)b * H + i] = kNegInf;
+    return;
+  }
+
+  const uint16_t* cache_b = a.cache + (int64_t)b * a.cache_sb;
+  const int ntiles = (t_end - t_begin + kTok - 1) / kTok;
+
+  // HBM -> LDS copy of one tile: wave w issues 1 KiB copies k = w, w+NW, ...
+  // Lane l of copy k fills tile chunk p = 64k + l; it fetches the logical
+  // chunk that the swizzle stores there. Rows past the split end are clamped
+  // to its last row (finite data; their weights are zero).
+  auto issue_tile = [&](int it, int buf) {
+    const int t0 = t_begin + it * kTok;
+    for (int k = w; k < kTileDma; k += NW) {
+      const int p = k * 64 + lane;
+      const int row = p / kChunks;
+      const int pc = p - row * kChunks;
+      const int c = pc ^ row_swizzle(row);
+      int t = t0 + row;
+      t = t < t_end ? t : t_end - 1;
+      load_to_lds16(cache_b + (int64_t)t * a.cache_st + 8 * c, lds + buf * kTileB + k * 1024);
+    }
+  };
+
+  // absorbed queries of this lane's heads, as B operands: q^[h][32ks + 8q4 .. +8]
+  bf16x8_t qb[HB][18];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const int h = (w * HB + hb) * 16 + l16;
+    const uint16_t* qp = a.q_hat + ((int64_t)b * H + h) * kRowE + 8 * q4;
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) qb[hb][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + 32 * ks));
+  }
+
+  float m_ref[HB];  // reference max (log2 units) of this lane's heads; fixed by the first tile
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) m_ref[hb] = kNegInf;
+  // lane-constant pieces of the LDS addresses
+  const int f_s = row_swizzle(l16);                         // rows l16 and l16 + 16
+  const int s_off0 = l16 * kRowB + 16 * ((0 + q4) ^ f_s);   // logical chunk 4ks + q4, ks even
+  const int s_off1 = l16 * kRowB + 16 * ((4 + q4) ^ f_s);   // ks odd
+  const int r1 = 4 * q4 + (l16 >> 2);                       // transposed reads: rows r1, r1 + 16
+  const int f_t = row_swizzle(r1);
+  const int hbit = (l16 & 3) >> 1;
+  int t_off[4];
+#pragma unroll
+  for (int cbl = 0; cbl < 4; ++cbl) t_off[cbl] = r1 * kRowB + 16 * ((2 * cbl + hbit) ^ f_t) + 8 * (l16 & 1);
+
+  __shared__ int restart_flag;
+  if (tid == 0) restart_flag = 0;
+
+  f32x4_t o[HB][32];
+  float l_part[HB];  // this lane's share of sum_j 2^(s_j - m_ref)
+  // One attempt normally; a further attempt only if some tile's max exceeded
+  // its head's reference by more than kRefHeadroom (the reference is raised to
+  // that tile max, a strictly larger observed value, so attempts are finite).
+  // A flagged attempt still runs to the end of the split (its accumulators
+  // are discarded); testing the flag only after the tile loop keeps the loop
+  // free of extra exits, which the register allocator needs to keep the
+  // accumulators resident in AGPRs.
+  for (;;) {
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll
+      for (int cb = 0; cb < 32; ++cb) o[hb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      l_part[hb] = 0.f;
+    }
+    issue_tile(0, 0);
+    for (int it = 0; it < ntiles; ++it) {
+      wait_vm_all();
+      __syncthreads();
+      if (it + 1 < ntiles) issue_tile(it + 1, (it + 1) & 1);
+      const LDS uint8_t* tile = lds + (it & 1) * kTileB;
+      const int nv = t_end - (t_begin + it * kTok);  // valid rows in this tile (may exceed 32)
+
+      // S^T = C Q^^T for tokens 0-15 (s[.][0]) and 16-31 (s[.][1]). The tile
+      // operands go through a ring of kSRing register slots: the read for k-step
+      // ks + kSRing - 1 is issued before the matrix ops of k-step ks, and the
+      // scheduling fences keep the compiler from hoisting every read (which
+      // would need more registers than a wave has).
+      constexpr int kSRing = 3;
+      f32x4_t s[HB][2];
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) s[hb][0] = s[hb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      u32x4_t ra0[kSRing], ra1[kSRing];
+      auto read_s = [&](int ks) {
+        const int off = ((ks & 1) ? s_off1 : s_off0) + 128 * (ks >> 1);
+        ra0[ks % kSRing] = *reinterpret_cast<const LDS u32x4_t*>(tile + off);
+        ra1[ks % kSRing] = *reinterpret_cast<const LDS u32x4_t*>(tile + off + 16 * kRowB);
+      };
+#pragma unroll
+      for (int ks = 0; ks < kSRing - 1; ++ks) read_s(ks);
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        if (ks + kSRing - 1 < 18) read_s(ks + kSRing - 1);
+        const bf16x8_t a0 = as_bf16x8(ra0[ks % kSRing]);
+        const bf16x8_t a1 = as_bf16x8(ra1[ks % kSRing]);
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+          s[hb][0] = mfma16x16x32(a0, qb[hb][ks], s[hb][0]);
+          s[hb][1] = mfma16x16x32(a1, qb[hb][ks], s[hb][1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      // the first transposed reads of the PV phase do not depend on P
+      constexpr int kTRing = 4;
+      i16x4_t tlo[kTRing], thi[kTRing];
+      auto read_t = [&](int cb) {
+        const int off = t_off[cb & 3] + 128 * (cb >> 2);
+        tlo[cb % kTRing] = lds_read_tr(tile + off);
+        thi[cb % kTRing] = lds_read_tr(tile + off + 16 * kRowB);
+      };
+#pragma unroll
+      for (int cb = 0; cb < kTRing - 1; ++cb) read_t(cb);
+
+      // online softmax; lane holds tokens 4q4+i and 16+4q4+i of head (hb, l16)
+      bf16x8_t pb[HB];
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = (4 * q4 + i < nv) ? s[hb][0][i] * a.scale_log2 : kNegInf;
+          x[4 + i] = (16 + 4 * q4 + i < nv) ? s[hb][1][i] * a.scale_log2 : kNegInf;
+        }
+        float mx = x[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (m_ref[hb] == kNegInf) m_ref[hb] = mx;  // first tile of the split
+        if (mx > m_ref[hb] + kRefHeadroom) {      // rare: restart with a raised reference
+          m_ref[hb] = mx;
+          restart_flag = 1;
+        }
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = exp2_hw(x[e] - m_ref[hb]);
+          l_part[hb] += p[e];
+        }
+        uint4 pw;
+        pw.x = cvt_bf16x2(p[0], p[1]);
+        pw.y = cvt_bf16x2(p[2], p[3]);
+        pw.z = cvt_bf16x2(p[4], p[5]);
+        pw.w = cvt_bf16x2(p[6], p[7]);
+        pb[hb] = as_bf16x8(pw);
+      }
+
+      // O^T[c, h] += sum_t C[t, c] P[h, t]; B-operand element e is token 4q4+e
+      // (e < 4) or 16+4q4+(e-4), matching the two transposed reads.
+#pragma unroll
+      for (int cb = 0; cb < 32; ++cb) {
+        if (cb + kTRing - 1 < 32) read_t(cb + kTRing - 1);
+        const bf16x8_t at = join_tr(tlo[cb % kTRing], thi[cb % kTRing]);
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) o[hb][cb] = mfma16x16x32(at, pb[hb], o[hb][cb]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+    }
+    wait_vm_all();
+    __syncthreads();
+    if (!restart_flag) break;
+    __syncthreads();  // every thread has seen the flag before it is cleared
+    if (tid == 0) restart_flag = 0;
+  }
+
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const int h = (w * HB + hb) * 16 + l16;
+    // the four lanes of a head hold disjoint token subsets of l
+    float l_tot = l_part[hb] + __shfl_xor(l_part[hb], 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    const float inv = 1.0f / l_tot;
+    uint16_t* po = a.part_out + ((int64_t)split * rows + (int64_t)b * H + h) * kDc + 4 * q4;
+#pragma unroll
+    for (int cb = 0; cb < 32; ++cb) {
+      uint2 v;
+      v.x = cvt_bf16x2(o[hb][cb][0] * inv, o[hb][cb][1] * inv);
+      v.y = cvt_bf16x2(o[hb][cb][2] * inv, o[hb][cb][3] * inv);
+      *reinterpret_cast<uint2*>(po + 16 * cb) = v;
+    }
+    if (q4 == 0) a.part_lse[split * rows + (int64_t)b * H + h] = (m_ref[hb] + log2_hw(l_tot)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. split merge + W_UV projection
+// ---------------------------------------------------------------------------
+// grid: H * n_groups workgroups of 8 waves; a workgroup serves one head and
+// `bpg` consecutive blocks of 16 batch rows, so W_UV,h is staged in LDS once
+// per workgroup. Workgroups of one head share an XCD (linear id % 8 = h % 8).
+// W_UV,h [512 x 128] is stored unpadded (256-byte rows) with an XOR swizzle of
+// the 16-byte chunk index, 2 * (row % 4), so the transposed reads (4 rows x
+// 32 bytes per 16-lane group) hit distinct banks.
+constexpr int kORowB = 1040;  // merged o~ row in LDS: 512 bf16 + 16 bytes pad
+
+__device__ __forceinline__ int wuv_swizzle(int row) { return 2 * (row & 3); }
+
+__global__ __launch_bounds__(512) void mla_merge_project_kernel(MlaArgs a, int n_groups, int bpg) {
+  __shared__ __attribute__((aligned(1024))) uint8_t w_smem[kDc * 256];   // 131072
+  __shared__ __attribute__((aligned(16))) uint8_t o_smem[16 * kORowB];   // 16640
+  LDS uint8_t* w_lds = (LDS uint8_t*)w_smem;
+  LDS uint8_t* o_lds = (LDS uint8_t*)o_smem;
+
+  const int H = a.num_heads;
+  const int B = a.batch;
+  const int x = blockIdx.x;
+  const int h = ((x >> 3) / n_groups) * 8 + (x & 7);
+  const int grp = (x >> 3) % n_groups;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int q4 = lane >> 4, l16 = lane & 15;
+  const int64_t rows = (int64_t)B * H;
+
+  {  // stage W_UV,h by the load-to-LDS path: 128 KiB = 128 wave-wide copies
+    const uint16_t* wsrc = a.w_uv + (int64_t)h * kDc * 128;
+    for (int k = w; k < 128; k += 8) {
+      const int p = k * 64 + lane;   // 16-byte chunk in LDS
+      const int row = p >> 4;
+      const int c = (p & 15) ^ wuv_swizzle(row);
+      load_to_lds16(wsrc + row * 128 + 8 * c, w_lds + k * 1024);
+    }
+  }
+
+  // transposed-read offsets for this wave's 16 output columns (n-block w)
+  const int tr_row = 8 * q4 + (l16 >> 2);        // + 32 ks (+4 for the upper half)
+  const int tr_chunk = 2 * w + ((l16 & 3) >> 1);
+  const int tr_half = 8 * (l16 & 1);
+
+  const int nbb = (B + 15) / 16;
+  for (int bbi = 0; bbi < bpg; ++bbi) {
+    const int bb = grp * bpg + bbi;
+    if (bb >= nbb) break;
+    // merge the splits: thread -> (row r, 16 columns)
+    {
+      const int r = tid >> 5;
+      const int cs = tid & 31;
+      const int bidx = bb * 16 + r;
+      float acc[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+      if (bidx < B) {
+        const int64_t row_id = (int64_t)bidx * H + h;
+        float M = kNegInf;
+        for (int s = 0; s < a.num_splits; ++s) M = fmaxf(M, a.part_lse[s * rows + row_id]);
+        float lse_out = kNegInf;
+        if (M != kNegInf) {
+          const float m2 = M * kLog2e;
+          float z = 0.f;
+          for (int s = 0; s < a.num_splits; ++s) {
+            const float v = a.part_lse[s * rows + row_id];
+            if (v != kNegInf) z += exp2_hw(fmaf(v, kLog2e, -m2));
+          }
+          const float inv_z = 1.0f / z;
+          for (int s = 0; s < a.num_splits; ++s) {
+            const float v = a.part_lse[s * rows + row_id];
+            if (v == kNegInf) continue;
+            const float wgt = exp2_hw(fmaf(v, kLog2e, -m2)) * inv_z;
+            const uint4* src = reinterpret_cast<const uint4*>(a.part_out + (s * rows + row_id) * kDc + 16 * cs);
+            const uint4 u0 = src[0], u1 = src[1];
+            float f[16];
+            unpack_bf16x8(u0, f);
+            unpack_bf16x8(u1, f + 8);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[e] = fmaf(wgt, f[e], acc[e]);
+          }
+          lse_out = M + log2_hw(z) * kLn2;
+        }
+        if (cs == 0 && a.lse) a.lse[row_id] = lse_out;
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        u32x4_t v;
+        v.x = cvt_bf16x2(acc[8 * j + 0], acc[8 * j + 1]);
+        v.y = cvt_bf16x2(acc[8 * j + 2], acc[8 * j + 3]);
+        v.z = cvt_bf16x2(acc[8 * j + 4], acc[8 * j + 5]);
+        v.w = cvt_bf16x2(acc[8 * j + 6], acc[8 * j + 7]);
+        *reinterpret_cast<LDS u32x4_t*>(o_lds + r * kORowB + 2 * (16 * cs + 8 * j)) = v;
+      }
+    }
+    wait_vm_all();
+    __syncthreads();
+
+    // out[b, e] = sum_c o~[b, c] W_UV[h, c, e]; wave w owns columns 16w .. 16w+15
+    f32x4_t acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int ks = 0; ks < 16; ++ks) {
+      const u32x4_t av = *reinterpret_cast<const LDS u32x4_t*>(o_lds + l16 * kORowB + 2 * (32 * ks + 8 * q4));
+      const int row_lo = 32 * ks + tr_row;
+      const int row_hi = row_lo + 4;
+      const i16x4_t lo = lds_read_tr(w_lds + row_lo * 256 + 16 * (tr_chunk ^ wuv_swizzle(row_lo)) + tr_half);
+      const i16x4_t hi = lds_read_tr(w_lds + row_hi * 256 + 16 * (tr_chunk ^ wuv_swizzle(row_hi)) + tr_half);
+      acc2 = mfma16x16x32(as_bf16x8(av), join_tr(lo, hi), acc2);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int bidx = bb * 16 + 4 * q4 + i;
+      if (bidx < B) a.out[((int64_t)bidx * H + h) * 128 + 16 * w + l16] = acc2[i];
+    }
+    __syncthreads();  // o_lds is rewritten by the next block
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mla_absorb(const MlaArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(mla_absorb_kernel, dim3(8, a.num_heads), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_attend(const MlaArgs& a, hipStream_t st) {
+  const dim3 grid(a.num_splits, a.batch);
+  switch (a.num_heads) {
+    case 16: hipLaunchKernelGGL((mla_attend_kernel<1, 1>), grid, dim3(64), 0, st, a); break;
+    case 32: hipLaunchKernelGGL((mla_attend_kernel<2, 1>), grid, dim3(128), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((mla_attend_kernel<4, 1>), grid, dim3(256), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((mla_attend_kernel<4, 2>), grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_merge_project(const MlaArgs& a, hipStream_t st) {
+  const int nbb = (a.batch + 15) / 16;
+  // enough workgroups for one per CU (256), each covering bpg batch blocks
+  int bpg = (nbb * a.num_heads + 255) / 256;
+  bpg = bpg < 1 ? 1 : (bpg > nbb ? nbb : bpg);
+  const int n_groups = (nbb + bpg - 1) / bpg;
+  hipLaunchKernelGGL(mla_merge_project_kernel, dim3(a.num_heads * n_groups), dim3(512), 0, st, a,
+                     n_groups, bpg);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t st) {
+  hipError_t e = launch_mla_absorb(a, st);
+  if (e != hipSuccess) return e;
+  e = launch_mla_attend(a, st);
+  if (e != hipSuccess) return e;
+  return launch_mla_merge_project(a, st);
+}
+
 }  // namespace da

@@ -158,7 +158,9 @@ typedef struct {
 } da_mla_params_t;
 
 /* Bytes of workspace da_mla_decode_absorbed needs (never 0 for valid
- * parameters: it holds the absorbed queries and the split partials). */
+ * parameters): the absorbed queries q^ [B, H, 576] bf16, the per-split
+ * partials o~_s [S, B, H, 512] bf16 and lse_s [S, B, H] float32, each
+ * starting on a 256-byte boundary in that order. */
 DA_EXPORT size_t da_mla_decode_workspace_size(const da_mla_params_t* params);
 
 /* Split count da_mla_decode_absorbed will use (>= 1), or 0 if invalid. */
@@ -173,8 +175,11 @@ DA_EXPORT int32_t da_mla_decode_num_splits(const da_mla_params_t* params);
  *   w_uv     [H, d_c, d_v] bf16, contiguous:    per-head slice, v^C_{j,h} = c_kv_j W_UV[h]
  *   out      [B, H, d_v] float32, contiguous
  *   lse      [B, H] float32, contiguous; may be NULL
- * Numerics: q~ and the softmax weights are rounded to bf16 before the matrix
- * cores; every accumulation is float32.
+ * Numerics: q~, the softmax weights, each split's o~_s and the merged o~ are
+ * rounded to bf16 before they enter the matrix cores or memory; every sum is
+ * accumulated in float32.
+ * Equivalent to da_mla_absorb_query, da_mla_attend_split_pass and
+ * da_mla_merge_project in sequence on the workspace buffers.
  */
 DA_EXPORT da_status_t da_mla_decode_absorbed(const da_mla_params_t* params,
                                    const void* q_nope, const void* q_rope,
@@ -183,6 +188,32 @@ DA_EXPORT da_status_t da_mla_decode_absorbed(const da_mla_params_t* params,
                                    float* out, float* lse,
                                    void* workspace, size_t workspace_bytes,
                                    void* hip_stream);
+
+/* Stage 1, query-side absorption (arganzheng.life section 4.5; jianzhnie.github.io
+ * section 4, "Absorb"): q_hat[b, h, :] = [q_nope[b,h] W_UK[h]^T (bf16) | q_rope[b,h]].
+ *   q_hat [B, H, d_c + d_rope] bf16, contiguous (written). */
+DA_EXPORT da_status_t da_mla_absorb_query(const da_mla_params_t* params,
+                                          const void* q_nope, const void* q_rope,
+                                          const void* w_uk, void* q_hat, void* hip_stream);
+
+/* Stage 2, attention of the absorbed queries over the shared latent rows,
+ * split along the sequence (arganzheng.life sections 4.5 and 5.2). With
+ * S = da_mla_decode_num_splits(params), writes for each split s
+ *   part_out [S, B, H, d_c] bf16:   o~_s = sum_{j in s} softmax_s(score)_j c_kv_j
+ *   part_lse [S, B, H] float32:     lse_s (-inf for a split with no rows). */
+DA_EXPORT da_status_t da_mla_attend_split_pass(const da_mla_params_t* params,
+                                               const void* q_hat, const void* kv_cache,
+                                               const int32_t* seq_lens,
+                                               void* part_out, float* part_lse,
+                                               void* hip_stream);
+
+/* Stage 3, merge the splits by log-sum-exp, then project by W_UV
+ * (arganzheng.life section 4.5, output side): out[b,h] = o~[b,h] W_UV[h];
+ * lse[b,h] = log sum_s exp(lse_s). Inputs as written by stage 2. */
+DA_EXPORT da_status_t da_mla_merge_project(const da_mla_params_t* params,
+                                           const void* part_out, const float* part_lse,
+                                           const void* w_uv, float* out, float* lse,
+                                           void* hip_stream);
 
 /* ------------------------------------------------------------------------ */
 /* Split-KV merge                                                            */
