@@ -320,12 +320,23 @@ def main():
                     choices=["step", "gqa", "mla", "mla-long", "gqa-ragged"])
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle time for the CPU baseline (0 disables)")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="also run one device-to-device copy of this many MiB after the timed "
+                         "steps (a kernel of known traffic, to scale hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(this library has no multi-GPU path).", file=sys.stderr)
         raise SystemExit(2)
     res, plans = run_gpu(args)
+    if args.calibration_copy_mib > 0:
+        import torch
+        n = args.calibration_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["calibration_copy_bytes"] = n
     if args.cpu_budget > 0:
         res["cpu_baseline"] = cpu_baseline(plans, args.cpu_budget)
     print(json.dumps(res), flush=True)

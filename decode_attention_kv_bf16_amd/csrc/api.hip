@@ -120,6 +120,7 @@ da_status_t check_mla_params(const da_mla_params_t* p) {
     return DA_ERR_UNSUPPORTED;
   if (p->num_heads % 16 != 0 || p->num_heads > 128) return DA_ERR_UNSUPPORTED;
   if (p->cache_stride_b < 0 || p->cache_stride_t < kMlaDc + kMlaRope ||
+      p->cache_stride_t > (1 << 24) ||
       (p->cache_stride_b * 2) % 16 != 0 || (p->cache_stride_t * 2) % 16 != 0)
     return DA_ERR_INVALID_ARGUMENT;
   return DA_OK;
@@ -142,6 +143,11 @@ MlaPlan plan_mla(const da_mla_params_t* p) {
     const int64_t s_max = ceil_div(p->max_seq_len, 128);
     s = s < s_max ? s : s_max;
   }
+  // a split's rows are addressed with 32-bit byte offsets: keep each split
+  // below 2 GiB of cache
+  const int64_t row_bytes = p->cache_stride_t * 2;
+  const int64_t s_min = ceil_div((int64_t)p->max_seq_len * row_bytes, (int64_t)1 << 31);
+  if (s < s_min) s = s_min;
   if (s > p->max_seq_len) s = p->max_seq_len;
   if (s < 1) s = 1;
   pl.chunk = (int)ceil_div(p->max_seq_len, s);

@@ -73,17 +73,40 @@ __device__ __forceinline__ void load_to_lds16(const void* src, LDS uint8_t* dst_
 
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
   return pack_bf16x2(lo, hi);
 }
 
-// XOR swizzle of the 16-byte chunk index inside a tile row. Chosen so that
-// (a) 16 consecutive rows read at one logical chunk (S^T operand) and
-// (b) 4 consecutive rows read at two adjacent chunks (transposed O^T operand)
-// both touch distinct LDS banks. Only the low 3 bits of the chunk change, so a
-// chunk stays inside its row (72 chunks = 9 groups of 8).
+// XOR swizzle of the 16-byte chunk index inside a tile row (rows are 1152
+// bytes = 72 chunks; only the low 3 bits of a chunk index change, so a chunk
+// stays inside its row). With r = row & 15:
+//   f(r) = ((r ^ (r >> 2)) & 3) << 1 | ((r >> 2) ^ (r >> 3)) & 1
+// makes both LDS read patterns conflict-free, for LDS bank groups of 128 and
+// of 256 bytes alike: (a) 16 consecutive rows at one logical chunk (the S^T
+// operand: f is a permutation on rows 0-7, on rows 8-15, on even rows and on
+// odd rows) and (b) 4 consecutive rows x 32 bytes (the transposed O^T
+// operand: f >> 1 differs across each aligned group of 4 rows, and across the
+// even and the odd rows of each group of 8).
 __device__ __forceinline__ int row_swizzle(int row) {
-  return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  return (((row ^ (row >> 2)) & 3) << 1) | (((row >> 2) ^ (row >> 3)) & 1);
+}
+
+// Buffer resource for raw (unswizzled, stride 0) byte addressing: loads past
+// num_records bytes return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_raw_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void buffer_load_to_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset,
+                                                     LDS uint8_t* dst_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS void*)dst_wave_base, 16, voffset, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -162,7 +185,13 @@ __global__ __launch_bounds__(64) void mla_absorb_kernel(MlaArgs a) {
 template <int NW, int HB>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_attend_kernel(MlaArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kTileB];
+  // LDS ring of kDepth tiles: up to kDepth - 1 tiles in flight from HBM while
+  // one is consumed. Each wave issues kCopies 1 KiB copies per tile, and a
+  // wave may have at most 63 vector-memory operations outstanding.
+  constexpr int kCopies = kTileDma / NW;
+  static_assert(kTileDma % NW == 0, "copies split evenly over the waves");
+  constexpr int kDepth = (3 * kCopies <= 63) ? 4 : 2;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kDepth * kTileB];
   LDS uint8_t* lds = (LDS uint8_t*)smem;
 
   constexpr int H = NW * 16 * HB;
@@ -186,20 +215,26 @@ void mla_attend_kernel(MlaArgs a) {
   const int ntiles = (t_end - t_begin + kTok - 1) / kTok;
 
   // HBM -> LDS copy of one tile: wave w issues 1 KiB copies k = w, w+NW, ...
-  // Lane l of copy k fills tile chunk p = 64k + l; it fetches the logical
-  // chunk that the swizzle stores there. Rows past the split end are clamped
-  // to its last row (finite data; their weights are zero).
+  // Lane l of copy k fills tile chunk p = 64k + l with the logical chunk that
+  // the swizzle stores there; its byte offset inside a tile is fixed, so it is
+  // computed once. Each tile gets a buffer resource that ends at the split's
+  // last row, so rows past it read as zeros (their weights are zero anyway).
+  const uint32_t row_bytes = (uint32_t)a.cache_st * 2u;
+  uint32_t voff[kCopies];
+#pragma unroll
+  for (int i = 0; i < kCopies; ++i) {
+    const int p = (w + NW * i) * 64 + lane;
+    const int row = p / kChunks;
+    const int c = (p - row * kChunks) ^ row_swizzle(row);
+    voff[i] = (uint32_t)row * row_bytes + 16u * (uint32_t)c;
+  }
   auto issue_tile = [&](int it, int buf) {
     const int t0 = t_begin + it * kTok;
-    for (int k = w; k < kTileDma; k += NW) {
-      const int p = k * 64 + lane;
-      const int row = p / kChunks;
-      const int pc = p - row * kChunks;
-      const int c = pc ^ row_swizzle(row);
-      int t = t0 + row;
-      t = t < t_end ? t : t_end - 1;
-      load_to_lds16(cache_b + (int64_t)t * a.cache_st + 8 * c, lds + buf * kTileB + k * 1024);
-    }
+    const __amdgpu_buffer_rsrc_t rsrc =
+        make_raw_rsrc(cache_b + (int64_t)t0 * a.cache_st, (uint32_t)(t_end - t0) * row_bytes);
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i)
+      buffer_load_to_lds16(rsrc, voff[i], lds + buf * kTileB + (w + NW * i) * 1024);
   };
 
   // absorbed queries of this lane's heads, as B operands: q^[h][32ks + 8q4 .. +8]
@@ -245,12 +280,23 @@ void mla_attend_kernel(MlaArgs a) {
       for (int cb = 0; cb < 32; ++cb) o[hb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       l_part[hb] = 0.f;
     }
-    issue_tile(0, 0);
+#pragma unroll
+    for (int j = 0; j < kDepth - 1; ++j)
+      if (j < ntiles) issue_tile(j, j);
     for (int it = 0; it < ntiles; ++it) {
-      wait_vm_all();
+      // tile `it` has landed once only the copies of later tiles are pending
+      const int ahead = min(kDepth - 2, ntiles - 1 - it);
+      if constexpr (kDepth >= 4) {
+        if (ahead >= 2) wait_vm<2 * kCopies>();
+        else if (ahead == 1) wait_vm<kCopies>();
+        else wait_vm<0>();
+      } else {
+        wait_vm<0>();  // two buffers: the one tile ahead is issued after this wait
+      }
       __syncthreads();
-      if (it + 1 < ntiles) issue_tile(it + 1, (it + 1) & 1);
-      const LDS uint8_t* tile = lds + (it & 1) * kTileB;
+      // the buffer refilled here was last read in iteration it - 1
+      if (it + kDepth - 1 < ntiles) issue_tile(it + kDepth - 1, (it + kDepth - 1) % kDepth);
+      const LDS uint8_t* tile = lds + (it % kDepth) * kTileB;
       const int nv = t_end - (t_begin + it * kTok);  // valid rows in this tile (may exceed 32)
 
       // S^T = C Q^^T for tokens 0-15 (s[.][0]) and 16-31 (s[.][1]). The tile
