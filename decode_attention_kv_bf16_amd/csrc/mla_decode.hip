@@ -73,6 +73,16 @@ __device__ __forceinline__ void load_to_lds16(const void* src, LDS uint8_t* dst_
 
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Workgroup barrier without the release fence of __syncthreads(): that fence
+// makes the compiler wait for every outstanding load-to-LDS copy (vmcnt(0)),
+// including the tiles meant to stay in flight, which empties the copy ring on
+// every tile. Ordering here is explicit instead: each wave waits for its own
+// copies of the tile with wait_vm<N>() before the barrier, and every LDS read
+// of the buffer being refilled has returned (its value was consumed) before
+// the wave reaches the barrier. The memory clobber keeps the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void tile_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -293,7 +303,7 @@ void mla_attend_kernel(MlaArgs a) {
       } else {
         wait_vm<0>();  // two buffers: the one tile ahead is issued after this wait
       }
-      __syncthreads();
+      tile_barrier();
       // the buffer refilled here was last read in iteration it - 1
       if (it + kDepth - 1 < ntiles) issue_tile(it + kDepth - 1, (it + kDepth - 1) % kDepth);
       const LDS uint8_t* tile = lds + (it % kDepth) * kTileB;
