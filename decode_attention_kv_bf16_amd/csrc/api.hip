@@ -115,6 +115,9 @@ da_status_t check_mla_params(const da_mla_params_t* p) {
       p->v_head_dim < 1)
     return DA_ERR_INVALID_ARGUMENT;
   if (!isfinite(p->softmax_scale)) return DA_ERR_INVALID_ARGUMENT;
+  // the attention kernel screens raw scores against a threshold, which needs a
+  // positive scale (the method's 1/sqrt(d) always is)
+  if (!(p->softmax_scale > 0.0f)) return DA_ERR_UNSUPPORTED;
   if (p->kv_lora_rank != kMlaDc || p->qk_rope_dim != kMlaRope || p->qk_nope_dim != kMlaNope ||
       p->v_head_dim != kMlaV)
     return DA_ERR_UNSUPPORTED;

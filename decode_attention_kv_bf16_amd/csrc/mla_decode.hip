@@ -114,9 +114,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_raw_rsrc(const void* base
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// One wave-wide 1 KiB copy HBM -> LDS (buffer_load_dwordx4 ... lds): lane l
+// reads 16 bytes at rsrc base + voffset and writes them at LDS byte address
+// lds_addr + 16 l (lds_addr is wave-uniform). Written in asm so that the compiler does not track
+// the copy: tracked, every LDS read after it waits for all outstanding copies
+// (vmcnt(0)), because the compiler cannot tell which LDS bytes a copy writes.
+// Completion is waited for explicitly with wait_vm<N>() instead. The asm has
+// no output register (the data goes to LDS); M0, which holds the LDS address,
+// is saved and restored around it.
 __device__ __forceinline__ void buffer_load_to_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset,
-                                                     LDS uint8_t* dst_wave_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS void*)dst_wave_base, 16, voffset, 0, 0, 0);
+                                                     uint32_t lds_addr) {
+  uint32_t saved_m0;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved_m0)
+      : "v"(voffset), "s"(rsrc), "s"(lds_addr)
+      : "memory");
 }
 
 // ---------------------------------------------------------------------------
@@ -238,13 +255,23 @@ void mla_attend_kernel(MlaArgs a) {
     const int c = (p - row * kChunks) ^ row_swizzle(row);
     voff[i] = (uint32_t)row * row_bytes + 16u * (uint32_t)c;
   }
-  auto issue_tile = [&](int it, int buf) {
+  // LDS destinations are computed in scalar registers: this wave's first copy
+  // slot of ring buffer 0, as a byte address
+  const uint32_t lds_w0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds + (uint32_t)w * 1024u);
+  // Tiles past the split's end get an empty range: their copies read nothing
+  // and fill the (unused) ring buffer with zeros, which keeps the number of
+  // copies in flight, and so every wait below, the same on every tile.
+  auto tile_rsrc = [&](int it) {
     const int t0 = t_begin + it * kTok;
-    const __amdgpu_buffer_rsrc_t rsrc =
-        make_raw_rsrc(cache_b + (int64_t)t0 * a.cache_st, (uint32_t)(t_end - t0) * row_bytes);
+    return make_raw_rsrc(cache_b + (int64_t)t0 * a.cache_st, (uint32_t)max(t_end - t0, 0) * row_bytes);
+  };
+  auto issue_copy = [&](__amdgpu_buffer_rsrc_t rsrc, int i, int buf) {
+    buffer_load_to_lds16(rsrc, voff[i], lds_w0 + (uint32_t)(buf * kTileB + NW * i * 1024));
+  };
+  auto issue_tile = [&](int it, int buf) {
+    const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc(it);
 #pragma unroll
-    for (int i = 0; i < kCopies; ++i)
-      buffer_load_to_lds16(rsrc, voff[i], lds + buf * kTileB + (w + NW * i) * 1024);
+    for (int i = 0; i < kCopies; ++i) issue_copy(rsrc, i, buf);
   };
 
   // absorbed queries of this lane's heads, as B operands: q^[h][32ks + 8q4 .. +8]
@@ -256,10 +283,18 @@ void mla_attend_kernel(MlaArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) qb[hb][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + 32 * ks));
   }
+  // The compiler does not see the tile copies, so its wait for these loads
+  // would be a vmcnt(0) at their first use, after the copies are in flight:
+  // take the wait here, before any copy is issued.
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) asm volatile("" ::"v"(qb[hb][ks]));
 
   float m_ref[HB];  // reference max (log2 units) of this lane's heads; fixed by the first tile
+  float thr[HB];    // raw score above which a head's reference must be raised
 #pragma unroll
-  for (int hb = 0; hb < HB; ++hb) m_ref[hb] = kNegInf;
+  for (int hb = 0; hb < HB; ++hb) m_ref[hb] = thr[hb] = kNegInf;
   // lane-constant pieces of the LDS addresses
   const int f_s = row_swizzle(l16);                         // rows l16 and l16 + 16
   const int s_off0 = l16 * kRowB + 16 * ((0 + q4) ^ f_s);   // logical chunk 4ks + q4, ks even
@@ -291,21 +326,17 @@ void mla_attend_kernel(MlaArgs a) {
       l_part[hb] = 0.f;
     }
 #pragma unroll
-    for (int j = 0; j < kDepth - 1; ++j)
-      if (j < ntiles) issue_tile(j, j);
+    for (int j = 0; j < kDepth - 1; ++j) issue_tile(j, j);
     for (int it = 0; it < ntiles; ++it) {
-      // tile `it` has landed once only the copies of later tiles are pending
-      const int ahead = min(kDepth - 2, ntiles - 1 - it);
-      if constexpr (kDepth >= 4) {
-        if (ahead >= 2) wait_vm<2 * kCopies>();
-        else if (ahead == 1) wait_vm<kCopies>();
-        else wait_vm<0>();
-      } else {
-        wait_vm<0>();  // two buffers: the one tile ahead is issued after this wait
-      }
+      // tile `it` has landed once only the copies of the kDepth - 2 tiles
+      // after it are pending
+      wait_vm<(kDepth - 2) * kCopies>();
       tile_barrier();
-      // the buffer refilled here was last read in iteration it - 1
-      if (it + kDepth - 1 < ntiles) issue_tile(it + kDepth - 1, (it + kDepth - 1) % kDepth);
+      // The buffer refilled in this iteration was last read in iteration
+      // it - 1. Its copies are spread over the k-steps of S^T below, so that
+      // their issue overlaps the matrix ops.
+      const int refill_buf = (it + kDepth - 1) % kDepth;
+      const __amdgpu_buffer_rsrc_t refill_rsrc = tile_rsrc(it + kDepth - 1);
       const LDS uint8_t* tile = lds + (it % kDepth) * kTileB;
       const int nv = t_end - (t_begin + it * kTok);  // valid rows in this tile (may exceed 32)
 
@@ -328,6 +359,8 @@ void mla_attend_kernel(MlaArgs a) {
       for (int ks = 0; ks < kSRing - 1; ++ks) read_s(ks);
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
+#pragma unroll
+        for (int i = ks * kCopies / 18; i < (ks + 1) * kCopies / 18; ++i) issue_copy(refill_rsrc, i, refill_buf);
         if (ks + kSRing - 1 < 18) read_s(ks + kSRing - 1);
         const bf16x8_t a0 = as_bf16x8(ra0[ks % kSRing]);
         const bf16x8_t a1 = as_bf16x8(ra1[ks % kSRing]);
@@ -350,32 +383,55 @@ void mla_attend_kernel(MlaArgs a) {
 #pragma unroll
       for (int cb = 0; cb < kTRing - 1; ++cb) read_t(cb);
 
-      // online softmax; lane holds tokens 4q4+i and 16+4q4+i of head (hb, l16)
+      // online softmax; lane holds tokens 4q4+i and 16+4q4+i of head (hb, l16).
+      // Rows past the split end (last tile only) get score -inf, weight 0.
+      const bool full_tile = nv >= kTok;
+      float smax[HB];
+      bool over = false;
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        if (!full_tile) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (4 * q4 + i >= nv) s[hb][0][i] = kNegInf;
+            if (16 + 4 * q4 + i >= nv) s[hb][1][i] = kNegInf;
+          }
+        }
+        float mx = fmaxf(s[hb][0][0], s[hb][1][0]);
+#pragma unroll
+        for (int i = 1; i < 4; ++i) mx = fmaxf(mx, fmaxf(s[hb][0][i], s[hb][1][i]));
+        smax[hb] = mx;
+        over |= mx > thr[hb];
+      }
+      // Only the first tile of a split (thr = -inf) and a score beyond the
+      // headroom need the head-wide max: the four lanes of a head combine
+      // theirs, so they agree on the reference.
+      if (__builtin_amdgcn_ballot_w64(over) != 0) {
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+          float mx = smax[hb] * a.scale_log2;
+          mx = fmaxf(mx, __shfl_xor(mx, 16));
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          if (m_ref[hb] == kNegInf) {
+            m_ref[hb] = mx;                          // first tile of the split
+          } else if (mx > m_ref[hb] + kRefHeadroom) {  // rare: restart with a raised reference
+            m_ref[hb] = mx;
+            restart_flag = 1;
+          }
+          thr[hb] = (m_ref[hb] + kRefHeadroom) / a.scale_log2;
+        }
+      }
       bf16x8_t pb[HB];
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[i] = (4 * q4 + i < nv) ? s[hb][0][i] * a.scale_log2 : kNegInf;
-          x[4 + i] = (16 + 4 * q4 + i < nv) ? s[hb][1][i] * a.scale_log2 : kNegInf;
-        }
-        float mx = x[0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (m_ref[hb] == kNegInf) m_ref[hb] = mx;  // first tile of the split
-        if (mx > m_ref[hb] + kRefHeadroom) {      // rare: restart with a raised reference
-          m_ref[hb] = mx;
-          restart_flag = 1;
-        }
+        const float mneg = -m_ref[hb];
         float p[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = exp2_hw(x[e] - m_ref[hb]);
-          l_part[hb] += p[e];
+        for (int i = 0; i < 4; ++i) {
+          p[i] = exp2_hw(fmaf(s[hb][0][i], a.scale_log2, mneg));
+          p[4 + i] = exp2_hw(fmaf(s[hb][1][i], a.scale_log2, mneg));
         }
+        l_part[hb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         uint4 pw;
         pw.x = cvt_bf16x2(p[0], p[1]);
         pw.y = cvt_bf16x2(p[2], p[3]);

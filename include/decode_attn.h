@@ -151,7 +151,8 @@ typedef struct {
   int32_t qk_nope_dim;     /* d_nope: must be 128 */
   int32_t v_head_dim;      /* d_v: must be 128 */
   int32_t max_seq_len;     /* L_max >= 1 */
-  float softmax_scale;     /* 1/sqrt(qk_nope_dim + qk_rope_dim) = 1/sqrt(192) for DeepSeek-V3 */
+  float softmax_scale;     /* 1/sqrt(qk_nope_dim + qk_rope_dim) = 1/sqrt(192) for DeepSeek-V3;
+                              must be finite and > 0 (else UNSUPPORTED) */
   int64_t cache_stride_b;  /* row [b, t] at kv_cache + b*cache_stride_b + t*cache_stride_t */
   int64_t cache_stride_t;  /* default layout [B, L_max, 576]: 576*L_max and 576 */
   int32_t num_splits;      /* S >= 1 forces a split count; 0 lets the library choose */

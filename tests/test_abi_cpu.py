@@ -151,7 +151,8 @@ def test_mla_and_combine_reject_bad_parameters():
                                         None, FAKE, ws_bytes, None)
     for field, val, code in [("kv_lora_rank", 256, 2), ("qk_rope_dim", 32, 2), ("num_heads", 24, 2),
                              ("num_heads", 256, 2), ("batch", 0, 1), ("cache_stride_t", 512, 1),
-                             ("max_seq_len", -1, 1)]:
+                             ("max_seq_len", -1, 1), ("softmax_scale", 0.0, 2), ("softmax_scale", -0.1, 2),
+                             ("softmax_scale", float("nan"), 1)]:
         p = mla()
         setattr(p, field, val)
         assert call_mla(p) == code, field

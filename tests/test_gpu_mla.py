@@ -93,10 +93,10 @@ def assert_small_L(inp, out, lse, what):
     bound = qtilde_score_bound(inp, range(B))
     full = np.isfinite(rl)
     assert_parity(out, lse, ro, rl, lse_atol=np.inf, what=what)   # outputs + empty rows
-    lerr = np.abs(lse - rl)
-    lim = np.maximum(1e-3, bound + 1e-5)
-    assert np.all(lerr[full] <= lim[full]), f"{what}: lse error {lerr[full].max():.3e} over bound"
-    return float(row_rel_err(out[full], ro[full]).max()), float(lerr[full].max())
+    lerr = np.abs(lse[full] - rl[full])
+    lim = np.maximum(1e-3, bound[full] + 1e-5)
+    assert np.all(lerr <= lim), f"{what}: lse error {lerr.max():.3e} over bound"
+    return float(row_rel_err(out[full], ro[full]).max()), float(lerr.max())
 
 
 EDGE = [
