@@ -20,7 +20,6 @@ bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -137,26 +136,19 @@ def setup_mla(cfg):
     return calls, alg, info, inp
 
 
-def kernel_source_hash(name):
-    """sha256 of the HIP source that holds a kernel (to tie profiles to code)."""
-    src = {"gqa_split_pass": "gqa_decode.hip", "mla_attend": "mla_decode.hip"}.get(name)
-    if src is None:
-        return None
-    with open(os.path.join(ROOT, "decode_attention_kv_bf16_amd", "csrc", src), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
-
-
-def measured_traffic(name, launches_alg_bytes):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; otherwise None."""
+def measured_traffic(name):
+    """HBM bytes per launch from the committed rocprofv3 counter runs
+    (profiles/hbm_traffic.json), if they were taken on the current kernel
+    source; otherwise None."""
+    from decode_attention_kv_bf16_amd.profiling import source_sha256
     path = os.path.join(PROFILE_DIR, "hbm_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f).get(name)
-    if not rec or rec.get("source_sha256") != kernel_source_hash(name):
+    if not rec or rec.get("source_sha256") != source_sha256(name):
         return None
-    return rec.get("bytes_per_launch")
+    return round(rec["bytes_per_launch"])
 
 
 def run_gpu(args):
@@ -227,7 +219,7 @@ def run_gpu(args):
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(dom, dom_bytes),
+                "traffic": measured_traffic(dom),
                 "alg_bytes_per_launch": int(dom_bytes), "avg_launch_us": round(dom_ms * 1e3, 2)}
 
     paths = {}
@@ -318,7 +310,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="step",
                     choices=["step", "gqa", "mla", "mla-long", "gqa-ragged"])
-    ap.add_argument("--cpu-budget", type=float, default=12.0,
+    ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle time for the CPU baseline (0 disables)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB after the timed "

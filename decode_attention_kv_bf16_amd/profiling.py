@@ -1,0 +1,155 @@
+"""Summaries of rocprofv3 output for this library's kernels.
+
+    python -m decode_attention_kv_bf16_amd.profiling stats KERNEL_STATS_CSV --command CMD --out FILE.md
+    python -m decode_attention_kv_bf16_amd.profiling traffic --fetch FETCH_DIR --write WRITE_DIR \
+        --copy-bytes N --fetch-command CMD --write-command CMD --workload NAME --out-md FILE.md
+
+`stats` turns a `--kernel-trace --stats --output-format csv` run into a
+per-kernel table of launch durations. `traffic` turns two counter runs
+(`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, both over a command that ends
+with a device-to-device copy of N bytes) into HBM bytes per launch: each
+counter's per-dispatch average (KiB) is scaled by the factor that makes the
+same counter read N bytes for the copy kernel (the last copy dispatch of the
+run). The result is merged into profiles/hbm_traffic.json, keyed by kernel,
+with the sha256 of the source file that holds the kernel, so that a reader
+can tell whether the figures still describe the current code.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+from collections import defaultdict
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+# short kernel name -> (substring of the device symbol, source file)
+KERNELS = {
+    "gqa_split_pass": ("gqa_decode_kernel", "gqa_decode.hip"),
+    "gqa_combine": ("splitkv_combine_kernel", "combine.hip"),
+    "mla_absorb": ("mla_absorb_kernel", "mla_decode.hip"),
+    "mla_attend": ("mla_attend_kernel", "mla_decode.hip"),
+    "mla_merge_project": ("mla_merge_project_kernel", "mla_decode.hip"),
+}
+
+
+def source_sha256(short: str):
+    if short not in KERNELS:
+        return None
+    with open(os.path.join(CSRC, KERNELS[short][1]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def short_name(symbol: str):
+    for short, (sub, _) in KERNELS.items():
+        if sub in symbol:
+            return short
+    return None
+
+
+def _find(path: str, suffix: str) -> str:
+    if os.path.isfile(path):
+        return path
+    for dirpath, _, files in os.walk(path):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(dirpath, f)
+    raise FileNotFoundError(f"no *{suffix} under {path}")
+
+
+def stats_table(stats_csv: str) -> str:
+    rows = list(csv.DictReader(open(_find(stats_csv, "kernel_stats.csv"))))
+    lines = ["| kernel | symbol | calls | avg us | min us | max us | share % |",
+             "|---|---|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        sym = r["Name"]
+        lines.append(f"| {short_name(sym) or '-'} | `{sym[:90]}` | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    return "\n".join(lines)
+
+
+def counter_averages(counter_dir: str, counter: str):
+    """Per short kernel name: average counter value per dispatch, and the value
+    for the last copy-kernel dispatch of the run (the calibration copy)."""
+    rows = list(csv.DictReader(open(_find(counter_dir, "counter_collection.csv"))))
+    per = defaultdict(list)
+    copy_val = None
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        v = float(r["Counter_Value"])
+        if "copyBuffer" in r["Kernel_Name"]:
+            copy_val = v
+            continue
+        s = short_name(r["Kernel_Name"])
+        if s:
+            per[s].append(v)
+    return {k: sum(v) / len(v) for k, v in per.items()}, {k: len(v) for k, v in per.items()}, copy_val
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--command", required=True)
+    s.add_argument("--title", default="rocprofv3 kernel durations")
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--fetch-command", required=True)
+    t.add_argument("--write-command", required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--alg-bytes", default="{}", help="JSON {kernel: algorithmic bytes per launch}")
+    t.add_argument("--out-md", required=True)
+    a = ap.parse_args(argv)
+
+    if a.cmd == "stats":
+        text = (f"# {a.title}\n\nCommand (run from the repository root):\n\n```\n{a.command}\n```\n\n"
+                f"{stats_table(a.csv)}\n")
+        with open(a.out, "w") as f:
+            f.write(text)
+        print(text)
+        return
+
+    fetch, nf, fcopy = counter_averages(a.fetch, "FETCH_SIZE")
+    write, nw, wcopy = counter_averages(a.write, "WRITE_SIZE")
+    if not fcopy or not wcopy:
+        raise SystemExit("no calibration copy dispatch found in the counter runs")
+    copy_kib = a.copy_bytes / 1024.0
+    ff, wf = copy_kib / fcopy, copy_kib / wcopy
+    alg = json.loads(a.alg_bytes)
+    path = os.path.join(PROFILE_DIR, "hbm_traffic.json")
+    rec = json.load(open(path)) if os.path.exists(path) else {}
+    lines = [f"# HBM traffic per launch: {a.workload}", "",
+             "Counter runs (from the repository root):", "", "```", a.fetch_command, a.write_command, "```", "",
+             f"Calibration: a device-to-device copy of {a.copy_bytes} bytes at the end of each run reads "
+             f"FETCH_SIZE = {fcopy:.1f} KiB and WRITE_SIZE = {wcopy:.1f} KiB, so the counters are scaled by "
+             f"{ff:.3f} (fetch) and {wf:.3f} (write).", "",
+             "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes / launch (scaled) | algorithmic bytes | ratio |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+    for k in sorted(set(fetch) & set(write)):
+        b = fetch[k] * 1024 * ff + write[k] * 1024 * wf
+        ab = alg.get(k)
+        ratio = f"{b / ab:.3f}" if ab else "-"
+        lines.append(f"| {k} | {nf[k]} | {fetch[k]:.1f} | {write[k]:.1f} | {b:.4g} | {ab if ab else '-'} | {ratio} |")
+        rec[k] = dict(bytes_per_launch=b, fetch_kib=fetch[k], write_kib=write[k], fetch_factor=ff,
+                      write_factor=wf, workload=a.workload, source_sha256=source_sha256(k),
+                      algorithmic_bytes=ab)
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    with open(a.out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    main()
