@@ -66,6 +66,27 @@ da_status_t check_gqa_params(const da_gqa_params_t* p) {
   return DA_OK;
 }
 
+// Split count for `units` independent work items of `len` rows each when
+// `slots` workgroups can be resident at once: the s in [1, s_max] that
+// minimises rounds(s) * (ceil(len / s) + overhead_rows), with rounds(s) =
+// ceil(units * s / slots) waves of workgroups, each as long as its chunk plus
+// a fixed per-workgroup cost. Lengths are taken as len for every item (the
+// lengths themselves stay on the device).
+int64_t choose_splits(int64_t units, int64_t len, int64_t slots, int64_t min_rows,
+                      int64_t overhead_rows) {
+  int64_t s_max = ceil_div(len, min_rows);
+  s_max = s_max < 1024 ? s_max : 1024;
+  int64_t best = 1, best_cost = -1;
+  for (int64_t s = 1; s <= s_max; ++s) {
+    const int64_t cost = ceil_div(units * s, slots) * (ceil_div(len, s) + overhead_rows);
+    if (best_cost < 0 || cost < best_cost) {
+      best = s;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 struct GqaPlan {
   int splits, chunk, heads_per_block;
   size_t part_out_bytes, part_lse_bytes, workspace;
@@ -80,14 +101,11 @@ GqaPlan plan_gqa(const da_gqa_params_t* p) {
   if (p->num_splits > 0) {
     s = p->num_splits;
   } else {
-    // Enough 4-wave workgroups for ~4 per CU, and no split longer than 1024
-    // rows (bounds the tail when lengths are ragged), but no split shorter
-    // than 256 rows unless the sequence itself is shorter.
-    const int64_t target = 4LL * device_cu_count();
-    s = ceil_div(target, units);
-    s = s > ceil_div(p->max_seq_len, 1024) ? s : ceil_div(p->max_seq_len, 1024);
-    const int64_t s_max = ceil_div(p->max_seq_len, 256);
-    s = s < s_max ? s : s_max;
+    // Workgroups resident at once: the kernel's occupancy on this device
+    // (2 per CU when no device can be asked); splits no shorter than 128 rows.
+    int bpc = da::gqa_blocks_per_cu(p->dtype == DA_DTYPE_BF16 ? 1 : 0, p->head_dim, pl.heads_per_block);
+    if (bpc < 1) bpc = 2;
+    s = choose_splits(units, p->max_seq_len, (int64_t)bpc * device_cu_count(), 128, 64);
   }
   if (s > p->max_seq_len) s = p->max_seq_len;
   if (s < 1) s = 1;
@@ -121,7 +139,12 @@ da_status_t check_mla_params(const da_mla_params_t* p) {
   if (p->kv_lora_rank != kMlaDc || p->qk_rope_dim != kMlaRope || p->qk_nope_dim != kMlaNope ||
       p->v_head_dim != kMlaV)
     return DA_ERR_UNSUPPORTED;
-  if (p->num_heads % 16 != 0 || p->num_heads > 128) return DA_ERR_UNSUPPORTED;
+  // head counts with an attention-kernel shape (multiples of 16 whose
+  // wave count divides a tile's 36 copies)
+  switch (p->num_heads) {
+    case 16: case 32: case 48: case 64: case 96: case 128: break;
+    default: return DA_ERR_UNSUPPORTED;
+  }
   if (p->cache_stride_b < 0 || p->cache_stride_t < kMlaDc + kMlaRope ||
       p->cache_stride_t > (1 << 24) ||
       (p->cache_stride_b * 2) % 16 != 0 || (p->cache_stride_t * 2) % 16 != 0)
@@ -140,11 +163,13 @@ MlaPlan plan_mla(const da_mla_params_t* p) {
   if (p->num_splits > 0) {
     s = p->num_splits;
   } else {
-    // One workgroup (all heads of one sequence) per CU; splits no shorter
-    // than 128 rows.
-    s = ceil_div(device_cu_count(), p->batch);
-    const int64_t s_max = ceil_div(p->max_seq_len, 128);
-    s = s < s_max ? s : s_max;
+    // One workgroup serves all heads of a split of one sequence; resident
+    // workgroups from the kernel's occupancy (1 per CU when no device can be
+    // asked); splits no shorter than 128 rows, and a fixed cost of about 128
+    // rows per workgroup (loading its queries, writing its partials).
+    int bpc = da::mla_attend_blocks_per_cu(p->num_heads);
+    if (bpc < 1) bpc = 1;
+    s = choose_splits(p->batch, p->max_seq_len, (int64_t)bpc * device_cu_count(), 128, 128);
   }
   // a split's rows are addressed with 32-bit byte offsets: keep each split
   // below 2 GiB of cache

@@ -22,6 +22,8 @@
 //   the 4 waves through LDS.
 //   Scores live in the base-2 domain: q is pre-multiplied by scale*log2(e) so
 //   each softmax weight is one v_exp_f32.
+#include <atomic>
+
 #include "da_device.h"
 #include "da_internal.h"
 
@@ -253,7 +255,52 @@ hipError_t launch_gh(const GqaArgs& a, hipStream_t st) {
   }
 }
 
+template <typename T, int D, int GH>
+int blocks_per_cu_t() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, reinterpret_cast<const void*>(&gqa_decode_kernel<T, D, GH>), kThreads, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return n;
+}
+
+template <typename T, int D>
+int blocks_per_cu_gh(int gh) {
+  switch (gh) {
+    case 1: return blocks_per_cu_t<T, D, 1>();
+    case 2: return blocks_per_cu_t<T, D, 2>();
+    case 3: return blocks_per_cu_t<T, D, 3>();
+    case 4: return blocks_per_cu_t<T, D, 4>();
+    case 5: return blocks_per_cu_t<T, D, 5>();
+    case 6: return blocks_per_cu_t<T, D, 6>();
+    case 7: return blocks_per_cu_t<T, D, 7>();
+    case 8: return blocks_per_cu_t<T, D, 8>();
+    default: return 0;
+  }
+}
+
 }  // namespace
+
+int gqa_blocks_per_cu(int dtype, int head_dim, int heads_per_block) {
+  if (heads_per_block < 1 || heads_per_block > 8) return 0;
+  // the answer depends only on the kernel's resources and the device type:
+  // cache it per instantiation
+  static std::atomic<int> cache[2][2][9];
+  const int di = dtype == 1 ? 1 : 0, hi = head_dim == 128 ? 1 : 0;
+  int n = cache[di][hi][heads_per_block].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (dtype == 1) {
+    n = head_dim == 128 ? blocks_per_cu_gh<uint16_t, 128>(heads_per_block)
+                        : blocks_per_cu_gh<uint16_t, 64>(heads_per_block);
+  } else {
+    n = head_dim == 128 ? blocks_per_cu_gh<float, 128>(heads_per_block)
+                        : blocks_per_cu_gh<float, 64>(heads_per_block);
+  }
+  if (n > 0) cache[di][hi][heads_per_block].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 hipError_t launch_gqa_decode(const GqaArgs& a, int dtype, int head_dim, hipStream_t st) {
   if (dtype == 1) {

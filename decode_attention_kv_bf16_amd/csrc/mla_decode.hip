@@ -604,16 +604,40 @@ hipError_t launch_mla_absorb(const MlaArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Head counts with an attention shape: NW waves of HB blocks of 16 heads, NW
+// dividing the 36 copies of a tile.
+template <typename F>
+bool with_attend_shape(int num_heads, F&& f) {
+  switch (num_heads) {
+    case 16: f(mla_attend_kernel<1, 1>, 1); return true;
+    case 32: f(mla_attend_kernel<2, 1>, 2); return true;
+    case 48: f(mla_attend_kernel<3, 1>, 3); return true;
+    case 64: f(mla_attend_kernel<4, 1>, 4); return true;
+    case 96: f(mla_attend_kernel<3, 2>, 3); return true;
+    case 128: f(mla_attend_kernel<4, 2>, 4); return true;
+    default: return false;
+  }
+}
+
 hipError_t launch_mla_attend(const MlaArgs& a, hipStream_t st) {
   const dim3 grid(a.num_splits, a.batch);
-  switch (a.num_heads) {
-    case 16: hipLaunchKernelGGL((mla_attend_kernel<1, 1>), grid, dim3(64), 0, st, a); break;
-    case 32: hipLaunchKernelGGL((mla_attend_kernel<2, 1>), grid, dim3(128), 0, st, a); break;
-    case 64: hipLaunchKernelGGL((mla_attend_kernel<4, 1>), grid, dim3(256), 0, st, a); break;
-    case 128: hipLaunchKernelGGL((mla_attend_kernel<4, 2>), grid, dim3(256), 0, st, a); break;
-    default: return hipErrorInvalidValue;
-  }
+  const bool ok = with_attend_shape(a.num_heads, [&](auto kernel, int nw) {
+    hipLaunchKernelGGL(kernel, grid, dim3(64 * nw), 0, st, a);
+  });
+  if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+int mla_attend_blocks_per_cu(int num_heads) {
+  int n = 0;
+  const bool ok = with_attend_shape(num_heads, [&](auto kernel, int nw) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(kernel), 64 * nw,
+                                                     0) != hipSuccess) {
+      (void)hipGetLastError();
+      n = 0;
+    }
+  });
+  return ok ? n : 0;
 }
 
 hipError_t launch_mla_merge_project(const MlaArgs& a, hipStream_t st) {

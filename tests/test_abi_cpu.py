@@ -79,21 +79,33 @@ def mla(B=64, H=128, L=4096, splits=0):
 
 @needs_lib
 @cpu_only
+def split_cost_model(units, length, slots, min_rows, overhead):
+    # the planner's rule, written out: fewest rounds x (chunk + fixed cost)
+    best = None
+    for s in range(1, min(-(-length // min_rows), 1024) + 1):
+        cost = -(-units * s // slots) * (-(-length // s) + overhead)
+        if best is None or cost < best[1]:
+            best = (s, cost)
+    return best[0]
+
+
 def test_split_planning_without_a_device():
-    # with no device the planner assumes a full MI355X (256 CUs)
+    # with no device the planner assumes a full MI355X (256 CUs) and an
+    # occupancy of 2 GQA / 1 MLA workgroups per CU
     L = da.lib()
     n = lambda p: L.da_gqa_decode_num_splits(ctypes.byref(p))
     ws = lambda p: L.da_gqa_decode_workspace_size(ctypes.byref(p))
-    assert n(gqa()) == 4                                   # Llama-3-8B: 256 (b, kv) pairs x 4
-    assert ws(gqa()) == 4 * 32 * 32 * 128 * 4 + 4 * 32 * 32 * 4
-    assert n(gqa(64, 32, 32, 128, 8192)) == 8              # ragged MHA: no split > 1024 rows
+    assert n(gqa()) == split_cost_model(256, 4096, 512, 128, 64) == 2   # Llama-3-8B: 256 (b, kv) pairs
+    assert ws(gqa()) == 2 * 32 * 32 * 128 * 4 + 2 * 32 * 32 * 4
+    assert n(gqa(64, 32, 32, 128, 8192)) == split_cost_model(2048, 8192, 512, 128, 64) == 1
     assert n(gqa(1, 4, 2, 64, 128, da.DA_DTYPE_F32)) == 1  # tiny: one split, no workspace
     assert ws(gqa(1, 4, 2, 64, 128, da.DA_DTYPE_F32)) == 0
     assert n(gqa(splits=7)) == 7
     assert n(gqa(L=5, splits=9)) == 5                      # never more splits than rows
     m = lambda p: L.da_mla_decode_num_splits(ctypes.byref(p))
-    assert m(mla()) == 4                                   # DeepSeek-V3 B=64: 256 workgroups
-    assert m(mla(4, 128, 32768)) == 64
+    assert m(mla()) == split_cost_model(64, 4096, 256, 128, 128) == 4     # DeepSeek-V3 B=64: 256 workgroups
+    assert m(mla(4, 128, 32768)) == split_cost_model(4, 32768, 256, 128, 128) == 64
+    assert m(mla(48, 128, 4096)) == split_cost_model(48, 4096, 256, 128, 128)
     assert L.da_mla_decode_workspace_size(ctypes.byref(mla())) >= 64 * 128 * 576 * 2
 
 
@@ -150,7 +162,7 @@ def test_mla_and_combine_reject_bad_parameters():
         return L.da_mla_decode_absorbed(ctypes.byref(p), ptr, FAKE, FAKE, None, FAKE, FAKE, FAKE,
                                         None, FAKE, ws_bytes, None)
     for field, val, code in [("kv_lora_rank", 256, 2), ("qk_rope_dim", 32, 2), ("num_heads", 24, 2),
-                             ("num_heads", 256, 2), ("batch", 0, 1), ("cache_stride_t", 512, 1),
+                             ("num_heads", 256, 2), ("num_heads", 80, 2), ("num_heads", 112, 2), ("batch", 0, 1), ("cache_stride_t", 512, 1),
                              ("max_seq_len", -1, 1), ("softmax_scale", 0.0, 2), ("softmax_scale", -0.1, 2),
                              ("softmax_scale", float("nan"), 1)]:
         p = mla()

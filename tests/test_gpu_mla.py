@@ -107,6 +107,8 @@ EDGE = [
     (2, 32, [65, 7]),
     (3, 16, [300, 1, 4097]),
     (5, 128, [2048, 17, 4000, 129, 64]),
+    (2, 48, [700, 33]),              # three-wave shapes
+    (3, 96, [1500, 2, 260]),
 ]
 
 
