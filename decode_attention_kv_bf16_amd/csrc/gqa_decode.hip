@@ -34,6 +34,20 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kEPL = 8;  // elements of a cache row owned by one lane
 
+// Cache rows are read once per launch: non-temporal loads (the `nt` cache
+// policy) stream them without displacing reusable lines, and measured faster
+// on MI355X (about 7.0 vs 6.2 TB/s for a plain streaming read of 512 MiB).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 load_stream(const float4* p) {
+  const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
 template <typename T>
 struct Row8;
 
@@ -43,6 +57,9 @@ struct Row8<uint16_t> {  // bfloat16 stored as bit patterns
     uint4 w;
   };
   static __device__ __forceinline__ Raw load(const uint16_t* p) {
+    return {load_stream(reinterpret_cast<const uint4*>(p))};
+  }
+  static __device__ __forceinline__ Raw load_plain(const uint16_t* p) {
     return {*reinterpret_cast<const uint4*>(p)};
   }
   static __device__ __forceinline__ Raw zero() { return {make_uint4(0u, 0u, 0u, 0u)}; }
@@ -55,6 +72,9 @@ struct Row8<float> {
     float4 a, b;
   };
   static __device__ __forceinline__ Raw load(const float* p) {
+    return {load_stream(reinterpret_cast<const float4*>(p)), load_stream(reinterpret_cast<const float4*>(p) + 1)};
+  }
+  static __device__ __forceinline__ Raw load_plain(const float* p) {
     return {reinterpret_cast<const float4*>(p)[0], reinterpret_cast<const float4*>(p)[1]};
   }
   static __device__ __forceinline__ Raw zero() {
@@ -105,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaArgs a) {
     const T* qp = reinterpret_cast<const T*>(a.q) + b * a.q_sb + col * kEPL;
 #pragma unroll
     for (int i = 0; i < GH; ++i) {
-      R::cvt(R::load(qp + (int64_t)(h0 + i) * a.q_sh), qf[i]);
+      R::cvt(R::load_plain(qp + (int64_t)(h0 + i) * a.q_sh), qf[i]);  // re-read by every split
 #pragma unroll
       for (int e = 0; e < kEPL; ++e) qf[i][e] *= a.scale_log2;
     }
