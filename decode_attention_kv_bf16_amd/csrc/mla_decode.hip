@@ -192,12 +192,12 @@ __global__ __launch_bounds__(64) void mla_absorb_kernel(MlaArgs a) {
       }
     }
   }
-  if (slice == 0) {  // append q_rope (already rotated) unchanged
-    for (int i = lane; i < B * 8; i += 64) {
-      const int b = i >> 3, ch = i & 7;
-      *reinterpret_cast<uint4*>(a.q_hat + ((int64_t)b * H + h) * kRowE + kDc + 8 * ch) =
-          *reinterpret_cast<const uint4*>(a.q_rope + ((int64_t)b * H + h) * 64 + 8 * ch);
-    }
+  // append q_rope (already rotated) unchanged: B x 8 16-byte chunks per head,
+  // spread over the 8 slice workgroups (one chunk per lane up to B = 64)
+  for (int i = slice * 64 + lane; i < B * 8; i += 8 * 64) {
+    const int b = i >> 3, ch = i & 7;
+    *reinterpret_cast<uint4*>(a.q_hat + ((int64_t)b * H + h) * kRowE + kDc + 8 * ch) =
+        *reinterpret_cast<const uint4*>(a.q_rope + ((int64_t)b * H + h) * 64 + 8 * ch);
   }
 }
 
@@ -548,17 +548,32 @@ __global__ __launch_bounds__(512) void mla_merge_project_kernel(MlaArgs a, int n
             if (v != kNegInf) z += exp2_hw(fmaf(v, kLog2e, -m2));
           }
           const float inv_z = 1.0f / z;
-          for (int s = 0; s < a.num_splits; ++s) {
-            const float v = a.part_lse[s * rows + row_id];
-            if (v == kNegInf) continue;
-            const float wgt = exp2_hw(fmaf(v, kLog2e, -m2)) * inv_z;
-            const uint4* src = reinterpret_cast<const uint4*>(a.part_out + (s * rows + row_id) * kDc + 16 * cs);
-            const uint4 u0 = src[0], u1 = src[1];
-            float f[16];
-            unpack_bf16x8(u0, f);
-            unpack_bf16x8(u1, f + 8);
+          // The partial rows are loaded kMergeBatch splits at a time, so their
+          // loads are in flight together. An empty split (lse -inf) was never
+          // written: its row is replaced by zeros rather than skipped.
+          constexpr int kMergeBatch = 4;
+          for (int s0 = 0; s0 < a.num_splits; s0 += kMergeBatch) {
+            uint4 u[kMergeBatch][2];
+            float wgt[kMergeBatch];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[e] = fmaf(wgt, f[e], acc[e]);
+            for (int j = 0; j < kMergeBatch; ++j) {
+              const int s = s0 + j;
+              const float v = s < a.num_splits ? a.part_lse[s * rows + row_id] : kNegInf;
+              wgt[j] = v == kNegInf ? 0.f : exp2_hw(fmaf(v, kLog2e, -m2)) * inv_z;
+              const int s_in = s < a.num_splits ? s : 0;
+              const uint4* src = reinterpret_cast<const uint4*>(a.part_out + (s_in * rows + row_id) * kDc + 16 * cs);
+              u[j][0] = src[0];
+              u[j][1] = src[1];
+            }
+#pragma unroll
+            for (int j = 0; j < kMergeBatch; ++j) {
+              const bool live = wgt[j] != 0.f;
+              float f[16];
+              unpack_bf16x8(live ? u[j][0] : make_uint4(0u, 0u, 0u, 0u), f);
+              unpack_bf16x8(live ? u[j][1] : make_uint4(0u, 0u, 0u, 0u), f + 8);
+#pragma unroll
+              for (int e = 0; e < 16; ++e) acc[e] = fmaf(wgt[j], f[e], acc[e]);
+            }
           }
           lse_out = M + log2_hw(z) * kLn2;
         }
