@@ -12,9 +12,16 @@ several copies of the caches, so that no step finds the previous step's cache
 in the 256 MB last-level (Infinity) cache.
 
 Prints ONE JSON line on stdout. `value` is algorithmic bytes per step (cache
-rows once, queries, weights, outputs) over the step time, in GB/s; the
-`roofline` object covers the dominant kernel, timed with HIP events recorded on
-the stream its launches go to; `cpu_baseline` times the fp64 CPU oracle on a
+rows once, queries, weights, outputs) over the wall time per step of the timed
+region, in GB/s. The timed region has no event between launches: an event
+makes the next kernel wait for the previous one to finish completely, so
+consecutive kernels no longer overlap at their edges. An untimed probe pass
+with an event between every two launches gives the per-kernel breakdown
+(`paths`) and picks the dominant kernel; a roofline pass of K further steps,
+with HIP events on the launch stream around every launch of that kernel, gives
+its average duration for the `roofline` object. Timing events are created
+without the system-scope fence of default events (which writes back and
+invalidates the caches at every event). `cpu_baseline` times the fp64 CPU oracle on a
 bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -41,6 +48,56 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+class HipTimingEvents:
+    """HIP events for timing only, created with hipEventDisableSystemFence.
+
+    A default event performs a system-scope release when it is reached, which
+    writes back and invalidates the GPU caches; on MI355X that costs the
+    stream several microseconds per event and slows the kernel after it. These
+    events skip the fence (their elapsed times are still ordered by the
+    stream). They bind to the HIP runtime torch has already loaded (same
+    soname), and are recorded on the stream the library's launches go to."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        import torch  # noqa: F401  (loads the process's HIP runtime first)
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        vp = ctypes.c_void_p
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [vp, vp]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        self.hip.hipEventDestroy.argtypes = [vp]
+        self.events = []
+
+    def create(self):
+        ev = self.ct.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(self.ct.byref(ev), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.events.append(ev)
+        return ev
+
+    def record(self, ev, stream):
+        rc = self.hip.hipEventRecord(ev, self.ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def close(self):
+        for ev in self.events:
+            self.hip.hipEventDestroy(ev)
+        self.events = []
 
 
 # ----------------------------------------------------------------------------
@@ -181,32 +238,65 @@ def run_gpu(args):
             fn()
     torch.cuda.synchronize()
 
-    # timed region: K steps, events between launches on the launch stream
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
+    hev = HipTimingEvents()
+
+    # Probe pass (untimed, after the warm-up): an event between every two
+    # launches gives the per-kernel breakdown and picks the dominant kernel.
+    n_probe = max(3, min(args.steps, 10))
+    ev = [[hev.create() for _ in range(len(names) + 1)] for _ in range(n_probe)]
+    for i in range(n_probe):
         e = ev[i]
-        e[0].record(stream)
+        hev.record(e[0], stream)
         for j, (_, fn) in enumerate(step_calls(args.warmup + i)):
             fn()
-            e[j + 1].record(stream)
+            hev.record(e[j + 1], stream)
+    torch.cuda.synchronize()
+    per_kernel = {n: float(np.mean([hev.elapsed_ms(ev[i][j], ev[i][j + 1]) for i in range(n_probe)]))
+                  for j, n in enumerate(names)}
+    dom = max(per_kernel, key=per_kernel.get)
+    dom_idx = names.index(dom)
+
+    # Timed region: exactly K steps, synchronised on both sides, with nothing
+    # between the launches (an event between two kernels makes the second wait
+    # for the first to finish completely, so consecutive kernels no longer
+    # overlap at their edges: the step would be measured slower than it runs).
+    step_ev = (hev.create(), hev.create())
+    base = args.warmup + n_probe
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    hev.record(step_ev[0], stream)
+    for i in range(args.steps):
+        for _, fn in step_calls(base + i):
+            fn()
+    hev.record(step_ev[1], stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    per_kernel = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
-                  for j, n in enumerate(names)}
-    ev_step_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][-1]) for i in range(args.steps)]))
+    ev_step_ms = hev.elapsed_ms(*step_ev) / args.steps
+
+    # Roofline pass: K more steps in which events on the launch stream bracket
+    # every launch of the dominant kernel; its average duration.
+    dom_ev = [(hev.create(), hev.create()) for _ in range(args.steps)]
+    base += args.steps
+    for i in range(args.steps):
+        for j, (_, fn) in enumerate(step_calls(base + i)):
+            if j == dom_idx:
+                hev.record(dom_ev[i][0], stream)
+                fn()
+                hev.record(dom_ev[i][1], stream)
+            else:
+                fn()
+    torch.cuda.synchronize()
+    dom_ms = float(np.mean([hev.elapsed_ms(a, b) for a, b in dom_ev]))
+    hev.close()
 
     total_bytes = sum(p[1][1]["total"] for p in plans)
     total_flops = sum(p[1][1]["flops"] for p in plans)
     value = total_bytes / (ms_per_step * 1e-3) / 1e9
     tflops = total_flops / (ms_per_step * 1e-3) / 1e12
 
-    # dominant kernel and its roofline
-    dom = max(per_kernel, key=per_kernel.get)
+    # dominant kernel's roofline
     kind, (calls, alg, info, _) = next(p for p in plans
                                        if any(dom == n for n, _ in p[1][0][0]))
     if dom == "gqa_split_pass":
@@ -215,7 +305,6 @@ def run_gpu(args):
         dom_bytes = alg["cache"]
     else:
         dom_bytes = alg["total"]
-    dom_ms = per_kernel[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -227,7 +316,7 @@ def run_gpu(args):
         ks = [n for n, _ in calls[0]]
         t_ms = sum(per_kernel[n] for n in ks)
         entry = dict(info)
-        entry.update(kernels_us={n: round(per_kernel[n] * 1e3, 2) for n in ks},
+        entry.update(probe_kernels_us={n: round(per_kernel[n] * 1e3, 2) for n in ks},
                      time_us=round(t_ms * 1e3, 2), alg_bytes=int(alg["total"]),
                      alg_gbs=round(alg["total"] / (t_ms * 1e-3) / 1e9, 1),
                      cache_gbs=round(alg["cache"] / (t_ms * 1e-3) / 1e9, 1),
