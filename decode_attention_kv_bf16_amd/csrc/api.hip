@@ -101,11 +101,17 @@ GqaPlan plan_gqa(const da_gqa_params_t* p) {
   if (p->num_splits > 0) {
     s = p->num_splits;
   } else {
-    // Workgroups resident at once: the kernel's occupancy on this device
-    // (2 per CU when no device can be asked); splits no shorter than 128 rows.
-    int bpc = da::gqa_blocks_per_cu(p->dtype == DA_DTYPE_BF16 ? 1 : 0, p->head_dim, pl.heads_per_block);
-    if (bpc < 1) bpc = 2;
-    s = choose_splits(units, p->max_seq_len, (int64_t)bpc * device_cu_count(), 128, 64);
+    // The pass streams the cache once: measured on MI355X, two 4-wave
+    // workgroups per CU (8 waves) already saturate HBM, and further splits
+    // only add partial rows and per-workgroup start-up. So: the fewest splits
+    // that give 2 workgroups per CU, but no chunk longer than 2048 rows (with
+    // ragged lengths the longest sequences set the tail) and none shorter
+    // than 128 rows.
+    s = ceil_div(2LL * device_cu_count(), units);
+    const int64_t s_tail = ceil_div(p->max_seq_len, 2048);
+    s = s > s_tail ? s : s_tail;
+    const int64_t s_max = ceil_div(p->max_seq_len, 128);
+    s = s < s_max ? s : s_max;
   }
   if (s > p->max_seq_len) s = p->max_seq_len;
   if (s < 1) s = 1;

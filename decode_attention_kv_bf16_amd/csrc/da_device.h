@@ -65,6 +65,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(da_f32x2_t{lo, hi}, da_bf16x2_t));
 }
 
+// c + a.lo * b.lo + a.hi * b.hi for packed bf16 pairs (v_dot2c_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(da_bf16x2_t, a), __builtin_bit_cast(da_bf16x2_t, b), c,
+                                         false);
+}
+
 // Merge two online-softmax states (m, l, acc) kept in the base-2 domain:
 // m is the running max of log2-scaled scores, l = sum 2^(s - m).
 // Returns the factors that rescale each side onto the common max.

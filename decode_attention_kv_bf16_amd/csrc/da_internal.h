@@ -29,11 +29,6 @@ struct GqaArgs {
 // dtype: 0 = f32, 1 = bf16 (matches da_dtype_t).
 hipError_t launch_gqa_decode(const GqaArgs& a, int dtype, int head_dim, hipStream_t stream);
 
-// Workgroups of the GQA kernel instantiation for (dtype, head_dim,
-// heads_per_block) that one CU holds at once on the current device; 0 if the
-// device cannot be queried.
-int gqa_blocks_per_cu(int dtype, int head_dim, int heads_per_block);
-
 // Log-sum-exp merge of split partials: rows = B * H.
 hipError_t launch_splitkv_combine(int32_t num_splits, int32_t rows, int32_t head_dim,
                                   const float* part_out, const float* part_lse,

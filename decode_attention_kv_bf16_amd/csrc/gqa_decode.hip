@@ -22,8 +22,6 @@
 //   the 4 waves through LDS.
 //   Scores live in the base-2 domain: q is pre-multiplied by scale*log2(e) so
 //   each softmax weight is one v_exp_f32.
-#include <atomic>
-
 #include "da_device.h"
 #include "da_internal.h"
 
@@ -120,16 +118,29 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaArgs a) {
     return;
   }
 
-  float qf[GH][kEPL];
+  // Queries. bf16: kept as packed pairs, scores by v_dot2c_f32_bf16 straight
+  // from the raw cache words (products of bf16 values are exact in fp32), and
+  // the scale is applied to the reduced score. fp32: converted, pre-scaled.
+  constexpr bool kBf16 = sizeof(T) == 2;
+  uint32_t qp[GH][kEPL / 2];
+  float qf[kBf16 ? 1 : GH][kEPL];
   {
-    const T* qp = reinterpret_cast<const T*>(a.q) + b * a.q_sb + col * kEPL;
+    const T* qsrc = reinterpret_cast<const T*>(a.q) + b * a.q_sb + col * kEPL;
 #pragma unroll
     for (int i = 0; i < GH; ++i) {
-      R::cvt(R::load_plain(qp + (int64_t)(h0 + i) * a.q_sh), qf[i]);  // re-read by every split
+      const typename R::Raw r = R::load_plain(qsrc + (int64_t)(h0 + i) * a.q_sh);  // re-read by every split
+      if constexpr (kBf16) {
+        const uint4 w = *reinterpret_cast<const uint4*>(&r);
+        qp[i][0] = w.x; qp[i][1] = w.y; qp[i][2] = w.z; qp[i][3] = w.w;
+      } else {
+        R::cvt(r, qf[i]);
 #pragma unroll
-      for (int e = 0; e < kEPL; ++e) qf[i][e] *= a.scale_log2;
+        for (int e = 0; e < kEPL; ++e) qf[i][e] *= a.scale_log2;
+      }
     }
   }
+  (void)qp;
+  (void)qf;
 
   float m[GH], l[GH], acc[GH][kEPL];
 #pragma unroll
@@ -156,23 +167,36 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaArgs a) {
         vw[u] = R::zero();
       }
     }
+    // scores (base-2 domain), one per (head, row of this lane group)
     float s[GH][U];
-    float vf[U][kEPL];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float kf[kEPL];
-      R::cvt(kw[u], kf);
-      R::cvt(vw[u], vf[u]);
       const bool valid = base + u * RPW + row < t_end;
+      if constexpr (kBf16) {
+        const uint4 w = *reinterpret_cast<const uint4*>(&kw[u]);
+        const uint32_t kk[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-      for (int i = 0; i < GH; ++i) {
-        float d = 0.f;
+        for (int i = 0; i < GH; ++i) {
+          float d = 0.f;
 #pragma unroll
-        for (int e = 0; e < kEPL; ++e) d = fmaf(qf[i][e], kf[e], d);
-        d = group_sum<LPT>(d);
-        s[i][u] = valid ? d : kNegInf;
+          for (int j = 0; j < 4; ++j) d = dot2_bf16(qp[i][j], kk[j], d);
+          d = group_sum<LPT>(d) * a.scale_log2;
+          s[i][u] = valid ? d : kNegInf;
+        }
+      } else {
+        float kf[kEPL];
+        R::cvt(kw[u], kf);
+#pragma unroll
+        for (int i = 0; i < GH; ++i) {
+          float d = 0.f;
+#pragma unroll
+          for (int e = 0; e < kEPL; ++e) d = fmaf(qf[i][e], kf[e], d);
+          d = group_sum<LPT>(d);
+          s[i][u] = valid ? d : kNegInf;
+        }
       }
     }
+    // online softmax: new running max, rescale, weights (s becomes p)
 #pragma unroll
     for (int i = 0; i < GH; ++i) {
       float mx = m[i];
@@ -185,12 +209,20 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaArgs a) {
       for (int e = 0; e < kEPL; ++e) acc[i][e] *= alpha;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float p = exp2_hw(s[i][u] - mu);
-        l[i] += p;
-#pragma unroll
-        for (int e = 0; e < kEPL; ++e) acc[i][e] = fmaf(p, vf[u][e], acc[i][e]);
+        s[i][u] = exp2_hw(s[i][u] - mu);
+        l[i] += s[i][u];
       }
       m[i] = mx;
+    }
+    // values, one row at a time
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float vf[kEPL];
+      R::cvt(vw[u], vf);
+#pragma unroll
+      for (int i = 0; i < GH; ++i)
+#pragma unroll
+        for (int e = 0; e < kEPL; ++e) acc[i][e] = fmaf(s[i][u], vf[e], acc[i][e]);
     }
   }
 
@@ -275,52 +307,7 @@ hipError_t launch_gh(const GqaArgs& a, hipStream_t st) {
   }
 }
 
-template <typename T, int D, int GH>
-int blocks_per_cu_t() {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&gqa_decode_kernel<T, D, GH>), kThreads, 0) != hipSuccess) {
-    (void)hipGetLastError();
-    return 0;
-  }
-  return n;
-}
-
-template <typename T, int D>
-int blocks_per_cu_gh(int gh) {
-  switch (gh) {
-    case 1: return blocks_per_cu_t<T, D, 1>();
-    case 2: return blocks_per_cu_t<T, D, 2>();
-    case 3: return blocks_per_cu_t<T, D, 3>();
-    case 4: return blocks_per_cu_t<T, D, 4>();
-    case 5: return blocks_per_cu_t<T, D, 5>();
-    case 6: return blocks_per_cu_t<T, D, 6>();
-    case 7: return blocks_per_cu_t<T, D, 7>();
-    case 8: return blocks_per_cu_t<T, D, 8>();
-    default: return 0;
-  }
-}
-
 }  // namespace
-
-int gqa_blocks_per_cu(int dtype, int head_dim, int heads_per_block) {
-  if (heads_per_block < 1 || heads_per_block > 8) return 0;
-  // the answer depends only on the kernel's resources and the device type:
-  // cache it per instantiation
-  static std::atomic<int> cache[2][2][9];
-  const int di = dtype == 1 ? 1 : 0, hi = head_dim == 128 ? 1 : 0;
-  int n = cache[di][hi][heads_per_block].load(std::memory_order_relaxed);
-  if (n > 0) return n;
-  if (dtype == 1) {
-    n = head_dim == 128 ? blocks_per_cu_gh<uint16_t, 128>(heads_per_block)
-                        : blocks_per_cu_gh<uint16_t, 64>(heads_per_block);
-  } else {
-    n = head_dim == 128 ? blocks_per_cu_gh<float, 128>(heads_per_block)
-                        : blocks_per_cu_gh<float, 64>(heads_per_block);
-  }
-  if (n > 0) cache[di][hi][heads_per_block].store(n, std::memory_order_relaxed);
-  return n;
-}
 
 hipError_t launch_gqa_decode(const GqaArgs& a, int dtype, int head_dim, hipStream_t st) {
   if (dtype == 1) {

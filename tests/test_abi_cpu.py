@@ -90,14 +90,16 @@ def split_cost_model(units, length, slots, min_rows, overhead):
 
 
 def test_split_planning_without_a_device():
-    # with no device the planner assumes a full MI355X (256 CUs) and an
-    # occupancy of 2 GQA / 1 MLA workgroups per CU
+    # with no device the planner assumes a full MI355X (256 CUs) and, for
+    # MLA, an occupancy of 1 workgroup per CU
     L = da.lib()
     n = lambda p: L.da_gqa_decode_num_splits(ctypes.byref(p))
     ws = lambda p: L.da_gqa_decode_workspace_size(ctypes.byref(p))
-    assert n(gqa()) == split_cost_model(256, 4096, 512, 128, 64) == 2   # Llama-3-8B: 256 (b, kv) pairs
+    # GQA: fewest splits giving 2 workgroups per CU, chunks of at most 2048 rows
+    assert n(gqa()) == 2                                   # Llama-3-8B: 256 (b, kv) pairs x 2 = 512
     assert ws(gqa()) == 2 * 32 * 32 * 128 * 4 + 2 * 32 * 32 * 4
-    assert n(gqa(64, 32, 32, 128, 8192)) == split_cost_model(2048, 8192, 512, 128, 64) == 1
+    assert n(gqa(64, 32, 32, 128, 8192)) == 4              # ragged MHA: 2048 units, 2048-row chunks
+    assert n(gqa(8, 8, 1, 128, 4096)) == 32                # MQA B=8: 8 units; chunks no shorter than 128 rows
     assert n(gqa(1, 4, 2, 64, 128, da.DA_DTYPE_F32)) == 1  # tiny: one split, no workspace
     assert ws(gqa(1, 4, 2, 64, 128, da.DA_DTYPE_F32)) == 0
     assert n(gqa(splits=7)) == 7
