@@ -23,8 +23,34 @@ __device__ __forceinline__ float dpp_mov(float v) {
 
 constexpr int kDppQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]: lane ^ 1
 constexpr int kDppQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppQuadReverse = 0x1B; // quad_perm [3,2,1,0]: lane i <- 3 - i within 4
 constexpr int kDppRowHalfMirror = 0x141;  // lane i <- 7 - i within 8
 constexpr int kDppRowMirror = 0x140;      // lane i <- 15 - i within 16
+constexpr int kDppRowRor4 = 0x124;        // rotate by 4 within 16
+constexpr int kDppRowRor8 = 0x128;        // rotate by 8 within 16
+// Every lane of a row of 16 receives the value of lane n of that row (DPP
+// row_newbcast). n must be a compile-time constant after unrolling: the
+// switch then folds to one move.
+__device__ __forceinline__ float row_bcast(int n, float v) {
+  switch (n) {
+    case 0: return dpp_mov<0x150>(v);
+    case 1: return dpp_mov<0x151>(v);
+    case 2: return dpp_mov<0x152>(v);
+    case 3: return dpp_mov<0x153>(v);
+    case 4: return dpp_mov<0x154>(v);
+    case 5: return dpp_mov<0x155>(v);
+    case 6: return dpp_mov<0x156>(v);
+    case 7: return dpp_mov<0x157>(v);
+    case 8: return dpp_mov<0x158>(v);
+    case 9: return dpp_mov<0x159>(v);
+    case 10: return dpp_mov<0x15A>(v);
+    case 11: return dpp_mov<0x15B>(v);
+    case 12: return dpp_mov<0x15C>(v);
+    case 13: return dpp_mov<0x15D>(v);
+    case 14: return dpp_mov<0x15E>(v);
+    default: return dpp_mov<0x15F>(v);
+  }
+}
 
 // Sum over aligned groups of N consecutive lanes (N in 1, 2, 4, 8, 16); every
 // lane of the group receives the group total.

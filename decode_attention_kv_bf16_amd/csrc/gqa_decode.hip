@@ -84,6 +84,37 @@ struct Row8<float> {
   }
 };
 
+// One stage of a reduce-scatter over the 16 lanes of a row: lanes are paired
+// by the DPP pattern CTRL (each pair has one "high" lane); of the n values
+// of a lane, the low lane keeps the sums of the first n/2 and the high lane
+// those of the last n/2. With n = 1 the stage is a plain pairwise sum.
+template <int CTRL, int N>
+__device__ __forceinline__ void reduce_scatter_stage(float* v, bool high) {
+  if constexpr (N >= 2) {
+#pragma unroll
+    for (int j = 0; j < N / 2; ++j) {
+      const float lo = v[j], hi = v[j + N / 2];
+      const float keep = high ? hi : lo;
+      const float send = high ? lo : hi;
+      v[j] = keep + dpp_mov<CTRL>(send);
+    }
+  } else {
+    v[0] += dpp_mov<CTRL>(v[0]);
+  }
+}
+
+// Lane (of a row of 16) that holds, after the reduce-scatter, the score of
+// token u (of the 4 a row group handles per step) for head h, and the index
+// of that score among the lane's values.
+template <int GH>
+__device__ __forceinline__ constexpr int rs_src_lane(int u, int h) {
+  return 4 * u + (GH >= 4 ? h / (GH / 4) : h * (4 / GH));
+}
+template <int GH>
+__device__ __forceinline__ constexpr int rs_src_reg(int h) {
+  return GH >= 4 ? h % (GH / 4) : 0;
+}
+
 template <typename T, int D, int GH>
 __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaArgs a) {
   constexpr int LPT = D / kEPL;   // lanes per cache row
@@ -151,6 +182,25 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaArgs a) {
     for (int e = 0; e < kEPL; ++e) acc[i][e] = 0.f;
   }
 
+  // bf16 rows of 128 with 1, 2, 4 or 8 heads per workgroup: the U x GH
+  // partial dot products of a lane are reduce-scattered over the 16 lanes of
+  // its row group, so each lane finishes kRsV (token, head) scores itself and
+  // takes one exponential per score instead of the whole row group repeating
+  // all of them. Lane c of a group then holds token u = c / 4 of the step.
+  // The running max and sum live with those scores; weights and rescale
+  // factors reach the lanes that hold the values by row broadcasts.
+  constexpr bool kRS = kBf16 && D == 128 && (GH == 1 || GH == 2 || GH == 4 || GH == 8);
+  constexpr int kRsN = U * GH;
+  constexpr int kRsV = kRsN >= 16 ? kRsN / 16 : 1;
+  float ms[kRsV], ls[kRsV];
+#pragma unroll
+  for (int k = 0; k < kRsV; ++k) {
+    ms[k] = kNegInf;
+    ls[k] = 0.f;
+  }
+  (void)ms;
+  (void)ls;
+
   const T* kp = reinterpret_cast<const T*>(a.k) + b * a.kv_sb + kvh * a.kv_sh + col * kEPL;
   const T* vp = reinterpret_cast<const T*>(a.v) + b * a.kv_sb + kvh * a.kv_sh + col * kEPL;
 
@@ -166,6 +216,61 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaArgs a) {
         kw[u] = R::zero();
         vw[u] = R::zero();
       }
+    }
+    if constexpr (kRS) {
+      float v[kRsN];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint4 w = *reinterpret_cast<const uint4*>(&kw[u]);
+        const uint32_t kk[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < GH; ++i) {
+          float d = 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) d = dot2_bf16(qp[i][j], kk[j], d);
+          v[u * GH + i] = d;
+        }
+      }
+      reduce_scatter_stage<kDppRowMirror, kRsN>(v, col >= 8);
+      reduce_scatter_stage<kDppRowHalfMirror, (kRsN >= 2 ? kRsN / 2 : 1)>(v, (col & 4) != 0);
+      reduce_scatter_stage<kDppQuadReverse, (kRsN >= 4 ? kRsN / 4 : 1)>(v, (col & 2) != 0);
+      reduce_scatter_stage<kDppQuadSwap1, (kRsN >= 8 ? kRsN / 8 : 1)>(v, (col & 1) != 0);
+      const bool valid = base + (col >> 2) * RPW + row < t_end;
+      float p[kRsV], alpha[kRsV];
+      bool moved = false;
+#pragma unroll
+      for (int k = 0; k < kRsV; ++k) {
+        const float sc = valid ? v[k] * a.scale_log2 : kNegInf;
+        float mx = fmaxf(sc, dpp_mov<kDppRowRor4>(sc));   // the group's 4 tokens of this head
+        mx = fmaxf(mx, dpp_mov<kDppRowRor8>(mx));
+        const float mn = fmaxf(ms[k], mx);
+        const float mu = (mn == kNegInf) ? 0.f : mn;
+        alpha[k] = exp2_hw(ms[k] - mu);
+        p[k] = exp2_hw(sc - mu);
+        ls[k] = ls[k] * alpha[k] + p[k];
+        moved |= mn != ms[k];
+        ms[k] = mn;
+      }
+      if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+#pragma unroll
+        for (int i = 0; i < GH; ++i) {
+          const float al = row_bcast(rs_src_lane<GH>(0, i), alpha[rs_src_reg<GH>(i)]);
+#pragma unroll
+          for (int e = 0; e < kEPL; ++e) acc[i][e] *= al;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float vf[kEPL];
+        R::cvt(vw[u], vf);
+#pragma unroll
+        for (int i = 0; i < GH; ++i) {
+          const float pb = row_bcast(rs_src_lane<GH>(u, i), p[rs_src_reg<GH>(i)]);
+#pragma unroll
+          for (int e = 0; e < kEPL; ++e) acc[i][e] = fmaf(pb, vf[e], acc[i][e]);
+        }
+      }
+      continue;
     }
     // scores (base-2 domain), one per (head, row of this lane group)
     float s[GH][U];
@@ -223,6 +328,21 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaArgs a) {
       for (int i = 0; i < GH; ++i)
 #pragma unroll
         for (int e = 0; e < kEPL; ++e) acc[i][e] = fmaf(s[i][u], vf[e], acc[i][e]);
+    }
+  }
+
+  if constexpr (kRS) {
+    // per-head running max and sum of this row group, in every lane: the sum
+    // over the group's 4 token lanes, then broadcast from the head's lane
+#pragma unroll
+    for (int k = 0; k < kRsV; ++k) {
+      ls[k] += dpp_mov<kDppRowRor4>(ls[k]);
+      ls[k] += dpp_mov<kDppRowRor8>(ls[k]);
+    }
+#pragma unroll
+    for (int i = 0; i < GH; ++i) {
+      m[i] = row_bcast(rs_src_lane<GH>(0, i), ms[rs_src_reg<GH>(i)]);
+      l[i] = row_bcast(rs_src_lane<GH>(0, i), ls[rs_src_reg<GH>(i)]);
     }
   }
 

@@ -139,15 +139,19 @@ __device__ __forceinline__ void buffer_load_to_lds16(__amdgpu_buffer_rsrc_t rsrc
 // ---------------------------------------------------------------------------
 // 1. query absorption
 // ---------------------------------------------------------------------------
-// grid (8 slices of 64 latent columns, H); one wave. Computes the transpose
+// 8 slices of 64 latent columns per head; one wave each. Computes the transpose
 // q~^T[c, b] = sum_e W_UK[h, c, e] q_nope[b, h, e] so that each lane ends up
 // with 4 consecutive latent columns of one batch row (one 8-byte store).
 // Both operands are read in their stored layout (e contiguous).
 constexpr int kAbsorbBatch = 64;   // batch rows per pass (4 blocks of 16)
 
 __global__ __launch_bounds__(64) void mla_absorb_kernel(MlaArgs a) {
-  const int slice = blockIdx.x;
-  const int h = blockIdx.y;
+  // Workgroups are dealt to the 8 XCDs round-robin by linear id; this mapping
+  // puts the 8 slices of a head on one XCD, so its q_nope column is fetched
+  // from HBM once and then served by that XCD's L2.
+  const int id = blockIdx.x;
+  const int slice = (id >> 3) & 7;
+  const int h = (id & 7) + 8 * (id >> 6);
   const int H = a.num_heads;
   const int B = a.batch;
   const int lane = threadIdx.x;
@@ -615,7 +619,7 @@ __global__ __launch_bounds__(512) void mla_merge_project_kernel(MlaArgs a, int n
 }  // namespace
 
 hipError_t launch_mla_absorb(const MlaArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(mla_absorb_kernel, dim3(8, a.num_heads), dim3(64), 0, st, a);
+  hipLaunchKernelGGL(mla_absorb_kernel, dim3(8 * a.num_heads), dim3(64), 0, st, a);  // H is a multiple of 8
   return hipGetLastError();
 }
 
