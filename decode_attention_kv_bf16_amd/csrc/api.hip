@@ -88,7 +88,7 @@ int64_t choose_splits(int64_t units, int64_t len, int64_t slots, int64_t min_row
 }
 
 struct GqaPlan {
-  int splits, chunk, heads_per_block;
+  int splits, chunk, heads_per_block, waves_per_block;
   size_t part_out_bytes, part_lse_bytes, workspace;
 };
 
@@ -97,19 +97,33 @@ GqaPlan plan_gqa(const da_gqa_params_t* p) {
   const int group = p->num_q_heads / p->num_kv_heads;
   pl.heads_per_block = gqa_heads_per_block(group);
   const int64_t units = (int64_t)p->batch * p->num_kv_heads * (group / pl.heads_per_block);
+  // The pass streams the cache once and is bound by HBM. Measured on MI355X:
+  // 8-16 waves per CU saturate it; every split beyond that only adds partial
+  // rows, a merge and per-workgroup start-up; and with many units the
+  // hardware's workgroup dispatch balances ragged lengths better than
+  // splitting does. Work units are (sequence, KV head, head group).
+  //  * at least 2 units per CU: one split, 4-wave workgroups;
+  //  * at least half a unit per CU: 4-wave workgroups, splits for 2 per CU;
+  //  * fewer units (small batches, few KV heads): 16-wave workgroups, one per
+  //    CU, as many splits as fit in one round (where that shape is built).
+  // Chunks stay at least 128 rows.
+  const int64_t cus = device_cu_count();
+  const bool wide = da::gqa_wide_supported(p->dtype == DA_DTYPE_BF16 ? 1 : 0, pl.heads_per_block);
   int64_t s;
   if (p->num_splits > 0) {
     s = p->num_splits;
+    pl.waves_per_block = (wide && 2 * units < cus && units * s <= cus) ? 16 : 4;
+  } else if (units >= 2 * cus) {
+    pl.waves_per_block = 4;
+    s = 1;
+  } else if (2 * units >= cus || !wide) {
+    pl.waves_per_block = 4;
+    s = ceil_div(2 * cus, units);
   } else {
-    // The pass streams the cache once: measured on MI355X, two 4-wave
-    // workgroups per CU (8 waves) already saturate HBM, and further splits
-    // only add partial rows and per-workgroup start-up. So: the fewest splits
-    // that give 2 workgroups per CU, but no chunk longer than 2048 rows (with
-    // ragged lengths the longest sequences set the tail) and none shorter
-    // than 128 rows.
-    s = ceil_div(2LL * device_cu_count(), units);
-    const int64_t s_tail = ceil_div(p->max_seq_len, 2048);
-    s = s > s_tail ? s : s_tail;
+    pl.waves_per_block = 16;
+    s = cus / units;
+  }
+  if (p->num_splits == 0) {
     const int64_t s_max = ceil_div(p->max_seq_len, 128);
     s = s < s_max ? s : s_max;
   }
@@ -250,6 +264,7 @@ da::GqaArgs gqa_args(const da_gqa_params_t* p, const GqaPlan& pl, const void* q,
   a.num_kv_heads = p->num_kv_heads;
   a.group = p->num_q_heads / p->num_kv_heads;
   a.heads_per_block = pl.heads_per_block;
+  a.waves_per_block = pl.waves_per_block;
   a.max_seq_len = p->max_seq_len;
   a.num_splits = pl.splits;
   a.chunk = pl.chunk;

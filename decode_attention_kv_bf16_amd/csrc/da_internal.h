@@ -22,12 +22,16 @@ struct GqaArgs {
   int64_t kv_sb, kv_st, kv_sh;
   int32_t batch, num_q_heads, num_kv_heads, group;   // group = Hq / Hkv
   int32_t heads_per_block;   // query heads one workgroup serves (divides group)
+  int32_t waves_per_block;   // 4 or 16
   int32_t max_seq_len, num_splits, chunk;            // chunk = tokens per split
   float scale_log2;          // softmax_scale * log2(e)
 };
 
 // dtype: 0 = f32, 1 = bf16 (matches da_dtype_t).
 hipError_t launch_gqa_decode(const GqaArgs& a, int dtype, int head_dim, hipStream_t stream);
+
+// Whether 16-wave workgroups exist for this dtype and heads per workgroup.
+bool gqa_wide_supported(int dtype, int heads_per_block);
 
 // Log-sum-exp merge of split partials: rows = B * H.
 hipError_t launch_splitkv_combine(int32_t num_splits, int32_t rows, int32_t head_dim,

@@ -28,8 +28,6 @@
 namespace da {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
 constexpr int kEPL = 8;  // elements of a cache row owned by one lane
 
 // Cache rows are read once per launch: non-temporal loads (the `nt` cache
@@ -115,8 +113,9 @@ __device__ __forceinline__ constexpr int rs_src_reg(int h) {
   return GH >= 4 ? h % (GH / 4) : 0;
 }
 
-template <typename T, int D, int GH>
-__global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaArgs a) {
+template <typename T, int D, int GH, int kWaves>
+__global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
+  constexpr int kThreads = kWaves * 64;
   constexpr int LPT = D / kEPL;   // lanes per cache row
   constexpr int RPW = 64 / LPT;   // rows covered by one wave-wide load
   constexpr int U = 16 / RPW;     // rows per lane per step
@@ -405,10 +404,24 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaArgs a) {
   }
 }
 
+// 16-wave workgroups hold at most 128 registers per lane: built only for the
+// instantiations that fit without spilling.
+template <typename T, int GH>
+constexpr bool wide_fits() {
+  return sizeof(T) == 2 ? GH <= 5 : GH <= 2;
+}
+
 template <typename T, int D, int GH>
 hipError_t launch_t(const GqaArgs& a, hipStream_t st) {
   const dim3 grid(a.num_splits, a.num_kv_heads * (a.group / GH), a.batch);
-  hipLaunchKernelGGL((gqa_decode_kernel<T, D, GH>), grid, dim3(kThreads), 0, st, a);
+  if constexpr (wide_fits<T, GH>()) {
+    if (a.waves_per_block == 16) {
+      hipLaunchKernelGGL((gqa_decode_kernel<T, D, GH, 16>), grid, dim3(16 * 64), 0, st, a);
+      return hipGetLastError();
+    }
+  }
+  if (a.waves_per_block != 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gqa_decode_kernel<T, D, GH, 4>), grid, dim3(4 * 64), 0, st, a);
   return hipGetLastError();
 }
 
@@ -428,6 +441,10 @@ hipError_t launch_gh(const GqaArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+bool gqa_wide_supported(int dtype, int heads_per_block) {
+  return dtype == 1 ? heads_per_block <= 5 : heads_per_block <= 2;
+}
 
 hipError_t launch_gqa_decode(const GqaArgs& a, int dtype, int head_dim, hipStream_t st) {
   if (dtype == 1) {

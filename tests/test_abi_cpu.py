@@ -95,11 +95,15 @@ def test_split_planning_without_a_device():
     L = da.lib()
     n = lambda p: L.da_gqa_decode_num_splits(ctypes.byref(p))
     ws = lambda p: L.da_gqa_decode_workspace_size(ctypes.byref(p))
-    # GQA: fewest splits giving 2 workgroups per CU, chunks of at most 2048 rows
-    assert n(gqa()) == 2                                   # Llama-3-8B: 256 (b, kv) pairs x 2 = 512
+    # GQA, with units = (b, kv head, head group): >= 2 per CU -> one split;
+    # >= half a CU's worth -> 4-wave workgroups, 2 per CU; fewer -> 16-wave
+    # workgroups, one per CU; chunks no shorter than 128 rows
+    assert n(gqa()) == 2                                   # Llama-3-8B: 256 units -> 512 workgroups
     assert ws(gqa()) == 2 * 32 * 32 * 128 * 4 + 2 * 32 * 32 * 4
-    assert n(gqa(64, 32, 32, 128, 8192)) == 4              # ragged MHA: 2048 units, 2048-row chunks
-    assert n(gqa(8, 8, 1, 128, 4096)) == 32                # MQA B=8: 8 units; chunks no shorter than 128 rows
+    assert n(gqa(64, 32, 32, 128, 8192)) == 1              # ragged MHA: 2048 units
+    assert n(gqa(16, 32, 8, 128, 4096)) == 4               # 128 units -> 4 splits
+    assert n(gqa(4, 32, 8, 128, 4096)) == 8                # 32 units -> 16-wave, 8 splits
+    assert n(gqa(8, 8, 1, 128, 4096)) == 32                # MQA B=8: 8 units (8 heads: 4-wave), 128-row floor
     assert n(gqa(1, 4, 2, 64, 128, da.DA_DTYPE_F32)) == 1  # tiny: one split, no workspace
     assert ws(gqa(1, 4, 2, 64, 128, da.DA_DTYPE_F32)) == 0
     assert n(gqa(splits=7)) == 7
@@ -144,7 +148,8 @@ def test_gqa_rejects_bad_parameters(mutate, code):
 @needs_lib
 @cpu_only
 def test_gqa_rejects_bad_pointers_and_workspace():
-    p = gqa()
+    p = gqa(16, 32, 8, 128, 4096)        # planned with 2 splits: needs a workspace
+    assert da.lib().da_gqa_decode_workspace_size(ctypes.byref(p)) > 0
     assert call_gqa(None) == 1
     assert call_gqa(p, q=None) == 1
     assert call_gqa(p, out=None) == 1
