@@ -531,37 +531,50 @@ __global__ __launch_bounds__(512) void mla_merge_project_kernel(MlaArgs a, int n
   for (int bbi = 0; bbi < bpg; ++bbi) {
     const int bb = grp * bpg + bbi;
     if (bb >= nbb) break;
-    // merge the splits: thread -> (row r, 16 columns)
+    // Merge the splits: thread (slot r, 16 columns). With R < 16 valid rows in
+    // the block, G = the largest power of two with G R <= 16 slots serve one
+    // row, slot group g summing the splits s = g (mod G); the G partial rows
+    // are then added through LDS. The weights exp(lse_s - lse) use all splits.
     {
+      const int R = min(16, B - bb * 16);
+      int G = 1;
+      while (2 * G * R <= 16) G *= 2;
       const int r = tid >> 5;
       const int cs = tid & 31;
-      const int bidx = bb * 16 + r;
+      const int rr = r / G, g = r % G;
+      const int bidx = bb * 16 + rr;
       float acc[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-      if (bidx < B) {
+      if (rr < R) {
         const int64_t row_id = (int64_t)bidx * H + h;
+        // max and normaliser of the split lse values: the 32 threads of the
+        // row (one half-wave) read every 32nd split each and combine
         float M = kNegInf;
-        for (int s = 0; s < a.num_splits; ++s) M = fmaxf(M, a.part_lse[s * rows + row_id]);
+        for (int s = cs; s < a.num_splits; s += 32) M = fmaxf(M, a.part_lse[s * rows + row_id]);
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
         float lse_out = kNegInf;
         if (M != kNegInf) {
           const float m2 = M * kLog2e;
           float z = 0.f;
-          for (int s = 0; s < a.num_splits; ++s) {
+          for (int s = cs; s < a.num_splits; s += 32) {
             const float v = a.part_lse[s * rows + row_id];
             if (v != kNegInf) z += exp2_hw(fmaf(v, kLog2e, -m2));
           }
+#pragma unroll
+          for (int off = 1; off < 32; off <<= 1) z += __shfl_xor(z, off);
           const float inv_z = 1.0f / z;
-          // The partial rows are loaded kMergeBatch splits at a time, so their
-          // loads are in flight together. An empty split (lse -inf) was never
-          // written: its row is replaced by zeros rather than skipped.
+          // the partial rows are loaded kMergeBatch splits at a time, so their
+          // loads are in flight together; an empty split (lse -inf) was never
+          // written: its row is replaced by zeros rather than skipped
           constexpr int kMergeBatch = 4;
-          for (int s0 = 0; s0 < a.num_splits; s0 += kMergeBatch) {
+          for (int s0 = g; s0 < a.num_splits; s0 += kMergeBatch * G) {
             uint4 u[kMergeBatch][2];
             float wgt[kMergeBatch];
 #pragma unroll
             for (int j = 0; j < kMergeBatch; ++j) {
-              const int s = s0 + j;
+              const int s = s0 + j * G;
               const float v = s < a.num_splits ? a.part_lse[s * rows + row_id] : kNegInf;
               wgt[j] = v == kNegInf ? 0.f : exp2_hw(fmaf(v, kLog2e, -m2)) * inv_z;
               const int s_in = s < a.num_splits ? s : 0;
@@ -581,16 +594,40 @@ __global__ __launch_bounds__(512) void mla_merge_project_kernel(MlaArgs a, int n
           }
           lse_out = M + log2_hw(z) * kLn2;
         }
-        if (cs == 0 && a.lse) a.lse[row_id] = lse_out;
+        if (g == 0 && cs == 0 && a.lse) a.lse[row_id] = lse_out;
       }
+      auto store_row = [&](int slot, const float* v) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        u32x4_t v;
-        v.x = cvt_bf16x2(acc[8 * j + 0], acc[8 * j + 1]);
-        v.y = cvt_bf16x2(acc[8 * j + 2], acc[8 * j + 3]);
-        v.z = cvt_bf16x2(acc[8 * j + 4], acc[8 * j + 5]);
-        v.w = cvt_bf16x2(acc[8 * j + 6], acc[8 * j + 7]);
-        *reinterpret_cast<LDS u32x4_t*>(o_lds + r * kORowB + 2 * (16 * cs + 8 * j)) = v;
+        for (int j = 0; j < 2; ++j) {
+          u32x4_t w;
+          w.x = cvt_bf16x2(v[8 * j + 0], v[8 * j + 1]);
+          w.y = cvt_bf16x2(v[8 * j + 2], v[8 * j + 3]);
+          w.z = cvt_bf16x2(v[8 * j + 4], v[8 * j + 5]);
+          w.w = cvt_bf16x2(v[8 * j + 6], v[8 * j + 7]);
+          *reinterpret_cast<LDS u32x4_t*>(o_lds + slot * kORowB + 2 * (16 * cs + 8 * j)) = w;
+        }
+      };
+      store_row(r, acc);
+      if (G > 1) {  // add the G partial rows of each valid row into slot rr
+        __syncthreads();
+        float fin[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) fin[e] = 0.f;
+        if (g == 0 && rr < R) {
+          for (int gg = 0; gg < G; ++gg) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const u32x4_t w =
+                  *reinterpret_cast<const LDS u32x4_t*>(o_lds + (rr * G + gg) * kORowB + 2 * (16 * cs + 8 * j));
+              float f[8];
+              unpack_bf16x8(uint4{w.x, w.y, w.z, w.w}, f);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) fin[8 * j + e] += f[e];
+            }
+          }
+        }
+        __syncthreads();
+        if (g == 0) store_row(rr, fin);
       }
     }
     wait_vm_all();
