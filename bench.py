@@ -184,7 +184,7 @@ def setup_mla(cfg):
     S = None
     for c in caches:
         absorb, attend, merge, _, _, bufs = da.mla_stages(qn, qr, c, wuk, wuv, sl, inp.scale)
-        S = bufs["part_out"].shape[0]
+        S = da.mla_num_splits(qn, qr, c, wuv) or "balanced"
         calls.append([("mla_absorb", absorb), ("mla_attend", attend), ("mla_merge_project", merge)])
     B, H, _ = qn.shape
     alg = mla_alg(B, H, int(inp.seq_lens.sum()))

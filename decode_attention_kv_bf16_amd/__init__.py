@@ -72,6 +72,8 @@ _SIGNATURES = {
                                      _vp, ctypes.c_size_t, _vp]),
     "da_mla_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MlaParams)]),
     "da_mla_decode_num_splits": (ctypes.c_int32, [ctypes.POINTER(MlaParams)]),
+    "da_mla_partials_size": (ctypes.c_int, [ctypes.POINTER(MlaParams), ctypes.POINTER(ctypes.c_size_t),
+                                            ctypes.POINTER(ctypes.c_size_t)]),
     "da_mla_decode_absorbed": (ctypes.c_int, [ctypes.POINTER(MlaParams), _vp, _vp, _vp, _vp, _vp,
                                               _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "da_mla_absorb_query": (ctypes.c_int, [ctypes.POINTER(MlaParams), _vp, _vp, _vp, _vp, _vp]),
@@ -317,13 +319,15 @@ def mla_stages(q_nope, q_rope, kv_cache, w_uk, w_uv, seq_lens=None, softmax_scal
     as mla_decode_absorbed does."""
     p = mla_params(q_nope, kv_cache, w_uv, q_rope, softmax_scale, num_splits)
     L = lib()
-    S = int(L.da_mla_decode_num_splits(ctypes.byref(p)))
+    po_bytes, pl_bytes = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(L.da_mla_partials_size(ctypes.byref(p), ctypes.byref(po_bytes), ctypes.byref(pl_bytes)),
+           "da_mla_partials_size")
     B, H, _ = q_nope.shape
-    d_c = kv_cache.shape[2] - q_rope.shape[2]
     dev = q_nope.device
     q_hat = torch.empty((B, H, kv_cache.shape[2]), dtype=torch.bfloat16, device=dev)
-    part_out = torch.empty((S, B, H, d_c), dtype=torch.bfloat16, device=dev)
-    part_lse = torch.empty((S, B, H), dtype=torch.float32, device=dev)
+    # opaque partial buffers (slots of o~_s and lse_s; the library's layout)
+    part_out = torch.empty((po_bytes.value,), dtype=torch.uint8, device=dev)
+    part_lse = torch.empty((pl_bytes.value // 4,), dtype=torch.float32, device=dev)
     out = torch.empty((B, H, w_uv.shape[2]), dtype=torch.float32, device=dev)
     lse = torch.empty((B, H), dtype=torch.float32, device=dev)
 
@@ -345,6 +349,8 @@ def mla_stages(q_nope, q_rope, kv_cache, w_uk, w_uv, seq_lens=None, softmax_scal
 
 
 def mla_num_splits(q_nope, q_rope, kv_cache, w_uv, num_splits: int = 0) -> int:
+    """Fixed split count per sequence, or 0 when the splits are balanced on the
+    device from the sequence lengths."""
     p = mla_params(q_nope, kv_cache, w_uv, q_rope, None, num_splits)
     return int(lib().da_mla_decode_num_splits(ctypes.byref(p)))
 

@@ -173,37 +173,56 @@ da_status_t check_mla_params(const da_mla_params_t* p) {
 }
 
 struct MlaPlan {
-  int splits, chunk;
-  size_t q_hat_bytes, part_out_bytes, part_lse_bytes, workspace;
+  int splits, chunk;   // fixed splits; splits == 0: balanced on the device
+  int wg_budget, slots;
+  size_t q_hat_bytes, part_out_bytes, part_lse_bytes, table_bytes, workspace;
 };
 
 MlaPlan plan_mla(const da_mla_params_t* p) {
   MlaPlan pl{};
-  int64_t s;
-  if (p->num_splits > 0) {
-    s = p->num_splits;
-  } else {
-    // One workgroup serves all heads of a split of one sequence; resident
-    // workgroups from the kernel's occupancy (1 per CU when no device can be
-    // asked); splits no shorter than 128 rows, and a fixed cost of about 128
-    // rows per workgroup (loading its queries, writing its partials).
-    int bpc = da::mla_attend_blocks_per_cu(p->num_heads);
-    if (bpc < 1) bpc = 1;
-    s = choose_splits(p->batch, p->max_seq_len, (int64_t)bpc * device_cu_count(), 128, 128);
-  }
-  // a split's rows are addressed with 32-bit byte offsets: keep each split
-  // below 2 GiB of cache
+  // One workgroup serves all heads of a split of one sequence; resident
+  // workgroups from the kernel's occupancy (1 per CU when no device can be
+  // asked).
+  int bpc = da::mla_attend_blocks_per_cu(p->num_heads);
+  if (bpc < 1) bpc = 1;
+  const int64_t budget = (int64_t)bpc * device_cu_count();
   const int64_t row_bytes = p->cache_stride_t * 2;
-  const int64_t s_min = ceil_div((int64_t)p->max_seq_len * row_bytes, (int64_t)1 << 31);
-  if (s < s_min) s = s_min;
-  if (s > p->max_seq_len) s = p->max_seq_len;
-  if (s < 1) s = 1;
-  pl.chunk = (int)ceil_div(p->max_seq_len, s);
-  pl.splits = (int)ceil_div(p->max_seq_len, pl.chunk);
+  // Balanced splits when the batch alone cannot fill the GPU (and B <= 512,
+  // what the device-side assignment handles): the split
+  // sizes then follow the actual lengths (device-side), so ragged batches
+  // keep every workgroup equally busy. A split's rows are addressed with
+  // 32-bit byte offsets: its chunk must stay below 2 GiB of cache.
+  const int64_t max_tiles = (int64_t)p->batch * ceil_div(p->max_seq_len, 32);
+  const int64_t max_chunk_rows = 32 * ceil_div(max_tiles, budget);
+  if (p->num_splits == 0 && p->batch < budget && p->batch <= 512 &&
+      max_chunk_rows * row_bytes < ((int64_t)1 << 31)) {
+    pl.splits = 0;
+    pl.chunk = 0;
+    pl.wg_budget = (int)budget;
+    pl.slots = (int)(budget + p->batch);
+  } else {
+    int64_t s;
+    if (p->num_splits > 0) {
+      s = p->num_splits;
+    } else {
+      // splits no shorter than 128 rows, and a fixed cost of about 128 rows
+      // per workgroup (loading its queries, writing its partials)
+      s = choose_splits(p->batch, p->max_seq_len, budget, 128, 128);
+    }
+    const int64_t s_min = ceil_div((int64_t)p->max_seq_len * row_bytes, (int64_t)1 << 31);
+    if (s < s_min) s = s_min;
+    if (s > p->max_seq_len) s = p->max_seq_len;
+    if (s < 1) s = 1;
+    pl.chunk = (int)ceil_div(p->max_seq_len, s);
+    pl.splits = (int)ceil_div(p->max_seq_len, pl.chunk);
+    pl.wg_budget = 0;
+    pl.slots = pl.splits * p->batch;
+  }
   const size_t rows = (size_t)p->batch * p->num_heads;
   pl.q_hat_bytes = round_up(rows * (kMlaDc + kMlaRope) * 2, 256);
-  pl.part_out_bytes = round_up((size_t)pl.splits * rows * kMlaDc * 2, 256);  // bf16
-  pl.part_lse_bytes = round_up((size_t)pl.splits * rows * sizeof(float), 256);
+  pl.part_out_bytes = round_up((size_t)pl.slots * p->num_heads * kMlaDc * 2, 256);  // bf16
+  pl.table_bytes = pl.splits == 0 ? round_up((size_t)p->batch * 2 * sizeof(int32_t), 256) : 0;
+  pl.part_lse_bytes = round_up((size_t)pl.slots * p->num_heads * sizeof(float), 256) + pl.table_bytes;
   pl.workspace = pl.q_hat_bytes + pl.part_out_bytes + pl.part_lse_bytes;
   return pl;
 }
@@ -243,8 +262,19 @@ da::MlaArgs mla_args(const da_mla_params_t* p, const MlaPlan& pl) {
   a.max_seq_len = p->max_seq_len;
   a.num_splits = pl.splits;
   a.chunk = pl.chunk;
+  a.wg_budget = pl.wg_budget;
+  a.slots = pl.slots;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
   return a;
+}
+
+// part_lse holds slots x H floats, then (balanced splits) the split table
+void set_partials(da::MlaArgs& a, const MlaPlan& pl, void* part_out, void* part_lse) {
+  a.part_out = static_cast<uint16_t*>(part_out);
+  a.part_lse = static_cast<float*>(part_lse);
+  a.split_table = pl.splits == 0 ? reinterpret_cast<int32_t*>(static_cast<char*>(part_lse) + pl.part_lse_bytes -
+                                                                pl.table_bytes)
+                                 : nullptr;
 }
 
 da::GqaArgs gqa_args(const da_gqa_params_t* p, const GqaPlan& pl, const void* q,
@@ -344,8 +374,18 @@ size_t da_mla_decode_workspace_size(const da_mla_params_t* p) {
 }
 
 int32_t da_mla_decode_num_splits(const da_mla_params_t* p) {
-  if (check_mla_params(p) != DA_OK) return 0;
+  if (check_mla_params(p) != DA_OK) return -1;
   return plan_mla(p).splits;
+}
+
+da_status_t da_mla_partials_size(const da_mla_params_t* p, size_t* part_out_bytes, size_t* part_lse_bytes) {
+  da_status_t st = check_mla_params(p);
+  if (st != DA_OK) return st;
+  if (!part_out_bytes || !part_lse_bytes) return DA_ERR_INVALID_ARGUMENT;
+  const MlaPlan pl = plan_mla(p);
+  *part_out_bytes = pl.part_out_bytes;
+  *part_lse_bytes = pl.part_lse_bytes;
+  return DA_OK;
 }
 
 da_status_t da_mla_decode_absorbed(const da_mla_params_t* p, const void* q_nope,
@@ -372,8 +412,7 @@ da_status_t da_mla_decode_absorbed(const da_mla_params_t* p, const void* q_nope,
   a.out = out;
   a.lse = lse;
   a.q_hat = reinterpret_cast<uint16_t*>(ws);
-  a.part_out = reinterpret_cast<uint16_t*>(ws + pl.q_hat_bytes);
-  a.part_lse = reinterpret_cast<float*>(ws + pl.q_hat_bytes + pl.part_out_bytes);
+  set_partials(a, pl, ws + pl.q_hat_bytes, ws + pl.q_hat_bytes + pl.part_out_bytes);
   return from_hip(da::launch_mla_decode(a, static_cast<hipStream_t>(hip_stream)));
 }
 
@@ -399,12 +438,12 @@ da_status_t da_mla_attend_split_pass(const da_mla_params_t* p, const void* q_hat
   st = check_ptrs16({q_hat, kv_cache, part_out, part_lse});
   if (st != DA_OK) return st;
   if (!aligned4(seq_lens)) return DA_ERR_INVALID_ARGUMENT;
-  da::MlaArgs a = mla_args(p, plan_mla(p));
+  const MlaPlan pl = plan_mla(p);
+  da::MlaArgs a = mla_args(p, pl);
   a.q_hat = static_cast<uint16_t*>(const_cast<void*>(q_hat));
   a.cache = static_cast<const uint16_t*>(kv_cache);
   a.seq_lens = seq_lens;
-  a.part_out = static_cast<uint16_t*>(part_out);
-  a.part_lse = part_lse;
+  set_partials(a, pl, part_out, part_lse);
   return from_hip(da::launch_mla_attend(a, static_cast<hipStream_t>(hip_stream)));
 }
 
@@ -416,9 +455,9 @@ da_status_t da_mla_merge_project(const da_mla_params_t* p, const void* part_out,
   st = check_ptrs16({part_out, w_uv, out});
   if (st != DA_OK) return st;
   if (!part_lse || !aligned4(part_lse) || !aligned4(lse)) return DA_ERR_INVALID_ARGUMENT;
-  da::MlaArgs a = mla_args(p, plan_mla(p));
-  a.part_out = static_cast<uint16_t*>(const_cast<void*>(part_out));
-  a.part_lse = const_cast<float*>(part_lse);
+  const MlaPlan pl = plan_mla(p);
+  da::MlaArgs a = mla_args(p, pl);
+  set_partials(a, pl, const_cast<void*>(part_out), const_cast<float*>(part_lse));
   a.w_uv = static_cast<const uint16_t*>(w_uv);
   a.out = out;
   a.lse = lse;

@@ -50,10 +50,20 @@ struct MlaArgs {
   float* out;                // [B, H, 128]
   float* lse;                // [B, H] or null
   uint16_t* q_hat;           // [B, H, 576] bf16: [q~ | q_rope]
-  uint16_t* part_out;        // [S, B, H, 512] bf16: each split's normalised o~_s
-  float* part_lse;           // [S, B, H]
+  // Split partials, slot-major: part_out [slots, H, 512] bf16 (each split's
+  // normalised o~_s), part_lse [slots, H]. Fixed splits: slot = s * B + b
+  // (num_splits per sequence, chunk rows each). Balanced splits
+  // (num_splits == 0): the attention workgroups size every sequence's splits
+  // from seq_lens so that all carry about the same number of tiles, give
+  // sequence b the slots P_b .. P_b + S_b - 1, and record P_b, S_b in
+  // split_table (2 B int32) for the merge.
+  uint16_t* part_out;
+  float* part_lse;
+  int32_t* split_table;
   int64_t cache_sb, cache_st;
   int32_t batch, num_heads, max_seq_len, num_splits, chunk;
+  int32_t wg_budget;         // balanced: tiles are spread over this many workgroups
+  int32_t slots;             // rows of part_out / H
   float scale_log2;
 };
 

@@ -206,6 +206,102 @@ __global__ __launch_bounds__(64) void mla_absorb_kernel(MlaArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// split assignment
+// ---------------------------------------------------------------------------
+struct SplitWork {
+  int b, slot, t_begin, t_end;  // wave-uniform
+  bool valid;
+};
+
+// Inclusive prefix sum over the 64 lanes of a wave by DPP (no LDS round
+// trips): shifts by 1, 2, 4, 8 within each row of 16 lanes (lanes with no
+// source add 0), then the last lane of row 0 is added to row 1 and of row 2
+// to row 3 (row_bcast:15), then the last lane of row 1 to rows 2 and 3
+// (row_bcast:31). Lanes that a step leaves out add 0.
+__device__ __forceinline__ int wave_inclusive_scan_i(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false); // row_bcast:15, rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false); // row_bcast:31, rows 2, 3
+  return x;
+}
+
+// The work of workgroup `wg`. Fixed splits: grid (S, B), chunk rows per split.
+// Balanced splits: every sequence b gets S_b = ceil(tiles_b / q) splits of q
+// tiles (32 rows) with q = ceil(total tiles / wg_budget), so that all splits
+// carry about the same work whatever the lengths; the splits of b take the
+// slots P_b .. P_b + S_b - 1 (P = exclusive prefix sum of S) and workgroup wg
+// serves slot wg. Every wave computes this from seq_lens on its own (its
+// results are wave-uniform); wave 0 of workgroup 0 publishes P and S for the
+// merge. A split is never empty; workgroups past the last slot get none.
+__device__ SplitWork assign_split(const MlaArgs& a, int lane, bool publish) {
+  SplitWork r{0, 0, 0, 0, false};
+  if (a.num_splits > 0) {
+    r.b = blockIdx.y;
+    r.slot = blockIdx.x * a.batch + blockIdx.y;
+    const int L = a.seq_lens ? a.seq_lens[r.b] : a.max_seq_len;
+    r.t_begin = blockIdx.x * a.chunk;
+    r.t_end = min(L, r.t_begin + a.chunk);
+    r.valid = true;
+    return r;
+  }
+  const int B = a.batch;
+  const int wg = blockIdx.x;
+  constexpr int kMaxChunks = 8;  // balanced splits are planned for B <= 512
+  const int n_chunks = (B + 63) >> 6;
+  // lengths of sequences c * 64 + lane, clamped to [0, max_seq_len] (rows past
+  // max_seq_len are never read, as with fixed splits); all loads are issued
+  // before the first use (clamped indexes, so no branch separates them)
+  int len[kMaxChunks];
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    const int b = min(c * 64 + lane, B - 1);
+    len[c] = a.seq_lens ? a.seq_lens[b] : a.max_seq_len;
+  }
+  int tiles_lane = 0;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    len[c] = c * 64 + lane < B ? min(max(len[c], 0), a.max_seq_len) : 0;
+    tiles_lane += (len[c] + kTok - 1) / kTok;
+  }
+  const int total = __builtin_amdgcn_readlane(wave_inclusive_scan_i(tiles_lane), 63);
+  const int q = max(1, (total + a.wg_budget - 1) / a.wg_budget);
+  int carry = 0;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    if (c >= n_chunks) break;
+    const int b = c * 64 + lane;
+    const int S = ((len[c] + kTok - 1) / kTok + q - 1) / q;
+    const int incl = wave_inclusive_scan_i(S);
+    const int P = carry + incl - S;
+    if (publish && b < B) {
+      a.split_table[2 * b] = P;
+      a.split_table[2 * b + 1] = S;
+    }
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(b < B && wg >= P && wg < P + S);
+    if (hit != 0) {
+      const int src = __builtin_ctzll(hit);
+      r.b = __builtin_amdgcn_readlane(b, src);
+      const int s = wg - __builtin_amdgcn_readlane(P, src);
+      const int L = __builtin_amdgcn_readlane(len[c], src);
+      r.slot = wg;
+      r.t_begin = s * q * kTok;
+      r.t_end = min(L, r.t_begin + q * kTok);
+      r.valid = true;
+    }
+    carry += __builtin_amdgcn_readlane(incl, 63);
+  }
+  // the values are wave-uniform; say so, so that they stay in scalar registers
+  r.b = __builtin_amdgcn_readfirstlane(r.b);
+  r.slot = __builtin_amdgcn_readfirstlane(r.slot);
+  r.t_begin = __builtin_amdgcn_readfirstlane(r.t_begin);
+  r.t_end = __builtin_amdgcn_readfirstlane(r.t_end);
+  return r;
+}
+
+// ---------------------------------------------------------------------------
 // 2. split-KV latent attention
 // ---------------------------------------------------------------------------
 // grid (split, sequence); NW waves, each owning HB blocks of 16 heads
@@ -230,15 +326,15 @@ void mla_attend_kernel(MlaArgs a) {
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int q4 = lane >> 4, l16 = lane & 15;
-  const int split = blockIdx.x;
-  const int b = blockIdx.y;
-  const int L = a.seq_lens ? a.seq_lens[b] : a.max_seq_len;
-  const int t_begin = split * a.chunk;
-  const int t_end = min(L, t_begin + a.chunk);
-  const int64_t rows = (int64_t)a.batch * H;
+  const SplitWork work = assign_split(a, lane, blockIdx.x == 0 && w == 0);
+  if (!work.valid) return;
+  const int b = work.b;
+  const int64_t slot = work.slot;
+  const int t_begin = work.t_begin;
+  const int t_end = work.t_end;
 
-  if (t_begin >= t_end) {
-    for (int i = tid; i < H; i += NW * 64) a.part_lse[split * rows + (int64_t)b * H + i] = kNegInf;
+  if (t_begin >= t_end) {  // fixed splits only: a split past the sequence's end
+    for (int i = tid; i < H; i += NW * 64) a.part_lse[slot * H + i] = kNegInf;
     return;
   }
 
@@ -470,7 +566,7 @@ void mla_attend_kernel(MlaArgs a) {
     float l_tot = l_part[hb] + __shfl_xor(l_part[hb], 16);
     l_tot += __shfl_xor(l_tot, 32);
     const float inv = 1.0f / l_tot;
-    uint16_t* po = a.part_out + ((int64_t)split * rows + (int64_t)b * H + h) * kDc + 4 * q4;
+    uint16_t* po = a.part_out + (slot * H + h) * kDc + 4 * q4;
 #pragma unroll
     for (int cb = 0; cb < 32; ++cb) {
       uint2 v;
@@ -478,7 +574,7 @@ void mla_attend_kernel(MlaArgs a) {
       v.y = cvt_bf16x2(o[hb][cb][2] * inv, o[hb][cb][3] * inv);
       *reinterpret_cast<uint2*>(po + 16 * cb) = v;
     }
-    if (q4 == 0) a.part_lse[split * rows + (int64_t)b * H + h] = (m_ref[hb] + log2_hw(l_tot)) * kLn2;
+    if (q4 == 0) a.part_lse[slot * H + h] = (m_ref[hb] + log2_hw(l_tot)) * kLn2;
   }
 }
 
@@ -548,18 +644,26 @@ __global__ __launch_bounds__(512) void mla_merge_project_kernel(MlaArgs a, int n
       for (int e = 0; e < 16; ++e) acc[e] = 0.f;
       if (rr < R) {
         const int64_t row_id = (int64_t)bidx * H + h;
+        // the splits of this sequence: slots s * B + b (fixed) or P_b + s
+        // (balanced, from the table the attention launch wrote)
+        const bool bal = a.num_splits == 0;
+        // (the table is clamped to the slots that exist)
+        const int P = bal ? min(max(a.split_table[2 * bidx], 0), a.slots) : 0;
+        const int n_s = bal ? min(a.split_table[2 * bidx + 1], a.slots - P) : a.num_splits;
+        const int64_t s_base = bal ? (int64_t)P * H + h : row_id;
+        const int64_t s_step = bal ? (int64_t)H : rows;
         // max and normaliser of the split lse values: the 32 threads of the
         // row (one half-wave) read every 32nd split each and combine
         float M = kNegInf;
-        for (int s = cs; s < a.num_splits; s += 32) M = fmaxf(M, a.part_lse[s * rows + row_id]);
+        for (int s = cs; s < n_s; s += 32) M = fmaxf(M, a.part_lse[s_base + s * s_step]);
 #pragma unroll
         for (int off = 1; off < 32; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
         float lse_out = kNegInf;
         if (M != kNegInf) {
           const float m2 = M * kLog2e;
           float z = 0.f;
-          for (int s = cs; s < a.num_splits; s += 32) {
-            const float v = a.part_lse[s * rows + row_id];
+          for (int s = cs; s < n_s; s += 32) {
+            const float v = a.part_lse[s_base + s * s_step];
             if (v != kNegInf) z += exp2_hw(fmaf(v, kLog2e, -m2));
           }
 #pragma unroll
@@ -569,16 +673,16 @@ __global__ __launch_bounds__(512) void mla_merge_project_kernel(MlaArgs a, int n
           // loads are in flight together; an empty split (lse -inf) was never
           // written: its row is replaced by zeros rather than skipped
           constexpr int kMergeBatch = 4;
-          for (int s0 = g; s0 < a.num_splits; s0 += kMergeBatch * G) {
+          for (int s0 = g; s0 < n_s; s0 += kMergeBatch * G) {
             uint4 u[kMergeBatch][2];
             float wgt[kMergeBatch];
 #pragma unroll
             for (int j = 0; j < kMergeBatch; ++j) {
               const int s = s0 + j * G;
-              const float v = s < a.num_splits ? a.part_lse[s * rows + row_id] : kNegInf;
+              const float v = s < n_s ? a.part_lse[s_base + s * s_step] : kNegInf;
               wgt[j] = v == kNegInf ? 0.f : exp2_hw(fmaf(v, kLog2e, -m2)) * inv_z;
-              const int s_in = s < a.num_splits ? s : 0;
-              const uint4* src = reinterpret_cast<const uint4*>(a.part_out + (s_in * rows + row_id) * kDc + 16 * cs);
+              const int s_in = s < n_s ? s : 0;
+              const uint4* src = reinterpret_cast<const uint4*>(a.part_out + (s_base + s_in * s_step) * kDc + 16 * cs);
               u[j][0] = src[0];
               u[j][1] = src[1];
             }
@@ -676,7 +780,7 @@ bool with_attend_shape(int num_heads, F&& f) {
 }
 
 hipError_t launch_mla_attend(const MlaArgs& a, hipStream_t st) {
-  const dim3 grid(a.num_splits, a.batch);
+  const dim3 grid = a.num_splits > 0 ? dim3(a.num_splits, a.batch) : dim3(a.slots, 1);
   const bool ok = with_attend_shape(a.num_heads, [&](auto kernel, int nw) {
     hipLaunchKernelGGL(kernel, grid, dim3(64 * nw), 0, st, a);
   });

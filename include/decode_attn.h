@@ -145,7 +145,7 @@ DA_EXPORT da_status_t da_gqa_decode_split_pass(const da_gqa_params_t* params,
 
 typedef struct {
   int32_t batch;           /* B >= 1 */
-  int32_t num_heads;       /* n_h: a multiple of 16, at most 128 */
+  int32_t num_heads;       /* n_h: 16, 32, 48, 64, 96 or 128 (else UNSUPPORTED) */
   int32_t kv_lora_rank;    /* d_c: must be 512 */
   int32_t qk_rope_dim;     /* d_rope: must be 64 */
   int32_t qk_nope_dim;     /* d_nope: must be 128 */
@@ -155,17 +155,41 @@ typedef struct {
                               must be finite and > 0 (else UNSUPPORTED) */
   int64_t cache_stride_b;  /* row [b, t] at kv_cache + b*cache_stride_b + t*cache_stride_t */
   int64_t cache_stride_t;  /* default layout [B, L_max, 576]: 576*L_max and 576 */
-  int32_t num_splits;      /* S >= 1 forces a split count; 0 lets the library choose */
+  int32_t num_splits;      /* S >= 1 forces S splits per sequence; 0 lets the library choose */
 } da_mla_params_t;
 
+/* Splitting (flash-decoding, arganzheng.life section 5.2). The attention of a
+ * sequence is split along its rows; each split leaves a partial o~_s and
+ * lse_s in a "slot", and the merge combines the slots of each sequence.
+ *  - Fixed splits (num_splits = S >= 1, or chosen by the library when the
+ *    batch alone fills the GPU): S splits of ceil(L_max / S) rows per
+ *    sequence, split s of sequence b in slot s*B + b.
+ *  - Balanced splits (num_splits = 0 and a batch smaller than the number of
+ *    resident workgroups): the split sizes are decided on the device from
+ *    seq_lens so that every split carries about the same number of rows,
+ *    whatever the spread of lengths; the slots of each sequence are recorded
+ *    in a small table after the lse values (see da_mla_partials_size).
+ * Slots hold part_out [slots, H, d_c] bf16 (normalised o~_s) and part_lse
+ * [slots, H] float32 (lse_s; -inf for a split with no rows). */
+
 /* Bytes of workspace da_mla_decode_absorbed needs (never 0 for valid
- * parameters): the absorbed queries q^ [B, H, 576] bf16, the per-split
- * partials o~_s [S, B, H, 512] bf16 and lse_s [S, B, H] float32, each
- * starting on a 256-byte boundary in that order. */
+ * parameters): the absorbed queries q^ [B, H, 576] bf16, then the two
+ * partial buffers of da_mla_partials_size, each starting on a 256-byte
+ * boundary in that order. */
 DA_EXPORT size_t da_mla_decode_workspace_size(const da_mla_params_t* params);
 
-/* Split count da_mla_decode_absorbed will use (>= 1), or 0 if invalid. */
+/* Fixed split count per sequence (>= 1); 0 when the splits are balanced on
+ * the device; -1 if the parameters are invalid. */
 DA_EXPORT int32_t da_mla_decode_num_splits(const da_mla_params_t* params);
+
+/* Sizes in bytes of the two partial buffers that da_mla_attend_split_pass
+ * writes and da_mla_merge_project reads: part_out (the o~_s of every slot)
+ * and part_lse (the lse_s of every slot, followed with balanced splits by
+ * the table of each sequence's slots). Their layout inside is the
+ * library's. Errors: as da_mla_decode_absorbed's parameter checks, or
+ * INVALID_ARGUMENT for a NULL output. */
+DA_EXPORT da_status_t da_mla_partials_size(const da_mla_params_t* params,
+                                           size_t* part_out_bytes, size_t* part_lse_bytes);
 
 /*
  *   q_nope   [B, H, d_nope] bf16, contiguous
@@ -198,10 +222,10 @@ DA_EXPORT da_status_t da_mla_absorb_query(const da_mla_params_t* params,
                                           const void* w_uk, void* q_hat, void* hip_stream);
 
 /* Stage 2, attention of the absorbed queries over the shared latent rows,
- * split along the sequence (arganzheng.life sections 4.5 and 5.2). With
- * S = da_mla_decode_num_splits(params), writes for each split s
- *   part_out [S, B, H, d_c] bf16:   o~_s = sum_{j in s} softmax_s(score)_j c_kv_j
- *   part_lse [S, B, H] float32:     lse_s (-inf for a split with no rows). */
+ * split along the sequence (arganzheng.life sections 4.5 and 5.2). Writes,
+ * for every split s of every sequence, o~_s = sum_{j in s} softmax_s(score)_j
+ * c_kv_j and lse_s into part_out and part_lse, two device buffers of the
+ * sizes da_mla_partials_size gives (16- and 4-byte aligned). */
 DA_EXPORT da_status_t da_mla_attend_split_pass(const da_mla_params_t* params,
                                                const void* q_hat, const void* kv_cache,
                                                const int32_t* seq_lens,
@@ -210,7 +234,8 @@ DA_EXPORT da_status_t da_mla_attend_split_pass(const da_mla_params_t* params,
 
 /* Stage 3, merge the splits by log-sum-exp, then project by W_UV
  * (arganzheng.life section 4.5, output side): out[b,h] = o~[b,h] W_UV[h];
- * lse[b,h] = log sum_s exp(lse_s). Inputs as written by stage 2. */
+ * lse[b,h] = log sum_s exp(lse_s). part_out and part_lse as written by
+ * stage 2 with the same parameters. */
 DA_EXPORT da_status_t da_mla_merge_project(const da_mla_params_t* params,
                                            const void* part_out, const float* part_lse,
                                            const void* w_uv, float* out, float* lse,

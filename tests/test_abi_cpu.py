@@ -109,10 +109,42 @@ def test_split_planning_without_a_device():
     assert n(gqa(splits=7)) == 7
     assert n(gqa(L=5, splits=9)) == 5                      # never more splits than rows
     m = lambda p: L.da_mla_decode_num_splits(ctypes.byref(p))
-    assert m(mla()) == split_cost_model(64, 4096, 256, 128, 128) == 4     # DeepSeek-V3 B=64: 256 workgroups
-    assert m(mla(4, 128, 32768)) == split_cost_model(4, 32768, 256, 128, 128) == 64
-    assert m(mla(48, 128, 4096)) == split_cost_model(48, 4096, 256, 128, 128)
+    # MLA: a batch below the resident workgroups (256) is split on the device
+    # by the actual lengths (0 = balanced); from 256 sequences on, fixed splits
+    assert m(mla()) == 0                                   # DeepSeek-V3 B=64
+    assert m(mla(4, 128, 32768)) == 0
+    assert m(mla(512, 128, 4096)) == split_cost_model(512, 4096, 256, 128, 128) == 1
+    assert m(mla(256, 128, 32768)) == split_cost_model(256, 32768, 256, 128, 128)
+    assert m(mla(splits=3)) == 3                           # forced: fixed splits
+    assert m(mla(H=80)) == -1                              # invalid
     assert L.da_mla_decode_workspace_size(ctypes.byref(mla())) >= 64 * 128 * 576 * 2
+
+
+def mla_partials(p):
+    po, pl = ctypes.c_size_t(), ctypes.c_size_t()
+    st = da.lib().da_mla_partials_size(ctypes.byref(p), ctypes.byref(po), ctypes.byref(pl))
+    return st, po.value, pl.value
+
+
+@needs_lib
+@cpu_only
+def test_mla_partials_size_without_a_device():
+    L = da.lib()
+    up = lambda n: -(-n // 256) * 256
+    # fixed splits: S * B slots of H rows (bf16 o~ of 512, float lse)
+    st, po, pl = mla_partials(mla(64, 128, 4096, splits=3))
+    assert st == 0 and po == up(3 * 64 * 128 * 512 * 2) and pl == up(3 * 64 * 128 * 4)
+    # balanced: at most (resident workgroups + B) slots, then 2 int32 per
+    # sequence for the table of each sequence's slots
+    st, po, pl = mla_partials(mla(64, 128, 4096))
+    assert st == 0 and po == up((256 + 64) * 128 * 512 * 2)
+    assert pl == up((256 + 64) * 128 * 4) + up(64 * 2 * 4)
+    # the workspace is q^ followed by the two partial buffers
+    for p in (mla(), mla(splits=3), mla(4, 16, 100)):
+        _, po, pl = mla_partials(p)
+        assert L.da_mla_decode_workspace_size(ctypes.byref(p)) == up(p.batch * p.num_heads * 576 * 2) + po + pl
+    assert mla_partials(mla(H=80))[0] == 2
+    assert L.da_mla_partials_size(ctypes.byref(mla()), None, None) == 1
 
 
 FAKE = ctypes.c_void_p(0x10000)       # 16-byte aligned, never dereferenced

@@ -88,6 +88,8 @@ EDGE = [
     (2, 6, 6, 64, [31, 2], "f32"),                     # fp32, D=64
     (2, 8, 4, 128, [513, 77], "f32"),                  # fp32, D=128
     (1, 14, 2, 128, [5000], "bf16"),                   # g=7
+    (2, 8, 8, 128, [3000, 5000], "bf16"),              # 16 units: 16-wave workgroups, 16 splits
+    (1, 32, 4, 128, [6000], "bf16"),                   # 8 heads per workgroup: 4-wave, 47 splits
 ]
 
 
