@@ -96,17 +96,13 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
 
 // XOR swizzle of the 16-byte chunk index inside a tile row (rows are 1152
 // bytes = 72 chunks; only the low 3 bits of a chunk index change, so a chunk
-// stays inside its row). With r = row & 15:
-//   f(r) = ((r ^ (r >> 2)) & 3) << 1 | ((r >> 2) ^ (r >> 3)) & 1
-// makes both LDS read patterns conflict-free, for LDS bank groups of 128 and
-// of 256 bytes alike: (a) 16 consecutive rows at one logical chunk (the S^T
-// operand: f is a permutation on rows 0-7, on rows 8-15, on even rows and on
-// odd rows) and (b) 4 consecutive rows x 32 bytes (the transposed O^T
-// operand: f >> 1 differs across each aligned group of 4 rows, and across the
-// even and the odd rows of each group of 8).
-__device__ __forceinline__ int row_swizzle(int row) {
-  return (((row ^ (row >> 2)) & 3) << 1) | (((row >> 2) ^ (row >> 3)) & 1);
-}
+// stays inside its aligned group of 8 and inside its row): f(r) = r mod 8.
+// Both read patterns of the tile are free of LDS bank conflicts with it, as
+// measured with the SQ_LDS_BANK_CONFLICT counter: (a) 16-byte reads of 16
+// consecutive rows at one logical chunk (the S^T operand) and (b) the
+// transposing 8-byte reads of 4 consecutive rows x 32 bytes (the O^T operand).
+// Rows r and r + 16 share f, so one lane offset serves both halves of a tile.
+__device__ __forceinline__ int row_swizzle(int row) { return row & 7; }
 
 // Buffer resource for raw (unswizzled, stride 0) byte addressing: loads past
 // num_records bytes return zero.
@@ -585,15 +581,17 @@ void mla_attend_kernel(MlaArgs a) {
 // `bpg` consecutive blocks of 16 batch rows, so W_UV,h is staged in LDS once
 // per workgroup. Workgroups of one head share an XCD (linear id % 8 = h % 8).
 // W_UV,h [512 x 128] is stored unpadded (256-byte rows) with an XOR swizzle of
-// the 16-byte chunk index, 2 * (row % 4), so the transposed reads (4 rows x
-// 32 bytes per 16-lane group) hit distinct banks.
-constexpr int kORowB = 1040;  // merged o~ row in LDS: 512 bf16 + 16 bytes pad
+// the 16-byte chunk index, and the merged o~ rows with a 1056-byte pitch; with
+// these, the transposed W_UV reads (4 rows x 32 bytes per 16-lane group, rows
+// 8 q4 + 0..3) and the 16-byte o~ reads (16 rows at one offset) are free of
+// LDS bank conflicts, as measured with the SQ_LDS_BANK_CONFLICT counter.
+constexpr int kORowB = 1056;  // merged o~ row in LDS: 512 bf16 + 32 bytes pad
 
-__device__ __forceinline__ int wuv_swizzle(int row) { return 2 * (row & 3); }
+__device__ __forceinline__ int wuv_swizzle(int row) { return 2 * ((row & 3) | (((row >> 3) & 1) << 2)); }
 
 __global__ __launch_bounds__(512) void mla_merge_project_kernel(MlaArgs a, int n_groups, int bpg) {
   __shared__ __attribute__((aligned(1024))) uint8_t w_smem[kDc * 256];   // 131072
-  __shared__ __attribute__((aligned(16))) uint8_t o_smem[16 * kORowB];   // 16640
+  __shared__ __attribute__((aligned(16))) uint8_t o_smem[16 * kORowB];   // 16896
   LDS uint8_t* w_lds = (LDS uint8_t*)w_smem;
   LDS uint8_t* o_lds = (LDS uint8_t*)o_smem;
 
