@@ -9,17 +9,21 @@
 // chapter 7, section 7.3).
 //
 // Work decomposition (MI355X: 256 CUs, wave64):
-//   grid  = (split, KV head x head sub-group, batch); block = 4 waves.
+//   grid  = (split, KV head x head sub-group, batch); block = kWaves waves
+//   (4; 16 when there are too few work units to give every CU two 4-wave
+//   workgroups, so that one workgroup per CU still keeps 16 waves streaming).
 //   A workgroup serves GH query heads that share one KV head, so each K/V byte
 //   is fetched from HBM once and used GH times from registers.
 //   A cache row of D elements is spread over D/8 consecutive lanes (8 elements,
 //   16 or 32 bytes per lane), so one wave-wide load covers 4 (D=128) or 8 (D=64)
 //   whole rows: fully used 64-byte segments on every load instruction.
 //   Each group of lanes that owns a row keeps its own online-softmax state
-//   (running max m, sum l, accumulator) in registers; the per-row dot product
-//   is reduced across the D/8 lanes with DPP row moves. States are merged
+//   (running max m, sum l, accumulator) in registers. The per-row dot products
+//   are combined across the D/8 lanes with DPP row moves: for bf16 rows of 128
+//   by a reduce-scatter that leaves each lane with whole scores of its own (one
+//   exponential per score), otherwise by a plain all-reduce. States are merged
 //   across the lanes of a wave at the end (cross-lane shuffles), then across
-//   the 4 waves through LDS.
+//   the waves through LDS.
 //   Scores live in the base-2 domain: q is pre-multiplied by scale*log2(e) so
 //   each softmax weight is one v_exp_f32.
 #include "da_device.h"
