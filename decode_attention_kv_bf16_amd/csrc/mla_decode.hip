@@ -407,6 +407,136 @@ void mla_attend_kernel(MlaArgs a) {
 
   f32x4_t o[HB][32];
   float l_part[HB];  // this lane's share of sum_j 2^(s_j - m_ref)
+  // --- the phases of one tile --------------------------------------------
+  // S^T = C Q^^T of tile `it` (ring buffer it % kDepth) for tokens 0-15
+  // (s[.][0]) and 16-31 (s[.][1]); the copies of tile `refill_it` go out
+  // spread over the k-steps, so that their issue overlaps the matrix ops. The
+  // tile operands go through a ring of kSRing register slots: the read for
+  // k-step ks + kSRing - 1 is issued before the matrix ops of k-step ks, and
+  // the scheduling fences keep the compiler from hoisting every read (which
+  // would need more registers than a wave has).
+  constexpr int kSRing = 3;
+  auto score_tile = [&](int it, int refill_it, f32x4_t (&s)[HB][2]) {
+    const int refill_buf = refill_it % kDepth;
+    const __amdgpu_buffer_rsrc_t refill_rsrc = tile_rsrc(refill_it);
+    const LDS uint8_t* tile = lds + (it % kDepth) * kTileB;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) s[hb][0] = s[hb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    u32x4_t ra0[kSRing], ra1[kSRing];
+    auto read_s = [&](int ks) {
+      const int off = ((ks & 1) ? s_off1 : s_off0) + 128 * (ks >> 1);
+      ra0[ks % kSRing] = *reinterpret_cast<const LDS u32x4_t*>(tile + off);
+      ra1[ks % kSRing] = *reinterpret_cast<const LDS u32x4_t*>(tile + off + 16 * kRowB);
+    };
+#pragma unroll
+    for (int ks = 0; ks < kSRing - 1; ++ks) read_s(ks);
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+#pragma unroll
+      for (int i = ks * kCopies / 18; i < (ks + 1) * kCopies / 18; ++i) issue_copy(refill_rsrc, i, refill_buf);
+      if (ks + kSRing - 1 < 18) read_s(ks + kSRing - 1);
+      const bf16x8_t a0 = as_bf16x8(ra0[ks % kSRing]);
+      const bf16x8_t a1 = as_bf16x8(ra1[ks % kSRing]);
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        s[hb][0] = mfma16x16x32(a0, qb[hb][ks], s[hb][0]);
+        s[hb][1] = mfma16x16x32(a1, qb[hb][ks], s[hb][1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Softmax reference of tile `it`: the lane holds tokens 4q4+i and 16+4q4+i
+  // of head (hb, l16); rows past the split end (last tile only) get score
+  // -inf, weight 0. Only the first tile of a split (thr = -inf) and a score
+  // beyond the headroom need the head-wide max: the four lanes of a head
+  // combine theirs, so they agree on the reference.
+  auto softmax_ref = [&](int it, f32x4_t (&s)[HB][2]) {
+    const int nv = t_end - (t_begin + it * kTok);  // valid rows in the tile (may exceed 32)
+    const bool full_tile = nv >= kTok;
+    float smax[HB];
+    bool over = false;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      if (!full_tile) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (4 * q4 + i >= nv) s[hb][0][i] = kNegInf;
+          if (16 + 4 * q4 + i >= nv) s[hb][1][i] = kNegInf;
+        }
+      }
+      float mx = fmaxf(s[hb][0][0], s[hb][1][0]);
+#pragma unroll
+      for (int i = 1; i < 4; ++i) mx = fmaxf(mx, fmaxf(s[hb][0][i], s[hb][1][i]));
+      smax[hb] = mx;
+      over |= mx > thr[hb];
+    }
+    if (__builtin_amdgcn_ballot_w64(over) != 0) {
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        float mx = smax[hb] * a.scale_log2;
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (m_ref[hb] == kNegInf) {
+          m_ref[hb] = mx;                            // first tile of the split
+        } else if (mx > m_ref[hb] + kRefHeadroom) {  // rare: restart with a raised reference
+          m_ref[hb] = mx;
+          restart_flag = 1;
+        }
+        thr[hb] = (m_ref[hb] + kRefHeadroom) / a.scale_log2;
+      }
+    }
+  };
+  // weight k of the lane (k = 8 hb + i; i < 4: token 4q4+i, else 16+4q4+i-4)
+  auto weight = [&](const f32x4_t (&s)[HB][2], int k) {
+    const int hb = k >> 3, i = k & 7;
+    const float v = i < 4 ? s[hb][0][i] : s[hb][1][i - 4];
+    return exp2_hw(fmaf(v, a.scale_log2, -m_ref[hb]));
+  };
+  // the weights as PV B operands (token order matching the transposed reads)
+  auto pack = [&](const float (&p)[8 * HB], bf16x8_t (&pb)[HB]) {
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      const float* q = p + 8 * hb;
+      l_part[hb] += ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+      uint4 pw;
+      pw.x = cvt_bf16x2(q[0], q[1]);
+      pw.y = cvt_bf16x2(q[2], q[3]);
+      pw.z = cvt_bf16x2(q[4], q[5]);
+      pw.w = cvt_bf16x2(q[6], q[7]);
+      pb[hb] = as_bf16x8(pw);
+    }
+  };
+  // O^T[c, h] += sum_t C[t, c] P[h, t] for the tile in ring buffer `buf`;
+  // B-operand element e is token 4q4+e (e < 4) or 16+4q4+(e-4), matching the
+  // two transposed reads. pv_start issues the first transposed reads (they do
+  // not depend on P); pv_run runs `extra(cb)` in the shadow of column block
+  // cb's matrix ops.
+  constexpr int kTRing = 4;
+  i16x4_t tlo[kTRing], thi[kTRing];
+  auto read_t = [&](const LDS uint8_t* tile, int cb) {
+    const int off = t_off[cb & 3] + 128 * (cb >> 2);
+    tlo[cb % kTRing] = lds_read_tr(tile + off);
+    thi[cb % kTRing] = lds_read_tr(tile + off + 16 * kRowB);
+  };
+  auto pv_start = [&](int buf) {
+    const LDS uint8_t* tile = lds + buf * kTileB;
+#pragma unroll
+    for (int cb = 0; cb < kTRing - 1; ++cb) read_t(tile, cb);
+  };
+  auto pv_run = [&](int buf, const bf16x8_t (&pb)[HB], auto&& extra) {
+    const LDS uint8_t* tile = lds + buf * kTileB;
+#pragma unroll
+    for (int cb = 0; cb < 32; ++cb) {
+      if (cb + kTRing - 1 < 32) read_t(tile, cb + kTRing - 1);
+      const bf16x8_t at = join_tr(tlo[cb % kTRing], thi[cb % kTRing]);
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) o[hb][cb] = mfma16x16x32(at, pb[hb], o[hb][cb]);
+      extra(cb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   // One attempt normally; a further attempt only if some tile's max exceeded
   // its head's reference by more than kRefHeadroom (the reference is raised to
   // that tile max, a strictly larger observed value, so attempts are finite).
@@ -421,132 +551,63 @@ void mla_attend_kernel(MlaArgs a) {
       for (int cb = 0; cb < 32; ++cb) o[hb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       l_part[hb] = 0.f;
     }
+    f32x4_t s[HB][2];
+    if constexpr (kDepth == 4) {
+      // Software pipeline: while the matrix cores run the PV of tile it - 1,
+      // the VALU computes the weights of tile it (a wave overlaps only a few
+      // VALU ops with each of its own matrix ops, so the 8 HB weights are
+      // spread over the 32 column blocks). Tile it - 1 stays in its ring
+      // buffer, so 2 tiles are in flight: tile it + 2 is refilled into the
+      // buffer of tile it - 2.
 #pragma unroll
-    for (int j = 0; j < kDepth - 1; ++j) issue_tile(j, j);
-    for (int it = 0; it < ntiles; ++it) {
-      // tile `it` has landed once only the copies of the kDepth - 2 tiles
-      // after it are pending
-      wait_vm<(kDepth - 2) * kCopies>();
-      tile_barrier();
-      // The buffer refilled in this iteration was last read in iteration
-      // it - 1. Its copies are spread over the k-steps of S^T below, so that
-      // their issue overlaps the matrix ops.
-      const int refill_buf = (it + kDepth - 1) % kDepth;
-      const __amdgpu_buffer_rsrc_t refill_rsrc = tile_rsrc(it + kDepth - 1);
-      const LDS uint8_t* tile = lds + (it % kDepth) * kTileB;
-      const int nv = t_end - (t_begin + it * kTok);  // valid rows in this tile (may exceed 32)
-
-      // S^T = C Q^^T for tokens 0-15 (s[.][0]) and 16-31 (s[.][1]). The tile
-      // operands go through a ring of kSRing register slots: the read for k-step
-      // ks + kSRing - 1 is issued before the matrix ops of k-step ks, and the
-      // scheduling fences keep the compiler from hoisting every read (which
-      // would need more registers than a wave has).
-      constexpr int kSRing = 3;
-      f32x4_t s[HB][2];
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb) s[hb][0] = s[hb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      u32x4_t ra0[kSRing], ra1[kSRing];
-      auto read_s = [&](int ks) {
-        const int off = ((ks & 1) ? s_off1 : s_off0) + 128 * (ks >> 1);
-        ra0[ks % kSRing] = *reinterpret_cast<const LDS u32x4_t*>(tile + off);
-        ra1[ks % kSRing] = *reinterpret_cast<const LDS u32x4_t*>(tile + off + 16 * kRowB);
-      };
-#pragma unroll
-      for (int ks = 0; ks < kSRing - 1; ++ks) read_s(ks);
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-#pragma unroll
-        for (int i = ks * kCopies / 18; i < (ks + 1) * kCopies / 18; ++i) issue_copy(refill_rsrc, i, refill_buf);
-        if (ks + kSRing - 1 < 18) read_s(ks + kSRing - 1);
-        const bf16x8_t a0 = as_bf16x8(ra0[ks % kSRing]);
-        const bf16x8_t a1 = as_bf16x8(ra1[ks % kSRing]);
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-          s[hb][0] = mfma16x16x32(a0, qb[hb][ks], s[hb][0]);
-          s[hb][1] = mfma16x16x32(a1, qb[hb][ks], s[hb][1]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-
-      // the first transposed reads of the PV phase do not depend on P
-      constexpr int kTRing = 4;
-      i16x4_t tlo[kTRing], thi[kTRing];
-      auto read_t = [&](int cb) {
-        const int off = t_off[cb & 3] + 128 * (cb >> 2);
-        tlo[cb % kTRing] = lds_read_tr(tile + off);
-        thi[cb % kTRing] = lds_read_tr(tile + off + 16 * kRowB);
-      };
-#pragma unroll
-      for (int cb = 0; cb < kTRing - 1; ++cb) read_t(cb);
-
-      // online softmax; lane holds tokens 4q4+i and 16+4q4+i of head (hb, l16).
-      // Rows past the split end (last tile only) get score -inf, weight 0.
-      const bool full_tile = nv >= kTok;
-      float smax[HB];
-      bool over = false;
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        if (!full_tile) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (4 * q4 + i >= nv) s[hb][0][i] = kNegInf;
-            if (16 + 4 * q4 + i >= nv) s[hb][1][i] = kNegInf;
-          }
-        }
-        float mx = fmaxf(s[hb][0][0], s[hb][1][0]);
-#pragma unroll
-        for (int i = 1; i < 4; ++i) mx = fmaxf(mx, fmaxf(s[hb][0][i], s[hb][1][i]));
-        smax[hb] = mx;
-        over |= mx > thr[hb];
-      }
-      // Only the first tile of a split (thr = -inf) and a score beyond the
-      // headroom need the head-wide max: the four lanes of a head combine
-      // theirs, so they agree on the reference.
-      if (__builtin_amdgcn_ballot_w64(over) != 0) {
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-          float mx = smax[hb] * a.scale_log2;
-          mx = fmaxf(mx, __shfl_xor(mx, 16));
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
-          if (m_ref[hb] == kNegInf) {
-            m_ref[hb] = mx;                          // first tile of the split
-          } else if (mx > m_ref[hb] + kRefHeadroom) {  // rare: restart with a raised reference
-            m_ref[hb] = mx;
-            restart_flag = 1;
-          }
-          thr[hb] = (m_ref[hb] + kRefHeadroom) / a.scale_log2;
-        }
-      }
+      for (int j = 0; j < 2; ++j) issue_tile(j, j);
       bf16x8_t pb[HB];
+      {
+        wait_vm<kCopies>();  // tile 0 has landed, tile 1 may be pending
+        tile_barrier();
+        score_tile(0, 2, s);
+        softmax_ref(0, s);
+        float p[8 * HB];
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        const float mneg = -m_ref[hb];
-        float p[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[i] = exp2_hw(fmaf(s[hb][0][i], a.scale_log2, mneg));
-          p[4 + i] = exp2_hw(fmaf(s[hb][1][i], a.scale_log2, mneg));
-        }
-        l_part[hb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-        uint4 pw;
-        pw.x = cvt_bf16x2(p[0], p[1]);
-        pw.y = cvt_bf16x2(p[2], p[3]);
-        pw.z = cvt_bf16x2(p[4], p[5]);
-        pw.w = cvt_bf16x2(p[6], p[7]);
-        pb[hb] = as_bf16x8(pw);
+        for (int k = 0; k < 8 * HB; ++k) p[k] = weight(s, k);
+        pack(p, pb);
       }
-
-      // O^T[c, h] += sum_t C[t, c] P[h, t]; B-operand element e is token 4q4+e
-      // (e < 4) or 16+4q4+(e-4), matching the two transposed reads.
-#pragma unroll
-      for (int cb = 0; cb < 32; ++cb) {
-        if (cb + kTRing - 1 < 32) read_t(cb + kTRing - 1);
-        const bf16x8_t at = join_tr(tlo[cb % kTRing], thi[cb % kTRing]);
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) o[hb][cb] = mfma16x16x32(at, pb[hb], o[hb][cb]);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int it = 1; it < ntiles; ++it) {
+        // tile `it` has landed once only the copies of tile it + 1 are pending;
+        // after the barrier every wave is also done with tile it - 2's buffer
+        wait_vm<kCopies>();
+        tile_barrier();
+        score_tile(it, it + 2, s);
+        pv_start((it - 1) % kDepth);
+        softmax_ref(it, s);
+        float p[8 * HB];
+        constexpr int kStep = 32 / (8 * HB);  // column blocks per weight
+        pv_run((it - 1) % kDepth, pb, [&](int cb) {
+          if (cb % kStep == 0) p[cb / kStep] = weight(s, cb / kStep);
+        });
+        pack(p, pb);
       }
-
+      pv_start((ntiles - 1) % kDepth);
+      pv_run((ntiles - 1) % kDepth, pb, [](int) {});
+    } else {
+#pragma unroll
+      for (int j = 0; j < kDepth - 1; ++j) issue_tile(j, j);
+      for (int it = 0; it < ntiles; ++it) {
+        // tile `it` has landed once only the copies of the kDepth - 2 tiles
+        // after it are pending; the buffer refilled in this iteration was last
+        // read in iteration it - 1
+        wait_vm<(kDepth - 2) * kCopies>();
+        tile_barrier();
+        score_tile(it, it + kDepth - 1, s);
+        pv_start(it % kDepth);
+        softmax_ref(it, s);
+        float p[8 * HB];
+#pragma unroll
+        for (int k = 0; k < 8 * HB; ++k) p[k] = weight(s, k);
+        bf16x8_t pb[HB];
+        pack(p, pb);
+        pv_run(it % kDepth, pb, [](int) {});
+      }
     }
     wait_vm_all();
     __syncthreads();
