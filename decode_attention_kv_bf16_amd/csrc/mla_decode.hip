@@ -224,12 +224,12 @@ __device__ __forceinline__ int wave_inclusive_scan_i(int x) {
   return x;
 }
 
-// The work of workgroup `wg`. Fixed splits: grid (S, B), chunk rows per split.
+// The work of a workgroup. Fixed splits: grid (S, B), chunk rows per split.
 // Balanced splits: every sequence b gets S_b = ceil(tiles_b / q) splits of q
 // tiles (32 rows) with q = ceil(total tiles / wg_budget), so that all splits
 // carry about the same work whatever the lengths; the splits of b take the
-// slots P_b .. P_b + S_b - 1 (P = exclusive prefix sum of S) and workgroup wg
-// serves slot wg. Every wave computes this from seq_lens on its own (its
+// slots P_b .. P_b + S_b - 1 (P = exclusive prefix sum of S) and work item wg
+// (a permutation of the workgroup id) serves slot wg. Every wave computes this from seq_lens on its own (its
 // results are wave-uniform); wave 0 of workgroup 0 publishes P and S for the
 // merge. A split is never empty; workgroups past the last slot get none.
 __device__ SplitWork assign_split(const MlaArgs& a, int lane, bool publish) {
@@ -244,7 +244,14 @@ __device__ SplitWork assign_split(const MlaArgs& a, int lane, bool publish) {
     return r;
   }
   const int B = a.batch;
-  const int wg = blockIdx.x;
+  // Work item of this workgroup. The first wg_budget items (the ones that run
+  // in the first round) go in consecutive runs of wg_budget / 8 to the XCDs,
+  // which take workgroups id = x (mod 8): the splits of one sequence, which
+  // share its absorbed queries, then mostly share an XCD and its L2. Items
+  // past wg_budget keep their id.
+  const int wg = (blockIdx.x < a.wg_budget && (a.wg_budget & 7) == 0)
+                     ? (blockIdx.x & 7) * (a.wg_budget >> 3) + (blockIdx.x >> 3)
+                     : blockIdx.x;
   constexpr int kMaxChunks = 8;  // balanced splits are planned for B <= 512
   const int n_chunks = (B + 63) >> 6;
   // lengths of sequences c * 64 + lane, clamped to [0, max_seq_len] (rows past
