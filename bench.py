@@ -159,9 +159,9 @@ def setup_gqa(cfg):
             da.gqa_decode_split_pass(q, kk, vv, sl, inp.scale, part_out=part_out, part_lse=part_lse)
 
         def combine():
-            if S > 1:
-                da.splitkv_combine(part_out, part_lse, out=out, lse=lse)
-        calls.append([("gqa_split_pass", split_pass), ("gqa_combine", combine)])
+            da.splitkv_combine(part_out, part_lse, out=out, lse=lse)
+        # with one split the pass writes the final output itself
+        calls.append([("gqa_split_pass", split_pass)] + ([("gqa_combine", combine)] if S > 1 else []))
     alg = gqa_alg(B, Hq, k0.shape[2], D, int(inp.seq_lens.sum()))
     info = dict(batch=B, q_heads=Hq, kv_heads=int(k0.shape[2]), head_dim=D,
                 seq_len=int(inp.seq_lens.max()), splits=S, cache_copies=len(copies))

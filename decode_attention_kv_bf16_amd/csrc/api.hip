@@ -103,7 +103,12 @@ GqaPlan plan_gqa(const da_gqa_params_t* p) {
   // hardware's workgroup dispatch balances ragged lengths better than
   // splitting does. Work units are (sequence, KV head, head group).
   //  * at least 2 units per CU: one split, 4-wave workgroups;
-  //  * at least half a unit per CU: 4-wave workgroups, splits for 2 per CU;
+  //  * the units divide the CUs with at most 2 splits (CUs / units in {1, 2}):
+  //    8-wave workgroups, CUs / units splits, exactly one per CU (config 2,
+  //    256 units: 85.7 against 87.8 us for two 4-wave splits and a combine);
+  //  * otherwise at least half a unit per CU: 4-wave workgroups, splits for 2
+  //    per CU (8-wave workgroups that do not fill the CUs evenly measured up
+  //    to 13% slower);
   //  * fewer units (small batches, few KV heads): 16-wave workgroups, one per
   //    CU, as many splits as fit in one round (where that shape is built).
   // Chunks stay at least 128 rows.
@@ -112,10 +117,14 @@ GqaPlan plan_gqa(const da_gqa_params_t* p) {
   int64_t s;
   if (p->num_splits > 0) {
     s = p->num_splits;
-    pl.waves_per_block = (wide && 2 * units < cus && units * s <= cus) ? 16 : 4;
+    pl.waves_per_block = (wide && 2 * units < cus && units * s <= cus) ? 16
+                         : (units * s == cus) ? 8 : 4;
   } else if (units >= 2 * cus) {
     pl.waves_per_block = 4;
     s = 1;
+  } else if (2 * units >= cus && cus % units == 0) {
+    pl.waves_per_block = 8;
+    s = cus / units;
   } else if (2 * units >= cus || !wide) {
     pl.waves_per_block = 4;
     s = ceil_div(2 * cus, units);

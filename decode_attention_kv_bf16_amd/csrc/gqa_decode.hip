@@ -10,8 +10,9 @@
 //
 // Work decomposition (MI355X: 256 CUs, wave64):
 //   grid  = (split, KV head x head sub-group, batch); block = kWaves waves
-//   (4; 16 when there are too few work units to give every CU two 4-wave
-//   workgroups, so that one workgroup per CU still keeps 16 waves streaming).
+//   (4; 8 when the workgroups fill the CUs exactly once; 16 when there are
+//   too few work units to give every CU two 4-wave workgroups, so that one
+//   workgroup per CU still keeps 16 waves streaming).
 //   A workgroup serves GH query heads that share one KV head, so each K/V byte
 //   is fetched from HBM once and used GH times from registers.
 //   A cache row of D elements is spread over D/8 consecutive lanes (8 elements,
@@ -423,6 +424,10 @@ hipError_t launch_t(const GqaArgs& a, hipStream_t st) {
       hipLaunchKernelGGL((gqa_decode_kernel<T, D, GH, 16>), grid, dim3(16 * 64), 0, st, a);
       return hipGetLastError();
     }
+  }
+  if (a.waves_per_block == 8) {
+    hipLaunchKernelGGL((gqa_decode_kernel<T, D, GH, 8>), grid, dim3(8 * 64), 0, st, a);
+    return hipGetLastError();
   }
   if (a.waves_per_block != 4) return hipErrorInvalidValue;
   hipLaunchKernelGGL((gqa_decode_kernel<T, D, GH, 4>), grid, dim3(4 * 64), 0, st, a);

@@ -96,12 +96,17 @@ def test_split_planning_without_a_device():
     n = lambda p: L.da_gqa_decode_num_splits(ctypes.byref(p))
     ws = lambda p: L.da_gqa_decode_workspace_size(ctypes.byref(p))
     # GQA, with units = (b, kv head, head group): >= 2 per CU -> one split;
-    # >= half a CU's worth -> 4-wave workgroups, 2 per CU; fewer -> 16-wave
-    # workgroups, one per CU; chunks no shorter than 128 rows
-    assert n(gqa()) == 2                                   # Llama-3-8B: 256 units -> 512 workgroups
-    assert ws(gqa()) == 2 * 32 * 32 * 128 * 4 + 2 * 32 * 32 * 4
+    # units dividing the CUs (CUs / units = 1 or 2) -> 8-wave workgroups that
+    # fill the CUs once; otherwise >= half a CU's worth -> 4-wave workgroups,
+    # 2 per CU; fewer -> 16-wave workgroups, one per CU; chunks no shorter
+    # than 128 rows
+    assert n(gqa()) == 1                                   # Llama-3-8B: 256 units -> 256 8-wave workgroups
+    assert ws(gqa()) == 0                                  # one split: no partials
     assert n(gqa(64, 32, 32, 128, 8192)) == 1              # ragged MHA: 2048 units
-    assert n(gqa(16, 32, 8, 128, 4096)) == 4               # 128 units -> 4 splits
+    assert n(gqa(16, 32, 8, 128, 4096)) == 2               # 128 units -> 8-wave, 2 splits
+    assert ws(gqa(16, 32, 8, 128, 4096)) == 2 * 16 * 32 * 128 * 4 + 2 * 16 * 32 * 4
+    assert n(gqa(24, 32, 8, 128, 4096)) == 3               # 192 units -> 4-wave, 2 per CU
+    assert n(gqa(48, 32, 8, 128, 4096)) == 2               # 384 units -> 4-wave, 2 per CU
     assert n(gqa(4, 32, 8, 128, 4096)) == 8                # 32 units -> 16-wave, 8 splits
     assert n(gqa(8, 8, 1, 128, 4096)) == 32                # MQA B=8: 8 units (8 heads: 4-wave), 128-row floor
     assert n(gqa(1, 4, 2, 64, 128, da.DA_DTYPE_F32)) == 1  # tiny: one split, no workspace

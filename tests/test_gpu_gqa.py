@@ -90,6 +90,11 @@ EDGE = [
     (1, 14, 2, 128, [5000], "bf16"),                   # g=7
     (2, 8, 8, 128, [3000, 5000], "bf16"),              # 16 units: 16-wave workgroups, 16 splits
     (1, 32, 4, 128, [6000], "bf16"),                   # 8 heads per workgroup: 4-wave, 47 splits
+    # units dividing the 256 CUs: 8-wave workgroups
+    (16, 32, 8, 128, [4096, 1, 0, 2000, 129, 4095, 77, 3000,
+                      1024, 33, 2500, 4096, 0, 640, 1500, 2], "bf16"),   # 128 units: 2 splits
+    (256, 8, 1, 128, [(37 * i) % 301 for i in range(256)], "bf16"),     # 8 heads per workgroup, 1 split
+    (32, 32, 8, 64, [(97 * i) % 700 + 1 for i in range(32)], "f32"),    # fp32, 1 split
 ]
 
 
