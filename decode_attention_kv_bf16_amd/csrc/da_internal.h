@@ -22,7 +22,8 @@ struct GqaArgs {
   int64_t kv_sb, kv_st, kv_sh;
   int32_t batch, num_q_heads, num_kv_heads, group;   // group = Hq / Hkv
   int32_t heads_per_block;   // query heads one workgroup serves (divides group)
-  int32_t waves_per_block;   // 4 or 16
+  int32_t waves_per_block;   // 4, 8 or 16
+  int32_t order_by_length;   // 1: workgroups take sequences longest first (needs batch <= 256)
   int32_t max_seq_len, num_splits, chunk;            // chunk = tokens per split
   float scale_log2;          // softmax_scale * log2(e)
 };

@@ -118,6 +118,30 @@ __device__ __forceinline__ constexpr int rs_src_reg(int h) {
   return GH >= 4 ? h % (GH / 4) : 0;
 }
 
+// The sequence of rank r when the batch is ordered by length, longest first
+// (ties by index, so the ranks are a permutation). Workgroups are dispatched
+// in id order, so giving the lowest ids the longest sequences lets the short
+// ones fill the end of a ragged batch (longest-processing-time-first
+// scheduling). B <= 256; every thread of the workgroup takes part.
+template <int kThreads>
+__device__ __forceinline__ int longest_first(const int32_t* seq_lens, int B, int r) {
+  __shared__ int s_len[256];
+  __shared__ int s_pick;
+  for (int i = threadIdx.x; i < B; i += kThreads) s_len[i] = seq_lens[i];
+  __syncthreads();
+  for (int c = threadIdx.x; c < B; c += kThreads) {
+    const int lc = s_len[c];
+    int rank = 0;
+    for (int j = 0; j < B; ++j) {
+      const int lj = s_len[j];
+      rank += (lj > lc) | ((lj == lc) & (j < c));
+    }
+    if (rank == r) s_pick = c;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(s_pick);
+}
+
 template <typename T, int D, int GH, int kWaves>
 __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
   constexpr int kThreads = kWaves * 64;
@@ -128,7 +152,7 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
   using R = Row8<T>;
 
   const int split = blockIdx.x;
-  const int b = blockIdx.z;
+  const int b = a.order_by_length ? longest_first<kThreads>(a.seq_lens, a.batch, blockIdx.z) : blockIdx.z;
   const int n_sub = a.group / GH;
   const int kvh = blockIdx.y / n_sub;
   const int h0 = kvh * a.group + (blockIdx.y % n_sub) * GH;

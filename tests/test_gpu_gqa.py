@@ -95,6 +95,9 @@ EDGE = [
                       1024, 33, 2500, 4096, 0, 640, 1500, 2], "bf16"),   # 128 units: 2 splits
     (256, 8, 1, 128, [(37 * i) % 301 for i in range(256)], "bf16"),     # 8 heads per workgroup, 1 split
     (32, 32, 8, 64, [(97 * i) % 700 + 1 for i in range(32)], "f32"),    # fp32, 1 split
+    # 2048 workgroups, more than stay resident: sequences taken longest first,
+    # with equal lengths (ties by index) and empty sequences
+    (64, 32, 32, 128, [(i % 5) * 97 + (i % 3) for i in range(64)], "bf16"),
 ]
 
 
