@@ -117,7 +117,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_raw_rsrc(const void* base
 // (vmcnt(0)), because the compiler cannot tell which LDS bytes a copy writes.
 // Completion is waited for explicitly with wait_vm<N>() instead. The asm has
 // no output register (the data goes to LDS); M0, which holds the LDS address,
-// is saved and restored around it.
+// is saved and restored around it. The cache rows are read once, so the copy
+// is non-temporal (`nt`): measured 1.7% faster for the attention kernel, which
+// runs at the board's power limit, where moving the cache in from HBM takes
+// about a quarter of its time.
 __device__ __forceinline__ void buffer_load_to_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset,
                                                      uint32_t lds_addr) {
   uint32_t saved_m0;
@@ -125,7 +128,7 @@ __device__ __forceinline__ void buffer_load_to_lds16(__amdgpu_buffer_rsrc_t rsrc
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen nt lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved_m0)
       : "v"(voffset), "s"(rsrc), "s"(lds_addr)
