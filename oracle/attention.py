@@ -207,3 +207,55 @@ def combine_ref(partial_out: np.ndarray, partial_lse: np.ndarray):
     po_safe = np.where(np.isfinite(pl)[..., None], po, 0.0)
     out = np.einsum("s...,s...d->...d", coef, po_safe)
     return out, lse
+
+
+# ----------------------------------------------------------------------------
+# paged KV caches
+# ----------------------------------------------------------------------------
+
+def paged_rows_ref(pool: np.ndarray, table_row, page_size: int, seq_len: int) -> np.ndarray:
+    """The first ``seq_len`` cached rows of one sequence held in a paged pool.
+
+    The cache of a sequence is cut into fixed-size blocks of ``page_size``
+    tokens that live anywhere in a shared pool [num_pages, page_size, ...];
+    the sequence's block table maps its logical block j to a physical page,
+    and the kernel consults that table when it reads the cache
+    (arganzheng.life, section 6.1 on paging: PagedAttention's blocks of 16
+    tokens by default, the logical-to-physical map looked up on every KV
+    read). Token t is therefore row t mod page_size of page table_row[t //
+    page_size]. Only the blocks that hold rows are read.
+    """
+    n_blocks = -(-int(seq_len) // page_size)
+    pages = np.asarray(table_row[:n_blocks], dtype=np.int64)
+    rows = pool[pages].reshape((n_blocks * page_size,) + pool.shape[2:])
+    return rows[:seq_len]
+
+
+def gqa_decode_paged_ref(q, k_pool, v_pool, block_table, page_size: int, seq_lens, scale: float):
+    """GQA decode over paged K and V pools [num_pages, page_size, Hkv, D]:
+    each sequence's rows are gathered in logical order (paged_rows_ref), then
+    attended exactly as by gqa_decode_ref."""
+    seq_lens = np.asarray(seq_lens, np.int64)
+    B = q.shape[0]
+    L = int(max(1, seq_lens.max(initial=0)))
+    k = np.zeros((B, L) + k_pool.shape[2:])
+    v = np.zeros((B, L) + v_pool.shape[2:])
+    for b in range(B):
+        Lb = int(seq_lens[b])
+        k[b, :Lb] = paged_rows_ref(k_pool, block_table[b], page_size, Lb)
+        v[b, :Lb] = paged_rows_ref(v_pool, block_table[b], page_size, Lb)
+    return gqa_decode_ref(q, k, v, seq_lens, scale)
+
+
+def mla_absorbed_paged_ref(q_nope, q_rope, cache_pool, block_table, page_size: int, seq_lens,
+                           w_uk, w_uv, scale: float, kv_lora_rank: int = 512):
+    """Absorbed MLA decode over a paged latent pool [num_pages, page_size,
+    d_c + d_rope]: rows gathered as by paged_rows_ref, then mla_absorbed_ref."""
+    seq_lens = np.asarray(seq_lens, np.int64)
+    B = q_nope.shape[0]
+    L = int(max(1, seq_lens.max(initial=0)))
+    cache = np.zeros((B, L) + cache_pool.shape[2:])
+    for b in range(B):
+        Lb = int(seq_lens[b])
+        cache[b, :Lb] = paged_rows_ref(cache_pool, block_table[b], page_size, Lb)
+    return mla_absorbed_ref(q_nope, q_rope, cache, seq_lens, w_uk, w_uv, scale, kv_lora_rank)

@@ -388,3 +388,101 @@ def test_planted_dropped_empty_split_guard_is_caught():
     assert np.isnan(naive).any()
     o, _ = combine_ref(po, pl)
     assert np.isfinite(o).all()
+
+
+# ----------------------------------------------------------------------------
+# paged caches (arganzheng.life section 6.1: blocks of page_size tokens in a
+# shared pool, found through a per-sequence block table)
+# ----------------------------------------------------------------------------
+
+import workloads as W
+from oracle.attention import gqa_decode_paged_ref, mla_absorbed_paged_ref
+
+
+def brute_paged_gqa(q, k_pool, v_pool, table, ps, seq_lens, scale):
+    """Scalar loops that look every row up in the block table themselves."""
+    B, Hq, D = q.shape
+    Hkv = k_pool.shape[2]
+    g = Hq // Hkv
+    out = np.zeros((B, Hq, D))
+    lse = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            kv = h // g
+            rows = [(int(table[b][t // ps]), t % ps) for t in range(int(seq_lens[b]))]
+            if not rows:
+                continue
+            s = [scale * math.fsum(q[b, h, d] * k_pool[p, r, kv, d] for d in range(D)) for p, r in rows]
+            m = max(s)
+            w = [math.exp(x - m) for x in s]
+            z = math.fsum(w)
+            lse[b, h] = m + math.log(z)
+            for d in range(D):
+                out[b, h, d] = math.fsum(w[j] * v_pool[p, r, kv, d] for j, (p, r) in enumerate(rows)) / z
+    return out, lse
+
+
+def paged_case(B, Hq, Hkv, D, lens, ps, seed, spare=3):
+    rng = np.random.default_rng(seed)
+    L = max(1, max(lens))
+    q = rng.standard_normal((B, Hq, D))
+    k = rng.standard_normal((B, L, Hkv, D))
+    v = rng.standard_normal((B, L, Hkv, D))
+    table, n = W.make_block_table(lens, ps, seed=seed, spare_pages=spare)
+    kp = W.paginate(k, lens, table, n, ps, np.nan)
+    vp = W.paginate(v, lens, table, n, ps, np.nan)
+    return q, k, v, kp, vp, table
+
+
+@pytest.mark.parametrize("ps,lens", [(2, [5, 1, 0, 4]), (4, [9, 3, 8]), (1, [3, 2])])
+def test_paged_gqa_brute_force(ps, lens):
+    q, k, v, kp, vp, table = paged_case(len(lens), 4, 2, 3, lens, ps, seed=5)
+    o, l = gqa_decode_paged_ref(q, kp, vp, table, ps, lens, 0.7)
+    bo, bl = brute_paged_gqa(q, kp, vp, table, ps, lens, 0.7)
+    np.testing.assert_allclose(o, bo, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(np.isfinite(l), np.isfinite(bl))
+    np.testing.assert_allclose(l[np.isfinite(l)], bl[np.isfinite(bl)], rtol=1e-12, atol=1e-12)
+
+
+def test_paged_gqa_equals_contiguous_and_ignores_physical_order():
+    lens = [37, 16, 0, 1, 64]
+    q, k, v, kp, vp, table = paged_case(5, 8, 2, 16, lens, 16, seed=6)
+    o, l = gqa_decode_paged_ref(q, kp, vp, table, 16, lens, 0.25)
+    ro, rl = gqa_decode_ref(q, k, v, lens, 0.25)     # the contiguous cache the pool was built from
+    np.testing.assert_array_equal(o, ro)
+    np.testing.assert_array_equal(l, rl)
+    # another physical placement of the same pages: the same result
+    t2, n2 = W.make_block_table(lens, 16, seed=99, spare_pages=5)
+    o2, l2 = gqa_decode_paged_ref(q, W.paginate(k, lens, t2, n2, 16, np.nan), W.paginate(v, lens, t2, n2, 16, np.nan),
+                                  t2, 16, lens, 0.25)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(l, l2)
+
+
+def test_paged_mla_equals_contiguous():
+    rng = np.random.default_rng(8)
+    B, H, dc, dr, dn = 3, 4, 8, 2, 5
+    lens = [20, 0, 7]
+    L = 20
+    qn, qr = rng.standard_normal((B, H, dn)), rng.standard_normal((B, H, dr))
+    cache = rng.standard_normal((B, L, dc + dr))
+    wuk, wuv = rng.standard_normal((H, dc, dn)), rng.standard_normal((H, dc, 6))
+    table, n = W.make_block_table(lens, 4, seed=3)
+    pool = W.paginate(cache, lens, table, n, 4, np.nan)
+    o, l = mla_absorbed_paged_ref(qn, qr, pool, table, 4, lens, wuk, wuv, 0.3, kv_lora_rank=dc)
+    ro, rl = mla_absorbed_ref(qn, qr, cache, lens, wuk, wuv, 0.3, kv_lora_rank=dc)
+    np.testing.assert_array_equal(o, ro)
+    np.testing.assert_array_equal(l, rl)
+
+
+def test_planted_reversed_page_order_is_caught(monkeypatch):
+    def broken(pool, table_row, page_size, seq_len):
+        n_blocks = -(-int(seq_len) // page_size)
+        pages = np.asarray(table_row[:n_blocks], dtype=np.int64)[::-1]   # blocks in the wrong order
+        rows = pool[pages].reshape((n_blocks * page_size,) + pool.shape[2:])
+        return rows[:seq_len]
+    monkeypatch.setattr(OA, "paged_rows_ref", broken)
+    q, k, v, kp, vp, table = paged_case(2, 4, 2, 3, [9, 8], 4, seed=5, spare=0)
+    o, l = OA.gqa_decode_paged_ref(q, kp, vp, table, 4, [9, 8], 0.7)
+    bo, bl = brute_paged_gqa(q, kp, vp, table, 4, [9, 8], 0.7)
+    assert not (np.all(np.isfinite(o)) and np.allclose(o, bo, rtol=1e-9))

@@ -77,3 +77,18 @@ def test_mla_config4_lengths_in_range():
     s = W.CONFIGS[4]
     lens = W.draw_seq_lens(s.batch, None, s.seq_len_range, 4)
     assert lens.min() >= 16384 and lens.max() <= 32768
+
+
+def test_paginate_places_every_row_and_fills_the_rest():
+    lens = [5, 0, 33, 16]
+    table, n = W.make_block_table(lens, 16, seed=4, spare_pages=2)
+    assert n == 1 + 0 + 3 + 1 + 2
+    used = table[table >= 0]
+    assert len(set(used.tolist())) == len(used) and used.max() < n      # pages are distinct and in the pool
+    assert np.all(table[1] == -1) and np.all(table[0, 1:] == -1)
+    cache = np.arange(4 * 40 * 3, dtype=np.int64).reshape(4, 40, 3)
+    pool = W.paginate(cache, lens, table, n, 16, -7)
+    for b, L in enumerate(lens):
+        for t in range(L):
+            np.testing.assert_array_equal(pool[table[b, t // 16], t % 16], cache[b, t])
+    assert (pool == -7).all(axis=-1).sum() == n * 16 - sum(lens)       # everything else is fill

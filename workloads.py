@@ -297,3 +297,40 @@ def make_mla_config(cfg: int, seed: int = BASE_SEED, pad_value: float = 0.0,
                     kv_lora_rank=s.kv_lora_rank, qk_rope_dim=s.qk_rope_dim,
                     qk_nope_dim=s.qk_nope_dim, v_head_dim=s.v_head_dim,
                     pad_value=pad_value, only_seqs=only_seqs)
+
+
+# ----------------------------------------------------------------------------
+# paged caches
+# ----------------------------------------------------------------------------
+
+def make_block_table(seq_lens: Sequence[int], page_size: int, seed: int = BASE_SEED,
+                     spare_pages: int = 3, max_blocks: Optional[int] = None):
+    """A block table for a paged cache: sequence b owns ceil(L_b / page_size)
+    pages, placed at seeded random physical positions of a pool that also
+    holds ``spare_pages`` unused pages. Entries past a sequence's pages are -1.
+    Returns (table [B, max_blocks] int32, number of pages in the pool)."""
+    seq_lens = np.asarray(seq_lens, np.int64)
+    n_blocks = -(-seq_lens // page_size)
+    width = int(max_blocks if max_blocks is not None else max(1, n_blocks.max(initial=0)))
+    assert width >= n_blocks.max(initial=0)
+    num_pages = int(n_blocks.sum()) + spare_pages
+    perm = np.random.default_rng([seed, 77]).permutation(num_pages)
+    table = np.full((len(seq_lens), width), -1, np.int32)
+    k = 0
+    for b, nb in enumerate(n_blocks):
+        table[b, :nb] = perm[k:k + nb]
+        k += int(nb)
+    return table, num_pages
+
+
+def paginate(cache: np.ndarray, seq_lens: Sequence[int], table: np.ndarray, num_pages: int,
+             page_size: int, fill) -> np.ndarray:
+    """Copy rows [0, L_b) of each sequence of a contiguous cache [B, L, ...]
+    into a pool [num_pages, page_size, ...] as the block table says; every
+    other pool row (spare pages, the tail of a last page) holds ``fill``."""
+    pool = np.full((num_pages, page_size) + cache.shape[2:], fill, dtype=cache.dtype)
+    for b, L in enumerate(np.asarray(seq_lens, np.int64)):
+        for j in range(-(-int(L) // page_size)):
+            rows = cache[b, j * page_size:min((j + 1) * page_size, int(L))]
+            pool[int(table[b, j]), :len(rows)] = rows
+    return pool
