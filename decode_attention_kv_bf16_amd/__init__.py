@@ -10,6 +10,9 @@ raises.
     out, lse = gqa_decode(q, k_cache, v_cache, seq_lens)
     out, lse = mla_decode_absorbed(q_nope, q_rope, kv_cache, w_uk, w_uv, seq_lens)
     out, lse = splitkv_combine(partial_out, partial_lse)
+    out, lse = gqa_decode_paged(q, k_pool, v_pool, block_table, page_size, seq_lens)
+    out, lse = mla_decode_absorbed_paged(q_nope, q_rope, cache_pool, block_table, page_size,
+                                         seq_lens, w_uk, w_uv)
 """
 from __future__ import annotations
 
@@ -62,7 +65,19 @@ class MlaParams(ctypes.Structure):
     ]
 
 
+class PagedKv(ctypes.Structure):
+    _fields_ = [
+        ("block_table", ctypes.c_void_p),
+        ("page_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("page_stride", ctypes.c_int64),
+    ]
+
+
 _vp = ctypes.c_void_p
+_GQA_P = ctypes.POINTER(GqaParams)
+_MLA_P = ctypes.POINTER(MlaParams)
+_PAGED_P = ctypes.POINTER(PagedKv)
 _SIGNATURES = {
     "da_gqa_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(GqaParams)]),
     "da_gqa_decode_num_splits": (ctypes.c_int32, [ctypes.POINTER(GqaParams)]),
@@ -81,12 +96,19 @@ _SIGNATURES = {
                                                 _vp, _vp]),
     "da_mla_merge_project": (ctypes.c_int, [ctypes.POINTER(MlaParams), _vp, _vp, _vp, _vp, _vp,
                                             _vp]),
+    "da_gqa_decode_paged": (ctypes.c_int, [_GQA_P, _PAGED_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                           ctypes.c_size_t, _vp]),
+    "da_mla_decode_absorbed_paged": (ctypes.c_int, [_MLA_P, _PAGED_P, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                    _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "da_mla_attend_split_pass_paged": (ctypes.c_int, [_MLA_P, _PAGED_P, _vp, _vp, _vp, _vp, _vp,
+                                                      _vp]),
     "da_splitkv_combine": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]),
     "da_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "da_version": (ctypes.c_int32, []),
     "da_gqa_params_size": (ctypes.c_size_t, []),
     "da_mla_params_size": (ctypes.c_size_t, []),
+    "da_paged_kv_size": (ctypes.c_size_t, []),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -110,7 +132,8 @@ def lib() -> ctypes.CDLL:
         fn.restype = res
         fn.argtypes = args
     if L.da_gqa_params_size() != ctypes.sizeof(GqaParams) or \
-            L.da_mla_params_size() != ctypes.sizeof(MlaParams):
+            L.da_mla_params_size() != ctypes.sizeof(MlaParams) or \
+            L.da_paged_kv_size() != ctypes.sizeof(PagedKv):
         raise RuntimeError("libdecode_attn.so parameter structs do not match this binding")
     _lib = L
     return L
@@ -242,6 +265,73 @@ def gqa_num_splits(q: torch.Tensor, k_cache: torch.Tensor, num_splits: int = 0) 
 
 
 # ----------------------------------------------------------------------------
+# paged pools
+# ----------------------------------------------------------------------------
+
+def paged_kv(block_table: torch.Tensor, page_size: int, pool: torch.Tensor) -> PagedKv:
+    """The paging descriptor for a pool [num_pages, page_size, ...] and a
+    block table [B, max_blocks_per_seq] int32 on the GPU."""
+    _require_cuda("block_table", block_table)
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous int32 tensor [B, max_blocks_per_seq]")
+    if pool.shape[1] != page_size:
+        raise ValueError(f"pool pages hold {pool.shape[1]} rows, page_size is {page_size}")
+    pg = PagedKv()
+    pg.block_table = block_table.data_ptr()
+    pg.page_size = int(page_size)
+    pg.max_blocks_per_seq = block_table.shape[1]
+    pg.page_stride = pool.stride(0)
+    return pg
+
+
+def _check_seq_lens(seq_lens: torch.Tensor, B: int):
+    _require_cuda("seq_lens", seq_lens)
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,) or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 tensor of shape [B]")
+
+
+def gqa_decode_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                     block_table: torch.Tensor, page_size: int, seq_lens: torch.Tensor,
+                     max_seq_len: Optional[int] = None, softmax_scale: Optional[float] = None,
+                     num_splits: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """gqa_decode over paged pools: k_pool, v_pool [num_pages, page_size, Hkv, D];
+    block_table [B, max_blocks_per_seq] int32 (token t of sequence b is row
+    t % page_size of page block_table[b, t // page_size]); seq_lens [B] int32.
+    max_seq_len (default: the table's capacity) bounds every seq_lens[b]."""
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool)):
+        _require_cuda(name, t)
+    if k_pool.dtype != q.dtype or v_pool.dtype != q.dtype:
+        raise ValueError("q, k_pool and v_pool must share a dtype")
+    if v_pool.shape != k_pool.shape or v_pool.stride() != k_pool.stride():
+        raise ValueError("v_pool must have the shape and strides of k_pool")
+    B = q.shape[0]
+    _check_seq_lens(seq_lens, B)
+    pg = paged_kv(block_table, page_size, k_pool)
+    if block_table.shape[0] != B:
+        raise ValueError("block_table must have one row per sequence")
+    if max_seq_len is None:
+        max_seq_len = block_table.shape[1] * page_size
+    if k_pool.shape[3] != q.shape[2] or k_pool.stride(3) != 1:
+        raise ValueError("k_pool must be [num_pages, page_size, Hkv, D] with a contiguous D axis")
+    # the params describe a [B, max_seq_len, Hkv, D] cache with the pool's
+    # token and head strides (the batch stride is unused for paged pools)
+    p = gqa_params(q, k_pool[:1].expand(B, -1, -1, -1), softmax_scale, num_splits)
+    p.max_seq_len = int(max_seq_len)
+    p.kv_stride_b = 0
+    L = lib()
+    Hq, D = q.shape[1], q.shape[2]
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ws_bytes = L.da_gqa_decode_workspace_size(ctypes.byref(p))
+    ws = _workspace(ws_bytes, q.device)
+    st = L.da_gqa_decode_paged(ctypes.byref(p), ctypes.byref(pg), _ptr(q), _ptr(k_pool),
+                               _ptr(v_pool), _ptr(seq_lens), _ptr(out), _ptr(lse), _ptr(ws),
+                               ws_bytes, _stream_handle())
+    _check(st, "da_gqa_decode_paged")
+    return out, lse
+
+
+# ----------------------------------------------------------------------------
 # absorbed MLA
 # ----------------------------------------------------------------------------
 
@@ -311,13 +401,71 @@ def mla_decode_absorbed(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_cache: to
     return out, lse
 
 
+def _mla_paged_params(q_nope, q_rope, cache_pool, w_uv, max_seq_len, softmax_scale,
+                      num_splits) -> MlaParams:
+    # the params describe a [B, max_seq_len, 576] cache with the pool's token
+    # stride (the batch stride is unused for paged pools)
+    p = mla_params(q_nope, cache_pool[:1].expand(q_nope.shape[0], -1, -1), w_uv, q_rope,
+                   softmax_scale, num_splits)
+    p.max_seq_len = int(max_seq_len)
+    p.cache_stride_b = 0
+    return p
+
+
+def mla_decode_absorbed_paged(q_nope: torch.Tensor, q_rope: torch.Tensor, cache_pool: torch.Tensor,
+                              block_table: torch.Tensor, page_size: int, seq_lens: torch.Tensor,
+                              w_uk: torch.Tensor, w_uv: torch.Tensor,
+                              max_seq_len: Optional[int] = None,
+                              softmax_scale: Optional[float] = None,
+                              num_splits: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mla_decode_absorbed over a paged latent pool cache_pool [num_pages,
+    page_size, 576] bf16 and block_table [B, max_blocks_per_seq] int32."""
+    for name, t in (("q_nope", q_nope), ("q_rope", q_rope), ("cache_pool", cache_pool),
+                    ("w_uk", w_uk), ("w_uv", w_uv)):
+        _require_cuda(name, t)
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+    for name, t in (("q_nope", q_nope), ("q_rope", q_rope), ("w_uk", w_uk), ("w_uv", w_uv)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, H, _ = q_nope.shape
+    _check_seq_lens(seq_lens, B)
+    if block_table.shape[0] != B:
+        raise ValueError("block_table must have one row per sequence")
+    pg = paged_kv(block_table, page_size, cache_pool)
+    if max_seq_len is None:
+        max_seq_len = block_table.shape[1] * page_size
+    p = _mla_paged_params(q_nope, q_rope, cache_pool, w_uv, max_seq_len, softmax_scale,
+                          num_splits)
+    L = lib()
+    out = torch.empty((B, H, w_uv.shape[2]), dtype=torch.float32, device=q_nope.device)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q_nope.device)
+    ws_bytes = L.da_mla_decode_workspace_size(ctypes.byref(p))
+    ws = _workspace(ws_bytes, q_nope.device)
+    st = L.da_mla_decode_absorbed_paged(ctypes.byref(p), ctypes.byref(pg), _ptr(q_nope),
+                                        _ptr(q_rope), _ptr(cache_pool), _ptr(seq_lens), _ptr(w_uk),
+                                        _ptr(w_uv), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
+                                        _stream_handle())
+    _check(st, "da_mla_decode_absorbed_paged")
+    return out, lse
+
+
 def mla_stages(q_nope, q_rope, kv_cache, w_uk, w_uv, seq_lens=None, softmax_scale=None,
-               num_splits: int = 0):
+               num_splits: int = 0, paged: Optional[Tuple[torch.Tensor, int, int]] = None):
     """The three stages of mla_decode_absorbed as separate callables sharing
     buffers: returns (absorb, attend, merge, out, lse, buffers). Calling
     absorb(); attend(); merge() in order on one stream fills out and lse exactly
-    as mla_decode_absorbed does."""
-    p = mla_params(q_nope, kv_cache, w_uv, q_rope, softmax_scale, num_splits)
+    as mla_decode_absorbed does. paged = (block_table, page_size, max_seq_len)
+    makes kv_cache a paged pool [num_pages, page_size, 576] and the attend
+    stage da_mla_attend_split_pass_paged."""
+    pg = None
+    if paged is not None:
+        table, page_size, max_seq_len = paged
+        pg = paged_kv(table, page_size, kv_cache)
+        p = _mla_paged_params(q_nope, q_rope, kv_cache, w_uv, max_seq_len, softmax_scale,
+                              num_splits)
+    else:
+        p = mla_params(q_nope, kv_cache, w_uv, q_rope, softmax_scale, num_splits)
     L = lib()
     po_bytes, pl_bytes = ctypes.c_size_t(), ctypes.c_size_t()
     _check(L.da_mla_partials_size(ctypes.byref(p), ctypes.byref(po_bytes), ctypes.byref(pl_bytes)),
@@ -336,9 +484,15 @@ def mla_stages(q_nope, q_rope, kv_cache, w_uk, w_uv, seq_lens=None, softmax_scal
                                      _ptr(q_hat), _stream_handle()), "da_mla_absorb_query")
 
     def attend():
-        _check(L.da_mla_attend_split_pass(ctypes.byref(p), _ptr(q_hat), _ptr(kv_cache),
-                                          _ptr(seq_lens), _ptr(part_out), _ptr(part_lse),
-                                          _stream_handle()), "da_mla_attend_split_pass")
+        if pg is None:
+            _check(L.da_mla_attend_split_pass(ctypes.byref(p), _ptr(q_hat), _ptr(kv_cache),
+                                              _ptr(seq_lens), _ptr(part_out), _ptr(part_lse),
+                                              _stream_handle()), "da_mla_attend_split_pass")
+        else:
+            _check(L.da_mla_attend_split_pass_paged(ctypes.byref(p), ctypes.byref(pg), _ptr(q_hat),
+                                                    _ptr(kv_cache), _ptr(seq_lens), _ptr(part_out),
+                                                    _ptr(part_lse), _stream_handle()),
+                   "da_mla_attend_split_pass_paged")
 
     def merge():
         _check(L.da_mla_merge_project(ctypes.byref(p), _ptr(part_out), _ptr(part_lse), _ptr(w_uv),
@@ -383,5 +537,5 @@ def splitkv_combine(partial_out: torch.Tensor, partial_lse: torch.Tensor,
 
 
 __all__ = ["gqa_decode", "mla_decode_absorbed", "splitkv_combine", "gqa_num_splits",
-           "mla_num_splits", "lib", "LIB_PATH", "GqaParams", "MlaParams", "DecodeAttnError",
-           "LibraryMissing"]
+           "mla_num_splits", "gqa_decode_paged", "mla_decode_absorbed_paged", "paged_kv", "lib",
+           "LIB_PATH", "GqaParams", "MlaParams", "PagedKv", "DecodeAttnError", "LibraryMissing"]

@@ -92,7 +92,9 @@ struct GqaPlan {
   size_t part_out_bytes, part_lse_bytes, workspace;
 };
 
-GqaPlan plan_gqa(const da_gqa_params_t* p) {
+// align: split boundaries on multiples of this many rows (16 for paged
+// pools, so that every 16-row step of the kernel lies in one page)
+GqaPlan plan_gqa(const da_gqa_params_t* p, int align = 1) {
   GqaPlan pl{};
   const int group = p->num_q_heads / p->num_kv_heads;
   pl.heads_per_block = gqa_heads_per_block(group);
@@ -138,7 +140,7 @@ GqaPlan plan_gqa(const da_gqa_params_t* p) {
   }
   if (s > p->max_seq_len) s = p->max_seq_len;
   if (s < 1) s = 1;
-  pl.chunk = (int)ceil_div(p->max_seq_len, s);
+  pl.chunk = (int)round_up((size_t)ceil_div(p->max_seq_len, s), (size_t)align);
   pl.splits = (int)ceil_div(p->max_seq_len, pl.chunk);  // drop splits that would be empty
   if (pl.splits > 1) {
     const size_t rows = (size_t)p->batch * p->num_q_heads;
@@ -222,7 +224,9 @@ MlaPlan plan_mla(const da_mla_params_t* p) {
     if (s < s_min) s = s_min;
     if (s > p->max_seq_len) s = p->max_seq_len;
     if (s < 1) s = 1;
-    pl.chunk = (int)ceil_div(p->max_seq_len, s);
+    // splits start on 32-row tiles (paged pools then have at most two pages
+    // per tile; the contiguous and the paged pass share one layout)
+    pl.chunk = (int)round_up((size_t)ceil_div(p->max_seq_len, s), 32);
     pl.splits = (int)ceil_div(p->max_seq_len, pl.chunk);
     pl.wg_budget = 0;
     pl.slots = pl.splits * p->batch;
@@ -319,6 +323,31 @@ da::GqaArgs gqa_args(const da_gqa_params_t* p, const GqaPlan& pl, const void* q,
   return a;
 }
 
+// Paged pools: a block table in device memory, pages of a power-of-two
+// number of rows >= 16, enough table entries per sequence for max_seq_len.
+da_status_t check_paged(const da_paged_kv_t* pg, int64_t max_seq_len, int64_t elem_bytes) {
+  if (!pg || !pg->block_table || !aligned4(pg->block_table)) return DA_ERR_INVALID_ARGUMENT;
+  const int64_t ps = pg->page_size;
+  if (ps < 16 || ps > (1 << 20) || (ps & (ps - 1)) != 0) return DA_ERR_INVALID_ARGUMENT;
+  if (pg->max_blocks_per_seq < ceil_div(max_seq_len, ps)) return DA_ERR_INVALID_ARGUMENT;
+  if (pg->page_stride <= 0 || (pg->page_stride * elem_bytes) % 16 != 0) return DA_ERR_INVALID_ARGUMENT;
+  return DA_OK;
+}
+
+int log2_exact(int64_t x) {
+  int k = 0;
+  while ((int64_t{1} << k) < x) ++k;
+  return k;
+}
+
+template <typename Args>
+void set_paged(Args& a, const da_paged_kv_t* pg) {
+  a.block_table = pg->block_table;
+  a.page_shift = log2_exact(pg->page_size);
+  a.max_blocks = pg->max_blocks_per_seq;
+  a.page_stride = pg->page_stride;
+}
+
 }  // namespace
 
 
@@ -369,6 +398,39 @@ da_status_t da_gqa_decode(const da_gqa_params_t* p, const void* q, const void* k
     if (!aligned16(workspace)) return DA_ERR_INVALID_ARGUMENT;
   }
   da::GqaArgs a = gqa_args(p, pl, q, k_cache, v_cache, seq_lens);
+  a.out = out;
+  a.lse = lse;
+  if (pl.splits > 1) {
+    a.part_out = reinterpret_cast<float*>(workspace);
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.part_out_bytes);
+  }
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  hipError_t e = da::launch_gqa_decode(a, p->dtype == DA_DTYPE_BF16 ? 1 : 0, p->head_dim, stream);
+  if (e != hipSuccess) return DA_ERR_HIP;
+  if (pl.splits > 1) {
+    e = da::launch_splitkv_combine(pl.splits, p->batch * p->num_q_heads, p->head_dim, a.part_out,
+                                   a.part_lse, out, lse, stream);
+  }
+  return from_hip(e);
+}
+
+da_status_t da_gqa_decode_paged(const da_gqa_params_t* p, const da_paged_kv_t* pages, const void* q,
+                                const void* k_pool, const void* v_pool, const int32_t* seq_lens,
+                                float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                void* hip_stream) {
+  da_status_t st = check_gqa_params(p);
+  if (st != DA_OK) return st;
+  st = check_paged(pages, p->max_seq_len, p->dtype == DA_DTYPE_BF16 ? 2 : 4);
+  if (st != DA_OK) return st;
+  st = check_gqa_buffers(q, k_pool, v_pool, seq_lens, out, lse);
+  if (st != DA_OK) return st;
+  const GqaPlan pl = plan_gqa(p, 16);
+  if (pl.workspace > 0) {
+    if (!workspace || workspace_bytes < pl.workspace) return DA_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned16(workspace)) return DA_ERR_INVALID_ARGUMENT;
+  }
+  da::GqaArgs a = gqa_args(p, pl, q, k_pool, v_pool, seq_lens);
+  set_paged(a, pages);
   a.out = out;
   a.lse = lse;
   if (pl.splits > 1) {
@@ -464,6 +526,58 @@ da_status_t da_mla_attend_split_pass(const da_mla_params_t* p, const void* q_hat
   return from_hip(da::launch_mla_attend(a, static_cast<hipStream_t>(hip_stream)));
 }
 
+da_status_t da_mla_decode_absorbed_paged(const da_mla_params_t* p, const da_paged_kv_t* pages,
+                                         const void* q_nope, const void* q_rope, const void* cache_pool,
+                                         const int32_t* seq_lens, const void* w_uk, const void* w_uv,
+                                         float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                         void* hip_stream) {
+  da_status_t st = check_mla_params(p);
+  if (st != DA_OK) return st;
+  st = check_paged(pages, p->max_seq_len, 2);
+  if (st != DA_OK) return st;
+  st = check_ptrs16({q_nope, q_rope, cache_pool, w_uk, w_uv, out});
+  if (st != DA_OK) return st;
+  if (!aligned4(seq_lens) || !aligned4(lse)) return DA_ERR_INVALID_ARGUMENT;
+  const MlaPlan pl = plan_mla(p);
+  if (!workspace || workspace_bytes < pl.workspace) return DA_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(workspace)) return DA_ERR_INVALID_ARGUMENT;
+  char* ws = static_cast<char*>(workspace);
+  da::MlaArgs a = mla_args(p, pl);
+  set_paged(a, pages);
+  a.q_nope = static_cast<const uint16_t*>(q_nope);
+  a.q_rope = static_cast<const uint16_t*>(q_rope);
+  a.cache = static_cast<const uint16_t*>(cache_pool);
+  a.seq_lens = seq_lens;
+  a.w_uk = static_cast<const uint16_t*>(w_uk);
+  a.w_uv = static_cast<const uint16_t*>(w_uv);
+  a.out = out;
+  a.lse = lse;
+  a.q_hat = reinterpret_cast<uint16_t*>(ws);
+  set_partials(a, pl, ws + pl.q_hat_bytes, ws + pl.q_hat_bytes + pl.part_out_bytes);
+  return from_hip(da::launch_mla_decode(a, static_cast<hipStream_t>(hip_stream)));
+}
+
+da_status_t da_mla_attend_split_pass_paged(const da_mla_params_t* p, const da_paged_kv_t* pages,
+                                           const void* q_hat, const void* cache_pool,
+                                           const int32_t* seq_lens, void* part_out, float* part_lse,
+                                           void* hip_stream) {
+  da_status_t st = check_mla_params(p);
+  if (st != DA_OK) return st;
+  st = check_paged(pages, p->max_seq_len, 2);
+  if (st != DA_OK) return st;
+  st = check_ptrs16({q_hat, cache_pool, part_out, part_lse});
+  if (st != DA_OK) return st;
+  if (!aligned4(seq_lens)) return DA_ERR_INVALID_ARGUMENT;
+  const MlaPlan pl = plan_mla(p);
+  da::MlaArgs a = mla_args(p, pl);
+  set_paged(a, pages);
+  a.q_hat = static_cast<uint16_t*>(const_cast<void*>(q_hat));
+  a.cache = static_cast<const uint16_t*>(cache_pool);
+  a.seq_lens = seq_lens;
+  set_partials(a, pl, part_out, part_lse);
+  return from_hip(da::launch_mla_attend(a, static_cast<hipStream_t>(hip_stream)));
+}
+
 da_status_t da_mla_merge_project(const da_mla_params_t* p, const void* part_out,
                                  const float* part_lse, const void* w_uv, float* out, float* lse,
                                  void* hip_stream) {
@@ -514,5 +628,6 @@ int32_t da_version(void) { return 100; }
 
 size_t da_gqa_params_size(void) { return sizeof(da_gqa_params_t); }
 size_t da_mla_params_size(void) { return sizeof(da_mla_params_t); }
+size_t da_paged_kv_size(void) { return sizeof(da_paged_kv_t); }
 
 }  // extern "C"

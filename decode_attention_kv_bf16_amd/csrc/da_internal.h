@@ -26,6 +26,13 @@ struct GqaArgs {
   int32_t order_by_length;   // 1: workgroups take sequences longest first (needs batch <= 256)
   int32_t max_seq_len, num_splits, chunk;            // chunk = tokens per split
   float scale_log2;          // softmax_scale * log2(e)
+  // Paged K/V pools (page_shift > 0): token t of sequence b is row
+  // t & (2^page_shift - 1) of page block_table[b * max_blocks + (t >> page_shift)]
+  // of each pool, pages page_stride elements apart; kv_sb is then unused.
+  // chunk is a multiple of 16, so each 16-token step lies in one page.
+  const int32_t* block_table;
+  int32_t page_shift, max_blocks;
+  int64_t page_stride;
 };
 
 // dtype: 0 = f32, 1 = bf16 (matches da_dtype_t).
@@ -66,12 +73,31 @@ struct MlaArgs {
   int32_t wg_budget;         // balanced: tiles are spread over this many workgroups
   int32_t slots;             // rows of part_out / H
   float scale_log2;
+  // Paged latent pool (page_shift > 0): token t of sequence b is row
+  // t & (2^page_shift - 1) of page block_table[b * max_blocks + (t >> page_shift)],
+  // pages page_stride elements apart; cache_sb is then unused. Splits start
+  // on 32-row tiles, so a tile spans at most two pages.
+  const int32_t* block_table;
+  int32_t page_shift, max_blocks;
+  int64_t page_stride;
 };
 
 hipError_t launch_mla_absorb(const MlaArgs& a, hipStream_t stream);
 hipError_t launch_mla_attend(const MlaArgs& a, hipStream_t stream);
 hipError_t launch_mla_merge_project(const MlaArgs& a, hipStream_t stream);
 hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream);  // all three
+
+// Entry i of a paged cache's block table, read through the constant address
+// space: the table is not written while a kernel runs, and so read, a load at
+// a wave-uniform index becomes a scalar load (s_load). That load is counted
+// by the scalar/LDS counter, not by the vector-memory counter that waits for
+// cache rows, so waiting for it does not wait for rows in flight. The
+// compiler makes a wave-uniform load from global memory a vector load when
+// it cannot prove the memory unwritten, with exactly that wait.
+__device__ __forceinline__ int32_t table_entry(const int32_t* table, int64_t i) {
+  typedef const __attribute__((address_space(4))) int32_t ConstI32;
+  return ((ConstI32*)table)[i];
+}
 
 // Workgroups of the MLA attention kernel for `num_heads` that one CU holds at
 // once on the current device; 0 if the device cannot be queried.

@@ -156,11 +156,12 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
   const int n_sub = a.group / GH;
   const int kvh = blockIdx.y / n_sub;
   const int h0 = kvh * a.group + (blockIdx.y % n_sub) * GH;
-  const int L = a.seq_lens ? a.seq_lens[b] : a.max_seq_len;
+  // clamped to [0, max_seq_len]: no read past the cache or the block table
+  const int L = a.seq_lens ? min(max(a.seq_lens[b], 0), a.max_seq_len) : a.max_seq_len;
   const int t_begin = split * a.chunk;
   const int t_end = min(L, t_begin + a.chunk);
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = lane / LPT;
   const int col = lane % LPT;
   const bool direct = a.num_splits == 1;
@@ -229,16 +230,35 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
   (void)ms;
   (void)ls;
 
-  const T* kp = reinterpret_cast<const T*>(a.k) + b * a.kv_sb + kvh * a.kv_sh + col * kEPL;
-  const T* vp = reinterpret_cast<const T*>(a.v) + b * a.kv_sb + kvh * a.kv_sh + col * kEPL;
+  // Paged pools (arganzheng.life section 6.1): the 16 rows of a step lie in
+  // one page (steps start on multiples of 16 and pages hold a power of two
+  // >= 16 rows), found in the block table. A step's entry is read one step
+  // before its rows are loaded and carried as the loaded value; its offset
+  // is computed before the next entry is read, so the wait for it falls on a
+  // load that completed with the previous step's rows. The index is clamped
+  // to the last row (t_end > 0 wherever this runs), so every read is valid
+  // and unconditional.
+  const bool paged = a.page_shift > 0;
+  const int64_t tab0 = (int64_t)b * a.max_blocks;
+  const int64_t kv_b = paged ? 0 : (int64_t)b * a.kv_sb;
+  const T* kp = reinterpret_cast<const T*>(a.k) + kv_b + kvh * a.kv_sh + col * kEPL;
+  const T* vp = reinterpret_cast<const T*>(a.v) + kv_b + kvh * a.kv_sh + col * kEPL;
+  auto step_page = [&](int base) -> int {
+    return paged ? table_entry(a.block_table, tab0 + (min(base, t_end - 1) >> a.page_shift)) : 0;
+  };
+  // element offset of the first row of the step at `base` (page: its entry)
+  auto step_off = [&](int base, int page) -> int64_t {
+    if (!paged) return (int64_t)base * a.kv_st;
+    return (int64_t)page * a.page_stride + (int64_t)(base & ((1 << a.page_shift) - 1)) * a.kv_st;
+  };
 
-  auto load_step = [&](int base, typename R::Raw (&kk)[U], typename R::Raw (&vv)[U]) {
+  auto load_step = [&](int base, int64_t off, typename R::Raw (&kk)[U], typename R::Raw (&vv)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = base + u * RPW + row;
       if (base < t_end && t < t_end) {
-        kk[u] = R::load(kp + (int64_t)t * a.kv_st);
-        vv[u] = R::load(vp + (int64_t)t * a.kv_st);
+        kk[u] = R::load(kp + off + (int64_t)(t - base) * a.kv_st);
+        vv[u] = R::load(vp + off + (int64_t)(t - base) * a.kv_st);
       } else {
         kk[u] = R::zero();
         vv[u] = R::zero();
@@ -249,14 +269,24 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
   // before the math of this one, two steps in flight per wave (ragged MHA
   // B = 64: 688 -> 680 us). With more heads per workgroup it measured slower.
   constexpr bool kPrefetch = kBf16 && GH == 1;
+  constexpr int kStep = kWaves * TOK;
   typename R::Raw kw[U], vw[U];
-  if constexpr (kPrefetch) load_step(t_begin + wave * TOK, kw, vw);
-  for (int base = t_begin + wave * TOK; base < t_end; base += kWaves * TOK) {
+  // page_n: table entry of the next step whose rows are loaded
+  int page_n = step_page(t_begin + wave * TOK);
+  if constexpr (kPrefetch) {
+    load_step(t_begin + wave * TOK, step_off(t_begin + wave * TOK, page_n), kw, vw);
+    page_n = step_page(t_begin + wave * TOK + kStep);
+  }
+  for (int base = t_begin + wave * TOK; base < t_end; base += kStep) {
     typename R::Raw kn[U], vn[U];
     if constexpr (kPrefetch) {
-      load_step(base + kWaves * TOK, kn, vn);
+      const int64_t off = step_off(base + kStep, page_n);
+      page_n = step_page(base + 2 * kStep);
+      load_step(base + kStep, off, kn, vn);
     } else {
-      load_step(base, kw, vw);
+      const int64_t off = step_off(base, page_n);
+      page_n = step_page(base + kStep);
+      load_step(base, off, kw, vw);
     }
     if constexpr (kRS) {
       float v[kRsN];
@@ -457,7 +487,7 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
 // instantiations that fit without spilling.
 template <typename T, int GH>
 constexpr bool wide_fits() {
-  return sizeof(T) == 2 ? GH <= 5 : GH <= 2;
+  return sizeof(T) == 2 ? GH <= 4 : GH <= 2;
 }
 
 template <typename T, int D, int GH>
@@ -496,7 +526,7 @@ hipError_t launch_gh(const GqaArgs& a, hipStream_t st) {
 }  // namespace
 
 bool gqa_wide_supported(int dtype, int heads_per_block) {
-  return dtype == 1 ? heads_per_block <= 5 : heads_per_block <= 2;
+  return dtype == 1 ? heads_per_block <= 4 : heads_per_block <= 2;
 }
 
 hipError_t launch_gqa_decode(const GqaArgs& a, int dtype, int head_dim, hipStream_t st) {

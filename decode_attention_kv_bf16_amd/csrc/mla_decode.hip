@@ -135,6 +135,31 @@ __device__ __forceinline__ void buffer_load_to_lds16(__amdgpu_buffer_rsrc_t rsrc
       : "memory");
 }
 
+// Two block-table entries of a paged pool, read with scalar loads that are
+// issued together and waited for once, inside this block (so no load is left
+// in flight when it ends). Written by hand because the compiler, short of
+// scalar registers here, uses the first entry before issuing the second
+// load, and so waits twice.
+__device__ __forceinline__ void load_two_entries(const int32_t* p0, const int32_t* p1, int32_t& e0,
+                                                 int32_t& e1) {
+  asm volatile(
+      "s_load_dword %0, %2, 0x0\n\t"
+      "s_load_dword %1, %3, 0x0\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&s"(e0), "=&s"(e1)
+      : "s"(p0), "s"(p1)
+      : "memory");
+}
+
+// Where the rows of one tile come from in a paged pool: a 32-row tile that
+// starts on a multiple of 32 is two halves of 16 rows, each inside one page
+// of >= 16 rows, and 16 rows (18 KiB) are exactly 18 of the tile's 1 KiB
+// copies, so each copy reads from one half, through that half's buffer
+// resource (its page, sized to its valid rows).
+struct PagedTile {
+  __amdgpu_buffer_rsrc_t half[2];
+};
+
 // ---------------------------------------------------------------------------
 // 1. query absorption
 // ---------------------------------------------------------------------------
@@ -240,7 +265,8 @@ __device__ SplitWork assign_split(const MlaArgs& a, int lane, bool publish) {
   if (a.num_splits > 0) {
     r.b = blockIdx.y;
     r.slot = blockIdx.x * a.batch + blockIdx.y;
-    const int L = a.seq_lens ? a.seq_lens[r.b] : a.max_seq_len;
+    // clamped to [0, max_seq_len]: no read past the cache or the block table
+    const int L = a.seq_lens ? min(max(a.seq_lens[r.b], 0), a.max_seq_len) : a.max_seq_len;
     r.t_begin = blockIdx.x * a.chunk;
     r.t_end = min(L, r.t_begin + a.chunk);
     r.valid = true;
@@ -315,7 +341,7 @@ __device__ SplitWork assign_split(const MlaArgs& a, int lane, bool publish) {
 // wave may hold its 256 accumulator registers plus the 144 registers of its
 // absorbed queries). Every wave reads each 32-row tile from LDS once and
 // feeds both of its head blocks from that read.
-template <int NW, int HB>
+template <int NW, int HB, bool kPaged>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_attend_kernel(MlaArgs a) {
   // LDS ring of kDepth tiles: up to kDepth - 1 tiles in flight from HBM while
@@ -353,13 +379,14 @@ void mla_attend_kernel(MlaArgs a) {
   // computed once. Each tile gets a buffer resource that ends at the split's
   // last row, so rows past it read as zeros (their weights are zero anyway).
   const uint32_t row_bytes = (uint32_t)a.cache_st * 2u;
+  // byte offset of the lane's chunk in the tile (paged: in its half-tile)
   uint32_t voff[kCopies];
 #pragma unroll
   for (int i = 0; i < kCopies; ++i) {
     const int p = (w + NW * i) * 64 + lane;
     const int row = p / kChunks;
     const int c = (p - row * kChunks) ^ row_swizzle(row);
-    voff[i] = (uint32_t)row * row_bytes + 16u * (uint32_t)c;
+    voff[i] = (uint32_t)(kPaged ? row & 15 : row) * row_bytes + 16u * (uint32_t)c;
   }
   // LDS destinations are computed in scalar registers: this wave's first copy
   // slot of ring buffer 0, as a byte address
@@ -367,17 +394,59 @@ void mla_attend_kernel(MlaArgs a) {
   // Tiles past the split's end get an empty range: their copies read nothing
   // and fill the (unused) ring buffer with zeros, which keeps the number of
   // copies in flight, and so every wait below, the same on every tile.
-  auto tile_rsrc = [&](int it) {
+  //
+  // Paged pools (arganzheng.life section 6.1): each half-tile's page is
+  // looked up in the block table with a scalar load. Both lookups are
+  // unconditional, at rows clamped to the split's last row (t_end > t_begin
+  // here, so the entry is always one of the sequence's), so they are issued
+  // together and waited for once; a half with no valid rows gets an empty
+  // resource.
+  const int64_t tab0 = (int64_t)b * a.max_blocks;
+  auto tile_src = [&](int it) {
     const int t0 = t_begin + it * kTok;
-    return make_raw_rsrc(cache_b + (int64_t)t0 * a.cache_st, (uint32_t)max(t_end - t0, 0) * row_bytes);
+    if constexpr (kPaged) {
+      int32_t page[2];
+      load_two_entries(a.block_table + tab0 + (min(t0, t_end - 1) >> a.page_shift),
+                       a.block_table + tab0 + (min(t0 + 16, t_end - 1) >> a.page_shift), page[0], page[1]);
+      PagedTile pt;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int th = t0 + 16 * hf;
+        // (the clamp is a vector instruction: made scalar again for the resource)
+        const int rows = __builtin_amdgcn_readfirstlane(min(max(t_end - th, 0), 16));
+        const uint16_t* base = a.cache + (int64_t)page[hf] * a.page_stride +
+                               (int64_t)(th & ((1 << a.page_shift) - 1)) * a.cache_st;
+        pt.half[hf] = make_raw_rsrc(base, (uint32_t)rows * row_bytes);
+      }
+      return pt;
+    } else {
+      return make_raw_rsrc(cache_b + (int64_t)t0 * a.cache_st, (uint32_t)max(t_end - t0, 0) * row_bytes);
+    }
   };
-  auto issue_copy = [&](__amdgpu_buffer_rsrc_t rsrc, int i, int buf) {
-    buffer_load_to_lds16(rsrc, voff[i], lds_w0 + (uint32_t)(buf * kTileB + NW * i * 1024));
+  using TileSrc = decltype(tile_src(0));
+  // the compiler waits for a tile's table lookups where this is called, when
+  // no LDS read is in flight (LDS reads and scalar loads share one counter)
+  auto settle = [&](const TileSrc& src) {
+    if constexpr (kPaged) asm volatile("" ::"s"(src.half[0]), "s"(src.half[1]));
+  };
+  auto issue_copy = [&](const TileSrc& src, int i, int buf) {
+    const uint32_t dst = lds_w0 + (uint32_t)(buf * kTileB + NW * i * 1024);
+    if constexpr (kPaged) {
+      // copy w + NW i reads the second half-tile iff it is >= kTileDma / 2;
+      // known at compile time (for an unrolled i) unless the copies of step i
+      // straddle it; wave-uniform in any case
+      constexpr int kHalf = kTileDma / 2;
+      const int second = NW * i >= kHalf ? 1 : NW * i + NW <= kHalf ? 0 : (w + NW * i >= kHalf);
+      buffer_load_to_lds16(__builtin_amdgcn_readfirstlane(second) ? src.half[1] : src.half[0], voff[i], dst);
+    } else {
+      buffer_load_to_lds16(src, voff[i], dst);
+    }
   };
   auto issue_tile = [&](int it, int buf) {
-    const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc(it);
+    const TileSrc src = tile_src(it);
+    settle(src);
 #pragma unroll
-    for (int i = 0; i < kCopies; ++i) issue_copy(rsrc, i, buf);
+    for (int i = 0; i < kCopies; ++i) issue_copy(src, i, buf);
   };
 
   // absorbed queries of this lane's heads, as B operands: q^[h][32ks + 8q4 .. +8]
@@ -426,9 +495,8 @@ void mla_attend_kernel(MlaArgs a) {
   // the scheduling fences keep the compiler from hoisting every read (which
   // would need more registers than a wave has).
   constexpr int kSRing = 3;
-  auto score_tile = [&](int it, int refill_it, f32x4_t (&s)[HB][2]) {
+  auto score_tile = [&](int it, int refill_it, const TileSrc& refill_src, f32x4_t (&s)[HB][2]) {
     const int refill_buf = refill_it % kDepth;
-    const __amdgpu_buffer_rsrc_t refill_rsrc = tile_rsrc(refill_it);
     const LDS uint8_t* tile = lds + (it % kDepth) * kTileB;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) s[hb][0] = s[hb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -443,7 +511,7 @@ void mla_attend_kernel(MlaArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
 #pragma unroll
-      for (int i = ks * kCopies / 18; i < (ks + 1) * kCopies / 18; ++i) issue_copy(refill_rsrc, i, refill_buf);
+      for (int i = ks * kCopies / 18; i < (ks + 1) * kCopies / 18; ++i) issue_copy(refill_src, i, refill_buf);
       if (ks + kSRing - 1 < 18) read_s(ks + kSRing - 1);
       const bf16x8_t a0 = as_bf16x8(ra0[ks % kSRing]);
       const bf16x8_t a1 = as_bf16x8(ra1[ks % kSRing]);
@@ -573,9 +641,11 @@ void mla_attend_kernel(MlaArgs a) {
       for (int j = 0; j < 2; ++j) issue_tile(j, j);
       bf16x8_t pb[HB];
       {
+        const TileSrc refill = tile_src(2);
         wait_vm<kCopies>();  // tile 0 has landed, tile 1 may be pending
         tile_barrier();
-        score_tile(0, 2, s);
+        settle(refill);
+        score_tile(0, 2, refill, s);
         softmax_ref(0, s);
         float p[8 * HB];
 #pragma unroll
@@ -585,9 +655,11 @@ void mla_attend_kernel(MlaArgs a) {
       for (int it = 1; it < ntiles; ++it) {
         // tile `it` has landed once only the copies of tile it + 1 are pending;
         // after the barrier every wave is also done with tile it - 2's buffer
+        const TileSrc refill = tile_src(it + 2);
         wait_vm<kCopies>();
         tile_barrier();
-        score_tile(it, it + 2, s);
+        settle(refill);
+        score_tile(it, it + 2, refill, s);
         pv_start((it - 1) % kDepth);
         softmax_ref(it, s);
         float p[8 * HB];
@@ -606,9 +678,11 @@ void mla_attend_kernel(MlaArgs a) {
         // tile `it` has landed once only the copies of the kDepth - 2 tiles
         // after it are pending; the buffer refilled in this iteration was last
         // read in iteration it - 1
+        const TileSrc refill = tile_src(it + kDepth - 1);
         wait_vm<(kDepth - 2) * kCopies>();
         tile_barrier();
-        score_tile(it, it + kDepth - 1, s);
+        settle(refill);
+        score_tile(it, it + kDepth - 1, refill, s);
         pv_start(it % kDepth);
         softmax_ref(it, s);
         float p[8 * HB];
@@ -835,31 +909,31 @@ hipError_t launch_mla_absorb(const MlaArgs& a, hipStream_t st) {
 
 // Head counts with an attention shape: NW waves of HB blocks of 16 heads, NW
 // dividing the 36 copies of a tile.
-template <typename F>
+template <bool kPaged, typename F>
 bool with_attend_shape(int num_heads, F&& f) {
   switch (num_heads) {
-    case 16: f(mla_attend_kernel<1, 1>, 1); return true;
-    case 32: f(mla_attend_kernel<2, 1>, 2); return true;
-    case 48: f(mla_attend_kernel<3, 1>, 3); return true;
-    case 64: f(mla_attend_kernel<4, 1>, 4); return true;
-    case 96: f(mla_attend_kernel<3, 2>, 3); return true;
-    case 128: f(mla_attend_kernel<4, 2>, 4); return true;
+    case 16: f(mla_attend_kernel<1, 1, kPaged>, 1); return true;
+    case 32: f(mla_attend_kernel<2, 1, kPaged>, 2); return true;
+    case 48: f(mla_attend_kernel<3, 1, kPaged>, 3); return true;
+    case 64: f(mla_attend_kernel<4, 1, kPaged>, 4); return true;
+    case 96: f(mla_attend_kernel<3, 2, kPaged>, 3); return true;
+    case 128: f(mla_attend_kernel<4, 2, kPaged>, 4); return true;
     default: return false;
   }
 }
 
 hipError_t launch_mla_attend(const MlaArgs& a, hipStream_t st) {
   const dim3 grid = a.num_splits > 0 ? dim3(a.num_splits, a.batch) : dim3(a.slots, 1);
-  const bool ok = with_attend_shape(a.num_heads, [&](auto kernel, int nw) {
-    hipLaunchKernelGGL(kernel, grid, dim3(64 * nw), 0, st, a);
-  });
+  auto launch = [&](auto kernel, int nw) { hipLaunchKernelGGL(kernel, grid, dim3(64 * nw), 0, st, a); };
+  const bool ok = a.page_shift > 0 ? with_attend_shape<true>(a.num_heads, launch)
+                                   : with_attend_shape<false>(a.num_heads, launch);
   if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 int mla_attend_blocks_per_cu(int num_heads) {
   int n = 0;
-  const bool ok = with_attend_shape(num_heads, [&](auto kernel, int nw) {
+  const bool ok = with_attend_shape<false>(num_heads, [&](auto kernel, int nw) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(kernel), 64 * nw,
                                                      0) != hipSuccess) {
       (void)hipGetLastError();

@@ -162,7 +162,8 @@ typedef struct {
  * sequence is split along its rows; each split leaves a partial o~_s and
  * lse_s in a "slot", and the merge combines the slots of each sequence.
  *  - Fixed splits (num_splits = S >= 1, or chosen by the library when the
- *    batch alone fills the GPU): S splits of ceil(L_max / S) rows per
+ *    batch alone fills the GPU): splits of ceil(L_max / S) rows rounded up
+ *    to a multiple of 32 (so at most S) per
  *    sequence, split s of sequence b in slot s*B + b.
  *  - Balanced splits (num_splits = 0 and a batch smaller than the number of
  *    resident workgroups): the split sizes are decided on the device from
@@ -242,6 +243,65 @@ DA_EXPORT da_status_t da_mla_merge_project(const da_mla_params_t* params,
                                            void* hip_stream);
 
 /* ------------------------------------------------------------------------ */
+/* Paged KV caches                                                           */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Paging ("Attention variants and KV cache", arganzheng.life, section 6.1):
+ * the cache rows of each sequence are cut into blocks of page_size tokens
+ * that live anywhere in a shared pool, and a per-sequence block table maps
+ * logical block j to a physical page; the kernels look the table up as they
+ * read the cache. Token t of sequence b is row t % page_size of page
+ * block_table[b * max_blocks_per_seq + t / page_size].
+ *
+ * The block table is device memory and is not read on the host. The caller
+ * guarantees that the entries for the blocks holding rows [0, seq_lens[b])
+ * are valid pages of the pool(s); the other entries are never read. Every
+ * other parameter keeps its meaning, except that the batch stride of the
+ * cache (kv_stride_b, cache_stride_b) is unused: a row's place inside its
+ * page is given by the token stride (kv_stride_t, cache_stride_t).
+ */
+typedef struct {
+  const int32_t* block_table; /* [B, max_blocks_per_seq] int32, device */
+  int32_t page_size;          /* rows per page: a power of two, 16 .. 2^20 */
+  int32_t max_blocks_per_seq; /* row length of block_table, >= ceil(max_seq_len / page_size) */
+  int64_t page_stride;        /* elements from one page of a pool to the next (> 0, 16-byte multiple) */
+} da_paged_kv_t;
+
+/* da_gqa_decode over paged pools: k_pool, v_pool [num_pages, page_size,
+ * Hkv, D] in the params' token and head strides; one block table for both.
+ * Splits start on multiples of 16 rows. The workspace that
+ * da_gqa_decode_workspace_size reports for the same params is large enough.
+ * Errors: as da_gqa_decode, and INVALID_ARGUMENT for a NULL `pages` or block
+ * table, a page_size that is not a power of two in [16, 2^20], too few
+ * blocks per sequence for max_seq_len, or a bad page_stride. */
+DA_EXPORT da_status_t da_gqa_decode_paged(const da_gqa_params_t* params, const da_paged_kv_t* pages,
+                                          const void* q, const void* k_pool, const void* v_pool,
+                                          const int32_t* seq_lens, float* out, float* lse,
+                                          void* workspace, size_t workspace_bytes,
+                                          void* hip_stream);
+
+/* da_mla_decode_absorbed over a paged latent pool cache_pool [num_pages,
+ * page_size, 576] bf16 (row = [c_kv | k_rope]). Workspace as
+ * da_mla_decode_workspace_size. Errors: as da_mla_decode_absorbed, plus the
+ * paging checks of da_gqa_decode_paged. */
+DA_EXPORT da_status_t da_mla_decode_absorbed_paged(const da_mla_params_t* params,
+                                                   const da_paged_kv_t* pages,
+                                                   const void* q_nope, const void* q_rope,
+                                                   const void* cache_pool, const int32_t* seq_lens,
+                                                   const void* w_uk, const void* w_uv,
+                                                   float* out, float* lse, void* workspace,
+                                                   size_t workspace_bytes, void* hip_stream);
+
+/* Stage 2 (da_mla_attend_split_pass) over a paged latent pool; its partials
+ * have the layout that da_mla_merge_project reads for the same params. */
+DA_EXPORT da_status_t da_mla_attend_split_pass_paged(const da_mla_params_t* params,
+                                                     const da_paged_kv_t* pages, const void* q_hat,
+                                                     const void* cache_pool, const int32_t* seq_lens,
+                                                     void* part_out, float* part_lse,
+                                                     void* hip_stream);
+
+/* ------------------------------------------------------------------------ */
 /* Split-KV merge                                                            */
 /* ------------------------------------------------------------------------ */
 
@@ -270,10 +330,11 @@ DA_EXPORT const char* da_status_string(da_status_t status);
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 DA_EXPORT int32_t da_version(void);
 
-/* sizeof(da_gqa_params_t) and sizeof(da_mla_params_t) as compiled, so that
- * bindings can check their struct mirrors. */
+/* sizeof(da_gqa_params_t), sizeof(da_mla_params_t) and sizeof(da_paged_kv_t)
+ * as compiled, so that bindings can check their struct mirrors. */
 DA_EXPORT size_t da_gqa_params_size(void);
 DA_EXPORT size_t da_mla_params_size(void);
+DA_EXPORT size_t da_paged_kv_size(void);
 
 #ifdef __cplusplus
 }

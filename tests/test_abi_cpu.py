@@ -50,6 +50,7 @@ def test_struct_mirrors_and_version():
     L = da.lib()
     assert L.da_gqa_params_size() == ctypes.sizeof(da.GqaParams) == 80
     assert L.da_mla_params_size() == ctypes.sizeof(da.MlaParams)
+    assert L.da_paged_kv_size() == ctypes.sizeof(da.PagedKv) == 24
     assert L.da_version() >= 100
     for s, txt in [(0, b"ok"), (1, b"invalid argument"), (2, b"unsupported configuration"),
                    (3, b"workspace too small"), (4, b"HIP runtime error"), (99, b"unknown status")]:
@@ -221,6 +222,57 @@ def test_mla_and_combine_reject_bad_parameters():
     assert comb(2, 1, 1, 2048, FAKE, FAKE, FAKE, None, None) == 1
     assert comb(2, 1, 1, 128, None, FAKE, FAKE, None, None) == 1
     assert comb(2, 1, 1, 128, FAKE_MIS, FAKE, FAKE, None, None) == 1
+
+
+def paging(table=FAKE, page_size=16, max_blocks=256, page_stride=16 * 8 * 128):
+    pg = da.PagedKv()
+    pg.block_table = table.value if table is not None else None
+    pg.page_size, pg.max_blocks_per_seq, pg.page_stride = page_size, max_blocks, page_stride
+    return pg
+
+
+@needs_lib
+@cpu_only
+@pytest.mark.parametrize("kw", [
+    dict(table=None),                          # no block table
+    dict(table=ctypes.c_void_p(0x10002)),      # misaligned table
+    dict(page_size=8),                         # below 16 rows
+    dict(page_size=48),                        # not a power of two
+    dict(page_size=1 << 21),                   # too large
+    dict(max_blocks=255),                      # 255 * 16 < 4096 rows
+    dict(page_stride=0),
+    dict(page_stride=4),                       # 8 bytes: not a 16-byte multiple
+])
+def test_paged_entry_points_reject_bad_paging(kw):
+    L = da.lib()
+    p = gqa(32, 32, 8, 128, 4096)
+    pg = paging(**kw)
+    assert L.da_gqa_decode_paged(ctypes.byref(p), ctypes.byref(pg), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 FAKE, FAKE, 1 << 40, None) == 1
+    m = mla(64, 128, 4096)
+    pgm = paging(**{"page_stride": 16 * 576, **kw})
+    assert L.da_mla_decode_absorbed_paged(ctypes.byref(m), ctypes.byref(pgm), FAKE, FAKE, FAKE,
+                                          FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == 1
+    assert L.da_mla_attend_split_pass_paged(ctypes.byref(m), ctypes.byref(pgm), FAKE, FAKE, FAKE,
+                                            FAKE, FAKE, None) == 1
+
+
+@needs_lib
+@cpu_only
+def test_paged_entry_points_reject_missing_descriptor_and_workspace():
+    L = da.lib()
+    p = gqa(16, 32, 8, 128, 4096)        # 2 splits: needs a workspace
+    assert L.da_gqa_decode_paged(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 1 << 40, None) == 1
+    pg = paging()
+    assert L.da_gqa_decode_paged(ctypes.byref(p), ctypes.byref(pg), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 FAKE, None, 0, None) == 3
+    m = mla(64, 128, 4096)
+    pgm = paging(page_stride=16 * 576)
+    assert L.da_mla_decode_absorbed_paged(ctypes.byref(m), None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                          FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == 1
+    assert L.da_mla_decode_absorbed_paged(ctypes.byref(m), ctypes.byref(pgm), FAKE, FAKE, FAKE,
+                                          FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, None) == 3
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
