@@ -7,6 +7,9 @@ One step is one pass of the whole hot path on synthetic inputs:
   * absorbed-MLA decode, DeepSeek-V3 shape: batch 64, 128 heads, latent cache
     [64, 4096, 576] bf16, W_UK / W_UV [128, 512, 128] (query absorption,
     split-KV latent attention, merge + W_UV projection).
+Other workloads (--workload): each path alone, long-context MLA, ragged
+MHA, and GQA / MLA over paged caches (pools of 16-row pages in a seeded
+random physical order, read through a block table).
 Inputs are resident in HBM before timing starts. Each step reads the next of
 several copies of the caches, so that no step finds the previous step's cache
 in the 256 MB last-level (Infinity) cache.
@@ -193,6 +196,80 @@ def setup_mla(cfg):
     return calls, alg, info, inp
 
 
+PAGE_SIZE = 16   # rows per page of the paged workloads (the common default)
+
+
+def paged_pools(seq_lens, caches, seed):
+    """Host pools [num_pages, PAGE_SIZE, ...] of the given contiguous caches,
+    pages in a seeded random physical order, and the block table."""
+    import workloads as W
+    table, n_pages = W.make_block_table(seq_lens, PAGE_SIZE, seed=seed, spare_pages=0)
+    return [W.paginate(c, seq_lens, table, n_pages, PAGE_SIZE, 0) for c in caches], table
+
+
+def setup_gqa_paged(cfg):
+    """The GQA workload of `cfg` with K and V in pools of 16-row pages."""
+    import torch
+    import workloads as W
+    import decode_attention_kv_bf16_amd as da
+    inp = W.make_gqa_config(cfg)
+    (kp_h, vp_h), table_h = paged_pools(inp.seq_lens, [inp.k, inp.v], seed=cfg)
+    q = to_dev_bf16(inp.q)
+    k0, v0 = to_dev_bf16(kp_h), to_dev_bf16(vp_h)
+    table = torch.from_numpy(table_h).cuda()
+    sl = torch.from_numpy(inp.seq_lens).cuda()
+    fp = k0.numel() * 2 * 2
+    n_copies = max(1, math.ceil(MALL_GUARD_BYTES / fp)) if fp < MALL_GUARD_BYTES else 1
+    copies = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(n_copies - 1)]
+    B, Hq, D = q.shape
+    L = inp.k.shape[1]
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    calls = []
+    for kk, vv in copies:
+        def call(kk=kk, vv=vv):
+            da.gqa_decode_paged(q, kk, vv, table, PAGE_SIZE, sl, max_seq_len=L,
+                                softmax_scale=inp.scale, out=out, lse=lse)
+        calls.append([("gqa_decode_paged", call)])
+    alg = gqa_alg(B, Hq, inp.k.shape[2], D, int(inp.seq_lens.sum()))
+    alg["total"] += table_h.nbytes
+    info = dict(batch=B, q_heads=Hq, kv_heads=int(inp.k.shape[2]), head_dim=D,
+                seq_len=int(inp.seq_lens.max()), page_size=PAGE_SIZE,
+                num_pages=int(kp_h.shape[0]), cache_copies=len(copies))
+    return calls, alg, info, (inp, dict(k_pool=kp_h, v_pool=vp_h, table=table_h))
+
+
+def setup_mla_paged(cfg):
+    """The MLA workload of `cfg` with the latent cache in a pool of 16-row pages."""
+    import torch
+    import workloads as W
+    import decode_attention_kv_bf16_amd as da
+    inp = W.make_mla_config(cfg)
+    (pool_h,), table_h = paged_pools(inp.seq_lens, [inp.cache], seed=cfg)
+    qn, qr = to_dev_bf16(inp.q_nope), to_dev_bf16(inp.q_rope)
+    wuk, wuv = to_dev_bf16(inp.w_uk), to_dev_bf16(inp.w_uv)
+    p0 = to_dev_bf16(pool_h)
+    table = torch.from_numpy(table_h).cuda()
+    sl = torch.from_numpy(inp.seq_lens).cuda()
+    fp = p0.numel() * 2
+    n_copies = max(1, math.ceil(MALL_GUARD_BYTES / fp)) if fp < MALL_GUARD_BYTES else 1
+    pools = [p0] + [p0.clone() for _ in range(n_copies - 1)]
+    L = inp.cache.shape[1]
+    calls = []
+    for pl in pools:
+        absorb, attend, merge, _, _, _ = da.mla_stages(qn, qr, pl, wuk, wuv, sl, inp.scale,
+                                                       paged=(table, PAGE_SIZE, L))
+        calls.append([("mla_absorb", absorb), ("mla_attend_paged", attend),
+                      ("mla_merge_project", merge)])
+    B, H, _ = qn.shape
+    alg = mla_alg(B, H, int(inp.seq_lens.sum()))
+    alg["total"] += table_h.nbytes
+    info = dict(batch=B, heads=H, seq_len=int(inp.seq_lens.max()),
+                total_rows=int(inp.seq_lens.sum()), page_size=PAGE_SIZE,
+                num_pages=int(pool_h.shape[0]), cache_copies=len(pools))
+    return calls, alg, info, (inp, dict(pool=pool_h, table=table_h))
+
+
 def measured_traffic(name):
     """HBM bytes per launch from the committed rocprofv3 counter runs
     (profiles/hbm_traffic.json), if they were taken on the current kernel
@@ -223,6 +300,10 @@ def run_gpu(args):
         plans.append(("mla", setup_mla(4)))
     if args.workload == "gqa-ragged":
         plans.append(("gqa", setup_gqa(5)))
+    if args.workload == "gqa-paged":
+        plans.append(("gqa-paged", setup_gqa_paged(2)))
+    if args.workload == "mla-paged":
+        plans.append(("mla-paged", setup_mla_paged(3)))
     n_rot = max(len(p[1][0]) for p in plans)
 
     def step_calls(i):
@@ -301,7 +382,7 @@ def run_gpu(args):
                                        if any(dom == n for n, _ in p[1][0][0]))
     if dom == "gqa_split_pass":
         dom_bytes = alg["cache"] + alg["q"]
-    elif dom == "mla_attend":
+    elif dom in ("mla_attend", "mla_attend_paged"):
         dom_bytes = alg["cache"]
     else:
         dom_bytes = alg["total"]
@@ -322,7 +403,7 @@ def run_gpu(args):
                      cache_gbs=round(alg["cache"] / (t_ms * 1e-3) / 1e9, 1),
                      tflops=round(alg["flops"] / (t_ms * 1e-3) / 1e12, 2),
                      hbm_frac=round(alg["total"] / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
-        if kind == "mla":
+        if kind.startswith("mla"):
             entry["mfma_frac"] = round(alg["flops"] / (t_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
         paths[kind] = entry
 
@@ -342,7 +423,9 @@ def workload_name(w):
     return {"step": "llama3-8b-gqa-b32-l4096 + deepseek-v3-mla-b64-l4096",
             "gqa": "llama3-8b-gqa-b32-l4096", "mla": "deepseek-v3-mla-b64-l4096",
             "mla-long": "deepseek-v3-mla-longctx-b4-l16k-32k",
-            "gqa-ragged": "llama2-7b-mha-ragged-b64-l1-8192"}[w]
+            "gqa-ragged": "llama2-7b-mha-ragged-b64-l1-8192",
+            "gqa-paged": "llama3-8b-gqa-b32-l4096-paged16",
+            "mla-paged": "deepseek-v3-mla-b64-l4096-paged16"}[w]
 
 
 # ----------------------------------------------------------------------------
@@ -350,7 +433,8 @@ def workload_name(w):
 # ----------------------------------------------------------------------------
 
 def cpu_baseline(plans, budget_s):
-    from oracle.attention import gqa_decode_ref, mla_absorbed_ref
+    from oracle.attention import (gqa_decode_paged_ref, gqa_decode_ref, mla_absorbed_paged_ref,
+                                  mla_absorbed_ref)
     import workloads as W
     try:
         from threadpoolctl import threadpool_info
@@ -360,11 +444,37 @@ def cpu_baseline(plans, budget_s):
     done_bytes, spent, samples = 0, 0.0, []
     per_kind_budget = budget_s / max(1, len(plans))
     for kind, (calls, alg, info, inp) in plans:
+        pools = None
+        if kind.endswith("-paged"):
+            inp, pools = inp
         t_kind, n = 0.0, 0
         B = len(inp.seq_lens)
         while t_kind < per_kind_budget and n < B:
             b = n
-            if kind == "gqa":
+            if kind == "gqa-paged":
+                f = (lambda a: W.bf16_to_f32(a).astype(np.float64))
+                L = int(inp.seq_lens[b])
+                pages = pools["table"][b, :-(-L // PAGE_SIZE)]
+                # only the sequence's own pages, renumbered, go to the oracle
+                tab = np.arange(len(pages), dtype=np.int32)[None]
+                args = (f(inp.q[b:b + 1]), f(pools["k_pool"][pages]), f(pools["v_pool"][pages]),
+                        tab, PAGE_SIZE, inp.seq_lens[b:b + 1], inp.scale)
+                t = time.perf_counter()
+                gqa_decode_paged_ref(*args)
+                dt = time.perf_counter() - t
+                a1 = gqa_alg(1, inp.q.shape[1], inp.k.shape[2], inp.q.shape[2], L)
+            elif kind == "mla-paged":
+                f = (lambda a: W.bf16_to_f32(a).astype(np.float64))
+                L = int(inp.seq_lens[b])
+                pages = pools["table"][b, :-(-L // PAGE_SIZE)]
+                tab = np.arange(len(pages), dtype=np.int32)[None]
+                args = (f(inp.q_nope[b:b + 1]), f(inp.q_rope[b:b + 1]), f(pools["pool"][pages]), tab,
+                        PAGE_SIZE, inp.seq_lens[b:b + 1], f(inp.w_uk), f(inp.w_uv), inp.scale)
+                t = time.perf_counter()
+                mla_absorbed_paged_ref(*args)
+                dt = time.perf_counter() - t
+                a1 = mla_alg(1, inp.q_nope.shape[1], L)
+            elif kind == "gqa":
                 f = (lambda a: W.bf16_to_f32(a).astype(np.float64))
                 L = int(inp.seq_lens[b])
                 args = (f(inp.q[b:b + 1]), f(inp.k[b:b + 1, :L]), f(inp.v[b:b + 1, :L]),
@@ -398,7 +508,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="step",
-                    choices=["step", "gqa", "mla", "mla-long", "gqa-ragged"])
+                    choices=["step", "gqa", "mla", "mla-long", "gqa-ragged", "gqa-paged",
+                             "mla-paged"])
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle time for the CPU baseline (0 disables)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,

@@ -293,7 +293,8 @@ def _check_seq_lens(seq_lens: torch.Tensor, B: int):
 def gqa_decode_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                      block_table: torch.Tensor, page_size: int, seq_lens: torch.Tensor,
                      max_seq_len: Optional[int] = None, softmax_scale: Optional[float] = None,
-                     num_splits: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+                     num_splits: int = 0, out: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """gqa_decode over paged pools: k_pool, v_pool [num_pages, page_size, Hkv, D];
     block_table [B, max_blocks_per_seq] int32 (token t of sequence b is row
     t % page_size of page block_table[b, t // page_size]); seq_lens [B] int32.
@@ -320,8 +321,10 @@ def gqa_decode_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor
     p.kv_stride_b = 0
     L = lib()
     Hq, D = q.shape[1], q.shape[2]
-    out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
-    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     ws_bytes = L.da_gqa_decode_workspace_size(ctypes.byref(p))
     ws = _workspace(ws_bytes, q.device)
     st = L.da_gqa_decode_paged(ctypes.byref(p), ctypes.byref(pg), _ptr(q), _ptr(k_pool),
