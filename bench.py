@@ -10,7 +10,11 @@ One step is one pass of the whole hot path on synthetic inputs:
 Other workloads (--workload): each path alone, long-context MLA, ragged
 MHA, and GQA / MLA over paged caches (pools of 16-row pages in a seeded
 random physical order, read through a block table).
-Inputs are resident in HBM before timing starts. Each step reads the next of
+Inputs are resident in HBM before timing starts. The default warm-up (200
+steps, about 40 ms) outlasts the board's power-management transient: in a
+kernel trace of this step, the first few milliseconds of back-to-back steps
+run the attention kernels up to a third slower than the steady state they
+reach after about 20 ms. Each step reads the next of
 several copies of the caches, so that no step finds the previous step's cache
 in the 256 MB last-level (Infinity) cache.
 
@@ -505,8 +509,8 @@ def cpu_baseline(plans, budget_s):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="step",
                     choices=["step", "gqa", "mla", "mla-long", "gqa-ragged", "gqa-paged",
                              "mla-paged"])

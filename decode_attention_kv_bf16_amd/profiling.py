@@ -28,26 +28,34 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
-# short kernel name -> (substring of the device symbol, source file)
+# short kernel name -> (substring of the device symbol, substrings of which
+# one must also occur, source file); the first entry that matches names a
+# symbol. The attention kernel's last template argument is the paged flag
+# (mangled "Lb1E", demangled ", true>": paged pool).
 KERNELS = {
-    "gqa_split_pass": ("gqa_decode_kernel", "gqa_decode.hip"),
-    "gqa_combine": ("splitkv_combine_kernel", "combine.hip"),
-    "mla_absorb": ("mla_absorb_kernel", "mla_decode.hip"),
-    "mla_attend": ("mla_attend_kernel", "mla_decode.hip"),
-    "mla_merge_project": ("mla_merge_project_kernel", "mla_decode.hip"),
+    "gqa_split_pass": ("gqa_decode_kernel", (), "gqa_decode.hip"),
+    "gqa_combine": ("splitkv_combine_kernel", (), "combine.hip"),
+    "mla_absorb": ("mla_absorb_kernel", (), "mla_decode.hip"),
+    "mla_attend_paged": ("mla_attend_kernel", ("Lb1E", ", true>"), "mla_decode.hip"),
+    "mla_attend": ("mla_attend_kernel", (), "mla_decode.hip"),
+    "mla_merge_project": ("mla_merge_project_kernel", (), "mla_decode.hip"),
 }
+# names under which a workload's launches of a kernel are recorded (GQA over
+# paged pools runs the GQA kernel as one library call, gqa_decode_paged)
+ALIASES = {"gqa_decode_paged": "gqa_split_pass"}
 
 
 def source_sha256(short: str):
+    short = ALIASES.get(short, short)
     if short not in KERNELS:
         return None
-    with open(os.path.join(CSRC, KERNELS[short][1]), "rb") as f:
+    with open(os.path.join(CSRC, KERNELS[short][2]), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
 def short_name(symbol: str):
-    for short, (sub, _) in KERNELS.items():
-        if sub in symbol:
+    for short, (sub, any_of, _) in KERNELS.items():
+        if sub in symbol and (not any_of or any(s in symbol for s in any_of)):
             return short
     return None
 
@@ -62,19 +70,54 @@ def _find(path: str, suffix: str) -> str:
     raise FileNotFoundError(f"no *{suffix} under {path}")
 
 
-def stats_table(stats_csv: str) -> str:
+def stats_table(stats_csv: str, rename=lambda s: s) -> str:
     rows = list(csv.DictReader(open(_find(stats_csv, "kernel_stats.csv"))))
     lines = ["| kernel | symbol | calls | avg us | min us | max us | share % |",
              "|---|---|---:|---:|---:|---:|---:|"]
     for r in rows:
         sym = r["Name"]
-        lines.append(f"| {short_name(sym) or '-'} | `{sym[:90]}` | {r['Calls']} | "
+        short = short_name(sym)
+        lines.append(f"| {rename(short) if short else '-'} | `{sym[:90]}` | {r['Calls']} | "
                      f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                      f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
     return "\n".join(lines)
 
 
-def counter_averages(counter_dir: str, counter: str):
+def _renamer(pairs):
+    """--rename KERNEL=NAME options as a function on short names."""
+    m = dict(p.split("=", 1) for p in pairs)
+    for new in m.values():
+        if ALIASES.get(new, new) not in KERNELS:
+            raise SystemExit(f"unknown kernel name {new}")
+    return lambda s: m.get(s, s)
+
+
+def tail_table(trace_dir: str, tail: int, rename=lambda s: s) -> str:
+    """Per kernel, the average duration of its last `tail` dispatches in the
+    kernel trace (the launches of the bench's last pass)."""
+    rows = list(csv.DictReader(open(_find(trace_dir, "kernel_trace.csv"))))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    per = defaultdict(list)
+    for r in rows:
+        s = short_name(r["Kernel_Name"])
+        if s:
+            per[rename(s)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = [f"| kernel | dispatches | avg us, last {tail} | min us | max us |", "|---|---:|---:|---:|---:|"]
+    for k, d in sorted(per.items()):
+        last = d[-tail:]
+        lines.append(f"| {k} | {len(d)} | {sum(last) / len(last):.2f} | {min(last):.2f} | {max(last):.2f} |")
+    return "\n".join(lines)
+
+
+def bench_roofline(log_path: str):
+    """The roofline object of the bench JSON line in a profiled run's output."""
+    for line in open(log_path):
+        if line.startswith("{"):
+            return json.loads(line).get("roofline")
+    return None
+
+
+def counter_averages(counter_dir: str, counter: str, rename=lambda s: s):
     """Per short kernel name: average counter value per dispatch, and the value
     for the last copy-kernel dispatch of the run (the calibration copy)."""
     rows = list(csv.DictReader(open(_find(counter_dir, "counter_collection.csv"))))
@@ -89,7 +132,7 @@ def counter_averages(counter_dir: str, counter: str):
             continue
         s = short_name(r["Kernel_Name"])
         if s:
-            per[s].append(v)
+            per[rename(s)].append(v)
     return {k: sum(v) / len(v) for k, v in per.items()}, {k: len(v) for k, v in per.items()}, copy_val
 
 
@@ -101,6 +144,10 @@ def main(argv=None):
     s.add_argument("--command", required=True)
     s.add_argument("--title", default="rocprofv3 kernel durations")
     s.add_argument("--out", required=True)
+    s.add_argument("--rename", action="append", default=[], help="KERNEL=NAME")
+    s.add_argument("--tail", type=int, default=0,
+                   help="also average each kernel's last N dispatches (the bench's roofline pass)")
+    s.add_argument("--bench-log", help="stdout of the profiled bench run (its JSON line)")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -110,18 +157,30 @@ def main(argv=None):
     t.add_argument("--workload", required=True)
     t.add_argument("--alg-bytes", default="{}", help="JSON {kernel: algorithmic bytes per launch}")
     t.add_argument("--out-md", required=True)
+    t.add_argument("--rename", action="append", default=[], help="KERNEL=NAME")
     a = ap.parse_args(argv)
 
     if a.cmd == "stats":
+        rn = _renamer(a.rename)
         text = (f"# {a.title}\n\nCommand (run from the repository root):\n\n```\n{a.command}\n```\n\n"
-                f"{stats_table(a.csv)}\n")
+                f"All dispatches of the run (rocprofv3 --stats):\n\n{stats_table(a.csv, rn)}\n")
+        if a.tail:
+            text += (f"\nLast {a.tail} dispatches of each kernel (the bench's roofline pass, after "
+                     f"warm-up, probe and timed passes):\n\n{tail_table(a.csv, a.tail, rn)}\n")
+        if a.bench_log:
+            rf = bench_roofline(a.bench_log)
+            if rf:
+                text += (f"\nThe bench line of this profiled run: dominant kernel `{rf['kernel']}`, "
+                         f"{rf['avg_launch_us']} us per launch from HIP events around each launch "
+                         f"of its roofline pass (events add a little to each launch).\n")
         with open(a.out, "w") as f:
             f.write(text)
         print(text)
         return
 
-    fetch, nf, fcopy = counter_averages(a.fetch, "FETCH_SIZE")
-    write, nw, wcopy = counter_averages(a.write, "WRITE_SIZE")
+    rn = _renamer(a.rename)
+    fetch, nf, fcopy = counter_averages(a.fetch, "FETCH_SIZE", rn)
+    write, nw, wcopy = counter_averages(a.write, "WRITE_SIZE", rn)
     if not fcopy or not wcopy:
         raise SystemExit("no calibration copy dispatch found in the counter runs")
     copy_kib = a.copy_bytes / 1024.0
