@@ -486,3 +486,148 @@ def test_planted_reversed_page_order_is_caught(monkeypatch):
     o, l = OA.gqa_decode_paged_ref(q, kp, vp, table, 4, [9, 8], 0.7)
     bo, bl = brute_paged_gqa(q, kp, vp, table, 4, [9, 8], 0.7)
     assert not (np.all(np.isfinite(o)) and np.allclose(o, bo, rtol=1e-9))
+
+
+# ----------------------------------------------------------------------------
+# FP8 (E4M3) caches ("Attention variants and KV cache", section 6.3)
+# ----------------------------------------------------------------------------
+
+import oracle.fp8 as OF
+from oracle.fp8 import dequantize_ref, e4m3_to_float, gqa_decode_fp8_ref
+
+
+def brute_e4m3(c: int) -> float:
+    """One code, from the OCP E4M3 definition, by scalar arithmetic."""
+    sign = -1.0 if c & 0x80 else 1.0
+    e, m = (c >> 3) & 15, c & 7
+    if e == 15 and m == 7:
+        return math.nan
+    return sign * (math.ldexp(m, -9) if e == 0 else math.ldexp(8 + m, e - 10))
+
+
+def test_e4m3_decoder_matches_torch_for_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = e4m3_to_float(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref)) and np.isnan(got).sum() == 2
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))     # -0 for 0x80
+
+
+def test_e4m3_defining_values_and_structure():
+    # OCP 8-bit floating point specification, E4M3: bias 7, largest normal
+    # 448 = 1.75 * 2^8, smallest normal 2^-6, smallest subnormal 2^-9
+    fixed = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+             0x39: 1.125, 0x40: 2.0, 0x7E: 448.0, 0xC0: -2.0, 0xFE: -448.0}
+    for c, v in fixed.items():
+        assert e4m3_to_float(np.array([c], np.uint8))[0] == v, hex(c)
+    codes = np.arange(256, dtype=np.uint8)
+    val = e4m3_to_float(codes)
+    assert all(val[c] == brute_e4m3(c) or (math.isnan(val[c]) and math.isnan(brute_e4m3(c)))
+               for c in range(256))
+    assert np.all(np.diff(val[:127]) > 0)                     # increasing over 0x00..0x7E
+    assert np.array_equal(val[128:255], -val[:127])           # sign symmetry
+    assert np.isnan(val[0x7F]) and np.isnan(val[0xFF])
+
+
+def test_planted_fnuz_bias_is_caught(monkeypatch):
+    # the other common E4M3 variant has bias 8; the pins above must notice
+    monkeypatch.setattr(OF, "E4M3_BIAS", 8)
+    with pytest.raises(AssertionError):
+        test_e4m3_decoder_matches_torch_for_every_code()
+
+
+def _fp8_inputs(B, Hq, Hkv, D, lens, seed):
+    rng = np.random.default_rng(seed)
+    L = max(lens)
+    codes = lambda: rng.integers(0, 256, (B, L, Hkv, D)).astype(np.uint8)
+    k, v = codes(), codes()
+    for x in (k, v):                                  # no NaN codes
+        x[(x & 0x7F) == 0x7F] = 0x38
+    ks = rng.uniform(0.01, 0.05, (B, L, Hkv))
+    vs = rng.uniform(0.5, 2.0, (B, L, Hkv))
+    q = rng.standard_normal((B, Hq, D))
+    return q, k, v, ks, vs
+
+
+def brute_gqa_fp8(q, k, v, ks, vs, seq_lens, scale):
+    """Scalar loops: decode each code, scale it, attend with math.fsum."""
+    B, Hq, D = q.shape
+    Hkv = k.shape[2]
+    g = Hq // Hkv
+    out = np.zeros((B, Hq, D))
+    lse = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        L = int(seq_lens[b])
+        for h in range(Hq):
+            kv = h // g
+            if L == 0:
+                continue
+            s = [scale * math.fsum(q[b, h, i] * brute_e4m3(int(k[b, j, kv, i])) * ks[b, j, kv]
+                                   for i in range(D)) for j in range(L)]
+            m = max(s)
+            e = [math.exp(x - m) for x in s]
+            z = math.fsum(e)
+            lse[b, h] = m + math.log(z)
+            for i in range(D):
+                out[b, h, i] = math.fsum(e[j] / z * brute_e4m3(int(v[b, j, kv, i])) * vs[b, j, kv]
+                                         for j in range(L))
+    return out, lse
+
+
+@pytest.mark.parametrize("Hq,Hkv,lens", [(4, 2, [3, 1]), (6, 3, [5, 0]), (2, 2, [4, 4])])
+def test_fp8_gqa_brute_force(Hq, Hkv, lens):
+    q, k, v, ks, vs = _fp8_inputs(len(lens), Hq, Hkv, 8, lens, seed=sum(lens) + Hq)
+    o, l = gqa_decode_fp8_ref(q, k, v, ks, vs, lens, 0.3)
+    bo, bl = brute_gqa_fp8(q, k, v, ks, vs, lens, 0.3)
+    np.testing.assert_allclose(o, bo, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l, bl, rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_gqa_scale_closed_forms():
+    q, k, v, ks, vs = _fp8_inputs(2, 4, 2, 16, [6, 3], seed=5)
+    lens = [6, 3]
+    # a zero key scale makes every score 0: the output is the mean of the
+    # dequantized values and lse = ln L
+    o, l = gqa_decode_fp8_ref(q, k, v, np.zeros_like(ks), vs, lens, 0.5)
+    for b, L in enumerate(lens):
+        vals = dequantize_ref(v[b, :L], vs[b, :L])            # [L, Hkv, D]
+        for h in range(4):
+            np.testing.assert_allclose(o[b, h], vals[:, h // 2].mean(axis=0), rtol=1e-12)
+            assert abs(l[b, h] - math.log(L)) < 1e-12
+    # doubling every value scale doubles the output and leaves lse alone
+    o1, l1 = gqa_decode_fp8_ref(q, k, v, ks, vs, lens, 0.5)
+    o2, l2 = gqa_decode_fp8_ref(q, k, v, ks, 2 * vs, lens, 0.5)
+    np.testing.assert_allclose(o2, 2 * o1, rtol=1e-12)
+    np.testing.assert_allclose(l2, l1, rtol=1e-12)
+    # a key scale that is huge for one token makes that token dominant
+    ks2 = ks.copy()
+    ks2[0, 2, :] = 1e4
+    k2 = k.copy()
+    k2[0, 2] = 0x38                                           # every element 1.0
+    q2 = np.abs(q)                                            # positive dot products
+    o3, _ = gqa_decode_fp8_ref(q2, k2, v, ks2, vs, lens, 0.5)
+    for h in range(4):
+        np.testing.assert_allclose(o3[0, h], dequantize_ref(v[0, 2], vs[0, 2])[h // 2], rtol=1e-9)
+
+
+def test_planted_swapped_kv_scales_are_caught():
+    q, k, v, ks, vs = _fp8_inputs(2, 4, 2, 8, [3, 2], seed=9)
+    bo, bl = brute_gqa_fp8(q, k, v, ks, vs, [3, 2], 0.4)
+    o, l = gqa_decode_fp8_ref(q, k, v, vs, ks, [3, 2], 0.4)   # the mistake
+    assert not np.allclose(o, bo, rtol=1e-3)
+
+
+def test_fp8_workload_codes_round_trip():
+    # the generator's codes decode to within half an E4M3 step of the drawn
+    # values, relative to the row's scale (round to nearest)
+    inp = W.make_gqa_fp8(2, 4, 2, 64, [7, 3], seed=4)
+    for b, L in enumerate(inp.seq_lens):
+        r = np.random.default_rng([4, 0, 2, b])
+        kf = r.standard_normal((L, 2, 64), dtype=np.float32)
+        deq = dequantize_ref(inp.k[b, :L], inp.k_scale[b, :L])
+        rel = np.abs(deq - kf) / np.abs(kf).max(axis=-1, keepdims=True)
+        assert rel.max() <= 2.0 ** -4 * 1.0001
+        assert np.all(np.abs(e4m3_to_float(inp.k[b, :L])) <= 448)
+    assert np.all(inp.k[0, 7:] == W.FP8_NAN_CODE) and np.isnan(inp.v_scale[1, 3:]).all()

@@ -334,3 +334,90 @@ def paginate(cache: np.ndarray, seq_lens: Sequence[int], table: np.ndarray, num_
             rows = cache[b, j * page_size:min((j + 1) * page_size, int(L))]
             pool[int(table[b, j]), :len(rows)] = rows
     return pool
+
+
+# ----------------------------------------------------------------------------
+# FP8 (E4M3) caches ("Attention variants and KV cache", section 6.3)
+# ----------------------------------------------------------------------------
+
+FP8_NAN_CODE = np.uint8(0x7F)
+E4M3_MAX = 448.0
+
+
+@dataclass
+class GQAFp8Inputs:
+    """Host copies of one GQA decode problem over an FP8 cache.
+
+    q [B, Hq, D] bf16 bit patterns; k, v [B, L_max, H_kv, D] uint8 E4M3 codes;
+    k_scale, v_scale [B, L_max, H_kv] float32: element (b, t, h, :) of K stands
+    for code * k_scale[b, t, h].
+    """
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    k_scale: np.ndarray
+    v_scale: np.ndarray
+    seq_lens: np.ndarray
+    scale: float
+    meta: dict = field(default_factory=dict)
+
+
+def encode_e4m3(x: np.ndarray) -> np.ndarray:
+    """float32 values (|x| <= 448) -> E4M3 codes, round to nearest even, by
+    torch's float8_e4m3fn conversion."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy()
+
+
+def make_gqa_fp8(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                 seq_lens: Sequence[int], cfg: int = 0, seed: int = BASE_SEED,
+                 max_seq_len: Optional[int] = None, scales: str = "token",
+                 pad_nan: bool = True) -> GQAFp8Inputs:
+    """q, K, V ~ N(0, 1) drawn from the same streams as make_gqa, with K and V
+    quantized to E4M3. scales="token": one scale per (sequence, token, KV
+    head) row, amax(|row|) / 448; scales="head": one per KV head over the whole
+    batch (repeated in the arrays). Rows past a sequence's length hold the NaN
+    code and NaN scales when pad_nan, else zeros."""
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    assert seq_lens.shape == (batch,)
+    L_max = int(max_seq_len if max_seq_len is not None else max(1, int(seq_lens.max(initial=0))))
+    assert int(seq_lens.max(initial=0)) <= L_max
+    B, Hq, Hkv, D = batch, num_q_heads, num_kv_heads, head_dim
+    q = bf16_round(_normal(np.random.default_rng([seed, cfg, 1]), (B, Hq, D)))
+    kf = np.zeros((B, L_max, Hkv, D), np.float32)
+    vf = np.zeros((B, L_max, Hkv, D), np.float32)
+    for b in range(B):
+        L = int(seq_lens[b])
+        r = np.random.default_rng([seed, cfg, 2, b])
+        kf[b, :L] = _normal(r, (L, Hkv, D))
+        vf[b, :L] = _normal(r, (L, Hkv, D))
+    valid = np.arange(L_max)[None, :] < seq_lens[:, None]          # [B, L]
+    out = []
+    for x in (kf, vf):
+        amax = np.abs(x).max(axis=-1)                                # [B, L, Hkv]
+        if scales == "head":
+            amax = np.broadcast_to(np.where(valid[..., None], amax, 0).max(axis=(0, 1)), amax.shape)
+        elif scales != "token":
+            raise ValueError(scales)
+        s = (np.maximum(amax, 1e-30) / E4M3_MAX).astype(np.float32)
+        codes = encode_e4m3(x / s[..., None])
+        pad_code, pad_scale = (FP8_NAN_CODE, np.nan) if pad_nan else (0, 0.0)
+        codes[~valid] = pad_code
+        s = np.where(valid[..., None], s, np.float32(pad_scale)).astype(np.float32)
+        out += [codes, s]
+    k, ks, v, vs = out
+    return GQAFp8Inputs(q, k, v, ks, vs, seq_lens, 1.0 / float(np.sqrt(D)),
+                        meta=dict(cfg=cfg, seed=seed, scales=scales))
+
+
+def make_gqa_fp8_config(cfg: int, seed: int = BASE_SEED, scales: str = "token",
+                        pad_nan: bool = False, batch: Optional[int] = None) -> GQAFp8Inputs:
+    """The shapes and lengths of a GQA config with the cache in E4M3."""
+    s = CONFIGS[cfg]
+    assert isinstance(s, GQAShape)
+    B = s.batch if batch is None else batch
+    lens = draw_seq_lens(s.batch, s.seq_len, s.seq_len_range, cfg, seed)[:B]
+    L_max = s.seq_len if s.seq_len is not None else s.seq_len_range[1]
+    return make_gqa_fp8(B, s.num_q_heads, s.num_kv_heads, s.head_dim, lens, cfg=cfg, seed=seed,
+                        max_seq_len=L_max, scales=scales, pad_nan=pad_nan)
