@@ -11,6 +11,7 @@ raises.
     out, lse = mla_decode_absorbed(q_nope, q_rope, kv_cache, w_uk, w_uv, seq_lens)
     out, lse = splitkv_combine(partial_out, partial_lse)
     out, lse = gqa_decode_paged(q, k_pool, v_pool, block_table, page_size, seq_lens)
+    out, lse = gqa_decode_fp8(q, k_codes, v_codes, k_scale, v_scale, seq_lens)
     out, lse = mla_decode_absorbed_paged(q_nope, q_rope, cache_pool, block_table, page_size,
                                          seq_lens, w_uk, w_uv)
 """
@@ -29,6 +30,7 @@ LIB_PATH = os.path.join(_PKG_DIR, "libdecode_attn.so")
 DA_OK = 0
 DA_DTYPE_F32 = 0
 DA_DTYPE_BF16 = 1
+DA_DTYPE_FP8_E4M3 = 2
 
 
 class GqaParams(ctypes.Structure):
@@ -74,6 +76,16 @@ class PagedKv(ctypes.Structure):
     ]
 
 
+class KvScales(ctypes.Structure):
+    _fields_ = [
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
+        ("stride_b", ctypes.c_int64),
+        ("stride_t", ctypes.c_int64),
+        ("stride_h", ctypes.c_int64),
+    ]
+
+
 _vp = ctypes.c_void_p
 _GQA_P = ctypes.POINTER(GqaParams)
 _MLA_P = ctypes.POINTER(MlaParams)
@@ -102,6 +114,8 @@ _SIGNATURES = {
                                                     _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "da_mla_attend_split_pass_paged": (ctypes.c_int, [_MLA_P, _PAGED_P, _vp, _vp, _vp, _vp, _vp,
                                                       _vp]),
+    "da_gqa_decode_fp8": (ctypes.c_int, [_GQA_P, ctypes.POINTER(KvScales), _vp, _vp, _vp, _vp, _vp,
+                                         _vp, _vp, ctypes.c_size_t, _vp]),
     "da_splitkv_combine": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]),
     "da_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -109,6 +123,7 @@ _SIGNATURES = {
     "da_gqa_params_size": (ctypes.c_size_t, []),
     "da_mla_params_size": (ctypes.c_size_t, []),
     "da_paged_kv_size": (ctypes.c_size_t, []),
+    "da_kv_scales_size": (ctypes.c_size_t, []),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -133,7 +148,8 @@ def lib() -> ctypes.CDLL:
         fn.argtypes = args
     if L.da_gqa_params_size() != ctypes.sizeof(GqaParams) or \
             L.da_mla_params_size() != ctypes.sizeof(MlaParams) or \
-            L.da_paged_kv_size() != ctypes.sizeof(PagedKv):
+            L.da_paged_kv_size() != ctypes.sizeof(PagedKv) or \
+            L.da_kv_scales_size() != ctypes.sizeof(KvScales):
         raise RuntimeError("libdecode_attn.so parameter structs do not match this binding")
     _lib = L
     return L
@@ -262,6 +278,65 @@ def gqa_decode_split_pass(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
 def gqa_num_splits(q: torch.Tensor, k_cache: torch.Tensor, num_splits: int = 0) -> int:
     p = gqa_params(q, k_cache, None, num_splits)
     return int(lib().da_gqa_decode_num_splits(ctypes.byref(p)))
+
+
+# ----------------------------------------------------------------------------
+# FP8 (E4M3) caches
+# ----------------------------------------------------------------------------
+
+def gqa_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   k_scale: torch.Tensor, v_scale: torch.Tensor,
+                   seq_lens: Optional[torch.Tensor] = None, softmax_scale: Optional[float] = None,
+                   num_splits: int = 0, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """gqa_decode over an E4M3 cache: q [B, Hq, D] bf16; k_cache, v_cache
+    [B, L_max, Hkv, D] uint8 codes (or torch.float8_e4m3fn); k_scale, v_scale
+    float32 of shape [B, L_max, Hkv] (broadcast views with zero strides are
+    fine: per token, per head). Element (b, t, h, :) of K stands for its code's
+    value times k_scale[b, t, h]."""
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("k_scale", k_scale),
+                    ("v_scale", v_scale)):
+        _require_cuda(name, t)
+    if q.dtype != torch.bfloat16:
+        raise ValueError("q must be bfloat16")
+    if k_cache.dtype == torch.float8_e4m3fn:
+        k_cache, v_cache = k_cache.view(torch.uint8), v_cache.view(torch.uint8)
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise ValueError("k_cache and v_cache must hold E4M3 codes (uint8 or float8_e4m3fn)")
+    if v_cache.shape != k_cache.shape or v_cache.stride() != k_cache.stride():
+        raise ValueError("v_cache must have the shape and strides of k_cache")
+    B, Hq, D = q.shape
+    Bk, L_max, Hkv, Dk = k_cache.shape
+    if Bk != B or Dk != D or q.stride(2) != 1 or k_cache.stride(3) != 1:
+        raise ValueError("q and the cache disagree, or the head_dim axis is not contiguous")
+    for name, s in (("k_scale", k_scale), ("v_scale", v_scale)):
+        if s.dtype != torch.float32 or s.shape != (B, L_max, Hkv):
+            raise ValueError(f"{name} must be float32 of shape [B, L_max, Hkv]")
+    if k_scale.stride() != v_scale.stride():
+        raise ValueError("k_scale and v_scale must share strides")
+    if seq_lens is not None:
+        _check_seq_lens(seq_lens, B)
+    p = GqaParams()
+    p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim, p.max_seq_len = B, Hq, Hkv, D, L_max
+    p.dtype = DA_DTYPE_FP8_E4M3
+    p.softmax_scale = (1.0 / math.sqrt(D)) if softmax_scale is None else float(softmax_scale)
+    p.q_stride_b, p.q_stride_h = q.stride(0), q.stride(1)
+    p.kv_stride_b, p.kv_stride_t, p.kv_stride_h = k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)
+    p.num_splits = int(num_splits)
+    sc = KvScales()
+    sc.k_scale, sc.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
+    sc.stride_b, sc.stride_t, sc.stride_h = k_scale.stride()
+    L = lib()
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ws_bytes = L.da_gqa_decode_workspace_size(ctypes.byref(p))
+    ws = _workspace(ws_bytes, q.device)
+    st = L.da_gqa_decode_fp8(ctypes.byref(p), ctypes.byref(sc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                             _ptr(seq_lens), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream_handle())
+    _check(st, "da_gqa_decode_fp8")
+    return out, lse
 
 
 # ----------------------------------------------------------------------------
@@ -540,5 +615,6 @@ def splitkv_combine(partial_out: torch.Tensor, partial_lse: torch.Tensor,
 
 
 __all__ = ["gqa_decode", "mla_decode_absorbed", "splitkv_combine", "gqa_num_splits",
-           "mla_num_splits", "gqa_decode_paged", "mla_decode_absorbed_paged", "paged_kv", "lib",
+           "mla_num_splits", "gqa_decode_paged", "mla_decode_absorbed_paged", "paged_kv",
+           "gqa_decode_fp8", "KvScales", "lib",
            "LIB_PATH", "GqaParams", "MlaParams", "PagedKv", "DecodeAttnError", "LibraryMissing"]

@@ -55,15 +55,25 @@ da_status_t check_gqa_params(const da_gqa_params_t* p) {
     return DA_ERR_INVALID_ARGUMENT;
   if (p->num_q_heads % p->num_kv_heads != 0) return DA_ERR_INVALID_ARGUMENT;
   if (p->num_q_heads > 65535) return DA_ERR_INVALID_ARGUMENT;
-  if (p->dtype != DA_DTYPE_F32 && p->dtype != DA_DTYPE_BF16) return DA_ERR_INVALID_ARGUMENT;
+  if (p->dtype != DA_DTYPE_F32 && p->dtype != DA_DTYPE_BF16 && p->dtype != DA_DTYPE_FP8_E4M3)
+    return DA_ERR_INVALID_ARGUMENT;
   if (!isfinite(p->softmax_scale)) return DA_ERR_INVALID_ARGUMENT;
   if (p->head_dim != 64 && p->head_dim != 128) return DA_ERR_UNSUPPORTED;
-  const int64_t esz = p->dtype == DA_DTYPE_BF16 ? 2 : 4;
-  const int64_t strides[5] = {p->q_stride_b, p->q_stride_h, p->kv_stride_b, p->kv_stride_t,
-                              p->kv_stride_h};
-  for (int64_t s : strides)
-    if (s < 0 || (s * esz) % 16 != 0) return DA_ERR_INVALID_ARGUMENT;
+  // element bytes of q and of the cache (fp8 caches take bf16 queries)
+  const int64_t q_esz = p->dtype == DA_DTYPE_F32 ? 4 : 2;
+  const int64_t kv_esz = p->dtype == DA_DTYPE_F32 ? 4 : p->dtype == DA_DTYPE_BF16 ? 2 : 1;
+  const int64_t q_strides[2] = {p->q_stride_b, p->q_stride_h};
+  const int64_t kv_strides[3] = {p->kv_stride_b, p->kv_stride_t, p->kv_stride_h};
+  for (int64_t s : q_strides)
+    if (s < 0 || (s * q_esz) % 16 != 0) return DA_ERR_INVALID_ARGUMENT;
+  for (int64_t s : kv_strides)
+    if (s < 0 || (s * kv_esz) % 16 != 0) return DA_ERR_INVALID_ARGUMENT;
   return DA_OK;
+}
+
+// Kernel dtype code (0 f32, 1 bf16, 2 fp8 cache with bf16 queries).
+int gqa_kernel_dtype(const da_gqa_params_t* p) {
+  return p->dtype == DA_DTYPE_F32 ? 0 : p->dtype == DA_DTYPE_BF16 ? 1 : 2;
 }
 
 // Split count for `units` independent work items of `len` rows each when
@@ -115,7 +125,7 @@ GqaPlan plan_gqa(const da_gqa_params_t* p, int align = 1) {
   //    CU, as many splits as fit in one round (where that shape is built).
   // Chunks stay at least 128 rows.
   const int64_t cus = device_cu_count();
-  const bool wide = da::gqa_wide_supported(p->dtype == DA_DTYPE_BF16 ? 1 : 0, pl.heads_per_block);
+  const bool wide = da::gqa_wide_supported(gqa_kernel_dtype(p), pl.heads_per_block);
   int64_t s;
   if (p->num_splits > 0) {
     s = p->num_splits;
@@ -348,6 +358,57 @@ void set_paged(Args& a, const da_paged_kv_t* pg) {
   a.page_stride = pg->page_stride;
 }
 
+// One GQA decode call: split pass (over paged pools when `pages`, over an
+// fp8 cache with `scales`), then the combine when there are several splits.
+da_status_t gqa_decode_impl(const da_gqa_params_t* p, const da_paged_kv_t* pages,
+                            const da_kv_scales_t* scales, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* seq_lens, float* out, float* lse,
+                            void* workspace, size_t workspace_bytes, void* hip_stream) {
+  da_status_t st = check_gqa_params(p);
+  if (st != DA_OK) return st;
+  if (pages) {
+    st = check_paged(pages, p->max_seq_len, p->dtype == DA_DTYPE_BF16 ? 2 : 4);
+    if (st != DA_OK) return st;
+  }
+  if (scales) {
+    if (!scales->k_scale || !scales->v_scale || !aligned4(scales->k_scale) ||
+        !aligned4(scales->v_scale) || scales->stride_b < 0 || scales->stride_t < 0 ||
+        scales->stride_h < 0)
+      return DA_ERR_INVALID_ARGUMENT;
+  }
+  st = check_gqa_buffers(q, k_cache, v_cache, seq_lens, out, lse);
+  if (st != DA_OK) return st;
+  // paged calls split on multiples of 16 rows (a step never straddles a page)
+  const GqaPlan pl = plan_gqa(p, pages ? 16 : 1);
+  if (pl.workspace > 0) {
+    if (!workspace || workspace_bytes < pl.workspace) return DA_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned16(workspace)) return DA_ERR_INVALID_ARGUMENT;
+  }
+  da::GqaArgs a = gqa_args(p, pl, q, k_cache, v_cache, seq_lens);
+  if (pages) set_paged(a, pages);
+  if (scales) {
+    a.k_scale = scales->k_scale;
+    a.v_scale = scales->v_scale;
+    a.sc_sb = scales->stride_b;
+    a.sc_st = scales->stride_t;
+    a.sc_sh = scales->stride_h;
+  }
+  a.out = out;
+  a.lse = lse;
+  if (pl.splits > 1) {
+    a.part_out = reinterpret_cast<float*>(workspace);
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.part_out_bytes);
+  }
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  hipError_t e = da::launch_gqa_decode(a, gqa_kernel_dtype(p), p->head_dim, stream);
+  if (e != hipSuccess) return DA_ERR_HIP;
+  if (pl.splits > 1) {
+    e = da::launch_splitkv_combine(pl.splits, p->batch * p->num_q_heads, p->head_dim, a.part_out,
+                                   a.part_lse, out, lse, stream);
+  }
+  return from_hip(e);
+}
+
 }  // namespace
 
 
@@ -369,6 +430,7 @@ da_status_t da_gqa_decode_split_pass(const da_gqa_params_t* p, const void* q,
                                      void* hip_stream) {
   da_status_t st = check_gqa_params(p);
   if (st != DA_OK) return st;
+  if (p->dtype == DA_DTYPE_FP8_E4M3) return DA_ERR_INVALID_ARGUMENT;   // needs scales
   st = check_gqa_buffers(q, k_cache, v_cache, seq_lens, part_out, part_lse);
   if (st != DA_OK) return st;
   if (!part_lse) return DA_ERR_INVALID_ARGUMENT;
@@ -381,70 +443,35 @@ da_status_t da_gqa_decode_split_pass(const da_gqa_params_t* p, const void* q,
     a.part_out = part_out;
     a.part_lse = part_lse;
   }
-  return from_hip(da::launch_gqa_decode(a, p->dtype == DA_DTYPE_BF16 ? 1 : 0, p->head_dim,
+  return from_hip(da::launch_gqa_decode(a, gqa_kernel_dtype(p), p->head_dim,
                                         static_cast<hipStream_t>(hip_stream)));
 }
 
 da_status_t da_gqa_decode(const da_gqa_params_t* p, const void* q, const void* k_cache,
                           const void* v_cache, const int32_t* seq_lens, float* out, float* lse,
                           void* workspace, size_t workspace_bytes, void* hip_stream) {
-  da_status_t st = check_gqa_params(p);
-  if (st != DA_OK) return st;
-  st = check_gqa_buffers(q, k_cache, v_cache, seq_lens, out, lse);
-  if (st != DA_OK) return st;
-  const GqaPlan pl = plan_gqa(p);
-  if (pl.workspace > 0) {
-    if (!workspace || workspace_bytes < pl.workspace) return DA_ERR_WORKSPACE_TOO_SMALL;
-    if (!aligned16(workspace)) return DA_ERR_INVALID_ARGUMENT;
-  }
-  da::GqaArgs a = gqa_args(p, pl, q, k_cache, v_cache, seq_lens);
-  a.out = out;
-  a.lse = lse;
-  if (pl.splits > 1) {
-    a.part_out = reinterpret_cast<float*>(workspace);
-    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.part_out_bytes);
-  }
-  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  hipError_t e = da::launch_gqa_decode(a, p->dtype == DA_DTYPE_BF16 ? 1 : 0, p->head_dim, stream);
-  if (e != hipSuccess) return DA_ERR_HIP;
-  if (pl.splits > 1) {
-    e = da::launch_splitkv_combine(pl.splits, p->batch * p->num_q_heads, p->head_dim, a.part_out,
-                                   a.part_lse, out, lse, stream);
-  }
-  return from_hip(e);
+  if (p && p->dtype == DA_DTYPE_FP8_E4M3) return DA_ERR_INVALID_ARGUMENT;   // needs scales
+  return gqa_decode_impl(p, nullptr, nullptr, q, k_cache, v_cache, seq_lens, out, lse, workspace,
+                         workspace_bytes, hip_stream);
 }
 
 da_status_t da_gqa_decode_paged(const da_gqa_params_t* p, const da_paged_kv_t* pages, const void* q,
                                 const void* k_pool, const void* v_pool, const int32_t* seq_lens,
                                 float* out, float* lse, void* workspace, size_t workspace_bytes,
                                 void* hip_stream) {
-  da_status_t st = check_gqa_params(p);
-  if (st != DA_OK) return st;
-  st = check_paged(pages, p->max_seq_len, p->dtype == DA_DTYPE_BF16 ? 2 : 4);
-  if (st != DA_OK) return st;
-  st = check_gqa_buffers(q, k_pool, v_pool, seq_lens, out, lse);
-  if (st != DA_OK) return st;
-  const GqaPlan pl = plan_gqa(p, 16);
-  if (pl.workspace > 0) {
-    if (!workspace || workspace_bytes < pl.workspace) return DA_ERR_WORKSPACE_TOO_SMALL;
-    if (!aligned16(workspace)) return DA_ERR_INVALID_ARGUMENT;
-  }
-  da::GqaArgs a = gqa_args(p, pl, q, k_pool, v_pool, seq_lens);
-  set_paged(a, pages);
-  a.out = out;
-  a.lse = lse;
-  if (pl.splits > 1) {
-    a.part_out = reinterpret_cast<float*>(workspace);
-    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.part_out_bytes);
-  }
-  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  hipError_t e = da::launch_gqa_decode(a, p->dtype == DA_DTYPE_BF16 ? 1 : 0, p->head_dim, stream);
-  if (e != hipSuccess) return DA_ERR_HIP;
-  if (pl.splits > 1) {
-    e = da::launch_splitkv_combine(pl.splits, p->batch * p->num_q_heads, p->head_dim, a.part_out,
-                                   a.part_lse, out, lse, stream);
-  }
-  return from_hip(e);
+  if (!pages) return DA_ERR_INVALID_ARGUMENT;
+  if (p && p->dtype == DA_DTYPE_FP8_E4M3) return DA_ERR_INVALID_ARGUMENT;
+  return gqa_decode_impl(p, pages, nullptr, q, k_pool, v_pool, seq_lens, out, lse, workspace,
+                         workspace_bytes, hip_stream);
+}
+
+da_status_t da_gqa_decode_fp8(const da_gqa_params_t* p, const da_kv_scales_t* scales, const void* q,
+                              const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                              float* out, float* lse, void* workspace, size_t workspace_bytes,
+                              void* hip_stream) {
+  if (!p || p->dtype != DA_DTYPE_FP8_E4M3 || !scales) return DA_ERR_INVALID_ARGUMENT;
+  return gqa_decode_impl(p, nullptr, scales, q, k_cache, v_cache, seq_lens, out, lse, workspace,
+                         workspace_bytes, hip_stream);
 }
 
 size_t da_mla_decode_workspace_size(const da_mla_params_t* p) {
@@ -629,5 +656,6 @@ int32_t da_version(void) { return 100; }
 size_t da_gqa_params_size(void) { return sizeof(da_gqa_params_t); }
 size_t da_mla_params_size(void) { return sizeof(da_mla_params_t); }
 size_t da_paged_kv_size(void) { return sizeof(da_paged_kv_t); }
+size_t da_kv_scales_size(void) { return sizeof(da_kv_scales_t); }
 
 }  // extern "C"

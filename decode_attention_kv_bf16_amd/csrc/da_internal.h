@@ -33,9 +33,14 @@ struct GqaArgs {
   const int32_t* block_table;
   int32_t page_shift, max_blocks;
   int64_t page_stride;
+  // FP8 (E4M3) caches (dtype 2): element (b, t, h, :) of K stands for its
+  // code times k_scale[b * sc_sb + t * sc_st + h * sc_sh] (V likewise).
+  const float* k_scale;
+  const float* v_scale;
+  int64_t sc_sb, sc_st, sc_sh;
 };
 
-// dtype: 0 = f32, 1 = bf16 (matches da_dtype_t).
+// dtype: 0 = f32, 1 = bf16, 2 = fp8 E4M3 cache with bf16 queries (matches da_dtype_t).
 hipError_t launch_gqa_decode(const GqaArgs& a, int dtype, int head_dim, hipStream_t stream);
 
 // Whether 16-wave workgroups exist for this dtype and heads per workgroup.

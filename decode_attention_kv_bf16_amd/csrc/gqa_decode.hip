@@ -27,6 +27,8 @@
 //   the waves through LDS.
 //   Scores live in the base-2 domain: q is pre-multiplied by scale*log2(e) so
 //   each softmax weight is one v_exp_f32.
+#include <type_traits>
+
 #include "da_device.h"
 #include "da_internal.h"
 
@@ -39,10 +41,15 @@ constexpr int kEPL = 8;  // elements of a cache row owned by one lane
 // policy) stream them without displacing reusable lines, and measured faster
 // on MI355X (about 7.0 vs 6.2 TB/s for a plain streaming read of 512 MiB).
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load_stream(const uint4* p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load_stream(const uint2* p) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
 }
 __device__ __forceinline__ float4 load_stream(const float4* p) {
   const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
@@ -84,6 +91,48 @@ struct Row8<float> {
   static __device__ __forceinline__ void cvt(const Raw& r, float* f) {
     f[0] = r.a.x; f[1] = r.a.y; f[2] = r.a.z; f[3] = r.a.w;
     f[4] = r.b.x; f[5] = r.b.y; f[6] = r.b.z; f[7] = r.b.w;
+  }
+};
+
+// E4M3 codes, one byte each (the OCP 8-bit floating-point format; FP8 caches,
+// "Attention variants and KV cache", arganzheng.life, section 6.3): 8
+// elements in 8 bytes. Every E4M3 value is exactly a bf16 value, so key words
+// become bf16 pairs for the dot2 score path (the conversion's scale operand is
+// 1.0: it only applies a power of two), and values are converted to fp32.
+template <>
+struct Row8<uint8_t> {
+  struct Raw {
+    uint2 w;
+  };
+  static __device__ __forceinline__ Raw load(const uint8_t* p) {
+    return {load_stream(reinterpret_cast<const uint2*>(p))};
+  }
+  static __device__ __forceinline__ Raw load_plain(const uint8_t* p) {
+    return {*reinterpret_cast<const uint2*>(p)};
+  }
+  static __device__ __forceinline__ Raw zero() { return {make_uint2(0u, 0u)}; }
+  static __device__ __forceinline__ void cvt(const Raw& r, float* f) {
+    const uint32_t w[2] = {r.w.x, r.w.y};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], true);
+      f[4 * j + 0] = lo[0];
+      f[4 * j + 1] = lo[1];
+      f[4 * j + 2] = hi[0];
+      f[4 * j + 3] = hi[1];
+    }
+  }
+  // the 8 elements as 4 words of bf16 pairs, in element order
+  static __device__ __forceinline__ uint4 bf16x8(const Raw& r) {
+    const uint32_t w[2] = {r.w.x, r.w.y};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      o[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[j], 1.0f, false));
+      o[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[j], 1.0f, true));
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
   }
 };
 
@@ -178,22 +227,27 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
     return;
   }
 
-  // Queries. bf16: kept as packed pairs, scores by v_dot2c_f32_bf16 straight
-  // from the raw cache words (products of bf16 values are exact in fp32), and
-  // the scale is applied to the reduced score. fp32: converted, pre-scaled.
-  constexpr bool kBf16 = sizeof(T) == 2;
+  // Queries. bf16 (and fp8 caches, whose queries are bf16): kept as packed
+  // pairs, scores by v_dot2c_f32_bf16 straight from the raw bf16 cache words
+  // (or the fp8 words converted to bf16 pairs, exactly); products of bf16
+  // values are exact in fp32, and the scale is applied to the reduced score.
+  // fp32: converted, pre-scaled.
+  constexpr bool kFp8 = sizeof(T) == 1;
+  constexpr bool kBf16 = sizeof(T) <= 2;
+  using TQ = typename std::conditional<kFp8, uint16_t, T>::type;
+  using RQ = Row8<TQ>;
   uint32_t qp[GH][kEPL / 2];
   float qf[kBf16 ? 1 : GH][kEPL];
   {
-    const T* qsrc = reinterpret_cast<const T*>(a.q) + b * a.q_sb + col * kEPL;
+    const TQ* qsrc = reinterpret_cast<const TQ*>(a.q) + b * a.q_sb + col * kEPL;
 #pragma unroll
     for (int i = 0; i < GH; ++i) {
-      const typename R::Raw r = R::load_plain(qsrc + (int64_t)(h0 + i) * a.q_sh);  // re-read by every split
+      const typename RQ::Raw r = RQ::load_plain(qsrc + (int64_t)(h0 + i) * a.q_sh);  // re-read by every split
       if constexpr (kBf16) {
         const uint4 w = *reinterpret_cast<const uint4*>(&r);
         qp[i][0] = w.x; qp[i][1] = w.y; qp[i][2] = w.z; qp[i][3] = w.w;
       } else {
-        R::cvt(r, qf[i]);
+        RQ::cvt(r, qf[i]);
 #pragma unroll
         for (int e = 0; e < kEPL; ++e) qf[i][e] *= a.scale_log2;
       }
@@ -252,6 +306,26 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
     return (int64_t)page * a.page_stride + (int64_t)(base & ((1 << a.page_shift) - 1)) * a.kv_st;
   };
 
+  // key words as bf16 pairs (fp8: converted exactly)
+  auto key_words = [](const typename R::Raw& r) -> uint4 {
+    if constexpr (kFp8) {
+      return R::bf16x8(r);
+    } else {
+      return *reinterpret_cast<const uint4*>(&r);
+    }
+  };
+  (void)key_words;
+  // FP8 caches: one fp32 scale per (token, KV head) for K and for V, read
+  // with the step's rows. A lane needs the scales of its own rows (kSc = U),
+  // or in the reduce-scatter path only of the token whose scores it finishes
+  // (token (col / 4) of its row group: kSc = 1).
+  constexpr int kSc = kFp8 ? (kRS ? 1 : U) : 1;
+  const float* ksc = kFp8 ? a.k_scale + b * a.sc_sb + kvh * a.sc_sh : nullptr;
+  const float* vsc = kFp8 ? a.v_scale + b * a.sc_sb + kvh * a.sc_sh : nullptr;
+  float ksl[kSc], vsl[kSc];
+  (void)ksl;
+  (void)vsl;
+
   auto load_step = [&](int base, int64_t off, typename R::Raw (&kk)[U], typename R::Raw (&vv)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -264,11 +338,20 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
         vv[u] = R::zero();
       }
     }
+    if constexpr (kFp8) {
+#pragma unroll
+      for (int j = 0; j < kSc; ++j) {
+        const int t = base + (kRS ? (col >> 2) : j) * RPW + row;
+        const bool ok = t < t_end;
+        ksl[j] = ok ? ksc[(int64_t)t * a.sc_st] : 0.f;
+        vsl[j] = ok ? vsc[(int64_t)t * a.sc_st] : 0.f;
+      }
+    }
   };
   // One head per workgroup (MHA, bf16): the rows of the next step are loaded
   // before the math of this one, two steps in flight per wave (ragged MHA
   // B = 64: 688 -> 680 us). With more heads per workgroup it measured slower.
-  constexpr bool kPrefetch = kBf16 && GH == 1;
+  constexpr bool kPrefetch = sizeof(T) == 2 && GH == 1;
   constexpr int kStep = kWaves * TOK;
   typename R::Raw kw[U], vw[U];
   // page_n: table entry of the next step whose rows are loaded
@@ -292,7 +375,7 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
       float v[kRsN];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const uint4 w = *reinterpret_cast<const uint4*>(&kw[u]);
+        const uint4 w = key_words(kw[u]);
         const uint32_t kk[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int i = 0; i < GH; ++i) {
@@ -311,7 +394,7 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
       bool moved = false;
 #pragma unroll
       for (int k = 0; k < kRsV; ++k) {
-        const float sc = valid ? v[k] * a.scale_log2 : kNegInf;
+        const float sc = valid ? v[k] * (kFp8 ? a.scale_log2 * ksl[0] : a.scale_log2) : kNegInf;
         float mx = fmaxf(sc, dpp_mov<kDppRowRor4>(sc));   // the group's 4 tokens of this head
         mx = fmaxf(mx, dpp_mov<kDppRowRor8>(mx));
         const float mn = fmaxf(ms[k], mx);
@@ -319,6 +402,7 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
         alpha[k] = exp2_hw(ms[k] - mu);
         p[k] = exp2_hw(sc - mu);
         ls[k] = ls[k] * alpha[k] + p[k];
+        if constexpr (kFp8) p[k] *= vsl[0];   // the value scale rides on the weight
         moved |= mn != ms[k];
         ms[k] = mn;
       }
@@ -348,14 +432,14 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
     for (int u = 0; u < U; ++u) {
       const bool valid = base + u * RPW + row < t_end;
       if constexpr (kBf16) {
-        const uint4 w = *reinterpret_cast<const uint4*>(&kw[u]);
+        const uint4 w = key_words(kw[u]);
         const uint32_t kk[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int i = 0; i < GH; ++i) {
           float d = 0.f;
 #pragma unroll
           for (int j = 0; j < 4; ++j) d = dot2_bf16(qp[i][j], kk[j], d);
-          d = group_sum<LPT>(d) * a.scale_log2;
+          d = group_sum<LPT>(d) * (kFp8 ? a.scale_log2 * ksl[u] : a.scale_log2);
           s[i][u] = valid ? d : kNegInf;
         }
       } else {
@@ -386,6 +470,7 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
       for (int u = 0; u < U; ++u) {
         s[i][u] = exp2_hw(s[i][u] - mu);
         l[i] += s[i][u];
+        if constexpr (kFp8) s[i][u] *= vsl[u];   // the value scale rides on the weight
       }
       m[i] = mx;
     }
@@ -487,7 +572,7 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
 // instantiations that fit without spilling.
 template <typename T, int GH>
 constexpr bool wide_fits() {
-  return sizeof(T) == 2 ? GH <= 4 : GH <= 2;
+  return sizeof(T) <= 2 ? GH <= 4 : GH <= 2;
 }
 
 template <typename T, int D, int GH>
@@ -526,7 +611,7 @@ hipError_t launch_gh(const GqaArgs& a, hipStream_t st) {
 }  // namespace
 
 bool gqa_wide_supported(int dtype, int heads_per_block) {
-  return dtype == 1 ? heads_per_block <= 4 : heads_per_block <= 2;
+  return dtype != 0 ? heads_per_block <= 4 : heads_per_block <= 2;
 }
 
 hipError_t launch_gqa_decode(const GqaArgs& a, int dtype, int head_dim, hipStream_t st) {
@@ -536,6 +621,9 @@ hipError_t launch_gqa_decode(const GqaArgs& a, int dtype, int head_dim, hipStrea
   } else if (dtype == 0) {
     if (head_dim == 128) return launch_gh<float, 128>(a, st);
     if (head_dim == 64) return launch_gh<float, 64>(a, st);
+  } else if (dtype == 2) {
+    if (head_dim == 128) return launch_gh<uint8_t, 128>(a, st);
+    if (head_dim == 64) return launch_gh<uint8_t, 64>(a, st);
   }
   return hipErrorInvalidValue;
 }

@@ -72,7 +72,8 @@ typedef enum {
 
 typedef enum {
   DA_DTYPE_F32 = 0,
-  DA_DTYPE_BF16 = 1
+  DA_DTYPE_BF16 = 1,
+  DA_DTYPE_FP8_E4M3 = 2   /* GQA only, da_gqa_decode_fp8: cache in E4M3, queries in bf16 */
 } da_dtype_t;
 
 /* ------------------------------------------------------------------------ */
@@ -85,11 +86,12 @@ typedef struct {
   int32_t num_kv_heads;    /* Hkv >= 1 */
   int32_t head_dim;        /* D: 64 or 128 */
   int32_t max_seq_len;     /* L_max >= 1: rows allocated per sequence */
-  da_dtype_t dtype;        /* element type of q, k_cache and v_cache */
+  da_dtype_t dtype;        /* element type of q, k_cache and v_cache (FP8_E4M3: see da_gqa_decode_fp8) */
   float softmax_scale;     /* usually 1/sqrt(head_dim) */
   int64_t q_stride_b;      /* q[b, h, d] at q + b*q_stride_b + h*q_stride_h + d */
   int64_t q_stride_h;
-  int64_t kv_stride_b;     /* k[b, t, kh, d] at k + b*kv_stride_b + t*kv_stride_t + kh*kv_stride_h + d */
+  int64_t kv_stride_b;     /* k[b, t, kh, d] at k + b*kv_stride_b + t*kv_stride_t + kh*kv_stride_h + d;
+                              all strides in elements of their own array */
   int64_t kv_stride_t;     /* default layout [B, L_max, Hkv, D]: */
   int64_t kv_stride_h;     /*   kv_stride_b = L_max*Hkv*D, kv_stride_t = Hkv*D, kv_stride_h = D */
   int32_t num_splits;      /* S >= 1 forces a split count; 0 lets the library choose */
@@ -302,6 +304,41 @@ DA_EXPORT da_status_t da_mla_attend_split_pass_paged(const da_mla_params_t* para
                                                      void* hip_stream);
 
 /* ------------------------------------------------------------------------ */
+/* FP8 (E4M3) KV caches                                                      */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Quantized caches ("Attention variants and KV cache", arganzheng.life,
+ * section 6.3): one byte per element in the E4M3 format (read here as the
+ * OCP 8-bit floating-point E4M3: bias 7, largest finite 448, no infinities),
+ * with fp32 scale factors, so that the bytes read at decode halve. Element
+ * (b, t, h, :) of K stands for E4M3(code) * k_scale[b, t, h]; V likewise with
+ * v_scale. The scale arrays are indexed through the strides below (in floats),
+ * so one scale per (token, KV head), per token (stride_h = 0) or per KV head
+ * (stride_b = stride_t = 0) are all the same call.
+ */
+typedef struct {
+  const float* k_scale;   /* device, 4-byte aligned */
+  const float* v_scale;   /* device, 4-byte aligned; same strides as k_scale */
+  int64_t stride_b;       /* scale of (b, t, h) at b*stride_b + t*stride_t + h*stride_h (>= 0) */
+  int64_t stride_t;
+  int64_t stride_h;
+} da_kv_scales_t;
+
+/* da_gqa_decode over an E4M3 cache. params->dtype must be DA_DTYPE_FP8_E4M3:
+ * q is bf16 (its strides in bf16 elements), k_cache and v_cache hold one-byte
+ * codes (their strides in bytes, multiples of 16). Scales are read only for
+ * rows [0, seq_lens[b]). Workspace as da_gqa_decode_workspace_size for the
+ * same params. Errors: as da_gqa_decode, and INVALID_ARGUMENT for another
+ * dtype, a NULL `scales` or scale pointer, a misaligned scale pointer or a
+ * negative scale stride. da_gqa_decode, da_gqa_decode_split_pass and
+ * da_gqa_decode_paged reject DA_DTYPE_FP8_E4M3 (they have no scales). */
+DA_EXPORT da_status_t da_gqa_decode_fp8(const da_gqa_params_t* params, const da_kv_scales_t* scales,
+                                        const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* seq_lens, float* out, float* lse,
+                                        void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------------ */
 /* Split-KV merge                                                            */
 /* ------------------------------------------------------------------------ */
 
@@ -330,11 +367,13 @@ DA_EXPORT const char* da_status_string(da_status_t status);
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 DA_EXPORT int32_t da_version(void);
 
-/* sizeof(da_gqa_params_t), sizeof(da_mla_params_t) and sizeof(da_paged_kv_t)
- * as compiled, so that bindings can check their struct mirrors. */
+/* sizeof(da_gqa_params_t), sizeof(da_mla_params_t), sizeof(da_paged_kv_t)
+ * and sizeof(da_kv_scales_t) as compiled, so that bindings can check their
+ * struct mirrors. */
 DA_EXPORT size_t da_gqa_params_size(void);
 DA_EXPORT size_t da_mla_params_size(void);
 DA_EXPORT size_t da_paged_kv_size(void);
+DA_EXPORT size_t da_kv_scales_size(void);
 
 #ifdef __cplusplus
 }

@@ -51,6 +51,7 @@ def test_struct_mirrors_and_version():
     assert L.da_gqa_params_size() == ctypes.sizeof(da.GqaParams) == 80
     assert L.da_mla_params_size() == ctypes.sizeof(da.MlaParams)
     assert L.da_paged_kv_size() == ctypes.sizeof(da.PagedKv) == 24
+    assert L.da_kv_scales_size() == ctypes.sizeof(da.KvScales) == 40
     assert L.da_version() >= 100
     for s, txt in [(0, b"ok"), (1, b"invalid argument"), (2, b"unsupported configuration"),
                    (3, b"workspace too small"), (4, b"HIP runtime error"), (99, b"unknown status")]:
@@ -273,6 +274,56 @@ def test_paged_entry_points_reject_missing_descriptor_and_workspace():
                                           FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == 1
     assert L.da_mla_decode_absorbed_paged(ctypes.byref(m), ctypes.byref(pgm), FAKE, FAKE, FAKE,
                                           FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, None) == 3
+
+
+def fp8_params(B=32, Hq=32, Hkv=8, D=128, L=4096):
+    p = gqa(B, Hq, Hkv, D, L)
+    p.dtype = da.DA_DTYPE_FP8_E4M3
+    p.kv_stride_b, p.kv_stride_t, p.kv_stride_h = L * Hkv * D, Hkv * D, D     # bytes
+    return p
+
+
+def scales(k=FAKE, v=FAKE, sb=4096 * 8, st=8, sh=1):
+    s = da.KvScales()
+    s.k_scale = k.value if k is not None else None
+    s.v_scale = v.value if v is not None else None
+    s.stride_b, s.stride_t, s.stride_h = sb, st, sh
+    return s
+
+
+@needs_lib
+def test_fp8_params_plan_like_bf16():
+    L = da.lib()
+    p = fp8_params()
+    assert L.da_gqa_decode_num_splits(ctypes.byref(p)) == L.da_gqa_decode_num_splits(ctypes.byref(gqa()))
+    p.kv_stride_t = 8 * 128 + 8          # 1032 bytes: not a multiple of 16
+    assert L.da_gqa_decode_num_splits(ctypes.byref(p)) == 0
+
+
+@needs_lib
+@cpu_only
+def test_fp8_entry_point_rejects_bad_arguments():
+    L = da.lib()
+
+    def call(p, s, ws_bytes=1 << 40):
+        return L.da_gqa_decode_fp8(ctypes.byref(p), ctypes.byref(s) if s is not None else None, FAKE,
+                                   FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
+    assert call(fp8_params(), None) == 1                       # no scales
+    assert call(fp8_params(), scales(k=None)) == 1
+    assert call(fp8_params(), scales(v=ctypes.c_void_p(0x10002))) == 1   # misaligned
+    assert call(fp8_params(), scales(st=-8)) == 1
+    bf = gqa()
+    assert call(bf, scales()) == 1                             # not the fp8 dtype
+    p = fp8_params()
+    p.q_stride_h = 132                                         # 264 bytes of bf16 q
+    assert call(p, scales()) == 1
+    p16 = fp8_params(16)                                       # two splits: needs a workspace
+    assert call(p16, scales(), ws_bytes=0) == 3
+    # the entry points without scales refuse the fp8 dtype
+    assert L.da_gqa_decode(ctypes.byref(fp8_params()), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                           1 << 40, None) == 1
+    assert L.da_gqa_decode_split_pass(ctypes.byref(fp8_params()), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      None) == 1
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):

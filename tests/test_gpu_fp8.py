@@ -1,0 +1,142 @@
+"""GPU parity of GQA decode over an FP8 (E4M3) cache ("Attention variants and
+KV cache", arganzheng.life, section 6.3) against the fp64 oracle, through
+the C ABI via the Python binding.
+
+The kernel decodes every code exactly (E4M3 values are bf16 values), so its
+only roundings are fp32 sums and the per-row scale products: results sit far
+inside the bar, and the tests also assert a tight 1e-4. Rows past each length
+hold the NaN code and NaN scales, so any read past the end poisons the row.
+"""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_kv_bf16_amd as da
+import workloads as W
+from gpu_util import announce, assert_parity, bf16_tensor
+from oracle.fp8 import gqa_decode_fp8_ref
+
+pytestmark = pytest.mark.gpu
+
+
+def to_device(inp):
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    return (bf16_tensor(inp.q), dev(inp.k), dev(inp.v), dev(inp.k_scale), dev(inp.v_scale),
+            dev(inp.seq_lens.astype(np.int32)))
+
+
+def run(inp, num_splits=0, scales=None):
+    q, k, v, ks, vs, sl = to_device(inp)
+    if scales is not None:
+        ks, vs = scales
+    out, lse = da.gqa_decode_fp8(q, k, v, ks, vs, sl, inp.scale, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+def oracle_rows(inp, seqs):
+    seqs = list(seqs)
+    Lm = int(max(1, inp.seq_lens[seqs].max()))
+    q = W.bf16_to_f32(inp.q[seqs]).astype(np.float64)
+    return gqa_decode_fp8_ref(q, inp.k[seqs, :Lm], inp.v[seqs, :Lm], inp.k_scale[seqs, :Lm],
+                              inp.v_scale[seqs, :Lm], inp.seq_lens[seqs], inp.scale)
+
+
+def check(inp, out, lse, seqs=None, what=""):
+    seqs = list(range(len(inp.seq_lens)) if seqs is None else seqs)
+    ro, rl = oracle_rows(inp, seqs)
+    assert_parity(out[seqs], lse[seqs], ro, rl, what=what)
+    assert_parity(out[seqs], lse[seqs], ro, rl, out_rtol=1e-4, lse_atol=1e-4, what=what + " tight")
+
+
+def test_config2_shapes_reduced_batch_all_rows():
+    announce("gqa fp8 B4 Hq32 Hkv8 D128 L4096")
+    inp = W.make_gqa_fp8(4, 32, 8, 128, [4096, 4096, 4096, 4096], seed=3)
+    out, lse = run(inp)
+    check(inp, out, lse, what="fp8 B4")
+
+
+def test_config2_full_size_sampled():
+    announce("gqa fp8 config2 full B32 L4096, sampled rows")
+    inp = W.make_gqa_fp8_config(2)
+    out, lse = run(inp)
+    check(inp, out, lse, seqs=[0, 17, 31], what="fp8 config2")
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+
+
+EDGE = [
+    # B, Hq, Hkv, D, lens
+    (4, 8, 2, 128, [0, 1, 15, 17]),                    # empty, L = 1, ragged tails
+    (2, 32, 1, 128, [700, 2049]),                      # MQA, g = 32
+    (3, 12, 4, 128, [100, 64, 1]),                     # g = 3 (no reduce-scatter path)
+    (2, 8, 8, 128, [3000, 5000]),                      # MHA: few units, 16-wave workgroups
+    (2, 16, 2, 64, [129, 4000]),                       # D = 64
+    (3, 14, 2, 64, [33, 1, 517]),                      # D = 64, g = 7
+    (16, 32, 8, 128, [4096, 1, 0, 2000, 129, 4095, 77, 3000,
+                      1024, 33, 2500, 4096, 0, 640, 1500, 2]),   # 8-wave, 2 splits
+    (64, 32, 32, 128, [(i % 5) * 97 + (i % 3) for i in range(64)]),   # longest-first order
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,lens", EDGE)
+def test_edge_cases(B, Hq, Hkv, D, lens):
+    announce(f"gqa fp8 edge B{B} Hq{Hq} Hkv{Hkv} D{D} lens{lens}")
+    inp = W.make_gqa_fp8(B, Hq, Hkv, D, lens, seed=13, max_seq_len=max(lens) + 5)
+    out, lse = run(inp)
+    check(inp, out, lse, what="fp8 edge")
+
+
+@pytest.mark.parametrize("splits", [1, 3, 16])
+def test_split_count_invariance(splits):
+    announce(f"gqa fp8 splits S={splits}")
+    inp = W.make_gqa_fp8(3, 16, 4, 128, [2500, 1, 777], seed=6, max_seq_len=2600)
+    out, lse = run(inp, num_splits=splits)
+    check(inp, out, lse, what=f"fp8 S={splits}")
+
+
+def test_per_head_scales_through_zero_strides():
+    # one scale per KV head: a [Hkv] vector expanded to [B, L, Hkv] with zero
+    # batch and token strides gives the same result as the full array
+    announce("gqa fp8 per-head scales (broadcast strides)")
+    inp = W.make_gqa_fp8(3, 16, 4, 128, [1000, 333, 2048], seed=8, max_seq_len=2048, scales="head",
+                         pad_nan=False)
+    ks_h = torch.from_numpy(inp.k_scale[0, 0].copy()).cuda()
+    vs_h = torch.from_numpy(inp.v_scale[0, 0].copy()).cuda()
+    B, L, H = inp.k_scale.shape
+    ks_b, vs_b = ks_h.expand(B, L, H), vs_h.expand(B, L, H)
+    assert ks_b.stride() == (0, 0, 1)
+    out_b, lse_b = run(inp, scales=(ks_b, vs_b))
+    out_f, lse_f = run(inp)
+    assert np.array_equal(out_b, out_f) and np.array_equal(lse_b, lse_f)
+    check(inp, out_b, lse_b, what="per-head scales")
+
+
+def test_fp8_matches_the_bf16_kernel_on_exact_values():
+    # scales that are powers of two make every dequantized element an exact
+    # bf16 value: the bf16 path on those values must give the same result to
+    # fp32 rounding
+    announce("gqa fp8 vs bf16 kernel on exact values")
+    inp = W.make_gqa_fp8(2, 32, 8, 128, [1500, 4096], seed=2, max_seq_len=4096, pad_nan=False)
+    inp.k_scale[:] = np.float32(2.0 ** -6)
+    inp.v_scale[:] = np.float32(2.0 ** -5)
+    out8, lse8 = run(inp)
+    from oracle.fp8 import dequantize_ref
+    kb = W.bf16_round(dequantize_ref(inp.k, inp.k_scale).astype(np.float32))
+    vb = W.bf16_round(dequantize_ref(inp.v, inp.v_scale).astype(np.float32))
+    sl = torch.from_numpy(inp.seq_lens.astype(np.int32)).cuda()
+    out16, lse16 = da.gqa_decode(bf16_tensor(inp.q), bf16_tensor(kb), bf16_tensor(vb), sl, inp.scale)
+    np.testing.assert_allclose(out8, out16.cpu().numpy(), rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(lse8, lse16.cpu().numpy(), rtol=0, atol=1e-5)
+
+
+def test_error_codes_with_real_buffers():
+    announce("gqa fp8 error codes")
+    q = torch.zeros((2, 8, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((2, 16, 2, 128), dtype=torch.uint8, device="cuda")
+    s = torch.ones((2, 16, 2), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        da.gqa_decode_fp8(q.float(), k, k, s, s)               # q must be bf16
+    with pytest.raises(ValueError):
+        da.gqa_decode_fp8(q, k, k, s[:, :8], s)                 # scale shape
+    out, lse = da.gqa_decode_fp8(q, k, k, s, s)                 # all-zero codes: mean of zeros
+    assert torch.all(out == 0) and torch.allclose(lse, torch.full_like(lse, float(np.log(16))))
