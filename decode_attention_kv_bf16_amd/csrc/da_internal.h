@@ -46,6 +46,11 @@ hipError_t launch_gqa_decode(const GqaArgs& a, int dtype, int head_dim, hipStrea
 // Whether 16-wave workgroups exist for this dtype and heads per workgroup.
 bool gqa_wide_supported(int dtype, int heads_per_block);
 
+// The matrix-core GQA kernel (gqa_mfma.hip): bf16 and fp8 caches, contiguous,
+// 4- or 8-wave workgroups, up to 16 heads per workgroup.
+bool gqa_mfma_supported(const GqaArgs& a, int dtype, int head_dim);
+hipError_t launch_gqa_mfma(const GqaArgs& a, int dtype, int head_dim, hipStream_t stream);
+
 // Log-sum-exp merge of split partials: rows = B * H.
 hipError_t launch_splitkv_combine(int32_t num_splits, int32_t rows, int32_t head_dim,
                                   const float* part_out, const float* part_lse,

@@ -167,30 +167,6 @@ __device__ __forceinline__ constexpr int rs_src_reg(int h) {
   return GH >= 4 ? h % (GH / 4) : 0;
 }
 
-// The sequence of rank r when the batch is ordered by length, longest first
-// (ties by index, so the ranks are a permutation). Workgroups are dispatched
-// in id order, so giving the lowest ids the longest sequences lets the short
-// ones fill the end of a ragged batch (longest-processing-time-first
-// scheduling). B <= 256; every thread of the workgroup takes part.
-template <int kThreads>
-__device__ __forceinline__ int longest_first(const int32_t* seq_lens, int B, int r) {
-  __shared__ int s_len[256];
-  __shared__ int s_pick;
-  for (int i = threadIdx.x; i < B; i += kThreads) s_len[i] = seq_lens[i];
-  __syncthreads();
-  for (int c = threadIdx.x; c < B; c += kThreads) {
-    const int lc = s_len[c];
-    int rank = 0;
-    for (int j = 0; j < B; ++j) {
-      const int lj = s_len[j];
-      rank += (lj > lc) | ((lj == lc) & (j < c));
-    }
-    if (rank == r) s_pick = c;
-  }
-  __syncthreads();
-  return __builtin_amdgcn_readfirstlane(s_pick);
-}
-
 template <typename T, int D, int GH, int kWaves>
 __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
   constexpr int kThreads = kWaves * 64;
@@ -326,7 +302,8 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
   (void)ksl;
   (void)vsl;
 
-  auto load_step = [&](int base, int64_t off, typename R::Raw (&kk)[U], typename R::Raw (&vv)[U]) {
+  auto load_step = [&](int base, int64_t off, typename R::Raw (&kk)[U], typename R::Raw (&vv)[U],
+                       float (&ks)[kSc], float (&vs)[kSc]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = base + u * RPW + row;
@@ -343,33 +320,36 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
       for (int j = 0; j < kSc; ++j) {
         const int t = base + (kRS ? (col >> 2) : j) * RPW + row;
         const bool ok = t < t_end;
-        ksl[j] = ok ? ksc[(int64_t)t * a.sc_st] : 0.f;
-        vsl[j] = ok ? vsc[(int64_t)t * a.sc_st] : 0.f;
+        ks[j] = ok ? ksc[(int64_t)t * a.sc_st] : 0.f;
+        vs[j] = ok ? vsc[(int64_t)t * a.sc_st] : 0.f;
       }
     }
   };
-  // One head per workgroup (MHA, bf16): the rows of the next step are loaded
-  // before the math of this one, two steps in flight per wave (ragged MHA
-  // B = 64: 688 -> 680 us). With more heads per workgroup it measured slower.
-  constexpr bool kPrefetch = sizeof(T) == 2 && GH == 1;
+  // The rows of the next step are loaded before the math of this one, two
+  // steps in flight per wave: for one bf16 head per workgroup (MHA; ragged
+  // B = 64: 688 -> 680 us; with more heads it measured slower) and for fp8
+  // caches, whose steps carry half the bytes, so that a wave's load latency
+  // is no longer hidden by the other waves alone (config 2 shape: 66 -> US us).
+  constexpr bool kPrefetch = (sizeof(T) == 2 && GH == 1) || kFp8;
   constexpr int kStep = kWaves * TOK;
   typename R::Raw kw[U], vw[U];
   // page_n: table entry of the next step whose rows are loaded
   int page_n = step_page(t_begin + wave * TOK);
   if constexpr (kPrefetch) {
-    load_step(t_begin + wave * TOK, step_off(t_begin + wave * TOK, page_n), kw, vw);
+    load_step(t_begin + wave * TOK, step_off(t_begin + wave * TOK, page_n), kw, vw, ksl, vsl);
     page_n = step_page(t_begin + wave * TOK + kStep);
   }
   for (int base = t_begin + wave * TOK; base < t_end; base += kStep) {
     typename R::Raw kn[U], vn[U];
+    float ksn[kSc], vsn[kSc];
     if constexpr (kPrefetch) {
       const int64_t off = step_off(base + kStep, page_n);
       page_n = step_page(base + 2 * kStep);
-      load_step(base + kStep, off, kn, vn);
+      load_step(base + kStep, off, kn, vn, ksn, vsn);
     } else {
       const int64_t off = step_off(base, page_n);
       page_n = step_page(base + kStep);
-      load_step(base, off, kw, vw);
+      load_step(base, off, kw, vw, ksl, vsl);
     }
     if constexpr (kRS) {
       float v[kRsN];
@@ -490,6 +470,11 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
       for (int u = 0; u < U; ++u) {
         kw[u] = kn[u];
         vw[u] = vn[u];
+      }
+#pragma unroll
+      for (int j = 0; j < kSc; ++j) {
+        ksl[j] = ksn[j];
+        vsl[j] = vsn[j];
       }
     }
   }
@@ -615,6 +600,7 @@ bool gqa_wide_supported(int dtype, int heads_per_block) {
 }
 
 hipError_t launch_gqa_decode(const GqaArgs& a, int dtype, int head_dim, hipStream_t st) {
+  if (gqa_mfma_supported(a, dtype, head_dim)) return launch_gqa_mfma(a, dtype, head_dim, st);
   if (dtype == 1) {
     if (head_dim == 128) return launch_gh<uint16_t, 128>(a, st);
     if (head_dim == 64) return launch_gh<uint16_t, 64>(a, st);

@@ -83,12 +83,6 @@ __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)
 // moving LDS accesses across it.
 __device__ __forceinline__ void tile_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Wait until at most N vector-memory operations of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N <= 63, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
   return pack_bf16x2(lo, hi);
@@ -103,37 +97,6 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
 // transposing 8-byte reads of 4 consecutive rows x 32 bytes (the O^T operand).
 // Rows r and r + 16 share f, so one lane offset serves both halves of a tile.
 __device__ __forceinline__ int row_swizzle(int row) { return row & 7; }
-
-// Buffer resource for raw (unswizzled, stride 0) byte addressing: loads past
-// num_records bytes return zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_raw_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// One wave-wide 1 KiB copy HBM -> LDS (buffer_load_dwordx4 ... lds): lane l
-// reads 16 bytes at rsrc base + voffset and writes them at LDS byte address
-// lds_addr + 16 l (lds_addr is wave-uniform). Written in asm so that the compiler does not track
-// the copy: tracked, every LDS read after it waits for all outstanding copies
-// (vmcnt(0)), because the compiler cannot tell which LDS bytes a copy writes.
-// Completion is waited for explicitly with wait_vm<N>() instead. The asm has
-// no output register (the data goes to LDS); M0, which holds the LDS address,
-// is saved and restored around it. The cache rows are read once, so the copy
-// is non-temporal (`nt`): measured 1.7% faster for the attention kernel, which
-// runs at the board's power limit, where moving the cache in from HBM takes
-// about a quarter of its time.
-__device__ __forceinline__ void buffer_load_to_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset,
-                                                     uint32_t lds_addr) {
-  uint32_t saved_m0;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen nt lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved_m0)
-      : "v"(voffset), "s"(rsrc), "s"(lds_addr)
-      : "memory");
-}
 
 // Two block-table entries of a paged pool, read with scalar loads that are
 // issued together and waited for once, inside this block (so no load is left

@@ -10,7 +10,8 @@ import torch
 
 import decode_attention_kv_bf16_amd as da
 import workloads as W
-from gpu_util import announce, assert_parity, bf16_tensor, f32_tensor, gqa_to_device
+from gpu_util import (announce, assert_parity, bf16_tensor, bf16_weight_bound, f32_tensor,
+                      gqa_to_device)
 from oracle.attention import combine_ref, gqa_decode_ref
 
 pytestmark = pytest.mark.gpu
@@ -28,6 +29,17 @@ def oracle_rows(inp, seqs):
     k = conv(inp.k[seqs, :Lm])
     v = conv(inp.v[seqs, :Lm])
     return gqa_decode_ref(q, k, v, inp.seq_lens[seqs], inp.scale)
+
+
+def weight_bound(inp, seqs, ro, rl):
+    """Per-row bound for kernels that round the softmax weights to bf16 for
+    the value product on the matrix cores (bf16 caches)."""
+    conv = (lambda a: W.bf16_to_f32(a).astype(np.float64)) if inp.dtype == "bf16" else \
+        (lambda a: a.astype(np.float64))
+    seqs = list(seqs)
+    Lm = int(max(1, inp.seq_lens[seqs].max()))
+    return bf16_weight_bound(conv(inp.q[seqs]), conv(inp.k[seqs, :Lm]), conv(inp.v[seqs, :Lm]),
+                             inp.seq_lens[seqs], inp.scale, ro, rl)
 
 
 def run(inp, num_splits=0, seq_lens=True):
@@ -53,7 +65,8 @@ def test_config2_reduced_batch_all_rows():
     out, lse = run(inp)
     ro, rl = oracle_rows(inp, range(4))
     assert_parity(out, lse, ro, rl, what="config2 B4")
-    assert_parity(out, lse, ro, rl, out_rtol=1e-4, lse_atol=1e-4, what="config2 B4 tight")
+    assert_parity(out, lse, ro, rl, out_rtol=weight_bound(inp, range(4), ro, rl), lse_atol=1e-4,
+                  what="config2 B4 tight")
 
 
 def test_config2_full_size_sampled():
@@ -119,7 +132,8 @@ def test_split_count_invariance(splits):
     out, lse = run(inp, num_splits=splits)
     ro, rl = oracle_rows(inp, range(3))
     assert_parity(out, lse, ro, rl, what=f"S={splits}")
-    assert_parity(out, lse, ro, rl, out_rtol=1e-4, lse_atol=1e-4, what=f"S={splits} tight")
+    assert_parity(out, lse, ro, rl, out_rtol=weight_bound(inp, range(3), ro, rl), lse_atol=1e-4,
+                  what=f"S={splits} tight")
     # same split count: bitwise reproducible (no float atomics)
     out2, lse2 = run(inp, num_splits=splits)
     assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
@@ -141,7 +155,9 @@ def test_head_mapping_one_hot(Hq, Hkv):
     exp = np.zeros((Hq, D))
     for h in range(Hq):
         exp[h, h // g] = 1.0
-    np.testing.assert_allclose(out.cpu().numpy(), np.broadcast_to(exp, (B, Hq, D)), atol=1e-5)
+    # the weights enter the value product in bf16 (relative error <= 2^-8
+    # each): the weights of a one-hot column sum to 1 within 2^-8
+    np.testing.assert_allclose(out.cpu().numpy(), np.broadcast_to(exp, (B, Hq, D)), atol=2.0 ** -8 + 1e-5)
 
 
 def test_strided_query_and_no_seq_lens():
