@@ -8,8 +8,9 @@ One step is one pass of the whole hot path on synthetic inputs:
     [64, 4096, 576] bf16, W_UK / W_UV [128, 512, 128] (query absorption,
     split-KV latent attention, merge + W_UV projection).
 Other workloads (--workload): each path alone, long-context MLA, ragged
-MHA, and GQA / MLA over paged caches (pools of 16-row pages in a seeded
-random physical order, read through a block table).
+MHA, GQA / MLA over paged caches (pools of 16-row pages in a seeded random
+physical order, read through a block table), and GQA over an FP8 (E4M3)
+cache with one fp32 scale per (token, KV head) for K and for V.
 Inputs are resident in HBM before timing starts. The default warm-up (200
 steps, about 40 ms) outlasts the board's power-management transient: in a
 kernel trace of this step, the first few milliseconds of back-to-back steps
@@ -274,6 +275,41 @@ def setup_mla_paged(cfg):
     return calls, alg, info, (inp, dict(pool=pool_h, table=table_h))
 
 
+def setup_gqa_fp8(cfg):
+    """The GQA workload of `cfg` with K and V in E4M3 and one fp32 scale per
+    (token, KV head) for each."""
+    import torch
+    import workloads as W
+    import decode_attention_kv_bf16_amd as da
+    inp = W.make_gqa_fp8_config(cfg)
+    q = to_dev_bf16(inp.q)
+    dev = lambda a: torch.from_numpy(a).cuda()
+    # scales token-major [B, L, Hkv] (a KV head's scales 32 bytes apart): in
+    # one process this layout measured 57.4 us per call against 68.4 us for
+    # head-major scales, whose reads are contiguous (and 1.2x fewer bytes)
+    k0, v0, ks, vs = dev(inp.k), dev(inp.v), dev(inp.k_scale), dev(inp.v_scale)
+    sl = torch.from_numpy(inp.seq_lens).cuda()
+    fp = k0.numel() * 2
+    n_copies = max(1, math.ceil(MALL_GUARD_BYTES / fp)) if fp < MALL_GUARD_BYTES else 1
+    copies = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(n_copies - 1)]
+    B, Hq, D = q.shape
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    calls = []
+    for kk, vv in copies:
+        def call(kk=kk, vv=vv):
+            da.gqa_decode_fp8(q, kk, vv, ks, vs, sl, inp.scale, out=out, lse=lse)
+        calls.append([("gqa_decode_fp8", call)])
+    alg = gqa_alg(B, Hq, inp.k.shape[2], D, int(inp.seq_lens.sum()), elem=1)
+    scale_bytes = 2 * int(inp.seq_lens.sum()) * inp.k.shape[2] * 4
+    alg["cache"] += scale_bytes
+    alg["total"] += scale_bytes
+    info = dict(batch=B, q_heads=Hq, kv_heads=int(inp.k.shape[2]), head_dim=D,
+                seq_len=int(inp.seq_lens.max()), cache="e4m3 + fp32 scale per (token, KV head)",
+                cache_copies=len(copies))
+    return calls, alg, info, inp
+
+
 def measured_traffic(name):
     """HBM bytes per launch from the committed rocprofv3 counter runs
     (profiles/hbm_traffic.json), if they were taken on the current kernel
@@ -308,6 +344,8 @@ def run_gpu(args):
         plans.append(("gqa-paged", setup_gqa_paged(2)))
     if args.workload == "mla-paged":
         plans.append(("mla-paged", setup_mla_paged(3)))
+    if args.workload == "gqa-fp8":
+        plans.append(("gqa-fp8", setup_gqa_fp8(2)))
     n_rot = max(len(p[1][0]) for p in plans)
 
     def step_calls(i):
@@ -429,7 +467,8 @@ def workload_name(w):
             "mla-long": "deepseek-v3-mla-longctx-b4-l16k-32k",
             "gqa-ragged": "llama2-7b-mha-ragged-b64-l1-8192",
             "gqa-paged": "llama3-8b-gqa-b32-l4096-paged16",
-            "mla-paged": "deepseek-v3-mla-b64-l4096-paged16"}[w]
+            "mla-paged": "deepseek-v3-mla-b64-l4096-paged16",
+            "gqa-fp8": "llama3-8b-gqa-b32-l4096-fp8e4m3"}[w]
 
 
 # ----------------------------------------------------------------------------
@@ -439,6 +478,7 @@ def workload_name(w):
 def cpu_baseline(plans, budget_s):
     from oracle.attention import (gqa_decode_paged_ref, gqa_decode_ref, mla_absorbed_paged_ref,
                                   mla_absorbed_ref)
+    from oracle.fp8 import gqa_decode_fp8_ref
     import workloads as W
     try:
         from threadpoolctl import threadpool_info
@@ -478,6 +518,15 @@ def cpu_baseline(plans, budget_s):
                 mla_absorbed_paged_ref(*args)
                 dt = time.perf_counter() - t
                 a1 = mla_alg(1, inp.q_nope.shape[1], L)
+            elif kind == "gqa-fp8":
+                L = int(inp.seq_lens[b])
+                args = (W.bf16_to_f32(inp.q[b:b + 1]).astype(np.float64), inp.k[b:b + 1, :L],
+                        inp.v[b:b + 1, :L], inp.k_scale[b:b + 1, :L], inp.v_scale[b:b + 1, :L],
+                        inp.seq_lens[b:b + 1], inp.scale)
+                t = time.perf_counter()
+                gqa_decode_fp8_ref(*args)
+                dt = time.perf_counter() - t
+                a1 = gqa_alg(1, inp.q.shape[1], inp.k.shape[2], inp.q.shape[2], L, elem=1)
             elif kind == "gqa":
                 f = (lambda a: W.bf16_to_f32(a).astype(np.float64))
                 L = int(inp.seq_lens[b])
@@ -513,7 +562,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="step",
                     choices=["step", "gqa", "mla", "mla-long", "gqa-ragged", "gqa-paged",
-                             "mla-paged"])
+                             "mla-paged", "gqa-fp8"])
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle time for the CPU baseline (0 disables)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,

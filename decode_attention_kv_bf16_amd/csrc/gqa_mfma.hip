@@ -87,6 +87,8 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_mfma_kernel(GqaArgs a) {
   constexpr int kScaleB = kFp8 ? 512 : 0;  // fp8: 64 key scales, then 64 value scales (32 used)
   constexpr int kSlotB = 2 * kPartB + kScaleB;   // [K | V | scales] of one step
   constexpr int kOps = 2 * kCopies + (kFp8 ? 2 : 0);   // vector-memory operations per step
+                                                         // (per-step scale copies are issued
+                                                         // even when skipped, see issue_step)
   static_assert((kSlots - 1) * kOps <= 63, "waits fit the vmcnt range");
   constexpr int kThreads = kWaves * 64;
   constexpr int kLdsB = kWaves * kSlots * kSlotB;
@@ -143,18 +145,14 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_mfma_kernel(GqaArgs a) {
 
   const int64_t pitch = a.kv_st * kEsz;   // bytes from one token's row to the next
   // Paged pools (arganzheng.life section 6.1; bf16): a step of 16 tokens
-  // starts on a multiple of 16 and lies in one page of >= 16 rows, found in
-  // the block table with one scalar load when the step is issued.
+  // starts on a multiple of 16 and lies in one page of >= 16 rows. Lane j
+  // holds the table entry of this wave's step 64 c + j (c = step / 64),
+  // loaded 64 steps at a time, so a step's page is a register read.
   const bool paged = a.page_shift > 0;
   const int64_t tab0 = (int64_t)b * a.max_blocks;
   const int64_t kv_b = paged ? 0 : (int64_t)b * a.kv_sb;
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + (kv_b + kvh * a.kv_sh) * kEsz;
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v) + (kv_b + kvh * a.kv_sh) * kEsz;
-  auto row0 = [&](int t0) -> int64_t {
-    if (!paged) return (int64_t)t0 * pitch;
-    const int64_t page = table_entry(a.block_table, tab0 + (t0 >> a.page_shift));
-    return page * a.page_stride * kEsz + (int64_t)(t0 & ((1 << a.page_shift) - 1)) * pitch;
-  };
   const float* ksc = kFp8 ? a.k_scale + b * a.sc_sb + kvh * a.sc_sh : nullptr;
   const float* vsc = kFp8 ? a.v_scale + b * a.sc_sb + kvh * a.sc_sh : nullptr;
 
@@ -177,11 +175,34 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_mfma_kernel(GqaArgs a) {
   // Every load of the loop is one of these untracked copies, kOps per step,
   // so a step's completion is an exact vmcnt wait (see wait_steps). FP8: the
   // step's 32 key and 32 value scales go to LDS too (lane l: token l % 32).
+  // (Paged pools add one vector load of table entries per 64 steps; the
+  // counter counts it as well, so it can only make a wait longer.)
   const uint32_t soff = (uint32_t)((lane & 31) * a.sc_st * 4);
-  auto issue_step = [&](int t0, int slot) {
+  // one key and one value scale for the whole split (zero token stride)
+  const float ks_fixed = kFp8 && a.sc_st == 0 ? ksc[0] : 0.f;
+  const float vs_fixed = kFp8 && a.sc_st == 0 ? vsc[0] : 0.f;
+  constexpr int kStride = kWaves * kTok;
+  const int first = t_begin + wave * kTok;
+  const int n = first < t_end ? (t_end - first + kStride - 1) / kStride : 0;
+  int pages = 0;
+  auto load_pages = [&](int i0) {   // entries of steps i0 .. i0 + 63 (a vector load)
+    const int i = i0 + lane;
+    pages = i < n ? a.block_table[tab0 + ((first + i * kStride) >> a.page_shift)] : 0;
+  };
+  if (paged) load_pages(0);
+  // byte offset of step i's first row (paged: in its page)
+  auto row0 = [&](int i) -> int64_t {
+    const int t0 = first + i * kStride;
+    if (!paged) return (int64_t)t0 * pitch;
+    if (i > 0 && (i & 63) == 0) load_pages(i);   // steps are issued in order
+    const int64_t page = __builtin_amdgcn_readlane(pages, i & 63);
+    return page * a.page_stride * kEsz + (int64_t)(t0 & ((1 << a.page_shift) - 1)) * pitch;
+  };
+  auto issue_step = [&](int i, int slot) {
+    const int t0 = first + i * kStride;
     const int valid = min(t_end - t0, kTok);   // rows past it read as zero
     const uint32_t nrec = (uint32_t)(valid * pitch);
-    const int64_t r0b = row0(t0);
+    const int64_t r0b = row0(i);
     const __amdgpu_buffer_rsrc_t kr = make_raw_rsrc(kbase + r0b, nrec);
     const __amdgpu_buffer_rsrc_t vr = make_raw_rsrc(vbase + r0b, nrec);
     const uint32_t dst = wlds_addr + slot * kSlotB;
@@ -190,9 +211,12 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_mfma_kernel(GqaArgs a) {
 #pragma unroll
     for (int k = 0; k < kCopies; ++k) buffer_load_to_lds16(vr, voff[k], dst + kPartB + k * 1024);
     if constexpr (kFp8) {
-      // the scales of tokens [0, valid): ((valid - 1) * stride + 1) floats
-      // (a zero token stride shares one scale across tokens)
-      const uint32_t srec = (uint32_t)(((valid - 1) * a.sc_st + 1) * 4);
+      // the scales of tokens [0, valid): ((valid - 1) * stride + 1) floats.
+      // With a zero token stride the scales do not change within the split:
+      // they are read once (fixed_scales), and these copies read nothing
+      // (an empty range reads as zero without a memory access), so that
+      // every step still counts kOps operations.
+      const uint32_t srec = a.sc_st == 0 ? 0u : (uint32_t)(((valid - 1) * a.sc_st + 1) * 4);
       const __amdgpu_buffer_rsrc_t ks = make_raw_rsrc(ksc + (int64_t)t0 * a.sc_st, srec);
       const __amdgpu_buffer_rsrc_t vs = make_raw_rsrc(vsc + (int64_t)t0 * a.sc_st, srec);
       buffer_load_to_lds4(ks, soff, dst + 2 * kPartB);
@@ -227,23 +251,26 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_mfma_kernel(GqaArgs a) {
 
   // This wave's steps: tokens [t_begin + (i kWaves + wave) kTok, + kTok) for
   // i < n; kSlots - 1 of them in flight ahead of the one being computed.
-  constexpr int kStride = kWaves * kTok;
-  const int first = t_begin + wave * kTok;
-  const int n = first < t_end ? (t_end - first + kStride - 1) / kStride : 0;
 #pragma unroll
   for (int i = 0; i < kSlots - 1; ++i)
-    if (i < n) issue_step(first + i * kStride, i);
+    if (i < n) issue_step(i, i);
   for (int i = 0; i < n; ++i) {
     const int t0 = first + i * kStride;
     const int slot = i % kSlots;
     // refill the buffer of step i - 1 (computed in the previous iteration)
-    if (i + kSlots - 1 < n) issue_step(t0 + (kSlots - 1) * kStride, (i + kSlots - 1) % kSlots);
+    if (i + kSlots - 1 < n) issue_step(i + kSlots - 1, (i + kSlots - 1) % kSlots);
     // step i has landed (the memory clobber keeps the LDS reads below)
     wait_steps(min(kSlots - 1, n - 1 - i));
     const LDS uint8_t* kt = wlds + slot * kSlotB;
     const LDS uint8_t* vt = kt + kPartB;
     float ksl[kFp8 ? kJ : 1], vsl[kFp8 ? kJ : 1];
-    if constexpr (kFp8) {
+    if (kFp8 && a.sc_st == 0) {
+#pragma unroll
+      for (int j = 0; j < (kFp8 ? kJ : 1); ++j) {
+        ksl[j] = ks_fixed;
+        vsl[j] = vs_fixed;
+      }
+    } else if constexpr (kFp8) {
       // scales of tokens tau(g, 0..7) = 4g..4g+3, 16+4g..16+4g+3
       const LDS uint8_t* sk = kt + 2 * kPartB;
       const u32x4_t k0 = lds_read16(sk + 16 * g), k1 = lds_read16(sk + 64 + 16 * g);

@@ -33,7 +33,9 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 # symbol. The attention kernel's last template argument is the paged flag
 # (mangled "Lb1E", demangled ", true>": paged pool).
 KERNELS = {
-    "gqa_split_pass": ("gqa_decode_kernel", (), "gqa_decode.hip"),
+    # the GQA pass runs on the matrix cores (gqa_mfma_kernel) or, for fp32
+    # and 16-wave shapes, on the vector ALUs (gqa_decode_kernel)
+    "gqa_split_pass": ("_kernel", ("gqa_decode_kernel", "gqa_mfma_kernel"), ("gqa_decode.hip", "gqa_mfma.hip")),
     "gqa_combine": ("splitkv_combine_kernel", (), "combine.hip"),
     "mla_absorb": ("mla_absorb_kernel", (), "mla_decode.hip"),
     "mla_attend_paged": ("mla_attend_kernel", ("Lb1E", ", true>"), "mla_decode.hip"),
@@ -42,15 +44,19 @@ KERNELS = {
 }
 # names under which a workload's launches of a kernel are recorded (GQA over
 # paged pools runs the GQA kernel as one library call, gqa_decode_paged)
-ALIASES = {"gqa_decode_paged": "gqa_split_pass"}
+ALIASES = {"gqa_decode_paged": "gqa_split_pass", "gqa_decode_fp8": "gqa_split_pass"}
 
 
 def source_sha256(short: str):
     short = ALIASES.get(short, short)
     if short not in KERNELS:
         return None
-    with open(os.path.join(CSRC, KERNELS[short][2]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    files = KERNELS[short][2]
+    h = hashlib.sha256()
+    for name in (files if isinstance(files, tuple) else (files,)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def short_name(symbol: str):

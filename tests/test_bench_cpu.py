@@ -21,7 +21,7 @@ def test_more_than_one_gpu_exits_with_a_message():
 
 
 def test_every_workload_has_a_name():
-    for w in ("step", "gqa", "mla", "mla-long", "gqa-ragged", "gqa-paged", "mla-paged"):
+    for w in ("step", "gqa", "mla", "mla-long", "gqa-ragged", "gqa-paged", "mla-paged", "gqa-fp8"):
         assert bench.workload_name(w)
 
 
@@ -40,10 +40,12 @@ def test_cpu_baseline_on_contiguous_and_paged_plans():
     m = W.make_mla(2, 16, [40, 7], seed=4, max_seq_len=48)
     (kp, vp), tg = bench.paged_pools(g.seq_lens, [g.k, g.v], seed=5)
     (pool,), tm = bench.paged_pools(m.seq_lens, [m.cache], seed=6)
+    f8 = W.make_gqa_fp8(2, 8, 2, 128, [40, 9], seed=7)
     plans = [("gqa", (None, None, None, g)), ("mla", (None, None, None, m)),
+             ("gqa-fp8", (None, None, None, f8)),
              ("gqa-paged", (None, None, None, (g, dict(k_pool=kp, v_pool=vp, table=tg)))),
              ("mla-paged", (None, None, None, (m, dict(pool=pool, table=tm))))]
     res = bench.cpu_baseline(plans, budget_s=4.0)
     assert res["kind"] == "oracle" and res["value"] > 0 and res["cores"] >= 1
-    for kind in ("gqa", "mla", "gqa-paged", "mla-paged"):
+    for kind in ("gqa", "mla", "gqa-paged", "mla-paged", "gqa-fp8"):
         assert f"{kind}: 2 of 2 sequences" in res["sample"]
