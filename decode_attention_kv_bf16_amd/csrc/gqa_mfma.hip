@@ -33,6 +33,8 @@
 // FP8 codes are converted to bf16 exactly (every E4M3 value is a bf16
 // value); the per-(token, KV head) key scale multiplies the score, the value
 // scale the weight.
+#include <type_traits>
+
 #include "da_device.h"
 #include "da_internal.h"
 
@@ -224,51 +226,41 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_mfma_kernel(GqaArgs a) {
     }
   };
   // wait until step i has landed, when `later` steps were issued after it
+  // (s_waitcnt takes an immediate: one branch per possible count)
   auto wait_steps = [](int later) {
-    if constexpr (kSlots > 3) {
-      if (later >= 3) {
-        wait_vm<3 * kOps>();
-        return;
-      }
-    }
-    if constexpr (kSlots > 2) {
-      if (later == 2) {
-        wait_vm<2 * kOps>();
-        return;
-      }
-    }
-    if (later >= 1) {
-      wait_vm<kOps>();
-      return;
-    }
+    if constexpr (kSlots > 7) if (later >= 7) return wait_vm<7 * kOps>();
+    if constexpr (kSlots > 6) if (later == 6) return wait_vm<6 * kOps>();
+    if constexpr (kSlots > 5) if (later == 5) return wait_vm<5 * kOps>();
+    if constexpr (kSlots > 4) if (later == 4) return wait_vm<4 * kOps>();
+    if constexpr (kSlots > 3) if (later == 3) return wait_vm<3 * kOps>();
+    if constexpr (kSlots > 2) if (later == 2) return wait_vm<2 * kOps>();
+    if (later >= 1) return wait_vm<kOps>();
     wait_vm<0>();
   };
+  static_assert(kSlots <= 8, "wait_steps covers up to 7 later steps");
 
   f32x4_t o[kDB];
 #pragma unroll
   for (int m = 0; m < kDB; ++m) o[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_ref = kNegInf, l_part = 0.f;
 
-  // This wave's steps: tokens [t_begin + (i kWaves + wave) kTok, + kTok) for
-  // i < n; kSlots - 1 of them in flight ahead of the one being computed.
-#pragma unroll
-  for (int i = 0; i < kSlots - 1; ++i)
-    if (i < n) issue_step(i, i);
-  for (int i = 0; i < n; ++i) {
+  // ---- the pieces of a step ----
+  // front_a: scores of step i and their base-2 weights' exponents z (the
+  // contraction element j is token 4g + j for bf16, tau(g, j) for fp8)
+  struct Front {
+    float z[kJ];
+    float zmax;
+    float vsl[kFp8 ? kJ : 1];
+  };
+  auto front_a = [&](int i, Front& f) {
     const int t0 = first + i * kStride;
-    const int slot = i % kSlots;
-    // refill the buffer of step i - 1 (computed in the previous iteration)
-    if (i + kSlots - 1 < n) issue_step(i + kSlots - 1, (i + kSlots - 1) % kSlots);
-    // step i has landed (the memory clobber keeps the LDS reads below)
-    wait_steps(min(kSlots - 1, n - 1 - i));
-    const LDS uint8_t* kt = wlds + slot * kSlotB;
-    const LDS uint8_t* vt = kt + kPartB;
-    float ksl[kFp8 ? kJ : 1], vsl[kFp8 ? kJ : 1];
+    const LDS uint8_t* kt = wlds + (i % kSlots) * kSlotB;
+    float ksl[kFp8 ? kJ : 1];
     if (kFp8 && a.sc_st == 0) {
 #pragma unroll
       for (int j = 0; j < (kFp8 ? kJ : 1); ++j) {
         ksl[j] = ks_fixed;
-        vsl[j] = vs_fixed;
+        f.vsl[j] = vs_fixed;
       }
     } else if constexpr (kFp8) {
       // scales of tokens tau(g, 0..7) = 4g..4g+3, 16+4g..16+4g+3
@@ -279,14 +271,12 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_mfma_kernel(GqaArgs a) {
       for (int j = 0; j < 4; ++j) {
         ksl[j] = __uint_as_float(k0[j]);
         ksl[4 + j] = __uint_as_float(k1[j]);
-        vsl[j] = __uint_as_float(v0[j]);
-        vsl[4 + j] = __uint_as_float(v1[j]);
+        f.vsl[j] = __uint_as_float(v0[j]);
+        f.vsl[4 + j] = __uint_as_float(v1[j]);
       }
     }
     (void)ksl;
-    (void)vsl;
-
-    // scores: s[hf][e] = S^T[token 16 hf + 4 g + e][head r]
+    // s[hf][e] = S^T[token 16 hf + 4 g + e][head r]
     f32x4_t s[kHalves];
 #pragma unroll
     for (int hf = 0; hf < kHalves; ++hf) {
@@ -295,81 +285,139 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_mfma_kernel(GqaArgs a) {
       s[hf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < kKS; ++c) {
-        bf16x8_t ak;
         if constexpr (kFp8) {
           if ((c & 1) == 0) {
             const u32x4_t w = lds_read16(krow + 16 * (kchunk(c) ^ swz(R)));
-            ak = fp8x8_to_bf16(w.x, w.y);
-            s[hf] = mfma32(ak, qb[c], s[hf]);
+            s[hf] = mfma32(fp8x8_to_bf16(w.x, w.y), qb[c], s[hf]);
             s[hf] = mfma32(fp8x8_to_bf16(w.z, w.w), qb[c + 1], s[hf]);
           }
         } else {
-          ak = __builtin_bit_cast(bf16x8_t, lds_read16(krow + 16 * (kchunk(c) ^ swz(R))));
+          const bf16x8_t ak = __builtin_bit_cast(bf16x8_t, lds_read16(krow + 16 * (kchunk(c) ^ swz(R))));
           s[hf] = mfma32(ak, qb[c], s[hf]);
         }
       }
     }
-
-    // weights, contraction element j (bf16: token 4g + j; fp8: tau(g, j)),
-    // base-2 domain
-    float z[kJ];
-    float zmax = kNegInf;
+    f.zmax = kNegInf;
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
       const int tj = kFp8 ? tau(g, j) : 4 * g + j;
       float scl = a.scale_log2;
       if constexpr (kFp8) scl *= ksl[j];
-      z[j] = t0 + tj < t_end ? (j < 4 ? s[0][j] : s[kHalves - 1][j & 3]) * scl : kNegInf;
-      zmax = fmaxf(zmax, z[j]);
+      f.z[j] = t0 + tj < t_end ? (j < 4 ? s[0][j] : s[kHalves - 1][j & 3]) * scl : kNegInf;
+      f.zmax = fmaxf(f.zmax, f.z[j]);
     }
-    if (__builtin_amdgcn_ballot_w64(zmax > m_ref + kHeadroom) != 0) {
-      // a new reference for every head: the max over the head's 4 lane groups
-      float mg = fmaxf(zmax, __shfl_xor(zmax, 16));
-      mg = fmaxf(mg, __shfl_xor(mg, 32));
-      const float m_new = fmaxf(m_ref, mg);
-      const float alpha = m_ref == kNegInf ? 0.f : exp2_hw(m_ref - m_new);
+  };
+  // whether some score exceeds its head's reference by more than kHeadroom
+  auto needs_new_ref = [&](const Front& f) {
+    return __builtin_amdgcn_ballot_w64(f.zmax > m_ref + kHeadroom) != 0;
+  };
+  // a new reference for every head (the max over its 4 lane groups); the
+  // accumulators are rescaled to it
+  auto new_ref = [&](const Front& f) {
+    float mg = fmaxf(f.zmax, __shfl_xor(f.zmax, 16));
+    mg = fmaxf(mg, __shfl_xor(mg, 32));
+    const float m_new = fmaxf(m_ref, mg);
+    const float alpha = m_ref == kNegInf ? 0.f : exp2_hw(m_ref - m_new);
 #pragma unroll
-      for (int m = 0; m < kDB; ++m) o[m] *= alpha;
-      l_part *= alpha;
-      m_ref = m_new;
-    }
+    for (int m = 0; m < kDB; ++m) o[m] *= alpha;
+    l_part *= alpha;
+    m_ref = m_new;
+  };
+  // front_b: the weights as the B operand of the value product
+  using PB = typename std::conditional<kFp8, bf16x8_t, i16x4_t>::type;
+  auto front_b = [&](const Front& f) -> PB {
     const float mu = m_ref == kNegInf ? 0.f : m_ref;
     float p[kJ];
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
-      p[j] = exp2_hw(z[j] - mu);
+      p[j] = exp2_hw(f.z[j] - mu);
       l_part += p[j];
-      if constexpr (kFp8) p[j] *= vsl[j];   // p is 0 for masked tokens
+      if constexpr (kFp8) p[j] *= f.vsl[j];   // p is 0 for masked tokens
     }
-
-    // O^T[d, h] += sum_t V[t, d] P[h, t], d-block m: d = 16 m + lane column
     if constexpr (kFp8) {
       uint4 pw;
       pw.x = pack_bf16x2(p[0], p[1]);
       pw.y = pack_bf16x2(p[2], p[3]);
       pw.z = pack_bf16x2(p[4], p[5]);
       pw.w = pack_bf16x2(p[6], p[7]);
-      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
-      const int R = 8 * g + (r >> 1);
-#pragma unroll
-      for (int m = 0; m < kDB; ++m) {
-        const i32x2_t c8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (LDS i32x2_t*)(vt + R * kRowB + 16 * (m ^ swz(R)) + 8 * (r & 1)));
-        o[m] = mfma32(fp8x8_to_bf16((uint32_t)c8.x, (uint32_t)c8.y), pb, o[m]);
-      }
+      return __builtin_bit_cast(bf16x8_t, pw);
     } else {
       const uint32_t pw[2] = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-      const i16x4_t pb = __builtin_bit_cast(i16x4_t, pw);
-      const int R = 4 * g + (r >> 2);
+      return __builtin_bit_cast(i16x4_t, pw);
+    }
+  };
+  // back: O^T[d, h] += sum_t V[t, d] P[h, t]; d-block m: d = 16 m + lane
+  // column. The transposed reads do not depend on the weights.
+  struct VOps {
+    typename std::conditional<kFp8, i32x2_t, i16x4_t>::type av[kDB];
+  };
+  auto back_reads = [&](int i, VOps& v) {
+    const LDS uint8_t* vt = wlds + (i % kSlots) * kSlotB + kPartB;
 #pragma unroll
-      for (int m = 0; m < kDB; ++m) {
+    for (int m = 0; m < kDB; ++m) {
+      if constexpr (kFp8) {
+        const int R = 8 * g + (r >> 1);
+        v.av[m] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (LDS i32x2_t*)(vt + R * kRowB + 16 * (m ^ swz(R)) + 8 * (r & 1)));
+      } else {
         // 4 bf16 at d = 16 m + 4 (r % 4): byte 32 m + 8 (r % 4) of the row
+        const int R = 4 * g + (r >> 2);
         const int lc = 2 * m + ((r & 3) >> 1);
-        const i16x4_t av = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        v.av[m] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (LDS i16x4_t*)(vt + R * kRowB + 16 * (lc ^ swz(R)) + 8 * (r & 1)));
-        o[m] = mfma16(av, pb, o[m]);
       }
     }
+  };
+  auto back_mfma = [&](const VOps& v, const PB& pb) {
+#pragma unroll
+    for (int m = 0; m < kDB; ++m) {
+      if constexpr (kFp8) {
+        o[m] = mfma32(fp8x8_to_bf16((uint32_t)v.av[m].x, (uint32_t)v.av[m].y), pb, o[m]);
+      } else {
+        o[m] = mfma16(v.av[m], pb, o[m]);
+      }
+    }
+  };
+
+  // This wave's steps: tokens [t_begin + (i kWaves + wave) kTok, + kTok) for
+  // i < n, kSlots - 1 issued ahead. Software pipeline: while the matrix
+  // cores run the value product of step i, the wave computes the scores and
+  // weights of step i + 1 (one wave per SIMD cannot hide a step's chain of
+  // dependent operations otherwise). Only when step i + 1 needs a new
+  // reference (the accumulators are rescaled) is the value product of step i
+  // run first, since its weights are relative to the old one.
+#pragma unroll
+  for (int i = 0; i < kSlots - 1; ++i)
+    if (i < n) issue_step(i, i);
+  PB pb_cur{};
+  if (n > 0) {
+    wait_steps(min(kSlots - 2, n - 1));   // step 0 has landed
+    Front f;
+    front_a(0, f);
+    if (needs_new_ref(f)) new_ref(f);
+    pb_cur = front_b(f);
+  }
+  for (int i = 0; i < n; ++i) {
+    // refill the buffer of step i - 1 (finished in the previous iteration)
+    if (i + kSlots - 1 < n) issue_step(i + kSlots - 1, (i + kSlots - 1) % kSlots);
+    VOps v;
+    back_reads(i, v);
+    bool done = false;
+    PB pb_next{};
+    if (i + 1 < n) {
+      // step i + 1 has landed (the memory clobber keeps its LDS reads below)
+      wait_steps(min(kSlots - 2, n - 2 - i));
+      Front f;
+      front_a(i + 1, f);
+      if (needs_new_ref(f)) {
+        back_mfma(v, pb_cur);
+        done = true;
+        new_ref(f);
+      }
+      pb_next = front_b(f);
+    }
+    if (!done) back_mfma(v, pb_cur);
+    pb_cur = pb_next;
   }
 
   // Per head: the normaliser over the 4 lane groups, then the waves merged
