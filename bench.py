@@ -310,6 +310,62 @@ def setup_gqa_fp8(cfg):
     return calls, alg, info, inp
 
 
+def replayed(wrapper_call):
+    """Run a binding call once and return a function that repeats its C call
+    with the same arguments. The append kernels take a few microseconds,
+    less than the Python wrapper's argument checks, so the step replays the
+    recorded call (the same launch) to keep the GPU, not Python, the limit."""
+    import decode_attention_kv_bf16_amd as da
+    with da.recorded_calls() as rec:
+        wrapper_call()
+    (fn, cargs), = rec
+
+    def call():
+        st = fn(*cargs)
+        if st != 0:
+            raise RuntimeError(f"{fn.__name__} failed with status {st}")
+    return call
+
+
+def setup_append(kind):
+    """One token appended per sequence with RoPE: the GQA cache of config 2
+    (B 32, Hq 32, Hkv 8, D 128, L 4096) or the MLA cache of config 3 (B 64,
+    H 128, rows of 576, L 4096), at seeded positions."""
+    import torch
+    import workloads as W
+    import decode_attention_kv_bf16_amd as da
+    if kind == "gqa-append":
+        B, Hq, Hkv, D, L = 32, 32, 8, 128, 4096
+        inp = W.make_gqa_append(B, Hq, Hkv, D, L, cfg=2)
+        q, kn, vn = (to_dev_bf16(x) for x in (inp.q, inp.k_new, inp.v_new))
+        kc = torch.zeros((B, L, Hkv, D), dtype=torch.bfloat16, device="cuda")
+        vc = torch.zeros_like(kc)
+        q_out = torch.empty_like(q)
+        pos = torch.from_numpy(inp.positions).cuda()
+
+        call = replayed(lambda: da.gqa_append_rope(q, kn, vn, pos, kc, vc, q_out=q_out))
+        # bytes: q read and written, k and v rows read and written, positions;
+        # FLOPs: 6 per rotated pair (q heads and the key heads)
+        alg = dict(cache=2 * (2 * B * Hkv * D * 2), q=2 * B * Hq * D * 2, out=0,
+                   flops=6 * B * (Hq + Hkv) * (D // 2))
+        alg["total"] = alg["cache"] + alg["q"] + 4 * B
+        info = dict(batch=B, q_heads=Hq, kv_heads=Hkv, head_dim=D, max_seq_len=L, rotary_dim=D,
+                    rope="half pairs, base 10000")
+        return [[("gqa_append_rope", call)]], alg, info, inp
+    B, H, L = 64, 128, 4096
+    inp = W.make_mla_append(B, H, L, cfg=3)
+    qr, kvn = to_dev_bf16(inp.q), to_dev_bf16(inp.k_new)
+    cache = torch.zeros((B, L, 576), dtype=torch.bfloat16, device="cuda")
+    q_out = torch.empty_like(qr)
+    pos = torch.from_numpy(inp.positions).cuda()
+
+    call = replayed(lambda: da.mla_append_rope(qr, kvn, pos, cache, q_rope_out=q_out))
+    alg = dict(cache=2 * B * 576 * 2, q=2 * B * H * 64 * 2, out=0, flops=6 * B * (H + 1) * 32)
+    alg["total"] = alg["cache"] + alg["q"] + 4 * B
+    info = dict(batch=B, heads=H, row=576, max_seq_len=L, rotary_dim=64, rope="half pairs, base 10000")
+    return [[("mla_append_rope", call)]], alg, info, inp
+
+
 def measured_traffic(name):
     """HBM bytes per launch from the committed rocprofv3 counter runs
     (profiles/hbm_traffic.json), if they were taken on the current kernel
@@ -346,6 +402,9 @@ def run_gpu(args):
         plans.append(("mla-paged", setup_mla_paged(3)))
     if args.workload == "gqa-fp8":
         plans.append(("gqa-fp8", setup_gqa_fp8(2)))
+    if args.workload == "append":
+        plans.append(("gqa-append", setup_append("gqa-append")))
+        plans.append(("mla-append", setup_append("mla-append")))
     n_rot = max(len(p[1][0]) for p in plans)
 
     def step_calls(i):
@@ -400,8 +459,27 @@ def run_gpu(args):
 
     # Roofline pass: K more steps in which events on the launch stream bracket
     # every launch of the dominant kernel; its average duration.
+    # When a step takes the GPU less time than Python needs to issue it (the
+    # few-microsecond append kernels), an event pair would time the issue gap,
+    # not the kernel. Then the pass starts behind a GPU busy-wait (a spin
+    # kernel of known length) long enough for every launch and event of the
+    # pass to be queued first, so the kernels run back to back as in a loop
+    # that is not limited by its host.
     dom_ev = [(hev.create(), hev.create()) for _ in range(args.steps)]
     base += args.steps
+    probe_step_ms = sum(per_kernel.values())
+    if probe_step_ms < 0.03:
+        cal = (hev.create(), hev.create())
+        hev.record(cal[0], stream)
+        torch.cuda._sleep(1_000_000)
+        hev.record(cal[1], stream)
+        torch.cuda.synchronize()
+        ms_per_mcycle = max(hev.elapsed_ms(*cal), 1e-3)
+        wanted_ms = 0.05 * args.steps * len(names) + 5.0     # generous: 50 us of issue per launch
+        torch.cuda._sleep(int(wanted_ms / ms_per_mcycle * 1_000_000))
+        roofline_queued = True
+    else:
+        roofline_queued = False
     for i in range(args.steps):
         for j, (_, fn) in enumerate(step_calls(base + i)):
             if j == dom_idx:
@@ -432,7 +510,8 @@ def run_gpu(args):
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(dom),
-                "alg_bytes_per_launch": int(dom_bytes), "avg_launch_us": round(dom_ms * 1e3, 2)}
+                "alg_bytes_per_launch": int(dom_bytes), "avg_launch_us": round(dom_ms * 1e3, 2),
+                "launches_queued_behind_spin": roofline_queued}
 
     paths = {}
     for kind, (calls, alg, info, _) in plans:
@@ -468,7 +547,8 @@ def workload_name(w):
             "gqa-ragged": "llama2-7b-mha-ragged-b64-l1-8192",
             "gqa-paged": "llama3-8b-gqa-b32-l4096-paged16",
             "mla-paged": "deepseek-v3-mla-b64-l4096-paged16",
-            "gqa-fp8": "llama3-8b-gqa-b32-l4096-fp8e4m3"}[w]
+            "gqa-fp8": "llama3-8b-gqa-b32-l4096-fp8e4m3",
+            "append": "cache append + rope: llama3-8b-gqa-b32-l4096 + deepseek-v3-mla-b64-l4096"}[w]
 
 
 # ----------------------------------------------------------------------------
@@ -479,6 +559,7 @@ def cpu_baseline(plans, budget_s):
     from oracle.attention import (gqa_decode_paged_ref, gqa_decode_ref, mla_absorbed_paged_ref,
                                   mla_absorbed_ref)
     from oracle.fp8 import gqa_decode_fp8_ref
+    from oracle.rope import gqa_append_rope_ref, mla_append_rope_ref
     import workloads as W
     try:
         from threadpoolctl import threadpool_info
@@ -492,7 +573,7 @@ def cpu_baseline(plans, budget_s):
         if kind.endswith("-paged"):
             inp, pools = inp
         t_kind, n = 0.0, 0
-        B = len(inp.seq_lens)
+        B = len(inp.positions) if kind.endswith("-append") else len(inp.seq_lens)
         while t_kind < per_kind_budget and n < B:
             b = n
             if kind == "gqa-paged":
@@ -527,6 +608,25 @@ def cpu_baseline(plans, budget_s):
                 gqa_decode_fp8_ref(*args)
                 dt = time.perf_counter() - t
                 a1 = gqa_alg(1, inp.q.shape[1], inp.k.shape[2], inp.q.shape[2], L, elem=1)
+            elif kind in ("gqa-append", "mla-append"):
+                # one sequence per call into a one-page pool (page size 16):
+                # the same rotation and row write, without copying a whole cache
+                tab = np.zeros((1, -(-4096 // 16)), np.int32)
+                if kind == "gqa-append":
+                    Hkv, D = inp.k_new.shape[1], inp.k_new.shape[2]
+                    pool = np.zeros((1, 16, Hkv, D))
+                    args = (inp.f64("q")[b:b + 1], inp.f64("k_new")[b:b + 1], inp.f64("v_new")[b:b + 1],
+                            inp.positions[b:b + 1], pool, pool, 4096, D, 0)
+                    t = time.perf_counter()
+                    gqa_append_rope_ref(*args, block_table=tab, page_size=16)
+                else:
+                    pool = np.zeros((1, 16, 576))
+                    args = (inp.f64("q")[b:b + 1], inp.f64("k_new")[b:b + 1], inp.positions[b:b + 1],
+                            pool, 4096, 64, 0)
+                    t = time.perf_counter()
+                    mla_append_rope_ref(*args, block_table=tab, page_size=16)
+                dt = time.perf_counter() - t
+                a1 = dict(total=alg["total"] // B)
             elif kind == "gqa":
                 f = (lambda a: W.bf16_to_f32(a).astype(np.float64))
                 L = int(inp.seq_lens[b])
@@ -562,7 +662,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="step",
                     choices=["step", "gqa", "mla", "mla-long", "gqa-ragged", "gqa-paged",
-                             "mla-paged", "gqa-fp8"])
+                             "mla-paged", "gqa-fp8", "append"])
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle time for the CPU baseline (0 disables)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,

@@ -14,6 +14,8 @@ raises.
     out, lse = gqa_decode_fp8(q, k_codes, v_codes, k_scale, v_scale, seq_lens)
     out, lse = mla_decode_absorbed_paged(q_nope, q_rope, cache_pool, block_table, page_size,
                                          seq_lens, w_uk, w_uv)
+    q_rot = gqa_append_rope(q, k_new, v_new, positions, k_cache, v_cache)
+    q_rope_rot = mla_append_rope(q_rope, kv_new, positions, kv_cache)
 """
 from __future__ import annotations
 
@@ -86,6 +88,20 @@ class KvScales(ctypes.Structure):
     ]
 
 
+ROPE_STYLES = {"half": 0, "interleaved": 1}
+
+
+class Append(ctypes.Structure):
+    _fields_ = [
+        ("rotary_dim", ctypes.c_int32),
+        ("rope_style", ctypes.c_int32),
+        ("rope_base", ctypes.c_double),
+        ("inv_freq", ctypes.c_void_p),
+        ("new_stride_b", ctypes.c_int64),
+        ("new_stride_h", ctypes.c_int64),
+    ]
+
+
 _vp = ctypes.c_void_p
 _GQA_P = ctypes.POINTER(GqaParams)
 _MLA_P = ctypes.POINTER(MlaParams)
@@ -116,6 +132,10 @@ _SIGNATURES = {
                                                       _vp]),
     "da_gqa_decode_fp8": (ctypes.c_int, [_GQA_P, ctypes.POINTER(KvScales), _vp, _vp, _vp, _vp, _vp,
                                          _vp, _vp, ctypes.c_size_t, _vp]),
+    "da_gqa_append_rope": (ctypes.c_int, [_GQA_P, ctypes.POINTER(Append), _PAGED_P, _vp, _vp, _vp,
+                                          _vp, _vp, _vp, _vp, _vp]),
+    "da_mla_append_rope": (ctypes.c_int, [_MLA_P, ctypes.POINTER(Append), _PAGED_P, _vp, _vp, _vp,
+                                          _vp, _vp, _vp]),
     "da_splitkv_combine": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]),
     "da_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -124,6 +144,7 @@ _SIGNATURES = {
     "da_mla_params_size": (ctypes.c_size_t, []),
     "da_paged_kv_size": (ctypes.c_size_t, []),
     "da_kv_scales_size": (ctypes.c_size_t, []),
+    "da_append_size": (ctypes.c_size_t, []),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -149,10 +170,41 @@ def lib() -> ctypes.CDLL:
     if L.da_gqa_params_size() != ctypes.sizeof(GqaParams) or \
             L.da_mla_params_size() != ctypes.sizeof(MlaParams) or \
             L.da_paged_kv_size() != ctypes.sizeof(PagedKv) or \
-            L.da_kv_scales_size() != ctypes.sizeof(KvScales):
+            L.da_kv_scales_size() != ctypes.sizeof(KvScales) or \
+            L.da_append_size() != ctypes.sizeof(Append):
         raise RuntimeError("libdecode_attn.so parameter structs do not match this binding")
     _lib = L
     return L
+
+
+_recorder: Optional[list] = None
+
+
+def _call(name: str, *args) -> int:
+    """Call a library entry point; inside recorded_calls() also record it."""
+    fn = getattr(lib(), name)
+    if _recorder is not None:
+        _recorder.append((fn, args))
+    return fn(*args)
+
+
+class recorded_calls:
+    """Records every library call made by the wrappers inside the block as
+    (C function, ctypes arguments). Calling fn(*args) later repeats exactly
+    that call (same buffers, parameters and stream) without the wrapper's
+    Python work, which matters for kernels that take a few microseconds. The
+    tensors the call used must stay alive for as long as it is replayed."""
+
+    def __enter__(self):
+        global _recorder
+        self.calls = []
+        _recorder = self.calls
+        return self.calls
+
+    def __exit__(self, *exc):
+        global _recorder
+        _recorder = None
+        return False
 
 
 def loaded_library_path() -> Optional[str]:
@@ -618,3 +670,126 @@ __all__ = ["gqa_decode", "mla_decode_absorbed", "splitkv_combine", "gqa_num_spli
            "mla_num_splits", "gqa_decode_paged", "mla_decode_absorbed_paged", "paged_kv",
            "gqa_decode_fp8", "KvScales", "lib",
            "LIB_PATH", "GqaParams", "MlaParams", "PagedKv", "DecodeAttnError", "LibraryMissing"]
+
+
+# ----------------------------------------------------------------------------
+# cache append with rotary position embedding
+# ----------------------------------------------------------------------------
+
+def _append_desc(rotary_dim: int, style: str, base: float, inv_freq: Optional[torch.Tensor],
+                 new_stride_b: int, new_stride_h: int) -> Append:
+    if style not in ROPE_STYLES:
+        raise ValueError(f"style must be one of {sorted(ROPE_STYLES)}")
+    ap = Append()
+    ap.rotary_dim, ap.rope_style, ap.rope_base = int(rotary_dim), ROPE_STYLES[style], float(base)
+    if inv_freq is not None:
+        _require_cuda("inv_freq", inv_freq)
+        if inv_freq.dtype != torch.float32 or inv_freq.shape != (rotary_dim // 2,) or \
+                not inv_freq.is_contiguous():
+            raise ValueError("inv_freq must be a contiguous float32 tensor of shape [rotary_dim / 2]")
+        ap.inv_freq = inv_freq.data_ptr()
+    ap.new_stride_b, ap.new_stride_h = int(new_stride_b), int(new_stride_h)
+    return ap
+
+
+def _check_positions(positions: torch.Tensor, B: int):
+    _require_cuda("positions", positions)
+    if positions.dtype != torch.int32 or positions.shape != (B,) or not positions.is_contiguous():
+        raise ValueError("positions must be a contiguous int32 tensor of shape [B]")
+
+
+def gqa_append_rope(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                    positions: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    rotary_dim: Optional[int] = None, style: str = "half", base: float = 10000.0,
+                    inv_freq: Optional[torch.Tensor] = None, q_out: Optional[torch.Tensor] = None,
+                    block_table: Optional[torch.Tensor] = None, page_size: int = 0,
+                    max_seq_len: Optional[int] = None) -> torch.Tensor:
+    """Append one token per sequence to a GQA cache, rotating q and the new key.
+
+    q [B, Hq, D]; k_new, v_new [B, Hkv, D] (same strides); positions [B] int32
+    (row written and rotation position; outside [0, L_max) skips the
+    sequence). k_cache, v_cache [B, L_max, Hkv, D], or paged pools
+    [num_pages, page_size, Hkv, D] with block_table [B, max_blocks] int32.
+    Returns q_out (the rotated queries; pass q_out=q to rotate in place).
+    rotary_dim defaults to D; style "half" pairs (i, i + r/2), "interleaved"
+    (2i, 2i + 1); inv_freq [r/2] float32 overrides base^(-2i/r)."""
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache),
+                    ("v_cache", v_cache)):
+        _require_cuda(name, t)
+    if len({t.dtype for t in (q, k_new, v_new, k_cache, v_cache)}) != 1:
+        raise ValueError("q, k_new, v_new and the caches must share a dtype")
+    if v_cache.shape != k_cache.shape or v_cache.stride() != k_cache.stride():
+        raise ValueError("v_cache must have the shape and strides of k_cache")
+    B, Hq, D = q.shape
+    if k_new.shape != (B, k_cache.shape[2], D) or v_new.shape != k_new.shape or \
+            v_new.stride() != k_new.stride() or k_new.stride(2) != 1:
+        raise ValueError("k_new and v_new must be [B, Hkv, D] with one stride set and a contiguous D axis")
+    _check_positions(positions, B)
+    if q_out is None:   # the C ABI writes q_out in q's strides
+        q_out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    if q_out.shape != q.shape or q_out.stride() != q.stride() or q_out.dtype != q.dtype:
+        raise ValueError("q_out must match q in shape, strides and dtype")
+    pg = None
+    if block_table is not None:
+        pg = paged_kv(block_table, page_size, k_cache)
+        if block_table.shape[0] != B:
+            raise ValueError("block_table must have one row per sequence")
+        L_max = block_table.shape[1] * page_size if max_seq_len is None else int(max_seq_len)
+        p = gqa_params(q, k_cache[:1].expand(B, -1, -1, -1), None, 0)
+        p.max_seq_len, p.kv_stride_b = L_max, 0
+    else:
+        p = gqa_params(q, k_cache, None, 0)
+    ap = _append_desc(D if rotary_dim is None else rotary_dim, style, base, inv_freq,
+                      k_new.stride(0), k_new.stride(1))
+    st = _call("da_gqa_append_rope", ctypes.byref(p), ctypes.byref(ap),
+                                  None if pg is None else ctypes.byref(pg), _ptr(q), _ptr(q_out),
+                                  _ptr(k_new), _ptr(v_new), _ptr(positions), _ptr(k_cache),
+                                  _ptr(v_cache), _stream_handle())
+    _check(st, "da_gqa_append_rope")
+    return q_out
+
+
+def mla_append_rope(q_rope: torch.Tensor, kv_new: torch.Tensor, positions: torch.Tensor,
+                    kv_cache: torch.Tensor, rotary_dim: int = 64, style: str = "half",
+                    base: float = 10000.0, inv_freq: Optional[torch.Tensor] = None,
+                    q_rope_out: Optional[torch.Tensor] = None,
+                    block_table: Optional[torch.Tensor] = None, page_size: int = 0,
+                    max_seq_len: Optional[int] = None) -> torch.Tensor:
+    """Append one latent row per sequence to an MLA cache: row positions[b]
+    becomes [kv_new[b, :512] ; RoPE(kv_new[b, 512:])], and the query rope
+    parts q_rope [B, H, 64] are rotated. kv_new [B, 576] bf16 (row-contiguous);
+    kv_cache [B, L_max, 576] bf16, or a paged pool [num_pages, page_size, 576]
+    with block_table. Returns q_rope_out (q_rope_out=q_rope rotates in place)."""
+    for name, t in (("q_rope", q_rope), ("kv_new", kv_new), ("kv_cache", kv_cache)):
+        _require_cuda(name, t)
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+    B, H, d_rope = q_rope.shape
+    if not q_rope.is_contiguous() or kv_new.dim() != 2 or kv_new.shape[0] != B or \
+            kv_new.shape[1] != kv_cache.shape[-1] or kv_new.stride(1) != 1:
+        raise ValueError("q_rope must be contiguous [B, H, 64] and kv_new [B, 576] with contiguous rows")
+    _check_positions(positions, B)
+    if q_rope_out is None:
+        q_rope_out = torch.empty_like(q_rope)
+    if q_rope_out.shape != q_rope.shape or not q_rope_out.is_contiguous() or q_rope_out.dtype != q_rope.dtype:
+        raise ValueError("q_rope_out must be a contiguous bf16 tensor shaped like q_rope")
+    d_c = kv_cache.shape[-1] - d_rope
+    # the params only carry shapes here; W_UV's shape is fixed by the format
+    fake_uv = torch.empty((H, d_c, 128), dtype=torch.bfloat16, device="meta")
+    q_nope = torch.empty((B, H, 128), dtype=torch.bfloat16, device="meta")
+    pg = None
+    if block_table is not None:
+        pg = paged_kv(block_table, page_size, kv_cache)
+        if block_table.shape[0] != B:
+            raise ValueError("block_table must have one row per sequence")
+        L_max = block_table.shape[1] * page_size if max_seq_len is None else int(max_seq_len)
+        p = _mla_paged_params(q_nope, q_rope, kv_cache, fake_uv, L_max, None, 0)
+    else:
+        p = mla_params(q_nope, kv_cache, fake_uv, q_rope, None, 0)
+    ap = _append_desc(rotary_dim, style, base, inv_freq, kv_new.stride(0), 0)
+    st = _call("da_mla_append_rope", ctypes.byref(p), ctypes.byref(ap),
+                                  None if pg is None else ctypes.byref(pg), _ptr(q_rope),
+                                  _ptr(q_rope_out), _ptr(kv_new), _ptr(positions), _ptr(kv_cache),
+                                  _stream_handle())
+    _check(st, "da_mla_append_rope")
+    return q_rope_out

@@ -409,10 +409,103 @@ da_status_t gqa_decode_impl(const da_gqa_params_t* p, const da_paged_kv_t* pages
   return from_hip(e);
 }
 
+// Append descriptor: rotary_dim a multiple of 8 in [8, max_rot], a known
+// pairing, a base > 1 or a caller table, new-row strides of 16-byte multiples.
+da_status_t check_append(const da_append_t* ap, int max_rot, int64_t esz) {
+  if (!ap) return DA_ERR_INVALID_ARGUMENT;
+  if (ap->rotary_dim < 8 || ap->rotary_dim > max_rot || ap->rotary_dim % 8 != 0)
+    return DA_ERR_INVALID_ARGUMENT;
+  if (ap->rope_style != DA_ROPE_HALF && ap->rope_style != DA_ROPE_INTERLEAVED)
+    return DA_ERR_INVALID_ARGUMENT;
+  if (ap->inv_freq) {
+    if (!aligned4(ap->inv_freq)) return DA_ERR_INVALID_ARGUMENT;
+  } else if (!(isfinite(ap->rope_base) && ap->rope_base > 1.0)) {
+    return DA_ERR_INVALID_ARGUMENT;
+  }
+  if (ap->new_stride_b < 0 || ap->new_stride_h < 0 || (ap->new_stride_b * esz) % 16 != 0 ||
+      (ap->new_stride_h * esz) % 16 != 0)
+    return DA_ERR_INVALID_ARGUMENT;
+  return DA_OK;
+}
+
+da::AppendArgs append_args(const da_append_t* ap, const da_paged_kv_t* pages,
+                           const int32_t* positions, int batch, int max_seq_len) {
+  da::AppendArgs a{};
+  a.new_sb = ap->new_stride_b;
+  a.new_sh = ap->new_stride_h;
+  a.positions = positions;
+  a.inv_freq = ap->inv_freq;
+  a.log2_base = ap->inv_freq ? 0.0 : log2(ap->rope_base);
+  a.rot = ap->rotary_dim;
+  a.style = ap->rope_style;
+  a.batch = batch;
+  a.max_seq_len = max_seq_len;
+  if (pages) set_paged(a, pages);
+  return a;
+}
+
 }  // namespace
 
 
 extern "C" {
+
+da_status_t da_gqa_append_rope(const da_gqa_params_t* p, const da_append_t* ap,
+                               const da_paged_kv_t* pages, const void* q, void* q_out,
+                               const void* k_new, const void* v_new, const int32_t* positions,
+                               void* k_cache, void* v_cache, void* hip_stream) {
+  da_status_t st = check_gqa_params(p);
+  if (st != DA_OK) return st;
+  if (p->dtype == DA_DTYPE_FP8_E4M3) return DA_ERR_UNSUPPORTED;
+  const int64_t esz = p->dtype == DA_DTYPE_BF16 ? 2 : 4;
+  st = check_append(ap, p->head_dim, esz);
+  if (st != DA_OK) return st;
+  if (pages && (st = check_paged(pages, p->max_seq_len, esz)) != DA_OK) return st;
+  st = check_ptrs16({q, q_out, k_new, v_new, k_cache, v_cache});
+  if (st != DA_OK) return st;
+  if (!positions || !aligned4(positions)) return DA_ERR_INVALID_ARGUMENT;
+  da::AppendArgs a = append_args(ap, pages, positions, p->batch, p->max_seq_len);
+  a.q = q;
+  a.q_out = q_out;
+  a.q_sb = p->q_stride_b;
+  a.q_sh = p->q_stride_h;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.c_sb = p->kv_stride_b;
+  a.c_st = p->kv_stride_t;
+  a.c_sh = p->kv_stride_h;
+  a.q_heads = p->num_q_heads;
+  a.kv_heads = p->num_kv_heads;
+  a.dim = p->head_dim;
+  return from_hip(da::launch_gqa_append_rope(a, gqa_kernel_dtype(p), static_cast<hipStream_t>(hip_stream)));
+}
+
+da_status_t da_mla_append_rope(const da_mla_params_t* p, const da_append_t* ap,
+                               const da_paged_kv_t* pages, const void* q_rope, void* q_rope_out,
+                               const void* kv_new, const int32_t* positions, void* kv_cache,
+                               void* hip_stream) {
+  da_status_t st = check_mla_params(p);
+  if (st != DA_OK) return st;
+  st = check_append(ap, kMlaRope, 2);
+  if (st != DA_OK) return st;
+  if (pages && (st = check_paged(pages, p->max_seq_len, 2)) != DA_OK) return st;
+  st = check_ptrs16({q_rope, q_rope_out, kv_new, kv_cache});
+  if (st != DA_OK) return st;
+  if (!positions || !aligned4(positions)) return DA_ERR_INVALID_ARGUMENT;
+  da::AppendArgs a = append_args(ap, pages, positions, p->batch, p->max_seq_len);
+  a.q = q_rope;
+  a.q_out = q_rope_out;
+  a.q_sb = (int64_t)p->num_heads * kMlaRope;
+  a.q_sh = kMlaRope;
+  a.k_new = kv_new;
+  a.k_cache = kv_cache;
+  a.c_sb = p->cache_stride_b;
+  a.c_st = p->cache_stride_t;
+  a.q_heads = p->num_heads;
+  a.dim = kMlaRope;
+  return from_hip(da::launch_mla_append_rope(a, static_cast<hipStream_t>(hip_stream)));
+}
 
 size_t da_gqa_decode_workspace_size(const da_gqa_params_t* p) {
   if (check_gqa_params(p) != DA_OK) return 0;
@@ -657,5 +750,6 @@ size_t da_gqa_params_size(void) { return sizeof(da_gqa_params_t); }
 size_t da_mla_params_size(void) { return sizeof(da_mla_params_t); }
 size_t da_paged_kv_size(void) { return sizeof(da_paged_kv_t); }
 size_t da_kv_scales_size(void) { return sizeof(da_kv_scales_t); }
+size_t da_append_size(void) { return sizeof(da_append_t); }
 
 }  // extern "C"

@@ -97,6 +97,31 @@ hipError_t launch_mla_attend(const MlaArgs& a, hipStream_t stream);
 hipError_t launch_mla_merge_project(const MlaArgs& a, hipStream_t stream);
 hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream);  // all three
 
+// Cache append with rotary embedding (append_rope.hip): one launch.
+struct AppendArgs {
+  const void* q;             // queries to rotate: GQA q [B, Hq, D]; MLA q_rope [B, H, 64]
+  void* q_out;               // same strides as q (may be q)
+  int64_t q_sb, q_sh;        // element strides
+  const void* k_new;         // GQA: new keys [B, Hkv, D]; MLA: new rows [B, 576] = [c_kv | k_rope]
+  const void* v_new;         // GQA: new values [B, Hkv, D]; MLA: unused
+  int64_t new_sb, new_sh;    // strides of k_new and v_new (MLA: new_sb only)
+  const int32_t* positions;  // [B]: cache row and rotation position; outside [0, max_seq_len): skipped
+  void* k_cache;             // GQA K cache / MLA latent cache
+  void* v_cache;             // GQA V cache
+  int64_t c_sb, c_st, c_sh;  // cache strides (c_sb unused when paged)
+  const int32_t* block_table;  // paged when page_shift > 0 (as GqaArgs)
+  int32_t page_shift, max_blocks;
+  int64_t page_stride;
+  const float* inv_freq;     // [r/2] or null: theta_i = 2^(-(2i/r) * log2_base)
+  double log2_base;
+  int32_t batch, q_heads, kv_heads, dim;   // dim: GQA head_dim (MLA: unused)
+  int32_t rot, style, max_seq_len;         // style 0 half, 1 interleaved
+};
+
+// dtype 0 f32, 1 bf16
+hipError_t launch_gqa_append_rope(const AppendArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_mla_append_rope(const AppendArgs& a, hipStream_t stream);
+
 // Entry i of a paged cache's block table, read through the constant address
 // space: the table is not written while a kernel runs, and so read, a load at
 // a wave-uniform index becomes a scalar load (s_load). That load is counted

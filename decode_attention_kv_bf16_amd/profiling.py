@@ -41,6 +41,8 @@ KERNELS = {
     "mla_attend_paged": ("mla_attend_kernel", ("Lb1E", ", true>"), "mla_decode.hip"),
     "mla_attend": ("mla_attend_kernel", (), "mla_decode.hip"),
     "mla_merge_project": ("mla_merge_project_kernel", (), "mla_decode.hip"),
+    "gqa_append_rope": ("gqa_append_rope_kernel", (), "append_rope.hip"),
+    "mla_append_rope": ("mla_append_rope_kernel", (), "append_rope.hip"),
 }
 # names under which a workload's launches of a kernel are recorded (GQA over
 # paged pools runs the GQA kernel as one library call, gqa_decode_paged)

@@ -339,6 +339,86 @@ DA_EXPORT da_status_t da_gqa_decode_fp8(const da_gqa_params_t* params, const da_
                                         void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* ------------------------------------------------------------------------ */
+/* Cache append with rotary position embedding                               */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The step before decode attention: each decode step computes one new k and
+ * v row per sequence and appends it to the cache, where the next steps find
+ * it ("KV Cache 如何影响了 LLM Inference", kakack.github.io, section 2.2).
+ * Keys and queries are rotated by their position first. For MLA, one
+ * projection gives 576 values per token: the first 512 are the latent c_kv
+ * (normalised by the caller), the last 64 are rotated and cached as the rope
+ * key that every head shares; each head's query rope part is rotated as well
+ * ("Attention variants and KV cache", arganzheng.life, section 4.2;
+ * jianzhnie.github.io "Multi-head Latent Attention", section 2).
+ *
+ * Rotation (the rotary form; the pages fix only that R_m depends on the
+ * position m alone and that R_m^T R_n = R_{n-m}, arganzheng.life section
+ * 4.4): the first r entries of a vector form r/2 pairs (a, b), and pair i
+ * becomes (a cos phi - b sin phi, a sin phi + b cos phi), phi = m * theta_i,
+ * theta_i = base^(-2i/r) or inv_freq[i]. Entries from r on are unchanged.
+ * Angles are formed and reduced to [-pi, pi] in double precision, their sine
+ * and cosine taken in float32, the products in float32, and each result is
+ * rounded once to the row's type.
+ *
+ * Sequence b is appended at row m = positions[b] (also its rotation
+ * position); a position outside [0, max_seq_len) skips the sequence: nothing
+ * of it is written. Every other cache row is left untouched. positions is
+ * device memory and not read on the host. New rows must not overlap the
+ * cache; q_out may be q itself (in place) but no other overlap.
+ */
+typedef enum {
+  DA_ROPE_HALF = 0,        /* pair i is entries (i, i + r/2) */
+  DA_ROPE_INTERLEAVED = 1  /* pair i is entries (2i, 2i + 1) */
+} da_rope_style_t;
+
+typedef struct {
+  int32_t rotary_dim;      /* r: a multiple of 8, 8 <= r <= head_dim (GQA) or qk_rope_dim (MLA) */
+  int32_t rope_style;      /* da_rope_style_t */
+  double rope_base;        /* theta_i = rope_base^(-2i/r); finite and > 1 unless inv_freq is set */
+  const float* inv_freq;   /* NULL, or device [r/2] float32 theta_i (for frequency-scaled variants) */
+  int64_t new_stride_b;    /* new rows: entry (b, h, d) at b*new_stride_b + h*new_stride_h + d */
+  int64_t new_stride_h;    /*   (in elements, >= 0, 16-byte multiples; MLA reads new_stride_b only) */
+} da_append_t;
+
+/* GQA append: q_out[b, h] = RoPE_m(q[b, h]); k_cache[b, m, kh] = RoPE_m(k_new[b, kh]);
+ * v_cache[b, m, kh] = v_new[b, kh], with m = positions[b].
+ *   params   as for da_gqa_decode; dtype BF16 or F32 (FP8_E4M3: UNSUPPORTED);
+ *            softmax_scale and num_splits are unused
+ *   q, q_out [B, Hq, D] in the params' q strides, dtype
+ *   k_new, v_new [B, Hkv, D] in the append strides, dtype
+ *   positions [B] int32, device
+ *   k_cache, v_cache [B, L_max, Hkv, D] in the params' kv strides, or paged
+ *            pools [num_pages, page_size, Hkv, D] when `pages` is not NULL
+ *            (rows then land on page block_table[b, m / page_size]; that
+ *            entry must be a valid page).
+ * Errors: as da_gqa_decode's checks, plus INVALID_ARGUMENT for a NULL append
+ * descriptor or buffer, a rotary_dim that is not a multiple of 8 in
+ * [8, head_dim], an unknown style, a base that is not finite and > 1 without
+ * inv_freq, a misaligned pointer or a bad stride, and the paging checks of
+ * da_gqa_decode_paged. */
+DA_EXPORT da_status_t da_gqa_append_rope(const da_gqa_params_t* params, const da_append_t* append,
+                                         const da_paged_kv_t* pages, const void* q, void* q_out,
+                                         const void* k_new, const void* v_new,
+                                         const int32_t* positions, void* k_cache, void* v_cache,
+                                         void* hip_stream);
+
+/* MLA append: q_rope_out[b, h] = RoPE_m(q_rope[b, h]); the cache row (b, m)
+ * becomes [kv_new[b, 0:512] ; RoPE_m(kv_new[b, 512:576])].
+ *   params   as for da_mla_decode_absorbed (softmax_scale and num_splits unused)
+ *   q_rope, q_rope_out [B, H, 64] bf16, contiguous
+ *   kv_new   [B, 576] bf16, row stride append->new_stride_b
+ *   kv_cache [B, L_max, 576] bf16 in the params' strides, or a paged pool
+ *            [num_pages, page_size, 576] when `pages` is not NULL.
+ * Errors: as da_gqa_append_rope, with rotary_dim in [8, 64]. */
+DA_EXPORT da_status_t da_mla_append_rope(const da_mla_params_t* params, const da_append_t* append,
+                                         const da_paged_kv_t* pages, const void* q_rope,
+                                         void* q_rope_out, const void* kv_new,
+                                         const int32_t* positions, void* kv_cache,
+                                         void* hip_stream);
+
+/* ------------------------------------------------------------------------ */
 /* Split-KV merge                                                            */
 /* ------------------------------------------------------------------------ */
 
@@ -367,13 +447,14 @@ DA_EXPORT const char* da_status_string(da_status_t status);
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 DA_EXPORT int32_t da_version(void);
 
-/* sizeof(da_gqa_params_t), sizeof(da_mla_params_t), sizeof(da_paged_kv_t)
- * and sizeof(da_kv_scales_t) as compiled, so that bindings can check their
+/* sizeof(da_gqa_params_t), sizeof(da_mla_params_t), sizeof(da_paged_kv_t),
+ * sizeof(da_kv_scales_t) and sizeof(da_append_t) as compiled, so that bindings can check their
  * struct mirrors. */
 DA_EXPORT size_t da_gqa_params_size(void);
 DA_EXPORT size_t da_mla_params_size(void);
 DA_EXPORT size_t da_paged_kv_size(void);
 DA_EXPORT size_t da_kv_scales_size(void);
+DA_EXPORT size_t da_append_size(void);
 
 #ifdef __cplusplus
 }

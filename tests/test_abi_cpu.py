@@ -52,6 +52,7 @@ def test_struct_mirrors_and_version():
     assert L.da_mla_params_size() == ctypes.sizeof(da.MlaParams)
     assert L.da_paged_kv_size() == ctypes.sizeof(da.PagedKv) == 24
     assert L.da_kv_scales_size() == ctypes.sizeof(da.KvScales) == 40
+    assert L.da_append_size() == ctypes.sizeof(da.Append) == 40
     assert L.da_version() >= 100
     for s, txt in [(0, b"ok"), (1, b"invalid argument"), (2, b"unsupported configuration"),
                    (3, b"workspace too small"), (4, b"HIP runtime error"), (99, b"unknown status")]:
@@ -324,6 +325,50 @@ def test_fp8_entry_point_rejects_bad_arguments():
                            1 << 40, None) == 1
     assert L.da_gqa_decode_split_pass(ctypes.byref(fp8_params()), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                       None) == 1
+
+
+def append_desc(r=128, style=0, base=10000.0, inv=None, sb=48 * 128, sh=128):
+    ap = da.Append()
+    ap.rotary_dim, ap.rope_style, ap.rope_base, ap.inv_freq = r, style, base, inv
+    ap.new_stride_b, ap.new_stride_h = sb, sh
+    return ap
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,code", [
+    ({"r": 0}, 1), ({"r": 12}, 1), ({"r": 136}, 1), ({"style": 2}, 1), ({"base": 1.0}, 1),
+    ({"base": float("nan")}, 1), ({"base": float("inf")}, 1), ({"inv": 0x10002}, 1),
+    ({"sb": -128}, 1), ({"sh": 4}, 1),
+])
+def test_append_rejects_bad_descriptors(kw, code):
+    L = da.lib()
+    ap = append_desc(**kw)
+    assert L.da_gqa_append_rope(ctypes.byref(gqa()), ctypes.byref(ap), None, FAKE, FAKE, FAKE, FAKE,
+                                FAKE, FAKE, FAKE, None) == code
+    mla_ap = append_desc(**{**{"r": 64, "sb": 576, "sh": 0}, **kw})
+    assert L.da_mla_append_rope(ctypes.byref(mla()), ctypes.byref(mla_ap), None, FAKE, FAKE, FAKE,
+                                FAKE, FAKE, None) == code
+
+
+@needs_lib
+def test_append_rejects_bad_buffers_and_dtypes():
+    L = da.lib()
+    ok = append_desc()
+
+    def gcall(p=None, ap=ok, pages=None, ptrs=None):
+        ptrs = ptrs or [FAKE] * 7
+        return L.da_gqa_append_rope(ctypes.byref(p or gqa()), None if ap is None else ctypes.byref(ap),
+                                    pages, *ptrs, None)
+    assert gcall(ap=None) == 1
+    assert gcall(p=gqa(dtype=da.DA_DTYPE_FP8_E4M3)) == 2            # no fp8 append
+    assert gcall(ptrs=[FAKE, None] + [FAKE] * 5) == 1               # no q_out
+    assert gcall(ptrs=[FAKE] * 4 + [ctypes.c_void_p(0x10002)] + [FAKE] * 2) == 1   # positions misaligned
+    assert gcall(ptrs=[FAKE] * 5 + [ctypes.c_void_p(0x10008), FAKE]) == 1          # cache misaligned
+    pg = da.PagedKv()
+    pg.block_table, pg.page_size, pg.max_blocks_per_seq, pg.page_stride = FAKE.value, 24, 256, 16 * 8 * 128
+    assert gcall(pages=ctypes.byref(pg)) == 1                       # page size not a power of two
+    assert L.da_mla_append_rope(ctypes.byref(mla()), ctypes.byref(append_desc(r=128, sb=576, sh=0)),
+                                None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1   # r > 64
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):

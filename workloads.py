@@ -20,6 +20,8 @@ Seeding recipe (every stream is numpy PCG64 via ``default_rng``):
                                 default_rng([seed, cfg, 2, b])
   * W_UK:                       default_rng([seed, cfg, 3])
   * W_UV:                       default_rng([seed, cfg, 4])
+  * append positions:           default_rng([seed, cfg, 5]) .integers(0, L_max)
+  * appended rows (q, k_new, v_new; or q_rope, kv_new): default_rng([seed, cfg, 6])
 Normals are drawn in float32 and rounded to bfloat16 with round-to-nearest-even.
 W_UK / W_UV are N(0, 1/512): variance 1/512, i.e. standard deviation 1/sqrt(512).
 
@@ -421,3 +423,52 @@ def make_gqa_fp8_config(cfg: int, seed: int = BASE_SEED, scales: str = "token",
     L_max = s.seq_len if s.seq_len is not None else s.seq_len_range[1]
     return make_gqa_fp8(B, s.num_q_heads, s.num_kv_heads, s.head_dim, lens, cfg=cfg, seed=seed,
                         max_seq_len=L_max, scales=scales, pad_nan=pad_nan)
+
+
+# ----------------------------------------------------------------------------
+# cache append: the new token's rows
+# ----------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class AppendInputs:
+    """The new rows of one decode step. GQA: q [B, Hq, D] and k_new, v_new
+    [B, Hkv, D]; MLA: q [B, H, 64] (the rope part of the queries), k_new
+    [B, 576] ([c_kv | k_rope] before rotation) and v_new None. positions [B]
+    int32. Storage as GQAInputs (uint16 bit patterns for bf16)."""
+    q: np.ndarray
+    k_new: np.ndarray
+    v_new: Optional[np.ndarray]
+    positions: np.ndarray
+    dtype: str
+
+    def f64(self, name: str) -> np.ndarray:
+        a = getattr(self, name)
+        return (bf16_to_f32(a) if self.dtype == "bf16" else a).astype(np.float64)
+
+
+def draw_positions(batch: int, max_seq_len: int, cfg: int = 0, seed: int = BASE_SEED) -> np.ndarray:
+    rng = np.random.default_rng([seed, cfg, 5])
+    return rng.integers(0, max_seq_len, size=batch).astype(np.int32)
+
+
+def make_gqa_append(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                    max_seq_len: int, dtype: str = "bf16", cfg: int = 0, seed: int = BASE_SEED,
+                    positions: Optional[Sequence[int]] = None) -> AppendInputs:
+    rng = np.random.default_rng([seed, cfg, 6])
+    q = _store(_normal(rng, (batch, num_q_heads, head_dim)), dtype)
+    k = _store(_normal(rng, (batch, num_kv_heads, head_dim)), dtype)
+    v = _store(_normal(rng, (batch, num_kv_heads, head_dim)), dtype)
+    pos = draw_positions(batch, max_seq_len, cfg, seed) if positions is None else \
+        np.asarray(positions, np.int32)
+    return AppendInputs(q, k, v, pos, dtype)
+
+
+def make_mla_append(batch: int, num_heads: int, max_seq_len: int, cfg: int = 0,
+                    seed: int = BASE_SEED, positions: Optional[Sequence[int]] = None,
+                    d_c: int = 512, d_rope: int = 64) -> AppendInputs:
+    rng = np.random.default_rng([seed, cfg, 6])
+    q_rope = bf16_round(_normal(rng, (batch, num_heads, d_rope)))
+    kv_new = bf16_round(_normal(rng, (batch, d_c + d_rope)))
+    pos = draw_positions(batch, max_seq_len, cfg, seed) if positions is None else \
+        np.asarray(positions, np.int32)
+    return AppendInputs(q_rope, kv_new, None, pos, "bf16")
