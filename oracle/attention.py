@@ -61,12 +61,18 @@ def kv_head_of(h: int, num_q_heads: int, num_kv_heads: int) -> int:
     return h // g
 
 
-def gqa_decode_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_lens, scale: float):
+def gqa_decode_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_lens, scale: float,
+                   window: int = 0):
     """GQA / MQA / MHA decode for one new query token per sequence.
 
     q [B, Hq, D]; k, v [B, L_max, Hkv, D] (cache layout [B, L, n_kv, d_head]);
     seq_lens [B]; scale usually 1/sqrt(D).
     Returns out [B, Hq, D] and lse [B, Hq] (natural log).
+
+    window w > 0: sliding-window attention, only the last w rows
+    [max(0, L - w), L) are attended ("Attention variants and KV cache",
+    section 5.3: each query sees at most w keys, the cache need keep only
+    the latest w tokens). w = 0 attends all L rows.
 
     s_j = scale * q_h . k_{j, kv(h)};  p = softmax_j(s);  o_h = sum_j p_j v_{j, kv(h)}.
     Decode reads the whole cache once per step (arganzheng.life section 2.2;
@@ -87,8 +93,9 @@ def gqa_decode_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_lens, scale:
     kv_of = np.array([kv_head_of(h, Hq, Hkv) for h in range(Hq)])
     for b in range(B):
         L = int(seq_lens[b])
-        Kb = k[b, :L][:, kv_of, :]              # [L, Hq, D]: the KV row each query head reads
-        Vb = v[b, :L][:, kv_of, :]
+        lo = max(0, L - window) if window > 0 else 0
+        Kb = k[b, lo:L][:, kv_of, :]            # [rows, Hq, D]: the KV row each query head reads
+        Vb = v[b, lo:L][:, kv_of, :]
         s = scale * np.einsum("lhd,hd->lh", Kb, q[b])
         out[b], lse[b] = _softmax_attend(s, Vb)
     return out, lse
@@ -231,10 +238,13 @@ def paged_rows_ref(pool: np.ndarray, table_row, page_size: int, seq_len: int) ->
     return rows[:seq_len]
 
 
-def gqa_decode_paged_ref(q, k_pool, v_pool, block_table, page_size: int, seq_lens, scale: float):
+def gqa_decode_paged_ref(q, k_pool, v_pool, block_table, page_size: int, seq_lens, scale: float,
+                         window: int = 0):
     """GQA decode over paged K and V pools [num_pages, page_size, Hkv, D]:
     each sequence's rows are gathered in logical order (paged_rows_ref), then
-    attended exactly as by gqa_decode_ref."""
+    attended exactly as by gqa_decode_ref. With a sliding window w only rows
+    [max(0, L - w), L) are gathered, so table entries of earlier blocks are
+    never looked at."""
     seq_lens = np.asarray(seq_lens, np.int64)
     B = q.shape[0]
     L = int(max(1, seq_lens.max(initial=0)))
@@ -242,9 +252,15 @@ def gqa_decode_paged_ref(q, k_pool, v_pool, block_table, page_size: int, seq_len
     v = np.zeros((B, L) + v_pool.shape[2:])
     for b in range(B):
         Lb = int(seq_lens[b])
-        k[b, :Lb] = paged_rows_ref(k_pool, block_table[b], page_size, Lb)
-        v[b, :Lb] = paged_rows_ref(v_pool, block_table[b], page_size, Lb)
-    return gqa_decode_ref(q, k, v, seq_lens, scale)
+        if window > 0:
+            for t in range(max(0, Lb - window), Lb):
+                page = int(block_table[b][t // page_size])
+                k[b, t] = k_pool[page, t % page_size]
+                v[b, t] = v_pool[page, t % page_size]
+        else:
+            k[b, :Lb] = paged_rows_ref(k_pool, block_table[b], page_size, Lb)
+            v[b, :Lb] = paged_rows_ref(v_pool, block_table[b], page_size, Lb)
+    return gqa_decode_ref(q, k, v, seq_lens, scale, window)
 
 
 def mla_absorbed_paged_ref(q_nope, q_rope, cache_pool, block_table, page_size: int, seq_lens,

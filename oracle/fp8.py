@@ -50,11 +50,13 @@ def dequantize_ref(codes, scales) -> np.ndarray:
     return e4m3_to_float(codes) * np.asarray(scales, dtype=np.float64)[..., None]
 
 
-def gqa_decode_fp8_ref(q, k_codes, v_codes, k_scale, v_scale, seq_lens, scale: float):
+def gqa_decode_fp8_ref(q, k_codes, v_codes, k_scale, v_scale, seq_lens, scale: float,
+                       window: int = 0):
     """GQA decode over an FP8 cache: q [B, Hq, D] float64; k_codes, v_codes
     [B, L, Hkv, D] uint8 E4M3; k_scale, v_scale [B, L, Hkv] (fp32 values).
     Each sequence's first L_b rows are decoded and scaled, then attended as by
-    gqa_decode_ref. Returns out [B, Hq, D] and lse [B, Hq]."""
+    gqa_decode_ref (with its sliding window w, if any). Returns out [B, Hq, D]
+    and lse [B, Hq]."""
     seq_lens = np.asarray(seq_lens, np.int64)
     B = q.shape[0]
     L = int(max(1, seq_lens.max(initial=0)))
@@ -64,4 +66,4 @@ def gqa_decode_fp8_ref(q, k_codes, v_codes, k_scale, v_scale, seq_lens, scale: f
         Lb = int(seq_lens[b])
         k[b, :Lb] = dequantize_ref(k_codes[b, :Lb], k_scale[b, :Lb])
         v[b, :Lb] = dequantize_ref(v_codes[b, :Lb], v_scale[b, :Lb])
-    return gqa_decode_ref(q, k, v, seq_lens, scale)
+    return gqa_decode_ref(q, k, v, seq_lens, scale, window)

@@ -631,3 +631,111 @@ def test_fp8_workload_codes_round_trip():
         assert rel.max() <= 2.0 ** -4 * 1.0001
         assert np.all(np.abs(e4m3_to_float(inp.k[b, :L])) <= 448)
     assert np.all(inp.k[0, 7:] == W.FP8_NAN_CODE) and np.isnan(inp.v_scale[1, 3:]).all()
+
+
+# ----------------------------------------------------------------------------
+# sliding window ("Attention variants and KV cache", section 5.3)
+# ----------------------------------------------------------------------------
+
+def brute_window(q, k, v, seq_lens, scale, w):
+    """Scalar loops over an explicit mask: row j is seen iff L - w <= j < L."""
+    B, Hq, D = q.shape
+    g = Hq // k.shape[2]
+    out = np.zeros((B, Hq, D))
+    lse = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        L = int(seq_lens[b])
+        for h in range(Hq):
+            js = [j for j in range(L) if j >= L - w]
+            if not js:
+                continue
+            s = [scale * math.fsum(q[b, h, d] * k[b, j, h // g, d] for d in range(D)) for j in js]
+            m = max(s)
+            e = [math.exp(x - m) for x in s]
+            z = math.fsum(e)
+            lse[b, h] = m + math.log(z)
+            for d in range(D):
+                out[b, h, d] = math.fsum(ei * v[b, j, h // g, d] for ei, j in zip(e, js)) / z
+    return out, lse
+
+
+@pytest.mark.parametrize("w", [1, 3, 7, 50])
+def test_window_brute_force(w):
+    q, k, v = rand(3, 4, 8), rand(3, 9, 2, 8), rand(3, 9, 2, 8)
+    lens = [9, 4, 0]
+    o, l = gqa_decode_ref(q, k, v, lens, 0.3, window=w)
+    bo, bl = brute_window(q, k, v, lens, 0.3, w)
+    np.testing.assert_allclose(o, bo, atol=1e-12)
+    np.testing.assert_allclose(l, bl, atol=1e-12)
+
+
+def test_window_closed_forms():
+    q, k, v = rand(2, 4, 16), rand(2, 12, 2, 16), rand(2, 12, 2, 16)
+    lens = [12, 5]
+    full = gqa_decode_ref(q, k, v, lens, 0.25)
+    for w in (12, 13, 1000):          # a window that holds every row changes nothing
+        o, l = gqa_decode_ref(q, k, v, lens, 0.25, window=w)
+        np.testing.assert_array_equal(o[0], full[0][0])
+    o, l = gqa_decode_ref(q, k, v, lens, 0.25, window=1)      # only the newest row
+    for b, L in enumerate(lens):
+        for h in range(4):
+            np.testing.assert_allclose(o[b, h], v[b, L - 1, h // 2], atol=1e-15)
+            np.testing.assert_allclose(l[b, h], 0.25 * q[b, h] @ k[b, L - 1, h // 2], atol=1e-12)
+    # shifted cache: the window over rows [L - w, L) == full attention over those rows at 0..w
+    w = 4
+    ks, vs = k[:, 12 - w:].copy(), v[:, 12 - w:].copy()
+    o, l = gqa_decode_ref(q[:1], k[:1], v[:1], [12], 0.25, window=w)
+    fo, fl = gqa_decode_ref(q[:1], ks[:1], vs[:1], [w], 0.25)
+    np.testing.assert_allclose(o, fo, atol=1e-13)
+    np.testing.assert_allclose(l, fl, atol=1e-13)
+
+
+def test_window_sees_at_most_w_rows():
+    # one-hot values by position make the output the softmax weights
+    L, w = 10, 4
+    q, k = rand(1, 1, 16), rand(1, L, 1, 16)
+    v = np.zeros((1, L, 1, 16))
+    for j in range(L):
+        v[0, j, 0, j] = 1.0
+    o, _ = gqa_decode_ref(q, k, v, [L], 0.5, window=w)
+    seen = np.nonzero(o[0, 0])[0]
+    assert list(seen) == list(range(L - w, L))
+
+
+def test_window_paged_and_fp8_forms():
+    from oracle.fp8 import dequantize_ref, gqa_decode_fp8_ref
+    q, k, v = rand(2, 4, 16), rand(2, 40, 2, 16), rand(2, 40, 2, 16)
+    lens, w, ps = [40, 23], 9, 16
+    want = gqa_decode_ref(q, k, v, lens, 0.2, window=w)
+    # pages in reverse order; entries of blocks before the window are -1
+    table = np.array([[-1, 1, 0], [-1, 3, -1]])
+    pool_k, pool_v = np.zeros((4, ps, 2, 16)), np.zeros((4, ps, 2, 16))
+    for b, L in enumerate(lens):
+        for t in range(max(0, L - w), L):
+            pool_k[table[b, t // ps], t % ps] = k[b, t]
+            pool_v[table[b, t // ps], t % ps] = v[b, t]
+    got = OA.gqa_decode_paged_ref(q, pool_k, pool_v, table, ps, lens, 0.2, window=w)
+    np.testing.assert_allclose(got[0], want[0], atol=1e-13)
+    codes = RNG.integers(0, 126, size=(2, 40, 2, 16)).astype(np.uint8)
+    sc = RNG.uniform(0.5, 2.0, size=(2, 40, 2))
+    got8 = gqa_decode_fp8_ref(q, codes, codes, sc, sc, lens, 0.2, window=w)
+    dq = dequantize_ref(codes, sc)
+    want8 = gqa_decode_ref(q, dq, dq, lens, 0.2, window=w)
+    np.testing.assert_allclose(got8[0], want8[0], atol=1e-13)
+
+
+def test_planted_off_by_one_window_fails_the_row_count_pin(monkeypatch):
+    orig = OA.gqa_decode_ref
+
+    def off_by_one(q, k, v, seq_lens, scale, window=0):
+        # [L - w, L] read as w + 1 rows
+        return orig(q, k, v, seq_lens, scale, window + 1 if window > 0 else 0)
+    monkeypatch.setattr(OA, "gqa_decode_ref", off_by_one)
+    global gqa_decode_ref
+    saved = gqa_decode_ref
+    gqa_decode_ref = off_by_one
+    try:
+        with pytest.raises(AssertionError):
+            test_window_sees_at_most_w_rows()
+    finally:
+        gqa_decode_ref = saved
