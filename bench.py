@@ -176,6 +176,34 @@ def setup_gqa(cfg):
     return calls, alg, info, inp
 
 
+WINDOW = 4096          # Mistral 7B's sliding window ("Attention variants and KV cache", section 5.3)
+WINDOW_CONTEXT = 8192  # rows per sequence in the cache; only the last WINDOW are attended
+
+
+def setup_gqa_window():
+    """Sliding-window GQA decode: config 2's shape (Mistral 7B has the same
+    32 query heads, 8 KV heads and d 128) with 8192 cached rows per sequence
+    and a 4096-row window, so each call reads the same bytes as config 2."""
+    import torch
+    import workloads as W
+    import decode_attention_kv_bf16_amd as da
+    inp = W.make_gqa(32, 32, 8, 128, [WINDOW_CONTEXT] * 32, cfg=2)
+    q = to_dev_bf16(inp.q)
+    k, v = to_dev_bf16(inp.k), to_dev_bf16(inp.v)
+    sl = torch.from_numpy(inp.seq_lens).cuda()
+    B, Hq, D = q.shape
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+
+    def call():
+        da.gqa_decode(q, k, v, sl, inp.scale, out=out, lse=lse, window=WINDOW)
+    rows = int(np.minimum(inp.seq_lens, WINDOW).sum())
+    alg = gqa_alg(B, Hq, k.shape[2], D, rows)
+    info = dict(batch=B, q_heads=Hq, kv_heads=int(k.shape[2]), head_dim=D, seq_len=WINDOW_CONTEXT,
+                window=WINDOW, splits=da.gqa_num_splits(q, k, window=WINDOW))
+    return [[("gqa_window", call)]], alg, info, inp
+
+
 def setup_mla(cfg):
     import torch
     import workloads as W
@@ -402,6 +430,8 @@ def run_gpu(args):
         plans.append(("mla-paged", setup_mla_paged(3)))
     if args.workload == "gqa-fp8":
         plans.append(("gqa-fp8", setup_gqa_fp8(2)))
+    if args.workload == "gqa-window":
+        plans.append(("gqa-window", setup_gqa_window()))
     if args.workload == "append":
         plans.append(("gqa-append", setup_append("gqa-append")))
         plans.append(("mla-append", setup_append("mla-append")))
@@ -500,7 +530,7 @@ def run_gpu(args):
     # dominant kernel's roofline
     kind, (calls, alg, info, _) = next(p for p in plans
                                        if any(dom == n for n, _ in p[1][0][0]))
-    if dom == "gqa_split_pass":
+    if dom in ("gqa_split_pass", "gqa_window"):
         dom_bytes = alg["cache"] + alg["q"]
     elif dom in ("mla_attend", "mla_attend_paged"):
         dom_bytes = alg["cache"]
@@ -548,6 +578,7 @@ def workload_name(w):
             "gqa-paged": "llama3-8b-gqa-b32-l4096-paged16",
             "mla-paged": "deepseek-v3-mla-b64-l4096-paged16",
             "gqa-fp8": "llama3-8b-gqa-b32-l4096-fp8e4m3",
+            "gqa-window": "mistral-7b-shape-gqa-b32-l8192-window4096",
             "append": "cache append + rope: llama3-8b-gqa-b32-l4096 + deepseek-v3-mla-b64-l4096"}[w]
 
 
@@ -627,6 +658,15 @@ def cpu_baseline(plans, budget_s):
                     mla_append_rope_ref(*args, block_table=tab, page_size=16)
                 dt = time.perf_counter() - t
                 a1 = dict(total=alg["total"] // B)
+            elif kind == "gqa-window":
+                f = (lambda a: W.bf16_to_f32(a).astype(np.float64))
+                L = int(inp.seq_lens[b])
+                args = (f(inp.q[b:b + 1]), f(inp.k[b:b + 1, :L]), f(inp.v[b:b + 1, :L]),
+                        inp.seq_lens[b:b + 1], inp.scale)
+                t = time.perf_counter()
+                gqa_decode_ref(*args, window=WINDOW)
+                dt = time.perf_counter() - t
+                a1 = gqa_alg(1, inp.q.shape[1], inp.k.shape[2], inp.q.shape[2], min(L, WINDOW))
             elif kind == "gqa":
                 f = (lambda a: W.bf16_to_f32(a).astype(np.float64))
                 L = int(inp.seq_lens[b])
@@ -662,7 +702,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="step",
                     choices=["step", "gqa", "mla", "mla-long", "gqa-ragged", "gqa-paged",
-                             "mla-paged", "gqa-fp8", "append"])
+                             "mla-paged", "gqa-fp8", "append", "gqa-window"])
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle time for the CPU baseline (0 disables)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,

@@ -50,6 +50,7 @@ class GqaParams(ctypes.Structure):
         ("kv_stride_t", ctypes.c_int64),
         ("kv_stride_h", ctypes.c_int64),
         ("num_splits", ctypes.c_int32),
+        ("sliding_window", ctypes.c_int32),
     ]
 
 
@@ -247,7 +248,7 @@ def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
 # ----------------------------------------------------------------------------
 
 def gqa_params(q: torch.Tensor, k_cache: torch.Tensor, softmax_scale: Optional[float] = None,
-               num_splits: int = 0) -> GqaParams:
+               num_splits: int = 0, window: int = 0) -> GqaParams:
     B, Hq, D = q.shape
     Bk, L_max, Hkv, Dk = k_cache.shape
     if Bk != B or Dk != D:
@@ -267,18 +268,20 @@ def gqa_params(q: torch.Tensor, k_cache: torch.Tensor, softmax_scale: Optional[f
     p.q_stride_b, p.q_stride_h = q.stride(0), q.stride(1)
     p.kv_stride_b, p.kv_stride_t, p.kv_stride_h = k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)
     p.num_splits = int(num_splits)
+    p.sliding_window = int(window)
     return p
 
 
 def gqa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                seq_lens: Optional[torch.Tensor] = None, softmax_scale: Optional[float] = None,
                num_splits: int = 0, out: Optional[torch.Tensor] = None,
-               lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+               lse: Optional[torch.Tensor] = None, window: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
     """GQA/MQA/MHA decode of one new token per sequence.
 
     q [B, Hq, D]; k_cache, v_cache [B, L_max, Hkv, D] (same dtype, bf16 or fp32,
     same strides); seq_lens [B] int32 on the GPU (None: all L_max).
     Returns out [B, Hq, D] float32 and lse [B, Hq] float32 (natural log).
+    window w > 0: sliding-window attention over the last w rows of each sequence.
     """
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
         _require_cuda(name, t)
@@ -290,7 +293,7 @@ def gqa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         _require_cuda("seq_lens", seq_lens)
         if seq_lens.dtype != torch.int32 or seq_lens.shape != (q.shape[0],) or not seq_lens.is_contiguous():
             raise ValueError("seq_lens must be a contiguous int32 tensor of shape [B]")
-    p = gqa_params(q, k_cache, softmax_scale, num_splits)
+    p = gqa_params(q, k_cache, softmax_scale, num_splits, window)
     L = lib()
     B, Hq, D = q.shape
     if out is None:
@@ -309,10 +312,10 @@ def gqa_decode_split_pass(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
                           seq_lens: Optional[torch.Tensor] = None,
                           softmax_scale: Optional[float] = None, num_splits: int = 0,
                           part_out: Optional[torch.Tensor] = None,
-                          part_lse: Optional[torch.Tensor] = None):
+                          part_lse: Optional[torch.Tensor] = None, window: int = 0):
     """The split pass alone: returns per-split (part_out [S,B,Hq,D], part_lse [S,B,Hq]).
     splitkv_combine() of these equals gqa_decode()."""
-    p = gqa_params(q, k_cache, softmax_scale, num_splits)
+    p = gqa_params(q, k_cache, softmax_scale, num_splits, window)
     L = lib()
     S = int(L.da_gqa_decode_num_splits(ctypes.byref(p)))
     B, Hq, D = q.shape
@@ -327,8 +330,8 @@ def gqa_decode_split_pass(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
     return part_out, part_lse
 
 
-def gqa_num_splits(q: torch.Tensor, k_cache: torch.Tensor, num_splits: int = 0) -> int:
-    p = gqa_params(q, k_cache, None, num_splits)
+def gqa_num_splits(q: torch.Tensor, k_cache: torch.Tensor, num_splits: int = 0, window: int = 0) -> int:
+    p = gqa_params(q, k_cache, None, num_splits, window)
     return int(lib().da_gqa_decode_num_splits(ctypes.byref(p)))
 
 
@@ -340,7 +343,7 @@ def gqa_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                    k_scale: torch.Tensor, v_scale: torch.Tensor,
                    seq_lens: Optional[torch.Tensor] = None, softmax_scale: Optional[float] = None,
                    num_splits: int = 0, out: Optional[torch.Tensor] = None,
-                   lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                   lse: Optional[torch.Tensor] = None, window: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
     """gqa_decode over an E4M3 cache: q [B, Hq, D] bf16; k_cache, v_cache
     [B, L_max, Hkv, D] uint8 codes (or torch.float8_e4m3fn); k_scale, v_scale
     float32 of shape [B, L_max, Hkv] (broadcast views with zero strides are
@@ -375,6 +378,7 @@ def gqa_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     p.q_stride_b, p.q_stride_h = q.stride(0), q.stride(1)
     p.kv_stride_b, p.kv_stride_t, p.kv_stride_h = k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)
     p.num_splits = int(num_splits)
+    p.sliding_window = int(window)
     sc = KvScales()
     sc.k_scale, sc.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
     sc.stride_b, sc.stride_t, sc.stride_h = k_scale.stride()
@@ -421,7 +425,7 @@ def gqa_decode_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor
                      block_table: torch.Tensor, page_size: int, seq_lens: torch.Tensor,
                      max_seq_len: Optional[int] = None, softmax_scale: Optional[float] = None,
                      num_splits: int = 0, out: Optional[torch.Tensor] = None,
-                     lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                     lse: Optional[torch.Tensor] = None, window: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
     """gqa_decode over paged pools: k_pool, v_pool [num_pages, page_size, Hkv, D];
     block_table [B, max_blocks_per_seq] int32 (token t of sequence b is row
     t % page_size of page block_table[b, t // page_size]); seq_lens [B] int32.
@@ -443,7 +447,7 @@ def gqa_decode_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor
         raise ValueError("k_pool must be [num_pages, page_size, Hkv, D] with a contiguous D axis")
     # the params describe a [B, max_seq_len, Hkv, D] cache with the pool's
     # token and head strides (the batch stride is unused for paged pools)
-    p = gqa_params(q, k_pool[:1].expand(B, -1, -1, -1), softmax_scale, num_splits)
+    p = gqa_params(q, k_pool[:1].expand(B, -1, -1, -1), softmax_scale, num_splits, window)
     p.max_seq_len = int(max_seq_len)
     p.kv_stride_b = 0
     L = lib()

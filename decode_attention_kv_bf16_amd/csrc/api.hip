@@ -51,7 +51,7 @@ int gqa_heads_per_block(int group) {
 da_status_t check_gqa_params(const da_gqa_params_t* p) {
   if (!p) return DA_ERR_INVALID_ARGUMENT;
   if (p->batch < 1 || p->batch > 65535 || p->num_q_heads < 1 || p->num_kv_heads < 1 ||
-      p->max_seq_len < 1 || p->head_dim < 1 || p->num_splits < 0)
+      p->max_seq_len < 1 || p->head_dim < 1 || p->num_splits < 0 || p->sliding_window < 0)
     return DA_ERR_INVALID_ARGUMENT;
   if (p->num_q_heads % p->num_kv_heads != 0) return DA_ERR_INVALID_ARGUMENT;
   if (p->num_q_heads > 65535) return DA_ERR_INVALID_ARGUMENT;
@@ -144,14 +144,20 @@ GqaPlan plan_gqa(const da_gqa_params_t* p, int align = 1) {
     pl.waves_per_block = 16;
     s = cus / units;
   }
+  // Rows a sequence can attend: all L_max, or with a sliding window w the
+  // rows [L - w, L), whose start the kernels round down to a multiple of 16
+  // on paged pools: at most w + 15 rows (the same bound for both, so that the
+  // workspace queries, which do not know about paging, cover paged calls).
+  const int64_t len = p->sliding_window > 0 && p->sliding_window + 15 < p->max_seq_len
+                          ? p->sliding_window + 15 : p->max_seq_len;
   if (p->num_splits == 0) {
-    const int64_t s_max = ceil_div(p->max_seq_len, 128);
+    const int64_t s_max = ceil_div(len, 128);
     s = s < s_max ? s : s_max;
   }
-  if (s > p->max_seq_len) s = p->max_seq_len;
+  if (s > len) s = len;
   if (s < 1) s = 1;
-  pl.chunk = (int)round_up((size_t)ceil_div(p->max_seq_len, s), (size_t)align);
-  pl.splits = (int)ceil_div(p->max_seq_len, pl.chunk);  // drop splits that would be empty
+  pl.chunk = (int)round_up((size_t)ceil_div(len, s), (size_t)align);
+  pl.splits = (int)ceil_div(len, pl.chunk);  // drop splits that would be empty
   if (pl.splits > 1) {
     const size_t rows = (size_t)p->batch * p->num_q_heads;
     pl.part_out_bytes = round_up((size_t)pl.splits * rows * p->head_dim * sizeof(float), 256);
@@ -329,6 +335,7 @@ da::GqaArgs gqa_args(const da_gqa_params_t* p, const GqaPlan& pl, const void* q,
   a.max_seq_len = p->max_seq_len;
   a.num_splits = pl.splits;
   a.chunk = pl.chunk;
+  a.window = p->sliding_window;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
   return a;
 }

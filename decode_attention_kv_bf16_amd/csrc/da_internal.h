@@ -25,6 +25,11 @@ struct GqaArgs {
   int32_t waves_per_block;   // 4, 8 or 16
   int32_t order_by_length;   // 1: workgroups take sequences longest first (needs batch <= 256)
   int32_t max_seq_len, num_splits, chunk;            // chunk = tokens per split
+  // Sliding window w > 0: sequence b attends rows [w0, L_b), w0 = max(0, L_b - w).
+  // Splits cover rows from w0 (contiguous caches) or from w0 rounded down to a
+  // multiple of 16 (paged pools, so that steps stay inside pages), and rows
+  // before w0 are masked. 0: every row.
+  int32_t window;
   float scale_log2;          // softmax_scale * log2(e)
   // Paged K/V pools (page_shift > 0): token t of sequence b is row
   // t & (2^page_shift - 1) of page block_table[b * max_blocks + (t >> page_shift)]

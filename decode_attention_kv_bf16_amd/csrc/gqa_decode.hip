@@ -183,7 +183,11 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
   const int h0 = kvh * a.group + (blockIdx.y % n_sub) * GH;
   // clamped to [0, max_seq_len]: no read past the cache or the block table
   const int L = a.seq_lens ? min(max(a.seq_lens[b], 0), a.max_seq_len) : a.max_seq_len;
-  const int t_begin = split * a.chunk;
+  // sliding window: rows before w0 are neither read nor weighted; splits
+  // start at w0 (paged: at the 16-row boundary below it, so steps stay
+  // inside pages)
+  const int w0 = a.window > 0 ? max(L - a.window, 0) : 0;
+  const int t_begin = (a.page_shift > 0 ? (w0 & ~15) : w0) + split * a.chunk;
   const int t_end = min(L, t_begin + a.chunk);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -307,7 +311,7 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = base + u * RPW + row;
-      if (base < t_end && t < t_end) {
+      if (base < t_end && t < t_end && t >= w0) {
         kk[u] = R::load(kp + off + (int64_t)(t - base) * a.kv_st);
         vv[u] = R::load(vp + off + (int64_t)(t - base) * a.kv_st);
       } else {
@@ -319,7 +323,7 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
 #pragma unroll
       for (int j = 0; j < kSc; ++j) {
         const int t = base + (kRS ? (col >> 2) : j) * RPW + row;
-        const bool ok = t < t_end;
+        const bool ok = t < t_end && t >= w0;
         ks[j] = ok ? ksc[(int64_t)t * a.sc_st] : 0.f;
         vs[j] = ok ? vsc[(int64_t)t * a.sc_st] : 0.f;
       }
@@ -369,7 +373,8 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
       reduce_scatter_stage<kDppRowHalfMirror, (kRsN >= 2 ? kRsN / 2 : 1)>(v, (col & 4) != 0);
       reduce_scatter_stage<kDppQuadReverse, (kRsN >= 4 ? kRsN / 4 : 1)>(v, (col & 2) != 0);
       reduce_scatter_stage<kDppQuadSwap1, (kRsN >= 8 ? kRsN / 8 : 1)>(v, (col & 1) != 0);
-      const bool valid = base + (col >> 2) * RPW + row < t_end;
+      const int tv = base + (col >> 2) * RPW + row;
+      const bool valid = tv < t_end && tv >= w0;
       float p[kRsV], alpha[kRsV];
       bool moved = false;
 #pragma unroll
@@ -410,7 +415,8 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
     float s[GH][U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const bool valid = base + u * RPW + row < t_end;
+      const int tv = base + u * RPW + row;
+      const bool valid = tv < t_end && tv >= w0;
       if constexpr (kBf16) {
         const uint4 w = key_words(kw[u]);
         const uint32_t kk[4] = {w.x, w.y, w.z, w.w};

@@ -104,7 +104,10 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_mfma_kernel(GqaArgs a) {
   const int kvh = blockIdx.y / n_sub;
   const int h0 = kvh * a.group + (blockIdx.y % n_sub) * GH;
   const int L = a.seq_lens ? min(max(a.seq_lens[b], 0), a.max_seq_len) : a.max_seq_len;
-  const int t_begin = split * a.chunk;
+  // sliding window: rows before w0 are masked; splits start at w0 (paged: at
+  // the 16-row boundary below it, so steps stay inside pages)
+  const int w0 = a.window > 0 ? max(L - a.window, 0) : 0;
+  const int t_begin = (a.page_shift > 0 ? (w0 & ~15) : w0) + split * a.chunk;
   const int t_end = min(L, t_begin + a.chunk);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -303,7 +306,8 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_mfma_kernel(GqaArgs a) {
       const int tj = kFp8 ? tau(g, j) : 4 * g + j;
       float scl = a.scale_log2;
       if constexpr (kFp8) scl *= ksl[j];
-      f.z[j] = t0 + tj < t_end ? (j < 4 ? s[0][j] : s[kHalves - 1][j & 3]) * scl : kNegInf;
+      f.z[j] = t0 + tj < t_end && t0 + tj >= w0 ? (j < 4 ? s[0][j] : s[kHalves - 1][j & 3]) * scl
+                                                : kNegInf;
       f.zmax = fmaxf(f.zmax, f.z[j]);
     }
   };

@@ -95,6 +95,8 @@ typedef struct {
   int64_t kv_stride_t;     /* default layout [B, L_max, Hkv, D]: */
   int64_t kv_stride_h;     /*   kv_stride_b = L_max*Hkv*D, kv_stride_t = Hkv*D, kv_stride_h = D */
   int32_t num_splits;      /* S >= 1 forces a split count; 0 lets the library choose */
+  int32_t sliding_window;  /* w >= 1: attend only rows [max(0, L_b - w), L_b) (sliding-window
+                              attention, arganzheng.life section 5.3); 0: all rows */
 } da_gqa_params_t;
 
 /* Bytes of workspace da_gqa_decode needs for these parameters (0 when the
@@ -117,6 +119,11 @@ DA_EXPORT int32_t da_gqa_decode_num_splits(const da_gqa_params_t* params);
  *   workspace  device buffer of at least da_gqa_decode_workspace_size() bytes
  *              (may be NULL when that size is 0); its contents are scratch.
  * Rows past seq_lens[b] are never read, so they may hold anything.
+ * With a sliding window w, rows before max(0, L_b - w) take no part: on a
+ * contiguous cache they are not read; on paged pools the rows of the window's
+ * first page from the 16-row boundary at or below L_b - w are read and given
+ * weight 0 (so they must be finite), and the table entries of earlier blocks
+ * are never read (their pages may be released).
  */
 DA_EXPORT da_status_t da_gqa_decode(const da_gqa_params_t* params,
                           const void* q, const void* k_cache, const void* v_cache,

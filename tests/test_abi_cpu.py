@@ -327,6 +327,24 @@ def test_fp8_entry_point_rejects_bad_arguments():
                                       None) == 1
 
 
+@needs_lib
+def test_sliding_window_planning_without_a_device():
+    L = da.lib()
+    full = gqa(B=2, Hq=8, Hkv=2)
+    bad = gqa(B=2, Hq=8, Hkv=2)
+    bad.sliding_window = -1
+    assert L.da_gqa_decode_num_splits(ctypes.byref(bad)) == 0
+    assert L.da_gqa_decode(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == 1
+    s_full = L.da_gqa_decode_num_splits(ctypes.byref(full))
+    for w in (1, 16, 100, 1000, 4081, 4096, 1 << 20):
+        p = gqa(B=2, Hq=8, Hkv=2)
+        p.sliding_window = w
+        s = L.da_gqa_decode_num_splits(ctypes.byref(p))
+        assert 1 <= s <= s_full
+        # planned on min(L_max, w + 15) rows: the splits cover them
+        assert L.da_gqa_decode_workspace_size(ctypes.byref(p)) <= L.da_gqa_decode_workspace_size(ctypes.byref(full))
+
+
 def append_desc(r=128, style=0, base=10000.0, inv=None, sb=48 * 128, sh=128):
     ap = da.Append()
     ap.rotary_dim, ap.rope_style, ap.rope_base, ap.inv_freq = r, style, base, inv
