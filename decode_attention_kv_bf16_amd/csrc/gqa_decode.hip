@@ -311,7 +311,7 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = base + u * RPW + row;
-      if (base < t_end && t < t_end && t >= w0) {
+      if (base < t_end && (uint32_t)(t - w0) < (uint32_t)(t_end - w0)) {
         kk[u] = R::load(kp + off + (int64_t)(t - base) * a.kv_st);
         vv[u] = R::load(vp + off + (int64_t)(t - base) * a.kv_st);
       } else {
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
 #pragma unroll
       for (int j = 0; j < kSc; ++j) {
         const int t = base + (kRS ? (col >> 2) : j) * RPW + row;
-        const bool ok = t < t_end && t >= w0;
+        const bool ok = (uint32_t)(t - w0) < (uint32_t)(t_end - w0);
         ks[j] = ok ? ksc[(int64_t)t * a.sc_st] : 0.f;
         vs[j] = ok ? vsc[(int64_t)t * a.sc_st] : 0.f;
       }
@@ -374,7 +374,7 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
       reduce_scatter_stage<kDppQuadReverse, (kRsN >= 4 ? kRsN / 4 : 1)>(v, (col & 2) != 0);
       reduce_scatter_stage<kDppQuadSwap1, (kRsN >= 8 ? kRsN / 8 : 1)>(v, (col & 1) != 0);
       const int tv = base + (col >> 2) * RPW + row;
-      const bool valid = tv < t_end && tv >= w0;
+      const bool valid = (uint32_t)(tv - w0) < (uint32_t)(t_end - w0);
       float p[kRsV], alpha[kRsV];
       bool moved = false;
 #pragma unroll
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int tv = base + u * RPW + row;
-      const bool valid = tv < t_end && tv >= w0;
+      const bool valid = (uint32_t)(tv - w0) < (uint32_t)(t_end - w0);
       if constexpr (kBf16) {
         const uint4 w = key_words(kw[u]);
         const uint32_t kk[4] = {w.x, w.y, w.z, w.w};

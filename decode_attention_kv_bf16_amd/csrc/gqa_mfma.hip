@@ -306,8 +306,9 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_mfma_kernel(GqaArgs a) {
       const int tj = kFp8 ? tau(g, j) : 4 * g + j;
       float scl = a.scale_log2;
       if constexpr (kFp8) scl *= ksl[j];
-      f.z[j] = t0 + tj < t_end && t0 + tj >= w0 ? (j < 4 ? s[0][j] : s[kHalves - 1][j & 3]) * scl
-                                                : kNegInf;
+      // row in [w0, t_end): one unsigned compare
+      f.z[j] = (uint32_t)(t0 + tj - w0) < (uint32_t)(t_end - w0)
+                   ? (j < 4 ? s[0][j] : s[kHalves - 1][j & 3]) * scl : kNegInf;
       f.zmax = fmaxf(f.zmax, f.z[j]);
     }
   };

@@ -20,7 +20,10 @@
  *
  *  Plus the split-KV merge (flash-decoding: split the cache along the
  *  sequence, softmax per split, merge the normalisers; arganzheng.life
- *  section 5.2).
+ *  section 5.2), paged and FP8 (E4M3) caches (section 6), sliding-window
+ *  GQA (section 5.3), and the step before decode: appending the new token's
+ *  rows to the cache with rotary position embedding (kakack.github.io
+ *  section 2.2; arganzheng.life sections 4.2 and 4.4).
  *
  * Conventions shared by every entry point
  *  - All pointers to tensors are DEVICE pointers on the current HIP device;
