@@ -17,9 +17,18 @@ Readings used here:
     per head or per token are the same arrays with repeated entries.
 The attention itself is then exactly gqa_decode_ref on the decoded values.
 
+Appending into such a cache (the decode step's append, "KV Cache 如何影响了
+LLM Inference" section 2.2, with the rotation of oracle/rope.py) quantizes
+each new (token, KV head) row x with s = max|x| / 448 (dynamic) or a given s
+(static), codes E4M3(x / s) rounded to nearest even, magnitudes clamped to
+448. The scale and x / s are taken in float32, the kernel's precision, since
+they decide integer codes.
+
 Parity status: pinned by tests/test_oracle_pins.py (decoder against torch's
 float8_e4m3fn conversion for all 256 codes and against the format's defining
-values; attention against brute force and closed forms with scales).
+values; attention against brute force and closed forms with scales; encoder
+against the decoder on every finite code, midpoints, clamping and torch's
+conversion).
 """
 from __future__ import annotations
 
@@ -67,3 +76,58 @@ def gqa_decode_fp8_ref(q, k_codes, v_codes, k_scale, v_scale, seq_lens, scale: f
         k[b, :Lb] = dequantize_ref(k_codes[b, :Lb], k_scale[b, :Lb])
         v[b, :Lb] = dequantize_ref(v_codes[b, :Lb], v_scale[b, :Lb])
     return gqa_decode_ref(q, k, v, seq_lens, scale, window)
+
+
+def e4m3_encode(y) -> np.ndarray:
+    """float32 values -> E4M3 codes (uint8), round to nearest even, |y|
+    clamped to 448, from the format's fields: below 2^-6 a multiple of 2^-9
+    (subnormal), else 1.m with 3 mantissa bits at the value's exponent."""
+    y = np.asarray(y, dtype=np.float64)
+    sign = np.where(np.signbit(y), 0x80, 0).astype(np.int64)
+    a = np.minimum(np.abs(y), E4M3_MAX)
+    sub = a < 2.0 ** -6
+    m_sub = np.rint(a * 512.0).astype(np.int64)              # numpy rint: half to even
+    e = np.floor(np.log2(np.where(sub, 1.0, a))).astype(np.int64)
+    q = np.exp2(e - 3.0)
+    m = np.rint(np.where(sub, 0.0, a) / q).astype(np.int64)   # 8..16 (16: next binade)
+    bump = m == 16
+    e = np.where(bump, e + 1, e)
+    m = np.where(bump, 8, m)
+    normal = ((e + E4M3_BIAS) << 3) | (m - 8)
+    return (sign | np.where(sub, m_sub, normal)).astype(np.uint8)
+
+
+def quantize_rows_ref(x, scale=None):
+    """x [..., D] (one row per leading index) -> (codes, scales). Dynamic
+    (scale None): s = max|x| / 448 per row; static: the given s per row. In
+    float32, as the kernel decides the codes; codes are 0 where s is 0."""
+    x32 = np.asarray(x, dtype=np.float32)
+    if scale is None:
+        s = (np.abs(x32).max(axis=-1) / np.float32(E4M3_MAX)).astype(np.float32)
+    else:
+        s = np.broadcast_to(np.asarray(scale, np.float32), x32.shape[:-1]).astype(np.float32)
+    safe = np.where(s == 0, np.float32(1), s)
+    y = (x32 / safe[..., None]).astype(np.float32)
+    codes = np.where((s == 0)[..., None], np.uint8(0), e4m3_encode(y))
+    return codes.astype(np.uint8), s
+
+
+def gqa_append_rope_fp8_ref(q, k_new, v_new, positions, max_seq_len: int, rotary_dim: int,
+                            style: int, base: float = 10000.0, static_scales=None):
+    """The new rows of an append into an E4M3 cache: q and k rotated in fp64
+    (oracle.rope.apply_rope_ref), each K and V row quantized by
+    quantize_rows_ref. q [B, Hq, D], k_new / v_new [B, Hkv, D] float64;
+    static_scales None (dynamic) or a pair of [B, Hkv] arrays. Returns
+    (q_rot, k_rot, k_codes, k_scales, v_codes, v_scales, written); the codes
+    are those of the rows written at positions[b] for the sequences in
+    `written`."""
+    from oracle.rope import apply_rope_ref
+    positions = np.asarray(positions, np.int64)
+    written = (positions >= 0) & (positions < max_seq_len)
+    pos = np.where(written, positions, 0)
+    q_rot = apply_rope_ref(q, pos, rotary_dim, style, base)
+    k_rot = apply_rope_ref(k_new, pos, rotary_dim, style, base)
+    ks, vs = (None, None) if static_scales is None else static_scales
+    k_codes, k_sc = quantize_rows_ref(k_rot, ks)
+    v_codes, v_sc = quantize_rows_ref(np.asarray(v_new, np.float64), vs)
+    return q_rot, k_rot, k_codes, k_sc, v_codes, v_sc, written

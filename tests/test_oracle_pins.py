@@ -739,3 +739,57 @@ def test_planted_off_by_one_window_fails_the_row_count_pin(monkeypatch):
             test_window_sees_at_most_w_rows()
     finally:
         gqa_decode_ref = saved
+
+
+# ----------------------------------------------------------------------------
+# E4M3 encoder and the fp8 append oracle
+# ----------------------------------------------------------------------------
+
+def test_e4m3_encoder_inverts_the_decoder_and_rounds_to_even():
+    from oracle.fp8 import e4m3_encode, e4m3_to_float
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)   # finite codes
+    vals = e4m3_to_float(codes)
+    got = e4m3_encode(vals.astype(np.float32))
+    # +0 and -0 both encode by their sign; every other value round-trips
+    assert np.array_equal(got, codes)
+    # midpoints between neighbours go to the even mantissa
+    pos = np.sort(e4m3_to_float(np.arange(0, 0x7F, dtype=np.uint8)))
+    mids = (pos[:-1] + pos[1:]) / 2
+    enc = e4m3_encode(mids.astype(np.float32))
+    dec = e4m3_to_float(enc)
+    lo_code = e4m3_encode(pos[:-1].astype(np.float32))
+    hi_code = e4m3_encode(pos[1:].astype(np.float32))
+    even = np.where(lo_code % 2 == 0, pos[:-1], pos[1:])
+    assert np.array_equal(dec, even), "ties must go to the even code"
+    assert np.all((enc == lo_code) | (enc == hi_code))
+    # clamping: beyond 448 the largest finite code, never NaN
+    assert list(e4m3_encode(np.array([448.0, 460.0, 1e6, -1e30], np.float32))) == [0x7E, 0x7E, 0x7E, 0xFE]
+
+
+def test_e4m3_encoder_agrees_with_torch():
+    from oracle.fp8 import e4m3_encode
+    x = (RNG.standard_normal(20000) * np.exp2(RNG.uniform(-12, 8, 20000))).astype(np.float32)
+    x = np.clip(x, -448, 448)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(e4m3_encode(x), want)
+
+
+def test_fp8_append_oracle_scales_and_codes():
+    from oracle.fp8 import dequantize_ref, gqa_append_rope_fp8_ref
+    from oracle.rope import STYLE_HALF
+    q, k, v = rand(3, 8, 64), rand(3, 2, 64), rand(3, 2, 64)
+    v[1, 1] = 0.0                                        # an all-zero row: scale 0, codes 0
+    out = gqa_append_rope_fp8_ref(q, k, v, [5, -1, 7], 10, 64, STYLE_HALF)
+    q_rot, k_rot, kc, ks, vc, vs, written = out
+    assert list(written) == [True, False, True]
+    np.testing.assert_allclose(ks, np.abs(k_rot).max(-1) / 448, rtol=1e-7)
+    assert vs[1, 1] == 0 and not vc[1, 1].any()
+    # each row's largest magnitude maps to 448, and decoding is within half a step
+    for codes, sc, x in ((kc, ks, k_rot), (vc, vs, v)):
+        dq = dequantize_ref(codes, sc)
+        rel = np.abs(dq - x) / np.maximum(np.abs(x).max(-1, keepdims=True), 1e-30)
+        assert rel.max() <= 2.0 ** -4 + 1e-6
+    # static scales are used as given
+    st = (np.full((3, 2), 0.01), np.full((3, 2), 0.02))
+    _, _, kc2, ks2, _, vs2, _ = gqa_append_rope_fp8_ref(q, k, v, [5, 0, 7], 10, 64, STYLE_HALF, static_scales=st)
+    assert np.all(ks2 == np.float32(0.01)) and np.all(vs2 == np.float32(0.02))
