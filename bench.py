@@ -380,6 +380,27 @@ def setup_append(kind):
         info = dict(batch=B, q_heads=Hq, kv_heads=Hkv, head_dim=D, max_seq_len=L, rotary_dim=D,
                     rope="half pairs, base 10000")
         return [[("gqa_append_rope", call)]], alg, info, inp
+    if kind == "gqa-append-fp8":
+        # config 2's shape into an E4M3 cache with per-(token, KV head) scales
+        # computed from the appended rows
+        B, Hq, Hkv, D, L = 32, 32, 8, 128, 4096
+        inp = W.make_gqa_append(B, Hq, Hkv, D, L, cfg=2)
+        q, kn, vn = (to_dev_bf16(x) for x in (inp.q, inp.k_new, inp.v_new))
+        kc = torch.zeros((B, L, Hkv, D), dtype=torch.uint8, device="cuda")
+        vc = torch.zeros_like(kc)
+        ks = torch.zeros((B, L, Hkv), dtype=torch.float32, device="cuda")
+        vs = torch.zeros_like(ks)
+        q_out = torch.empty_like(q)
+        pos = torch.from_numpy(inp.positions).cuda()
+        call = replayed(lambda: da.gqa_append_rope_fp8(q, kn, vn, pos, kc, vc, ks, vs, q_out=q_out))
+        # bytes: q read and written (bf16), k and v rows read (bf16) and written
+        # (codes + one fp32 scale per row), positions
+        alg = dict(cache=2 * B * Hkv * (D * 2 + D + 4), q=2 * B * Hq * D * 2, out=0,
+                   flops=6 * B * (Hq + Hkv) * (D // 2))
+        alg["total"] = alg["cache"] + alg["q"] + 4 * B
+        info = dict(batch=B, q_heads=Hq, kv_heads=Hkv, head_dim=D, max_seq_len=L, rotary_dim=D,
+                    cache="e4m3, scale per (token, KV head) computed", rope="half pairs, base 10000")
+        return [[("gqa_append_rope_fp8", call)]], alg, info, inp
     B, H, L = 64, 128, 4096
     inp = W.make_mla_append(B, H, L, cfg=3)
     qr, kvn = to_dev_bf16(inp.q), to_dev_bf16(inp.k_new)
@@ -435,6 +456,8 @@ def run_gpu(args):
     if args.workload == "append":
         plans.append(("gqa-append", setup_append("gqa-append")))
         plans.append(("mla-append", setup_append("mla-append")))
+    if args.workload == "append-fp8":
+        plans.append(("gqa-append-fp8", setup_append("gqa-append-fp8")))
     n_rot = max(len(p[1][0]) for p in plans)
 
     def step_calls(i):
@@ -579,6 +602,7 @@ def workload_name(w):
             "mla-paged": "deepseek-v3-mla-b64-l4096-paged16",
             "gqa-fp8": "llama3-8b-gqa-b32-l4096-fp8e4m3",
             "gqa-window": "mistral-7b-shape-gqa-b32-l8192-window4096",
+            "append-fp8": "cache append + rope into e4m3: llama3-8b-gqa-b32-l4096",
             "append": "cache append + rope: llama3-8b-gqa-b32-l4096 + deepseek-v3-mla-b64-l4096"}[w]
 
 
@@ -591,6 +615,7 @@ def cpu_baseline(plans, budget_s):
                                   mla_absorbed_ref)
     from oracle.fp8 import gqa_decode_fp8_ref
     from oracle.rope import gqa_append_rope_ref, mla_append_rope_ref
+    from oracle.fp8 import gqa_append_rope_fp8_ref
     import workloads as W
     try:
         from threadpoolctl import threadpool_info
@@ -604,7 +629,7 @@ def cpu_baseline(plans, budget_s):
         if kind.endswith("-paged"):
             inp, pools = inp
         t_kind, n = 0.0, 0
-        B = len(inp.positions) if kind.endswith("-append") else len(inp.seq_lens)
+        B = len(inp.positions) if "-append" in kind else len(inp.seq_lens)
         while t_kind < per_kind_budget and n < B:
             b = n
             if kind == "gqa-paged":
@@ -639,6 +664,13 @@ def cpu_baseline(plans, budget_s):
                 gqa_decode_fp8_ref(*args)
                 dt = time.perf_counter() - t
                 a1 = gqa_alg(1, inp.q.shape[1], inp.k.shape[2], inp.q.shape[2], L, elem=1)
+            elif kind == "gqa-append-fp8":
+                t = time.perf_counter()
+                gqa_append_rope_fp8_ref(inp.f64("q")[b:b + 1], inp.f64("k_new")[b:b + 1],
+                                        inp.f64("v_new")[b:b + 1], inp.positions[b:b + 1], 4096,
+                                        inp.q.shape[2], 0)
+                dt = time.perf_counter() - t
+                a1 = dict(total=alg["total"] // B)
             elif kind in ("gqa-append", "mla-append"):
                 # one sequence per call into a one-page pool (page size 16):
                 # the same rotation and row write, without copying a whole cache
@@ -702,7 +734,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="step",
                     choices=["step", "gqa", "mla", "mla-long", "gqa-ragged", "gqa-paged",
-                             "mla-paged", "gqa-fp8", "append", "gqa-window"])
+                             "mla-paged", "gqa-fp8", "append", "gqa-window",
+                             "append-fp8"])
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle time for the CPU baseline (0 disables)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,

@@ -135,6 +135,9 @@ _SIGNATURES = {
                                          _vp, _vp, ctypes.c_size_t, _vp]),
     "da_gqa_append_rope": (ctypes.c_int, [_GQA_P, ctypes.POINTER(Append), _PAGED_P, _vp, _vp, _vp,
                                           _vp, _vp, _vp, _vp, _vp]),
+    "da_gqa_append_rope_fp8": (ctypes.c_int, [_GQA_P, ctypes.POINTER(Append), _PAGED_P,
+                                              ctypes.POINTER(KvScales), _vp, _vp, _vp, _vp, _vp, _vp,
+                                              _vp, _vp]),
     "da_mla_append_rope": (ctypes.c_int, [_MLA_P, ctypes.POINTER(Append), _PAGED_P, _vp, _vp, _vp,
                                           _vp, _vp, _vp]),
     "da_splitkv_combine": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -750,6 +753,60 @@ def gqa_append_rope(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                                   _ptr(k_new), _ptr(v_new), _ptr(positions), _ptr(k_cache),
                                   _ptr(v_cache), _stream_handle())
     _check(st, "da_gqa_append_rope")
+    return q_out
+
+
+def gqa_append_rope_fp8(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                        positions: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                        k_scale: torch.Tensor, v_scale: torch.Tensor,
+                        rotary_dim: Optional[int] = None, style: str = "half", base: float = 10000.0,
+                        inv_freq: Optional[torch.Tensor] = None,
+                        q_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """gqa_append_rope into an E4M3 cache: q, k_new, v_new bf16; k_cache,
+    v_cache uint8 codes [B, L_max, Hkv, D]; k_scale, v_scale float32
+    [B, L_max, Hkv]. With a nonzero token stride the appended rows' scales are computed
+    (max|x| / 448) and written; with a zero token stride (broadcast per-head
+    scales) they are read. Returns q_out."""
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache),
+                    ("v_cache", v_cache), ("k_scale", k_scale), ("v_scale", v_scale)):
+        _require_cuda(name, t)
+    if any(t.dtype != torch.bfloat16 for t in (q, k_new, v_new)):
+        raise ValueError("q, k_new and v_new must be bfloat16")
+    if k_cache.dtype == torch.float8_e4m3fn:
+        k_cache, v_cache = k_cache.view(torch.uint8), v_cache.view(torch.uint8)
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise ValueError("k_cache and v_cache must hold E4M3 codes (uint8 or float8_e4m3fn)")
+    if v_cache.shape != k_cache.shape or v_cache.stride() != k_cache.stride():
+        raise ValueError("v_cache must have the shape and strides of k_cache")
+    if k_scale.dtype != torch.float32 or v_scale.dtype != torch.float32 or \
+            k_scale.stride() != v_scale.stride() or k_scale.dim() != 3:
+        raise ValueError("k_scale and v_scale must be float32 [B, L_max, Hkv] with one stride set")
+    B, Hq, D = q.shape
+    if k_new.shape != (B, k_cache.shape[2], D) or v_new.shape != k_new.shape or \
+            v_new.stride() != k_new.stride() or k_new.stride(2) != 1:
+        raise ValueError("k_new and v_new must be [B, Hkv, D] with one stride set and a contiguous D axis")
+    _check_positions(positions, B)
+    if q_out is None:
+        q_out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    if q_out.shape != q.shape or q_out.stride() != q.stride() or q_out.dtype != q.dtype:
+        raise ValueError("q_out must match q in shape, strides and dtype")
+    p = GqaParams()
+    p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim = B, Hq, k_cache.shape[2], D
+    p.dtype = DA_DTYPE_FP8_E4M3
+    p.softmax_scale = 1.0 / math.sqrt(D)
+    p.q_stride_b, p.q_stride_h = q.stride(0), q.stride(1)
+    p.kv_stride_t, p.kv_stride_h = k_cache.stride(1), k_cache.stride(2)
+    p.max_seq_len, p.kv_stride_b = k_cache.shape[1], k_cache.stride(0)
+    sc = KvScales()
+    sc.k_scale, sc.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
+    sc.stride_b, sc.stride_t, sc.stride_h = k_scale.stride()
+    ap = _append_desc(D if rotary_dim is None else rotary_dim, style, base, inv_freq,
+                      k_new.stride(0), k_new.stride(1))
+    st = _call("da_gqa_append_rope_fp8", ctypes.byref(p), ctypes.byref(ap), None,
+               ctypes.byref(sc), _ptr(q), _ptr(q_out),
+               _ptr(k_new), _ptr(v_new), _ptr(positions), _ptr(k_cache), _ptr(v_cache),
+               _stream_handle())
+    _check(st, "da_gqa_append_rope_fp8")
     return q_out
 
 

@@ -488,6 +488,47 @@ da_status_t da_gqa_append_rope(const da_gqa_params_t* p, const da_append_t* ap,
   return from_hip(da::launch_gqa_append_rope(a, gqa_kernel_dtype(p), static_cast<hipStream_t>(hip_stream)));
 }
 
+da_status_t da_gqa_append_rope_fp8(const da_gqa_params_t* p, const da_append_t* ap,
+                                   const da_paged_kv_t* pages, const da_kv_scales_t* sc,
+                                   const void* q, void* q_out, const void* k_new, const void* v_new,
+                                   const int32_t* positions, void* k_cache, void* v_cache,
+                                   void* hip_stream) {
+  da_status_t st = check_gqa_params(p);
+  if (st != DA_OK) return st;
+  if (p->dtype != DA_DTYPE_FP8_E4M3) return DA_ERR_INVALID_ARGUMENT;
+  st = check_append(ap, p->head_dim, 2);     // new rows are bf16
+  if (st != DA_OK) return st;
+  if (pages) return DA_ERR_UNSUPPORTED;      // no paged E4M3 caches (decode has none either)
+  if (!sc || !sc->k_scale || !sc->v_scale || !aligned4(sc->k_scale) || !aligned4(sc->v_scale) ||
+      sc->stride_b < 0 || sc->stride_t < 0 || sc->stride_h < 0)
+    return DA_ERR_INVALID_ARGUMENT;
+  if (sc->stride_t != 0 && sc->stride_h == 0) return DA_ERR_UNSUPPORTED;
+  st = check_ptrs16({q, q_out, k_new, v_new, k_cache, v_cache});
+  if (st != DA_OK) return st;
+  if (!positions || !aligned4(positions)) return DA_ERR_INVALID_ARGUMENT;
+  da::AppendArgs a = append_args(ap, pages, positions, p->batch, p->max_seq_len);
+  a.q = q;
+  a.q_out = q_out;
+  a.q_sb = p->q_stride_b;
+  a.q_sh = p->q_stride_h;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.c_sb = p->kv_stride_b;
+  a.c_st = p->kv_stride_t;
+  a.c_sh = p->kv_stride_h;
+  a.q_heads = p->num_q_heads;
+  a.kv_heads = p->num_kv_heads;
+  a.dim = p->head_dim;
+  a.k_scale = const_cast<float*>(sc->k_scale);
+  a.v_scale = const_cast<float*>(sc->v_scale);
+  a.sc_sb = sc->stride_b;
+  a.sc_st = sc->stride_t;
+  a.sc_sh = sc->stride_h;
+  return from_hip(da::launch_gqa_append_rope_fp8(a, static_cast<hipStream_t>(hip_stream)));
+}
+
 da_status_t da_mla_append_rope(const da_mla_params_t* p, const da_append_t* ap,
                                const da_paged_kv_t* pages, const void* q_rope, void* q_rope_out,
                                const void* kv_new, const int32_t* positions, void* kv_cache,

@@ -187,7 +187,104 @@ __global__ __launch_bounds__(kThreads) void mla_append_rope_kernel(AppendArgs a)
   if (valid) pc.finish(a.style, cs);
 }
 
+// fp32 -> OCP E4M3 code, round to nearest even, magnitudes clamped to the
+// largest finite 448 (the format has no infinities). From the format's
+// fields: below 2^-6 the code is a multiple of 2^-9 (subnormal), above it
+// the float's mantissa is rounded to 3 bits at bit 20.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fminf(fabsf(y), 448.f);
+  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.f);        // 0..8 (8 is 2^-6)
+  const uint32_t bits = __float_as_uint(a);
+  const uint32_t r = bits + 0x7ffffu + ((bits >> 20) & 1u);            // RNE to 3 mantissa bits
+  const uint32_t e = ((r >> 23) & 0xffu) - 127u + 7u;                  // biased E4M3 exponent
+  return sign | (e << 3) | ((r >> 20) & 7u);
+}
+
+// GQA append into an E4M3 cache. Rows are rotated (keys) in fp32 as in the
+// bf16 kernel, then each (token, KV head) row of K and of V is quantized:
+// dynamic scales (scale token stride != 0): s = amax(|row|) / 448, written;
+// static scales (token stride 0): s read. Codes = E4M3(x / s) (0 when s is 0).
+// The row's d/8 pieces sit on consecutive lanes, so its amax is a butterfly
+// over those lanes; every lane takes part in it.
+__global__ __launch_bounds__(kThreads) void gqa_append_rope_fp8_kernel(AppendArgs a) {
+  __shared__ float2 cs[kMaxPairs];
+  const int b = blockIdx.y;
+  const int pos = a.positions[b];
+  if (pos < 0 || pos >= a.max_seq_len) return;
+  const int per_row = a.dim / 8;
+  const int item = blockIdx.x * kThreads + threadIdx.x;
+  const int row = item / per_row, j = item - row * per_row;
+  const bool valid = row < a.q_heads + 2 * a.kv_heads;
+  const bool is_q = row < a.q_heads;
+  const bool rot_piece = j < a.rot / 8;
+  const int kv = row - a.q_heads;
+  const bool is_k = kv < a.kv_heads;
+  const int h = is_k ? kv : kv - a.kv_heads;
+  Piece<uint16_t> pc;
+  if (valid) {
+    if (is_q) {
+      const int64_t o = (int64_t)b * a.q_sb + (int64_t)row * a.q_sh;
+      pc.load(static_cast<const uint16_t*>(a.q) + o, static_cast<uint16_t*>(a.q_out) + o, j, rot_piece,
+              a.rot, a.style);
+    } else {
+      const uint16_t* src = static_cast<const uint16_t*>(is_k ? a.k_new : a.v_new) +
+                            (int64_t)b * a.new_sb + (int64_t)h * a.new_sh;
+      pc.load(src, nullptr, j, is_k && rot_piece, a.rot, a.style);
+    }
+  }
+  make_table(a, pos, cs);
+  if (valid && is_q) pc.finish(a.style, cs);
+  // K/V rows: values in fp32 (rotated for keys)
+  float l[4] = {0.f, 0.f, 0.f, 0.f}, hv[4] = {0.f, 0.f, 0.f, 0.f};
+  const bool kv_row = valid && !is_q;
+  if (kv_row) {
+    Quad<uint16_t>::to_f(pc.lo, l);
+    Quad<uint16_t>::to_f(pc.hi, hv);
+    if (pc.rotated) {
+      if (a.style == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) rotate(l[k], hv[k], cs[4 * j + k]);
+      } else {
+        rotate(l[0], l[1], cs[4 * j + 0]);
+        rotate(l[2], l[3], cs[4 * j + 1]);
+        rotate(hv[0], hv[1], cs[4 * j + 2]);
+        rotate(hv[2], hv[3], cs[4 * j + 3]);
+      }
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) amax = fmaxf(amax, fmaxf(fabsf(l[k]), fabsf(hv[k])));
+  for (int m = 1; m < per_row; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+  if (!kv_row) return;
+  const int64_t sc_idx = (int64_t)b * a.sc_sb + (int64_t)pos * a.sc_st + (int64_t)h * a.sc_sh;
+  float* scales = is_k ? a.k_scale : a.v_scale;
+  const bool dynamic = a.sc_st != 0;
+  const float s = dynamic ? amax / 448.f : scales[sc_idx];
+  if (dynamic && j == 0) scales[sc_idx] = s;
+  uint32_t lo = 0, hi = 0;
+  if (s != 0.f) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      lo |= e4m3_code(l[k] / s) << (8 * k);
+      hi |= e4m3_code(hv[k] / s) << (8 * k);
+    }
+  }
+  uint8_t* dst = static_cast<uint8_t*>(is_k ? a.k_cache : a.v_cache) + row_offset(a, b, pos) +
+                 (int64_t)h * a.c_sh;
+  *reinterpret_cast<uint32_t*>(dst + pc.off_lo) = lo;
+  *reinterpret_cast<uint32_t*>(dst + pc.off_hi) = hi;
+}
+
 }  // namespace
+
+hipError_t launch_gqa_append_rope_fp8(const AppendArgs& a, hipStream_t stream) {
+  const int items = (a.q_heads + 2 * a.kv_heads) * (a.dim / 8);
+  const dim3 grid((items + kThreads - 1) / kThreads, a.batch);
+  gqa_append_rope_fp8_kernel<<<grid, kThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
 
 hipError_t launch_gqa_append_rope(const AppendArgs& a, int dtype, hipStream_t stream) {
   const int items = (a.q_heads + 2 * a.kv_heads) * (a.dim / 8);

@@ -121,11 +121,17 @@ struct AppendArgs {
   double log2_base;
   int32_t batch, q_heads, kv_heads, dim;   // dim: GQA head_dim (MLA: unused)
   int32_t rot, style, max_seq_len;         // style 0 half, 1 interleaved
+  // E4M3 caches: scales of K and V rows, (b, t, h) at b*sc_sb + t*sc_st + h*sc_sh;
+  // sc_st != 0: computed per (token, head) and written; sc_st == 0: read
+  float* k_scale;
+  float* v_scale;
+  int64_t sc_sb, sc_st, sc_sh;
 };
 
 // dtype 0 f32, 1 bf16
 hipError_t launch_gqa_append_rope(const AppendArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_mla_append_rope(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_gqa_append_rope_fp8(const AppendArgs& a, hipStream_t stream);
 
 // Entry i of a paged cache's block table, read through the constant address
 // space: the table is not written while a kernel runs, and so read, a load at

@@ -41,6 +41,7 @@ KERNELS = {
     "mla_attend_paged": ("mla_attend_kernel", ("Lb1E", ", true>"), "mla_decode.hip"),
     "mla_attend": ("mla_attend_kernel", (), "mla_decode.hip"),
     "mla_merge_project": ("mla_merge_project_kernel", (), "mla_decode.hip"),
+    "gqa_append_rope_fp8": ("gqa_append_rope_fp8_kernel", (), "append_rope.hip"),
     "gqa_append_rope": ("gqa_append_rope_kernel", (), "append_rope.hip"),
     "mla_append_rope": ("mla_append_rope_kernel", (), "append_rope.hip"),
 }

@@ -414,6 +414,28 @@ DA_EXPORT da_status_t da_gqa_append_rope(const da_gqa_params_t* params, const da
                                          const int32_t* positions, void* k_cache, void* v_cache,
                                          void* hip_stream);
 
+/* GQA append into an E4M3 cache (params->dtype DA_DTYPE_FP8_E4M3; the
+ * quantized cache of arganzheng.life section 6.3, as da_gqa_decode_fp8 reads
+ * it). q, q_out, k_new and v_new are bf16; the new key is rotated in float32
+ * as by da_gqa_append_rope, then each appended (token, KV head) row x of K
+ * and of V is stored as codes E4M3(x / s), rounded to nearest even with
+ * magnitudes clamped to 448 (all codes 0 when s is 0), where s is
+ *  - per (token, KV head), when scales->stride_t != 0: s = max|x| / 448 in
+ *    float32, written to k_scale / v_scale at the row's index (the entry
+ *    point writes through these pointers; stride_h must then be nonzero);
+ *  - read from the arrays, when stride_t == 0 (per-head or per-tensor scales,
+ *    fixed by the caller).
+ * k_cache and v_cache hold one-byte codes (strides in bytes), contiguous
+ * caches only: `pages` must be NULL (paged E4M3 pools: UNSUPPORTED, as for
+ * decode). Errors: as da_gqa_append_rope, plus those of da_gqa_decode_fp8 for
+ * the scales, and UNSUPPORTED for a nonzero token stride with a zero head
+ * stride. */
+DA_EXPORT da_status_t da_gqa_append_rope_fp8(const da_gqa_params_t* params, const da_append_t* append,
+                                             const da_paged_kv_t* pages, const da_kv_scales_t* scales,
+                                             const void* q, void* q_out, const void* k_new,
+                                             const void* v_new, const int32_t* positions,
+                                             void* k_cache, void* v_cache, void* hip_stream);
+
 /* MLA append: q_rope_out[b, h] = RoPE_m(q_rope[b, h]); the cache row (b, m)
  * becomes [kv_new[b, 0:512] ; RoPE_m(kv_new[b, 512:576])].
  *   params   as for da_mla_decode_absorbed (softmax_scale and num_splits unused)

@@ -389,6 +389,34 @@ def test_append_rejects_bad_buffers_and_dtypes():
                                 None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1   # r > 64
 
 
+@needs_lib
+def test_fp8_append_rejects_bad_arguments():
+    L = da.lib()
+
+    def sc(st=8, sh=1, k=FAKE):
+        s = da.KvScales()
+        s.k_scale, s.v_scale = k.value if k is not None else None, FAKE.value
+        s.stride_b, s.stride_t, s.stride_h = 4096 * 8, st, sh
+        return s
+
+    def call(p, scales, pages=None, ap=None):
+        ap = ap or append_desc()
+        return L.da_gqa_append_rope_fp8(ctypes.byref(p), ctypes.byref(ap), pages,
+                                        None if scales is None else ctypes.byref(scales),
+                                        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    f8 = gqa(dtype=da.DA_DTYPE_FP8_E4M3)
+    f8.kv_stride_b, f8.kv_stride_t, f8.kv_stride_h = 4096 * 8 * 128, 8 * 128, 128
+    assert call(gqa(), sc()) == 1                                  # not the fp8 dtype
+    assert call(f8, None) == 1                                     # no scales
+    assert call(f8, sc(k=None)) == 1
+    assert call(f8, sc(st=8, sh=0)) == 2                           # dynamic per-token, shared by heads
+    assert call(f8, sc(st=-8)) == 1
+    pg = da.PagedKv()
+    pg.block_table, pg.page_size, pg.max_blocks_per_seq, pg.page_stride = FAKE.value, 16, 256, 16 * 8 * 128
+    assert call(f8, sc(), pages=ctypes.byref(pg)) == 2             # no paged E4M3 pools
+    assert call(f8, sc(), ap=append_desc(r=12)) == 1
+
+
 def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(da, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(da, "_lib", None)

@@ -22,7 +22,7 @@ def test_more_than_one_gpu_exits_with_a_message():
 
 def test_every_workload_has_a_name():
     for w in ("step", "gqa", "mla", "mla-long", "gqa-ragged", "gqa-paged", "mla-paged", "gqa-fp8",
-              "append", "gqa-window"):
+              "append", "gqa-window", "append-fp8"):
         assert bench.workload_name(w)
 
 
@@ -47,8 +47,10 @@ def test_cpu_baseline_on_contiguous_and_paged_plans():
              ("gqa-paged", (None, None, None, (g, dict(k_pool=kp, v_pool=vp, table=tg)))),
              ("mla-paged", (None, None, None, (m, dict(pool=pool, table=tm)))),
              ("gqa-append", (None, dict(total=2000), None, W.make_gqa_append(2, 8, 2, 128, 4096))),
-             ("mla-append", (None, dict(total=2000), None, W.make_mla_append(2, 16, 4096)))]
+             ("mla-append", (None, dict(total=2000), None, W.make_mla_append(2, 16, 4096))),
+             ("gqa-append-fp8", (None, dict(total=2000), None, W.make_gqa_append(2, 8, 2, 128, 4096)))]
     res = bench.cpu_baseline(plans, budget_s=4.0)
     assert res["kind"] == "oracle" and res["value"] > 0 and res["cores"] >= 1
-    for kind in ("gqa", "mla", "gqa-paged", "mla-paged", "gqa-fp8", "gqa-append", "mla-append"):
+    for kind in ("gqa", "mla", "gqa-paged", "mla-paged", "gqa-fp8", "gqa-append", "mla-append",
+                 "gqa-append-fp8"):
         assert f"{kind}: 2 of 2 sequences" in res["sample"]

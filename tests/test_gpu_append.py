@@ -314,3 +314,86 @@ def test_error_codes_with_real_buffers():
         da.gqa_append_rope(q, kn, kn, pos, kc, kc.clone(), style="diagonal")
     with pytest.raises(ValueError):
         da.gqa_append_rope(q, kn, kn, pos.long(), kc, kc.clone())
+
+
+# ----------------------------------------------------------------------------
+# E4M3 caches
+# ----------------------------------------------------------------------------
+
+def e4m3_step(y):
+    """Spacing of E4M3 values around |y|."""
+    a = np.abs(y)
+    return np.where(a < 2.0 ** -6, 2.0 ** -9, np.exp2(np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 3))
+
+
+@pytest.mark.parametrize("static", [False, True])
+@pytest.mark.parametrize("style,r", [("half", None), ("interleaved", 64)])
+def test_fp8_append(static, style, r):
+    from oracle.fp8 import e4m3_to_float, gqa_append_rope_fp8_ref
+    B, Hq, Hkv, D, L = 6, 16, 4, 128, 300
+    announce(f"gqa append fp8 static{static} {style} r{r}")
+    inp = W.make_gqa_append(B, Hq, Hkv, D, L, seed=41, positions=[0, 299, -1, 150, 300, 7])
+    rr = D if r is None else r
+    q, kn, vn = (bf16_tensor(x) for x in (inp.q, inp.k_new, inp.v_new))
+    pos = torch.from_numpy(inp.positions).cuda()
+    kc = torch.full((B, L, Hkv, D), 0x11, dtype=torch.uint8, device="cuda")
+    vc = kc.clone()
+    k0 = kc.clone()
+    if static:
+        sk = np.array([0.01, 0.02, 0.005, 0.03], np.float32)
+        sv = np.array([0.02, 0.01, 0.04, 0.008], np.float32)
+        ks = torch.from_numpy(sk).cuda().expand(B, L, Hkv)
+        vs = torch.from_numpy(sv).cuda().expand(B, L, Hkv)
+        static_np = (np.broadcast_to(sk, (B, Hkv)), np.broadcast_to(sv, (B, Hkv)))
+    else:
+        ks = torch.full((B, L, Hkv), -1.0, device="cuda")
+        vs = ks.clone()
+        static_np = None
+    ks0, vs0 = ks.clone(), vs.clone()
+    q_out = da.gqa_append_rope_fp8(q, kn, vn, pos, kc, vc, ks, vs, rotary_dim=rr, style=style)
+    torch.cuda.synchronize()
+    qf, knf, vnf = inp.f64("q"), inp.f64("k_new"), inp.f64("v_new")
+    q_rot, k_rot, kcode, ksc, vcode, vsc, written = gqa_append_rope_fp8_ref(
+        qf, knf, vnf, inp.positions, L, rr, STYLES[style], static_scales=static_np)
+    assert_rotated(host_f64(q_out)[written], qf[written], q_rot[written], rr, STYLES[style], "bf16", "q")
+    kc_h, vc_h = kc.cpu().numpy(), vc.cpu().numpy()
+    ks_h, vs_h = ks.cpu().numpy(), vs.cpu().numpy()
+    mask = np.zeros((B, L), bool)
+    for b in np.nonzero(written)[0]:
+        p = int(inp.positions[b])
+        mask[b, p] = True
+        # values: the same float32 decision on both sides, so codes and scales are equal
+        assert np.array_equal(vc_h[b, p], vcode[b]), f"v codes of row {b}"
+        assert np.array_equal(vs_h[b, p], vsc[b]), f"v scales of row {b}"
+        # keys: rotated in float32 by the kernel, in float64 by the oracle; the
+        # scale agrees to float32 rounding and each code is a nearest E4M3 value
+        np.testing.assert_allclose(ks_h[b, p], ksc[b], rtol=2.0 ** -20)
+        y = np.clip(k_rot[b] / ksc[b][:, None].astype(np.float64), -448.0, 448.0)   # clamped codes
+        dec = e4m3_to_float(kc_h[b, p])
+        assert np.all(np.abs(dec - y) <= 0.5 * e4m3_step(y) * (1 + 1e-3) + 1e-6 * np.abs(y)), f"k codes of row {b}"
+    others = ~mask
+    assert np.array_equal(kc_h[others], k0.cpu().numpy()[others]) and np.array_equal(vc_h[others], k0.cpu().numpy()[others])
+    if not static:
+        assert np.array_equal(ks_h[others], ks0.cpu().numpy()[others])
+        assert np.array_equal(vs_h[others], vs0.cpu().numpy()[others])
+
+
+def test_fp8_append_then_decode():
+    from oracle.fp8 import dequantize_ref
+    announce("gqa append fp8 then decode")
+    B, Hq, Hkv, D, L = 3, 32, 8, 128, 500
+    cache = W.make_gqa_fp8(B, Hq, Hkv, D, [L] * B, seed=42, pad_nan=False)
+    lens = np.array([500, 1, 257], np.int32)
+    app = W.make_gqa_append(B, Hq, Hkv, D, L, seed=43, positions=lens - 1)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    kc, vc, ks, vs = d(cache.k), d(cache.v), d(cache.k_scale), d(cache.v_scale)
+    q_rot = da.gqa_append_rope_fp8(bf16_tensor(app.q), bf16_tensor(app.k_new), bf16_tensor(app.v_new),
+                                   d(app.positions), kc, vc, ks, vs)
+    out, lse = da.gqa_decode_fp8(q_rot, kc, vc, ks, vs, d(lens), 1 / np.sqrt(D))
+    torch.cuda.synchronize()
+    # the oracle decodes the cache the kernel left (codes and scales as written)
+    kd = dequantize_ref(kc.cpu().numpy(), ks.cpu().numpy())
+    vd = dequantize_ref(vc.cpu().numpy(), vs.cpu().numpy())
+    ro, rl = gqa_decode_ref(host_f64(q_rot), kd, vd, lens, 1 / np.sqrt(D))
+    err = np.abs(out.cpu().numpy() - ro).max(axis=-1) / np.abs(ro).max(axis=-1)
+    assert err.max() <= 1e-2 and np.abs(lse.cpu().numpy() - rl).max() <= 1e-3
