@@ -99,10 +99,26 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_mfma_kernel(GqaArgs a) {
 
   const int GH = a.heads_per_block;
   const int split = blockIdx.x;
-  const int b = a.order_by_length ? longest_first<kThreads>(a.seq_lens, a.batch, blockIdx.z) : blockIdx.z;
+  // Per-(token, KV head) fp8 scales stored token-major put the scales of a
+  // token's KV heads in one 32-byte sector. Workgroups are dealt to the 8
+  // XCDs round-robin by linear id, so with the natural order a sequence's KV
+  // heads land on 8 different XCDs and each fetches the whole sector for its
+  // 4 bytes. With one split per sequence and a multiple of 8 sequences, the
+  // (head, sequence) pairs are renumbered so that all workgroups of a
+  // sequence share an XCD (linear id mod 8) and its L2 serves the sector to
+  // the others.
+  int gy = blockIdx.y, gz = blockIdx.z;
+  if (kFp8 && a.sc_st != 0 && a.sc_sh != 0 && gridDim.x == 1 && !a.order_by_length &&
+      (gridDim.z & 7) == 0) {
+    const int lin = blockIdx.y + gridDim.y * blockIdx.z;
+    const int q = lin >> 3;
+    gy = q % gridDim.y;
+    gz = (lin & 7) + 8 * (q / gridDim.y);
+  }
+  const int b = a.order_by_length ? longest_first<kThreads>(a.seq_lens, a.batch, gz) : gz;
   const int n_sub = a.group / GH;
-  const int kvh = blockIdx.y / n_sub;
-  const int h0 = kvh * a.group + (blockIdx.y % n_sub) * GH;
+  const int kvh = gy / n_sub;
+  const int h0 = kvh * a.group + (gy % n_sub) * GH;
   const int L = a.seq_lens ? min(max(a.seq_lens[b], 0), a.max_seq_len) : a.max_seq_len;
   // sliding window: rows before w0 are masked; splits start at w0 (paged: at
   // the 16-row boundary below it, so steps stay inside pages)
