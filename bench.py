@@ -9,8 +9,14 @@ One step is one pass of the whole hot path on synthetic inputs:
     split-KV latent attention, merge + W_UV projection).
 Other workloads (--workload): each path alone, long-context MLA, ragged
 MHA, GQA / MLA over paged caches (pools of 16-row pages in a seeded random
-physical order, read through a block table), and GQA over an FP8 (E4M3)
-cache with one fp32 scale per (token, KV head) for K and for V.
+physical order, read through a block table), GQA over an FP8 (E4M3)
+cache with one fp32 scale per (token, KV head) for K and for V, sliding-window
+GQA (8192 cached rows, window 4096), and the step before decode: appending the
+new token's rows with RoPE (bf16 GQA and MLA caches, `append`; an E4M3 GQA
+cache, `append-fp8`). The append kernels take a few microseconds, less than
+the Python binding's per-call checks, so those steps replay the recorded C
+calls, and their roofline pass is queued behind a GPU spin so the launches
+are issued ahead of the GPU.
 Inputs are resident in HBM before timing starts. The default warm-up (200
 steps, about 40 ms) outlasts the board's power-management transient: in a
 kernel trace of this step, the first few milliseconds of back-to-back steps
