@@ -785,6 +785,9 @@ def gqa_append_rope_fp8(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tenso
     if k_new.shape != (B, k_cache.shape[2], D) or v_new.shape != k_new.shape or \
             v_new.stride() != k_new.stride() or k_new.stride(2) != 1:
         raise ValueError("k_new and v_new must be [B, Hkv, D] with one stride set and a contiguous D axis")
+    if k_cache.shape[0] != B or k_cache.stride(3) != 1 or \
+            k_scale.shape != (B, k_cache.shape[1], k_cache.shape[2]) or v_scale.shape != k_scale.shape:
+        raise ValueError("k_cache must be [B, L_max, Hkv, D] (contiguous D) and the scales [B, L_max, Hkv]")
     _check_positions(positions, B)
     if q_out is None:
         q_out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
