@@ -131,3 +131,27 @@ def gqa_append_rope_fp8_ref(q, k_new, v_new, positions, max_seq_len: int, rotary
     k_codes, k_sc = quantize_rows_ref(k_rot, ks)
     v_codes, v_sc = quantize_rows_ref(np.asarray(v_new, np.float64), vs)
     return q_rot, k_rot, k_codes, k_sc, v_codes, v_sc, written
+
+
+def gqa_decode_fp8_paged_ref(q, k_pool, v_pool, k_scale_pool, v_scale_pool, block_table,
+                             page_size: int, seq_lens, scale: float, window: int = 0):
+    """GQA decode over paged E4M3 pools: codes [num_pages, page_size, Hkv, D]
+    and scales [num_pages, page_size, Hkv], both addressed through one block
+    table ("Attention variants and KV cache" sections 6.1 and 6.3): token t of
+    sequence b is row t mod page_size of page block_table[b, t // page_size].
+    The attended rows (all, or the last `window`) are gathered in logical
+    order, decoded and scaled, then attended as by gqa_decode_ref."""
+    from oracle.attention import gqa_decode_ref
+    seq_lens = np.asarray(seq_lens, np.int64)
+    B = q.shape[0]
+    L = int(max(1, seq_lens.max(initial=0)))
+    k = np.zeros((B, L) + k_pool.shape[2:])
+    v = np.zeros((B, L) + v_pool.shape[2:])
+    for b in range(B):
+        Lb = int(seq_lens[b])
+        lo = max(0, Lb - window) if window > 0 else 0
+        for t in range(lo, Lb):
+            page, r = int(block_table[b][t // page_size]), t % page_size
+            k[b, t] = dequantize_ref(k_pool[page, r], k_scale_pool[page, r])
+            v[b, t] = dequantize_ref(v_pool[page, r], v_scale_pool[page, r])
+    return gqa_decode_ref(q, k, v, seq_lens, scale, window)

@@ -793,3 +793,35 @@ def test_fp8_append_oracle_scales_and_codes():
     st = (np.full((3, 2), 0.01), np.full((3, 2), 0.02))
     _, _, kc2, ks2, _, vs2, _ = gqa_append_rope_fp8_ref(q, k, v, [5, 0, 7], 10, 64, STYLE_HALF, static_scales=st)
     assert np.all(ks2 == np.float32(0.01)) and np.all(vs2 == np.float32(0.02))
+
+
+def test_fp8_paged_oracle_equals_the_contiguous_one():
+    from oracle.fp8 import gqa_decode_fp8_paged_ref, gqa_decode_fp8_ref
+    B, L, Hkv, D, ps = 2, 70, 2, 16, 32
+    q = rand(B, 4, D)
+    codes_k = RNG.integers(0, 126, size=(B, L, Hkv, D)).astype(np.uint8)
+    codes_v = RNG.integers(0, 126, size=(B, L, Hkv, D)).astype(np.uint8)
+    sk, sv = RNG.uniform(0.5, 2, (B, L, Hkv)), RNG.uniform(0.5, 2, (B, L, Hkv))
+    lens = [70, 40]
+    table = np.array([[4, 0, 2], [-1, 3, -1]])         # sequence 1 only attends its window
+    pk = np.full((5, ps, Hkv, D), 0x7F, np.uint8)
+    pv = pk.copy()
+    psk, psv = np.full((5, ps, Hkv), np.nan), np.full((5, ps, Hkv), np.nan)
+    for b, Lb in enumerate(lens):
+        for t in range(Lb):
+            page = table[b, t // ps]
+            if page < 0:
+                continue
+            pk[page, t % ps], pv[page, t % ps] = codes_k[b, t], codes_v[b, t]
+            psk[page, t % ps], psv[page, t % ps] = sk[b, t], sv[b, t]
+    w = 8                                                 # rows 32..39 of sequence 1 lie on page 3
+    for win in (0, w):
+        lens_used = lens if win == 0 else lens
+        want = gqa_decode_fp8_ref(q, codes_k, codes_v, sk, sv, lens_used, 0.3, window=win)
+        if win == 0:   # sequence 1's first block is released: compare sequence 0 only
+            got = gqa_decode_fp8_paged_ref(q[:1], pk, pv, psk, psv, table[:1], ps, lens[:1], 0.3)
+            np.testing.assert_allclose(got[0], want[0][:1], atol=1e-13)
+        else:
+            got = gqa_decode_fp8_paged_ref(q, pk, pv, psk, psv, table, ps, lens, 0.3, window=win)
+            np.testing.assert_allclose(got[0], want[0], atol=1e-13)
+            np.testing.assert_allclose(got[1], want[1], atol=1e-13)
