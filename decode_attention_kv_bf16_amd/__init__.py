@@ -140,6 +140,8 @@ _SIGNATURES = {
                                               _vp, _vp]),
     "da_mla_append_rope": (ctypes.c_int, [_MLA_P, ctypes.POINTER(Append), _PAGED_P, _vp, _vp, _vp,
                                           _vp, _vp, _vp]),
+    "da_gqa_decode_fp8_paged": (ctypes.c_int, [_GQA_P, _PAGED_P, ctypes.POINTER(KvScales), _vp, _vp, _vp,
+                                               _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "da_splitkv_combine": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]),
     "da_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -401,6 +403,66 @@ def gqa_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
 # ----------------------------------------------------------------------------
 # paged pools
 # ----------------------------------------------------------------------------
+
+def gqa_decode_fp8_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                         k_scale: torch.Tensor, v_scale: torch.Tensor, block_table: torch.Tensor,
+                         page_size: int, seq_lens: torch.Tensor, max_seq_len: Optional[int] = None,
+                         softmax_scale: Optional[float] = None, num_splits: int = 0,
+                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                         window: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """gqa_decode_fp8 over paged E4M3 pools: k_pool, v_pool [num_pages,
+    page_size, Hkv, D] uint8 codes (page_size >= 32); k_scale, v_scale
+    float32 [num_pages, page_size, Hkv] (or a per-head [Hkv] vector expanded
+    with zero strides); block_table [B, max_blocks] int32; seq_lens [B] int32."""
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("k_scale", k_scale),
+                    ("v_scale", v_scale)):
+        _require_cuda(name, t)
+    if q.dtype != torch.bfloat16:
+        raise ValueError("q must be bfloat16")
+    if k_pool.dtype == torch.float8_e4m3fn:
+        k_pool, v_pool = k_pool.view(torch.uint8), v_pool.view(torch.uint8)
+    if k_pool.dtype != torch.uint8 or v_pool.dtype != torch.uint8:
+        raise ValueError("k_pool and v_pool must hold E4M3 codes (uint8 or float8_e4m3fn)")
+    if v_pool.shape != k_pool.shape or v_pool.stride() != k_pool.stride() or k_pool.stride(3) != 1:
+        raise ValueError("v_pool must have the shape and strides of k_pool, with a contiguous D axis")
+    n_pages, ps, Hkv, D = k_pool.shape
+    for name, sc in (("k_scale", k_scale), ("v_scale", v_scale)):
+        if sc.dtype != torch.float32 or sc.shape != (n_pages, ps, Hkv):
+            raise ValueError(f"{name} must be float32 of shape [num_pages, page_size, Hkv]")
+    if k_scale.stride() != v_scale.stride():
+        raise ValueError("k_scale and v_scale must share strides")
+    B, Hq, Dq = q.shape
+    if Dq != D or q.stride(2) != 1:
+        raise ValueError("q and the pools disagree, or the head_dim axis is not contiguous")
+    _check_seq_lens(seq_lens, B)
+    pg = paged_kv(block_table, page_size, k_pool)
+    if block_table.shape[0] != B:
+        raise ValueError("block_table must have one row per sequence")
+    p = GqaParams()
+    p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim = B, Hq, Hkv, D
+    p.max_seq_len = block_table.shape[1] * page_size if max_seq_len is None else int(max_seq_len)
+    p.dtype = DA_DTYPE_FP8_E4M3
+    p.softmax_scale = (1.0 / math.sqrt(D)) if softmax_scale is None else float(softmax_scale)
+    p.q_stride_b, p.q_stride_h = q.stride(0), q.stride(1)
+    p.kv_stride_b, p.kv_stride_t, p.kv_stride_h = 0, k_pool.stride(1), k_pool.stride(2)
+    p.num_splits = int(num_splits)
+    p.sliding_window = int(window)
+    sc = KvScales()
+    sc.k_scale, sc.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
+    sc.stride_b, sc.stride_t, sc.stride_h = k_scale.stride()
+    L = lib()
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ws_bytes = L.da_gqa_decode_workspace_size(ctypes.byref(p))
+    ws = _workspace(ws_bytes, q.device)
+    st = L.da_gqa_decode_fp8_paged(ctypes.byref(p), ctypes.byref(pg), ctypes.byref(sc), _ptr(q),
+                                   _ptr(k_pool), _ptr(v_pool), _ptr(seq_lens), _ptr(out), _ptr(lse),
+                                   _ptr(ws), ws_bytes, _stream_handle())
+    _check(st, "da_gqa_decode_fp8_paged")
+    return out, lse
+
 
 def paged_kv(block_table: torch.Tensor, page_size: int, pool: torch.Tensor) -> PagedKv:
     """The paging descriptor for a pool [num_pages, page_size, ...] and a

@@ -125,7 +125,8 @@ GqaPlan plan_gqa(const da_gqa_params_t* p, int align = 1) {
   //    CU, as many splits as fit in one round (where that shape is built).
   // Chunks stay at least 128 rows.
   const int64_t cus = device_cu_count();
-  const bool wide = da::gqa_wide_supported(gqa_kernel_dtype(p), pl.heads_per_block);
+  // (paged fp8 pools run on the matrix-core kernel only: no 16-wave plans)
+  const bool wide = da::gqa_wide_supported(gqa_kernel_dtype(p), pl.heads_per_block) && align < 32;
   int64_t s;
   if (p->num_splits > 0) {
     s = p->num_splits;
@@ -146,10 +147,11 @@ GqaPlan plan_gqa(const da_gqa_params_t* p, int align = 1) {
   }
   // Rows a sequence can attend: all L_max, or with a sliding window w the
   // rows [L - w, L), whose start the kernels round down to a multiple of 16
-  // on paged pools: at most w + 15 rows (the same bound for both, so that the
-  // workspace queries, which do not know about paging, cover paged calls).
-  const int64_t len = p->sliding_window > 0 && p->sliding_window + 15 < p->max_seq_len
-                          ? p->sliding_window + 15 : p->max_seq_len;
+  // (32 for fp8) on paged pools: at most w + 31 rows (the same bound for
+  // both, so that the workspace queries, which do not know about paging,
+  // cover paged calls).
+  const int64_t len = p->sliding_window > 0 && p->sliding_window + 31 < p->max_seq_len
+                          ? p->sliding_window + 31 : p->max_seq_len;
   if (p->num_splits == 0) {
     const int64_t s_max = ceil_div(len, 128);
     s = s < s_max ? s : s_max;
@@ -374,7 +376,8 @@ da_status_t gqa_decode_impl(const da_gqa_params_t* p, const da_paged_kv_t* pages
   da_status_t st = check_gqa_params(p);
   if (st != DA_OK) return st;
   if (pages) {
-    st = check_paged(pages, p->max_seq_len, p->dtype == DA_DTYPE_BF16 ? 2 : 4);
+    st = check_paged(pages, p->max_seq_len,
+                     p->dtype == DA_DTYPE_F32 ? 4 : p->dtype == DA_DTYPE_BF16 ? 2 : 1);
     if (st != DA_OK) return st;
   }
   if (scales) {
@@ -385,8 +388,10 @@ da_status_t gqa_decode_impl(const da_gqa_params_t* p, const da_paged_kv_t* pages
   }
   st = check_gqa_buffers(q, k_cache, v_cache, seq_lens, out, lse);
   if (st != DA_OK) return st;
-  // paged calls split on multiples of 16 rows (a step never straddles a page)
-  const GqaPlan pl = plan_gqa(p, pages ? 16 : 1);
+  // paged calls split on multiples of 16 rows (32 for fp8), so that a step
+  // never straddles a page
+  const bool fp8 = p->dtype == DA_DTYPE_FP8_E4M3;
+  const GqaPlan pl = plan_gqa(p, pages ? (fp8 ? 32 : 16) : 1);
   if (pl.workspace > 0) {
     if (!workspace || workspace_bytes < pl.workspace) return DA_ERR_WORKSPACE_TOO_SMALL;
     if (!aligned16(workspace)) return DA_ERR_INVALID_ARGUMENT;
@@ -402,6 +407,7 @@ da_status_t gqa_decode_impl(const da_gqa_params_t* p, const da_paged_kv_t* pages
   }
   a.out = out;
   a.lse = lse;
+  if (pages && fp8 && !da::gqa_mfma_supported(a, 2, p->head_dim)) return DA_ERR_UNSUPPORTED;
   if (pl.splits > 1) {
     a.part_out = reinterpret_cast<float*>(workspace);
     a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.part_out_bytes);
@@ -557,7 +563,12 @@ da_status_t da_mla_append_rope(const da_mla_params_t* p, const da_append_t* ap,
 
 size_t da_gqa_decode_workspace_size(const da_gqa_params_t* p) {
   if (check_gqa_params(p) != DA_OK) return 0;
-  return plan_gqa(p).workspace;
+  size_t ws = plan_gqa(p).workspace;
+  if (p->dtype == DA_DTYPE_FP8_E4M3) {   // paged fp8 pools plan without 16-wave shapes
+    const size_t paged = plan_gqa(p, 32).workspace;
+    ws = paged > ws ? paged : ws;
+  }
+  return ws;
 }
 
 int32_t da_gqa_decode_num_splits(const da_gqa_params_t* p) {
@@ -612,6 +623,20 @@ da_status_t da_gqa_decode_fp8(const da_gqa_params_t* p, const da_kv_scales_t* sc
                               void* hip_stream) {
   if (!p || p->dtype != DA_DTYPE_FP8_E4M3 || !scales) return DA_ERR_INVALID_ARGUMENT;
   return gqa_decode_impl(p, nullptr, scales, q, k_cache, v_cache, seq_lens, out, lse, workspace,
+                         workspace_bytes, hip_stream);
+}
+
+da_status_t da_gqa_decode_fp8_paged(const da_gqa_params_t* p, const da_paged_kv_t* pages,
+                                    const da_kv_scales_t* scales, const void* q, const void* k_pool,
+                                    const void* v_pool, const int32_t* seq_lens, float* out,
+                                    float* lse, void* workspace, size_t workspace_bytes,
+                                    void* hip_stream) {
+  if (!p || p->dtype != DA_DTYPE_FP8_E4M3 || !scales || !pages) return DA_ERR_INVALID_ARGUMENT;
+  // 32-token steps inside one page; scales that do not vary with the row are
+  // per head (a per-page scale has no meaning for the method)
+  if (pages->page_size < 32) return DA_ERR_UNSUPPORTED;
+  if (scales->stride_t == 0 && scales->stride_b != 0) return DA_ERR_UNSUPPORTED;
+  return gqa_decode_impl(p, pages, scales, q, k_pool, v_pool, seq_lens, out, lse, workspace,
                          workspace_bytes, hip_stream);
 }
 

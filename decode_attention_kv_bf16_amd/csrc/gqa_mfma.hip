@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_mfma_kernel(GqaArgs a) {
   // sliding window: rows before w0 are masked; splits start at w0 (paged: at
   // the 16-row boundary below it, so steps stay inside pages)
   const int w0 = a.window > 0 ? max(L - a.window, 0) : 0;
-  const int t_begin = (a.page_shift > 0 ? (w0 & ~15) : w0) + split * a.chunk;
+  const int t_begin = (a.page_shift > 0 ? (w0 & ~(kTok - 1)) : w0) + split * a.chunk;
   const int t_end = min(L, t_begin + a.chunk);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -174,8 +174,11 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_mfma_kernel(GqaArgs a) {
   const int64_t kv_b = paged ? 0 : (int64_t)b * a.kv_sb;
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + (kv_b + kvh * a.kv_sh) * kEsz;
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v) + (kv_b + kvh * a.kv_sh) * kEsz;
-  const float* ksc = kFp8 ? a.k_scale + b * a.sc_sb + kvh * a.sc_sh : nullptr;
-  const float* vsc = kFp8 ? a.v_scale + b * a.sc_sb + kvh * a.sc_sh : nullptr;
+  // fp8 scales: (b, t, h) at b sc_sb + t sc_st + h sc_sh; on paged pools the
+  // scale arrays are paged like the codes: (page, row, h) at page sc_sb +
+  // row sc_st + h sc_sh
+  const float* ksc = kFp8 ? a.k_scale + (paged ? 0 : b * a.sc_sb) + kvh * a.sc_sh : nullptr;
+  const float* vsc = kFp8 ? a.v_scale + (paged ? 0 : b * a.sc_sb) + kvh * a.sc_sh : nullptr;
 
   // Both K and V of a step go HBM -> LDS by whole rows (lane l of copy k
   // fills LDS byte k*1024 + 16 l: row R, physical chunk pc, from logical
@@ -238,8 +241,12 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_mfma_kernel(GqaArgs a) {
       // (an empty range reads as zero without a memory access), so that
       // every step still counts kOps operations.
       const uint32_t srec = a.sc_st == 0 ? 0u : (uint32_t)(((valid - 1) * a.sc_st + 1) * 4);
-      const __amdgpu_buffer_rsrc_t ks = make_raw_rsrc(ksc + (int64_t)t0 * a.sc_st, srec);
-      const __amdgpu_buffer_rsrc_t vs = make_raw_rsrc(vsc + (int64_t)t0 * a.sc_st, srec);
+      int64_t s0 = (int64_t)t0 * a.sc_st;
+      if (paged)   // the step's page (row0 above has loaded its table entry)
+        s0 = (int64_t)__builtin_amdgcn_readlane(pages, i & 63) * a.sc_sb +
+             (int64_t)(t0 & ((1 << a.page_shift) - 1)) * a.sc_st;
+      const __amdgpu_buffer_rsrc_t ks = make_raw_rsrc(ksc + s0, srec);
+      const __amdgpu_buffer_rsrc_t vs = make_raw_rsrc(vsc + s0, srec);
       buffer_load_to_lds4(ks, soff, dst + 2 * kPartB);
       buffer_load_to_lds4(vs, soff, dst + 2 * kPartB + 256);
     }
@@ -502,8 +509,10 @@ hipError_t launch_t(const GqaArgs& a, hipStream_t st) {
 }  // namespace
 
 bool gqa_mfma_supported(const GqaArgs& a, int dtype, int head_dim) {
-  // paged pools: bf16 only (16-token steps, each inside one page)
-  return (dtype == 1 || (dtype == 2 && a.page_shift == 0)) && (head_dim == 64 || head_dim == 128) &&
+  // paged pools: each step inside one page (bf16 16-token steps; fp8
+  // 32-token steps need pages of at least 32 rows)
+  return (dtype == 1 || (dtype == 2 && (a.page_shift == 0 || a.page_shift >= 5))) &&
+         (head_dim == 64 || head_dim == 128) &&
          (a.waves_per_block == 4 || a.waves_per_block == 8) && a.heads_per_block <= 16;
 }
 

@@ -342,7 +342,8 @@ typedef struct {
  * same params. Errors: as da_gqa_decode, and INVALID_ARGUMENT for another
  * dtype, a NULL `scales` or scale pointer, a misaligned scale pointer or a
  * negative scale stride. da_gqa_decode, da_gqa_decode_split_pass and
- * da_gqa_decode_paged reject DA_DTYPE_FP8_E4M3 (they have no scales). */
+ * da_gqa_decode_paged reject DA_DTYPE_FP8_E4M3 (they have no scales); paged
+ * E4M3 pools go through da_gqa_decode_fp8_paged. */
 DA_EXPORT da_status_t da_gqa_decode_fp8(const da_gqa_params_t* params, const da_kv_scales_t* scales,
                                         const void* q, const void* k_cache, const void* v_cache,
                                         const int32_t* seq_lens, float* out, float* lse,
@@ -449,6 +450,24 @@ DA_EXPORT da_status_t da_mla_append_rope(const da_mla_params_t* params, const da
                                          void* q_rope_out, const void* kv_new,
                                          const int32_t* positions, void* kv_cache,
                                          void* hip_stream);
+
+/* da_gqa_decode_fp8 over paged E4M3 pools: k_pool, v_pool [num_pages,
+ * page_size, Hkv, D] codes (strides in bytes) and scales paged the same way:
+ * the scale of row r of page P for KV head h is at P*stride_b + r*stride_t +
+ * h*stride_h (stride_b is the scales' page stride), or one scale per head
+ * (stride_b = stride_t = 0). One block table serves codes and scales
+ * (arganzheng.life sections 6.1 and 6.3). Pages hold at least 32 rows (the
+ * kernel's fp8 steps are 32 tokens inside one page); splits start on
+ * multiples of 32 rows. Workspace as da_gqa_decode_workspace_size for the
+ * same params. Errors: as da_gqa_decode_fp8 and da_gqa_decode_paged, and
+ * UNSUPPORTED for pages of fewer than 32 rows or scales that vary by page
+ * only (stride_t = 0 with stride_b != 0). */
+DA_EXPORT da_status_t da_gqa_decode_fp8_paged(const da_gqa_params_t* params, const da_paged_kv_t* pages,
+                                              const da_kv_scales_t* scales, const void* q,
+                                              const void* k_pool, const void* v_pool,
+                                              const int32_t* seq_lens, float* out, float* lse,
+                                              void* workspace, size_t workspace_bytes,
+                                              void* hip_stream);
 
 /* ------------------------------------------------------------------------ */
 /* Split-KV merge                                                            */

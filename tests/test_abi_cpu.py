@@ -417,6 +417,29 @@ def test_fp8_append_rejects_bad_arguments():
     assert call(f8, sc(), ap=append_desc(r=12)) == 1
 
 
+@needs_lib
+def test_fp8_paged_rejects_small_pages_and_per_page_scales():
+    L = da.lib()
+    f8 = gqa(dtype=da.DA_DTYPE_FP8_E4M3)
+    f8.kv_stride_b, f8.kv_stride_t, f8.kv_stride_h = 0, 8 * 128, 128
+
+    def call(ps=32, sb=32 * 8, st=8, p=f8, pages=True, scales=True):
+        pg = da.PagedKv()
+        pg.block_table, pg.page_size, pg.max_blocks_per_seq, pg.page_stride = FAKE.value, ps, 4096, ps * 8 * 128
+        s = da.KvScales()
+        s.k_scale, s.v_scale = FAKE.value, FAKE.value
+        s.stride_b, s.stride_t, s.stride_h = sb, st, 1
+        return L.da_gqa_decode_fp8_paged(ctypes.byref(p), ctypes.byref(pg) if pages else None,
+                                         ctypes.byref(s) if scales else None, FAKE, FAKE, FAKE, FAKE,
+                                         FAKE, FAKE, FAKE, 1 << 40, None)
+    assert call(ps=16) == 2                 # fp8 steps are 32 rows
+    assert call(st=0) == 2                  # scales varying by page only
+    assert call(pages=False) == 1
+    assert call(scales=False) == 1
+    assert call(p=gqa()) == 1               # not the fp8 dtype
+    assert call(ps=24) == 2
+
+
 def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(da, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(da, "_lib", None)

@@ -146,3 +146,87 @@ def test_error_codes_with_real_buffers():
         da.gqa_decode_fp8(q, k, k, s[:, :8], s)                 # scale shape
     out, lse = da.gqa_decode_fp8(q, k, k, s, s)                 # all-zero codes: mean of zeros
     assert torch.all(out == 0) and torch.allclose(lse, torch.full_like(lse, float(np.log(16))))
+
+
+# ----------------------------------------------------------------------------
+# paged E4M3 pools ("Attention variants and KV cache", sections 6.1 and 6.3)
+# ----------------------------------------------------------------------------
+
+def paged_fp8(inp, ps, seed, window=0):
+    """Codes and scales paged through one table (seeded random page order);
+    unused pool rows hold the NaN code and NaN scales, and with a window the
+    pages wholly before the window's first 32-row step are released (entry
+    -1, contents NaN)."""
+    lens = inp.seq_lens
+    table, n_pages = W.make_block_table(lens, ps, seed=seed)
+    kp = W.paginate(inp.k, lens, table, n_pages, ps, W.FP8_NAN_CODE)
+    vp = W.paginate(inp.v, lens, table, n_pages, ps, W.FP8_NAN_CODE)
+    ksp = W.paginate(inp.k_scale, lens, table, n_pages, ps, np.float32("nan"))
+    vsp = W.paginate(inp.v_scale, lens, table, n_pages, ps, np.float32("nan"))
+    if window:
+        for b, L in enumerate(lens):
+            first = (max(0, int(L) - window) & ~31) // ps
+            for j in range(first):
+                for arr, fill in ((kp, W.FP8_NAN_CODE), (vp, W.FP8_NAN_CODE), (ksp, np.nan), (vsp, np.nan)):
+                    arr[table[b, j]] = fill
+                table[b, j] = -1
+    return kp, vp, ksp, vsp, table
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,lens,ps,window,splits", [
+    (4, 32, 8, [4096, 700, 33, 0], 32, 0, 0),
+    (3, 16, 2, [3000, 17, 2049], 64, 0, 0),
+    (3, 16, 2, [3000, 17, 2049], 256, 1000, 0),
+    (2, 8, 8, [5000, 3333], 32, 0, 0),                 # MHA, few units
+    (3, 16, 4, [2500, 1, 777], 32, 300, 5),
+])
+def test_paged_fp8(B, Hq, Hkv, lens, ps, window, splits):
+    from oracle.fp8 import gqa_decode_fp8_paged_ref
+    announce(f"gqa fp8 paged B{B} Hq{Hq} Hkv{Hkv} ps{ps} w{window} S{splits} lens{lens}")
+    inp = W.make_gqa_fp8(B, Hq, Hkv, 128, lens, seed=51)
+    kp, vp, ksp, vsp, table = paged_fp8(inp, ps, seed=52, window=window)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    out, lse = da.gqa_decode_fp8_paged(bf16_tensor(inp.q), d(kp), d(vp), d(ksp), d(vsp), d(table), ps,
+                                       d(inp.seq_lens.astype(np.int32)), max_seq_len=inp.k.shape[1],
+                                       softmax_scale=inp.scale, num_splits=splits, window=window)
+    torch.cuda.synchronize()
+    q64 = W.bf16_to_f32(inp.q).astype(np.float64)
+    ro, rl = gqa_decode_fp8_paged_ref(q64, kp, vp, ksp, vsp, table, ps, inp.seq_lens, inp.scale, window=window)
+    assert_parity(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, what="fp8 paged")
+
+
+def test_paged_fp8_config2_full_size_sampled():
+    from oracle.fp8 import gqa_decode_fp8_paged_ref
+    announce("gqa fp8 paged config2 full B32 L4096 ps32, sampled rows")
+    inp = W.make_gqa_fp8_config(2)
+    kp, vp, ksp, vsp, table = paged_fp8(inp, 32, seed=53)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    out, lse = da.gqa_decode_fp8_paged(bf16_tensor(inp.q), d(kp), d(vp), d(ksp), d(vsp), d(table), 32,
+                                       d(inp.seq_lens.astype(np.int32)), softmax_scale=inp.scale)
+    torch.cuda.synchronize()
+    seqs = [0, 19, 31]
+    q64 = W.bf16_to_f32(inp.q[seqs]).astype(np.float64)
+    ro, rl = gqa_decode_fp8_paged_ref(q64, kp, vp, ksp, vsp, table[seqs], 32, inp.seq_lens[seqs], inp.scale)
+    assert_parity(out.cpu().numpy()[seqs], lse.cpu().numpy()[seqs], ro, rl, what="fp8 paged config2")
+
+
+def test_paged_fp8_per_head_scales():
+    from oracle.fp8 import gqa_decode_fp8_paged_ref
+    announce("gqa fp8 paged per-head scales")
+    inp = W.make_gqa_fp8(3, 16, 4, 128, [1000, 333, 2048], seed=54, max_seq_len=2048, scales="head",
+                         pad_nan=False)
+    kp, vp, _, _, table = paged_fp8(inp, 64, seed=55)
+    kh, vh = inp.k_scale[0, 0].copy(), inp.v_scale[0, 0].copy()
+    n_pages = kp.shape[0]
+    ks = torch.from_numpy(kh).cuda().expand(n_pages, 64, 4)
+    vs = torch.from_numpy(vh).cuda().expand(n_pages, 64, 4)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    out, lse = da.gqa_decode_fp8_paged(bf16_tensor(inp.q), d(kp), d(vp), ks, vs, d(table), 64,
+                                       d(inp.seq_lens.astype(np.int32)), max_seq_len=2048,
+                                       softmax_scale=inp.scale)
+    torch.cuda.synchronize()
+    q64 = W.bf16_to_f32(inp.q).astype(np.float64)
+    ksp = np.broadcast_to(kh, (n_pages, 64, 4))
+    vsp = np.broadcast_to(vh, (n_pages, 64, 4))
+    ro, rl = gqa_decode_fp8_paged_ref(q64, kp, vp, ksp, vsp, table, 64, inp.seq_lens, inp.scale)
+    assert_parity(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, what="fp8 paged per-head scales")
