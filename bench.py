@@ -421,6 +421,45 @@ def setup_append(kind):
     return [[("mla_append_rope", call)]], alg, info, inp
 
 
+def setup_gqa_fp8_paged(cfg):
+    """The fp8 workload of `cfg` over paged pools: codes and per-(token, KV
+    head) scales in 32-row pages placed in a seeded random physical order."""
+    import torch
+    import workloads as W
+    import decode_attention_kv_bf16_amd as da
+    inp = W.make_gqa_fp8_config(cfg)
+    lens = inp.seq_lens
+    ps = 32
+    table, n_pages = W.make_block_table(lens, ps, seed=cfg, spare_pages=0)
+    pools = [W.paginate(x, lens, table, n_pages, ps, 0) for x in (inp.k, inp.v, inp.k_scale, inp.v_scale)]
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    first = [d(x) for x in pools]
+    fp = sum(t.numel() * t.element_size() for t in first)
+    n_copies = max(1, math.ceil(MALL_GUARD_BYTES / fp))
+    copies = [first] + [[t.clone() for t in first] for _ in range(n_copies - 1)]
+    tab = d(table)
+    q = to_dev_bf16(inp.q)
+    sl = torch.from_numpy(lens).cuda()
+    B, Hq, D = q.shape
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    calls = []
+    for kp, vp, ksp, vsp in copies:
+        def call(kp=kp, vp=vp, ksp=ksp, vsp=vsp):
+            da.gqa_decode_fp8_paged(q, kp, vp, ksp, vsp, tab, ps, sl, max_seq_len=inp.k.shape[1],
+                                    softmax_scale=inp.scale, out=out, lse=lse)
+        calls.append([("gqa_decode_fp8_paged", call)])
+    alg = gqa_alg(B, Hq, inp.k.shape[2], D, int(lens.sum()), elem=1)
+    scale_bytes = 2 * int(lens.sum()) * inp.k.shape[2] * 4
+    table_bytes = table.size * 4
+    alg["cache"] += scale_bytes + table_bytes
+    alg["total"] += scale_bytes + table_bytes
+    info = dict(batch=B, q_heads=Hq, kv_heads=int(inp.k.shape[2]), head_dim=D, seq_len=int(lens.max()),
+                page_size=ps, cache="e4m3 + fp32 scale per (token, KV head), paged",
+                cache_copies=len(copies))
+    return calls, alg, info, (inp, dict(pools=pools, table=table))
+
+
 def measured_traffic(name):
     """HBM bytes per launch from the committed rocprofv3 counter runs
     (profiles/hbm_traffic.json), if they were taken on the current kernel
@@ -457,6 +496,8 @@ def run_gpu(args):
         plans.append(("mla-paged", setup_mla_paged(3)))
     if args.workload == "gqa-fp8":
         plans.append(("gqa-fp8", setup_gqa_fp8(2)))
+    if args.workload == "gqa-fp8-paged":
+        plans.append(("gqa-fp8-paged", setup_gqa_fp8_paged(2)))
     if args.workload == "gqa-window":
         plans.append(("gqa-window", setup_gqa_window()))
     if args.workload == "append":
@@ -561,6 +602,8 @@ def run_gpu(args):
                                        if any(dom == n for n, _ in p[1][0][0]))
     if dom in ("gqa_split_pass", "gqa_window"):
         dom_bytes = alg["cache"] + alg["q"]
+    elif dom == "gqa_decode_fp8_paged":
+        dom_bytes = alg["cache"] + alg["q"]
     elif dom in ("mla_attend", "mla_attend_paged"):
         dom_bytes = alg["cache"]
     else:
@@ -608,6 +651,7 @@ def workload_name(w):
             "mla-paged": "deepseek-v3-mla-b64-l4096-paged16",
             "gqa-fp8": "llama3-8b-gqa-b32-l4096-fp8e4m3",
             "gqa-window": "mistral-7b-shape-gqa-b32-l8192-window4096",
+            "gqa-fp8-paged": "llama3-8b-gqa-b32-l4096-fp8e4m3-paged32",
             "append-fp8": "cache append + rope into e4m3: llama3-8b-gqa-b32-l4096",
             "append": "cache append + rope: llama3-8b-gqa-b32-l4096 + deepseek-v3-mla-b64-l4096"}[w]
 
@@ -661,6 +705,18 @@ def cpu_baseline(plans, budget_s):
                 mla_absorbed_paged_ref(*args)
                 dt = time.perf_counter() - t
                 a1 = mla_alg(1, inp.q_nope.shape[1], L)
+            elif kind == "gqa-fp8-paged":
+                from oracle.fp8 import gqa_decode_fp8_paged_ref
+                L = int(inp.seq_lens[b])
+                kp, vp, ksp, vsp = pools["pools"]
+                pages = pools["table"][b, :-(-L // 32)]
+                tab = np.arange(len(pages), dtype=np.int32)[None]
+                args = (W.bf16_to_f32(inp.q[b:b + 1]).astype(np.float64), kp[pages], vp[pages], ksp[pages],
+                        vsp[pages], tab, 32, inp.seq_lens[b:b + 1], inp.scale)
+                t = time.perf_counter()
+                gqa_decode_fp8_paged_ref(*args)
+                dt = time.perf_counter() - t
+                a1 = gqa_alg(1, inp.q.shape[1], inp.k.shape[2], inp.q.shape[2], L, elem=1)
             elif kind == "gqa-fp8":
                 L = int(inp.seq_lens[b])
                 args = (W.bf16_to_f32(inp.q[b:b + 1]).astype(np.float64), inp.k[b:b + 1, :L],
@@ -741,7 +797,7 @@ def main():
     ap.add_argument("--workload", default="step",
                     choices=["step", "gqa", "mla", "mla-long", "gqa-ragged", "gqa-paged",
                              "mla-paged", "gqa-fp8", "append", "gqa-window",
-                             "append-fp8"])
+                             "append-fp8", "gqa-fp8-paged"])
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle time for the CPU baseline (0 disables)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,

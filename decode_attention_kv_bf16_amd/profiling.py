@@ -48,7 +48,7 @@ KERNELS = {
 # names under which a workload's launches of a kernel are recorded (GQA over
 # paged pools runs the GQA kernel as one library call, gqa_decode_paged)
 ALIASES = {"gqa_decode_paged": "gqa_split_pass", "gqa_decode_fp8": "gqa_split_pass",
-           "gqa_window": "gqa_split_pass"}
+           "gqa_window": "gqa_split_pass", "gqa_decode_fp8_paged": "gqa_split_pass"}
 
 
 def source_sha256(short: str):

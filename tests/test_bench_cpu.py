@@ -22,7 +22,7 @@ def test_more_than_one_gpu_exits_with_a_message():
 
 def test_every_workload_has_a_name():
     for w in ("step", "gqa", "mla", "mla-long", "gqa-ragged", "gqa-paged", "mla-paged", "gqa-fp8",
-              "append", "gqa-window", "append-fp8"):
+              "append", "gqa-window", "append-fp8", "gqa-fp8-paged"):
         assert bench.workload_name(w)
 
 
