@@ -165,10 +165,9 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_mfma_kernel(GqaArgs a) {
   }
 
   const int64_t pitch = a.kv_st * kEsz;   // bytes from one token's row to the next
-  // Paged pools (arganzheng.life section 6.1; bf16): a step of 16 tokens
-  // starts on a multiple of 16 and lies in one page of >= 16 rows. Lane j
-  // holds the table entry of this wave's step 64 c + j (c = step / 64),
-  // loaded 64 steps at a time, so a step's page is a register read.
+  // Paged pools (arganzheng.life section 6.1): a step of 16 tokens (bf16) or
+  // 32 (fp8) starts on a multiple of its size and lies in one page of at
+  // least that many rows; its page comes from the block table (step_page).
   const bool paged = a.page_shift > 0;
   const int64_t tab0 = (int64_t)b * a.max_blocks;
   const int64_t kv_b = paged ? 0 : (int64_t)b * a.kv_sb;
@@ -208,25 +207,27 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_mfma_kernel(GqaArgs a) {
   constexpr int kStride = kWaves * kTok;
   const int first = t_begin + wave * kTok;
   const int n = first < t_end ? (t_end - first + kStride - 1) / kStride : 0;
-  int pages = 0;
-  auto load_pages = [&](int i0) {   // entries of steps i0 .. i0 + 63 (a vector load)
-    const int i = i0 + lane;
-    pages = i < n ? a.block_table[tab0 + ((first + i * kStride) >> a.page_shift)] : 0;
-  };
-  if (paged) load_pages(0);
-  // byte offset of step i's first row (paged: in its page)
-  auto row0 = [&](int i) -> int64_t {
-    const int t0 = first + i * kStride;
-    if (!paged) return (int64_t)t0 * pitch;
-    if (i > 0 && (i & 63) == 0) load_pages(i);   // steps are issued in order
-    const int64_t page = __builtin_amdgcn_readlane(pages, i & 63);
-    return page * a.page_stride * kEsz + (int64_t)(t0 & ((1 << a.page_shift) - 1)) * pitch;
+  // Paged pools: each step's table entry is read with a scalar load
+  // (table_entry, through the constant address space) one step ahead of its
+  // use. A scalar load is counted by lgkmcnt, so its wait never waits for the
+  // row copies in flight; a vector load of entries read back with readlane
+  // made the compiler wait for every vector load before each use (the fp8
+  // path, which reads the entry twice per step, lost 25% to it). Indices are
+  // clamped to the wave's last step, so every read is a valid entry.
+  int32_t page_next = paged && n > 0 ? table_entry(a.block_table, tab0 + (first >> a.page_shift)) : 0;
+  auto step_page = [&](int i) -> int64_t {   // called once per step, in step order
+    const int64_t cur = page_next;
+    const int nx = i + 1 < n ? i + 1 : n - 1;
+    page_next = table_entry(a.block_table, tab0 + ((first + nx * kStride) >> a.page_shift));
+    return cur;
   };
   auto issue_step = [&](int i, int slot) {
     const int t0 = first + i * kStride;
     const int valid = min(t_end - t0, kTok);   // rows past it read as zero
     const uint32_t nrec = (uint32_t)(valid * pitch);
-    const int64_t r0b = row0(i);
+    const int64_t page = paged ? step_page(i) : 0;
+    const int64_t r0b = paged ? page * a.page_stride * kEsz + (int64_t)(t0 & ((1 << a.page_shift) - 1)) * pitch
+                              : (int64_t)t0 * pitch;
     const __amdgpu_buffer_rsrc_t kr = make_raw_rsrc(kbase + r0b, nrec);
     const __amdgpu_buffer_rsrc_t vr = make_raw_rsrc(vbase + r0b, nrec);
     const uint32_t dst = wlds_addr + slot * kSlotB;
@@ -242,9 +243,7 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_mfma_kernel(GqaArgs a) {
       // every step still counts kOps operations.
       const uint32_t srec = a.sc_st == 0 ? 0u : (uint32_t)(((valid - 1) * a.sc_st + 1) * 4);
       int64_t s0 = (int64_t)t0 * a.sc_st;
-      if (paged)   // the step's page (row0 above has loaded its table entry)
-        s0 = (int64_t)__builtin_amdgcn_readlane(pages, i & 63) * a.sc_sb +
-             (int64_t)(t0 & ((1 << a.page_shift) - 1)) * a.sc_st;
+      if (paged) s0 = page * a.sc_sb + (int64_t)(t0 & ((1 << a.page_shift) - 1)) * a.sc_st;
       const __amdgpu_buffer_rsrc_t ks = make_raw_rsrc(ksc + s0, srec);
       const __amdgpu_buffer_rsrc_t vs = make_raw_rsrc(vsc + s0, srec);
       buffer_load_to_lds4(ks, soff, dst + 2 * kPartB);
