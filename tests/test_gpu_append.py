@@ -397,3 +397,25 @@ def test_fp8_append_then_decode():
     ro, rl = gqa_decode_ref(host_f64(q_rot), kd, vd, lens, 1 / np.sqrt(D))
     err = np.abs(out.cpu().numpy() - ro).max(axis=-1) / np.abs(ro).max(axis=-1)
     assert err.max() <= 1e-2 and np.abs(lse.cpu().numpy() - rl).max() <= 1e-3
+
+
+def test_recorded_call_replays_the_same_launch():
+    # the binding's recorded_calls(): repeating the recorded C call does what
+    # the wrapper call did (the bench's append steps rely on it)
+    announce("recorded call replay")
+    B, Hq, Hkv, D, L = 4, 8, 2, 128, 64
+    inp = W.make_gqa_append(B, Hq, Hkv, D, L, seed=61)
+    q, kn, vn = (bf16_tensor(x) for x in (inp.q, inp.k_new, inp.v_new))
+    pos = torch.from_numpy(inp.positions).cuda()
+    kc = torch.zeros((B, L, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    vc, qo = torch.zeros_like(kc), torch.empty_like(q)
+    with da.recorded_calls() as rec:
+        da.gqa_append_rope(q, kn, vn, pos, kc, vc, q_out=qo)
+    torch.cuda.synchronize()
+    (fn, args), = rec
+    want = (kc.clone(), vc.clone(), qo.clone())
+    kc.zero_(); vc.zero_(); qo.zero_()
+    assert fn(*args) == 0
+    torch.cuda.synchronize()
+    for got, w in zip((kc, vc, qo), want):
+        assert torch.equal(got.view(torch.int16), w.view(torch.int16))
