@@ -124,7 +124,7 @@ _SIGNATURES = {
     "da_mla_attend_split_pass": (ctypes.c_int, [ctypes.POINTER(MlaParams), _vp, _vp, _vp, _vp,
                                                 _vp, _vp]),
     "da_mla_merge_project": (ctypes.c_int, [ctypes.POINTER(MlaParams), _vp, _vp, _vp, _vp, _vp,
-                                            _vp]),
+                                            _vp, _vp]),
     "da_gqa_decode_paged": (ctypes.c_int, [_GQA_P, _PAGED_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                            ctypes.c_size_t, _vp]),
     "da_mla_decode_absorbed_paged": (ctypes.c_int, [_MLA_P, _PAGED_P, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -671,7 +671,9 @@ def mla_stages(q_nope, q_rope, kv_cache, w_uk, w_uv, seq_lens=None, softmax_scal
            "da_mla_partials_size")
     B, H, _ = q_nope.shape
     dev = q_nope.device
-    q_hat = torch.empty((B, H, kv_cache.shape[2]), dtype=torch.bfloat16, device=dev)
+    # absorbed queries [B, H, 576], then the low parts of q~ [B, H, 512]
+    d_c = w_uv.shape[1]
+    q_hat = torch.empty((B * H * (kv_cache.shape[2] + d_c),), dtype=torch.bfloat16, device=dev)
     # opaque partial buffers (slots of o~_s and lse_s; the library's layout)
     part_out = torch.empty((po_bytes.value,), dtype=torch.uint8, device=dev)
     part_lse = torch.empty((pl_bytes.value // 4,), dtype=torch.float32, device=dev)
@@ -694,8 +696,8 @@ def mla_stages(q_nope, q_rope, kv_cache, w_uk, w_uv, seq_lens=None, softmax_scal
                    "da_mla_attend_split_pass_paged")
 
     def merge():
-        _check(L.da_mla_merge_project(ctypes.byref(p), _ptr(part_out), _ptr(part_lse), _ptr(w_uv),
-                                      _ptr(out), _ptr(lse), _stream_handle()),
+        _check(L.da_mla_merge_project(ctypes.byref(p), _ptr(q_hat), _ptr(part_out), _ptr(part_lse),
+                                      _ptr(w_uv), _ptr(out), _ptr(lse), _stream_handle()),
                "da_mla_merge_project")
 
     return absorb, attend, merge, out, lse, dict(q_hat=q_hat, part_out=part_out, part_lse=part_lse)

@@ -250,7 +250,8 @@ MlaPlan plan_mla(const da_mla_params_t* p) {
     pl.slots = pl.splits * p->batch;
   }
   const size_t rows = (size_t)p->batch * p->num_heads;
-  pl.q_hat_bytes = round_up(rows * (kMlaDc + kMlaRope) * 2, 256);
+  // q^ [B, H, 576] bf16, then the low parts q~_lo [B, H, 512] bf16
+  pl.q_hat_bytes = round_up(rows * (kMlaDc + kMlaRope + kMlaDc) * 2, 256);
   pl.part_out_bytes = round_up((size_t)pl.slots * p->num_heads * kMlaDc * 2, 256);  // bf16
   pl.table_bytes = pl.splits == 0 ? round_up((size_t)p->batch * 2 * sizeof(int32_t), 256) : 0;
   pl.part_lse_bytes = round_up((size_t)pl.slots * p->num_heads * sizeof(float), 256) + pl.table_bytes;
@@ -296,7 +297,15 @@ da::MlaArgs mla_args(const da_mla_params_t* p, const MlaPlan& pl) {
   a.wg_budget = pl.wg_budget;
   a.slots = pl.slots;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  a.scale = p->softmax_scale;
   return a;
+}
+
+// The absorbed-query buffer: q^ [B, H, 576] bf16 followed by q~_lo [B, H, 512].
+void set_q_hat(da::MlaArgs& a, const void* buf) {
+  uint16_t* base = static_cast<uint16_t*>(const_cast<void*>(buf));
+  a.q_hat = base;
+  a.q_lo = base + (size_t)a.batch * a.num_heads * (kMlaDc + kMlaRope);
 }
 
 // part_lse holds slots x H floats, then (balanced splits) the split table
@@ -683,7 +692,7 @@ da_status_t da_mla_decode_absorbed(const da_mla_params_t* p, const void* q_nope,
   a.w_uv = static_cast<const uint16_t*>(w_uv);
   a.out = out;
   a.lse = lse;
-  a.q_hat = reinterpret_cast<uint16_t*>(ws);
+  set_q_hat(a, ws);
   set_partials(a, pl, ws + pl.q_hat_bytes, ws + pl.q_hat_bytes + pl.part_out_bytes);
   return from_hip(da::launch_mla_decode(a, static_cast<hipStream_t>(hip_stream)));
 }
@@ -698,7 +707,7 @@ da_status_t da_mla_absorb_query(const da_mla_params_t* p, const void* q_nope, co
   a.q_nope = static_cast<const uint16_t*>(q_nope);
   a.q_rope = static_cast<const uint16_t*>(q_rope);
   a.w_uk = static_cast<const uint16_t*>(w_uk);
-  a.q_hat = static_cast<uint16_t*>(q_hat);
+  set_q_hat(a, q_hat);
   return from_hip(da::launch_mla_absorb(a, static_cast<hipStream_t>(hip_stream)));
 }
 
@@ -712,7 +721,7 @@ da_status_t da_mla_attend_split_pass(const da_mla_params_t* p, const void* q_hat
   if (!aligned4(seq_lens)) return DA_ERR_INVALID_ARGUMENT;
   const MlaPlan pl = plan_mla(p);
   da::MlaArgs a = mla_args(p, pl);
-  a.q_hat = static_cast<uint16_t*>(const_cast<void*>(q_hat));
+  set_q_hat(a, q_hat);
   a.cache = static_cast<const uint16_t*>(kv_cache);
   a.seq_lens = seq_lens;
   set_partials(a, pl, part_out, part_lse);
@@ -745,7 +754,7 @@ da_status_t da_mla_decode_absorbed_paged(const da_mla_params_t* p, const da_page
   a.w_uv = static_cast<const uint16_t*>(w_uv);
   a.out = out;
   a.lse = lse;
-  a.q_hat = reinterpret_cast<uint16_t*>(ws);
+  set_q_hat(a, ws);
   set_partials(a, pl, ws + pl.q_hat_bytes, ws + pl.q_hat_bytes + pl.part_out_bytes);
   return from_hip(da::launch_mla_decode(a, static_cast<hipStream_t>(hip_stream)));
 }
@@ -764,24 +773,25 @@ da_status_t da_mla_attend_split_pass_paged(const da_mla_params_t* p, const da_pa
   const MlaPlan pl = plan_mla(p);
   da::MlaArgs a = mla_args(p, pl);
   set_paged(a, pages);
-  a.q_hat = static_cast<uint16_t*>(const_cast<void*>(q_hat));
+  set_q_hat(a, q_hat);
   a.cache = static_cast<const uint16_t*>(cache_pool);
   a.seq_lens = seq_lens;
   set_partials(a, pl, part_out, part_lse);
   return from_hip(da::launch_mla_attend(a, static_cast<hipStream_t>(hip_stream)));
 }
 
-da_status_t da_mla_merge_project(const da_mla_params_t* p, const void* part_out,
+da_status_t da_mla_merge_project(const da_mla_params_t* p, const void* q_hat, const void* part_out,
                                  const float* part_lse, const void* w_uv, float* out, float* lse,
                                  void* hip_stream) {
   da_status_t st = check_mla_params(p);
   if (st != DA_OK) return st;
-  st = check_ptrs16({part_out, w_uv, out});
+  st = check_ptrs16({q_hat, part_out, w_uv, out});
   if (st != DA_OK) return st;
   if (!part_lse || !aligned4(part_lse) || !aligned4(lse)) return DA_ERR_INVALID_ARGUMENT;
   const MlaPlan pl = plan_mla(p);
   da::MlaArgs a = mla_args(p, pl);
   set_partials(a, pl, const_cast<void*>(part_out), const_cast<float*>(part_lse));
+  set_q_hat(a, q_hat);
   a.w_uv = static_cast<const uint16_t*>(w_uv);
   a.out = out;
   a.lse = lse;

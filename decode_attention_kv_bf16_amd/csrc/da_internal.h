@@ -72,7 +72,12 @@ struct MlaArgs {
   const uint16_t* w_uv;      // [H, 512, 128]
   float* out;                // [B, H, 128]
   float* lse;                // [B, H] or null
-  uint16_t* q_hat;           // [B, H, 576] bf16: [q~ | q_rope]
+  uint16_t* q_hat;           // [B, H, 576] bf16: [bf16(q~) | q_rope]
+  // [B, H, 512] bf16: the part of q~ that bf16(q~) leaves out, q~ - bf16(q~)
+  // rounded to bf16. The scores use bf16(q~) (the matrix-core operand); the
+  // merge adds scale * q~_lo . o~ to each lse, the first-order change of the
+  // log-sum-exp when the scores move by scale * q~_lo . c_j.
+  uint16_t* q_lo;
   // Split partials, slot-major: part_out [slots, H, 512] bf16 (each split's
   // normalised o~_s), part_lse [slots, H]. Fixed splits: slot = s * B + b
   // (num_splits per sequence, chunk rows each). Balanced splits
@@ -87,7 +92,8 @@ struct MlaArgs {
   int32_t batch, num_heads, max_seq_len, num_splits, chunk;
   int32_t wg_budget;         // balanced: tiles are spread over this many workgroups
   int32_t slots;             // rows of part_out / H
-  float scale_log2;
+  float scale_log2;          // softmax_scale * log2(e)
+  float scale;               // softmax_scale
   // Paged latent pool (page_shift > 0): token t of sequence b is row
   // t & (2^page_shift - 1) of page block_table[b * max_blocks + (t >> page_shift)],
   // pages page_stride elements apart; cache_sb is then unused. Splits start

@@ -173,12 +173,16 @@ __global__ __launch_bounds__(64) void mla_absorb_kernel(MlaArgs a) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x32(wa[cb][ks], qb[bb][ks], acc);
-        // lane holds q~[b][c0 + 16cb + 4q4 + i], i = 0..3
+        // lane holds q~[b][c0 + 16cb + 4q4 + i], i = 0..3: bf16(q~) goes to
+        // q^, and what the rounding left out (exact in float32) to q~_lo
         if (b < B) {
-          uint2 v;
+          uint2 v, r;
           v.x = cvt_bf16x2(acc[0], acc[1]);
           v.y = cvt_bf16x2(acc[2], acc[3]);
+          r.x = cvt_bf16x2(acc[0] - bf16_lo(v.x), acc[1] - bf16_hi(v.x));
+          r.y = cvt_bf16x2(acc[2] - bf16_lo(v.y), acc[3] - bf16_hi(v.y));
           *reinterpret_cast<uint2*>(a.q_hat + ((int64_t)b * H + h) * kRowE + c0 + 16 * cb + 4 * q4) = v;
+          *reinterpret_cast<uint2*>(a.q_lo + ((int64_t)b * H + h) * kDc + c0 + 16 * cb + 4 * q4) = r;
         }
       }
     }
@@ -729,20 +733,28 @@ __global__ __launch_bounds__(512) void mla_merge_project_kernel(MlaArgs a, int n
   const int tr_chunk = 2 * w + ((l16 & 3) >> 1);
   const int tr_half = 8 * (l16 & 1);
 
+  __shared__ float lse_sm[16];   // merged lse of the block's rows, before the correction
+  const int r = tid >> 5;        // thread (row slot r, columns 16 cs .. 16 cs + 15)
+  const int cs = tid & 31;
   const int nbb = (B + 15) / 16;
   for (int bbi = 0; bbi < bpg; ++bbi) {
     const int bb = grp * bpg + bbi;
     if (bb >= nbb) break;
+    const int R = min(16, B - bb * 16);
+    // q~_lo of row r of the block (columns 16 cs ..), for the lse correction
+    uint4 lo[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
+    if (r < R && a.lse) {
+      const uint4* src = reinterpret_cast<const uint4*>(a.q_lo + ((int64_t)(bb * 16 + r) * H + h) * kDc + 16 * cs);
+      lo[0] = src[0];
+      lo[1] = src[1];
+    }
     // Merge the splits: thread (slot r, 16 columns). With R < 16 valid rows in
     // the block, G = the largest power of two with G R <= 16 slots serve one
     // row, slot group g summing the splits s = g (mod G); the G partial rows
     // are then added through LDS. The weights exp(lse_s - lse) use all splits.
     {
-      const int R = min(16, B - bb * 16);
       int G = 1;
       while (2 * G * R <= 16) G *= 2;
-      const int r = tid >> 5;
-      const int cs = tid & 31;
       const int rr = r / G, g = r % G;
       const int bidx = bb * 16 + rr;
       float acc[16];
@@ -804,7 +816,7 @@ __global__ __launch_bounds__(512) void mla_merge_project_kernel(MlaArgs a, int n
           }
           lse_out = M + log2_hw(z) * kLn2;
         }
-        if (g == 0 && cs == 0 && a.lse) a.lse[row_id] = lse_out;
+        if (g == 0 && cs == 0) lse_sm[rr] = lse_out;
       }
       auto store_row = [&](int slot, const float* v) {
 #pragma unroll
@@ -842,6 +854,29 @@ __global__ __launch_bounds__(512) void mla_merge_project_kernel(MlaArgs a, int n
     }
     wait_vm_all();
     __syncthreads();
+
+    // lse of row r: the scores were computed with bf16(q~); with q~ itself
+    // every score of the row moves by scale q~_lo . c_j, which moves the
+    // log-sum-exp by sum_j p_j scale q~_lo . c_j = scale q~_lo . o~ to first
+    // order (o~ = sum_j p_j c_j, the merged row in LDS). What remains is of
+    // second order in these shifts (~1e-6 at the method's scales).
+    if (a.lse) {
+      float d = 0.f;
+      if (r < R) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const u32x4_t ov = *reinterpret_cast<const LDS u32x4_t*>(o_lds + r * kORowB + 2 * (16 * cs + 8 * j));
+          float fo[8], fl[8];
+          unpack_bf16x8(uint4{ov.x, ov.y, ov.z, ov.w}, fo);
+          unpack_bf16x8(lo[j], fl);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) d = fmaf(fo[e], fl[e], d);
+        }
+      }
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) d += __shfl_xor(d, off);
+      if (r < R && cs == 0) a.lse[(int64_t)(bb * 16 + r) * H + h] = lse_sm[r] + a.scale * d;
+    }
 
     // out[b, e] = sum_c o~[b, c] W_UV[h, c, e]; wave w owns columns 16w .. 16w+15
     f32x4_t acc2 = {0.f, 0.f, 0.f, 0.f};

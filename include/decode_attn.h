@@ -186,9 +186,9 @@ typedef struct {
  * [slots, H] float32 (lse_s; -inf for a split with no rows). */
 
 /* Bytes of workspace da_mla_decode_absorbed needs (never 0 for valid
- * parameters): the absorbed queries q^ [B, H, 576] bf16, then the two
- * partial buffers of da_mla_partials_size, each starting on a 256-byte
- * boundary in that order. */
+ * parameters): the absorbed-query buffer of da_mla_absorb_query (B*H*1088
+ * bf16), then the two partial buffers of da_mla_partials_size, each
+ * starting on a 256-byte boundary in that order. */
 DA_EXPORT size_t da_mla_decode_workspace_size(const da_mla_params_t* params);
 
 /* Fixed split count per sequence (>= 1); 0 when the splits are balanced on
@@ -215,7 +215,10 @@ DA_EXPORT da_status_t da_mla_partials_size(const da_mla_params_t* params,
  *   lse      [B, H] float32, contiguous; may be NULL
  * Numerics: q~, the softmax weights, each split's o~_s and the merged o~ are
  * rounded to bf16 before they enter the matrix cores or memory; every sum is
- * accumulated in float32.
+ * accumulated in float32. The scores use bf16(q~); the part of q~ that this
+ * rounding drops, q~_lo, is kept, and each lse is corrected by
+ * scale * q~_lo . o~ (the first-order change of the log-sum-exp when every
+ * score moves by scale * q~_lo . c_j), so lse follows the unrounded q~.
  * Equivalent to da_mla_absorb_query, da_mla_attend_split_pass and
  * da_mla_merge_project in sequence on the workspace buffers.
  */
@@ -228,8 +231,12 @@ DA_EXPORT da_status_t da_mla_decode_absorbed(const da_mla_params_t* params,
                                    void* hip_stream);
 
 /* Stage 1, query-side absorption (arganzheng.life section 4.5; jianzhnie.github.io
- * section 4, "Absorb"): q_hat[b, h, :] = [q_nope[b,h] W_UK[h]^T (bf16) | q_rope[b,h]].
- *   q_hat [B, H, d_c + d_rope] bf16, contiguous (written). */
+ * section 4, "Absorb"): with q~ = q_nope[b,h] W_UK[h]^T (float32 accumulation),
+ * q_hat[b, h, :] = [bf16(q~) | q_rope[b,h]].
+ *   q_hat  B*H*(2 d_c + d_rope) bf16 = B*H*1088, contiguous (written): first
+ *          the absorbed queries [B, H, d_c + d_rope], then the low parts
+ *          q~_lo [B, H, d_c] = bf16(q~ - bf16(q~)), which stage 3 uses to
+ *          correct the lse. */
 DA_EXPORT da_status_t da_mla_absorb_query(const da_mla_params_t* params,
                                           const void* q_nope, const void* q_rope,
                                           const void* w_uk, void* q_hat, void* hip_stream);
@@ -247,9 +254,10 @@ DA_EXPORT da_status_t da_mla_attend_split_pass(const da_mla_params_t* params,
 
 /* Stage 3, merge the splits by log-sum-exp, then project by W_UV
  * (arganzheng.life section 4.5, output side): out[b,h] = o~[b,h] W_UV[h];
- * lse[b,h] = log sum_s exp(lse_s). part_out and part_lse as written by
- * stage 2 with the same parameters. */
-DA_EXPORT da_status_t da_mla_merge_project(const da_mla_params_t* params,
+ * lse[b,h] = log sum_s exp(lse_s) + scale * q~_lo[b,h] . o~[b,h]. q_hat is
+ * stage 1's buffer (its q~_lo part is read), part_out and part_lse as
+ * written by stage 2 with the same parameters. */
+DA_EXPORT da_status_t da_mla_merge_project(const da_mla_params_t* params, const void* q_hat,
                                            const void* part_out, const float* part_lse,
                                            const void* w_uv, float* out, float* lse,
                                            void* hip_stream);

@@ -26,3 +26,20 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_sessionfinish(session, exitstatus):
+    # DA_PARITY_RECORD=path: write the largest errors of every GPU parity check
+    path = os.environ.get("DA_PARITY_RECORD")
+    if not path:
+        return
+    try:
+        from gpu_util import RECORD
+    except Exception:  # pragma: no cover  (no GPU test was collected)
+        return
+    import json
+    d = os.path.dirname(path)
+    if d:
+        os.makedirs(d, exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(dict(exitstatus=int(exitstatus), checks=RECORD), f, indent=1, sort_keys=True)

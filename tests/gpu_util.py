@@ -7,6 +7,7 @@ The bar for floating-point outputs (bf16 inputs, fp32 accumulation):
 Rows whose reference is empty (lse_ref = -inf) must come back exactly
 out = 0 and lse = -inf.
 """
+import os
 import sys
 
 import numpy as np
@@ -14,6 +15,18 @@ import torch
 
 OUT_RTOL = 1e-2
 LSE_ATOL = 1e-3
+
+# Largest errors seen per parity check, keyed by test and check name; written
+# to the file named by DA_PARITY_RECORD at the end of the session (conftest).
+RECORD = {}
+
+
+def _record(what, rel, lerr, out_rtol, lse_atol):
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    tol = np.asarray(out_rtol, dtype=np.float64)
+    RECORD[f"{test} :: {what}"] = dict(max_row_rel_err=rel, max_lse_abs_err=lerr,
+                                       out_rtol=float(tol.max()) if tol.size else None,
+                                       lse_atol=float(lse_atol))
 
 
 def announce(msg: str):
@@ -59,11 +72,13 @@ def assert_parity(out, lse, ref_out, ref_lse, out_rtol=OUT_RTOL, lse_atol=LSE_AT
         assert np.all(out[empty] == 0), f"{what}: empty rows must give out=0"
     full = ~empty
     if not full.any():
+        _record(what, 0.0, 0.0, out_rtol, lse_atol)
         return 0.0, 0.0
     assert np.isfinite(out[full]).all(), f"{what}: non-finite outputs"
     assert np.isfinite(lse[full]).all(), f"{what}: non-finite lse"
     rel = row_rel_err(out[full], ref_out[full])
     lerr = np.abs(lse[full] - ref_lse[full])
+    _record(what, float(rel.max()), float(lerr.max()), out_rtol, lse_atol)
     tol = np.broadcast_to(np.asarray(out_rtol, dtype=np.float64), np.shape(ref_lse))[full]
     assert np.all(rel <= tol), f"{what}: row-relative output error {rel.max():.3e} over its bound"
     assert lerr.max() <= lse_atol, f"{what}: max lse error {lerr.max():.3e} > {lse_atol}"

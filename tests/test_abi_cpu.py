@@ -147,10 +147,11 @@ def test_mla_partials_size_without_a_device():
     st, po, pl = mla_partials(mla(64, 128, 4096))
     assert st == 0 and po == up((256 + 64) * 128 * 512 * 2)
     assert pl == up((256 + 64) * 128 * 4) + up(64 * 2 * 4)
-    # the workspace is q^ followed by the two partial buffers
+    # the workspace is the absorbed-query buffer (q^ of 576 and q~_lo of 512
+    # bf16 per row) followed by the two partial buffers
     for p in (mla(), mla(splits=3), mla(4, 16, 100)):
         _, po, pl = mla_partials(p)
-        assert L.da_mla_decode_workspace_size(ctypes.byref(p)) == up(p.batch * p.num_heads * 576 * 2) + po + pl
+        assert L.da_mla_decode_workspace_size(ctypes.byref(p)) == up(p.batch * p.num_heads * 1088 * 2) + po + pl
     assert mla_partials(mla(H=80))[0] == 2
     assert L.da_mla_partials_size(ctypes.byref(mla()), None, None) == 1
 

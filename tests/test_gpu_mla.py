@@ -1,15 +1,11 @@
 """GPU parity of the absorbed-MLA decode path against the fp64 oracle,
 called through the C ABI via the Python binding.
 
-Tolerances: the bar (row-relative output error <= 1e-2, |lse error| <= 1e-3)
-is asserted on the DeepSeek-V3 shapes (L >= 4096). The kernel rounds the
-absorbed query q~ to bf16 before the matrix cores, which moves each score by
-at most scale * 2^-8 * sum_c |q~_c c_jc| (bf16 round-to-nearest-even has
-relative error <= 2^-8). The lse is a log-sum-exp of the scores, so its error
-is at most the largest score error. With thousands of rows these per-row
-errors average out far below 1e-3. For a handful of rows they do not, so
-short-sequence edge cases assert |lse error| <= max(1e-3, that bound),
-computed per row from the data.
+Every check holds the bar: row-relative output error <= 1e-2 and
+|lse error| <= 1e-3, for every sequence length from 1 row up. The kernel's
+scores use the absorbed query rounded to bf16; the library corrects each lse
+by the first-order effect of that rounding, so short sequences (where the
+score shifts of a few rows do not average out) meet the same bar as long ones.
 """
 import numpy as np
 import pytest
@@ -18,7 +14,7 @@ import torch
 import decode_attention_kv_bf16_amd as da
 import workloads as W
 from gpu_util import announce, assert_parity, mla_to_device, row_rel_err
-from oracle.attention import absorb_query_ref, mla_absorbed_ref
+from oracle.attention import mla_absorbed_ref
 
 pytestmark = pytest.mark.gpu
 
@@ -30,25 +26,17 @@ def f64(bits):
 
 
 def oracle_rows(inp, seqs):
-    seqs = list(seqs)
-    Lm = int(max(1, inp.seq_lens[seqs].max()))
-    return mla_absorbed_ref(f64(inp.q_nope[seqs]), f64(inp.q_rope[seqs]), f64(inp.cache[seqs, :Lm]),
-                            inp.seq_lens[seqs], f64(inp.w_uk), f64(inp.w_uv), inp.scale)
-
-
-def qtilde_score_bound(inp, seqs):
-    """Per (b, h): scale * 2^-8 * max_j sum_c |q~_c| |c_jc| (bound on the score
-    shift caused by rounding q~ to bf16)."""
-    seqs = list(seqs)
-    qt = np.abs(absorb_query_ref(f64(inp.q_nope[seqs]), f64(inp.w_uk)))   # [b, H, 512]
-    out = np.zeros(qt.shape[:2])
-    for i, b in enumerate(seqs):
+    """The oracle one sequence at a time (bounded memory), stacked."""
+    wuk, wuv = f64(inp.w_uk), f64(inp.w_uv)
+    outs, lses = [], []
+    for b in seqs:
         L = int(inp.seq_lens[b])
-        if L == 0:
-            continue
-        c = np.abs(f64(inp.cache[b, :L, :512]))                          # [L, 512]
-        out[i] = (c @ qt[i].T).max(axis=0)                               # [H]
-    return inp.scale * 2.0 ** -8 * out
+        o, l = mla_absorbed_ref(f64(inp.q_nope[b:b + 1]), f64(inp.q_rope[b:b + 1]),
+                                f64(inp.cache[b:b + 1, :max(L, 1)]), inp.seq_lens[b:b + 1], wuk, wuv,
+                                inp.scale)
+        outs.append(o[0])
+        lses.append(l[0])
+    return np.stack(outs), np.stack(lses)
 
 
 def run(inp, num_splits=0):
@@ -67,15 +55,13 @@ def test_config3_reduced_batch_all_rows():
     print("config3 B4 max row rel err, max lse err:", err)
 
 
-def test_config3_full_size_sampled():
-    announce("mla config3 full B64 H128 L4096, sampled rows")
+def test_config3_full_size_all_rows():
+    announce("mla config3 full B64 H128 L4096, every row")
     inp = W.make_mla_config(3)
     out, lse = run(inp)
-    seqs = [0, 31, 63]
-    ro, rl = oracle_rows(inp, seqs)
-    err = assert_parity(out[seqs], lse[seqs], ro, rl, what="config3 full")
+    ro, rl = oracle_rows(inp, range(64))
+    err = assert_parity(out, lse, ro, rl, what="config3 full")
     print("config3 full max row rel err, max lse err:", err)
-    assert np.isfinite(out).all() and np.isfinite(lse).all()
 
 
 def test_config4_long_context_all_rows():
@@ -87,19 +73,10 @@ def test_config4_long_context_all_rows():
     print("config4 max row rel err, max lse err:", err, "lens", inp.seq_lens)
 
 
-def assert_small_L(inp, out, lse, what, seqs=None):
+def assert_all(inp, out, lse, what, seqs=None):
     seqs = list(range(len(inp.seq_lens)) if seqs is None else seqs)
-    out, lse = out[seqs], lse[seqs]
     ro, rl = oracle_rows(inp, seqs)
-    bound = qtilde_score_bound(inp, seqs)
-    full = np.isfinite(rl)
-    assert_parity(out, lse, ro, rl, lse_atol=np.inf, what=what)   # outputs + empty rows
-    lerr = np.abs(lse[full] - rl[full])
-    lim = np.maximum(1e-3, bound[full] + 1e-5)
-    assert np.all(lerr <= lim), f"{what}: lse error {lerr.max():.3e} over bound"
-    if not full.any():
-        return 0.0, 0.0
-    return float(row_rel_err(out[full], ro[full]).max()), float(lerr.max())
+    return assert_parity(out[seqs], lse[seqs], ro, rl, what=what)
 
 
 EDGE = [
@@ -122,7 +99,7 @@ def test_edge_cases(B, H, lens):
     announce(f"mla edge B{B} H{H} lens{lens}")
     inp = W.make_mla(B, H, lens, seed=21, max_seq_len=max(lens) + 5, pad_value=NAN)
     out, lse = run(inp)
-    print("errors:", assert_small_L(inp, out, lse, what=f"edge {lens}"))
+    print("errors:", assert_all(inp, out, lse, what=f"edge {lens}"))
 
 
 @pytest.mark.parametrize("splits", [1, 2, 5, 0, 40])
@@ -151,8 +128,7 @@ def test_balanced_splits_over_many_sequences():
     assert da.mla_num_splits(qn, qr, cache, wuv) == 0      # balanced on the device
     del qn, qr, cache, wuv
     p_out, p_lse = run(inp)
-    for c0 in range(0, 300, 50):
-        print(assert_small_L(inp, p_out, p_lse, what=f"B300 seqs {c0}..", seqs=range(c0, c0 + 50)))
+    print(assert_all(inp, p_out, p_lse, what="B300"))
 
 
 def test_stages_compose_to_the_full_call():
@@ -216,6 +192,5 @@ def test_late_dominant_row_forces_reference_restart():
     out, lse = run(inp, num_splits=1)
     ro, rl = oracle_rows(inp, range(B))
     assert rl[0, 5] > 100                      # the planted row dominates head 5
-    # one row carries almost all the weight, so no averaging of the q~ rounding:
-    # the lse is held to the per-row bound of the short-sequence cases
-    print("errors:", assert_small_L(inp, out, lse, what="late dominant row"))
+    # one row carries almost all the weight (no averaging of score errors)
+    print("errors:", assert_parity(out, lse, ro, rl, what="late dominant row"))
