@@ -660,133 +660,145 @@ def workload_name(w):
 # CPU baseline: the fp64 oracle on a bounded sample of the same workload
 # ----------------------------------------------------------------------------
 
-def cpu_baseline(plans, budget_s):
+def oracle_calls(kind, inp):
+    """One closure per sequence that runs the fp64 oracle on that sequence
+    alone, with the cached rows it covers (1 per sequence for appends).
+    Inputs are widened to fp64 outside the closures (not timed)."""
     from oracle.attention import (gqa_decode_paged_ref, gqa_decode_ref, mla_absorbed_paged_ref,
                                   mla_absorbed_ref)
-    from oracle.fp8 import gqa_decode_fp8_ref
+    from oracle.fp8 import gqa_append_rope_fp8_ref, gqa_decode_fp8_paged_ref, gqa_decode_fp8_ref
     from oracle.rope import gqa_append_rope_ref, mla_append_rope_ref
-    from oracle.fp8 import gqa_append_rope_fp8_ref
     import workloads as W
+    f = (lambda a: W.bf16_to_f32(a).astype(np.float64))
+    pools = None
+    if kind.endswith("-paged"):
+        inp, pools = inp
+    calls = []
+    if "-append" in kind:
+        for b in range(len(inp.positions)):
+            if kind == "gqa-append-fp8":
+                args = (inp.f64("q")[b:b + 1], inp.f64("k_new")[b:b + 1], inp.f64("v_new")[b:b + 1],
+                        inp.positions[b:b + 1], 4096, inp.q.shape[2], 0)
+                calls.append((lambda a=args: gqa_append_rope_fp8_ref(*a), 1))
+                continue
+            # one sequence per call into a one-page pool (page size 16): the
+            # same rotation and row write, without copying a whole cache
+            tab = np.zeros((1, -(-4096 // 16)), np.int32)
+            if kind == "gqa-append":
+                Hkv, D = inp.k_new.shape[1], inp.k_new.shape[2]
+                pool = np.zeros((1, 16, Hkv, D))
+                args = (inp.f64("q")[b:b + 1], inp.f64("k_new")[b:b + 1], inp.f64("v_new")[b:b + 1],
+                        inp.positions[b:b + 1], pool, pool, 4096, D, 0)
+                calls.append((lambda a=args, t=tab: gqa_append_rope_ref(*a, block_table=t, page_size=16), 1))
+            else:
+                pool = np.zeros((1, 16, 576))
+                args = (inp.f64("q")[b:b + 1], inp.f64("k_new")[b:b + 1], inp.positions[b:b + 1],
+                        pool, 4096, 64, 0)
+                calls.append((lambda a=args, t=tab: mla_append_rope_ref(*a, block_table=t, page_size=16), 1))
+        return calls
+    lens = inp.seq_lens
+    for b in range(len(lens)):
+        L = int(lens[b])
+        sl = lens[b:b + 1]
+        if kind in ("gqa-paged", "mla-paged", "gqa-fp8-paged"):
+            ps = 32 if kind == "gqa-fp8-paged" else PAGE_SIZE
+            pages = pools["table"][b, :max(1, -(-L // ps))]
+            # only the sequence's own pages, renumbered, go to the oracle
+            tab = np.arange(len(pages), dtype=np.int32)[None]
+        if kind == "gqa-paged":
+            args = (f(inp.q[b:b + 1]), f(pools["k_pool"][pages]), f(pools["v_pool"][pages]), tab,
+                    PAGE_SIZE, sl, inp.scale)
+            calls.append((lambda a=args: gqa_decode_paged_ref(*a), L))
+        elif kind == "mla-paged":
+            args = (f(inp.q_nope[b:b + 1]), f(inp.q_rope[b:b + 1]), f(pools["pool"][pages]), tab,
+                    PAGE_SIZE, sl, f(inp.w_uk), f(inp.w_uv), inp.scale)
+            calls.append((lambda a=args: mla_absorbed_paged_ref(*a), L))
+        elif kind == "gqa-fp8-paged":
+            kp, vp, ksp, vsp = pools["pools"]
+            args = (f(inp.q[b:b + 1]), kp[pages], vp[pages], ksp[pages], vsp[pages], tab, 32, sl, inp.scale)
+            calls.append((lambda a=args: gqa_decode_fp8_paged_ref(*a), L))
+        elif kind == "gqa-fp8":
+            args = (f(inp.q[b:b + 1]), inp.k[b:b + 1, :L], inp.v[b:b + 1, :L], inp.k_scale[b:b + 1, :L],
+                    inp.v_scale[b:b + 1, :L], sl, inp.scale)
+            calls.append((lambda a=args: gqa_decode_fp8_ref(*a), L))
+        elif kind in ("gqa", "gqa-window"):
+            conv = f if inp.dtype == "bf16" else (lambda a: a.astype(np.float64))
+            args = (conv(inp.q[b:b + 1]), conv(inp.k[b:b + 1, :L]), conv(inp.v[b:b + 1, :L]), sl, inp.scale)
+            w = WINDOW if kind == "gqa-window" else 0
+            calls.append((lambda a=args, w=w: gqa_decode_ref(*a, window=w), min(L, w) if w else L))
+        else:
+            args = (f(inp.q_nope[b:b + 1]), f(inp.q_rope[b:b + 1]), f(inp.cache[b:b + 1, :L]), sl,
+                    f(inp.w_uk), f(inp.w_uv), inp.scale)
+            calls.append((lambda a=args: mla_absorbed_ref(*a), L))
+    return calls
+
+
+def cpu_model():
     try:
-        from threadpoolctl import threadpool_info
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def cpu_baseline(plans, budget_s):
+    """The fp64 oracle on the host cores, timed for one step's worth of work.
+
+    For every path of the step the oracle runs one sequence per call. The
+    sample is every sequence when that fits the time budget, else the first
+    sequences of each path; the time of the whole step is the sample's time
+    scaled by (the path's cached rows / the sample's rows). Each timing is the
+    median of 3 runs, with numpy's BLAS at all host threads and again at one
+    thread. value = the step's algorithmic bytes (weights counted once per
+    call, as for the GPU) / the all-thread step time, in GB/s."""
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
+        threadpool_limits = None
         threads = 1
-    done_bytes, spent, samples = 0, 0.0, []
-    per_kind_budget = budget_s / max(1, len(plans))
+    paths = []
     for kind, (calls, alg, info, inp) in plans:
-        pools = None
-        if kind.endswith("-paged"):
-            inp, pools = inp
-        t_kind, n = 0.0, 0
-        B = len(inp.positions) if "-append" in kind else len(inp.seq_lens)
-        while t_kind < per_kind_budget and n < B:
-            b = n
-            if kind == "gqa-paged":
-                f = (lambda a: W.bf16_to_f32(a).astype(np.float64))
-                L = int(inp.seq_lens[b])
-                pages = pools["table"][b, :-(-L // PAGE_SIZE)]
-                # only the sequence's own pages, renumbered, go to the oracle
-                tab = np.arange(len(pages), dtype=np.int32)[None]
-                args = (f(inp.q[b:b + 1]), f(pools["k_pool"][pages]), f(pools["v_pool"][pages]),
-                        tab, PAGE_SIZE, inp.seq_lens[b:b + 1], inp.scale)
-                t = time.perf_counter()
-                gqa_decode_paged_ref(*args)
-                dt = time.perf_counter() - t
-                a1 = gqa_alg(1, inp.q.shape[1], inp.k.shape[2], inp.q.shape[2], L)
-            elif kind == "mla-paged":
-                f = (lambda a: W.bf16_to_f32(a).astype(np.float64))
-                L = int(inp.seq_lens[b])
-                pages = pools["table"][b, :-(-L // PAGE_SIZE)]
-                tab = np.arange(len(pages), dtype=np.int32)[None]
-                args = (f(inp.q_nope[b:b + 1]), f(inp.q_rope[b:b + 1]), f(pools["pool"][pages]), tab,
-                        PAGE_SIZE, inp.seq_lens[b:b + 1], f(inp.w_uk), f(inp.w_uv), inp.scale)
-                t = time.perf_counter()
-                mla_absorbed_paged_ref(*args)
-                dt = time.perf_counter() - t
-                a1 = mla_alg(1, inp.q_nope.shape[1], L)
-            elif kind == "gqa-fp8-paged":
-                from oracle.fp8 import gqa_decode_fp8_paged_ref
-                L = int(inp.seq_lens[b])
-                kp, vp, ksp, vsp = pools["pools"]
-                pages = pools["table"][b, :-(-L // 32)]
-                tab = np.arange(len(pages), dtype=np.int32)[None]
-                args = (W.bf16_to_f32(inp.q[b:b + 1]).astype(np.float64), kp[pages], vp[pages], ksp[pages],
-                        vsp[pages], tab, 32, inp.seq_lens[b:b + 1], inp.scale)
-                t = time.perf_counter()
-                gqa_decode_fp8_paged_ref(*args)
-                dt = time.perf_counter() - t
-                a1 = gqa_alg(1, inp.q.shape[1], inp.k.shape[2], inp.q.shape[2], L, elem=1)
-            elif kind == "gqa-fp8":
-                L = int(inp.seq_lens[b])
-                args = (W.bf16_to_f32(inp.q[b:b + 1]).astype(np.float64), inp.k[b:b + 1, :L],
-                        inp.v[b:b + 1, :L], inp.k_scale[b:b + 1, :L], inp.v_scale[b:b + 1, :L],
-                        inp.seq_lens[b:b + 1], inp.scale)
-                t = time.perf_counter()
-                gqa_decode_fp8_ref(*args)
-                dt = time.perf_counter() - t
-                a1 = gqa_alg(1, inp.q.shape[1], inp.k.shape[2], inp.q.shape[2], L, elem=1)
-            elif kind == "gqa-append-fp8":
-                t = time.perf_counter()
-                gqa_append_rope_fp8_ref(inp.f64("q")[b:b + 1], inp.f64("k_new")[b:b + 1],
-                                        inp.f64("v_new")[b:b + 1], inp.positions[b:b + 1], 4096,
-                                        inp.q.shape[2], 0)
-                dt = time.perf_counter() - t
-                a1 = dict(total=alg["total"] // B)
-            elif kind in ("gqa-append", "mla-append"):
-                # one sequence per call into a one-page pool (page size 16):
-                # the same rotation and row write, without copying a whole cache
-                tab = np.zeros((1, -(-4096 // 16)), np.int32)
-                if kind == "gqa-append":
-                    Hkv, D = inp.k_new.shape[1], inp.k_new.shape[2]
-                    pool = np.zeros((1, 16, Hkv, D))
-                    args = (inp.f64("q")[b:b + 1], inp.f64("k_new")[b:b + 1], inp.f64("v_new")[b:b + 1],
-                            inp.positions[b:b + 1], pool, pool, 4096, D, 0)
-                    t = time.perf_counter()
-                    gqa_append_rope_ref(*args, block_table=tab, page_size=16)
-                else:
-                    pool = np.zeros((1, 16, 576))
-                    args = (inp.f64("q")[b:b + 1], inp.f64("k_new")[b:b + 1], inp.positions[b:b + 1],
-                            pool, 4096, 64, 0)
-                    t = time.perf_counter()
-                    mla_append_rope_ref(*args, block_table=tab, page_size=16)
-                dt = time.perf_counter() - t
-                a1 = dict(total=alg["total"] // B)
-            elif kind == "gqa-window":
-                f = (lambda a: W.bf16_to_f32(a).astype(np.float64))
-                L = int(inp.seq_lens[b])
-                args = (f(inp.q[b:b + 1]), f(inp.k[b:b + 1, :L]), f(inp.v[b:b + 1, :L]),
-                        inp.seq_lens[b:b + 1], inp.scale)
-                t = time.perf_counter()
-                gqa_decode_ref(*args, window=WINDOW)
-                dt = time.perf_counter() - t
-                a1 = gqa_alg(1, inp.q.shape[1], inp.k.shape[2], inp.q.shape[2], min(L, WINDOW))
-            elif kind == "gqa":
-                f = (lambda a: W.bf16_to_f32(a).astype(np.float64))
-                L = int(inp.seq_lens[b])
-                args = (f(inp.q[b:b + 1]), f(inp.k[b:b + 1, :L]), f(inp.v[b:b + 1, :L]),
-                        inp.seq_lens[b:b + 1], inp.scale)
-                t = time.perf_counter()
-                gqa_decode_ref(*args)
-                dt = time.perf_counter() - t
-                a1 = gqa_alg(1, inp.q.shape[1], inp.k.shape[2], inp.q.shape[2], L)
-            else:
-                f = (lambda a: W.bf16_to_f32(a).astype(np.float64))
-                L = int(inp.seq_lens[b])
-                args = (f(inp.q_nope[b:b + 1]), f(inp.q_rope[b:b + 1]), f(inp.cache[b:b + 1, :L]),
-                        inp.seq_lens[b:b + 1], f(inp.w_uk), f(inp.w_uv), inp.scale)
-                t = time.perf_counter()
-                mla_absorbed_ref(*args)
-                dt = time.perf_counter() - t
-                a1 = mla_alg(1, inp.q_nope.shape[1], L)
-            t_kind += dt
-            done_bytes += a1["total"]
-            n += 1
-        spent += t_kind
-        samples.append(f"{kind}: {n} of {B} sequences")
-    return dict(value=round(done_bytes / spent / 1e9, 4), unit="GB/s", cores=int(threads),
-                kind="oracle", sample="; ".join(samples) + f"; {spent:.1f} s of oracle time",
-                seconds=round(spent, 2))
+        oc = oracle_calls(kind, inp)
+        paths.append(dict(kind=kind, calls=oc, rows=sum(r for _, r in oc), alg_bytes=int(alg["total"])))
+    # pilot: each path's first call, to size the sample
+    for p in paths:
+        t = time.perf_counter()
+        p["calls"][0][0]()
+        p["pilot"] = max(time.perf_counter() - t, 1e-6)
+    # 3 runs at all threads and 3 at one thread, one thread assumed up to 4x
+    # slower: one all-thread run may take budget / 15
+    per_path = budget_s / 15.0 / len(paths)
+    for p in paths:
+        n = int(max(1, min(len(p["calls"]), per_path // p["pilot"])))
+        p["sample"] = p["calls"][:n]
+        p["sample_rows"] = max(1, sum(r for _, r in p["sample"]))
+
+    def step_seconds():
+        total = 0.0
+        for p in paths:
+            t = time.perf_counter()
+            for fn, _ in p["sample"]:
+                fn()
+            total += (time.perf_counter() - t) * p["rows"] / p["sample_rows"]
+        return total
+
+    all_t = float(np.median([step_seconds() for _ in range(3)]))
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            one_t = float(np.median([step_seconds() for _ in range(3)]))
+    else:  # pragma: no cover
+        one_t = all_t
+    step_bytes = sum(p["alg_bytes"] for p in paths)
+    sample = "; ".join(f"{p['kind']}: {len(p['sample'])} of {len(p['calls'])} sequences" for p in paths)
+    return dict(value=round(step_bytes / all_t / 1e9, 4), unit="GB/s", cores=int(threads), kind="oracle",
+                sample=sample + ", step time scaled by cached rows, median of 3 runs",
+                seconds=all_t, step_alg_bytes=int(step_bytes),
+                single_thread=dict(value=round(step_bytes / one_t / 1e9, 4), seconds=round(one_t, 4)),
+                host_cpus=os.cpu_count(), cpu_model=cpu_model())
 
 
 def main():

@@ -42,10 +42,13 @@ def test_cpu_baseline_on_contiguous_and_paged_plans():
     (kp, vp), tg = bench.paged_pools(g.seq_lens, [g.k, g.v], seed=5)
     (pool,), tm = bench.paged_pools(m.seq_lens, [m.cache], seed=6)
     f8 = W.make_gqa_fp8(2, 8, 2, 128, [40, 9], seed=7)
-    plans = [("gqa", (None, None, None, g)), ("mla", (None, None, None, m)),
-             ("gqa-fp8", (None, None, None, f8)),
-             ("gqa-paged", (None, None, None, (g, dict(k_pool=kp, v_pool=vp, table=tg)))),
-             ("mla-paged", (None, None, None, (m, dict(pool=pool, table=tm)))),
+    ga = bench.gqa_alg(2, 8, 2, 128, int(g.seq_lens.sum()))
+    ma = bench.mla_alg(2, 16, int(m.seq_lens.sum()))
+    fa = bench.gqa_alg(2, 8, 2, 128, int(f8.seq_lens.sum()), elem=1)
+    plans = [("gqa", (None, ga, None, g)), ("mla", (None, ma, None, m)),
+             ("gqa-fp8", (None, fa, None, f8)),
+             ("gqa-paged", (None, ga, None, (g, dict(k_pool=kp, v_pool=vp, table=tg)))),
+             ("mla-paged", (None, ma, None, (m, dict(pool=pool, table=tm)))),
              ("gqa-append", (None, dict(total=2000), None, W.make_gqa_append(2, 8, 2, 128, 4096))),
              ("mla-append", (None, dict(total=2000), None, W.make_mla_append(2, 16, 4096))),
              ("gqa-append-fp8", (None, dict(total=2000), None, W.make_gqa_append(2, 8, 2, 128, 4096)))]
@@ -54,3 +57,19 @@ def test_cpu_baseline_on_contiguous_and_paged_plans():
     for kind in ("gqa", "mla", "gqa-paged", "mla-paged", "gqa-fp8", "gqa-append", "mla-append",
                  "gqa-append-fp8"):
         assert f"{kind}: 2 of 2 sequences" in res["sample"]
+    # one byte basis with the GPU figure: the step's algorithmic bytes (MLA
+    # weights once per call, not once per sequence) over the oracle's seconds
+    step_bytes = 2 * ga["total"] + 2 * ma["total"] + fa["total"] + 3 * 2000
+    assert res["step_alg_bytes"] == step_bytes
+    assert abs(res["value"] - step_bytes / res["seconds"] / 1e9) <= 1e-4 * res["value"] + 1e-4
+    assert res["single_thread"]["seconds"] > 0 and res["cpu_model"]
+
+
+def test_cpu_baseline_scales_a_partial_sample_by_rows():
+    # a budget too small for every sequence: the first sequences are timed
+    # and the step time is scaled by the path's rows over the sample's
+    g = W.make_gqa(6, 8, 2, 128, [64, 32, 32, 32, 32, 32], "bf16", seed=3, max_seq_len=64)
+    ga = bench.gqa_alg(6, 8, 2, 128, int(g.seq_lens.sum()))
+    res = bench.cpu_baseline([("gqa", (None, ga, None, g))], budget_s=1e-9)
+    assert "gqa: 1 of 6 sequences" in res["sample"]
+    assert abs(res["value"] - ga["total"] / res["seconds"] / 1e9) <= 1e-4 * res["value"] + 1e-4
