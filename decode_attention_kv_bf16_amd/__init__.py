@@ -123,6 +123,9 @@ _SIGNATURES = {
     "da_mla_absorb_query": (ctypes.c_int, [ctypes.POINTER(MlaParams), _vp, _vp, _vp, _vp, _vp]),
     "da_mla_attend_split_pass": (ctypes.c_int, [ctypes.POINTER(MlaParams), _vp, _vp, _vp, _vp,
                                                 _vp, _vp]),
+    "da_mla_decode_absorbed_noalloc": (ctypes.c_int, [ctypes.POINTER(MlaParams), _vp, _vp, _vp, _vp, _vp,
+                                                      _vp, _vp, _vp, _vp]),
+    "da_noalloc_scratch_bytes": (ctypes.c_size_t, []),
     "da_mla_merge_project": (ctypes.c_int, [ctypes.POINTER(MlaParams), _vp, _vp, _vp, _vp, _vp,
                                             _vp, _vp]),
     "da_gqa_decode_paged": (ctypes.c_int, [_GQA_P, _PAGED_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -597,6 +600,40 @@ def mla_decode_absorbed(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_cache: to
                                   _ptr(seq_lens), _ptr(w_uk), _ptr(w_uv), _ptr(out), _ptr(lse),
                                   _ptr(ws), ws_bytes, _stream_handle())
     _check(st, "da_mla_decode_absorbed")
+    return out, lse
+
+
+def mla_decode_absorbed_noalloc(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_cache: torch.Tensor,
+                                w_uk: torch.Tensor, w_uv: torch.Tensor,
+                                seq_lens: Optional[torch.Tensor] = None,
+                                softmax_scale: Optional[float] = None, num_splits: int = 0,
+                                out: Optional[torch.Tensor] = None,
+                                lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mla_decode_absorbed through da_mla_decode_absorbed_noalloc: no
+    workspace is allocated (the library's built-in scratch serves). With out
+    and lse given, the call allocates nothing at all."""
+    for name, t in (("q_nope", q_nope), ("q_rope", q_rope), ("kv_cache", kv_cache),
+                    ("w_uk", w_uk), ("w_uv", w_uv)):
+        _require_cuda(name, t)
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+    for name, t in (("q_nope", q_nope), ("q_rope", q_rope), ("w_uk", w_uk), ("w_uv", w_uv)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, H, _ = q_nope.shape
+    if q_rope.shape[:2] != (B, H) or w_uk.shape[0] != H or w_uv.shape[0] != H:
+        raise ValueError("head counts disagree")
+    if seq_lens is not None:
+        _check_seq_lens(seq_lens, B)
+    p = mla_params(q_nope, kv_cache, w_uv, q_rope, softmax_scale, num_splits)
+    if out is None:
+        out = torch.empty((B, H, w_uv.shape[2]), dtype=torch.float32, device=q_nope.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q_nope.device)
+    st = lib().da_mla_decode_absorbed_noalloc(ctypes.byref(p), _ptr(q_nope), _ptr(q_rope), _ptr(kv_cache),
+                                              _ptr(seq_lens), _ptr(w_uk), _ptr(w_uv), _ptr(out), _ptr(lse),
+                                              _stream_handle())
+    _check(st, "da_mla_decode_absorbed_noalloc")
     return out, lse
 
 

@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <initializer_list>
+#include <mutex>
 
 #include "da_internal.h"
 #include "decode_attn.h"
@@ -469,6 +470,41 @@ da::AppendArgs append_args(const da_append_t* ap, const da_paged_kv_t* pages,
 }  // namespace
 
 
+// ---------------------------------------------------------------------------
+// Scratch for the call that allocates nothing
+// ---------------------------------------------------------------------------
+// A file-scope device array in place of a caller workspace: each device that
+// loads the library holds its own copy until the process ends. Host code never
+// passes the array's name to a kernel (on the host it stands for a host-side
+// shadow, not a device address): its device address is looked up once per
+// device and kept here.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];
+
+// Device address of the current device's scratch; null if it cannot be had.
+void* current_device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_addr[dev] = ptr;
+  }
+  return g_scratch_addr[dev];
+}
+}  // namespace
+
 extern "C" {
 
 da_status_t da_gqa_append_rope(const da_gqa_params_t* p, const da_append_t* ap,
@@ -695,6 +731,26 @@ da_status_t da_mla_decode_absorbed(const da_mla_params_t* p, const void* q_nope,
   set_q_hat(a, ws);
   set_partials(a, pl, ws + pl.q_hat_bytes, ws + pl.q_hat_bytes + pl.part_out_bytes);
   return from_hip(da::launch_mla_decode(a, static_cast<hipStream_t>(hip_stream)));
+}
+
+size_t da_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+da_status_t da_mla_decode_absorbed_noalloc(const da_mla_params_t* p, const void* q_nope,
+                                           const void* q_rope, const void* kv_cache,
+                                           const int32_t* seq_lens, const void* w_uk, const void* w_uv,
+                                           float* out, float* lse, void* hip_stream) {
+  da_status_t st = check_mla_params(p);
+  if (st != DA_OK) return st;
+  const size_t need = plan_mla(p).workspace;
+  if (need > kScratchBytes) return DA_ERR_WORKSPACE_TOO_SMALL;
+  st = check_ptrs16({q_nope, q_rope, kv_cache, w_uk, w_uv, out});
+  if (st != DA_OK) return st;
+  if (!aligned4(seq_lens) || !aligned4(lse)) return DA_ERR_INVALID_ARGUMENT;
+  void* ws = current_device_scratch();
+  if (!ws) return DA_ERR_HIP;
+  // the scratch needs no clearing: every call writes each byte it reads first
+  return da_mla_decode_absorbed(p, q_nope, q_rope, kv_cache, seq_lens, w_uk, w_uv, out, lse, ws,
+                                kScratchBytes, hip_stream);
 }
 
 da_status_t da_mla_absorb_query(const da_mla_params_t* p, const void* q_nope, const void* q_rope,

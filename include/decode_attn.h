@@ -230,6 +230,31 @@ DA_EXPORT da_status_t da_mla_decode_absorbed(const da_mla_params_t* params,
                                    void* workspace, size_t workspace_bytes,
                                    void* hip_stream);
 
+/*
+ * da_mla_decode_absorbed without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation). Same arguments, kernels and
+ * results as da_mla_decode_absorbed; its workspace is a fixed scratch array
+ * built into the library (da_noalloc_scratch_bytes(): 64 MiB), of which
+ * every device that loads the library holds its own copy until the process
+ * ends. The call allocates and frees nothing.
+ * Calls that overlap on one device (other streams, other threads) share that
+ * array and race: order them on one stream. Nothing needs clearing between
+ * calls: every call writes each scratch byte before reading it.
+ * Errors: as da_mla_decode_absorbed; WORKSPACE_TOO_SMALL (before anything is
+ * launched) when these parameters need more workspace than the scratch
+ * holds (da_mla_decode_workspace_size > da_noalloc_scratch_bytes); HIP when
+ * the scratch's device address cannot be obtained.
+ */
+DA_EXPORT da_status_t da_mla_decode_absorbed_noalloc(const da_mla_params_t* params,
+                                                     const void* q_nope, const void* q_rope,
+                                                     const void* kv_cache, const int32_t* seq_lens,
+                                                     const void* w_uk, const void* w_uv,
+                                                     float* out, float* lse, void* hip_stream);
+
+/* Bytes of the built-in scratch that da_mla_decode_absorbed_noalloc uses. */
+DA_EXPORT size_t da_noalloc_scratch_bytes(void);
+
 /* Stage 1, query-side absorption (arganzheng.life section 4.5; jianzhnie.github.io
  * section 4, "Absorb"): with q~ = q_nope[b,h] W_UK[h]^T (float32 accumulation),
  * q_hat[b, h, :] = [bf16(q~) | q_rope[b,h]].
@@ -435,8 +460,8 @@ DA_EXPORT da_status_t da_gqa_append_rope(const da_gqa_params_t* params, const da
  *  - read from the arrays, when stride_t == 0 (per-head or per-tensor scales,
  *    fixed by the caller).
  * k_cache and v_cache hold one-byte codes (strides in bytes), contiguous
- * caches only: `pages` must be NULL (paged E4M3 pools: UNSUPPORTED, as for
- * decode). Errors: as da_gqa_append_rope, plus those of da_gqa_decode_fp8 for
+ * caches only: `pages` must be NULL (appending into paged E4M3 pools is
+ * UNSUPPORTED; da_gqa_decode_fp8_paged reads such pools). Errors: as da_gqa_append_rope, plus those of da_gqa_decode_fp8 for
  * the scales, and UNSUPPORTED for a nonzero token stride with a zero head
  * stride. */
 DA_EXPORT da_status_t da_gqa_append_rope_fp8(const da_gqa_params_t* params, const da_append_t* append,

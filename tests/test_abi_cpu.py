@@ -446,3 +446,21 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(da, "_lib", None)
     with pytest.raises(da.LibraryMissing):
         da.lib()
+
+
+@needs_lib
+@cpu_only
+def test_noalloc_mla_rejects_oversize_on_the_host():
+    # parameters whose workspace exceeds the built-in scratch are rejected
+    # before anything else (no device needed, nothing launched)
+    L = da.lib()
+    assert L.da_noalloc_scratch_bytes() == 64 << 20
+    big = mla(512, 128, 32768)
+    assert L.da_mla_decode_workspace_size(ctypes.byref(big)) > 64 << 20
+    st = L.da_mla_decode_absorbed_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                                          None, None)
+    assert st == 3
+    assert L.da_mla_decode_absorbed_noalloc(ctypes.byref(mla(H=80)), FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                            FAKE, None, None) == 2
+    # config 3 fits
+    assert L.da_mla_decode_workspace_size(ctypes.byref(mla())) <= 64 << 20
