@@ -14,15 +14,17 @@
 //  1. mla_absorb_kernel   q^ = [q_nope W_UK^T | q_rope] (bf16) for all (b, h).
 //  2. mla_attend_kernel   one workgroup per (split, sequence); for 128 heads,
 //     4 waves of 32 heads each (one wave per SIMD, accumulators in AGPRs).
-//     32-row latent tiles are copied HBM -> LDS by the load-to-LDS path
-//     (global_load_lds_dwordx4, no register staging), double-buffered; each
-//     tile is read from LDS as the A operand of S^T (row-major 16-byte reads)
-//     and, transposed by ds_read_b64_tr_b16, as the A operand of O^T. Each
-//     head's softmax reference max is fixed by its first tile, so the
-//     accumulators are never rescaled in the loop (see kRefHeadroom). Each
-//     split writes its normalised o~_s (bf16) and lse_s.
-//  3. mla_merge_project_kernel  merges the splits by log-sum-exp and multiplies
-//     by W_UV,h on the matrix cores (W_UV,h staged in LDS, read transposed).
+//     32-row latent tiles are copied HBM -> LDS by the buffer load-to-LDS
+//     path (buffer_load_dwordx4 ... lds, no register staging) into a ring of
+//     4 tiles; each tile is read from LDS as the A operand of S^T (row-major
+//     16-byte reads) and, transposed by ds_read_b64_tr_b16, as the A operand
+//     of O^T. Each head's softmax reference max is fixed by its first tile, so
+//     the accumulators are never rescaled in the loop (see kRefHeadroom).
+//     Each split writes its normalised o~_s (bf16) and lse_s.
+//  3. mla_merge_project_kernel  merges the splits by log-sum-exp, corrects each
+//     lse for the bf16 rounding of q~ (with q~_lo from kernel 1) and
+//     multiplies by W_UV,h on the matrix cores (W_UV,h staged in LDS, read
+//     transposed).
 #include "da_device.h"
 #include "da_internal.h"
 
