@@ -24,6 +24,16 @@ each new (token, KV head) row x with s = max|x| / 448 (dynamic) or a given s
 448. The scale and x / s are taken in float32, the kernel's precision, since
 they decide integer codes.
 
+An absorbed-MLA latent cache in E4M3 ("Attention variants and KV cache",
+section 4.8 item 3: the nope and rope ranges of a cached row have different
+numeric ranges and are quantized apart; section 6.3 for the format and the
+halved bytes): row j = [c_kv_j (512) ; k_rope_j (64)] is stored as 576
+codes with two fp32 scales per (sequence, token), one for the c_kv range
+and one for the k_rope range. Its value is
+[decode(codes[:512]) * scale_nope ; decode(codes[512:]) * scale_rope];
+the attention is then exactly mla_absorbed_ref on those values. Quantizing
+such a row takes each range's own dynamic scale max|range| / 448.
+
 Parity status: pinned by tests/test_oracle_pins.py (decoder against torch's
 float8_e4m3fn conversion for all 256 codes and against the format's defining
 values; attention against brute force and closed forms with scales; encoder
@@ -155,3 +165,39 @@ def gqa_decode_fp8_paged_ref(q, k_pool, v_pool, k_scale_pool, v_scale_pool, bloc
             k[b, t] = dequantize_ref(k_pool[page, r], k_scale_pool[page, r])
             v[b, t] = dequantize_ref(v_pool[page, r], v_scale_pool[page, r])
     return gqa_decode_ref(q, k, v, seq_lens, scale, window)
+
+
+def dequantize_mla_rows_ref(codes, scale_nope, scale_rope, kv_lora_rank: int = 512) -> np.ndarray:
+    """Latent rows [..., d_c + d_rope] from E4M3 codes with one scale per row
+    for the c_kv range [0, d_c) and one for the k_rope range [d_c, ...)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    nope = dequantize_ref(c[..., :kv_lora_rank], scale_nope)
+    rope = dequantize_ref(c[..., kv_lora_rank:], scale_rope)
+    return np.concatenate([nope, rope], axis=-1)
+
+
+def quantize_mla_rows_ref(rows, kv_lora_rank: int = 512):
+    """rows [..., d_c + d_rope] -> (codes, scale_nope, scale_rope): each range
+    quantized by quantize_rows_ref with its own dynamic scale."""
+    rows = np.asarray(rows)
+    cn, sn = quantize_rows_ref(rows[..., :kv_lora_rank])
+    cr, sr = quantize_rows_ref(rows[..., kv_lora_rank:])
+    return np.concatenate([cn, cr], axis=-1), sn, sr
+
+
+def mla_absorbed_fp8_ref(q_nope, q_rope, codes, scale_nope, scale_rope, seq_lens, w_uk, w_uv,
+                         scale: float, kv_lora_rank: int = 512):
+    """Absorbed MLA decode over an E4M3 latent cache: codes [B, L, d_c + d_rope]
+    uint8, scale_nope and scale_rope [B, L]; each sequence's first L_b rows are
+    dequantized range by range (dequantize_mla_rows_ref) and attended as by
+    mla_absorbed_ref. Returns out [B, H, d_v] and lse [B, H]."""
+    from oracle.attention import mla_absorbed_ref
+    seq_lens = np.asarray(seq_lens, np.int64)
+    B = np.shape(q_nope)[0]
+    L = int(max(1, seq_lens.max(initial=0)))
+    rows = np.zeros((B, L, np.shape(codes)[2]))
+    for b in range(B):
+        Lb = int(seq_lens[b])
+        rows[b, :Lb] = dequantize_mla_rows_ref(codes[b, :Lb], scale_nope[b, :Lb], scale_rope[b, :Lb],
+                                               kv_lora_rank)
+    return mla_absorbed_ref(q_nope, q_rope, rows, seq_lens, w_uk, w_uv, scale, kv_lora_rank)

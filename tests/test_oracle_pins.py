@@ -634,6 +634,139 @@ def test_fp8_workload_codes_round_trip():
 
 
 # ----------------------------------------------------------------------------
+# MLA over an E4M3 latent cache, nope and rope ranges scaled apart
+# ("Attention variants and KV cache", sections 4.8 and 6.3)
+# ----------------------------------------------------------------------------
+
+def _mla_fp8_inputs(B, H, d_c, d_r, d_n, lens, seed):
+    rng = np.random.default_rng(seed)
+    L = max(lens)
+    codes = rng.integers(0, 256, (B, L, d_c + d_r)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38                 # no NaN codes
+    sn = rng.uniform(0.002, 0.01, (B, L))                 # the nope range: small values
+    sr = rng.uniform(0.05, 0.2, (B, L))                   # the rope range: larger ones
+    qn = rng.standard_normal((B, H, d_n))
+    qr = rng.standard_normal((B, H, d_r))
+    wuk = rng.standard_normal((H, d_c, d_n)) / math.sqrt(d_c)
+    wuv = rng.standard_normal((H, d_c, 5)) / math.sqrt(d_c)
+    return qn, qr, codes, sn, sr, wuk, wuv
+
+
+def brute_mla_fp8(qn, qr, codes, sn, sr, seq_lens, wuk, wuv, scale, d_c):
+    """Scalar loops with math.fsum: decode every code, scale it by its
+    range's scale, absorb, attend the latent rows, project."""
+    B, H, d_n = qn.shape
+    d_v = wuv.shape[2]
+    out = np.zeros((B, H, d_v))
+    lse = np.full((B, H), -np.inf)
+    for b in range(B):
+        L = int(seq_lens[b])
+        if L == 0:
+            continue
+        rows = [[brute_e4m3(int(codes[b, j, c])) * (sn[b, j] if c < d_c else sr[b, j])
+                 for c in range(codes.shape[2])] for j in range(L)]
+        for h in range(H):
+            qt = [math.fsum(wuk[h, c, e] * qn[b, h, e] for e in range(d_n)) for c in range(d_c)]
+            qh = qt + list(qr[b, h])
+            s = [scale * math.fsum(qh[c] * rows[j][c] for c in range(len(qh))) for j in range(L)]
+            m = max(s)
+            ex = [math.exp(x - m) for x in s]
+            z = math.fsum(ex)
+            lse[b, h] = m + math.log(z)
+            ot = [math.fsum(ex[j] / z * rows[j][c] for j in range(L)) for c in range(d_c)]
+            for e in range(d_v):
+                out[b, h, e] = math.fsum(ot[c] * wuv[h, c, e] for c in range(d_c))
+    return out, lse
+
+
+@pytest.mark.parametrize("H,d_c,d_r,lens", [(2, 8, 4, [3, 1]), (3, 4, 2, [5, 0]), (1, 8, 0, [4])])
+def test_fp8_mla_brute_force(H, d_c, d_r, lens):
+    qn, qr, codes, sn, sr, wuk, wuv = _mla_fp8_inputs(len(lens), H, d_c, d_r, 3, lens, seed=H + d_c)
+    o, l = OF.mla_absorbed_fp8_ref(qn, qr, codes, sn, sr, lens, wuk, wuv, 0.4, kv_lora_rank=d_c)
+    bo, bl = brute_mla_fp8(qn, qr, codes, sn, sr, lens, wuk, wuv, 0.4, d_c)
+    np.testing.assert_allclose(o, bo, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(l, bl, rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_mla_ranges_scale_apart():
+    qn, qr, codes, sn, sr, wuk, wuv = _mla_fp8_inputs(2, 3, 8, 4, 3, [6, 4], seed=17)
+    lens = [6, 4]
+    o1, l1 = OF.mla_absorbed_fp8_ref(qn, qr, codes, sn, sr, lens, wuk, wuv, 0.5, kv_lora_rank=8)
+    # the rope scale multiplies only the rope part of every score: scaling it
+    # by c equals scaling q_rope by c, and leaves the value (c_kv) alone
+    o2, l2 = OF.mla_absorbed_fp8_ref(qn, qr, codes, sn, 3 * sr, lens, wuk, wuv, 0.5, kv_lora_rank=8)
+    o3, l3 = OF.mla_absorbed_fp8_ref(qn, 3 * qr, codes, sn, sr, lens, wuk, wuv, 0.5, kv_lora_rank=8)
+    np.testing.assert_allclose(o2, o3, rtol=1e-12)
+    np.testing.assert_allclose(l2, l3, rtol=1e-12)
+    # a zero rope scale removes the rope term: the same as q_rope = 0
+    o4, l4 = OF.mla_absorbed_fp8_ref(qn, qr, codes, sn, 0 * sr, lens, wuk, wuv, 0.5, kv_lora_rank=8)
+    o5, l5 = OF.mla_absorbed_fp8_ref(qn, 0 * qr, codes, sn, sr, lens, wuk, wuv, 0.5, kv_lora_rank=8)
+    np.testing.assert_allclose(o4, o5, rtol=1e-12)
+    np.testing.assert_allclose(l4, l5, rtol=1e-12)
+    # zero nope and rope scales: every score 0, the rows are zero: lse = ln L, out = 0
+    o6, l6 = OF.mla_absorbed_fp8_ref(qn, qr, codes, 0 * sn, 0 * sr, lens, wuk, wuv, 0.5, kv_lora_rank=8)
+    np.testing.assert_allclose(l6, np.log(np.asarray(lens, float))[:, None] * np.ones((1, 3)), rtol=1e-13)
+    assert np.all(o6 == 0)
+    # the ranges are not interchangeable: one scale for the whole row differs
+    o7, _ = OF.mla_absorbed_fp8_ref(qn, qr, codes, sn, sn, lens, wuk, wuv, 0.5, kv_lora_rank=8)
+    assert not np.allclose(o7, o1, rtol=1e-3)
+
+
+def test_fp8_mla_equals_bf16_oracle_on_dequantized_rows_and_explicit_path():
+    from oracle.attention import mla_absorbed_ref, mla_explicit_ref
+    qn, qr, codes, sn, sr, wuk, wuv = _mla_fp8_inputs(2, 4, 16, 8, 6, [7, 3], seed=23)
+    lens = [7, 3]
+    o, l = OF.mla_absorbed_fp8_ref(qn, qr, codes, sn, sr, lens, wuk, wuv, 0.3, kv_lora_rank=16)
+    rows = OF.dequantize_mla_rows_ref(codes, sn, sr, kv_lora_rank=16)
+    # the dequantized row is the pair of ranges, each at its own scale
+    assert np.array_equal(rows[..., :16], e4m3_to_float(codes[..., :16]) * sn[..., None])
+    assert np.array_equal(rows[..., 16:], e4m3_to_float(codes[..., 16:]) * sr[..., None])
+    ob, lb = mla_absorbed_ref(qn, qr, rows, lens, wuk, wuv, 0.3, kv_lora_rank=16)
+    oe, le = mla_explicit_ref(qn, qr, rows, lens, wuk, wuv, 0.3, kv_lora_rank=16)
+    np.testing.assert_allclose(o, ob, rtol=1e-13)
+    np.testing.assert_allclose(o, oe, rtol=1e-10)
+    np.testing.assert_allclose(l, le, rtol=1e-12)
+
+
+def test_fp8_mla_quantizer_scales_each_range_by_its_own_max():
+    rng = np.random.default_rng(31)
+    rows = np.concatenate([rng.standard_normal((5, 512)) * 1e-3, rng.standard_normal((5, 64)) * 300], axis=1)
+    rows = rows.astype(np.float32)
+    codes, sn, sr = OF.quantize_mla_rows_ref(rows)
+    np.testing.assert_array_equal(sn, (np.abs(rows[:, :512]).max(axis=1) / np.float32(448)).astype(np.float32))
+    np.testing.assert_array_equal(sr, (np.abs(rows[:, 512:]).max(axis=1) / np.float32(448)).astype(np.float32))
+    back = OF.dequantize_mla_rows_ref(codes, sn, sr)
+    # round to nearest: within half an E4M3 step (relative 2^-4) of each range's max
+    for lo, hi, s in ((0, 512, sn), (512, 576, sr)):
+        err = np.abs(back[:, lo:hi] - rows[:, lo:hi]) / (448 * s[:, None])
+        assert err.max() <= 2.0 ** -4
+    # with ranges this far apart one scale for the whole row would put the
+    # nope values below E4M3's smallest subnormal (they become 0); the
+    # separate scales keep them to 3 significant bits
+    c1, s1 = OF.quantize_rows_ref(rows)
+    one = OF.dequantize_ref(c1, s1)
+    sep_err = np.abs(back[:, :512] - rows[:, :512]).max()
+    one_err = np.abs(one[:, :512] - rows[:, :512]).max()
+    assert sep_err * 10 < one_err
+
+
+def test_fp8_mla_workload_codes_round_trip():
+    # each range decodes to within half an E4M3 step of the drawn values,
+    # relative to that range's own scale; padding rows are NaN
+    inp = W.make_mla_fp8(2, 16, [9, 4], seed=6, max_seq_len=12, rope_std=50.0)
+    for b, L in enumerate(inp.seq_lens):
+        x = np.random.default_rng([6, 0, 2, b]).standard_normal((L, 576), dtype=np.float32)
+        x[:, 512:] *= np.float32(50.0)
+        back = OF.dequantize_mla_rows_ref(inp.cache[b, :L], inp.scale_nope[b, :L], inp.scale_rope[b, :L])
+        for lo, hi, s in ((0, 512, inp.scale_nope[b, :L]), (512, 576, inp.scale_rope[b, :L])):
+            assert (np.abs(back[:, lo:hi] - x[:, lo:hi]) / (448 * s[:, None])).max() <= 2.0 ** -4
+    assert np.all(inp.cache[0, 9:] == W.FP8_NAN_CODE) and np.isnan(inp.scale_rope[1, 4:]).all()
+    # same queries and weights as the bf16 generator
+    m = W.make_mla(2, 16, [9, 4], seed=6, max_seq_len=12)
+    assert np.array_equal(inp.q_nope, m.q_nope) and np.array_equal(inp.w_uv, m.w_uv)
+
+
+# ----------------------------------------------------------------------------
 # sliding window ("Attention variants and KV cache", section 5.3)
 # ----------------------------------------------------------------------------
 

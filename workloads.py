@@ -301,6 +301,66 @@ def make_mla_config(cfg: int, seed: int = BASE_SEED, pad_value: float = 0.0,
                     pad_value=pad_value, only_seqs=only_seqs)
 
 
+@dataclass
+class MLAFp8Inputs:
+    """Host copies of one absorbed-MLA decode problem over an E4M3 latent cache.
+
+    q_nope, q_rope, w_uk, w_uv as in MLAInputs (bf16 bit patterns); cache
+    [B, L_max, d_c + d_rope] uint8 E4M3 codes; scale_nope, scale_rope
+    [B, L_max] float32: row (b, t) stands for
+    [code[:d_c] * scale_nope[b, t] ; code[d_c:] * scale_rope[b, t]].
+    """
+    q_nope: np.ndarray
+    q_rope: np.ndarray
+    cache: np.ndarray
+    scale_nope: np.ndarray
+    scale_rope: np.ndarray
+    w_uk: np.ndarray
+    w_uv: np.ndarray
+    seq_lens: np.ndarray
+    scale: float
+    meta: dict = field(default_factory=dict)
+
+
+def make_mla_fp8(batch: int, num_heads: int, seq_lens: Sequence[int], cfg: int = 0,
+                 seed: int = BASE_SEED, max_seq_len: Optional[int] = None,
+                 rope_std: float = 1.0, pad_nan: bool = True) -> MLAFp8Inputs:
+    """DeepSeek-V3 latent shapes (d_c 512, d_rope 64, d_nope = d_v = 128). The
+    queries and weights are make_mla's (same streams); each cached row is drawn
+    as make_mla draws it (k_rope times rope_std), in float32, and each of its
+    two ranges is quantized with its own scale max|range| / 448. Rows past a
+    sequence's length hold the NaN code and NaN scales when pad_nan, else 0."""
+    m = make_mla(batch, num_heads, [0] * batch, cfg=cfg, seed=seed, max_seq_len=1)
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    L_max = int(max_seq_len if max_seq_len is not None else max(1, int(seq_lens.max(initial=0))))
+    B = batch
+    codes = np.full((B, L_max, 576), FP8_NAN_CODE if pad_nan else 0, np.uint8)
+    pad = np.float32(np.nan if pad_nan else 0.0)
+    sn = np.full((B, L_max), pad, np.float32)
+    sr = np.full((B, L_max), pad, np.float32)
+    for b in range(B):
+        L = int(seq_lens[b])
+        if L == 0:
+            continue
+        x = _normal(np.random.default_rng([seed, cfg, 2, b]), (L, 576))
+        x[:, 512:] *= np.float32(rope_std)
+        for lo, hi, sc in ((0, 512, sn), (512, 576, sr)):
+            s = (np.maximum(np.abs(x[:, lo:hi]).max(axis=1), 1e-30) / E4M3_MAX).astype(np.float32)
+            codes[b, :L, lo:hi] = encode_e4m3(x[:, lo:hi] / s[:, None])
+            sc[b, :L] = s
+    return MLAFp8Inputs(m.q_nope, m.q_rope, codes, sn, sr, m.w_uk, m.w_uv, seq_lens, m.scale,
+                        meta=dict(cfg=cfg, seed=seed, rope_std=rope_std))
+
+
+def make_mla_fp8_config(cfg: int, seed: int = BASE_SEED) -> MLAFp8Inputs:
+    """An MLA config's shapes and lengths with the latent cache in E4M3."""
+    s = CONFIGS[cfg]
+    assert isinstance(s, MLAShape)
+    lens = draw_seq_lens(s.batch, s.seq_len, s.seq_len_range, cfg, seed)
+    L_max = s.seq_len if s.seq_len is not None else s.seq_len_range[1]
+    return make_mla_fp8(s.batch, s.num_heads, lens, cfg=cfg, seed=seed, max_seq_len=L_max)
+
+
 # ----------------------------------------------------------------------------
 # paged caches
 # ----------------------------------------------------------------------------
