@@ -35,6 +35,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 #define LDS __attribute__((address_space(3)))
 
 constexpr int kDc = 512;            // latent (value) width
@@ -50,6 +51,10 @@ constexpr int kTileDma = kTileB / 1024;       // wave-wide 1 KiB copies per tile
 // split with a raised reference instead of rescaling the accumulators, which
 // live in AGPRs where arithmetic cannot touch them.
 constexpr float kRefHeadroom = 64.0f;
+// LDS row of one head's normalised 512-wide output when a split stages it for
+// the store: 1 KiB + 16 bytes, so that the 32 heads a store instruction covers
+// fall on different banks.
+constexpr int kOutRowB = kDc * 2 + 16;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -99,6 +104,16 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
 // transposing 8-byte reads of 4 consecutive rows x 32 bytes (the O^T operand).
 // Rows r and r + 16 share f, so one lane offset serves both halves of a tile.
 __device__ __forceinline__ int row_swizzle(int row) { return row & 7; }
+
+// The swizzle of the 32x32x16 kernel, whose operand reads take other row
+// sets: (a) 16-byte reads of 32 consecutive rows at one logical chunk and
+// (b) transposing 8-byte reads of 4 consecutive rows x 64 bytes per 32 lanes.
+// With f(r) = r mod 8 both conflict 2-way (rows one apart on the same banks;
+// measured 50% conflict cycles); f(r) = 4 ((r >> 1) & 1) + ((r >> 2) & 3)
+// gives rows 4k and 4k + 2 disjoint chunk sets and any 8 rows of one parity
+// 8 different ones, and measured no conflict cycles for either pattern. f is
+// the same for rows r and r + 16, not for r and r + 8.
+__device__ __forceinline__ int row_swizzle32(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
 
 // Two block-table entries of a paged pool, read with scalar loads that are
 // issued together and waited for once, inside this block (so no load is left
@@ -689,6 +704,366 @@ void mla_attend_kernel(MlaArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// 2b. split-KV latent attention on 32x32x16 matrix ops
+// ---------------------------------------------------------------------------
+// The same computation, tiles, LDS ring, split assignment and softmax
+// reference as mla_attend_kernel, for head counts that are multiples of 32:
+// NW waves of 32 heads each, every wave one 32x32 block of heads. A 32x32x16
+// operation does the work of two 16x16x32 ones in one instruction, so a
+// 32-row tile takes a wave 36 score and 32 value instructions instead of 72
+// and 64, and each lane keeps the 32 tokens' scores of one head in 16
+// registers. One wave per SIMD issues every instruction of its tile in
+// order, so the instructions around the matrix ops (LDS reads, softmax, copy
+// issue, waits) bound how busy the matrix core can be; this form issues
+// about half as many.
+//
+// Operand layouts of v_mfma_f32_32x32x16_bf16 (lane l, g = l / 32):
+//   A [32 x 16]: row l % 32, k = 8 g .. 8 g + 7     (8 bf16 per lane)
+//   B [16 x 32]: column l % 32, k = 8 g .. 8 g + 7
+//   D [32 x 32]: column l % 32, rows 8 i + 4 g + r in register 4 i + r
+// Scores S^T = C q^^T: A = the tile's rows (row-major 16-byte LDS reads),
+// B = q^ of the lane's head, D = [token x head]: lane l holds head l % 32 at
+// tokens 8 i + 4 g + r. Values O^T += C[:, :512]^T P^T in 16 column blocks of
+// 32: B = the weights, contraction element e of matrix op m standing for
+// token 16 m + 8 (e / 4) + 4 g + e % 4, which is exactly score register
+// 8 m + e of the lane; A = the tile read transposed, 4 rows per
+// ds_read_b64_tr_b16, two reads per operand (rows 16 m + 4 g .. + 3 and
+// 16 m + 8 + 4 g .. + 3).
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// The score chain in vector registers. The 32x32 output accumulators take all
+// 256 accumulation registers of a wave; left to itself the compiler also puts
+// the score accumulator there and moves 16 output registers out and back on
+// every tile. Written as asm with "v" operands, the chain stays in vector
+// registers. Hazards the compiler does not see in asm: a chained operation
+// reading the previous one's result as its accumulator input with the same
+// shape and registers needs no wait (the hardware forwards it); vector-ALU
+// reads of the final result need the result written back, so the last step
+// of the chain is followed by 24 wait states inside its own asm block. The
+// A and B operands come from LDS and global loads, whose completion the
+// compiler's own waits cover (it sees the asm's register operands).
+__device__ __forceinline__ void qk_first(f32x16_t& s, bf16x8_t a, bf16x8_t b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void qk_next(f32x16_t& s, bf16x8_t a, bf16x8_t b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void qk_last(f32x16_t& s, bf16x8_t a, bf16x8_t b) {
+  asm volatile(
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+      "s_nop 7\n\t"
+      "s_nop 7\n\t"
+      "s_nop 7"
+      : "+v"(s)
+      : "v"(a), "v"(b));
+}
+
+template <int NW, bool kPaged>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_attend32_kernel(MlaArgs a) {
+  constexpr int kCopies = kTileDma / NW;
+  static_assert(kTileDma % NW == 0, "copies split evenly over the waves");
+  constexpr int kDepth = (3 * kCopies <= 63) ? 4 : 2;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kDepth * kTileB];
+  LDS uint8_t* lds = (LDS uint8_t*)smem;
+  static_assert(kDepth * kTileB >= NW * 32 * kOutRowB, "the output staging fits in the ring");
+
+  constexpr int H = NW * 32;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int j16 = lane & 15, q16 = lane >> 4;
+  const SplitWork work = assign_split(a, lane, blockIdx.x == 0 && w == 0);
+  if (!work.valid) return;
+  const int b = work.b;
+  const int64_t slot = work.slot;
+  const int t_begin = work.t_begin;
+  const int t_end = work.t_end;
+
+  if (t_begin >= t_end) {  // fixed splits only: a split past the sequence's end
+    for (int i = tid; i < H; i += NW * 64) a.part_lse[slot * H + i] = kNegInf;
+    return;
+  }
+
+  const uint16_t* cache_b = a.cache + (int64_t)b * a.cache_sb;
+  const int ntiles = (t_end - t_begin + kTok - 1) / kTok;
+
+  // HBM -> LDS copies of one tile, exactly as in mla_attend_kernel
+  const uint32_t row_bytes = (uint32_t)a.cache_st * 2u;
+  uint32_t voff[kCopies];
+#pragma unroll
+  for (int i = 0; i < kCopies; ++i) {
+    const int p = (w + NW * i) * 64 + lane;
+    const int row = p / kChunks;
+    const int c = (p - row * kChunks) ^ row_swizzle32(row);
+    voff[i] = (uint32_t)(kPaged ? row & 15 : row) * row_bytes + 16u * (uint32_t)c;
+  }
+  const uint32_t lds_w0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds + (uint32_t)w * 1024u);
+  const int64_t tab0 = (int64_t)b * a.max_blocks;
+  auto tile_src = [&](int it) {
+    const int t0 = t_begin + it * kTok;
+    if constexpr (kPaged) {
+      int32_t page[2];
+      load_two_entries(a.block_table + tab0 + (min(t0, t_end - 1) >> a.page_shift),
+                       a.block_table + tab0 + (min(t0 + 16, t_end - 1) >> a.page_shift), page[0], page[1]);
+      PagedTile pt;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int th = t0 + 16 * hf;
+        const int rows = __builtin_amdgcn_readfirstlane(min(max(t_end - th, 0), 16));
+        const uint16_t* base = a.cache + (int64_t)page[hf] * a.page_stride +
+                               (int64_t)(th & ((1 << a.page_shift) - 1)) * a.cache_st;
+        pt.half[hf] = make_raw_rsrc(base, (uint32_t)rows * row_bytes);
+      }
+      return pt;
+    } else {
+      return make_raw_rsrc(cache_b + (int64_t)t0 * a.cache_st, (uint32_t)max(t_end - t0, 0) * row_bytes);
+    }
+  };
+  using TileSrc = decltype(tile_src(0));
+  auto settle = [&](const TileSrc& src) {
+    if constexpr (kPaged) asm volatile("" ::"s"(src.half[0]), "s"(src.half[1]));
+  };
+  auto issue_copy = [&](const TileSrc& src, int i, int buf) {
+    const uint32_t dst = lds_w0 + (uint32_t)(buf * kTileB + NW * i * 1024);
+    if constexpr (kPaged) {
+      constexpr int kHalf = kTileDma / 2;
+      const int second = NW * i >= kHalf ? 1 : NW * i + NW <= kHalf ? 0 : (w + NW * i >= kHalf);
+      buffer_load_to_lds16(__builtin_amdgcn_readfirstlane(second) ? src.half[1] : src.half[0], voff[i], dst);
+    } else {
+      buffer_load_to_lds16(src, voff[i], dst);
+    }
+  };
+  auto issue_tile = [&](int it, int buf) {
+    const TileSrc src = tile_src(it);
+    settle(src);
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) issue_copy(src, i, buf);
+  };
+
+  // absorbed query of the lane's head as B operands: q^[h][16 ks + 8 g .. + 8]
+  const int h = 32 * w + l32;
+  bf16x8_t qb[36];
+  {
+    const uint16_t* qp = a.q_hat + ((int64_t)b * H + h) * kRowE + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks) qb[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + 16 * ks));
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks) asm volatile("" ::"v"(qb[ks]));
+  }
+
+  float m_ref = kNegInf;  // reference max (log2 units) of the lane's head, fixed by the first tile
+  float thr = kNegInf;    // raw score above which the reference must be raised
+  // score operand reads: row l32, logical chunk 2 ks + g -> 8 (ks / 4) + ((2 (ks % 4) + g) ^ f)
+  const int f_s = row_swizzle32(l32);
+  int s_off[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) s_off[m] = l32 * kRowB + 16 * ((2 * m + g) ^ f_s);
+  // transposed reads: rows r_t (+ 16 m) and r_t + 8 (+ 16 m) with r_t = 4 (q16 / 2) + j16 / 4,
+  // columns 32 cb + 16 (q16 % 2) + 0..15; the swizzle differs for the two rows
+  const int r_t = 4 * (q16 >> 1) + (j16 >> 2);
+  int t_off[2][2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int cbl = 0; cbl < 2; ++cbl)
+      t_off[hf][cbl] = (r_t + 8 * hf) * kRowB +
+                       16 * ((4 * cbl + 2 * (q16 & 1) + ((j16 & 3) >> 1)) ^ row_swizzle32(r_t + 8 * hf)) +
+                       8 * (j16 & 1);
+
+  __shared__ int restart_flag;
+  if (tid == 0) restart_flag = 0;
+
+  f32x16_t o[16];
+  float l_part;  // this lane's share of sum_j 2^(s_j - m_ref) (the other tokens are in lane l ^ 32)
+
+  // S^T of tile `it`; the copies of tile `refill_it` go out spread over the k-steps
+  constexpr int kSRing = 5;
+  auto score_tile = [&](int it, int refill_it, const TileSrc& refill_src, f32x16_t& s) {
+    const int refill_buf = refill_it % kDepth;
+    const LDS uint8_t* tile = lds + (it % kDepth) * kTileB;
+    u32x4_t ra[kSRing];
+#pragma unroll
+    for (int ks = 0; ks < kSRing - 1; ++ks)
+      ra[ks] = *reinterpret_cast<const LDS u32x4_t*>(tile + s_off[ks & 3] + 128 * (ks >> 2));
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks) {
+#pragma unroll
+      for (int i = ks * kCopies / 36; i < (ks + 1) * kCopies / 36; ++i) issue_copy(refill_src, i, refill_buf);
+      const int kn = ks + kSRing - 1;
+      if (kn < 36) ra[kn % kSRing] = *reinterpret_cast<const LDS u32x4_t*>(tile + s_off[kn & 3] + 128 * (kn >> 2));
+      if (ks == 0)
+        qk_first(s, as_bf16x8(ra[0]), qb[0]);
+      else if (ks < 35)
+        qk_next(s, as_bf16x8(ra[ks % kSRing]), qb[ks]);
+      else
+        qk_last(s, as_bf16x8(ra[ks % kSRing]), qb[ks]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Softmax reference of tile `it` (as in mla_attend_kernel): rows past the
+  // split end get score -inf; only a split's first tile and a score beyond the
+  // headroom need the head-wide max, taken with the partner lane l ^ 32.
+  auto softmax_ref = [&](int it, f32x16_t& s) {
+    const int nv = t_end - (t_begin + it * kTok);
+    if (nv < kTok) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + 4 * g + (r & 3) >= nv) s[r] = kNegInf;
+    }
+    float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+    for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);
+    mx = fmaxf(mx, s[15]);
+    if (__builtin_amdgcn_ballot_w64(mx > thr) != 0) {
+      float m2 = mx * a.scale_log2;
+      m2 = fmaxf(m2, __shfl_xor(m2, 32));
+      if (m_ref == kNegInf) {
+        m_ref = m2;                              // first tile of the split
+      } else if (m2 > m_ref + kRefHeadroom) {   // rare: restart with a raised reference
+        m_ref = m2;
+        restart_flag = 1;
+      }
+      thr = (m_ref + kRefHeadroom) / a.scale_log2;
+    }
+  };
+  auto weight = [&](const f32x16_t& s, int r) { return exp2_hw(fmaf(s[r], a.scale_log2, -m_ref)); };
+  auto pack = [&](const float (&p)[16], bf16x8_t (&pb)[2]) {
+    l_part += (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]))) +
+              (((p[8] + p[9]) + (p[10] + p[11])) + ((p[12] + p[13]) + (p[14] + p[15])));
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      uint4 pw;
+      pw.x = cvt_bf16x2(p[8 * m + 0], p[8 * m + 1]);
+      pw.y = cvt_bf16x2(p[8 * m + 2], p[8 * m + 3]);
+      pw.z = cvt_bf16x2(p[8 * m + 4], p[8 * m + 5]);
+      pw.w = cvt_bf16x2(p[8 * m + 6], p[8 * m + 7]);
+      pb[m] = as_bf16x8(pw);
+    }
+  };
+  // O^T += C^T P^T for the tile in ring buffer `buf`, matrix op k = 16 m + cb;
+  // `extra(k)` runs in the shadow of matrix op k
+  constexpr int kTRing = 4;
+  i16x4_t tlo[kTRing], thi[kTRing];
+  auto read_t = [&](const LDS uint8_t* tile, int k) {
+    const int m = k >> 4, cb = k & 15;
+    const int off = 128 * (cb >> 1) + 16 * m * kRowB;
+    tlo[k % kTRing] = lds_read_tr(tile + t_off[0][cb & 1] + off);
+    thi[k % kTRing] = lds_read_tr(tile + t_off[1][cb & 1] + off);
+  };
+  auto pv_start = [&](int buf) {
+    const LDS uint8_t* tile = lds + buf * kTileB;
+#pragma unroll
+    for (int k = 0; k < kTRing - 1; ++k) read_t(tile, k);
+  };
+  auto pv_run = [&](int buf, const bf16x8_t (&pb)[2], auto&& extra) {
+    const LDS uint8_t* tile = lds + buf * kTileB;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      if (k + kTRing - 1 < 32) read_t(tile, k + kTRing - 1);
+      const int m = k >> 4, cb = k & 15;
+      o[cb] = mfma32x32x16(join_tr(tlo[k % kTRing], thi[k % kTRing]), pb[m], o[cb]);
+      extra(k);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  for (;;) {
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb) o[cb] = f32x16_t{};
+    l_part = 0.f;
+    f32x16_t s;
+    bf16x8_t pb[2];
+    if constexpr (kDepth == 4) {
+      // as in mla_attend_kernel: the weights of tile `it` are computed in the
+      // shadow of the value product of tile it - 1; tiles it + 1 and it + 2
+      // are in flight
+#pragma unroll
+      for (int j = 0; j < 2; ++j) issue_tile(j, j);
+      {
+        const TileSrc refill = tile_src(2);
+        wait_vm<kCopies>();
+        tile_barrier();
+        settle(refill);
+        score_tile(0, 2, refill, s);
+        softmax_ref(0, s);
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[r] = weight(s, r);
+        pack(p, pb);
+      }
+      for (int it = 1; it < ntiles; ++it) {
+        const TileSrc refill = tile_src(it + 2);
+        wait_vm<kCopies>();
+        tile_barrier();
+        settle(refill);
+        score_tile(it, it + 2, refill, s);
+        pv_start((it - 1) % kDepth);
+        softmax_ref(it, s);
+        float p[16];
+        pv_run((it - 1) % kDepth, pb, [&](int k) {
+          if ((k & 1) == 0) p[k >> 1] = weight(s, k >> 1);
+        });
+        pack(p, pb);
+      }
+      pv_start((ntiles - 1) % kDepth);
+      pv_run((ntiles - 1) % kDepth, pb, [](int) {});
+    } else {
+#pragma unroll
+      for (int j = 0; j < kDepth - 1; ++j) issue_tile(j, j);
+      for (int it = 0; it < ntiles; ++it) {
+        const TileSrc refill = tile_src(it + kDepth - 1);
+        wait_vm<(kDepth - 2) * kCopies>();
+        tile_barrier();
+        settle(refill);
+        score_tile(it, it + kDepth - 1, refill, s);
+        pv_start(it % kDepth);
+        softmax_ref(it, s);
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[r] = weight(s, r);
+        pack(p, pb);
+        pv_run(it % kDepth, pb, [](int) {});
+      }
+    }
+    wait_vm_all();
+    __syncthreads();
+    if (!restart_flag) break;
+    __syncthreads();  // every thread has seen the flag before it is cleared
+    if (tid == 0) restart_flag = 0;
+  }
+
+  // o~_s = O / l (bf16) through LDS (the ring is free: every wave has passed
+  // the barrier above), so that each head's 1 KiB row leaves in whole 16-byte
+  // pieces: lane l holds columns 32 cb + 8 i + 4 g .. + 3 of head l % 32
+  float l_tot = l_part + __shfl_xor(l_part, 32);
+  const float inv = 1.0f / l_tot;
+  LDS uint8_t* stage = lds + w * 32 * kOutRowB;
+#pragma unroll
+  for (int cb = 0; cb < 16; ++cb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u32x2_t v;
+      v.x = cvt_bf16x2(o[cb][4 * i + 0] * inv, o[cb][4 * i + 1] * inv);
+      v.y = cvt_bf16x2(o[cb][4 * i + 2] * inv, o[cb][4 * i + 3] * inv);
+      *reinterpret_cast<LDS u32x2_t*>(stage + l32 * kOutRowB + 2 * (32 * cb + 8 * i + 4 * g)) = v;
+    }
+  __syncthreads();
+  uint16_t* po = a.part_out + (slot * H + 32 * w) * kDc;
+#pragma unroll 4
+  for (int r = 0; r < 32; ++r)
+    *reinterpret_cast<u32x4_t*>(po + r * kDc + 8 * lane) =
+        *reinterpret_cast<const LDS u32x4_t*>(stage + r * kOutRowB + 16 * lane);
+  if (g == 0) a.part_lse[slot * H + h] = (m_ref + log2_hw(l_tot)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
 // 3. split merge + W_UV projection
 // ---------------------------------------------------------------------------
 // grid: H * n_groups workgroups of 8 waves; a workgroup serves one head and
@@ -703,9 +1078,29 @@ constexpr int kORowB = 1056;  // merged o~ row in LDS: 512 bf16 + 32 bytes pad
 
 __device__ __forceinline__ int wuv_swizzle(int row) { return 2 * ((row & 3) | (((row >> 3) & 1) << 2)); }
 
+// Per thread, the merge is online over its splits: a running reference m,
+// normaliser z and 16 weighted columns, rescaled when m grows. A batch of
+// kMergeBatch splits (their o~_s pieces and lse_s) is loaded at once, so a
+// row of up to kMergeBatch splits per thread is one round trip; the first
+// batch of the next block is loaded while the current block is projected.
+constexpr int kMergeBatch = 8;
+
+struct MergeRow {
+  int n_s;            // splits of the row the thread serves (0: no row)
+  int64_t s_base;     // part_lse index of split 0 of that row and head
+  int64_t s_step;     // index step between its splits
+};
+
+struct MergeBatch {
+  uint4 u[kMergeBatch][2];
+  float lse[kMergeBatch];
+};
+
 __global__ __launch_bounds__(512) void mla_merge_project_kernel(MlaArgs a, int n_groups, int bpg) {
   __shared__ __attribute__((aligned(1024))) uint8_t w_smem[kDc * 256];   // 131072
   __shared__ __attribute__((aligned(16))) uint8_t o_smem[16 * kORowB];   // 16896
+  __shared__ float m_sm[16], z_sm[16];  // reference and normaliser of each thread row
+  __shared__ float lse_sm[16];          // merged lse of the block's rows, before the correction
   LDS uint8_t* w_lds = (LDS uint8_t*)w_smem;
   LDS uint8_t* o_lds = (LDS uint8_t*)o_smem;
 
@@ -718,7 +1113,10 @@ __global__ __launch_bounds__(512) void mla_merge_project_kernel(MlaArgs a, int n
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int q4 = lane >> 4, l16 = lane & 15;
+  const int r = tid >> 5;        // thread (row slot r, columns 16 cs .. 16 cs + 15)
+  const int cs = tid & 31;
   const int64_t rows = (int64_t)B * H;
+  const bool bal = a.num_splits == 0;
 
   {  // stage W_UV,h by the load-to-LDS path: 128 KiB = 128 wave-wide copies
     const uint16_t* wsrc = a.w_uv + (int64_t)h * kDc * 128;
@@ -735,14 +1133,66 @@ __global__ __launch_bounds__(512) void mla_merge_project_kernel(MlaArgs a, int n
   const int tr_chunk = 2 * w + ((l16 & 3) >> 1);
   const int tr_half = 8 * (l16 & 1);
 
-  __shared__ float lse_sm[16];   // merged lse of the block's rows, before the correction
-  const int r = tid >> 5;        // thread (row slot r, columns 16 cs .. 16 cs + 15)
-  const int cs = tid & 31;
+  // Rows of block bb: R <= 16 valid rows; G = the largest power of two with
+  // G R <= 16 thread rows serve one row, group g taking the splits s = g
+  // (mod G). Slot r serves row r / G, group r % G.
+  auto block_rows = [&](int bb) { return min(16, B - bb * 16); };
+  auto groups_of = [](int R) {
+    int G = 1;
+    while (2 * G * R <= 16) G *= 2;
+    return G;
+  };
+  auto row_of = [&](int bb) -> MergeRow {
+    const int R = block_rows(bb);
+    const int G = groups_of(R);
+    const int rr = r / G;
+    MergeRow m{0, 0, 0};
+    if (rr >= R) return m;
+    const int bidx = bb * 16 + rr;
+    if (bal) {
+      // the splits of this sequence: slots P_b .. P_b + S_b - 1 (from the
+      // table the attention launch wrote), clamped to the slots that exist
+      const int P = min(max(a.split_table[2 * bidx], 0), a.slots);
+      m.n_s = min(a.split_table[2 * bidx + 1], a.slots - P);
+      m.s_base = (int64_t)P * H + h;
+      m.s_step = H;
+    } else {
+      m.n_s = a.num_splits;          // slots s * B + b
+      m.s_base = (int64_t)bidx * H + h;
+      m.s_step = rows;
+    }
+    return m;
+  };
+  // loads of the thread's splits g + G (j0 + j), j < kMergeBatch; splits that
+  // do not exist read nothing (lse -inf)
+  auto load_batch = [&](const MergeRow& m, int G, int g, int j0, MergeBatch& bt) {
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int s = g + G * (j0 + j);
+      bt.lse[j] = kNegInf;
+      bt.u[j][0] = bt.u[j][1] = make_uint4(0u, 0u, 0u, 0u);
+      if (s < m.n_s) {
+        const int64_t idx = m.s_base + s * m.s_step;
+        bt.lse[j] = a.part_lse[idx];
+        const uint4* src = reinterpret_cast<const uint4*>(a.part_out + idx * kDc + 16 * cs);
+        bt.u[j][0] = src[0];
+        bt.u[j][1] = src[1];
+      }
+    }
+  };
+
   const int nbb = (B + 15) / 16;
+  const int bb0 = grp * bpg;
+  MergeRow cur = bb0 < nbb ? row_of(bb0) : MergeRow{0, 0, 0};
+  MergeBatch bt;
+  if (bb0 < nbb) load_batch(cur, groups_of(block_rows(bb0)), r % groups_of(block_rows(bb0)), 0, bt);
+
   for (int bbi = 0; bbi < bpg; ++bbi) {
-    const int bb = grp * bpg + bbi;
+    const int bb = bb0 + bbi;
     if (bb >= nbb) break;
-    const int R = min(16, B - bb * 16);
+    const int R = block_rows(bb);
+    const int G = groups_of(R);
+    const int rr = r / G, g = r % G;
     // q~_lo of row r of the block (columns 16 cs ..), for the lse correction
     uint4 lo[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
     if (r < R && a.lse) {
@@ -750,111 +1200,107 @@ __global__ __launch_bounds__(512) void mla_merge_project_kernel(MlaArgs a, int n
       lo[0] = src[0];
       lo[1] = src[1];
     }
-    // Merge the splits: thread (slot r, 16 columns). With R < 16 valid rows in
-    // the block, G = the largest power of two with G R <= 16 slots serve one
-    // row, slot group g summing the splits s = g (mod G); the G partial rows
-    // are then added through LDS. The weights exp(lse_s - lse) use all splits.
-    {
-      int G = 1;
-      while (2 * G * R <= 16) G *= 2;
-      const int rr = r / G, g = r % G;
-      const int bidx = bb * 16 + rr;
-      float acc[16];
+    // online merge of the thread's splits (log2 domain)
+    float m2 = kNegInf, z = 0.f;
+    float acc[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-      if (rr < R) {
-        const int64_t row_id = (int64_t)bidx * H + h;
-        // the splits of this sequence: slots s * B + b (fixed) or P_b + s
-        // (balanced, from the table the attention launch wrote)
-        const bool bal = a.num_splits == 0;
-        // (the table is clamped to the slots that exist)
-        const int P = bal ? min(max(a.split_table[2 * bidx], 0), a.slots) : 0;
-        const int n_s = bal ? min(a.split_table[2 * bidx + 1], a.slots - P) : a.num_splits;
-        const int64_t s_base = bal ? (int64_t)P * H + h : row_id;
-        const int64_t s_step = bal ? (int64_t)H : rows;
-        // max and normaliser of the split lse values: the 32 threads of the
-        // row (one half-wave) read every 32nd split each and combine
-        float M = kNegInf;
-        for (int s = cs; s < n_s; s += 32) M = fmaxf(M, a.part_lse[s_base + s * s_step]);
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    for (int j0 = 0;; j0 += kMergeBatch) {
+      float bm = kNegInf;
 #pragma unroll
-        for (int off = 1; off < 32; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
-        float lse_out = kNegInf;
-        if (M != kNegInf) {
-          const float m2 = M * kLog2e;
-          float z = 0.f;
-          for (int s = cs; s < n_s; s += 32) {
-            const float v = a.part_lse[s_base + s * s_step];
-            if (v != kNegInf) z += exp2_hw(fmaf(v, kLog2e, -m2));
-          }
+      for (int j = 0; j < kMergeBatch; ++j) bm = fmaxf(bm, bt.lse[j] * kLog2e);
+      if (bm != kNegInf) {
+        const float mn = fmaxf(m2, bm);
+        const float f = exp2_hw(m2 - mn);   // 0 when m2 is -inf
+        z *= f;
 #pragma unroll
-          for (int off = 1; off < 32; off <<= 1) z += __shfl_xor(z, off);
-          const float inv_z = 1.0f / z;
-          // the partial rows are loaded kMergeBatch splits at a time, so their
-          // loads are in flight together; an empty split (lse -inf) was never
-          // written: its row is replaced by zeros rather than skipped
-          constexpr int kMergeBatch = 4;
-          for (int s0 = g; s0 < n_s; s0 += kMergeBatch * G) {
-            uint4 u[kMergeBatch][2];
-            float wgt[kMergeBatch];
+        for (int e = 0; e < 16; ++e) acc[e] *= f;
 #pragma unroll
-            for (int j = 0; j < kMergeBatch; ++j) {
-              const int s = s0 + j * G;
-              const float v = s < n_s ? a.part_lse[s_base + s * s_step] : kNegInf;
-              wgt[j] = v == kNegInf ? 0.f : exp2_hw(fmaf(v, kLog2e, -m2)) * inv_z;
-              const int s_in = s < n_s ? s : 0;
-              const uint4* src = reinterpret_cast<const uint4*>(a.part_out + (s_base + s_in * s_step) * kDc + 16 * cs);
-              u[j][0] = src[0];
-              u[j][1] = src[1];
-            }
+        for (int j = 0; j < kMergeBatch; ++j) {
+          const float wj = bt.lse[j] == kNegInf ? 0.f : exp2_hw(fmaf(bt.lse[j], kLog2e, -mn));
+          z += wj;
+          float fv[16];
+          unpack_bf16x8(bt.u[j][0], fv);
+          unpack_bf16x8(bt.u[j][1], fv + 8);
 #pragma unroll
-            for (int j = 0; j < kMergeBatch; ++j) {
-              const bool live = wgt[j] != 0.f;
-              float f[16];
-              unpack_bf16x8(live ? u[j][0] : make_uint4(0u, 0u, 0u, 0u), f);
-              unpack_bf16x8(live ? u[j][1] : make_uint4(0u, 0u, 0u, 0u), f + 8);
-#pragma unroll
-              for (int e = 0; e < 16; ++e) acc[e] = fmaf(wgt[j], f[e], acc[e]);
-            }
-          }
-          lse_out = M + log2_hw(z) * kLn2;
+          for (int e = 0; e < 16; ++e) acc[e] = fmaf(wj, fv[e], acc[e]);
         }
-        if (g == 0 && cs == 0) lse_sm[rr] = lse_out;
+        m2 = mn;
       }
-      auto store_row = [&](int slot, const float* v) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          u32x4_t w;
-          w.x = cvt_bf16x2(v[8 * j + 0], v[8 * j + 1]);
-          w.y = cvt_bf16x2(v[8 * j + 2], v[8 * j + 3]);
-          w.z = cvt_bf16x2(v[8 * j + 4], v[8 * j + 5]);
-          w.w = cvt_bf16x2(v[8 * j + 6], v[8 * j + 7]);
-          *reinterpret_cast<LDS u32x4_t*>(o_lds + slot * kORowB + 2 * (16 * cs + 8 * j)) = w;
-        }
-      };
-      store_row(r, acc);
-      if (G > 1) {  // add the G partial rows of each valid row into slot rr
-        __syncthreads();
-        float fin[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) fin[e] = 0.f;
-        if (g == 0 && rr < R) {
-          for (int gg = 0; gg < G; ++gg) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              const u32x4_t w =
-                  *reinterpret_cast<const LDS u32x4_t*>(o_lds + (rr * G + gg) * kORowB + 2 * (16 * cs + 8 * j));
-              float f[8];
-              unpack_bf16x8(uint4{w.x, w.y, w.z, w.w}, f);
-#pragma unroll
-              for (int e = 0; e < 8; ++e) fin[8 * j + e] += f[e];
-            }
-          }
-        }
-        __syncthreads();
-        if (g == 0) store_row(rr, fin);
-      }
+      if (g + G * (j0 + kMergeBatch) >= cur.n_s) break;
+      load_batch(cur, G, g, j0 + kMergeBatch, bt);
     }
-    wait_vm_all();
+    // this wave's W_UV copies have landed (the barriers below make every
+    // wave's visible); waited for here, before the next block's loads go out
+    if (bbi == 0) wait_vm_all();
+    // the next block's rows and first batch, in flight during this block's
+    // combine and projection
+    MergeRow nxt{0, 0, 0};
+    if (bbi + 1 < bpg && bb + 1 < nbb) {
+      nxt = row_of(bb + 1);
+      const int G1 = groups_of(block_rows(bb + 1));
+      load_batch(nxt, G1, r % G1, 0, bt);
+    }
+
+    auto store_row = [&](int slot, const float* v) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        u32x4_t wv;
+        wv.x = cvt_bf16x2(v[8 * j + 0], v[8 * j + 1]);
+        wv.y = cvt_bf16x2(v[8 * j + 2], v[8 * j + 3]);
+        wv.z = cvt_bf16x2(v[8 * j + 4], v[8 * j + 5]);
+        wv.w = cvt_bf16x2(v[8 * j + 6], v[8 * j + 7]);
+        *reinterpret_cast<LDS u32x4_t*>(o_lds + slot * kORowB + 2 * (16 * cs + 8 * j)) = wv;
+      }
+    };
+    if (G == 1) {
+      // one thread row per row: o~ = acc / z, lse = m + log z
+      if (rr < R) {
+        const float inv = z > 0.f ? 1.0f / z : 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] *= inv;
+        if (cs == 0) lse_sm[rr] = z > 0.f ? (m2 + log2_hw(z)) * kLn2 : kNegInf;
+      }
+      store_row(r, acc);
+    } else {
+      // G groups per row: share each group's (m, z), scale its columns by
+      // 2^(m_g - M) / Z and add the G rows through LDS
+      if (cs == 0) {
+        m_sm[r] = m2;
+        z_sm[r] = z;
+      }
+      __syncthreads();
+      float M = kNegInf, Z = 0.f;
+      if (rr < R) {
+        for (int gg = 0; gg < G; ++gg) M = fmaxf(M, m_sm[rr * G + gg]);
+        if (M != kNegInf)
+          for (int gg = 0; gg < G; ++gg) Z += z_sm[rr * G + gg] * exp2_hw(m_sm[rr * G + gg] - M);
+      }
+      const float f = (rr < R && Z > 0.f && m2 != kNegInf) ? exp2_hw(m2 - M) / Z : 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] *= f;
+      store_row(r, acc);
+      __syncthreads();
+      float fin[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) fin[e] = 0.f;
+      if (g == 0 && rr < R) {
+        for (int gg = 0; gg < G; ++gg) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const u32x4_t wv =
+                *reinterpret_cast<const LDS u32x4_t*>(o_lds + (rr * G + gg) * kORowB + 2 * (16 * cs + 8 * j));
+            float fv[8];
+            unpack_bf16x8(uint4{wv.x, wv.y, wv.z, wv.w}, fv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) fin[8 * j + e] += fv[e];
+          }
+        }
+        if (cs == 0) lse_sm[rr] = Z > 0.f ? (M + log2_hw(Z)) * kLn2 : kNegInf;
+      }
+      __syncthreads();
+      if (g == 0) store_row(rr, fin);
+    }
     __syncthreads();
 
     // lse of row r: the scores were computed with bf16(q~); with q~ itself
@@ -887,9 +1333,9 @@ __global__ __launch_bounds__(512) void mla_merge_project_kernel(MlaArgs a, int n
       const u32x4_t av = *reinterpret_cast<const LDS u32x4_t*>(o_lds + l16 * kORowB + 2 * (32 * ks + 8 * q4));
       const int row_lo = 32 * ks + tr_row;
       const int row_hi = row_lo + 4;
-      const i16x4_t lo = lds_read_tr(w_lds + row_lo * 256 + 16 * (tr_chunk ^ wuv_swizzle(row_lo)) + tr_half);
-      const i16x4_t hi = lds_read_tr(w_lds + row_hi * 256 + 16 * (tr_chunk ^ wuv_swizzle(row_hi)) + tr_half);
-      acc2 = mfma16x16x32(as_bf16x8(av), join_tr(lo, hi), acc2);
+      const i16x4_t lo_t = lds_read_tr(w_lds + row_lo * 256 + 16 * (tr_chunk ^ wuv_swizzle(row_lo)) + tr_half);
+      const i16x4_t hi_t = lds_read_tr(w_lds + row_hi * 256 + 16 * (tr_chunk ^ wuv_swizzle(row_hi)) + tr_half);
+      acc2 = mfma16x16x32(as_bf16x8(av), join_tr(lo_t, hi_t), acc2);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -897,6 +1343,7 @@ __global__ __launch_bounds__(512) void mla_merge_project_kernel(MlaArgs a, int n
       if (bidx < B) a.out[((int64_t)bidx * H + h) * 128 + 16 * w + l16] = acc2[i];
     }
     __syncthreads();  // o_lds is rewritten by the next block
+    cur = nxt;
   }
 }
 
@@ -907,17 +1354,18 @@ hipError_t launch_mla_absorb(const MlaArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Head counts with an attention shape: NW waves of HB blocks of 16 heads, NW
-// dividing the 36 copies of a tile.
+// Head counts with an attention shape. Multiples of 32 run the 32x32x16
+// kernel (NW waves of 32 heads); 16 and 48 the 16x16x32 one (NW waves of HB
+// blocks of 16 heads). NW divides the 36 copies of a tile.
 template <bool kPaged, typename F>
 bool with_attend_shape(int num_heads, F&& f) {
   switch (num_heads) {
     case 16: f(mla_attend_kernel<1, 1, kPaged>, 1); return true;
-    case 32: f(mla_attend_kernel<2, 1, kPaged>, 2); return true;
+    case 32: f(mla_attend32_kernel<1, kPaged>, 1); return true;
     case 48: f(mla_attend_kernel<3, 1, kPaged>, 3); return true;
-    case 64: f(mla_attend_kernel<4, 1, kPaged>, 4); return true;
-    case 96: f(mla_attend_kernel<3, 2, kPaged>, 3); return true;
-    case 128: f(mla_attend_kernel<4, 2, kPaged>, 4); return true;
+    case 64: f(mla_attend32_kernel<2, kPaged>, 2); return true;
+    case 96: f(mla_attend32_kernel<3, kPaged>, 3); return true;
+    case 128: f(mla_attend32_kernel<4, kPaged>, 4); return true;
     default: return false;
   }
 }
