@@ -143,73 +143,131 @@ struct PagedTile {
 // ---------------------------------------------------------------------------
 // 1. query absorption
 // ---------------------------------------------------------------------------
-// 8 slices of 64 latent columns per head; one wave each. Computes the transpose
-// q~^T[c, b] = sum_e W_UK[h, c, e] q_nope[b, h, e] so that each lane ends up
-// with 4 consecutive latent columns of one batch row (one 8-byte store).
-// Both operands are read in their stored layout (e contiguous).
-constexpr int kAbsorbBatch = 64;   // batch rows per pass (4 blocks of 16)
+// A workgroup of 4 waves serves one head h, one half of the 512 latent
+// columns (256) and up to 64 batch rows. W_UK[h] rows of its half (64 KiB)
+// are copied HBM -> LDS by the load-to-LDS path; q_nope rows of its batch
+// block (16 KiB) by ordinary loads into LDS. Wave w computes
+// q~^T[c, b] = sum_e W_UK[h, c, e] q_nope[b, h, e] for columns 64 w .. + 63
+// on 16x16x32 matrix ops (both operands read from LDS, 16-byte reads of 16
+// rows at one chunk, rows XOR-swizzled by row mod 16), then writes bf16(q~)
+// and q~_lo = bf16(q~ - bf16(q~)) into LDS, so that every row of q^ and of
+// q~_lo leaves in whole 16-byte pieces. The workgroups of the first half
+// also copy q_rope into q^.
+constexpr int kAbsorbRows = 64;    // batch rows per workgroup
+constexpr int kAbsorbCols = 256;   // latent columns per workgroup
+constexpr int kAbsorbOutB = 2 * kAbsorbCols * 2 + 16;   // staged row: hi | lo (bf16) + pad
 
-__global__ __launch_bounds__(64) void mla_absorb_kernel(MlaArgs a) {
-  // Workgroups are dealt to the 8 XCDs round-robin by linear id; this mapping
-  // puts the 8 slices of a head on one XCD, so its q_nope column is fetched
-  // from HBM once and then served by that XCD's L2.
-  const int id = blockIdx.x;
-  const int slice = (id >> 3) & 7;
-  const int h = (id & 7) + 8 * (id >> 6);
+__device__ __forceinline__ int absorb_chunk(int row, int chunk) { return chunk ^ (row & 15); }
+
+__global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a) {
+  // W rows (256 x 256 B), then q rows (64 x 256 B); once both are read, the
+  // same bytes stage the outputs (64 rows x kAbsorbOutB)
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kAbsorbCols * 256 + kAbsorbRows * 256];
+  static_assert(kAbsorbRows * kAbsorbOutB <= kAbsorbCols * 256 + kAbsorbRows * 256, "staging fits");
+  LDS uint8_t* w_lds = (LDS uint8_t*)smem;
+  LDS uint8_t* q_lds = w_lds + kAbsorbCols * 256;
+
   const int H = a.num_heads;
   const int B = a.batch;
-  const int lane = threadIdx.x;
+  // grid: (head, half) pairs, batch blocks; the two halves of a head share an
+  // XCD (linear id mod 8 picks the XCD) so its q_nope rows come from one L2
+  const int x = blockIdx.x;
+  const int h = (x >> 4) * 8 + (x & 7);
+  const int half = (x >> 3) & 1;
+  const int b0 = blockIdx.y * kAbsorbRows;
+  const int nb = min(kAbsorbRows, B - b0);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
   const int q4 = lane >> 4, l16 = lane & 15;
-  const int c0 = 64 * slice;
+  const int c0 = half * kAbsorbCols;
 
-  bf16x8_t wa[4][4];   // A: W_UK[h, c0 + 16cb + l16, 32ks + 8q4 .. +8]
-  const uint16_t* wp = a.w_uk + ((int64_t)h * kDc + c0 + l16) * 128 + 8 * q4;
+  {  // W_UK[h, c0 .. c0 + 255, :]: 64 wave-wide 1 KiB copies, 16 per wave;
+     // lane l of copy k fills LDS chunk 64 k + l (row 4k + l / 16)
+    const uint16_t* wsrc = a.w_uk + ((int64_t)h * kDc + c0) * 128;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int k = w + 4 * i;
+      const int p = k * 64 + lane;
+      const int row = p >> 4;
+      const int c = absorb_chunk(row, p & 15);
+      load_to_lds16(wsrc + row * 128 + 8 * c, w_lds + k * 1024);
+    }
+  }
+  {  // q_nope rows b0 .. b0 + nb - 1 of head h (zeros past the batch)
+    for (int p = tid; p < kAbsorbRows * 16; p += 256) {
+      const int row = p >> 4, c = p & 15;
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (row < nb) v = *reinterpret_cast<const u32x4_t*>(a.q_nope + ((int64_t)(b0 + row) * H + h) * 128 + 8 * c);
+      *reinterpret_cast<LDS u32x4_t*>(q_lds + row * 256 + 16 * absorb_chunk(row, c)) = v;
+    }
+  }
+  wait_vm_all();
+  __syncthreads();
+
+  // wave w: columns c0 + 64 w + 16 cb + (0..15), batch rows 16 bb + (0..15)
+  f32x4_t acc[4][4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      wa[cb][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(wp + cb * 16 * 128 + 32 * ks));
-
-  for (int b0 = 0; b0 < B; b0 += kAbsorbBatch) {
-    bf16x8_t qb[4][4];  // B: q_nope[b0 + 16bb + l16, h, 32ks + 8q4 .. +8]
+    for (int bb = 0; bb < 4; ++bb) acc[cb][bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
-      const int b = b0 + 16 * bb + l16;
+  for (int ks = 0; ks < 4; ++ks) {
+    bf16x8_t wa[4], qb[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (b < B) v = *reinterpret_cast<const uint4*>(a.q_nope + ((int64_t)b * H + h) * 128 + 32 * ks + 8 * q4);
-        qb[bb][ks] = as_bf16x8(v);
-      }
+    for (int cb = 0; cb < 4; ++cb) {
+      const int row = 64 * w + 16 * cb + l16;
+      wa[cb] = as_bf16x8(*reinterpret_cast<const LDS u32x4_t*>(w_lds + row * 256 + 16 * absorb_chunk(row, 4 * ks + q4)));
     }
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) {
-      const int b = b0 + 16 * bb + l16;
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x32(wa[cb][ks], qb[bb][ks], acc);
-        // lane holds q~[b][c0 + 16cb + 4q4 + i], i = 0..3: bf16(q~) goes to
-        // q^, and what the rounding left out (exact in float32) to q~_lo
-        if (b < B) {
-          uint2 v, r;
-          v.x = cvt_bf16x2(acc[0], acc[1]);
-          v.y = cvt_bf16x2(acc[2], acc[3]);
-          r.x = cvt_bf16x2(acc[0] - bf16_lo(v.x), acc[1] - bf16_hi(v.x));
-          r.y = cvt_bf16x2(acc[2] - bf16_lo(v.y), acc[3] - bf16_hi(v.y));
-          *reinterpret_cast<uint2*>(a.q_hat + ((int64_t)b * H + h) * kRowE + c0 + 16 * cb + 4 * q4) = v;
-          *reinterpret_cast<uint2*>(a.q_lo + ((int64_t)b * H + h) * kDc + c0 + 16 * cb + 4 * q4) = r;
-        }
-      }
+      const int row = 16 * bb + l16;
+      qb[bb] = as_bf16x8(*reinterpret_cast<const LDS u32x4_t*>(q_lds + row * 256 + 16 * absorb_chunk(row, 4 * ks + q4)));
     }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) acc[cb][bb] = mfma16x16x32(wa[cb], qb[bb], acc[cb][bb]);
   }
-  // append q_rope (already rotated) unchanged: B x 8 16-byte chunks per head,
-  // spread over the 8 slice workgroups (one chunk per lane up to B = 64)
-  for (int i = slice * 64 + lane; i < B * 8; i += 8 * 64) {
-    const int b = i >> 3, ch = i & 7;
-    *reinterpret_cast<uint4*>(a.q_hat + ((int64_t)b * H + h) * kRowE + kDc + 8 * ch) =
-        *reinterpret_cast<const uint4*>(a.q_rope + ((int64_t)b * H + h) * 64 + 8 * ch);
+  __syncthreads();   // every wave is done reading W and q: their bytes become the staging area
+
+  // lane holds q~[b = 16 bb + l16][c = 64 w + 16 cb + 4 q4 + i], i = 0..3:
+  // bf16(q~) to the row's first half, what the rounding left out (exact in
+  // float32) to its second half
+  LDS uint8_t* st = w_lds;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+      const f32x4_t v = acc[cb][bb];
+      u32x2_t hi, lo;
+      hi.x = cvt_bf16x2(v[0], v[1]);
+      hi.y = cvt_bf16x2(v[2], v[3]);
+      lo.x = cvt_bf16x2(v[0] - bf16_lo(hi.x), v[1] - bf16_hi(hi.x));
+      lo.y = cvt_bf16x2(v[2] - bf16_lo(hi.y), v[3] - bf16_hi(hi.y));
+      const int row = 16 * bb + l16;
+      const int col = 64 * w + 16 * cb + 4 * q4;
+      *reinterpret_cast<LDS u32x2_t*>(st + row * kAbsorbOutB + 2 * col) = hi;
+      *reinterpret_cast<LDS u32x2_t*>(st + row * kAbsorbOutB + 2 * (kAbsorbCols + col)) = lo;
+    }
+  __syncthreads();
+
+  // rows out: each row's 256 hi and 256 lo columns are 2 x 32 pieces of 16 B
+  for (int p = tid; p < nb * 64; p += 256) {
+    const int row = p >> 6, piece = p & 63;
+    const int part = piece >> 5, c8 = (piece & 31) * 8;
+    const u32x4_t v = *reinterpret_cast<const LDS u32x4_t*>(st + row * kAbsorbOutB + 2 * (part * kAbsorbCols + c8));
+    const int64_t bh = (int64_t)(b0 + row) * H + h;
+    uint16_t* dst = part == 0 ? a.q_hat + bh * kRowE + c0 + c8 : a.q_lo + bh * kDc + c0 + c8;
+    *reinterpret_cast<u32x4_t*>(dst) = v;
+  }
+  if (half == 0) {  // q_rope (already rotated) into q^: 8 pieces of 16 B per row
+    for (int p = tid; p < nb * 8; p += 256) {
+      const int row = p >> 3, ch = p & 7;
+      const int64_t bh = (int64_t)(b0 + row) * H + h;
+      *reinterpret_cast<u32x4_t*>(a.q_hat + bh * kRowE + kDc + 8 * ch) =
+          *reinterpret_cast<const u32x4_t*>(a.q_rope + bh * 64 + 8 * ch);
+    }
   }
 }
 
@@ -1350,7 +1408,9 @@ __global__ __launch_bounds__(512) void mla_merge_project_kernel(MlaArgs a, int n
 }  // namespace
 
 hipError_t launch_mla_absorb(const MlaArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(mla_absorb_kernel, dim3(8 * a.num_heads), dim3(64), 0, st, a);  // H is a multiple of 8
+  // H is a multiple of 8: (head, half) pairs in runs of 8 heads per half
+  hipLaunchKernelGGL(mla_absorb_kernel, dim3(2 * a.num_heads, (a.batch + kAbsorbRows - 1) / kAbsorbRows), dim3(256),
+                     0, st, a);
   return hipGetLastError();
 }
 
