@@ -114,6 +114,76 @@ class HipTimingEvents:
         self.events = []
 
 
+class Telemetry:
+    """Samples the GPU's current shader clock (the active level of
+    pp_dpm_sclk) and board power (hwmon power1_input) from sysfs every
+    ~20 ms in a background thread while a region runs. Reports medians;
+    an empty result where the files are not readable."""
+
+    def __init__(self):
+        import glob
+        self.sclk_path = self.power_path = None
+        for card in sorted(glob.glob("/sys/class/drm/card*/device")):
+            p = os.path.join(card, "pp_dpm_sclk")
+            if self.sclk_path is None and os.path.exists(p):
+                self.sclk_path = p
+                hw = sorted(glob.glob(os.path.join(card, "hwmon", "hwmon*", "power1_input")))
+                self.power_path = hw[0] if hw else None
+        self.samples = []
+
+    def _read(self):
+        rec = {}
+        try:
+            if self.sclk_path:
+                for line in open(self.sclk_path).read().splitlines():
+                    if line.strip().endswith("*"):
+                        rec["sclk_mhz"] = float(line.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz"))
+            if self.power_path:
+                rec["power_w"] = int(open(self.power_path).read().strip()) / 1e6
+        except (OSError, ValueError, IndexError):
+            pass
+        return rec
+
+    def __enter__(self):
+        import threading
+        self._stop = threading.Event()
+
+        def loop():
+            while not self._stop.is_set():
+                r = self._read()
+                if r:
+                    self.samples.append(r)
+                self._stop.wait(0.02)
+        self._thread = threading.Thread(target=loop, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join()
+
+    def summary(self):
+        out = {"samples": len(self.samples)}
+        for k in ("sclk_mhz", "power_w"):
+            v = [r[k] for r in self.samples if k in r]
+            if v:
+                out[k + "_median"] = round(float(np.median(v)), 1)
+        return out
+
+
+def rocm_version():
+    for path in ("/opt/rocm/.info/version",):
+        try:
+            return open(path).read().strip()
+        except OSError:
+            pass
+    try:
+        import torch
+        return f"hip {torch.version.hip}"
+    except Exception:  # pragma: no cover
+        return "unknown"
+
+
 # ----------------------------------------------------------------------------
 # algorithmic traffic and work (what the method must move / compute)
 # ----------------------------------------------------------------------------
@@ -546,16 +616,31 @@ def run_gpu(args):
     step_ev = (hev.create(), hev.create())
     base = args.warmup + n_probe
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    hev.record(step_ev[0], stream)
+    with Telemetry() as tele:
+        t0 = time.perf_counter()
+        hev.record(step_ev[0], stream)
+        for i in range(args.steps):
+            for _, fn in step_calls(base + i):
+                fn()
+        hev.record(step_ev[1], stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    ev_step_ms = hev.elapsed_ms(*step_ev) / args.steps
+
+    # Step distribution: K more steps with an event at every step boundary
+    # (none between the kernels of a step): median, p10 and p90 per step.
+    base += args.steps
+    bound_ev = [hev.create() for _ in range(args.steps + 1)]
+    hev.record(bound_ev[0], stream)
     for i in range(args.steps):
         for _, fn in step_calls(base + i):
             fn()
-    hev.record(step_ev[1], stream)
+        hev.record(bound_ev[i + 1], stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    ev_step_ms = hev.elapsed_ms(*step_ev) / args.steps
+    per_step = np.array([hev.elapsed_ms(bound_ev[i], bound_ev[i + 1]) for i in range(args.steps)])
+    step_stats = dict(median=round(float(np.median(per_step)), 4), p10=round(float(np.percentile(per_step, 10)), 4),
+                      p90=round(float(np.percentile(per_step, 90)), 4))
 
     # Roofline pass: K more steps in which events on the launch stream bracket
     # every launch of the dominant kernel; its average duration.
@@ -631,15 +716,73 @@ def run_gpu(args):
         paths[kind] = entry
 
     prop = torch.cuda.get_device_properties(0)
+    if args.workload == "step" and args.extra_paths:
+        # configs 4 and 5, timed on their own after the headline step (not
+        # part of it): long-context MLA and ragged MHA
+        for key, setup in (("mla_long", lambda: setup_mla(4)), ("gqa_ragged", lambda: setup_gqa(5))):
+            paths[key] = time_path(key, setup(), args, hev, stream)
+            torch.cuda.empty_cache()
+
+    prop = torch.cuda.get_device_properties(0)
     res = dict(metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=args.steps,
                warmup=args.warmup, ms_per_step=round(ms_per_step, 4), higher_is_better=True,
                scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
                config=dict(workload=workload_name(args.workload), parallelism="single-gpu"),
-               tflops=round(tflops, 2), event_ms_per_step=round(ev_step_ms, 4),
+               tflops=round(tflops, 2), event_ms_per_step=round(ev_step_ms, 4), step_ms=step_stats,
                roofline=roofline, paths=paths,
                device=dict(name=prop.name, cus=prop.multi_processor_count,
-                           arch=getattr(prop, "gcnArchName", "")))
+                           arch=getattr(prop, "gcnArchName", ""), rocm=rocm_version(),
+                           timed_region=tele.summary()))
     return res, plans
+
+
+def time_path(key, plan, args, hev, stream):
+    """A workload timed alone: warm-up, then its calls back to back with an
+    event at every call boundary (median, p10, p90 per call) and, in a second
+    pass, events around its dominant kernel (the attention or split pass)."""
+    import torch
+    calls, alg, info, _ = plan
+    names = [n for n, _ in calls[0]]
+    n = len(calls)
+    for i in range(max(args.warmup, 20)):
+        for _, fn in calls[i % n]:
+            fn()
+    steps = max(args.steps, 20)
+    ev = [hev.create() for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    with Telemetry() as tele:
+        hev.record(ev[0], stream)
+        for i in range(steps):
+            for _, fn in calls[i % n]:
+                fn()
+            hev.record(ev[i + 1], stream)
+        torch.cuda.synchronize()
+    t = np.array([hev.elapsed_ms(ev[i], ev[i + 1]) for i in range(steps)])
+    dom = "mla_attend" if "mla_attend" in names else "gqa_split_pass"
+    j = names.index(dom)
+    dev = [(hev.create(), hev.create()) for _ in range(steps)]
+    for i in range(steps):
+        for k, (_, fn) in enumerate(calls[i % n]):
+            if k == j:
+                hev.record(dev[i][0], stream)
+                fn()
+                hev.record(dev[i][1], stream)
+            else:
+                fn()
+    torch.cuda.synchronize()
+    dom_ms = float(np.mean([hev.elapsed_ms(a, b) for a, b in dev]))
+    med = float(np.median(t))
+    dom_bytes = alg["cache"] if dom == "mla_attend" else alg["cache"] + alg["q"]
+    entry = dict(info)
+    entry.update(time_us=round(med * 1e3, 2), p10_us=round(float(np.percentile(t, 10)) * 1e3, 2),
+                 p90_us=round(float(np.percentile(t, 90)) * 1e3, 2), alg_bytes=int(alg["total"]),
+                 alg_gbs=round(alg["total"] / (med * 1e-3) / 1e9, 1),
+                 tflops=round(alg["flops"] / (med * 1e-3) / 1e12, 2),
+                 roofline_frac=round(alg["total"] / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 dominant_kernel=dict(kernel=dom, avg_launch_us=round(dom_ms * 1e3, 2),
+                                      hbm_frac=round(dom_bytes / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)),
+                 timed_region=tele.summary())
+    return entry
 
 
 def workload_name(w):
@@ -812,6 +955,8 @@ def main():
                              "append-fp8", "gqa-fp8-paged"])
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle time for the CPU baseline (0 disables)")
+    ap.add_argument("--no-extra-paths", dest="extra_paths", action="store_false",
+                    help="skip timing the long-context MLA and ragged MHA workloads after the step")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB after the timed "
                          "steps (a kernel of known traffic, to scale hardware byte counters)")
