@@ -88,5 +88,49 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
     return LIB_PATH
 
 
+# Host-side sanitizers for the ABI check: on hipcc lines each flag follows
+# -Xarch_host, so the device code is built as usual.
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+HOST_CHECK_SRC = os.path.join(ROOT, "tests", "host_check", "abi_host_check.cpp")
+HOST_CHECK_EXE = os.path.join(BUILD_DIR, "abi_host_check")
+
+
+def build_host_check(verbose: bool = False) -> str:
+    """Build the ABI host check: api.hip with AddressSanitizer and
+    UndefinedBehaviorSanitizer on its host code, the other sources as usual,
+    and the driver tests/host_check/abi_host_check.cpp, linked into one
+    executable. Returns its path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    cc = hipcc()
+    objs = []
+    for src in sources():
+        obj = os.path.join(BUILD_DIR, "san_" + os.path.basename(src) + ".o")
+        extra = SANITIZE_HOST if os.path.basename(src) == "api.hip" else []
+        rc, out = _run([cc, *COMMON_FLAGS, *extra, "-g", "-c", src, "-o", obj])
+        if rc != 0:
+            print(out, file=sys.stderr)
+            raise RuntimeError(f"compiling {src} for the host check failed")
+        objs.append(obj)
+    drv = os.path.join(BUILD_DIR, "abi_host_check.o")
+    gxx = shutil.which("g++") or "g++"
+    rc, out = _run([gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                    f"-I{INCLUDE}", "-c", HOST_CHECK_SRC, "-o", drv])
+    if rc != 0:
+        print(out, file=sys.stderr)
+        raise RuntimeError("compiling the host check driver failed")
+    rocm_lib = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(cc))), "lib")
+    rc, out = _run([gxx, "-fsanitize=address,undefined", drv, *objs, f"-L{rocm_lib}", "-lamdhip64",
+                    f"-Wl,-rpath,{rocm_lib}", "-o", HOST_CHECK_EXE])
+    if rc != 0:
+        print(out, file=sys.stderr)
+        raise RuntimeError("linking the host check failed")
+    if verbose:
+        print(f"built {HOST_CHECK_EXE}")
+    return HOST_CHECK_EXE
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    if len(sys.argv) > 1 and sys.argv[1] == "host-check":
+        build_host_check(verbose=True)

@@ -2,6 +2,7 @@
 // layout and kernel dispatch. Every check runs on the host before any launch.
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include <atomic>
 #include <initializer_list>
@@ -34,6 +35,22 @@ int device_cu_count() {
 }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Strides beyond 2^48 elements address nothing a device can hold; rejecting
+// them first keeps every later stride product inside int64.
+constexpr int64_t kMaxStride = int64_t(1) << 48;
+inline bool stride_in_range(int64_t s) { return s >= 0 && s <= kMaxStride; }
+inline bool stride_ok(int64_t s, int64_t esz) { return stride_in_range(s) && (s * esz) % 16 == 0; }
+
+// The dtype field as the caller wrote it. A C caller may store any int32 in
+// an enum field; reading one outside the enumerators through the enum type is
+// undefined in C++, so the bits are copied out as an int.
+inline int32_t dtype_code(const da_gqa_params_t* p) {
+  int32_t v;
+  static_assert(sizeof(p->dtype) == sizeof(v), "enum field is 32 bits");
+  memcpy(&v, &p->dtype, sizeof(v));
+  return v;
+}
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -56,25 +73,26 @@ da_status_t check_gqa_params(const da_gqa_params_t* p) {
     return DA_ERR_INVALID_ARGUMENT;
   if (p->num_q_heads % p->num_kv_heads != 0) return DA_ERR_INVALID_ARGUMENT;
   if (p->num_q_heads > 65535) return DA_ERR_INVALID_ARGUMENT;
-  if (p->dtype != DA_DTYPE_F32 && p->dtype != DA_DTYPE_BF16 && p->dtype != DA_DTYPE_FP8_E4M3)
+  if (p->max_seq_len > (1 << 30)) return DA_ERR_UNSUPPORTED;   // split arithmetic stays in int32
+  if (dtype_code(p) != DA_DTYPE_F32 && dtype_code(p) != DA_DTYPE_BF16 && dtype_code(p) != DA_DTYPE_FP8_E4M3)
     return DA_ERR_INVALID_ARGUMENT;
   if (!isfinite(p->softmax_scale)) return DA_ERR_INVALID_ARGUMENT;
   if (p->head_dim != 64 && p->head_dim != 128) return DA_ERR_UNSUPPORTED;
   // element bytes of q and of the cache (fp8 caches take bf16 queries)
-  const int64_t q_esz = p->dtype == DA_DTYPE_F32 ? 4 : 2;
-  const int64_t kv_esz = p->dtype == DA_DTYPE_F32 ? 4 : p->dtype == DA_DTYPE_BF16 ? 2 : 1;
+  const int64_t q_esz = dtype_code(p) == DA_DTYPE_F32 ? 4 : 2;
+  const int64_t kv_esz = dtype_code(p) == DA_DTYPE_F32 ? 4 : dtype_code(p) == DA_DTYPE_BF16 ? 2 : 1;
   const int64_t q_strides[2] = {p->q_stride_b, p->q_stride_h};
   const int64_t kv_strides[3] = {p->kv_stride_b, p->kv_stride_t, p->kv_stride_h};
   for (int64_t s : q_strides)
-    if (s < 0 || (s * q_esz) % 16 != 0) return DA_ERR_INVALID_ARGUMENT;
+    if (!stride_ok(s, q_esz)) return DA_ERR_INVALID_ARGUMENT;
   for (int64_t s : kv_strides)
-    if (s < 0 || (s * kv_esz) % 16 != 0) return DA_ERR_INVALID_ARGUMENT;
+    if (!stride_ok(s, kv_esz)) return DA_ERR_INVALID_ARGUMENT;
   return DA_OK;
 }
 
 // Kernel dtype code (0 f32, 1 bf16, 2 fp8 cache with bf16 queries).
 int gqa_kernel_dtype(const da_gqa_params_t* p) {
-  return p->dtype == DA_DTYPE_F32 ? 0 : p->dtype == DA_DTYPE_BF16 ? 1 : 2;
+  return dtype_code(p) == DA_DTYPE_F32 ? 0 : dtype_code(p) == DA_DTYPE_BF16 ? 1 : 2;
 }
 
 // Split count for `units` independent work items of `len` rows each when
@@ -151,8 +169,8 @@ GqaPlan plan_gqa(const da_gqa_params_t* p, int align = 1) {
   // (32 for fp8) on paged pools: at most w + 31 rows (the same bound for
   // both, so that the workspace queries, which do not know about paging,
   // cover paged calls).
-  const int64_t len = p->sliding_window > 0 && p->sliding_window + 31 < p->max_seq_len
-                          ? p->sliding_window + 31 : p->max_seq_len;
+  const int64_t len = p->sliding_window > 0 && (int64_t)p->sliding_window + 31 < p->max_seq_len
+                          ? (int64_t)p->sliding_window + 31 : p->max_seq_len;
   if (p->num_splits == 0) {
     const int64_t s_max = ceil_div(len, 128);
     s = s < s_max ? s : s_max;
@@ -176,6 +194,14 @@ GqaPlan plan_gqa(const da_gqa_params_t* p, int align = 1) {
 
 constexpr int kMlaDc = 512, kMlaRope = 64, kMlaNope = 128, kMlaV = 128;
 
+struct MlaPlan;
+MlaPlan plan_mla(const da_mla_params_t* p);
+bool mla_plan_oversize(const da_mla_params_t* p);
+
+// Rows per sequence beyond 2^30 are refused by every entry point: split and
+// chunk arithmetic then stays inside int32.
+constexpr int32_t kMaxSeqLen = 1 << 30;
+
 da_status_t check_mla_params(const da_mla_params_t* p) {
   if (!p) return DA_ERR_INVALID_ARGUMENT;
   if (p->batch < 1 || p->batch > 65535 || p->num_heads < 1 || p->max_seq_len < 1 ||
@@ -195,16 +221,18 @@ da_status_t check_mla_params(const da_mla_params_t* p) {
     case 16: case 32: case 48: case 64: case 96: case 128: break;
     default: return DA_ERR_UNSUPPORTED;
   }
-  if (p->cache_stride_b < 0 || p->cache_stride_t < kMlaDc + kMlaRope ||
-      p->cache_stride_t > (1 << 24) ||
-      (p->cache_stride_b * 2) % 16 != 0 || (p->cache_stride_t * 2) % 16 != 0)
+  if (p->max_seq_len > kMaxSeqLen) return DA_ERR_UNSUPPORTED;
+  if (!stride_ok(p->cache_stride_b, 2) || p->cache_stride_t < kMlaDc + kMlaRope ||
+      p->cache_stride_t > (1 << 24) || !stride_ok(p->cache_stride_t, 2))
     return DA_ERR_INVALID_ARGUMENT;
+  if (mla_plan_oversize(p)) return DA_ERR_UNSUPPORTED;
   return DA_OK;
 }
 
 struct MlaPlan {
   int splits, chunk;   // fixed splits; splits == 0: balanced on the device
   int wg_budget, slots;
+  bool oversize;       // the split slots would not fit an int32 (parameters unsupported)
   size_t q_hat_bytes, part_out_bytes, part_lse_bytes, table_bytes, workspace;
 };
 
@@ -248,7 +276,9 @@ MlaPlan plan_mla(const da_mla_params_t* p) {
     pl.chunk = (int)round_up((size_t)ceil_div(p->max_seq_len, s), 32);
     pl.splits = (int)ceil_div(p->max_seq_len, pl.chunk);
     pl.wg_budget = 0;
-    pl.slots = pl.splits * p->batch;
+    const int64_t slots = (int64_t)pl.splits * p->batch;
+    pl.oversize = slots > INT32_MAX / 128;
+    pl.slots = pl.oversize ? 0 : (int)slots;
   }
   const size_t rows = (size_t)p->batch * p->num_heads;
   // q^ [B, H, 576] bf16, then the low parts q~_lo [B, H, 512] bf16
@@ -259,6 +289,8 @@ MlaPlan plan_mla(const da_mla_params_t* p) {
   pl.workspace = pl.q_hat_bytes + pl.part_out_bytes + pl.part_lse_bytes;
   return pl;
 }
+
+bool mla_plan_oversize(const da_mla_params_t* p) { return plan_mla(p).oversize; }
 
 da_status_t from_hip(hipError_t e) { return e == hipSuccess ? DA_OK : DA_ERR_HIP; }
 
@@ -359,7 +391,7 @@ da_status_t check_paged(const da_paged_kv_t* pg, int64_t max_seq_len, int64_t el
   const int64_t ps = pg->page_size;
   if (ps < 16 || ps > (1 << 20) || (ps & (ps - 1)) != 0) return DA_ERR_INVALID_ARGUMENT;
   if (pg->max_blocks_per_seq < ceil_div(max_seq_len, ps)) return DA_ERR_INVALID_ARGUMENT;
-  if (pg->page_stride <= 0 || (pg->page_stride * elem_bytes) % 16 != 0) return DA_ERR_INVALID_ARGUMENT;
+  if (pg->page_stride <= 0 || !stride_ok(pg->page_stride, elem_bytes)) return DA_ERR_INVALID_ARGUMENT;
   return DA_OK;
 }
 
@@ -387,20 +419,20 @@ da_status_t gqa_decode_impl(const da_gqa_params_t* p, const da_paged_kv_t* pages
   if (st != DA_OK) return st;
   if (pages) {
     st = check_paged(pages, p->max_seq_len,
-                     p->dtype == DA_DTYPE_F32 ? 4 : p->dtype == DA_DTYPE_BF16 ? 2 : 1);
+                     dtype_code(p) == DA_DTYPE_F32 ? 4 : dtype_code(p) == DA_DTYPE_BF16 ? 2 : 1);
     if (st != DA_OK) return st;
   }
   if (scales) {
     if (!scales->k_scale || !scales->v_scale || !aligned4(scales->k_scale) ||
-        !aligned4(scales->v_scale) || scales->stride_b < 0 || scales->stride_t < 0 ||
-        scales->stride_h < 0)
+        !aligned4(scales->v_scale) || !stride_in_range(scales->stride_b) || !stride_in_range(scales->stride_t) ||
+        !stride_in_range(scales->stride_h))
       return DA_ERR_INVALID_ARGUMENT;
   }
   st = check_gqa_buffers(q, k_cache, v_cache, seq_lens, out, lse);
   if (st != DA_OK) return st;
   // paged calls split on multiples of 16 rows (32 for fp8), so that a step
   // never straddles a page
-  const bool fp8 = p->dtype == DA_DTYPE_FP8_E4M3;
+  const bool fp8 = dtype_code(p) == DA_DTYPE_FP8_E4M3;
   const GqaPlan pl = plan_gqa(p, pages ? (fp8 ? 32 : 16) : 1);
   if (pl.workspace > 0) {
     if (!workspace || workspace_bytes < pl.workspace) return DA_ERR_WORKSPACE_TOO_SMALL;
@@ -445,8 +477,7 @@ da_status_t check_append(const da_append_t* ap, int max_rot, int64_t esz) {
   } else if (!(isfinite(ap->rope_base) && ap->rope_base > 1.0)) {
     return DA_ERR_INVALID_ARGUMENT;
   }
-  if (ap->new_stride_b < 0 || ap->new_stride_h < 0 || (ap->new_stride_b * esz) % 16 != 0 ||
-      (ap->new_stride_h * esz) % 16 != 0)
+  if (!stride_ok(ap->new_stride_b, esz) || !stride_ok(ap->new_stride_h, esz))
     return DA_ERR_INVALID_ARGUMENT;
   return DA_OK;
 }
@@ -513,8 +544,8 @@ da_status_t da_gqa_append_rope(const da_gqa_params_t* p, const da_append_t* ap,
                                void* k_cache, void* v_cache, void* hip_stream) {
   da_status_t st = check_gqa_params(p);
   if (st != DA_OK) return st;
-  if (p->dtype == DA_DTYPE_FP8_E4M3) return DA_ERR_UNSUPPORTED;
-  const int64_t esz = p->dtype == DA_DTYPE_BF16 ? 2 : 4;
+  if (dtype_code(p) == DA_DTYPE_FP8_E4M3) return DA_ERR_UNSUPPORTED;
+  const int64_t esz = dtype_code(p) == DA_DTYPE_BF16 ? 2 : 4;
   st = check_append(ap, p->head_dim, esz);
   if (st != DA_OK) return st;
   if (pages && (st = check_paged(pages, p->max_seq_len, esz)) != DA_OK) return st;
@@ -546,12 +577,12 @@ da_status_t da_gqa_append_rope_fp8(const da_gqa_params_t* p, const da_append_t* 
                                    void* hip_stream) {
   da_status_t st = check_gqa_params(p);
   if (st != DA_OK) return st;
-  if (p->dtype != DA_DTYPE_FP8_E4M3) return DA_ERR_INVALID_ARGUMENT;
+  if (dtype_code(p) != DA_DTYPE_FP8_E4M3) return DA_ERR_INVALID_ARGUMENT;
   st = check_append(ap, p->head_dim, 2);     // new rows are bf16
   if (st != DA_OK) return st;
   if (pages) return DA_ERR_UNSUPPORTED;      // no paged E4M3 caches (decode has none either)
   if (!sc || !sc->k_scale || !sc->v_scale || !aligned4(sc->k_scale) || !aligned4(sc->v_scale) ||
-      sc->stride_b < 0 || sc->stride_t < 0 || sc->stride_h < 0)
+      !stride_in_range(sc->stride_b) || !stride_in_range(sc->stride_t) || !stride_in_range(sc->stride_h))
     return DA_ERR_INVALID_ARGUMENT;
   if (sc->stride_t != 0 && sc->stride_h == 0) return DA_ERR_UNSUPPORTED;
   st = check_ptrs16({q, q_out, k_new, v_new, k_cache, v_cache});
@@ -609,7 +640,7 @@ da_status_t da_mla_append_rope(const da_mla_params_t* p, const da_append_t* ap,
 size_t da_gqa_decode_workspace_size(const da_gqa_params_t* p) {
   if (check_gqa_params(p) != DA_OK) return 0;
   size_t ws = plan_gqa(p).workspace;
-  if (p->dtype == DA_DTYPE_FP8_E4M3) {   // paged fp8 pools plan without 16-wave shapes
+  if (dtype_code(p) == DA_DTYPE_FP8_E4M3) {   // paged fp8 pools plan without 16-wave shapes
     const size_t paged = plan_gqa(p, 32).workspace;
     ws = paged > ws ? paged : ws;
   }
@@ -627,7 +658,7 @@ da_status_t da_gqa_decode_split_pass(const da_gqa_params_t* p, const void* q,
                                      void* hip_stream) {
   da_status_t st = check_gqa_params(p);
   if (st != DA_OK) return st;
-  if (p->dtype == DA_DTYPE_FP8_E4M3) return DA_ERR_INVALID_ARGUMENT;   // needs scales
+  if (dtype_code(p) == DA_DTYPE_FP8_E4M3) return DA_ERR_INVALID_ARGUMENT;   // needs scales
   st = check_gqa_buffers(q, k_cache, v_cache, seq_lens, part_out, part_lse);
   if (st != DA_OK) return st;
   if (!part_lse) return DA_ERR_INVALID_ARGUMENT;
@@ -647,7 +678,7 @@ da_status_t da_gqa_decode_split_pass(const da_gqa_params_t* p, const void* q,
 da_status_t da_gqa_decode(const da_gqa_params_t* p, const void* q, const void* k_cache,
                           const void* v_cache, const int32_t* seq_lens, float* out, float* lse,
                           void* workspace, size_t workspace_bytes, void* hip_stream) {
-  if (p && p->dtype == DA_DTYPE_FP8_E4M3) return DA_ERR_INVALID_ARGUMENT;   // needs scales
+  if (p && dtype_code(p) == DA_DTYPE_FP8_E4M3) return DA_ERR_INVALID_ARGUMENT;   // needs scales
   return gqa_decode_impl(p, nullptr, nullptr, q, k_cache, v_cache, seq_lens, out, lse, workspace,
                          workspace_bytes, hip_stream);
 }
@@ -657,7 +688,7 @@ da_status_t da_gqa_decode_paged(const da_gqa_params_t* p, const da_paged_kv_t* p
                                 float* out, float* lse, void* workspace, size_t workspace_bytes,
                                 void* hip_stream) {
   if (!pages) return DA_ERR_INVALID_ARGUMENT;
-  if (p && p->dtype == DA_DTYPE_FP8_E4M3) return DA_ERR_INVALID_ARGUMENT;
+  if (p && dtype_code(p) == DA_DTYPE_FP8_E4M3) return DA_ERR_INVALID_ARGUMENT;
   return gqa_decode_impl(p, pages, nullptr, q, k_pool, v_pool, seq_lens, out, lse, workspace,
                          workspace_bytes, hip_stream);
 }
@@ -666,7 +697,7 @@ da_status_t da_gqa_decode_fp8(const da_gqa_params_t* p, const da_kv_scales_t* sc
                               const void* k_cache, const void* v_cache, const int32_t* seq_lens,
                               float* out, float* lse, void* workspace, size_t workspace_bytes,
                               void* hip_stream) {
-  if (!p || p->dtype != DA_DTYPE_FP8_E4M3 || !scales) return DA_ERR_INVALID_ARGUMENT;
+  if (!p || dtype_code(p) != DA_DTYPE_FP8_E4M3 || !scales) return DA_ERR_INVALID_ARGUMENT;
   return gqa_decode_impl(p, nullptr, scales, q, k_cache, v_cache, seq_lens, out, lse, workspace,
                          workspace_bytes, hip_stream);
 }
@@ -676,7 +707,7 @@ da_status_t da_gqa_decode_fp8_paged(const da_gqa_params_t* p, const da_paged_kv_
                                     const void* v_pool, const int32_t* seq_lens, float* out,
                                     float* lse, void* workspace, size_t workspace_bytes,
                                     void* hip_stream) {
-  if (!p || p->dtype != DA_DTYPE_FP8_E4M3 || !scales || !pages) return DA_ERR_INVALID_ARGUMENT;
+  if (!p || dtype_code(p) != DA_DTYPE_FP8_E4M3 || !scales || !pages) return DA_ERR_INVALID_ARGUMENT;
   // 32-token steps inside one page; scales that do not vary with the row are
   // per head (a per-page scale has no meaning for the method)
   if (pages->page_size < 32) return DA_ERR_UNSUPPORTED;
@@ -872,7 +903,10 @@ da_status_t da_splitkv_combine(int32_t num_splits, int32_t batch, int32_t num_he
                                              static_cast<hipStream_t>(hip_stream)));
 }
 
-const char* da_status_string(da_status_t s) {
+const char* da_status_string(da_status_t status) {
+  int32_t s;   // the caller's value, which may lie outside the enumerators
+  static_assert(sizeof(status) == sizeof(s), "enum is 32 bits");
+  memcpy(&s, &status, sizeof(s));
   switch (s) {
     case DA_OK: return "ok";
     case DA_ERR_INVALID_ARGUMENT: return "invalid argument";

@@ -464,3 +464,22 @@ def test_noalloc_mla_rejects_oversize_on_the_host():
                                             FAKE, None, None) == 2
     # config 3 fits
     assert L.da_mla_decode_workspace_size(ctypes.byref(mla())) <= 64 << 20
+
+
+@cpu_only
+def test_host_checks_under_address_and_undefined_behaviour_sanitizers():
+    # The argument checks and planners of every entry point, built with
+    # AddressSanitizer and UndefinedBehaviorSanitizer on the host side, over a
+    # sweep of valid, edge and hostile parameters (the driver refuses to run
+    # where a GPU could receive its fake pointers).
+    import subprocess
+    from decode_attention_kv_bf16_amd import build as B
+    exe = B.HOST_CHECK_EXE
+    srcs = B.sources() + [B.HOST_CHECK_SRC, os.path.join(ROOT, "include", "decode_attn.h")]
+    if not os.path.exists(exe) or os.path.getmtime(exe) < max(os.path.getmtime(f) for f in srcs):
+        B.build_host_check()
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:halt_on_error=1",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    r = subprocess.run([exe, "5000"], capture_output=True, text=True, timeout=600, env=env)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
+    assert "host checks passed" in r.stdout
