@@ -89,6 +89,15 @@ class KvScales(ctypes.Structure):
     ]
 
 
+class MlaScales(ctypes.Structure):
+    _fields_ = [
+        ("nope_scale", ctypes.c_void_p),
+        ("rope_scale", ctypes.c_void_p),
+        ("stride_b", ctypes.c_int64),
+        ("stride_t", ctypes.c_int64),
+    ]
+
+
 ROPE_STYLES = {"half": 0, "interleaved": 1}
 
 
@@ -126,6 +135,9 @@ _SIGNATURES = {
     "da_mla_decode_absorbed_noalloc": (ctypes.c_int, [ctypes.POINTER(MlaParams), _vp, _vp, _vp, _vp, _vp,
                                                       _vp, _vp, _vp, _vp]),
     "da_noalloc_scratch_bytes": (ctypes.c_size_t, []),
+    "da_mla_decode_fp8_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MlaParams)]),
+    "da_mla_decode_absorbed_fp8": (ctypes.c_int, [_MLA_P, ctypes.POINTER(MlaScales), _vp, _vp, _vp, _vp,
+                                                  _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "da_mla_merge_project": (ctypes.c_int, [ctypes.POINTER(MlaParams), _vp, _vp, _vp, _vp, _vp,
                                             _vp, _vp]),
     "da_gqa_decode_paged": (ctypes.c_int, [_GQA_P, _PAGED_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -153,6 +165,7 @@ _SIGNATURES = {
     "da_mla_params_size": (ctypes.c_size_t, []),
     "da_paged_kv_size": (ctypes.c_size_t, []),
     "da_kv_scales_size": (ctypes.c_size_t, []),
+    "da_mla_scales_size": (ctypes.c_size_t, []),
     "da_append_size": (ctypes.c_size_t, []),
 }
 
@@ -180,6 +193,7 @@ def lib() -> ctypes.CDLL:
             L.da_mla_params_size() != ctypes.sizeof(MlaParams) or \
             L.da_paged_kv_size() != ctypes.sizeof(PagedKv) or \
             L.da_kv_scales_size() != ctypes.sizeof(KvScales) or \
+            L.da_mla_scales_size() != ctypes.sizeof(MlaScales) or \
             L.da_append_size() != ctypes.sizeof(Append):
         raise RuntimeError("libdecode_attn.so parameter structs do not match this binding")
     _lib = L
@@ -600,6 +614,59 @@ def mla_decode_absorbed(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_cache: to
                                   _ptr(seq_lens), _ptr(w_uk), _ptr(w_uv), _ptr(out), _ptr(lse),
                                   _ptr(ws), ws_bytes, _stream_handle())
     _check(st, "da_mla_decode_absorbed")
+    return out, lse
+
+
+def mla_decode_absorbed_fp8(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_codes: torch.Tensor,
+                            scale_nope: torch.Tensor, scale_rope: torch.Tensor,
+                            w_uk: torch.Tensor, w_uv: torch.Tensor,
+                            seq_lens: Optional[torch.Tensor] = None,
+                            softmax_scale: Optional[float] = None, num_splits: int = 0,
+                            out: Optional[torch.Tensor] = None,
+                            lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mla_decode_absorbed over an E4M3 latent cache: kv_codes [B, L_max, 576]
+    uint8 codes (or torch.float8_e4m3fn); scale_nope, scale_rope float32
+    [B, L_max] (zero-stride views are fine): row (b, t) stands for
+    [code[:512] * scale_nope[b, t] ; code[512:] * scale_rope[b, t]]. The other
+    arguments as for mla_decode_absorbed."""
+    for name, t in (("q_nope", q_nope), ("q_rope", q_rope), ("kv_codes", kv_codes),
+                    ("scale_nope", scale_nope), ("scale_rope", scale_rope), ("w_uk", w_uk), ("w_uv", w_uv)):
+        _require_cuda(name, t)
+    for name, t in (("q_nope", q_nope), ("q_rope", q_rope), ("w_uk", w_uk), ("w_uv", w_uv)):
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if kv_codes.dtype == torch.float8_e4m3fn:
+        kv_codes = kv_codes.view(torch.uint8)
+    if kv_codes.dtype != torch.uint8:
+        raise ValueError("kv_codes must hold E4M3 codes (uint8 or float8_e4m3fn)")
+    B, H, _ = q_nope.shape
+    if q_rope.shape[:2] != (B, H) or w_uk.shape[0] != H or w_uv.shape[0] != H:
+        raise ValueError("head counts disagree")
+    L_max = kv_codes.shape[1]
+    for name, sc in (("scale_nope", scale_nope), ("scale_rope", scale_rope)):
+        if sc.dtype != torch.float32 or sc.shape != (B, L_max):
+            raise ValueError(f"{name} must be float32 of shape [B, L_max]")
+    if scale_nope.stride() != scale_rope.stride():
+        raise ValueError("scale_nope and scale_rope must share strides")
+    if seq_lens is not None:
+        _check_seq_lens(seq_lens, B)
+    p = mla_params(q_nope, kv_codes, w_uv, q_rope, softmax_scale, num_splits)
+    sc = MlaScales()
+    sc.nope_scale, sc.rope_scale = scale_nope.data_ptr(), scale_rope.data_ptr()
+    sc.stride_b, sc.stride_t = scale_nope.stride()
+    L = lib()
+    if out is None:
+        out = torch.empty((B, H, w_uv.shape[2]), dtype=torch.float32, device=q_nope.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q_nope.device)
+    ws_bytes = L.da_mla_decode_fp8_workspace_size(ctypes.byref(p))
+    ws = _workspace(ws_bytes, q_nope.device)
+    st = L.da_mla_decode_absorbed_fp8(ctypes.byref(p), ctypes.byref(sc), _ptr(q_nope), _ptr(q_rope),
+                                      _ptr(kv_codes), _ptr(seq_lens), _ptr(w_uk), _ptr(w_uv), _ptr(out),
+                                      _ptr(lse), _ptr(ws), ws_bytes, _stream_handle())
+    _check(st, "da_mla_decode_absorbed_fp8")
     return out, lse
 
 

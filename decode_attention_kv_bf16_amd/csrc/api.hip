@@ -41,6 +41,9 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 constexpr int64_t kMaxStride = int64_t(1) << 48;
 inline bool stride_in_range(int64_t s) { return s >= 0 && s <= kMaxStride; }
 inline bool stride_ok(int64_t s, int64_t esz) { return stride_in_range(s) && (s * esz) % 16 == 0; }
+// Token stride of fp8 scale arrays: the decode kernels copy a tile's scales
+// with 32-bit byte offsets (31 tokens x 4 bytes x stride), so it is bounded.
+inline bool scale_stride_t_ok(int64_t s) { return s >= 0 && s <= (int64_t(1) << 24); }
 
 // The dtype field as the caller wrote it. A C caller may store any int32 in
 // an enum field; reading one outside the enumerators through the enum type is
@@ -195,14 +198,17 @@ GqaPlan plan_gqa(const da_gqa_params_t* p, int align = 1) {
 constexpr int kMlaDc = 512, kMlaRope = 64, kMlaNope = 128, kMlaV = 128;
 
 struct MlaPlan;
-MlaPlan plan_mla(const da_mla_params_t* p);
-bool mla_plan_oversize(const da_mla_params_t* p);
+// fp8: the attention stage reads an E4M3 latent cache (one-byte rows, its
+// own kernel's occupancy)
+MlaPlan plan_mla(const da_mla_params_t* p, bool fp8 = false);
+bool mla_plan_oversize(const da_mla_params_t* p, bool fp8);
 
 // Rows per sequence beyond 2^30 are refused by every entry point: split and
 // chunk arithmetic then stays inside int32.
 constexpr int32_t kMaxSeqLen = 1 << 30;
 
-da_status_t check_mla_params(const da_mla_params_t* p) {
+// cache strides count elements of the cache: bf16 (fp8 false) or bytes (fp8)
+da_status_t check_mla_params(const da_mla_params_t* p, bool fp8 = false) {
   if (!p) return DA_ERR_INVALID_ARGUMENT;
   if (p->batch < 1 || p->batch > 65535 || p->num_heads < 1 || p->max_seq_len < 1 ||
       p->num_splits < 0 || p->kv_lora_rank < 1 || p->qk_rope_dim < 0 || p->qk_nope_dim < 1 ||
@@ -222,10 +228,11 @@ da_status_t check_mla_params(const da_mla_params_t* p) {
     default: return DA_ERR_UNSUPPORTED;
   }
   if (p->max_seq_len > kMaxSeqLen) return DA_ERR_UNSUPPORTED;
-  if (!stride_ok(p->cache_stride_b, 2) || p->cache_stride_t < kMlaDc + kMlaRope ||
-      p->cache_stride_t > (1 << 24) || !stride_ok(p->cache_stride_t, 2))
+  const int64_t esz = fp8 ? 1 : 2;
+  if (!stride_ok(p->cache_stride_b, esz) || p->cache_stride_t < kMlaDc + kMlaRope ||
+      p->cache_stride_t > (1 << 24) || !stride_ok(p->cache_stride_t, esz))
     return DA_ERR_INVALID_ARGUMENT;
-  if (mla_plan_oversize(p)) return DA_ERR_UNSUPPORTED;
+  if (mla_plan_oversize(p, fp8)) return DA_ERR_UNSUPPORTED;
   return DA_OK;
 }
 
@@ -236,15 +243,15 @@ struct MlaPlan {
   size_t q_hat_bytes, part_out_bytes, part_lse_bytes, table_bytes, workspace;
 };
 
-MlaPlan plan_mla(const da_mla_params_t* p) {
+MlaPlan plan_mla(const da_mla_params_t* p, bool fp8) {
   MlaPlan pl{};
   // One workgroup serves all heads of a split of one sequence; resident
   // workgroups from the kernel's occupancy (1 per CU when no device can be
   // asked).
-  int bpc = da::mla_attend_blocks_per_cu(p->num_heads);
+  int bpc = fp8 ? da::mla_attend_fp8_blocks_per_cu(p->num_heads) : da::mla_attend_blocks_per_cu(p->num_heads);
   if (bpc < 1) bpc = 1;
   const int64_t budget = (int64_t)bpc * device_cu_count();
-  const int64_t row_bytes = p->cache_stride_t * 2;
+  const int64_t row_bytes = p->cache_stride_t * (fp8 ? 1 : 2);
   // Balanced splits when the batch alone cannot fill the GPU (and B <= 512,
   // what the device-side assignment handles): the split
   // sizes then follow the actual lengths (device-side), so ragged batches
@@ -290,7 +297,7 @@ MlaPlan plan_mla(const da_mla_params_t* p) {
   return pl;
 }
 
-bool mla_plan_oversize(const da_mla_params_t* p) { return plan_mla(p).oversize; }
+bool mla_plan_oversize(const da_mla_params_t* p, bool fp8) { return plan_mla(p, fp8).oversize; }
 
 da_status_t from_hip(hipError_t e) { return e == hipSuccess ? DA_OK : DA_ERR_HIP; }
 
@@ -424,7 +431,7 @@ da_status_t gqa_decode_impl(const da_gqa_params_t* p, const da_paged_kv_t* pages
   }
   if (scales) {
     if (!scales->k_scale || !scales->v_scale || !aligned4(scales->k_scale) ||
-        !aligned4(scales->v_scale) || !stride_in_range(scales->stride_b) || !stride_in_range(scales->stride_t) ||
+        !aligned4(scales->v_scale) || !stride_in_range(scales->stride_b) || !scale_stride_t_ok(scales->stride_t) ||
         !stride_in_range(scales->stride_h))
       return DA_ERR_INVALID_ARGUMENT;
   }
@@ -764,6 +771,47 @@ da_status_t da_mla_decode_absorbed(const da_mla_params_t* p, const void* q_nope,
   return from_hip(da::launch_mla_decode(a, static_cast<hipStream_t>(hip_stream)));
 }
 
+size_t da_mla_decode_fp8_workspace_size(const da_mla_params_t* p) {
+  if (check_mla_params(p, true) != DA_OK) return 0;
+  return plan_mla(p, true).workspace;
+}
+
+da_status_t da_mla_decode_absorbed_fp8(const da_mla_params_t* p, const da_mla_scales_t* scales,
+                                       const void* q_nope, const void* q_rope, const void* kv_codes,
+                                       const int32_t* seq_lens, const void* w_uk, const void* w_uv,
+                                       float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                       void* hip_stream) {
+  da_status_t st = check_mla_params(p, true);
+  if (st != DA_OK) return st;
+  if (!scales || !scales->nope_scale || !scales->rope_scale || !aligned4(scales->nope_scale) ||
+      !aligned4(scales->rope_scale) || !stride_in_range(scales->stride_b) ||
+      !scale_stride_t_ok(scales->stride_t))
+    return DA_ERR_INVALID_ARGUMENT;
+  st = check_ptrs16({q_nope, q_rope, kv_codes, w_uk, w_uv, out});
+  if (st != DA_OK) return st;
+  if (!aligned4(seq_lens) || !aligned4(lse)) return DA_ERR_INVALID_ARGUMENT;
+  const MlaPlan pl = plan_mla(p, true);
+  if (!workspace || workspace_bytes < pl.workspace) return DA_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(workspace)) return DA_ERR_INVALID_ARGUMENT;
+  char* ws = static_cast<char*>(workspace);
+  da::MlaArgs a = mla_args(p, pl);
+  a.q_nope = static_cast<const uint16_t*>(q_nope);
+  a.q_rope = static_cast<const uint16_t*>(q_rope);
+  a.cache8 = static_cast<const uint8_t*>(kv_codes);
+  a.sc_nope = scales->nope_scale;
+  a.sc_rope = scales->rope_scale;
+  a.sc_sb = scales->stride_b;
+  a.sc_st = scales->stride_t;
+  a.seq_lens = seq_lens;
+  a.w_uk = static_cast<const uint16_t*>(w_uk);
+  a.w_uv = static_cast<const uint16_t*>(w_uv);
+  a.out = out;
+  a.lse = lse;
+  set_q_hat(a, ws);
+  set_partials(a, pl, ws + pl.q_hat_bytes, ws + pl.q_hat_bytes + pl.part_out_bytes);
+  return from_hip(da::launch_mla_decode_fp8(a, static_cast<hipStream_t>(hip_stream)));
+}
+
 size_t da_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 da_status_t da_mla_decode_absorbed_noalloc(const da_mla_params_t* p, const void* q_nope,
@@ -921,6 +969,7 @@ int32_t da_version(void) { return 100; }
 
 size_t da_gqa_params_size(void) { return sizeof(da_gqa_params_t); }
 size_t da_mla_params_size(void) { return sizeof(da_mla_params_t); }
+size_t da_mla_scales_size(void) { return sizeof(da_mla_scales_t); }
 size_t da_paged_kv_size(void) { return sizeof(da_paged_kv_t); }
 size_t da_kv_scales_size(void) { return sizeof(da_kv_scales_t); }
 size_t da_append_size(void) { return sizeof(da_append_t); }

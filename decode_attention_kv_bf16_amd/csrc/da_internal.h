@@ -101,12 +101,23 @@ struct MlaArgs {
   const int32_t* block_table;
   int32_t page_shift, max_blocks;
   int64_t page_stride;
+  // E4M3 latent cache (launch_mla_attend_fp8): cache8 holds one-byte codes,
+  // cache_sb and cache_st then count bytes; row (b, t) stands for
+  // [decode(code[:512]) * sc_nope[b sc_sb + t sc_st] ; decode(code[512:]) * sc_rope[...]].
+  const uint8_t* cache8;
+  const float* sc_nope;
+  const float* sc_rope;
+  int64_t sc_sb, sc_st;
 };
 
 hipError_t launch_mla_absorb(const MlaArgs& a, hipStream_t stream);
 hipError_t launch_mla_attend(const MlaArgs& a, hipStream_t stream);
 hipError_t launch_mla_merge_project(const MlaArgs& a, hipStream_t stream);
 hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream);  // all three
+// The attention stage over an E4M3 latent cache (mla_fp8.hip); absorb and
+// merge are the bf16 path's. Head counts 16, 32, 48, 64, 96, 128.
+hipError_t launch_mla_attend_fp8(const MlaArgs& a, hipStream_t stream);
+hipError_t launch_mla_decode_fp8(const MlaArgs& a, hipStream_t stream);  // absorb, attend_fp8, merge
 
 // Cache append with rotary embedding (append_rope.hip): one launch.
 struct AppendArgs {
@@ -154,5 +165,6 @@ __device__ __forceinline__ int32_t table_entry(const int32_t* table, int64_t i) 
 // Workgroups of the MLA attention kernel for `num_heads` that one CU holds at
 // once on the current device; 0 if the device cannot be queried.
 int mla_attend_blocks_per_cu(int num_heads);
+int mla_attend_fp8_blocks_per_cu(int num_heads);
 
 }  // namespace da

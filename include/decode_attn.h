@@ -364,7 +364,7 @@ typedef struct {
   const float* k_scale;   /* device, 4-byte aligned */
   const float* v_scale;   /* device, 4-byte aligned; same strides as k_scale */
   int64_t stride_b;       /* scale of (b, t, h) at b*stride_b + t*stride_t + h*stride_h (>= 0) */
-  int64_t stride_t;
+  int64_t stride_t;       /* 0 .. 2^24 for decode */
   int64_t stride_h;
 } da_kv_scales_t;
 
@@ -373,14 +373,51 @@ typedef struct {
  * codes (their strides in bytes, multiples of 16). Scales are read only for
  * rows [0, seq_lens[b]). Workspace as da_gqa_decode_workspace_size for the
  * same params. Errors: as da_gqa_decode, and INVALID_ARGUMENT for another
- * dtype, a NULL `scales` or scale pointer, a misaligned scale pointer or a
- * negative scale stride. da_gqa_decode, da_gqa_decode_split_pass and
- * da_gqa_decode_paged reject DA_DTYPE_FP8_E4M3 (they have no scales); paged
- * E4M3 pools go through da_gqa_decode_fp8_paged. */
+ * dtype, a NULL `scales` or scale pointer, a misaligned scale pointer, a
+ * negative scale stride or a token stride above 2^24. da_gqa_decode,
+ * da_gqa_decode_split_pass and da_gqa_decode_paged reject DA_DTYPE_FP8_E4M3
+ * (they have no scales); paged E4M3 pools go through da_gqa_decode_fp8_paged. */
 DA_EXPORT da_status_t da_gqa_decode_fp8(const da_gqa_params_t* params, const da_kv_scales_t* scales,
                                         const void* q, const void* k_cache, const void* v_cache,
                                         const int32_t* seq_lens, float* out, float* lse,
                                         void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * An absorbed-MLA latent cache in E4M3: row (b, t) is 576 one-byte codes, and
+ * its two ranges carry their own fp32 scales, because the c_kv and k_rope
+ * parts of a latent row have different numeric ranges ("Attention variants
+ * and KV cache", arganzheng.life, section 4.8; the one-byte format, section
+ * 6.3). The row stands for
+ *   [E4M3(code[0:512]) * nope_scale[b, t] ; E4M3(code[512:576]) * rope_scale[b, t]].
+ */
+typedef struct {
+  const float* nope_scale;  /* device, 4-byte aligned: scale of the c_kv range of (b, t) */
+  const float* rope_scale;  /* device, 4-byte aligned: scale of the k_rope range; same strides */
+  int64_t stride_b;         /* scale of (b, t) at b*stride_b + t*stride_t (floats, >= 0) */
+  int64_t stride_t;         /* 0 .. 2^24 (0: one scale per sequence) */
+} da_mla_scales_t;
+
+/* Workspace of da_mla_decode_absorbed_fp8 for these params (the layout of
+ * da_mla_decode_workspace_size; the split plan follows the E4M3 kernel). 0
+ * for invalid parameters. */
+DA_EXPORT size_t da_mla_decode_fp8_workspace_size(const da_mla_params_t* params);
+
+/* da_mla_decode_absorbed over an E4M3 latent cache kv_codes [B, L_max, 576]
+ * uint8, whose strides params->cache_stride_b and cache_stride_t count BYTES
+ * here (multiples of 16; cache_stride_t >= 576). q_nope, q_rope, w_uk, w_uv,
+ * out and lse as for da_mla_decode_absorbed (bf16 inputs, fp32 outputs).
+ * Codes and scales are read only for rows [0, seq_lens[b]) (rows past them
+ * may hold anything, NaN codes included). Every head count of
+ * da_mla_decode_absorbed is supported. Errors: as da_mla_decode_absorbed,
+ * and INVALID_ARGUMENT for a NULL `scales` or scale pointer, a misaligned
+ * scale pointer, a negative scale stride or a token stride above 2^24. */
+DA_EXPORT da_status_t da_mla_decode_absorbed_fp8(const da_mla_params_t* params,
+                                                 const da_mla_scales_t* scales, const void* q_nope,
+                                                 const void* q_rope, const void* kv_codes,
+                                                 const int32_t* seq_lens, const void* w_uk,
+                                                 const void* w_uv, float* out, float* lse,
+                                                 void* workspace, size_t workspace_bytes,
+                                                 void* hip_stream);
 
 /* ------------------------------------------------------------------------ */
 /* Cache append with rotary position embedding                               */
@@ -538,6 +575,7 @@ DA_EXPORT size_t da_gqa_params_size(void);
 DA_EXPORT size_t da_mla_params_size(void);
 DA_EXPORT size_t da_paged_kv_size(void);
 DA_EXPORT size_t da_kv_scales_size(void);
+DA_EXPORT size_t da_mla_scales_size(void);
 DA_EXPORT size_t da_append_size(void);
 
 #ifdef __cplusplus

@@ -100,6 +100,16 @@ void fixed_cases() {
   expect("mla negative scale", da_mla_decode_absorbed(&m, FAKE, FAKE, FAKE, nullptr, FAKE, FAKE, (float*)FAKE, nullptr, FAKE, BIG, nullptr), DA_ERR_UNSUPPORTED);
   m = mla();
   expect("mla workspace", da_mla_decode_absorbed(&m, FAKE, FAKE, FAKE, nullptr, FAKE, FAKE, (float*)FAKE, nullptr, FAKE, 10, nullptr), DA_ERR_WORKSPACE_TOO_SMALL);
+  m = mla();
+  m.cache_stride_b = 4096 * 576; m.cache_stride_t = 576;   // bytes for the E4M3 call
+  {
+    da_mla_scales_t ms8{(const float*)FAKE, (const float*)FAKE, 4096, 1};
+    expect("mla fp8 valid", launched(da_mla_decode_absorbed_fp8(&m, &ms8, FAKE, FAKE, FAKE, nullptr, FAKE, FAKE, (float*)FAKE, nullptr,
+                                                                FAKE, BIG, nullptr)), 1);
+    ms8.stride_t = (int64_t(1) << 24) + 1;
+    expect("mla fp8 scale stride", da_mla_decode_absorbed_fp8(&m, &ms8, FAKE, FAKE, FAKE, nullptr, FAKE, FAKE, (float*)FAKE, nullptr,
+                                                              FAKE, BIG, nullptr), DA_ERR_INVALID_ARGUMENT);
+  }
   m = mla(512, 128, 32768);
   expect("mla noalloc oversize", da_mla_decode_absorbed_noalloc(&m, FAKE, FAKE, FAKE, nullptr, FAKE, FAKE, (float*)FAKE, nullptr, nullptr), DA_ERR_WORKSPACE_TOO_SMALL);
   // paging
@@ -114,7 +124,7 @@ void fixed_cases() {
   // small queries
   expect("struct sizes", da_gqa_params_size() == sizeof(da_gqa_params_t) && da_mla_params_size() == sizeof(da_mla_params_t) &&
                              da_paged_kv_size() == sizeof(da_paged_kv_t) && da_kv_scales_size() == sizeof(da_kv_scales_t) &&
-                             da_append_size() == sizeof(da_append_t), 1);
+                             da_append_size() == sizeof(da_append_t) && da_mla_scales_size() == sizeof(da_mla_scales_t), 1);
   for (int s = -1; s < 7; ++s) expect("status string", da_status_string((da_status_t)s) != nullptr, 1);
 }
 
@@ -183,6 +193,13 @@ void sweep(int n) {
     expect("mla absorb status", ok_status(da_mla_absorb_query(&m, FAKE, FAKE, FAKE, FAKE, nullptr)), 1);
     expect("mla attend status", ok_status(da_mla_attend_split_pass(&m, FAKE, FAKE, nullptr, FAKE, (float*)FAKE, nullptr)), 1);
     expect("mla merge status", ok_status(da_mla_merge_project(&m, FAKE, FAKE, (const float*)FAKE, FAKE, (float*)FAKE, nullptr, nullptr)), 1);
+    da_mla_scales_t ms8{};
+    ms8.nope_scale = next_u64() % 8 ? (const float*)FAKE : nullptr;
+    ms8.rope_scale = (const float*)(next_u64() % 8 ? FAKE : FAKE_MIS);
+    ms8.stride_b = pick(st_menu); ms8.stride_t = pick(st_menu);
+    (void)da_mla_decode_fp8_workspace_size(&m);
+    expect("mla fp8 status", ok_status(da_mla_decode_absorbed_fp8(&m, next_u64() % 8 ? &ms8 : nullptr, FAKE, FAKE, FAKE, nullptr,
+                                                                  FAKE, FAKE, (float*)FAKE, nullptr, FAKE, BIG, nullptr)), 1);
     expect("mla paged status", ok_status(da_mla_decode_absorbed_paged(&m, &pg, FAKE, FAKE, FAKE, nullptr, FAKE, FAKE, (float*)FAKE, nullptr, FAKE, BIG, nullptr)), 1);
     expect("mla attend paged status", ok_status(da_mla_attend_split_pass_paged(&m, &pg, FAKE, FAKE, nullptr, FAKE, (float*)FAKE, nullptr)), 1);
     expect("mla append status", ok_status(da_mla_append_rope(&m, &ap, next_u64() % 2 ? &pg : nullptr, FAKE, FAKE, FAKE,

@@ -328,6 +328,48 @@ def test_fp8_entry_point_rejects_bad_arguments():
                                       None) == 1
 
 
+def mla_scales(n=FAKE, r=FAKE, sb=4096, st=1):
+    s = da.MlaScales()
+    s.nope_scale, s.rope_scale, s.stride_b, s.stride_t = n, r, sb, st
+    return s
+
+
+@needs_lib
+@cpu_only
+def test_mla_fp8_entry_point_rejects_bad_arguments():
+    L = da.lib()
+
+    def call(p, s, ws_bytes=1 << 40, codes=FAKE):
+        return L.da_mla_decode_absorbed_fp8(ctypes.byref(p), ctypes.byref(s) if s is not None else None,
+                                            FAKE, FAKE, codes, None, FAKE, FAKE, FAKE, None, FAKE,
+                                            ws_bytes, None)
+    # the same workspace layout as the bf16 call for these shapes
+    assert L.da_mla_decode_fp8_workspace_size(ctypes.byref(mla())) > 0
+    assert call(mla(), None) == 1                              # no scales
+    assert call(mla(), mla_scales(n=None)) == 1
+    assert call(mla(), mla_scales(r=ctypes.c_void_p(0x10002))) == 1   # misaligned
+    assert call(mla(), mla_scales(st=-1)) == 1
+    assert call(mla(), mla_scales(sb=-1)) == 1
+    assert call(mla(), mla_scales(st=(1 << 24) + 1)) == 1      # token stride beyond 2^24
+    assert call(mla(), mla_scales(), codes=None) == 1
+    assert call(mla(), mla_scales(), codes=FAKE_MIS) == 1
+    assert call(mla(), mla_scales(), ws_bytes=10) == 3
+    p = mla()
+    p.cache_stride_t = 584                                     # bytes: not a multiple of 16
+    assert call(p, mla_scales()) == 1
+    assert L.da_mla_decode_fp8_workspace_size(ctypes.byref(p)) == 0
+    p.cache_stride_t = 592                                     # 16-byte multiple: fine in bytes
+    assert L.da_mla_decode_fp8_workspace_size(ctypes.byref(p)) > 0
+    for field, val, code in [("kv_lora_rank", 256, 2), ("num_heads", 24, 2), ("batch", 0, 1),
+                             ("softmax_scale", 0.0, 2)]:
+        p = mla()
+        setattr(p, field, val)
+        assert call(p, mla_scales()) == code, field
+    # the GQA fp8 call bounds its token stride the same way
+    assert L.da_gqa_decode_fp8(ctypes.byref(fp8_params()), ctypes.byref(scales(st=(1 << 24) + 8)), FAKE,
+                               FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == 1
+
+
 @needs_lib
 def test_sliding_window_planning_without_a_device():
     L = da.lib()
