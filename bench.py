@@ -197,11 +197,11 @@ def gqa_alg(B, Hq, Hkv, D, total_rows, elem=2):
     return dict(cache=cache, q=q, out=out, total=cache + q + out, flops=4 * Hq * D * total_rows)
 
 
-def mla_alg(B, H, total_rows, d_c=512, d_r=64, d_n=128, d_v=128):
-    """Bytes: every cached latent row (576 bf16) once, W_UK and W_UV once,
-    q_nope/q_rope, fp32 out + lse. FLOPs: per cached row 2*H*(576 + 512), plus
-    the two per-head projections 2*B*H*d_c*(d_n + d_v)."""
-    cache = total_rows * (d_c + d_r) * 2
+def mla_alg(B, H, total_rows, d_c=512, d_r=64, d_n=128, d_v=128, elem=2):
+    """Bytes: every cached latent row (576 elements of `elem` bytes) once,
+    W_UK and W_UV once, q_nope/q_rope, fp32 out + lse. FLOPs: per cached row
+    2*H*(576 + 512), plus the two per-head projections 2*B*H*d_c*(d_n + d_v)."""
+    cache = total_rows * (d_c + d_r) * elem
     weights = 2 * H * d_c * 128 * 2
     q = B * H * (d_n + d_r) * 2
     out = B * H * (d_v + 1) * 4
@@ -303,6 +303,49 @@ def setup_mla(cfg):
     info = dict(batch=B, heads=H, seq_len=int(inp.seq_lens.max()),
                 total_rows=int(inp.seq_lens.sum()), splits=S, cache_copies=len(caches))
     return calls, alg, info, inp
+
+
+def setup_mla_fp8(cfg):
+    """The MLA workload of `cfg` with the latent cache in E4M3 and two fp32
+    scales per (sequence, token), one for the c_kv range and one for the
+    k_rope range; one call of the whole decode per step."""
+    import torch
+    import workloads as W
+    import decode_attention_kv_bf16_amd as da
+    inp = W.make_mla_fp8_config(cfg)
+    qn, qr = to_dev_bf16(inp.q_nope), to_dev_bf16(inp.q_rope)
+    wuk, wuv = to_dev_bf16(inp.w_uk), to_dev_bf16(inp.w_uv)
+    c0 = torch.from_numpy(inp.cache).cuda()
+    sn, sr = torch.from_numpy(inp.scale_nope).cuda(), torch.from_numpy(inp.scale_rope).cuda()
+    sl = torch.from_numpy(inp.seq_lens).cuda()
+    fp = c0.numel()
+    n_copies = max(1, math.ceil(MALL_GUARD_BYTES / fp)) if fp < MALL_GUARD_BYTES else 1
+    caches = [c0] + [c0.clone() for _ in range(n_copies - 1)]
+    B, H, _ = qn.shape
+    out = torch.empty((B, H, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    calls = []
+    for c in caches:
+        def call(c=c):
+            da.mla_decode_absorbed_fp8(qn, qr, c, sn, sr, wuk, wuv, sl, inp.scale, out=out, lse=lse)
+        calls.append([("mla_decode_fp8", call)])
+    rows = int(inp.seq_lens.sum())
+    alg = mla_alg(B, H, rows, elem=1)
+    scale_bytes = 2 * rows * 4
+    alg["cache"] += scale_bytes
+    alg["total"] += scale_bytes
+    info = dict(batch=B, heads=H, seq_len=int(inp.seq_lens.max()), total_rows=rows,
+                cache="e4m3 + fp32 c_kv and k_rope scales per (sequence, token)", cache_copies=len(caches))
+    return calls, alg, info, inp
+
+
+def binding_roofline(alg, t_ms):
+    """Which roofline binds a whole call (the larger of its HBM time and its
+    bf16 matrix-core time at peak) and the fraction of it reached."""
+    hbm_ms = alg["total"] / (HBM_PEAK_GBS * 1e9) * 1e3
+    mfma_ms = alg["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e3
+    bound = "mfma" if mfma_ms > hbm_ms else "hbm"
+    return dict(bound=bound, frac=round(max(hbm_ms, mfma_ms) / t_ms, 4))
 
 
 PAGE_SIZE = 16   # rows per page of the paged workloads (the common default)
@@ -568,6 +611,8 @@ def run_gpu(args):
         plans.append(("gqa-fp8", setup_gqa_fp8(2)))
     if args.workload == "gqa-fp8-paged":
         plans.append(("gqa-fp8-paged", setup_gqa_fp8_paged(2)))
+    if args.workload == "mla-fp8":
+        plans.append(("mla-fp8", setup_mla_fp8(3)))
     if args.workload == "gqa-window":
         plans.append(("gqa-window", setup_gqa_window()))
     if args.workload == "append":
@@ -713,13 +758,16 @@ def run_gpu(args):
                      hbm_frac=round(alg["total"] / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
         if kind.startswith("mla"):
             entry["mfma_frac"] = round(alg["flops"] / (t_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+        entry["binding_roofline"] = binding_roofline(alg, t_ms)
         paths[kind] = entry
 
     prop = torch.cuda.get_device_properties(0)
     if args.workload == "step" and args.extra_paths:
         # configs 4 and 5, timed on their own after the headline step (not
         # part of it): long-context MLA and ragged MHA
-        for key, setup in (("mla_long", lambda: setup_mla(4)), ("gqa_ragged", lambda: setup_gqa(5))):
+        # configs 4 and 5, then the E4M3 caches of configs 2 and 3
+        for key, setup in (("mla_long", lambda: setup_mla(4)), ("gqa_ragged", lambda: setup_gqa(5)),
+                           ("gqa_fp8", lambda: setup_gqa_fp8(2)), ("mla_fp8", lambda: setup_mla_fp8(3))):
             paths[key] = time_path(key, setup(), args, hev, stream)
             torch.cuda.empty_cache()
 
@@ -758,7 +806,8 @@ def time_path(key, plan, args, hev, stream):
             hev.record(ev[i + 1], stream)
         torch.cuda.synchronize()
     t = np.array([hev.elapsed_ms(ev[i], ev[i + 1]) for i in range(steps)])
-    dom = "mla_attend" if "mla_attend" in names else "gqa_split_pass"
+    # the attention kernel (or the whole call, for one-call paths)
+    dom = "mla_attend" if "mla_attend" in names else "gqa_split_pass" if "gqa_split_pass" in names else names[0]
     j = names.index(dom)
     dev = [(hev.create(), hev.create()) for _ in range(steps)]
     for i in range(steps):
@@ -772,7 +821,8 @@ def time_path(key, plan, args, hev, stream):
     torch.cuda.synchronize()
     dom_ms = float(np.mean([hev.elapsed_ms(a, b) for a, b in dev]))
     med = float(np.median(t))
-    dom_bytes = alg["cache"] if dom == "mla_attend" else alg["cache"] + alg["q"]
+    dom_bytes = (alg["cache"] if dom == "mla_attend" else alg["cache"] + alg["q"] if dom == "gqa_split_pass"
+                 else alg["total"])
     entry = dict(info)
     entry.update(time_us=round(med * 1e3, 2), p10_us=round(float(np.percentile(t, 10)) * 1e3, 2),
                  p90_us=round(float(np.percentile(t, 90)) * 1e3, 2), alg_bytes=int(alg["total"]),
@@ -781,6 +831,7 @@ def time_path(key, plan, args, hev, stream):
                  roofline_frac=round(alg["total"] / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                  dominant_kernel=dict(kernel=dom, avg_launch_us=round(dom_ms * 1e3, 2),
                                       hbm_frac=round(dom_bytes / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)),
+                 binding_roofline=binding_roofline(alg, med),
                  timed_region=tele.summary())
     return entry
 
@@ -795,6 +846,7 @@ def workload_name(w):
             "gqa-fp8": "llama3-8b-gqa-b32-l4096-fp8e4m3",
             "gqa-window": "mistral-7b-shape-gqa-b32-l8192-window4096",
             "gqa-fp8-paged": "llama3-8b-gqa-b32-l4096-fp8e4m3-paged32",
+            "mla-fp8": "deepseek-v3-mla-b64-l4096-fp8e4m3-nope-rope-scales",
             "append-fp8": "cache append + rope into e4m3: llama3-8b-gqa-b32-l4096",
             "append": "cache append + rope: llama3-8b-gqa-b32-l4096 + deepseek-v3-mla-b64-l4096"}[w]
 
@@ -809,7 +861,8 @@ def oracle_calls(kind, inp):
     Inputs are widened to fp64 outside the closures (not timed)."""
     from oracle.attention import (gqa_decode_paged_ref, gqa_decode_ref, mla_absorbed_paged_ref,
                                   mla_absorbed_ref)
-    from oracle.fp8 import gqa_append_rope_fp8_ref, gqa_decode_fp8_paged_ref, gqa_decode_fp8_ref
+    from oracle.fp8 import (gqa_append_rope_fp8_ref, gqa_decode_fp8_paged_ref, gqa_decode_fp8_ref,
+                            mla_absorbed_fp8_ref)
     from oracle.rope import gqa_append_rope_ref, mla_append_rope_ref
     import workloads as W
     f = (lambda a: W.bf16_to_f32(a).astype(np.float64))
@@ -864,6 +917,11 @@ def oracle_calls(kind, inp):
             args = (f(inp.q[b:b + 1]), inp.k[b:b + 1, :L], inp.v[b:b + 1, :L], inp.k_scale[b:b + 1, :L],
                     inp.v_scale[b:b + 1, :L], sl, inp.scale)
             calls.append((lambda a=args: gqa_decode_fp8_ref(*a), L))
+        elif kind == "mla-fp8":
+            args = (f(inp.q_nope[b:b + 1]), f(inp.q_rope[b:b + 1]), inp.cache[b:b + 1, :L],
+                    inp.scale_nope[b:b + 1, :L], inp.scale_rope[b:b + 1, :L], sl, f(inp.w_uk), f(inp.w_uv),
+                    inp.scale)
+            calls.append((lambda a=args: mla_absorbed_fp8_ref(*a), L))
         elif kind in ("gqa", "gqa-window"):
             conv = f if inp.dtype == "bf16" else (lambda a: a.astype(np.float64))
             args = (conv(inp.q[b:b + 1]), conv(inp.k[b:b + 1, :L]), conv(inp.v[b:b + 1, :L]), sl, inp.scale)
@@ -952,7 +1010,7 @@ def main():
     ap.add_argument("--workload", default="step",
                     choices=["step", "gqa", "mla", "mla-long", "gqa-ragged", "gqa-paged",
                              "mla-paged", "gqa-fp8", "append", "gqa-window",
-                             "append-fp8", "gqa-fp8-paged"])
+                             "append-fp8", "gqa-fp8-paged", "mla-fp8"])
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle time for the CPU baseline (0 disables)")
     ap.add_argument("--no-extra-paths", dest="extra_paths", action="store_false",

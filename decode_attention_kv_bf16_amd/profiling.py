@@ -37,10 +37,13 @@ KERNELS = {
     # and 16-wave shapes, on the vector ALUs (gqa_decode_kernel)
     "gqa_split_pass": ("_kernel", ("gqa_decode_kernel", "gqa_mfma_kernel"), ("gqa_decode.hip", "gqa_mfma.hip")),
     "gqa_combine": ("splitkv_combine_kernel", (), "combine.hip"),
-    "mla_absorb": ("mla_absorb_kernel", (), "mla_decode.hip"),
-    "mla_attend_paged": ("mla_attend_kernel", ("Lb1E", ", true>"), "mla_decode.hip"),
-    "mla_attend": ("mla_attend_kernel", (), "mla_decode.hip"),
-    "mla_merge_project": ("mla_merge_project_kernel", (), "mla_decode.hip"),
+    "mla_absorb": ("mla_absorb_kernel", (), ("mla_decode.hip", "mla_common.h")),
+    # the E4M3 latent kernel first: its name also contains "mla_attend"
+    "mla_attend_fp8": ("mla_attend_fp8_kernel", (), ("mla_fp8.hip", "mla_common.h")),
+    # 16 or 48 heads: mla_attend_kernel; multiples of 32: mla_attend32_kernel
+    "mla_attend_paged": ("mla_attend", ("Lb1E", ", true>"), ("mla_decode.hip", "mla_common.h")),
+    "mla_attend": ("mla_attend", ("mla_attend_kernel", "mla_attend32_kernel"), ("mla_decode.hip", "mla_common.h")),
+    "mla_merge_project": ("mla_merge_project_kernel", (), ("mla_decode.hip", "mla_common.h")),
     "gqa_append_rope_fp8": ("gqa_append_rope_fp8_kernel", (), "append_rope.hip"),
     "gqa_append_rope": ("gqa_append_rope_kernel", (), "append_rope.hip"),
     "mla_append_rope": ("mla_append_rope_kernel", (), "append_rope.hip"),

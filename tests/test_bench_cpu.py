@@ -22,7 +22,7 @@ def test_more_than_one_gpu_exits_with_a_message():
 
 def test_every_workload_has_a_name():
     for w in ("step", "gqa", "mla", "mla-long", "gqa-ragged", "gqa-paged", "mla-paged", "gqa-fp8",
-              "append", "gqa-window", "append-fp8", "gqa-fp8-paged"):
+              "append", "gqa-window", "append-fp8", "gqa-fp8-paged", "mla-fp8"):
         assert bench.workload_name(w)
 
 
@@ -42,11 +42,13 @@ def test_cpu_baseline_on_contiguous_and_paged_plans():
     (kp, vp), tg = bench.paged_pools(g.seq_lens, [g.k, g.v], seed=5)
     (pool,), tm = bench.paged_pools(m.seq_lens, [m.cache], seed=6)
     f8 = W.make_gqa_fp8(2, 8, 2, 128, [40, 9], seed=7)
+    m8 = W.make_mla_fp8(2, 16, [33, 5], seed=8, max_seq_len=40)
     ga = bench.gqa_alg(2, 8, 2, 128, int(g.seq_lens.sum()))
     ma = bench.mla_alg(2, 16, int(m.seq_lens.sum()))
     fa = bench.gqa_alg(2, 8, 2, 128, int(f8.seq_lens.sum()), elem=1)
+    m8a = bench.mla_alg(2, 16, int(m8.seq_lens.sum()), elem=1)
     plans = [("gqa", (None, ga, None, g)), ("mla", (None, ma, None, m)),
-             ("gqa-fp8", (None, fa, None, f8)),
+             ("gqa-fp8", (None, fa, None, f8)), ("mla-fp8", (None, m8a, None, m8)),
              ("gqa-paged", (None, ga, None, (g, dict(k_pool=kp, v_pool=vp, table=tg)))),
              ("mla-paged", (None, ma, None, (m, dict(pool=pool, table=tm)))),
              ("gqa-append", (None, dict(total=2000), None, W.make_gqa_append(2, 8, 2, 128, 4096))),
@@ -54,12 +56,12 @@ def test_cpu_baseline_on_contiguous_and_paged_plans():
              ("gqa-append-fp8", (None, dict(total=2000), None, W.make_gqa_append(2, 8, 2, 128, 4096)))]
     res = bench.cpu_baseline(plans, budget_s=4.0)
     assert res["kind"] == "oracle" and res["value"] > 0 and res["cores"] >= 1
-    for kind in ("gqa", "mla", "gqa-paged", "mla-paged", "gqa-fp8", "gqa-append", "mla-append",
+    for kind in ("gqa", "mla", "gqa-paged", "mla-paged", "gqa-fp8", "mla-fp8", "gqa-append", "mla-append",
                  "gqa-append-fp8"):
         assert f"{kind}: 2 of 2 sequences" in res["sample"]
     # one byte basis with the GPU figure: the step's algorithmic bytes (MLA
     # weights once per call, not once per sequence) over the oracle's seconds
-    step_bytes = 2 * ga["total"] + 2 * ma["total"] + fa["total"] + 3 * 2000
+    step_bytes = 2 * ga["total"] + 2 * ma["total"] + fa["total"] + m8a["total"] + 3 * 2000
     assert res["step_alg_bytes"] == step_bytes
     assert abs(res["value"] - step_bytes / res["seconds"] / 1e9) <= 1e-4 * res["value"] + 1e-4
     assert res["single_thread"]["seconds"] > 0 and res["cpu_model"]
@@ -73,3 +75,27 @@ def test_cpu_baseline_scales_a_partial_sample_by_rows():
     res = bench.cpu_baseline([("gqa", (None, ga, None, g))], budget_s=1e-9)
     assert "gqa: 1 of 6 sequences" in res["sample"]
     assert abs(res["value"] - ga["total"] / res["seconds"] / 1e9) <= 1e-4 * res["value"] + 1e-4
+
+
+def test_binding_roofline_picks_the_longer_bound():
+    # config-3 MLA in bf16 is HBM-bound on spec numbers; in E4M3 (half the
+    # cache bytes, the same matrix work) the matrix cores bind
+    bf = bench.mla_alg(64, 128, 64 * 4096)
+    f8 = bench.mla_alg(64, 128, 64 * 4096, elem=1)
+    assert bench.binding_roofline(bf, 1.0)["bound"] == "hbm"
+    assert bench.binding_roofline(f8, 1.0)["bound"] == "mfma"
+    r = bench.binding_roofline(f8, 0.060)
+    assert abs(r["frac"] - f8["flops"] / 2.5e15 / 0.060e-3) < 1e-3
+
+
+def test_profile_summaries_name_every_attention_kernel():
+    from decode_attention_kv_bf16_amd.profiling import short_name, source_sha256
+    ns = "void da::(anonymous namespace)::"
+    assert short_name(ns + "mla_attend32_kernel<4, false>(da::MlaArgs)") == "mla_attend"
+    assert short_name(ns + "mla_attend32_kernel<4, true>(da::MlaArgs)") == "mla_attend_paged"
+    assert short_name(ns + "mla_attend_kernel<1, 1, false>(da::MlaArgs)") == "mla_attend"
+    assert short_name(ns + "mla_attend_fp8_kernel<4>(da::MlaArgs)") == "mla_attend_fp8"
+    assert short_name("_ZN2da12_GLOBAL__N_119mla_attend32_kernelILi4ELb1EEEvNS_7MlaArgsE") == "mla_attend_paged"
+    assert short_name(ns + "mla_merge_project_kernel(da::MlaArgs, int, int)") == "mla_merge_project"
+    for k in ("mla_attend", "mla_attend_fp8", "mla_absorb", "gqa_split_pass"):
+        assert len(source_sha256(k)) == 64
