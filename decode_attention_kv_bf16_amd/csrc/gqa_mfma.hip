@@ -495,10 +495,16 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_mfma_kernel(GqaArgs a) {
 template <typename T, int D>
 hipError_t launch_t(const GqaArgs& a, hipStream_t st) {
   const dim3 grid(a.num_splits, a.num_kv_heads * (a.group / a.heads_per_block), a.batch);
-  // 4 waves, each with 3 steps in flight (the LDS holds 4 per wave); the
-  // planner's 8-wave workgroups run as 4-wave ones with the same grid
+  // bf16: 4 waves, each with 3 steps in flight (the LDS holds 4 per wave).
+  // fp8: 6 waves with 2 in flight each (3 slots): the same bytes in flight
+  // per CU on more waves measured 6% faster (51.8 against 55.2 us, config 2
+  // shape), a wave's step work overlapping another's wait. The planner's
+  // 8-wave workgroups run as these shapes with the same grid.
   if (a.waves_per_block == 8 || a.waves_per_block == 4) {
-    hipLaunchKernelGGL((gqa_mfma_kernel<T, D, 4, 4>), grid, dim3(4 * 64), 0, st, a);
+    if constexpr (sizeof(T) == 1)
+      hipLaunchKernelGGL((gqa_mfma_kernel<T, D, 6, 3>), grid, dim3(6 * 64), 0, st, a);
+    else
+      hipLaunchKernelGGL((gqa_mfma_kernel<T, D, 4, 4>), grid, dim3(4 * 64), 0, st, a);
   } else {
     return hipErrorInvalidValue;
   }
