@@ -54,7 +54,7 @@ def test_cpu_baseline_on_contiguous_and_paged_plans():
              ("gqa-append", (None, dict(total=2000), None, W.make_gqa_append(2, 8, 2, 128, 4096))),
              ("mla-append", (None, dict(total=2000), None, W.make_mla_append(2, 16, 4096))),
              ("gqa-append-fp8", (None, dict(total=2000), None, W.make_gqa_append(2, 8, 2, 128, 4096)))]
-    res = bench.cpu_baseline(plans, budget_s=4.0)
+    res = bench.cpu_baseline(plans, budget_s=30.0)   # room for every sequence even on a loaded host
     assert res["kind"] == "oracle" and res["value"] > 0 and res["cores"] >= 1
     for kind in ("gqa", "mla", "gqa-paged", "mla-paged", "gqa-fp8", "mla-fp8", "gqa-append", "mla-append",
                  "gqa-append-fp8"):
