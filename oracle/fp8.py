@@ -201,3 +201,27 @@ def mla_absorbed_fp8_ref(q_nope, q_rope, codes, scale_nope, scale_rope, seq_lens
         rows[b, :Lb] = dequantize_mla_rows_ref(codes[b, :Lb], scale_nope[b, :Lb], scale_rope[b, :Lb],
                                                kv_lora_rank)
     return mla_absorbed_ref(q_nope, q_rope, rows, seq_lens, w_uk, w_uv, scale, kv_lora_rank)
+
+
+def mla_absorbed_fp8_paged_ref(q_nope, q_rope, code_pool, scale_nope_pool, scale_rope_pool, block_table,
+                               page_size: int, seq_lens, w_uk, w_uv, scale: float, kv_lora_rank: int = 512):
+    """Absorbed MLA decode over a paged E4M3 latent pool ("Attention variants
+    and KV cache", section 6.1 for the pages and the block table; sections
+    4.8 and 6.3 for the two scaled ranges): code_pool [num_pages, page_size,
+    d_c + d_rope] uint8, scale pools [num_pages, page_size] paged like the
+    codes. Each sequence's codes and scales are gathered in logical order
+    through its table row (oracle.attention.paged_rows_ref), then attended as
+    by mla_absorbed_fp8_ref."""
+    from oracle.attention import paged_rows_ref
+    seq_lens = np.asarray(seq_lens, np.int64)
+    B = np.shape(q_nope)[0]
+    L = int(max(1, seq_lens.max(initial=0)))
+    codes = np.zeros((B, L, np.shape(code_pool)[2]), np.uint8)
+    sn = np.zeros((B, L))
+    sr = np.zeros((B, L))
+    for b in range(B):
+        Lb = int(seq_lens[b])
+        codes[b, :Lb] = paged_rows_ref(code_pool, block_table[b], page_size, Lb)
+        sn[b, :Lb] = paged_rows_ref(scale_nope_pool, block_table[b], page_size, Lb)
+        sr[b, :Lb] = paged_rows_ref(scale_rope_pool, block_table[b], page_size, Lb)
+    return mla_absorbed_fp8_ref(q_nope, q_rope, codes, sn, sr, seq_lens, w_uk, w_uv, scale, kv_lora_rank)

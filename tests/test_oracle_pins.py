@@ -766,6 +766,36 @@ def test_fp8_mla_workload_codes_round_trip():
     assert np.array_equal(inp.q_nope, m.q_nope) and np.array_equal(inp.w_uv, m.w_uv)
 
 
+def test_fp8_mla_paged_gathers_through_the_table():
+    # per-row brute force through the table on a tiny pool, equality with the
+    # contiguous reference on the same rows, invariance to the physical page
+    # order, and a planted reversed page order caught
+    qn, qr, codes, sn, sr, wuk, wuv = _mla_fp8_inputs(2, 3, 8, 4, 3, [7, 3], seed=41)
+    lens = np.array([7, 3])
+    ps = 2
+    table, n_pages = W.make_block_table(lens, ps, seed=5, spare_pages=2)
+    cp = W.paginate(codes, lens, table, n_pages, ps, W.FP8_NAN_CODE)
+    snp = W.paginate(sn, lens, table, n_pages, ps, np.nan)
+    srp = W.paginate(sr, lens, table, n_pages, ps, np.nan)
+    for b, L in enumerate(lens):
+        for t in range(L):
+            pg, r = table[b, t // ps], t % ps
+            assert np.array_equal(cp[pg, r], codes[b, t]) and snp[pg, r] == sn[b, t] and srp[pg, r] == sr[b, t]
+    o, l = OF.mla_absorbed_fp8_paged_ref(qn, qr, cp, snp, srp, table, ps, lens, wuk, wuv, 0.4, kv_lora_rank=8)
+    oc, lc = OF.mla_absorbed_fp8_ref(qn, qr, codes, sn, sr, lens, wuk, wuv, 0.4, kv_lora_rank=8)
+    assert np.array_equal(o, oc) and np.array_equal(l, lc)
+    table2, n2 = W.make_block_table(lens, ps, seed=99, spare_pages=0)
+    cp2 = W.paginate(codes, lens, table2, n2, ps, W.FP8_NAN_CODE)
+    o2, _ = OF.mla_absorbed_fp8_paged_ref(qn, qr, cp2, W.paginate(sn, lens, table2, n2, ps, np.nan),
+                                          W.paginate(sr, lens, table2, n2, ps, np.nan), table2, ps, lens, wuk,
+                                          wuv, 0.4, kv_lora_rank=8)
+    assert np.array_equal(o2, oc)
+    bad = table.copy()
+    bad[0, :4] = bad[0, :4][::-1]
+    ob, _ = OF.mla_absorbed_fp8_paged_ref(qn, qr, cp, snp, srp, bad, ps, lens, wuk, wuv, 0.4, kv_lora_rank=8)
+    assert not np.allclose(ob[0], oc[0], rtol=1e-6)
+
+
 # ----------------------------------------------------------------------------
 # sliding window ("Attention variants and KV cache", section 5.3)
 # ----------------------------------------------------------------------------
