@@ -339,6 +339,45 @@ def setup_mla_fp8(cfg):
     return calls, alg, info, inp
 
 
+def setup_mla_fp8_paged(cfg):
+    """The E4M3 MLA workload of `cfg` with the codes and both scale arrays in
+    pools of 16-row pages (one block table)."""
+    import torch
+    import workloads as W
+    import decode_attention_kv_bf16_amd as da
+    inp = W.make_mla_fp8_config(cfg)
+    (cp_h, snp_h, srp_h), table_h = paged_pools(inp.seq_lens, [inp.cache, inp.scale_nope, inp.scale_rope],
+                                                seed=cfg)
+    qn, qr = to_dev_bf16(inp.q_nope), to_dev_bf16(inp.q_rope)
+    wuk, wuv = to_dev_bf16(inp.w_uk), to_dev_bf16(inp.w_uv)
+    c0 = torch.from_numpy(cp_h).cuda()
+    snp, srp = torch.from_numpy(snp_h).cuda(), torch.from_numpy(srp_h).cuda()
+    table = torch.from_numpy(table_h).cuda()
+    sl = torch.from_numpy(inp.seq_lens).cuda()
+    fp = c0.numel()
+    n_copies = max(1, math.ceil(MALL_GUARD_BYTES / fp)) if fp < MALL_GUARD_BYTES else 1
+    pools = [c0] + [c0.clone() for _ in range(n_copies - 1)]
+    B, H, _ = qn.shape
+    L = inp.cache.shape[1]
+    out = torch.empty((B, H, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    calls = []
+    for pl in pools:
+        def call(pl=pl):
+            da.mla_decode_absorbed_fp8_paged(qn, qr, pl, snp, srp, table, PAGE_SIZE, sl, wuk, wuv, max_seq_len=L,
+                                             softmax_scale=inp.scale, out=out, lse=lse)
+        calls.append([("mla_decode_fp8_paged", call)])
+    rows = int(inp.seq_lens.sum())
+    alg = mla_alg(B, H, rows, elem=1)
+    extra = 2 * rows * 4 + table_h.nbytes
+    alg["cache"] += 2 * rows * 4
+    alg["total"] += extra
+    info = dict(batch=B, heads=H, seq_len=int(inp.seq_lens.max()), total_rows=rows, page_size=PAGE_SIZE,
+                num_pages=int(cp_h.shape[0]), cache="e4m3 + fp32 c_kv and k_rope scales, paged",
+                cache_copies=len(pools))
+    return calls, alg, info, (inp, dict(pools=(cp_h, snp_h, srp_h), table=table_h))
+
+
 def binding_roofline(alg, t_ms):
     """Which roofline binds a whole call (the larger of its HBM time and its
     bf16 matrix-core time at peak) and the fraction of it reached."""
@@ -613,6 +652,8 @@ def run_gpu(args):
         plans.append(("gqa-fp8-paged", setup_gqa_fp8_paged(2)))
     if args.workload == "mla-fp8":
         plans.append(("mla-fp8", setup_mla_fp8(3)))
+    if args.workload == "mla-fp8-paged":
+        plans.append(("mla-fp8-paged", setup_mla_fp8_paged(3)))
     if args.workload == "gqa-window":
         plans.append(("gqa-window", setup_gqa_window()))
     if args.workload == "append":
@@ -847,6 +888,7 @@ def workload_name(w):
             "gqa-window": "mistral-7b-shape-gqa-b32-l8192-window4096",
             "gqa-fp8-paged": "llama3-8b-gqa-b32-l4096-fp8e4m3-paged32",
             "mla-fp8": "deepseek-v3-mla-b64-l4096-fp8e4m3-nope-rope-scales",
+            "mla-fp8-paged": "deepseek-v3-mla-b64-l4096-fp8e4m3-nope-rope-scales-paged16",
             "append-fp8": "cache append + rope into e4m3: llama3-8b-gqa-b32-l4096",
             "append": "cache append + rope: llama3-8b-gqa-b32-l4096 + deepseek-v3-mla-b64-l4096"}[w]
 
@@ -862,7 +904,7 @@ def oracle_calls(kind, inp):
     from oracle.attention import (gqa_decode_paged_ref, gqa_decode_ref, mla_absorbed_paged_ref,
                                   mla_absorbed_ref)
     from oracle.fp8 import (gqa_append_rope_fp8_ref, gqa_decode_fp8_paged_ref, gqa_decode_fp8_ref,
-                            mla_absorbed_fp8_ref)
+                            mla_absorbed_fp8_paged_ref, mla_absorbed_fp8_ref)
     from oracle.rope import gqa_append_rope_ref, mla_append_rope_ref
     import workloads as W
     f = (lambda a: W.bf16_to_f32(a).astype(np.float64))
@@ -896,7 +938,7 @@ def oracle_calls(kind, inp):
     for b in range(len(lens)):
         L = int(lens[b])
         sl = lens[b:b + 1]
-        if kind in ("gqa-paged", "mla-paged", "gqa-fp8-paged"):
+        if kind in ("gqa-paged", "mla-paged", "gqa-fp8-paged", "mla-fp8-paged"):
             ps = 32 if kind == "gqa-fp8-paged" else PAGE_SIZE
             pages = pools["table"][b, :max(1, -(-L // ps))]
             # only the sequence's own pages, renumbered, go to the oracle
@@ -917,6 +959,11 @@ def oracle_calls(kind, inp):
             args = (f(inp.q[b:b + 1]), inp.k[b:b + 1, :L], inp.v[b:b + 1, :L], inp.k_scale[b:b + 1, :L],
                     inp.v_scale[b:b + 1, :L], sl, inp.scale)
             calls.append((lambda a=args: gqa_decode_fp8_ref(*a), L))
+        elif kind == "mla-fp8-paged":
+            cp, snp, srp = pools["pools"]
+            args = (f(inp.q_nope[b:b + 1]), f(inp.q_rope[b:b + 1]), cp[pages], snp[pages], srp[pages], tab,
+                    PAGE_SIZE, sl, f(inp.w_uk), f(inp.w_uv), inp.scale)
+            calls.append((lambda a=args: mla_absorbed_fp8_paged_ref(*a), L))
         elif kind == "mla-fp8":
             args = (f(inp.q_nope[b:b + 1]), f(inp.q_rope[b:b + 1]), inp.cache[b:b + 1, :L],
                     inp.scale_nope[b:b + 1, :L], inp.scale_rope[b:b + 1, :L], sl, f(inp.w_uk), f(inp.w_uv),
@@ -1010,7 +1057,7 @@ def main():
     ap.add_argument("--workload", default="step",
                     choices=["step", "gqa", "mla", "mla-long", "gqa-ragged", "gqa-paged",
                              "mla-paged", "gqa-fp8", "append", "gqa-window",
-                             "append-fp8", "gqa-fp8-paged", "mla-fp8"])
+                             "append-fp8", "gqa-fp8-paged", "mla-fp8", "mla-fp8-paged"])
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle time for the CPU baseline (0 disables)")
     ap.add_argument("--no-extra-paths", dest="extra_paths", action="store_false",

@@ -138,6 +138,9 @@ _SIGNATURES = {
     "da_mla_decode_fp8_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MlaParams)]),
     "da_mla_decode_absorbed_fp8": (ctypes.c_int, [_MLA_P, ctypes.POINTER(MlaScales), _vp, _vp, _vp, _vp,
                                                   _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "da_mla_decode_absorbed_fp8_paged": (ctypes.c_int, [_MLA_P, _PAGED_P, ctypes.POINTER(MlaScales), _vp, _vp,
+                                                        _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                                                        _vp]),
     "da_mla_merge_project": (ctypes.c_int, [ctypes.POINTER(MlaParams), _vp, _vp, _vp, _vp, _vp,
                                             _vp, _vp]),
     "da_gqa_decode_paged": (ctypes.c_int, [_GQA_P, _PAGED_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -667,6 +670,63 @@ def mla_decode_absorbed_fp8(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_codes
                                       _ptr(kv_codes), _ptr(seq_lens), _ptr(w_uk), _ptr(w_uv), _ptr(out),
                                       _ptr(lse), _ptr(ws), ws_bytes, _stream_handle())
     _check(st, "da_mla_decode_absorbed_fp8")
+    return out, lse
+
+
+def mla_decode_absorbed_fp8_paged(q_nope: torch.Tensor, q_rope: torch.Tensor, code_pool: torch.Tensor,
+                                  scale_nope: torch.Tensor, scale_rope: torch.Tensor,
+                                  block_table: torch.Tensor, page_size: int, seq_lens: torch.Tensor,
+                                  w_uk: torch.Tensor, w_uv: torch.Tensor,
+                                  max_seq_len: Optional[int] = None,
+                                  softmax_scale: Optional[float] = None, num_splits: int = 0,
+                                  out: Optional[torch.Tensor] = None,
+                                  lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mla_decode_absorbed_fp8 over a paged E4M3 latent pool: code_pool
+    [num_pages, page_size, 576] uint8 codes (or float8_e4m3fn); scale_nope,
+    scale_rope float32 [num_pages, page_size] (paged like the codes; zero
+    strides are fine); block_table [B, max_blocks] int32; seq_lens [B] int32."""
+    for name, t in (("q_nope", q_nope), ("q_rope", q_rope), ("code_pool", code_pool),
+                    ("scale_nope", scale_nope), ("scale_rope", scale_rope), ("w_uk", w_uk), ("w_uv", w_uv)):
+        _require_cuda(name, t)
+    for name, t in (("q_nope", q_nope), ("q_rope", q_rope), ("w_uk", w_uk), ("w_uv", w_uv)):
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if code_pool.dtype == torch.float8_e4m3fn:
+        code_pool = code_pool.view(torch.uint8)
+    if code_pool.dtype != torch.uint8:
+        raise ValueError("code_pool must hold E4M3 codes (uint8 or float8_e4m3fn)")
+    B, H, _ = q_nope.shape
+    if q_rope.shape[:2] != (B, H) or w_uk.shape[0] != H or w_uv.shape[0] != H:
+        raise ValueError("head counts disagree")
+    for name, sc in (("scale_nope", scale_nope), ("scale_rope", scale_rope)):
+        if sc.dtype != torch.float32 or sc.shape != tuple(code_pool.shape[:2]):
+            raise ValueError(f"{name} must be float32 of shape [num_pages, page_size]")
+    if scale_nope.stride() != scale_rope.stride():
+        raise ValueError("scale_nope and scale_rope must share strides")
+    _check_seq_lens(seq_lens, B)
+    if block_table.shape[0] != B:
+        raise ValueError("block_table must have one row per sequence")
+    pg = paged_kv(block_table, page_size, code_pool)
+    if max_seq_len is None:
+        max_seq_len = block_table.shape[1] * page_size
+    p = _mla_paged_params(q_nope, q_rope, code_pool, w_uv, max_seq_len, softmax_scale, num_splits)
+    sc = MlaScales()
+    sc.nope_scale, sc.rope_scale = scale_nope.data_ptr(), scale_rope.data_ptr()
+    sc.stride_b, sc.stride_t = scale_nope.stride()
+    L = lib()
+    if out is None:
+        out = torch.empty((B, H, w_uv.shape[2]), dtype=torch.float32, device=q_nope.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q_nope.device)
+    ws_bytes = L.da_mla_decode_fp8_workspace_size(ctypes.byref(p))
+    ws = _workspace(ws_bytes, q_nope.device)
+    st = L.da_mla_decode_absorbed_fp8_paged(ctypes.byref(p), ctypes.byref(pg), ctypes.byref(sc), _ptr(q_nope),
+                                            _ptr(q_rope), _ptr(code_pool), _ptr(seq_lens), _ptr(w_uk),
+                                            _ptr(w_uv), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
+                                            _stream_handle())
+    _check(st, "da_mla_decode_absorbed_fp8_paged")
     return out, lse
 
 

@@ -776,13 +776,20 @@ size_t da_mla_decode_fp8_workspace_size(const da_mla_params_t* p) {
   return plan_mla(p, true).workspace;
 }
 
-da_status_t da_mla_decode_absorbed_fp8(const da_mla_params_t* p, const da_mla_scales_t* scales,
-                                       const void* q_nope, const void* q_rope, const void* kv_codes,
-                                       const int32_t* seq_lens, const void* w_uk, const void* w_uv,
-                                       float* out, float* lse, void* workspace, size_t workspace_bytes,
-                                       void* hip_stream) {
+namespace {
+
+// One E4M3 MLA call: absorb, the E4M3 attention (over paged pools when
+// `pages`), merge + project.
+da_status_t mla_fp8_impl(const da_mla_params_t* p, const da_paged_kv_t* pages, const da_mla_scales_t* scales,
+                         const void* q_nope, const void* q_rope, const void* kv_codes, const int32_t* seq_lens,
+                         const void* w_uk, const void* w_uv, float* out, float* lse, void* workspace,
+                         size_t workspace_bytes, void* hip_stream) {
   da_status_t st = check_mla_params(p, true);
   if (st != DA_OK) return st;
+  if (pages) {
+    st = check_paged(pages, p->max_seq_len, 1);
+    if (st != DA_OK) return st;
+  }
   if (!scales || !scales->nope_scale || !scales->rope_scale || !aligned4(scales->nope_scale) ||
       !aligned4(scales->rope_scale) || !stride_in_range(scales->stride_b) ||
       !scale_stride_t_ok(scales->stride_t))
@@ -795,6 +802,7 @@ da_status_t da_mla_decode_absorbed_fp8(const da_mla_params_t* p, const da_mla_sc
   if (!aligned16(workspace)) return DA_ERR_INVALID_ARGUMENT;
   char* ws = static_cast<char*>(workspace);
   da::MlaArgs a = mla_args(p, pl);
+  if (pages) set_paged(a, pages);
   a.q_nope = static_cast<const uint16_t*>(q_nope);
   a.q_rope = static_cast<const uint16_t*>(q_rope);
   a.cache8 = static_cast<const uint8_t*>(kv_codes);
@@ -810,6 +818,27 @@ da_status_t da_mla_decode_absorbed_fp8(const da_mla_params_t* p, const da_mla_sc
   set_q_hat(a, ws);
   set_partials(a, pl, ws + pl.q_hat_bytes, ws + pl.q_hat_bytes + pl.part_out_bytes);
   return from_hip(da::launch_mla_decode_fp8(a, static_cast<hipStream_t>(hip_stream)));
+}
+
+}  // namespace
+
+da_status_t da_mla_decode_absorbed_fp8(const da_mla_params_t* p, const da_mla_scales_t* scales,
+                                       const void* q_nope, const void* q_rope, const void* kv_codes,
+                                       const int32_t* seq_lens, const void* w_uk, const void* w_uv,
+                                       float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                       void* hip_stream) {
+  return mla_fp8_impl(p, nullptr, scales, q_nope, q_rope, kv_codes, seq_lens, w_uk, w_uv, out, lse, workspace,
+                      workspace_bytes, hip_stream);
+}
+
+da_status_t da_mla_decode_absorbed_fp8_paged(const da_mla_params_t* p, const da_paged_kv_t* pages,
+                                             const da_mla_scales_t* scales, const void* q_nope,
+                                             const void* q_rope, const void* code_pool, const int32_t* seq_lens,
+                                             const void* w_uk, const void* w_uv, float* out, float* lse,
+                                             void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!pages) return DA_ERR_INVALID_ARGUMENT;
+  return mla_fp8_impl(p, pages, scales, q_nope, q_rope, code_pool, seq_lens, w_uk, w_uv, out, lse, workspace,
+                      workspace_bytes, hip_stream);
 }
 
 size_t da_noalloc_scratch_bytes(void) { return kScratchBytes; }

@@ -40,10 +40,12 @@ constexpr int kRowB8 = kRowE;                    // 576 bytes of codes per row
 constexpr int kChunks8 = kRowB8 / 16;            // 36 chunks of 16 bytes
 constexpr int kTileB8 = kTok * kRowB8;           // 18432 bytes
 constexpr int kTileCopies8 = kTileB8 / 1024;     // 18 wave-wide copies
-constexpr int kTileOps8 = kTileCopies8 + 2;      // + the nope and the rope scales
-// Scales of a tile after its codes: nope at +0 (lanes 0-31; lanes 32-63
-// repeat them at +128), rope at +256 (+384).
-constexpr int kSlotB8 = kTileB8 + 512;
+// Scales of a tile after its codes, in 256-byte blocks, one per 4-byte copy.
+// Contiguous caches: two copies, nope then rope, each the tile's 32 tokens
+// (lanes 0-31; lanes 32-63 repeat them). Paged pools: the tile's two 16-row
+// halves may lie in different pages, so four copies, nope half 0, nope half
+// 1, rope half 0, rope half 1, each 16 tokens (lanes 0-15).
+constexpr int kSlotB8 = kTileB8 + 1024;
 static_assert(kTileB8 % 1024 == 0 && kChunks8 % 4 == 0, "tile geometry");
 
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
@@ -107,20 +109,31 @@ __device__ __forceinline__ void copy4(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff
                :: "v"(voffset), "s"(rsrc), "{m0}"(lds_addr) : "memory");
 }
 
+// Where a tile's rows come from. Contiguous: one range of codes and the two
+// scale ranges. Paged: each 16-row half has its own page (codes resource and
+// page index, from which the scale resources are made when they are copied).
+template <bool kPaged>
 struct TileSrc8 {
-  __amdgpu_buffer_rsrc_t codes, nope, rope;
+  __amdgpu_buffer_rsrc_t codes[kPaged ? 2 : 1];
+  __amdgpu_buffer_rsrc_t nope, rope;   // contiguous only
+  int page[2], row0[2], rows[2];       // paged only: page, first row in it, valid rows
 };
 
 // grid (split, sequence) or (slot) as mla_attend32_kernel; NW waves of 32
 // heads (NW in 1, 2, 4).
-template <int NW>
+template <int NW, bool kPaged>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_attend_fp8_kernel(MlaArgs a) {
-  static_assert(kTileOps8 % NW == 0, "copies split evenly over the waves");
-  constexpr int kOps = kTileOps8 / NW;           // copies per wave per tile
+  constexpr int kScaleOps = kPaged ? 4 : 2;
+  constexpr int kTileOps = kTileCopies8 + kScaleOps;  // copies per tile
+  constexpr int kOps = (kTileOps + NW - 1) / NW;       // copies of the busiest wave per tile
+  // scale block of range r (0 nope, 1 rope) for tokens 16 hf .. 16 hf + 15
+  constexpr int kRangeStride = kPaged ? 512 : 256;
+  constexpr int kHalfStride = kPaged ? 256 : 64;
   constexpr int kAhead = NW == 4 ? 4 : 2;        // tiles issued ahead of the score product
   constexpr int kDepth = kAhead + 2;             // + the tile being scored and the one in the value product
   static_assert((kAhead - 1) * kOps <= 63, "vmcnt range");
+  static_assert(kSlotB8 % 256 == 0 && kTileCopies8 % 2 == 0, "slot geometry");
   constexpr int kRingB = kDepth * kSlotB8;
   constexpr int kStageB = NW * 32 * kOutRowB;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kRingB > kStageB ? kRingB : kStageB];
@@ -146,55 +159,132 @@ void mla_attend_fp8_kernel(MlaArgs a) {
   }
   const int ntiles = (t_end - t_begin + kTok - 1) / kTok;
 
-  // Copy k of this wave is tile copy j = w + NW k: j < 18 is 1 KiB of codes
-  // (lane l fills tile byte 1024 j + 16 l: row R, physical chunk pc, from
-  // logical chunk pc ^ swz8(R)); j = 18 the nope scales, j = 19 the rope
-  // scales (lane l: token l % 32).
+  // Copy k of this wave is tile copy j = w + NW k (k < n_ops): j < 18 is
+  // 1 KiB of codes (lane l fills tile byte 1024 j + 16 l: row R, physical
+  // chunk pc, from logical chunk pc ^ swz8(R); paged: copies 0-8 are rows
+  // 0-15, the first half, 9-17 the second); j >= 18 is scale copy e = j - 18
+  // into scale block e.
+  // this wave's copies per tile (paged, 4 waves: 6 for waves 0-1, 5 for 2-3)
+  const int n_ops = (kTileOps - w + NW - 1) / NW;
   const uint32_t row_bytes = (uint32_t)a.cache_st;
-  const uint32_t sc_off = (uint32_t)(l32 * a.sc_st * 4);
+  const uint32_t sc_off = (uint32_t)((kPaged ? (lane & 15) : l32) * a.sc_st * 4);
+  // The code copy (0..17) that this wave's copy k makes, or -1 for a scale
+  // copy; the same assignment as issue_op below.
+  auto copy_index = [&](int k) {
+    if (NW == 1) return k < kTileCopies8 ? k : -1;
+    if (NW * (k + 1) <= kTileCopies8) return w + NW * k;
+    if (kPaged) {
+      if (NW == 2) return -1;                      // k = 9, 10: scales
+      return k == 4 ? -1 : 16 + min(w, 1);         // k = 5: copies 16 and 17 (waves 0 and 1)
+    }
+    const int j = w + NW * k;
+    return j < kTileCopies8 ? j : -1;
+  };
   uint32_t voff[kOps];
 #pragma unroll
   for (int k = 0; k < kOps; ++k) {
-    const int j = w + NW * k;
-    const int o = 1024 * min(j, kTileCopies8 - 1) + 16 * lane;
+    const int j = copy_index(k);
+    const int o = 1024 * max(j, 0) + 16 * lane;
     const int R = o / kRowB8, pc = (o - R * kRowB8) / 16;
-    voff[k] = j < kTileCopies8 ? (uint32_t)R * row_bytes + 16u * (uint32_t)(pc ^ swz8(R)) : sc_off;
+    voff[k] = j >= 0 ? (uint32_t)(kPaged ? R & 15 : R) * row_bytes + 16u * (uint32_t)(pc ^ swz8(R)) : sc_off;
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-  const uint8_t* codes_b = a.cache8 + (int64_t)b * a.cache_sb;
-  const float* sn_b = a.sc_nope + (int64_t)b * a.sc_sb;
-  const float* sr_b = a.sc_rope + (int64_t)b * a.sc_sb;
+  const int64_t tab0 = (int64_t)b * a.max_blocks;
+  const int page_mask = (1 << a.page_shift) - 1;
   auto tile_src = [&](int it) {
     const int t0 = t_begin + it * kTok;
-    // rows past `valid` read as zero (wave-uniform; said so for the buffer resources)
-    const int valid = __builtin_amdgcn_readfirstlane(max(min(t_end - t0, kTok), 0));
-    const uint32_t sbytes = valid > 0 ? (uint32_t)(((int64_t)(valid - 1) * a.sc_st + 1) * 4) : 0u;
-    TileSrc8 s;
-    s.codes = make_raw_rsrc(codes_b + (int64_t)t0 * a.cache_st, (uint32_t)valid * row_bytes);
-    s.nope = make_raw_rsrc(sn_b + (int64_t)t0 * a.sc_st, sbytes);
-    s.rope = make_raw_rsrc(sr_b + (int64_t)t0 * a.sc_st, sbytes);
+    TileSrc8<kPaged> s;
+    if constexpr (kPaged) {
+      int32_t pg[2];
+      load_two_entries(a.block_table + tab0 + (min(t0, t_end - 1) >> a.page_shift),
+                       a.block_table + tab0 + (min(t0 + 16, t_end - 1) >> a.page_shift), pg[0], pg[1]);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int th = t0 + 16 * hf;
+        s.page[hf] = __builtin_amdgcn_readfirstlane(pg[hf]);
+        s.row0[hf] = __builtin_amdgcn_readfirstlane(th & page_mask);
+        s.rows[hf] = __builtin_amdgcn_readfirstlane(min(max(t_end - th, 0), 16));
+        s.codes[hf] = make_raw_rsrc(a.cache8 + (int64_t)pg[hf] * a.page_stride + (int64_t)s.row0[hf] * a.cache_st,
+                                    (uint32_t)s.rows[hf] * row_bytes);
+      }
+    } else {
+      // rows past `valid` read as zero (wave-uniform; said so for the buffer resources)
+      const int valid = __builtin_amdgcn_readfirstlane(max(min(t_end - t0, kTok), 0));
+      const uint32_t sbytes = valid > 0 ? (uint32_t)(((int64_t)(valid - 1) * a.sc_st + 1) * 4) : 0u;
+      const int64_t sc0 = (int64_t)b * a.sc_sb + (int64_t)t0 * a.sc_st;
+      s.codes[0] = make_raw_rsrc(a.cache8 + (int64_t)b * a.cache_sb + (int64_t)t0 * a.cache_st,
+                                 (uint32_t)valid * row_bytes);
+      s.nope = make_raw_rsrc(a.sc_nope + sc0, sbytes);
+      s.rope = make_raw_rsrc(a.sc_rope + sc0, sbytes);
+    }
     return s;
   };
-  // Which copies a wave makes: every copy but the last is codes (one wave:
-  // all but the last two); the last copy of wave w is codes for w + NW k < 18,
-  // else the nope (18) or rope (19) scales. Decided once, in scalar flags.
-  const int j_last = w + NW * (kOps - 1);
-  const bool last_codes = j_last < kTileCopies8;
-  const bool last_rope = j_last > kTileCopies8;
-  auto issue_op = [&](const TileSrc8& src, int k, int buf) {
+  auto settle = [&](const TileSrc8<kPaged>& src) {
+    if constexpr (kPaged) asm volatile("" ::"s"(src.codes[0]), "s"(src.codes[1]));
+  };
+  // scale copy e of a tile into scale block e
+  auto issue_scale = [&](const TileSrc8<kPaged>& src, int e, uint32_t base) {
+    const uint32_t dst = base + kTileB8 + 256u * (uint32_t)e;
+    if constexpr (kPaged) {
+      // (e is wave-uniform; the selects keep every operand in scalar registers)
+      const bool hf = (e & 1) != 0;
+      const int n = __builtin_amdgcn_readfirstlane(hf ? src.rows[1] : src.rows[0]);
+      const int pgv = __builtin_amdgcn_readfirstlane(hf ? src.page[1] : src.page[0]);
+      const int r0v = __builtin_amdgcn_readfirstlane(hf ? src.row0[1] : src.row0[0]);
+      const float* sc = (e >> 1) ? a.sc_rope : a.sc_nope;
+      const uint32_t sbytes = n > 0 ? (uint32_t)(((int64_t)(n - 1) * a.sc_st + 1) * 4) : 0u;
+      copy4(make_raw_rsrc(sc + (int64_t)pgv * a.sc_sb + (int64_t)r0v * a.sc_st, sbytes), sc_off, dst);
+    } else {
+      copy4(e ? src.rope : src.nope, sc_off, dst);
+    }
+  };
+  // Copy k of this wave. Which kind of copy a k is must not depend on the
+  // wave at run time beyond one plain branch: a per-copy test of the copy
+  // index inside the unrolled score loop multiplied the code and pushed the
+  // absorbed queries into scratch memory (whose loads wait for every copy in
+  // flight). Scale copy e of a wave is chosen by selects.
+  auto issue_op = [&](const TileSrc8<kPaged>& src, int k, int buf) {
     const uint32_t base = lds0 + (uint32_t)(buf * kSlotB8);
-    const uint32_t dst = base + 1024u * (uint32_t)(w + NW * k);
-    if (NW == 1 && k >= kTileCopies8)   // one wave: k = 18, 19 are the scales
-      copy4(k == kTileCopies8 ? src.nope : src.rope, voff[k], base + kTileB8 + 256 * (k - kTileCopies8));
-    else if (NW == 1 || k < kOps - 1 || last_codes)
-      copy16(src.codes, voff[k], dst);
-    else
-      copy4(last_rope ? src.rope : src.nope, voff[k], base + kTileB8 + (last_rope ? 256 : 0));
+    auto codes = [&](int j) {   // j < 18, wave-uniform
+      const bool hf = kPaged && j >= kTileCopies8 / 2;
+      copy16(hf ? src.codes[kPaged ? 1 : 0] : src.codes[0], voff[k], base + 1024u * (uint32_t)j);
+    };
+    if (NW == 1) {              // one wave: every index is known here
+      if (k < kTileCopies8)
+        codes(k);
+      else
+        issue_scale(src, k - kTileCopies8, base);
+    } else if (NW * (k + 1) <= kTileCopies8) {   // codes for every wave
+      codes(w + NW * k);
+    } else if constexpr (kPaged) {
+      if (NW == 2) {
+        issue_scale(src, 2 * (k - 9) + w, base);      // k = 9: nope of half w; k = 10: rope of half w
+      } else if (k == 4) {
+        issue_scale(src, w, base);                    // wave w: scale copy w
+      } else if (w < 2) {
+        codes(16 + w);                                // k = 5: copies 16 and 17 (n_ops 6 and 5)
+      }
+    } else {
+      // contiguous, last copy: codes for w + NW k < 18, else scale copy w + NW k - 18
+      const int j = w + NW * k;
+      if (j < kTileCopies8)
+        codes(j);
+      else
+        issue_scale(src, j - kTileCopies8, base);
+    }
   };
   auto issue_tile = [&](int it, int buf) {
-    const TileSrc8 src = tile_src(it);
+    const TileSrc8<kPaged> src = tile_src(it);
+    settle(src);
 #pragma unroll
     for (int k = 0; k < kOps; ++k) issue_op(src, k, buf);
+  };
+  // wait until this wave's copies of the oldest tile in flight have landed
+  auto wait_tile = [&]() {
+    if (n_ops == kOps)
+      wait_vm<(kAhead - 1) * kOps>();
+    else
+      wait_vm<(kAhead - 1) * (kOps - 1)>();
   };
 
   // absorbed query of the lane's head as B operands (zero for padding heads)
@@ -225,7 +315,8 @@ void mla_attend_fp8_kernel(MlaArgs a) {
 #pragma unroll
   for (int cbl = 0; cbl < 2; ++cbl) t_off[cbl] = r_t * kRowB8 + 16 * ((2 * cbl + (q16 & 1)) ^ swz8(r_t)) + 8 * (j16 & 1);
   // scales of the lane's score registers 4 a .. 4 a + 3: tokens
-  // 16 (a / 2) + 8 g + 4 (a % 2) + 0..3
+  // 16 (a / 2) + 8 g + 4 (a % 2) + 0..3, in range r's block of half a / 2 at
+  // kRangeStride r + kHalfStride (a / 2) + 4 (8 g + 4 (a % 2))
   const int sc_lds = kTileB8 + 4 * 8 * g;
 
   __shared__ int restart_flag;
@@ -235,7 +326,7 @@ void mla_attend_fp8_kernel(MlaArgs a) {
   float l_part;  // this lane's share of sum_j 2^(s_j - m_ref) (the other tokens are in lane l ^ 32)
 
   constexpr int kSRing = 5;
-  auto score_tile = [&](int it, int refill_it, const TileSrc8& refill_src, f32x16_t& sn, f32x16_t& sr) {
+  auto score_tile = [&](int it, int refill_it, const TileSrc8<kPaged>& refill_src, f32x16_t& sn, f32x16_t& sr) {
     const int refill_buf = refill_it % kDepth;
     const LDS uint8_t* tile = lds + (it % kDepth) * kSlotB8;
     u32x2_t ra[kSRing];
@@ -267,9 +358,9 @@ void mla_attend_fp8_kernel(MlaArgs a) {
     const LDS uint8_t* sc = lds + (it % kDepth) * kSlotB8 + sc_lds;
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
-      const int off = 4 * (16 * (a4 >> 1) + 4 * (a4 & 1));
+      const int off = kHalfStride * (a4 >> 1) + 16 * (a4 & 1);
       const f32x4_t fn = *reinterpret_cast<const LDS f32x4_t*>(sc + off);
-      const f32x4_t fr = *reinterpret_cast<const LDS f32x4_t*>(sc + 256 + off);
+      const f32x4_t fr = *reinterpret_cast<const LDS f32x4_t*>(sc + kRangeStride + off);
 #pragma unroll
       for (int r = 0; r < 4; ++r) sn[4 * a4 + r] = fmaf(fn[r], sn[4 * a4 + r], fr[r] * sr[4 * a4 + r]);
     }
@@ -308,8 +399,8 @@ void mla_attend_fp8_kernel(MlaArgs a) {
     const LDS uint8_t* sc = lds + (it % kDepth) * kSlotB8 + sc_lds;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const f32x4_t f0 = *reinterpret_cast<const LDS f32x4_t*>(sc + 4 * 16 * m);
-      const f32x4_t f1 = *reinterpret_cast<const LDS f32x4_t*>(sc + 4 * (16 * m + 4));
+      const f32x4_t f0 = *reinterpret_cast<const LDS f32x4_t*>(sc + kHalfStride * m);
+      const f32x4_t f1 = *reinterpret_cast<const LDS f32x4_t*>(sc + kHalfStride * m + 16);
       u32x4_t pw;
       pw.x = cvt_bf16x2(p[8 * m + 0] * f0[0], p[8 * m + 1] * f0[1]);
       pw.y = cvt_bf16x2(p[8 * m + 2] * f0[2], p[8 * m + 3] * f0[3]);
@@ -361,8 +452,8 @@ void mla_attend_fp8_kernel(MlaArgs a) {
 #pragma unroll
     for (int j = 0; j < kAhead; ++j) issue_tile(j, j);
     {
-      const TileSrc8 refill = tile_src(kAhead);
-      wait_vm<(kAhead - 1) * kOps>();
+      const TileSrc8<kPaged> refill = tile_src(kAhead);
+      wait_tile();
       tile_barrier();
       score_tile(0, kAhead, refill, sn, sr);
       apply_scales(0, sn, sr);
@@ -373,8 +464,8 @@ void mla_attend_fp8_kernel(MlaArgs a) {
       pack(0, p, pb);
     }
     for (int it = 1; it < ntiles; ++it) {
-      const TileSrc8 refill = tile_src(it + kAhead);
-      wait_vm<(kAhead - 1) * kOps>();
+      const TileSrc8<kPaged> refill = tile_src(it + kAhead);
+      wait_tile();
       tile_barrier();
       score_tile(it, it + kAhead, refill, sn, sr);
       pv_start((it - 1) % kDepth);
@@ -418,12 +509,12 @@ void mla_attend_fp8_kernel(MlaArgs a) {
   if (g == 0 && h < H) a.part_lse[slot * H + h] = (m_ref + log2_hw(l_tot)) * kLn2;
 }
 
-template <typename F>
+template <bool kPaged, typename F>
 bool with_fp8_shape(int num_heads, F&& f) {
   switch (num_heads) {
-    case 16: case 32: f(mla_attend_fp8_kernel<1>, 1); return true;
-    case 48: case 64: f(mla_attend_fp8_kernel<2>, 2); return true;
-    case 96: case 128: f(mla_attend_fp8_kernel<4>, 4); return true;
+    case 16: case 32: f(mla_attend_fp8_kernel<1, kPaged>, 1); return true;
+    case 48: case 64: f(mla_attend_fp8_kernel<2, kPaged>, 2); return true;
+    case 96: case 128: f(mla_attend_fp8_kernel<4, kPaged>, 4); return true;
     default: return false;
   }
 }
@@ -433,13 +524,15 @@ bool with_fp8_shape(int num_heads, F&& f) {
 hipError_t launch_mla_attend_fp8(const MlaArgs& a, hipStream_t st) {
   const dim3 grid = a.num_splits > 0 ? dim3(a.num_splits, a.batch) : dim3(a.slots, 1);
   auto launch = [&](auto kernel, int nw) { hipLaunchKernelGGL(kernel, grid, dim3(64 * nw), 0, st, a); };
-  if (a.page_shift > 0 || !with_fp8_shape(a.num_heads, launch)) return hipErrorInvalidValue;
+  const bool ok = a.page_shift > 0 ? with_fp8_shape<true>(a.num_heads, launch)
+                                   : with_fp8_shape<false>(a.num_heads, launch);
+  if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 int mla_attend_fp8_blocks_per_cu(int num_heads) {
   int n = 0;
-  const bool ok = with_fp8_shape(num_heads, [&](auto kernel, int nw) {
+  const bool ok = with_fp8_shape<false>(num_heads, [&](auto kernel, int nw) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(kernel), 64 * nw,
                                                      0) != hipSuccess) {
       (void)hipGetLastError();

@@ -39,6 +39,7 @@ KERNELS = {
     "gqa_combine": ("splitkv_combine_kernel", (), "combine.hip"),
     "mla_absorb": ("mla_absorb_kernel", (), ("mla_decode.hip", "mla_common.h")),
     # the E4M3 latent kernel first: its name also contains "mla_attend"
+    "mla_attend_fp8_paged": ("mla_attend_fp8_kernel", ("Lb1E", ", true>"), ("mla_fp8.hip", "mla_common.h")),
     "mla_attend_fp8": ("mla_attend_fp8_kernel", (), ("mla_fp8.hip", "mla_common.h")),
     # 16 or 48 heads: mla_attend_kernel; multiples of 32: mla_attend32_kernel
     "mla_attend_paged": ("mla_attend", ("Lb1E", ", true>"), ("mla_decode.hip", "mla_common.h")),

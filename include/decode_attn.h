@@ -419,6 +419,23 @@ DA_EXPORT da_status_t da_mla_decode_absorbed_fp8(const da_mla_params_t* params,
                                                  void* workspace, size_t workspace_bytes,
                                                  void* hip_stream);
 
+/* da_mla_decode_absorbed_fp8 over a paged E4M3 latent pool code_pool
+ * [num_pages, page_size, 576] bytes (params->cache_stride_t in bytes; the
+ * batch stride is unused; pages->page_stride in bytes). The scales are paged
+ * like the codes: the scales of row r of page P are at P*stride_b + r*stride_t
+ * of nope_scale and rope_scale. Splits start on 32-row tiles; each 16-row
+ * half of a tile lies in one page. Workspace as da_mla_decode_fp8_workspace_size.
+ * Errors: as da_mla_decode_absorbed_fp8, plus the paging checks of
+ * da_gqa_decode_paged (a NULL `pages` is INVALID_ARGUMENT). */
+DA_EXPORT da_status_t da_mla_decode_absorbed_fp8_paged(const da_mla_params_t* params,
+                                                       const da_paged_kv_t* pages,
+                                                       const da_mla_scales_t* scales,
+                                                       const void* q_nope, const void* q_rope,
+                                                       const void* code_pool, const int32_t* seq_lens,
+                                                       const void* w_uk, const void* w_uv, float* out,
+                                                       float* lse, void* workspace,
+                                                       size_t workspace_bytes, void* hip_stream);
+
 /* ------------------------------------------------------------------------ */
 /* Cache append with rotary position embedding                               */
 /* ------------------------------------------------------------------------ */

@@ -200,6 +200,9 @@ void sweep(int n) {
     (void)da_mla_decode_fp8_workspace_size(&m);
     expect("mla fp8 status", ok_status(da_mla_decode_absorbed_fp8(&m, next_u64() % 8 ? &ms8 : nullptr, FAKE, FAKE, FAKE, nullptr,
                                                                   FAKE, FAKE, (float*)FAKE, nullptr, FAKE, BIG, nullptr)), 1);
+    expect("mla fp8 paged status", ok_status(da_mla_decode_absorbed_fp8_paged(&m, next_u64() % 8 ? &pg : nullptr,
+                                                                              &ms8, FAKE, FAKE, FAKE, nullptr, FAKE, FAKE,
+                                                                              (float*)FAKE, nullptr, FAKE, BIG, nullptr)), 1);
     expect("mla paged status", ok_status(da_mla_decode_absorbed_paged(&m, &pg, FAKE, FAKE, FAKE, nullptr, FAKE, FAKE, (float*)FAKE, nullptr, FAKE, BIG, nullptr)), 1);
     expect("mla attend paged status", ok_status(da_mla_attend_split_pass_paged(&m, &pg, FAKE, FAKE, nullptr, FAKE, (float*)FAKE, nullptr)), 1);
     expect("mla append status", ok_status(da_mla_append_rope(&m, &ap, next_u64() % 2 ? &pg : nullptr, FAKE, FAKE, FAKE,

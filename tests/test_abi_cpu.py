@@ -365,6 +365,18 @@ def test_mla_fp8_entry_point_rejects_bad_arguments():
         p = mla()
         setattr(p, field, val)
         assert call(p, mla_scales()) == code, field
+    # paged pools: the descriptor is required and checked like the other paged calls
+    def call_paged(p, pg, s=mla_scales()):
+        return L.da_mla_decode_absorbed_fp8_paged(ctypes.byref(p), ctypes.byref(pg) if pg is not None else None,
+                                                  ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                  None, FAKE, 1 << 40, None)
+    mp = mla()
+    mp.cache_stride_b = 0
+    assert call_paged(mp, None) == 1
+    assert call_paged(mp, paging(page_size=48, page_stride=16 * 576)) == 1        # not a power of two
+    assert call_paged(mp, paging(max_blocks=255, page_stride=16 * 576)) == 1      # too few blocks
+    assert call_paged(mp, paging(page_stride=16 * 576 + 8)) == 1                  # not a 16-byte multiple
+    assert call_paged(mp, paging(page_stride=16 * 576), mla_scales(st=-1)) == 1
     # the GQA fp8 call bounds its token stride the same way
     assert L.da_gqa_decode_fp8(ctypes.byref(fp8_params()), ctypes.byref(scales(st=(1 << 24) + 8)), FAKE,
                                FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == 1

@@ -22,7 +22,7 @@ def test_more_than_one_gpu_exits_with_a_message():
 
 def test_every_workload_has_a_name():
     for w in ("step", "gqa", "mla", "mla-long", "gqa-ragged", "gqa-paged", "mla-paged", "gqa-fp8",
-              "append", "gqa-window", "append-fp8", "gqa-fp8-paged", "mla-fp8"):
+              "append", "gqa-window", "append-fp8", "gqa-fp8-paged", "mla-fp8", "mla-fp8-paged"):
         assert bench.workload_name(w)
 
 
@@ -47,8 +47,10 @@ def test_cpu_baseline_on_contiguous_and_paged_plans():
     ma = bench.mla_alg(2, 16, int(m.seq_lens.sum()))
     fa = bench.gqa_alg(2, 8, 2, 128, int(f8.seq_lens.sum()), elem=1)
     m8a = bench.mla_alg(2, 16, int(m8.seq_lens.sum()), elem=1)
+    (cp, snp, srp), t8 = bench.paged_pools(m8.seq_lens, [m8.cache, m8.scale_nope, m8.scale_rope], seed=9)
     plans = [("gqa", (None, ga, None, g)), ("mla", (None, ma, None, m)),
              ("gqa-fp8", (None, fa, None, f8)), ("mla-fp8", (None, m8a, None, m8)),
+             ("mla-fp8-paged", (None, m8a, None, (m8, dict(pools=(cp, snp, srp), table=t8)))),
              ("gqa-paged", (None, ga, None, (g, dict(k_pool=kp, v_pool=vp, table=tg)))),
              ("mla-paged", (None, ma, None, (m, dict(pool=pool, table=tm)))),
              ("gqa-append", (None, dict(total=2000), None, W.make_gqa_append(2, 8, 2, 128, 4096))),
@@ -56,12 +58,12 @@ def test_cpu_baseline_on_contiguous_and_paged_plans():
              ("gqa-append-fp8", (None, dict(total=2000), None, W.make_gqa_append(2, 8, 2, 128, 4096)))]
     res = bench.cpu_baseline(plans, budget_s=30.0)   # room for every sequence even on a loaded host
     assert res["kind"] == "oracle" and res["value"] > 0 and res["cores"] >= 1
-    for kind in ("gqa", "mla", "gqa-paged", "mla-paged", "gqa-fp8", "mla-fp8", "gqa-append", "mla-append",
-                 "gqa-append-fp8"):
+    for kind in ("gqa", "mla", "gqa-paged", "mla-paged", "gqa-fp8", "mla-fp8", "mla-fp8-paged", "gqa-append",
+                 "mla-append", "gqa-append-fp8"):
         assert f"{kind}: 2 of 2 sequences" in res["sample"]
     # one byte basis with the GPU figure: the step's algorithmic bytes (MLA
     # weights once per call, not once per sequence) over the oracle's seconds
-    step_bytes = 2 * ga["total"] + 2 * ma["total"] + fa["total"] + m8a["total"] + 3 * 2000
+    step_bytes = 2 * ga["total"] + 2 * ma["total"] + fa["total"] + 2 * m8a["total"] + 3 * 2000
     assert res["step_alg_bytes"] == step_bytes
     assert abs(res["value"] - step_bytes / res["seconds"] / 1e9) <= 1e-4 * res["value"] + 1e-4
     assert res["single_thread"]["seconds"] > 0 and res["cpu_model"]
@@ -94,7 +96,8 @@ def test_profile_summaries_name_every_attention_kernel():
     assert short_name(ns + "mla_attend32_kernel<4, false>(da::MlaArgs)") == "mla_attend"
     assert short_name(ns + "mla_attend32_kernel<4, true>(da::MlaArgs)") == "mla_attend_paged"
     assert short_name(ns + "mla_attend_kernel<1, 1, false>(da::MlaArgs)") == "mla_attend"
-    assert short_name(ns + "mla_attend_fp8_kernel<4>(da::MlaArgs)") == "mla_attend_fp8"
+    assert short_name(ns + "mla_attend_fp8_kernel<4, false>(da::MlaArgs)") == "mla_attend_fp8"
+    assert short_name(ns + "mla_attend_fp8_kernel<4, true>(da::MlaArgs)") == "mla_attend_fp8_paged"
     assert short_name("_ZN2da12_GLOBAL__N_119mla_attend32_kernelILi4ELb1EEEvNS_7MlaArgsE") == "mla_attend_paged"
     assert short_name(ns + "mla_merge_project_kernel(da::MlaArgs, int, int)") == "mla_merge_project"
     for k in ("mla_attend", "mla_attend_fp8", "mla_absorb", "gqa_split_pass"):

@@ -169,3 +169,80 @@ def test_error_codes_with_real_buffers():
     torch.cuda.synchronize()
     ro, rl = oracle_rows(inp, range(2))
     assert_parity(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, what="mla fp8 e4m3fn view")
+
+
+# ----------------------------------------------------------------------------
+# paged E4M3 latent pools
+# ----------------------------------------------------------------------------
+
+def paged_fp8(inp, ps, seed):
+    """Pools of the input's codes and scales in a seeded random page order;
+    every pool row that holds no cached row is NaN (code and scales)."""
+    table, n_pages = W.make_block_table(inp.seq_lens, ps, seed=seed, spare_pages=3,
+                                        max_blocks=-(-inp.cache.shape[1] // ps))
+    cp = W.paginate(inp.cache, inp.seq_lens, table, n_pages, ps, W.FP8_NAN_CODE)
+    snp = W.paginate(inp.scale_nope, inp.seq_lens, table, n_pages, ps, np.float32(np.nan))
+    srp = W.paginate(inp.scale_rope, inp.seq_lens, table, n_pages, ps, np.float32(np.nan))
+    return cp, snp, srp, table
+
+
+def run_paged(inp, ps, seed, num_splits=0):
+    from oracle.fp8 import mla_absorbed_fp8_paged_ref
+    cp, snp, srp, table = paged_fp8(inp, ps, seed)
+    qn, qr = bf16_tensor(inp.q_nope), bf16_tensor(inp.q_rope)
+    wuk, wuv = bf16_tensor(inp.w_uk), bf16_tensor(inp.w_uv)
+    sl = torch.from_numpy(inp.seq_lens.astype(np.int32)).cuda()
+    out, lse = da.mla_decode_absorbed_fp8_paged(qn, qr, torch.from_numpy(cp).cuda(), f32_tensor(snp),
+                                                f32_tensor(srp), torch.from_numpy(table).cuda(), ps, sl, wuk,
+                                                wuv, max_seq_len=inp.cache.shape[1], softmax_scale=inp.scale,
+                                                num_splits=num_splits)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    # the oracle per sequence, through its own pages
+    wuk64, wuv64 = f64(inp.w_uk), f64(inp.w_uv)
+    ro, rl = [], []
+    for b in range(len(inp.seq_lens)):
+        o, l = mla_absorbed_fp8_paged_ref(f64(inp.q_nope[b:b + 1]), f64(inp.q_rope[b:b + 1]), cp, snp, srp,
+                                          table[b:b + 1], ps, inp.seq_lens[b:b + 1], wuk64, wuv64, inp.scale)
+        ro.append(o[0])
+        rl.append(l[0])
+    return out, lse, np.stack(ro), np.stack(rl)
+
+
+PAGED = [
+    # B, H, lens, page size, splits
+    (3, 128, [700, 33, 1], 16, 0),
+    (2, 64, [1000, 257], 32, 0),
+    (4, 32, [0, 100, 511, 64], 64, 0),
+    (2, 16, [300, 2049], 16, 3),
+    (3, 96, [1500, 2, 260], 128, 0),
+    (2, 48, [129, 700], 16, 0),
+]
+
+
+@pytest.mark.parametrize("B,H,lens,ps,splits", PAGED)
+def test_paged_matches_oracle(B, H, lens, ps, splits):
+    announce(f"mla fp8 paged B{B} H{H} ps{ps} S{splits} lens{lens}")
+    inp = W.make_mla_fp8(B, H, lens, seed=31, max_seq_len=max(lens) + 40)
+    out, lse, ro, rl = run_paged(inp, ps, seed=32, num_splits=splits)
+    err = assert_parity(out, lse, ro, rl, what=f"mla fp8 paged ps{ps}")
+    print("paged errors:", err)
+
+
+def test_paged_equals_contiguous_bit_for_bit():
+    # the same rows, the same split plan: the paged kernel reads the same
+    # tiles from other addresses, so the results agree exactly
+    announce("mla fp8 paged vs contiguous, bitwise")
+    inp = W.make_mla_fp8(4, 128, [2000, 512, 31, 1200], seed=33, max_seq_len=2048)
+    out_c, lse_c = run(inp)
+    out_p, lse_p, ro, rl = run_paged(inp, 16, seed=34)
+    assert np.array_equal(out_c, out_p) and np.array_equal(lse_c, lse_p)
+    assert_parity(out_p, lse_p, ro, rl, what="mla fp8 paged bitwise case")
+
+
+def test_paged_config3_full_size_all_rows():
+    announce("mla fp8 paged config3 full B64 H128 L4096, 16-row pages, every row")
+    inp = W.make_mla_fp8_config(3)
+    out, lse, ro, rl = run_paged(inp, 16, seed=35)
+    err = assert_parity(out, lse, ro, rl, what="mla fp8 paged config3")
+    print("paged config3 errors:", err)
