@@ -20,6 +20,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libdecode_attn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+# per-kernel register, spill and scratch figures that the compiler reported
+# for the last build (kernel-resource-usage remarks)
+RESOURCES_PATH = os.path.join(BUILD_DIR, "kernel_resources.json")
 
 ARCH = "gfx950"
 COMMON_FLAGS = [
@@ -56,6 +59,26 @@ def _run(cmd):
     return p.returncode, "\n".join(lines)
 
 
+def parse_resource_usage(text: str) -> dict:
+    """{kernel symbol: {field: int}} from the compiler's kernel-resource-usage
+    remarks ("Function Name: X", then "VGPRs: n", "ScratchSize [bytes/lane]: n", ...)."""
+    out, cur = {}, None
+    for ln in text.splitlines():
+        if "remark:" not in ln:
+            continue
+        body = ln.split("remark:", 1)[1].split("[-Rpass-analysis")[0].strip()
+        if body.startswith("Function Name:"):
+            cur = body.split(":", 1)[1].strip()
+            out[cur] = {}
+        elif cur and ":" in body:
+            key, val = body.rsplit(":", 1)
+            try:
+                out[cur][key.strip()] = int(val.strip())
+            except ValueError:
+                pass
+    return out
+
+
 def build(verbose: bool = False, jobs: int = 0) -> str:
     """Compile every HIP source and link the shared library. Returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
@@ -65,15 +88,18 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
 
     def compile_one(pair):
         src, obj = pair
-        return src, _run([cc, *COMMON_FLAGS, "-c", src, "-o", obj])
+        return src, _run([cc, *COMMON_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj])
 
     jobs = jobs or min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
     with ThreadPoolExecutor(jobs) as ex:
         results = list(ex.map(compile_one, zip(srcs, objs)))
     failed = False
+    resources = {}
     for src, (rc, out) in results:
-        if out.strip() and (verbose or rc != 0):
-            print(f"[{os.path.basename(src)}]\n{out}", file=sys.stderr)
+        resources.update(parse_resource_usage(out))
+        shown = "\n".join(ln for ln in out.splitlines() if "kernel-resource-usage" not in ln)
+        if shown.strip() and (verbose or rc != 0):
+            print(f"[{os.path.basename(src)}]\n{shown}", file=sys.stderr)
         failed |= rc != 0
     if failed:
         raise RuntimeError("HIP compilation failed")
@@ -83,6 +109,9 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
         print(out, file=sys.stderr)
         raise RuntimeError("link failed")
     os.replace(tmp, LIB_PATH)
+    import json
+    with open(RESOURCES_PATH, "w") as f:
+        json.dump(resources, f, indent=1, sort_keys=True)
     if verbose:
         print(f"built {LIB_PATH}")
     return LIB_PATH

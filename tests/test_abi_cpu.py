@@ -537,3 +537,21 @@ def test_host_checks_under_address_and_undefined_behaviour_sanitizers():
     r = subprocess.run([exe, "5000"], capture_output=True, text=True, timeout=600, env=env)
     assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
     assert "host checks passed" in r.stdout
+
+
+def test_no_kernel_uses_scratch_memory():
+    # A kernel that spills vector registers, or keeps a runtime-indexed local
+    # array, gets scratch memory; its loads are counted with the untracked
+    # load-to-LDS copies, so their waits drain the copy pipelines. The build
+    # records the compiler's per-kernel figures; every kernel must have none.
+    import json
+    from decode_attention_kv_bf16_amd import build as B
+    if not os.path.exists(B.RESOURCES_PATH):
+        pytest.skip("no build record (run the build first)")
+    res = json.load(open(B.RESOURCES_PATH))
+    assert len(res) >= 20
+    bad = {k: v for k, v in res.items()
+           if v.get("ScratchSize [bytes/lane]", 0) or v.get("VGPRs Spill", 0)}
+    assert not bad, bad
+    for k, v in res.items():
+        assert v.get("LDS Size [bytes/block]", 0) <= 160 * 1024, k
