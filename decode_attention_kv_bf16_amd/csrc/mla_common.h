@@ -93,6 +93,19 @@ __device__ __forceinline__ int row_swizzle(int row) { return row & 7; }
 // the same for rows r and r + 16, not for r and r + 8.
 __device__ __forceinline__ int row_swizzle32(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
 
+// Load-to-LDS copies as in da_device.h, with the LDS address handed to the
+// asm in M0 through an "{m0}" operand instead of saving and restoring M0
+// inside it (fewer scalar registers live across the unrolled loop). The
+// s_nop is the wait state an LDS copy needs after M0 is written.
+__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset, uint32_t lds_addr) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+               :: "v"(voffset), "s"(rsrc), "{m0}"(lds_addr) : "memory");
+}
+__device__ __forceinline__ void copy4(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset, uint32_t lds_addr) {
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :: "v"(voffset), "s"(rsrc), "{m0}"(lds_addr) : "memory");
+}
+
 // Two block-table entries of a paged pool, read with scalar loads that are
 // issued together and waited for once, inside this block (so no load is left
 // in flight when it ends). Written by hand because the compiler, short of

@@ -33,18 +33,21 @@ namespace {
 // ---------------------------------------------------------------------------
 // 1. query absorption
 // ---------------------------------------------------------------------------
-// A workgroup of 4 waves serves one head h, one half of the 512 latent
-// columns (256) and up to 64 batch rows. W_UK[h] rows of its half (64 KiB)
-// are copied HBM -> LDS by the load-to-LDS path; q_nope rows of its batch
-// block (16 KiB) by ordinary loads into LDS. Wave w computes
-// q~^T[c, b] = sum_e W_UK[h, c, e] q_nope[b, h, e] for columns 64 w .. + 63
-// on 16x16x32 matrix ops (both operands read from LDS, 16-byte reads of 16
-// rows at one chunk, rows XOR-swizzled by row mod 16), then writes bf16(q~)
-// and q~_lo = bf16(q~ - bf16(q~)) into LDS, so that every row of q^ and of
-// q~_lo leaves in whole 16-byte pieces. The workgroups of the first half
-// also copy q_rope into q^.
+// A workgroup of 4 waves serves one head h, one of the kAbsorbParts slices
+// of the 512 latent columns and up to 64 batch rows. W_UK[h] rows of its
+// slice are copied HBM -> LDS by the load-to-LDS path; q_nope rows of its
+// batch block (16 KiB) by ordinary loads into LDS. Wave w computes
+// q~^T[c, b] = sum_e W_UK[h, c, e] q_nope[b, h, e] for its kAbsorbCols / 4
+// columns on 16x16x32 matrix ops (both operands read from LDS, 16-byte reads
+// of 16 rows at one chunk, rows XOR-swizzled by row mod 16), then writes
+// bf16(q~) and q~_lo = bf16(q~ - bf16(q~)) into LDS, so that every row of q^
+// and of q~_lo leaves in whole 16-byte pieces. The workgroups of the first
+// slice also copy q_rope into q^. Quarter slices (48 KiB of LDS) let several
+// workgroups share a CU, so one's copies overlap another's stores.
 constexpr int kAbsorbRows = 64;    // batch rows per workgroup
-constexpr int kAbsorbCols = 256;   // latent columns per workgroup
+constexpr int kAbsorbParts = 4;    // column slices per head
+constexpr int kAbsorbCols = kDc / kAbsorbParts;   // latent columns per workgroup
+constexpr int kAbsorbCB = kAbsorbCols / 64;       // 16-column blocks per wave
 constexpr int kAbsorbOutB = 2 * kAbsorbCols * 2 + 16;   // staged row: hi | lo (bf16) + pad
 
 __device__ __forceinline__ int absorb_chunk(int row, int chunk) { return chunk ^ (row & 15); }
@@ -59,11 +62,11 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a) {
 
   const int H = a.num_heads;
   const int B = a.batch;
-  // grid: (head, half) pairs, batch blocks; the two halves of a head share an
+  // grid: (head, slice) pairs, batch blocks; the slices of a head share an
   // XCD (linear id mod 8 picks the XCD) so its q_nope rows come from one L2
   const int x = blockIdx.x;
-  const int h = (x >> 4) * 8 + (x & 7);
-  const int half = (x >> 3) & 1;
+  const int h = (x / (8 * kAbsorbParts)) * 8 + (x & 7);
+  const int half = (x >> 3) % kAbsorbParts;   // the slice
   const int b0 = blockIdx.y * kAbsorbRows;
   const int nb = min(kAbsorbRows, B - b0);
   const int tid = threadIdx.x;
@@ -72,11 +75,11 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a) {
   const int q4 = lane >> 4, l16 = lane & 15;
   const int c0 = half * kAbsorbCols;
 
-  {  // W_UK[h, c0 .. c0 + 255, :]: 64 wave-wide 1 KiB copies, 16 per wave;
-     // lane l of copy k fills LDS chunk 64 k + l (row 4k + l / 16)
+  {  // W_UK[h, c0 .. c0 + kAbsorbCols - 1, :]: kAbsorbCols / 4 wave-wide 1 KiB
+     // copies; lane l of copy k fills LDS chunk 64 k + l (row 4k + l / 16)
     const uint16_t* wsrc = a.w_uk + ((int64_t)h * kDc + c0) * 128;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < kAbsorbCols / 16; ++i) {
       const int k = w + 4 * i;
       const int p = k * 64 + lane;
       const int row = p >> 4;
@@ -95,18 +98,18 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a) {
   wait_vm_all();
   __syncthreads();
 
-  // wave w: columns c0 + 64 w + 16 cb + (0..15), batch rows 16 bb + (0..15)
-  f32x4_t acc[4][4];
+  // wave w: columns c0 + 16 (kAbsorbCB w + cb) + (0..15), batch rows 16 bb + (0..15)
+  f32x4_t acc[kAbsorbCB][4];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
+  for (int cb = 0; cb < kAbsorbCB; ++cb)
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) acc[cb][bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    bf16x8_t wa[4], qb[4];
+    bf16x8_t wa[kAbsorbCB], qb[4];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      const int row = 64 * w + 16 * cb + l16;
+    for (int cb = 0; cb < kAbsorbCB; ++cb) {
+      const int row = 16 * (kAbsorbCB * w + cb) + l16;
       wa[cb] = as_bf16x8(*reinterpret_cast<const LDS u32x4_t*>(w_lds + row * 256 + 16 * absorb_chunk(row, 4 * ks + q4)));
     }
 #pragma unroll
@@ -115,18 +118,18 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a) {
       qb[bb] = as_bf16x8(*reinterpret_cast<const LDS u32x4_t*>(q_lds + row * 256 + 16 * absorb_chunk(row, 4 * ks + q4)));
     }
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+    for (int cb = 0; cb < kAbsorbCB; ++cb)
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) acc[cb][bb] = mfma16x16x32(wa[cb], qb[bb], acc[cb][bb]);
   }
   __syncthreads();   // every wave is done reading W and q: their bytes become the staging area
 
-  // lane holds q~[b = 16 bb + l16][c = 64 w + 16 cb + 4 q4 + i], i = 0..3:
+  // lane holds q~[b = 16 bb + l16][c = 16 (kAbsorbCB w + cb) + 4 q4 + i], i = 0..3:
   // bf16(q~) to the row's first half, what the rounding left out (exact in
   // float32) to its second half
   LDS uint8_t* st = w_lds;
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
+  for (int cb = 0; cb < kAbsorbCB; ++cb)
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) {
       const f32x4_t v = acc[cb][bb];
@@ -136,16 +139,17 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a) {
       lo.x = cvt_bf16x2(v[0] - bf16_lo(hi.x), v[1] - bf16_hi(hi.x));
       lo.y = cvt_bf16x2(v[2] - bf16_lo(hi.y), v[3] - bf16_hi(hi.y));
       const int row = 16 * bb + l16;
-      const int col = 64 * w + 16 * cb + 4 * q4;
+      const int col = 16 * (kAbsorbCB * w + cb) + 4 * q4;
       *reinterpret_cast<LDS u32x2_t*>(st + row * kAbsorbOutB + 2 * col) = hi;
       *reinterpret_cast<LDS u32x2_t*>(st + row * kAbsorbOutB + 2 * (kAbsorbCols + col)) = lo;
     }
   __syncthreads();
 
-  // rows out: each row's 256 hi and 256 lo columns are 2 x 32 pieces of 16 B
-  for (int p = tid; p < nb * 64; p += 256) {
-    const int row = p >> 6, piece = p & 63;
-    const int part = piece >> 5, c8 = (piece & 31) * 8;
+  // rows out: each row's kAbsorbCols hi and lo columns are 2 x kAbsorbCols / 8 pieces of 16 B
+  constexpr int kPieces = kAbsorbCols / 8;
+  for (int p = tid; p < nb * 2 * kPieces; p += 256) {
+    const int row = p / (2 * kPieces), piece = p % (2 * kPieces);
+    const int part = piece / kPieces, c8 = (piece % kPieces) * 8;
     const u32x4_t v = *reinterpret_cast<const LDS u32x4_t*>(st + row * kAbsorbOutB + 2 * (part * kAbsorbCols + c8));
     const int64_t bh = (int64_t)(b0 + row) * H + h;
     uint16_t* dst = part == 0 ? a.q_hat + bh * kRowE + c0 + c8 : a.q_lo + bh * kDc + c0 + c8;
@@ -265,9 +269,9 @@ void mla_attend_kernel(MlaArgs a) {
       // straddle it; wave-uniform in any case
       constexpr int kHalf = kTileDma / 2;
       const int second = NW * i >= kHalf ? 1 : NW * i + NW <= kHalf ? 0 : (w + NW * i >= kHalf);
-      buffer_load_to_lds16(__builtin_amdgcn_readfirstlane(second) ? src.half[1] : src.half[0], voff[i], dst);
+      copy16(__builtin_amdgcn_readfirstlane(second) ? src.half[1] : src.half[0], voff[i], dst);
     } else {
-      buffer_load_to_lds16(src, voff[i], dst);
+      copy16(src, voff[i], dst);
     }
   };
   auto issue_tile = [&](int it, int buf) {
@@ -593,7 +597,7 @@ void mla_attend32_kernel(MlaArgs a) {
   if (!work.valid) return;
   const int b = work.b;
   const int64_t slot = work.slot;
-  const int t_begin = work.t_begin;
+  int t_begin = work.t_begin;   // re-read per pass of the restart loop (see there)
   const int t_end = work.t_end;
 
   if (t_begin >= t_end) {  // fixed splits only: a split past the sequence's end
@@ -645,9 +649,9 @@ void mla_attend32_kernel(MlaArgs a) {
     if constexpr (kPaged) {
       constexpr int kHalf = kTileDma / 2;
       const int second = NW * i >= kHalf ? 1 : NW * i + NW <= kHalf ? 0 : (w + NW * i >= kHalf);
-      buffer_load_to_lds16(__builtin_amdgcn_readfirstlane(second) ? src.half[1] : src.half[0], voff[i], dst);
+      copy16(__builtin_amdgcn_readfirstlane(second) ? src.half[1] : src.half[0], voff[i], dst);
     } else {
-      buffer_load_to_lds16(src, voff[i], dst);
+      copy16(src, voff[i], dst);
     }
   };
   auto issue_tile = [&](int it, int buf) {
@@ -786,6 +790,10 @@ void mla_attend32_kernel(MlaArgs a) {
   };
 
   for (;;) {
+    // Opaque to the compiler: otherwise it hoists the first tiles' copy
+    // sources out of this loop, and their scalar registers stay live (and
+    // spill) through all of it.
+    asm volatile("" : "+s"(t_begin));
 #pragma unroll
     for (int cb = 0; cb < 16; ++cb) o[cb] = f32x16_t{};
     l_part = 0.f;
@@ -1162,7 +1170,7 @@ __global__ __launch_bounds__(512) void mla_merge_project_kernel(MlaArgs a, int n
 
 hipError_t launch_mla_absorb(const MlaArgs& a, hipStream_t st) {
   // H is a multiple of 8: (head, half) pairs in runs of 8 heads per half
-  hipLaunchKernelGGL(mla_absorb_kernel, dim3(2 * a.num_heads, (a.batch + kAbsorbRows - 1) / kAbsorbRows), dim3(256),
+  hipLaunchKernelGGL(mla_absorb_kernel, dim3(kAbsorbParts * a.num_heads, (a.batch + kAbsorbRows - 1) / kAbsorbRows), dim3(256),
                      0, st, a);
   return hipGetLastError();
 }

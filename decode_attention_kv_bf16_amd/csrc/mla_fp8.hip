@@ -96,19 +96,6 @@ __device__ __forceinline__ void qk8_last(f32x16_t& s, bf16x8_t a, bf16x8_t b) {
       : "v"(a), "v"(b));
 }
 
-// Load-to-LDS copies as in da_device.h, with the LDS address handed to the
-// asm in M0 through an "{m0}" operand instead of saving and restoring M0
-// inside it (fewer scalar registers live across the unrolled loop). The
-// s_nop is the wait state an LDS copy needs after M0 is written.
-__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset, uint32_t lds_addr) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
-               :: "v"(voffset), "s"(rsrc), "{m0}"(lds_addr) : "memory");
-}
-__device__ __forceinline__ void copy4(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset, uint32_t lds_addr) {
-  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
-               :: "v"(voffset), "s"(rsrc), "{m0}"(lds_addr) : "memory");
-}
-
 // Where a tile's rows come from. Contiguous: one range of codes and the two
 // scale ranges. Paged: each 16-row half has its own page (codes resource and
 // page index, from which the scale resources are made when they are copied).
