@@ -257,9 +257,9 @@ WINDOW_CONTEXT = 8192  # rows per sequence in the cache; only the last WINDOW ar
 
 
 def setup_gqa_window():
-    """Sliding-window GQA decode: config 2's shape (Mistral 7B has the same
+    """Sliding-window GQA decode: the Llama-3-8B GQA shape (Mistral 7B has the same
     32 query heads, 8 KV heads and d 128) with 8192 cached rows per sequence
-    and a 4096-row window, so each call reads the same bytes as config 2."""
+    and a 4096-row window, so each call reads the same bytes as the 4096-row call without a window."""
     import torch
     import workloads as W
     import decode_attention_kv_bf16_amd as da
@@ -514,8 +514,8 @@ def replayed(wrapper_call):
 
 
 def setup_append(kind):
-    """One token appended per sequence with RoPE: the GQA cache of config 2
-    (B 32, Hq 32, Hkv 8, D 128, L 4096) or the MLA cache of config 3 (B 64,
+    """One token appended per sequence with RoPE: the Llama-3-8B GQA cache
+    (B 32, Hq 32, Hkv 8, D 128, L 4096) or the DeepSeek-V3 MLA cache (B 64,
     H 128, rows of 576, L 4096), at seeded positions."""
     import torch
     import workloads as W
@@ -539,7 +539,7 @@ def setup_append(kind):
                     rope="half pairs, base 10000")
         return [[("gqa_append_rope", call)]], alg, info, inp
     if kind == "gqa-append-fp8":
-        # config 2's shape into an E4M3 cache with per-(token, KV head) scales
+        # the Llama-3-8B GQA shape into an E4M3 cache with per-(token, KV head) scales
         # computed from the appended rows
         B, Hq, Hkv, D, L = 32, 32, 8, 128, 4096
         inp = W.make_gqa_append(B, Hq, Hkv, D, L, cfg=2)
@@ -802,15 +802,15 @@ def run_gpu(args):
         entry["binding_roofline"] = binding_roofline(alg, t_ms)
         paths[kind] = entry
 
-    prop = torch.cuda.get_device_properties(0)
     if args.workload == "step" and args.extra_paths:
-        # configs 4 and 5, timed on their own after the headline step (not
-        # part of it): long-context MLA and ragged MHA
-        # configs 4 and 5, then the E4M3 caches of configs 2 and 3
+        # timed on their own after the headline step (not part of it):
+        # long-context MLA, ragged MHA, then E4M3 caches of the step's GQA and
+        # MLA shapes
         for key, setup in (("mla_long", lambda: setup_mla(4)), ("gqa_ragged", lambda: setup_gqa(5)),
                            ("gqa_fp8", lambda: setup_gqa_fp8(2)), ("mla_fp8", lambda: setup_mla_fp8(3))):
             paths[key] = time_path(key, setup(), args, hev, stream)
             torch.cuda.empty_cache()
+    ceiling = hbm_ceiling(hev, stream) if args.hbm_probe else None
 
     prop = torch.cuda.get_device_properties(0)
     res = dict(metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=args.steps,
@@ -821,8 +821,56 @@ def run_gpu(args):
                roofline=roofline, paths=paths,
                device=dict(name=prop.name, cus=prop.multi_processor_count,
                            arch=getattr(prop, "gcnArchName", ""), rocm=rocm_version(),
-                           timed_region=tele.summary()))
+                           timed_region=tele.summary(), measured_hbm=ceiling))
     return res, plans
+
+
+def hbm_ceiling(hev, stream, read_mib=2048, copy_mib=1024, reps=8):
+    """The device's measured streaming rates, context for the roofline
+    fractions: the library's read probe over a read_mib buffer and its copy
+    probe over copy_mib (read + write bytes counted), over a few grid sizes
+    (workgroups per CU) and load depths, median of `reps` event-timed launches
+    each. The best shape is the ceiling; every shape is reported."""
+    import torch
+    import decode_attention_kv_bf16_amd as da
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = {"read_bytes": read_mib << 20, "copy_bytes": copy_mib << 20, "per_shape": {}}
+    buf = torch.empty(read_mib << 20, dtype=torch.uint8, device="cuda")
+    buf.random_(0, 256)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ev = [hev.create() for _ in range(2 * reps)]
+
+    def median_ms(launch):
+        for _ in range(2):
+            launch()
+        for r in range(reps):
+            hev.record(ev[2 * r], stream)
+            launch()
+            hev.record(ev[2 * r + 1], stream)
+        stream.synchronize()
+        return float(np.median([hev.elapsed_ms(ev[2 * r], ev[2 * r + 1]) for r in range(reps)]))
+
+    best = {"read": (0.0, None), "copy": (0.0, None)}
+    for wg_per_cu, depth in ((1, 4), (1, 8), (1, 16), (1.5, 4), (1.5, 8), (2, 4), (2, 8)):
+        blocks = int(wg_per_cu * cus)
+        tbs = buf.numel() / median_ms(lambda: da.probe_stream_read(buf, sink, blocks, depth)) / 1e9
+        key = f"read_{wg_per_cu}wg_per_cu_depth{depth}"
+        out["per_shape"][key] = round(tbs, 3)
+        best["read"] = max(best["read"], (tbs, key))
+    del buf
+    src = torch.empty(copy_mib << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for wg_per_cu, depth in ((1, 4), (1, 8), (2, 4), (2, 8)):
+        blocks = int(wg_per_cu * cus)
+        tbs = 2 * src.numel() / median_ms(lambda: da.probe_stream_copy(src, dst, blocks, depth)) / 1e9
+        key = f"copy_{wg_per_cu}wg_per_cu_depth{depth}"
+        out["per_shape"][key] = round(tbs, 3)
+        best["copy"] = max(best["copy"], (tbs, key))
+    del src, dst
+    torch.cuda.empty_cache()
+    out["read_tb_s"], out["read_shape"] = round(best["read"][0], 3), best["read"][1]
+    out["copy_tb_s"], out["copy_shape"] = round(best["copy"][0], 3), best["copy"][1]
+    return out
 
 
 def time_path(key, plan, args, hev, stream):
@@ -1001,7 +1049,10 @@ def cpu_baseline(plans, budget_s):
     scaled by (the path's cached rows / the sample's rows). Each timing is the
     median of 3 runs, with numpy's BLAS at all host threads and again at one
     thread. value = the step's algorithmic bytes (weights counted once per
-    call, as for the GPU) / the all-thread step time, in GB/s."""
+    call, as for the GPU) / the all-thread step time, in GB/s. `seconds` is
+    that scaled step time; `wall_seconds` the host time the whole measurement
+    took."""
+    t_start = time.perf_counter()
     try:
         from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
@@ -1045,6 +1096,7 @@ def cpu_baseline(plans, budget_s):
     return dict(value=round(step_bytes / all_t / 1e9, 4), unit="GB/s", cores=int(threads), kind="oracle",
                 sample=sample + ", step time scaled by cached rows, median of 3 runs",
                 seconds=all_t, step_alg_bytes=int(step_bytes),
+                wall_seconds=round(time.perf_counter() - t_start, 2),
                 single_thread=dict(value=round(step_bytes / one_t / 1e9, 4), seconds=round(one_t, 4)),
                 host_cpus=os.cpu_count(), cpu_model=cpu_model())
 
@@ -1058,10 +1110,12 @@ def main():
                     choices=["step", "gqa", "mla", "mla-long", "gqa-ragged", "gqa-paged",
                              "mla-paged", "gqa-fp8", "append", "gqa-window",
                              "append-fp8", "gqa-fp8-paged", "mla-fp8", "mla-fp8-paged"])
-    ap.add_argument("--cpu-budget", type=float, default=20.0,
+    ap.add_argument("--cpu-budget", type=float, default=40.0,
                     help="seconds of oracle time for the CPU baseline (0 disables)")
     ap.add_argument("--no-extra-paths", dest="extra_paths", action="store_false",
                     help="skip timing the long-context MLA and ragged MHA workloads after the step")
+    ap.add_argument("--no-hbm-probe", dest="hbm_probe", action="store_false",
+                    help="skip measuring the device's streaming read and copy rates")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB after the timed "
                          "steps (a kernel of known traffic, to scale hardware byte counters)")

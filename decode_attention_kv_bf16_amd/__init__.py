@@ -162,6 +162,10 @@ _SIGNATURES = {
                                                _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "da_splitkv_combine": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]),
+    "da_probe_stream_read": (ctypes.c_int, [_vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                            _vp, _vp]),
+    "da_probe_stream_copy": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, ctypes.c_int32,
+                                            ctypes.c_int32, _vp]),
     "da_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "da_version": (ctypes.c_int32, []),
     "da_gqa_params_size": (ctypes.c_size_t, []),
@@ -1085,3 +1089,37 @@ def mla_append_rope(q_rope: torch.Tensor, kv_new: torch.Tensor, positions: torch
                                   _stream_handle())
     _check(st, "da_mla_append_rope")
     return q_rope_out
+
+
+# ----------------------------------------------------------------------------
+# streaming probes (bandwidth ceiling; not part of the attention path)
+# ----------------------------------------------------------------------------
+
+def _probe_buffer(name: str, t: torch.Tensor):
+    _require_cuda(name, t)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def probe_stream_read(src: torch.Tensor, sink: torch.Tensor, blocks: int = 0, depth: int = 8) -> None:
+    """Read every byte of `src` once; XOR the XOR of its 32-bit words into
+    sink[0] (an int32 device tensor the caller clears). blocks = workgroups
+    (0: one per compute unit); depth = 16-byte loads in flight per thread."""
+    _probe_buffer("src", src)
+    _require_cuda("sink", sink)
+    if sink.dtype != torch.int32 or sink.numel() < 1:
+        raise ValueError("sink must be an int32 tensor with at least one element")
+    nbytes = src.numel() * src.element_size()
+    _check(_call("da_probe_stream_read", _ptr(src), nbytes, blocks, depth, _ptr(sink),
+                 _stream_handle()), "da_probe_stream_read")
+
+
+def probe_stream_copy(src: torch.Tensor, dst: torch.Tensor, blocks: int = 0, depth: int = 4) -> None:
+    """Copy the bytes of `src` into `dst` (same byte size, no overlap)."""
+    _probe_buffer("src", src)
+    _probe_buffer("dst", dst)
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same byte size")
+    _check(_call("da_probe_stream_copy", _ptr(src), _ptr(dst), nbytes, blocks, depth,
+                 _stream_handle()), "da_probe_stream_copy")

@@ -38,6 +38,14 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 // Strides beyond 2^48 elements address nothing a device can hold; rejecting
 // them first keeps every later stride product inside int64.
+// Streaming probes: at most this many workgroups, 0 picking one per compute
+// unit; 4, 8 or 16 loads in flight per thread.
+constexpr int32_t kMaxProbeBlocks = 1 << 20;
+inline int32_t probe_blocks(int32_t blocks) { return blocks == 0 ? device_cu_count() : blocks; }
+inline bool probe_shape_ok(int32_t blocks, int32_t depth) {
+  return blocks >= 0 && blocks <= kMaxProbeBlocks && (depth == 4 || depth == 8 || depth == 16);
+}
+
 constexpr int64_t kMaxStride = int64_t(1) << 48;
 inline bool stride_in_range(int64_t s) { return s >= 0 && s <= kMaxStride; }
 inline bool stride_ok(int64_t s, int64_t esz) { return stride_in_range(s) && (s * esz) % 16 == 0; }
@@ -138,8 +146,8 @@ GqaPlan plan_gqa(const da_gqa_params_t* p, int align = 1) {
   // splitting does. Work units are (sequence, KV head, head group).
   //  * at least 2 units per CU: one split, 4-wave workgroups;
   //  * the units divide the CUs with at most 2 splits (CUs / units in {1, 2}):
-  //    8-wave workgroups, CUs / units splits, exactly one per CU (config 2,
-  //    256 units: 85.7 against 87.8 us for two 4-wave splits and a combine);
+  //    8-wave workgroups, CUs / units splits, exactly one per CU (Llama-3-8B
+  //    GQA at B 32, 256 units: 85.7 against 87.8 us for two 4-wave splits and a combine);
   //  * otherwise at least half a unit per CU: 4-wave workgroups, splits for 2
   //    per CU (8-wave workgroups that do not fill the CUs evenly measured up
   //    to 13% slower);
@@ -978,6 +986,26 @@ da_status_t da_splitkv_combine(int32_t num_splits, int32_t batch, int32_t num_he
   return from_hip(da::launch_splitkv_combine(num_splits, batch * num_heads, head_dim, partial_out,
                                              partial_lse, out, lse,
                                              static_cast<hipStream_t>(hip_stream)));
+}
+
+da_status_t da_probe_stream_read(const void* src, int64_t bytes, int32_t blocks, int32_t depth,
+                                 uint32_t* sink, void* hip_stream) {
+  if (!src || !sink || bytes <= 0 || bytes % 16 != 0 || !probe_shape_ok(blocks, depth))
+    return DA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return DA_ERR_INVALID_ARGUMENT;
+  return from_hip(da::launch_stream_read(src, bytes, probe_blocks(blocks), depth, sink,
+                                         static_cast<hipStream_t>(hip_stream)));
+}
+
+da_status_t da_probe_stream_copy(const void* src, void* dst, int64_t bytes, int32_t blocks,
+                                 int32_t depth, void* hip_stream) {
+  if (!src || !dst || bytes <= 0 || bytes % 16 != 0 || !probe_shape_ok(blocks, depth))
+    return DA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(src) || !aligned16(dst)) return DA_ERR_INVALID_ARGUMENT;
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+  if (s0 < d0 + (uintptr_t)bytes && d0 < s0 + (uintptr_t)bytes) return DA_ERR_INVALID_ARGUMENT;
+  return from_hip(da::launch_stream_copy(src, dst, bytes, probe_blocks(blocks), depth,
+                                         static_cast<hipStream_t>(hip_stream)));
 }
 
 const char* da_status_string(da_status_t status) {

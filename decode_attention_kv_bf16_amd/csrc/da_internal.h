@@ -57,6 +57,13 @@ bool gqa_mfma_supported(const GqaArgs& a, int dtype, int head_dim);
 hipError_t launch_gqa_mfma(const GqaArgs& a, int dtype, int head_dim, hipStream_t stream);
 
 // Log-sum-exp merge of split partials: rows = B * H.
+// Streaming probes (hbm_probe.hip): bytes is a positive multiple of 16,
+// depth (16-byte loads in flight per thread) is 4, 8 or 16.
+hipError_t launch_stream_read(const void* src, int64_t bytes, int32_t blocks, int32_t depth,
+                              uint32_t* sink, hipStream_t st);
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, int32_t blocks,
+                              int32_t depth, hipStream_t st);
+
 hipError_t launch_splitkv_combine(int32_t num_splits, int32_t rows, int32_t head_dim,
                                   const float* part_out, const float* part_lse,
                                   float* out, float* lse, hipStream_t stream);

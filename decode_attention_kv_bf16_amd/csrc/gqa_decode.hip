@@ -333,7 +333,7 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_kernel(GqaArgs a) {
   // steps in flight per wave: for one bf16 head per workgroup (MHA; ragged
   // B = 64: 688 -> 680 us; with more heads it measured slower) and for fp8
   // caches, whose steps carry half the bytes, so that a wave's load latency
-  // is no longer hidden by the other waves alone (config 2 shape: 66 -> US us).
+  // is no longer hidden by the other waves alone.
   constexpr bool kPrefetch = (sizeof(T) == 2 && GH == 1) || kFp8;
   constexpr int kStep = kWaves * TOK;
   typename R::Raw kw[U], vw[U];

@@ -4,6 +4,9 @@
     python -m decode_attention_kv_bf16_amd.profiling traffic --fetch FETCH_DIR --write WRITE_DIR \
         --copy-bytes N --fetch-command CMD --write-command CMD --workload NAME --out-md FILE.md
 
+    python -m decode_attention_kv_bf16_amd.profiling counters DIR [DIR ...] --command CMD \
+        [--command CMD ...] --out FILE.md
+
 `stats` turns a `--kernel-trace --stats --output-format csv` run into a
 per-kernel table of launch durations. `traffic` turns two counter runs
 (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, both over a command that ends
@@ -12,7 +15,10 @@ counter's per-dispatch average (KiB) is scaled by the factor that makes the
 same counter read N bytes for the copy kernel (the last copy dispatch of the
 run). The result is merged into profiles/hbm_traffic.json, keyed by kernel,
 with the sha256 of the source file that holds the kernel, so that a reader
-can tell whether the figures still describe the current code.
+can tell whether the figures still describe the current code. `counters`
+averages any `--pmc` counters per kernel and dispatch over one or more counter
+runs and derives, where its inputs were collected, the matrix-core, vector-ALU
+and LDS utilisation and the shader clock (see counter_table).
 """
 from __future__ import annotations
 
@@ -48,6 +54,8 @@ KERNELS = {
     "gqa_append_rope_fp8": ("gqa_append_rope_fp8_kernel", (), "append_rope.hip"),
     "gqa_append_rope": ("gqa_append_rope_kernel", (), "append_rope.hip"),
     "mla_append_rope": ("mla_append_rope_kernel", (), "append_rope.hip"),
+    "probe_stream_read": ("stream_read_kernel", (), "hbm_probe.hip"),
+    "probe_stream_copy": ("stream_copy_kernel", (), "hbm_probe.hip"),
 }
 # names under which a workload's launches of a kernel are recorded (GQA over
 # paged pools runs the GQA kernel as one library call, gqa_decode_paged)
@@ -150,6 +158,62 @@ def counter_averages(counter_dir: str, counter: str, rename=lambda s: s):
     return {k: sum(v) / len(v) for k, v in per.items()}, {k: len(v) for k, v in per.items()}, copy_val
 
 
+def _dispatches(counter_dir: str, rename=lambda s: s):
+    """{dispatch id: (short kernel name, duration ns, {counter: value})} of one
+    counter run; dispatches of kernels outside this library are dropped."""
+    out = {}
+    for r in csv.DictReader(open(_find(counter_dir, "counter_collection.csv"))):
+        s = short_name(r["Kernel_Name"])
+        if not s:
+            continue
+        d = out.setdefault(r["Dispatch_Id"], [rename(s), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]), {}])
+        d[2][r["Counter_Name"]] = float(r["Counter_Value"])
+    return out
+
+
+def counter_table(dirs, cus: int = 256, xccs: int = 8):
+    """Per kernel: dispatches, mean duration under counters, the mean of every
+    counter collected, and derived figures that follow rocprofv3's own
+    derived-counter definitions (its --list-avail output). A counter with
+    per-XCC instances is summed over the XCCs in the CSV, so GRBM_GUI_ACTIVE is
+    divided by their number to give the elapsed GPU cycles of one XCC (what
+    those definitions reduce with max):
+      mfma_busy_pct  = 100 SQ_VALU_MFMA_BUSY_CYCLES / (gui * 4 * CUs)   (MfmaUtil)
+      valu_busy_pct  = 100 SQ_ACTIVE_INST_VALU / CUs / gui              (VALUBusy)
+      lds_busy_pct   = 100 SQ_LDS_IDX_ACTIVE / (gui * CUs)              (LdsUtil)
+      lds_conflicts_per_access = SQ_LDS_BANK_CONFLICT /
+                                 (SQ_LDS_IDX_ACTIVE - SQ_LDS_BANK_CONFLICT) (LdsBankConflict)
+      sclk_ghz       = gui / duration_ns
+    Derived counters requested by name (MfmaUtil, ...) are averaged as they are."""
+    per = defaultdict(lambda: {"n": 0, "dur": [], "vals": defaultdict(list)})
+    for d in dirs:
+        for _, (name, dur, vals) in _dispatches(d).items():
+            rec = per[name]
+            rec["dur"].append(dur)
+            for k, v in vals.items():
+                rec["vals"][k].append(v)
+    rows = {}
+    for name, rec in per.items():
+        mean = {k: sum(v) / len(v) for k, v in rec["vals"].items()}
+        dur = sum(rec["dur"]) / len(rec["dur"])
+        row = {"dispatches": len(rec["dur"]), "duration_us": dur / 1e3, "counters": mean}
+        gui = mean.get("GRBM_GUI_ACTIVE")
+        if gui:
+            gui /= xccs
+            row["sclk_ghz"] = gui / dur
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+                row["mfma_busy_pct"] = 100 * mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * 4 * cus)
+            if "SQ_ACTIVE_INST_VALU" in mean:
+                row["valu_busy_pct"] = 100 * mean["SQ_ACTIVE_INST_VALU"] / cus / gui
+            if "SQ_LDS_IDX_ACTIVE" in mean:
+                row["lds_busy_pct"] = 100 * mean["SQ_LDS_IDX_ACTIVE"] / (gui * cus)
+        if "SQ_LDS_BANK_CONFLICT" in mean and "SQ_LDS_IDX_ACTIVE" in mean:
+            den = mean["SQ_LDS_IDX_ACTIVE"] - mean["SQ_LDS_BANK_CONFLICT"]
+            row["lds_conflicts_per_access"] = mean["SQ_LDS_BANK_CONFLICT"] / den if den > 0 else None
+        rows[name] = row
+    return rows
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -172,7 +236,38 @@ def main(argv=None):
     t.add_argument("--alg-bytes", default="{}", help="JSON {kernel: algorithmic bytes per launch}")
     t.add_argument("--out-md", required=True)
     t.add_argument("--rename", action="append", default=[], help="KERNEL=NAME")
+    c = sub.add_parser("counters")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--command", action="append", required=True)
+    c.add_argument("--title", default="rocprofv3 counters per kernel")
+    c.add_argument("--note", default="")
+    c.add_argument("--out", required=True)
     a = ap.parse_args(argv)
+
+    if a.cmd == "counters":
+        rows = counter_table(a.dirs)
+        derived = ("sclk_ghz", "mfma_busy_pct", "valu_busy_pct", "lds_busy_pct", "lds_conflicts_per_access")
+        names = sorted({k for r in rows.values() for k in r["counters"]})
+        lines = [f"# {a.title}", "", "Counter runs (from the repository root):", "", "```", *a.command, "```", ""]
+        if a.note:
+            lines += [a.note, ""]
+        lines += ["Derived figures (rocprofv3's own definitions, GRBM_GUI_ACTIVE taken per XCC):", "",
+                  "| kernel | dispatches | us under counters | " + " | ".join(derived) + " |",
+                  "|---|---:|---:|" + "---:|" * len(derived)]
+        fmt = lambda v: "-" if v is None else f"{v:.3g}"
+        for k in sorted(rows):
+            r = rows[k]
+            lines.append(f"| {k} | {r['dispatches']} | {r['duration_us']:.2f} | "
+                         + " | ".join(fmt(r.get(d)) for d in derived) + " |")
+        lines += ["", "Counter means per dispatch (hardware counters summed over the device's instances; "
+                  "rocprofv3's derived counters as it reports them):", "",
+                  "| kernel | " + " | ".join(names) + " |", "|---|" + "---:|" * len(names)]
+        for k in sorted(rows):
+            lines.append(f"| {k} | " + " | ".join(fmt(rows[k]["counters"].get(n)) for n in names) + " |")
+        with open(a.out, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+        return
 
     if a.cmd == "stats":
         rn = _renamer(a.rename)

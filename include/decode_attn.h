@@ -576,6 +576,33 @@ DA_EXPORT da_status_t da_splitkv_combine(int32_t num_splits, int32_t batch, int3
                                float* out, float* lse, void* hip_stream);
 
 /* ------------------------------------------------------------------------ */
+/* Streaming probes                                                          */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Measurement aids, not part of the attention path: the rate at which this
+ * device streams a large buffer out of (and back into) HBM. That rate is the
+ * ceiling decode attention works against: every decode step reads each
+ * sequence's whole K/V history, so at large batch that read sets the step
+ * time (arganzheng.life, section 2.4).
+ * Time them with events on hip_stream over a buffer well beyond the caches.
+ *
+ * da_probe_stream_read reads `bytes` bytes at `src` once and XORs the XOR of
+ * all its 32-bit words into *sink (device memory, 4-byte aligned; the caller
+ * clears it first if it wants that value). Calls sharing a sink on different
+ * streams race.
+ * da_probe_stream_copy copies `bytes` bytes from src to dst (no overlap).
+ * bytes > 0 and a multiple of 16; src and dst 16-byte aligned. blocks is the
+ * number of 256-thread workgroups (1 .. 2^20), or 0 for one per compute unit;
+ * depth, the 16-byte loads each thread keeps in flight, is 4, 8 or 16.
+ * Anything else returns DA_ERR_INVALID_ARGUMENT and launches nothing.
+ */
+DA_EXPORT da_status_t da_probe_stream_read(const void* src, int64_t bytes, int32_t blocks,
+                                           int32_t depth, uint32_t* sink, void* hip_stream);
+DA_EXPORT da_status_t da_probe_stream_copy(const void* src, void* dst, int64_t bytes,
+                                           int32_t blocks, int32_t depth, void* hip_stream);
+
+/* ------------------------------------------------------------------------ */
 /* Miscellany                                                                */
 /* ------------------------------------------------------------------------ */
 

@@ -516,7 +516,7 @@ def test_noalloc_mla_rejects_oversize_on_the_host():
     assert st == 3
     assert L.da_mla_decode_absorbed_noalloc(ctypes.byref(mla(H=80)), FAKE, FAKE, FAKE, None, FAKE, FAKE,
                                             FAKE, None, None) == 2
-    # config 3 fits
+    # DeepSeek-V3 MLA at B 64, L 4096 fits
     assert L.da_mla_decode_workspace_size(ctypes.byref(mla())) <= 64 << 20
 
 
@@ -555,3 +555,28 @@ def test_no_kernel_uses_scratch_memory():
     assert not bad, bad
     for k, v in res.items():
         assert v.get("LDS Size [bytes/block]", 0) <= 160 * 1024, k
+
+
+@needs_lib
+@cpu_only
+def test_stream_probes_reject_bad_arguments():
+    L = da.lib()
+    read, copy = L.da_probe_stream_read, L.da_probe_stream_copy
+    big = ctypes.c_void_p(0x40000000)
+    assert read(None, 1 << 20, 0, 8, FAKE, None) == 1
+    assert read(FAKE, 1 << 20, 0, 8, None, None) == 1
+    assert read(FAKE, 0, 0, 8, FAKE, None) == 1
+    assert read(FAKE, 24, 0, 8, FAKE, None) == 1            # not a multiple of 16
+    assert read(FAKE_MIS, 1 << 20, 0, 8, FAKE, None) == 1
+    assert read(FAKE, 1 << 20, -1, 8, FAKE, None) == 1
+    assert read(FAKE, 1 << 20, (1 << 20) + 1, 8, FAKE, None) == 1
+    for depth in (0, 1, 2, 6, 32):
+        assert read(FAKE, 1 << 20, 0, depth, FAKE, None) == 1
+        assert copy(FAKE, big, 1 << 20, 0, depth, None) == 1
+    assert read(FAKE, 1 << 20, 0, 8, ctypes.c_void_p(FAKE.value + 2), None) == 1
+    assert copy(FAKE, None, 1 << 20, 0, 4, None) == 1
+    assert copy(FAKE, big, 1 << 20, -5, 4, None) == 1
+    assert copy(FAKE, FAKE, 1 << 20, 0, 4, None) == 1        # overlapping
+    assert copy(FAKE, ctypes.c_void_p(FAKE.value + 16), 64, 0, 4, None) == 1
+    assert copy(FAKE, big, 40, 0, 4, None) == 1
+    assert copy(FAKE_MIS, big, 64, 0, 4, None) == 1

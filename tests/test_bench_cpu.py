@@ -80,7 +80,7 @@ def test_cpu_baseline_scales_a_partial_sample_by_rows():
 
 
 def test_binding_roofline_picks_the_longer_bound():
-    # config-3 MLA in bf16 is HBM-bound on spec numbers; in E4M3 (half the
+    # DeepSeek-V3 MLA (B 64, L 4096) in bf16 is HBM-bound on spec numbers; in E4M3 (half the
     # cache bytes, the same matrix work) the matrix cores bind
     bf = bench.mla_alg(64, 128, 64 * 4096)
     f8 = bench.mla_alg(64, 128, 64 * 4096, elem=1)
@@ -102,3 +102,39 @@ def test_profile_summaries_name_every_attention_kernel():
     assert short_name(ns + "mla_merge_project_kernel(da::MlaArgs, int, int)") == "mla_merge_project"
     for k in ("mla_attend", "mla_attend_fp8", "mla_absorb", "gqa_split_pass"):
         assert len(source_sha256(k)) == 64
+    assert short_name(ns + "stream_read_kernel<8>(unsigned int const*, long, unsigned int*)") == \
+        "probe_stream_read"
+
+
+def test_counter_summary_follows_the_derived_counter_definitions(tmp_path):
+    """Two dispatches of one kernel, counters summed over 8 XCCs: the derived
+    figures are rocprofv3's MfmaUtil, VALUBusy, LdsUtil and LdsBankConflict
+    with GRBM_GUI_ACTIVE taken per XCC, and the clock is cycles / duration."""
+    from decode_attention_kv_bf16_amd.profiling import counter_table
+    hdr = ('"Correlation_Id","Dispatch_Id","Agent_Id","Queue_Id","Process_Id","Thread_Id","Grid_Size",'
+           '"Kernel_Id","Kernel_Name","Workgroup_Size","LDS_Block_Size","Scratch_Size","VGPR_Count",'
+           '"Accum_VGPR_Count","SGPR_Count","Counter_Name","Counter_Value","Start_Timestamp","End_Timestamp"')
+    name = "void da::(anonymous namespace)::mla_attend32_kernel<4, false>(da::MlaArgs)"
+    gui_per_xcc, dur_ns = 200_000, 100_000          # 2.0 GHz
+    vals = {"GRBM_GUI_ACTIVE": 8 * gui_per_xcc,
+            "SQ_VALU_MFMA_BUSY_CYCLES": 0.5 * gui_per_xcc * 1024,   # half of every SIMD's cycles
+            "SQ_ACTIVE_INST_VALU": 0.25 * gui_per_xcc * 256,
+            "SQ_LDS_IDX_ACTIVE": 0.2 * gui_per_xcc * 256,
+            "SQ_LDS_BANK_CONFLICT": 0.04 * gui_per_xcc * 256}
+    lines = [hdr]
+    for disp in (1, 2):
+        t0 = 1_000_000 * disp
+        for c, v in vals.items():
+            lines.append(f'{disp},{disp},"Agent 1",1,1,1,1,1,"{name}",256,0,0,8,0,32,"{c}",{v},{t0},{t0 + dur_ns}')
+        lines.append(f'{disp + 9},{disp + 9},"Agent 1",1,1,1,1,1,"__amd_rocclr_copyBuffer",256,0,0,8,0,32,'
+                     f'"GRBM_GUI_ACTIVE",5,{t0},{t0 + 10}')
+    (tmp_path / "run_counter_collection.csv").write_text("\n".join(lines) + "\n")
+    rows = counter_table([str(tmp_path)])
+    assert set(rows) == {"mla_attend"}
+    r = rows["mla_attend"]
+    assert r["dispatches"] == 2 and abs(r["duration_us"] - 100.0) < 1e-9
+    assert abs(r["sclk_ghz"] - 2.0) < 1e-9
+    assert abs(r["mfma_busy_pct"] - 50.0) < 1e-9
+    assert abs(r["valu_busy_pct"] - 25.0) < 1e-9
+    assert abs(r["lds_busy_pct"] - 20.0) < 1e-9
+    assert abs(r["lds_conflicts_per_access"] - 0.04 / 0.16) < 1e-9

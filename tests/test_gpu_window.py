@@ -68,7 +68,7 @@ def poison_before_window(cache, lens, w, dtype):
 
 CASES = [
     # B, Hq, Hkv, D, lens, w, dtype, splits
-    (32, 32, 8, 128, [4096] * 32, 1000, "bf16", 0),           # config 2 shape, one split
+    (32, 32, 8, 128, [4096] * 32, 1000, "bf16", 0),           # Llama-3-8B GQA shape, one split
     (4, 32, 8, 128, [4096, 700, 1, 0], 1024, "bf16", 0),       # few units: split windows
     (3, 16, 2, 128, [3000, 17, 2049], 100, "bf16", 0),
     (3, 16, 2, 128, [3000, 17, 2049], 1, "bf16", 0),          # only the newest row
