@@ -612,8 +612,9 @@ def setup_gqa_fp8_paged(cfg):
     return calls, alg, info, (inp, dict(pools=pools, table=table))
 
 
-def measured_traffic(name):
-    """HBM bytes per launch from the committed rocprofv3 counter runs
+def measured_traffic(workload, name):
+    """HBM bytes per launch of kernel `name` in bench workload `workload`
+    (its --workload value) from the committed rocprofv3 counter runs
     (profiles/hbm_traffic.json), if they were taken on the current kernel
     source; otherwise None."""
     from decode_attention_kv_bf16_amd.profiling import source_sha256
@@ -621,7 +622,7 @@ def measured_traffic(name):
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        rec = json.load(f).get(name)
+        rec = json.load(f).get(workload, {}).get(name)
     if not rec or rec.get("source_sha256") != source_sha256(name):
         return None
     return round(rec["bytes_per_launch"])
@@ -782,7 +783,7 @@ def run_gpu(args):
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(dom),
+                "traffic": measured_traffic(args.workload, dom),
                 "alg_bytes_per_launch": int(dom_bytes), "avg_launch_us": round(dom_ms * 1e3, 2),
                 "launches_queued_behind_spin": roofline_queued}
 

@@ -13,9 +13,10 @@ per-kernel table of launch durations. `traffic` turns two counter runs
 with a device-to-device copy of N bytes) into HBM bytes per launch: each
 counter's per-dispatch average (KiB) is scaled by the factor that makes the
 same counter read N bytes for the copy kernel (the last copy dispatch of the
-run). The result is merged into profiles/hbm_traffic.json, keyed by kernel,
-with the sha256 of the source file that holds the kernel, so that a reader
-can tell whether the figures still describe the current code. `counters`
+run). The result is merged into profiles/hbm_traffic.json, keyed by the
+bench workload (`--key`, its --workload value) and then by kernel, with the
+sha256 of the source files that hold the kernel, so that a reader can tell
+whether the figures still describe the current code. `counters`
 averages any `--pmc` counters per kernel and dispatch over one or more counter
 runs and derives, where its inputs were collected, the matrix-core, vector-ALU
 and LDS utilisation and the shader clock (see counter_table).
@@ -233,6 +234,7 @@ def main(argv=None):
     t.add_argument("--fetch-command", required=True)
     t.add_argument("--write-command", required=True)
     t.add_argument("--workload", required=True)
+    t.add_argument("--key", required=True, help="the bench's --workload value the runs used")
     t.add_argument("--alg-bytes", default="{}", help="JSON {kernel: algorithmic bytes per launch}")
     t.add_argument("--out-md", required=True)
     t.add_argument("--rename", action="append", default=[], help="KERNEL=NAME")
@@ -309,9 +311,9 @@ def main(argv=None):
         ab = alg.get(k)
         ratio = f"{b / ab:.3f}" if ab else "-"
         lines.append(f"| {k} | {nf[k]} | {fetch[k]:.1f} | {write[k]:.1f} | {b:.4g} | {ab if ab else '-'} | {ratio} |")
-        rec[k] = dict(bytes_per_launch=b, fetch_kib=fetch[k], write_kib=write[k], fetch_factor=ff,
-                      write_factor=wf, workload=a.workload, source_sha256=source_sha256(k),
-                      algorithmic_bytes=ab)
+        rec.setdefault(a.key, {})[k] = dict(bytes_per_launch=b, fetch_kib=fetch[k], write_kib=write[k],
+                                            fetch_factor=ff, write_factor=wf, workload=a.workload,
+                                            source_sha256=source_sha256(k), algorithmic_bytes=ab)
     with open(path, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
     with open(a.out_md, "w") as f:
