@@ -6,6 +6,7 @@
 
     python -m decode_attention_kv_bf16_amd.profiling counters DIR [DIR ...] --command CMD \
         [--command CMD ...] --out FILE.md
+    python -m decode_attention_kv_bf16_amd.profiling parity RECORD.json --command CMD --out FILE.md
 
 `stats` turns a `--kernel-trace --stats --output-format csv` run into a
 per-kernel table of launch durations. `traffic` turns two counter runs
@@ -19,7 +20,9 @@ sha256 of the source files that hold the kernel, so that a reader can tell
 whether the figures still describe the current code. `counters`
 averages any `--pmc` counters per kernel and dispatch over one or more counter
 runs and derives, where its inputs were collected, the matrix-core, vector-ALU
-and LDS utilisation and the shader clock (see counter_table).
+and LDS utilisation and the shader clock (see counter_table). `parity` turns
+the record a GPU test run writes (DA_PARITY_RECORD=path) into a table of the
+largest errors of every parity check.
 """
 from __future__ import annotations
 
@@ -215,6 +218,26 @@ def counter_table(dirs, cus: int = 256, xccs: int = 8):
     return rows
 
 
+def parity_table(rec: dict, command: str) -> str:
+    """Markdown table of a GPU test run's parity record: per check, the
+    largest row-relative output error and |lse error| with the bars it was
+    held to; a summary line for the MLA checks."""
+    rows = sorted(rec["checks"].items())
+    mla = [v for k, v in rows if "mla" in k.lower()]
+    lines = ["# GPU parity: largest errors per check", "", "Command (from the repository root, on one MI355X):", "",
+             "    " + command, "",
+             f"pytest exit status {rec['exitstatus']}; {len(rows)} parity checks. Bar: row-relative output error "
+             "<= 1e-2, |lse error| <= 1e-3 (some checks also hold a tighter per-row bound, shown as out_rtol).", ""]
+    if mla:
+        lines += [f"MLA checks: {len(mla)}; largest |lse error| {max(v['max_lse_abs_err'] for v in mla):.2e}; "
+                  f"largest row-relative output error {max(v['max_row_rel_err'] for v in mla):.2e}.", ""]
+    lines += ["| max row rel err | max lse err | out_rtol | lse_atol | test :: check |", "|---|---|---|---|---|"]
+    for k, v in rows:
+        lines.append(f"| {v['max_row_rel_err']:.2e} | {v['max_lse_abs_err']:.2e} | {v['out_rtol']:.1e} | "
+                     f"{v['lse_atol']:.0e} | {k.replace('tests/', '').replace('|', '/')} |")
+    return "\n".join(lines) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -244,7 +267,18 @@ def main(argv=None):
     c.add_argument("--title", default="rocprofv3 counters per kernel")
     c.add_argument("--note", default="")
     c.add_argument("--out", required=True)
+    pr = sub.add_parser("parity")
+    pr.add_argument("record")
+    pr.add_argument("--command", required=True)
+    pr.add_argument("--out", required=True)
     a = ap.parse_args(argv)
+
+    if a.cmd == "parity":
+        text = parity_table(json.load(open(a.record)), a.command)
+        with open(a.out, "w") as f:
+            f.write(text)
+        print(text)
+        return
 
     if a.cmd == "counters":
         rows = counter_table(a.dirs)

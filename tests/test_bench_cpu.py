@@ -138,3 +138,16 @@ def test_counter_summary_follows_the_derived_counter_definitions(tmp_path):
     assert abs(r["valu_busy_pct"] - 25.0) < 1e-9
     assert abs(r["lds_busy_pct"] - 20.0) < 1e-9
     assert abs(r["lds_conflicts_per_access"] - 0.04 / 0.16) < 1e-9
+
+
+def test_parity_table_lists_every_check_and_the_mla_summary():
+    from decode_attention_kv_bf16_amd.profiling import parity_table
+    rec = {"exitstatus": 0, "checks": {
+        "tests/test_gpu_mla.py::test_a :: mla config3": dict(max_row_rel_err=6e-3, max_lse_abs_err=2e-5,
+                                                              out_rtol=1e-2, lse_atol=1e-3),
+        "tests/test_gpu_gqa.py::test_b :: gqa config2": dict(max_row_rel_err=3e-3, max_lse_abs_err=1e-6,
+                                                              out_rtol=1e-2, lse_atol=1e-3)}}
+    text = parity_table(rec, "pytest tests -m gpu")
+    assert "2 parity checks" in text and "MLA checks: 1" in text
+    assert "| 6.00e-03 | 2.00e-05 |" in text and "| 3.00e-03 | 1.00e-06 |" in text
+    assert "tests/" not in text.split("| test :: check |")[1]
