@@ -128,7 +128,7 @@ HOST_CHECK_EXE = os.path.join(BUILD_DIR, "abi_host_check")
 def build_host_check(verbose: bool = False) -> str:
     """Build the ABI host check: api.hip with AddressSanitizer and
     UndefinedBehaviorSanitizer on its host code, the other sources as usual,
-    and the driver tests/host_check/abi_host_check.cpp, linked into one
+    and the checking program tests/host_check/abi_host_check.cpp, linked into one
     executable. Returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()

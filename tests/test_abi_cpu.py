@@ -524,7 +524,7 @@ def test_noalloc_mla_rejects_oversize_on_the_host():
 def test_host_checks_under_address_and_undefined_behaviour_sanitizers():
     # The argument checks and planners of every entry point, built with
     # AddressSanitizer and UndefinedBehaviorSanitizer on the host side, over a
-    # sweep of valid, edge and hostile parameters (the driver refuses to run
+    # sweep of valid, edge and hostile parameters (the program refuses to run
     # where a GPU could receive its fake pointers).
     import subprocess
     from decode_attention_kv_bf16_amd import build as B
