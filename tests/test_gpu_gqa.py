@@ -110,6 +110,8 @@ EDGE = [
     # 2048 workgroups, more than stay resident: sequences taken longest first,
     # with equal lengths (ties by index) and empty sequences
     (64, 32, 32, 128, [(i % 5) * 97 + (i % 3) for i in range(64)], "bf16"),
+    # one long sequence: 128K rows over many splits and a ragged last step
+    (1, 32, 8, 128, [131069], "bf16"),
 ]
 
 

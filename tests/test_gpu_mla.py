@@ -91,6 +91,7 @@ EDGE = [
     (3, 96, [1500, 2, 260]),
     (2, 128, [0, 0]),                # nothing to attend to at all
     (7, 128, [1, 5000, 0, 33, 12000, 64, 2]),   # lengths spread over 4 orders
+    (1, 128, [65533]),               # one long sequence over every workgroup
 ]
 
 
