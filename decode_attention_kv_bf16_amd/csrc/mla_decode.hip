@@ -1036,7 +1036,10 @@ __global__ __launch_bounds__(512) void mla_merge_project_kernel(MlaArgs a, int n
         for (int e = 0; e < 16; ++e) acc[e] *= f;
 #pragma unroll
         for (int j = 0; j < kMergeBatch; ++j) {
-          const float wj = bt.lse[j] == kNegInf ? 0.f : exp2_hw(fmaf(bt.lse[j], kLog2e, -mn));
+          // an empty split (lse -inf: a fixed split past the sequence's end,
+          // or no split) wrote no pieces; what its slot holds is never used
+          if (bt.lse[j] == kNegInf) continue;
+          const float wj = exp2_hw(fmaf(bt.lse[j], kLog2e, -mn));
           z += wj;
           float fv[16];
           unpack_bf16x8(bt.u[j][0], fv);

@@ -144,6 +144,27 @@ def test_stages_compose_to_the_full_call():
     assert torch.equal(out, out_s) and torch.equal(lse, lse_s)
 
 
+@pytest.mark.parametrize("B", [5, 20])   # one 16-row merge block (two thread groups per row), two blocks
+def test_empty_fixed_splits_are_never_read(B):
+    """Fixed splits past a sequence's end write lse -inf and no pieces; the
+    merge must not read their slots. The partial buffers are filled with NaN
+    before the attention stage, so any read of an empty slot shows."""
+    announce(f"mla empty fixed splits B{B}")
+    lens = [2048, 17, 4000, 129, 64] * (B // 5)
+    inp = W.make_mla(B, 128, lens, seed=8, max_seq_len=4000, pad_value=NAN)
+    qn, qr, cache, wuk, wuv, sl = mla_to_device(inp)
+    absorb, attend, merge, out, lse, bufs = da.mla_stages(qn, qr, cache, wuk, wuv, sl, inp.scale,
+                                                          num_splits=3)
+    bufs["part_out"].fill_(0xFF)                 # bf16 0xFFFF: NaN
+    bufs["part_lse"].fill_(float("nan"))
+    absorb()
+    attend()
+    merge()
+    torch.cuda.synchronize()
+    ro, rl = oracle_rows(inp, range(B))
+    assert_parity(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, what="mla empty fixed splits")
+
+
 def test_identity_projection_reduces_to_mqa():
     # W_UK, W_UV = selection of the first 128 latent columns, q_rope = 0:
     # absorbed MLA becomes MQA over K = V = c_kv[:, :128] with 128 heads sharing it
