@@ -151,3 +151,38 @@ def test_parity_table_lists_every_check_and_the_mla_summary():
     assert "2 parity checks" in text and "MLA checks: 1" in text
     assert "| 6.00e-03 | 2.00e-05 |" in text and "| 3.00e-03 | 1.00e-06 |" in text
     assert "tests/" not in text.split("| test :: check |")[1]
+
+
+def test_traffic_summary_scales_counters_by_the_copy_kernel(tmp_path, monkeypatch):
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by the factors
+    that make the run's closing copy kernel read its known size, and the
+    record lands under the bench workload and the kernel name."""
+    import json
+    from decode_attention_kv_bf16_amd import profiling
+    monkeypatch.setattr(profiling, "PROFILE_DIR", str(tmp_path))
+    hdr = ('"Correlation_Id","Dispatch_Id","Agent_Id","Queue_Id","Process_Id","Thread_Id","Grid_Size",'
+           '"Kernel_Id","Kernel_Name","Workgroup_Size","LDS_Block_Size","Scratch_Size","VGPR_Count",'
+           '"Accum_VGPR_Count","SGPR_Count","Counter_Name","Counter_Value","Start_Timestamp","End_Timestamp"')
+    name = "void da::(anonymous namespace)::mla_attend32_kernel<4, false>(da::MlaArgs)"
+    copy_bytes = 512 << 20
+
+    def run_dir(counter, kernel_kib, copy_kib):
+        d = tmp_path / counter
+        d.mkdir()
+        rows = [hdr]
+        for disp, v in ((1, kernel_kib), (2, kernel_kib + 2.0)):
+            rows.append(f'{disp},{disp},"Agent 1",1,1,1,1,1,"{name}",256,0,0,8,0,32,"{counter}",{v},0,10')
+        rows.append(f'3,3,"Agent 1",1,1,1,1,1,"__amd_rocclr_copyBuffer",256,0,0,8,0,32,"{counter}",{copy_kib},0,10')
+        (d / "run_counter_collection.csv").write_text("\n".join(rows) + "\n")
+        return str(d)
+
+    fetch = run_dir("FETCH_SIZE", 1000.0, copy_bytes / 1024 / 2)    # the copy's reads count half
+    write = run_dir("WRITE_SIZE", 100.0, copy_bytes / 1024)
+    profiling.main(["traffic", "--fetch", fetch, "--write", write, "--copy-bytes", str(copy_bytes),
+                    "--fetch-command", "f", "--write-command", "w", "--workload", "mla test",
+                    "--key", "mla", "--alg-bytes", '{"mla_attend": 2000000}',
+                    "--out-md", str(tmp_path / "t.md")])
+    rec = json.load(open(tmp_path / "hbm_traffic.json"))["mla"]["mla_attend"]
+    assert abs(rec["fetch_factor"] - 2.0) < 1e-12 and abs(rec["write_factor"] - 1.0) < 1e-12
+    assert abs(rec["bytes_per_launch"] - (1001.0 * 1024 * 2 + 101.0 * 1024)) < 1e-6
+    assert rec["algorithmic_bytes"] == 2000000 and len(rec["source_sha256"]) == 64
