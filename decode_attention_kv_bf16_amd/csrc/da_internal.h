@@ -79,7 +79,8 @@ struct MlaArgs {
   const uint16_t* w_uv;      // [H, 512, 128]
   float* out;                // [B, H, 128]
   float* lse;                // [B, H] or null
-  uint16_t* q_hat;           // [B, H, 576] bf16: [bf16(q~) | q_rope]
+  uint16_t* q_hat;           // [B, H, 576] bf16: [bf16(q~) | q_rope], in operand order
+                             // when H is a multiple of 32 (qhat_index, mla_common.h)
   // [B, H, 512] bf16: the part of q~ that bf16(q~) leaves out, q~ - bf16(q~)
   // rounded to bf16. The scores use bf16(q~) (the matrix-core operand); the
   // merge adds scale * q~_lo . o~ to each lse, the first-order change of the

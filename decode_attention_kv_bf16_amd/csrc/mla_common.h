@@ -34,6 +34,23 @@ constexpr float kRefHeadroom = 64.0f;
 // fall on different banks.
 constexpr int kOutRowB = kDc * 2 + 16;
 
+// Where the absorbed queries q^ [B, H, 576] (bf16) live. When H is a
+// multiple of 32 they are stored in the operand order of the 32x32x16
+// attention kernels: for sequence b and head block hb (heads 32 hb .. + 31),
+// 36 k-steps of 1 KiB, step ks holding for lane l = 32 g + i the 8 values
+// q^[b, 32 hb + i][16 ks + 8 g .. + 7]. A wave's load of one step is then one
+// contiguous KiB; in row order it touched 32 rows at 32 bytes each, and the
+// 147 KiB of a sequence's queries took about 3.7 us longer to arrive at the
+// start of every split. Other head counts keep rows [B, H, 576].
+// qhat_index: element offset of q^[b, h, c] for c a multiple of 8.
+__device__ __forceinline__ int64_t qhat_index(const MlaArgs& a, int b, int h, int c) {
+  if (a.num_heads % 32 == 0) {
+    const int64_t blk = (int64_t)b * (a.num_heads / 32) + h / 32;
+    return (blk * 36 + c / 16) * 512 + ((((c >> 3) & 1) << 5) + (h & 31)) * 8;
+  }
+  return ((int64_t)b * a.num_heads + h) * kRowE + c;
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 

@@ -11,7 +11,8 @@
 // O^T += C[:, :512]^T P^T, which runs on the matrix cores.
 //
 // Kernels
-//  1. mla_absorb_kernel   q^ = [q_nope W_UK^T | q_rope] (bf16) for all (b, h).
+//  1. mla_absorb_kernel   q^ = [q_nope W_UK^T | q_rope] (bf16) for all (b, h),
+//     stored in the attention kernels' operand order (qhat_index).
 //  2. mla_attend_kernel   one workgroup per (split, sequence); for 128 heads,
 //     4 waves of 32 heads each (one wave per SIMD, accumulators in AGPRs).
 //     32-row latent tiles are copied HBM -> LDS by the buffer load-to-LDS
@@ -62,11 +63,22 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a) {
 
   const int H = a.num_heads;
   const int B = a.batch;
-  // grid: (head, slice) pairs, batch blocks; the slices of a head share an
-  // XCD (linear id mod 8 picks the XCD) so its q_nope rows come from one L2
+  // grid: (head, slice) pairs, batch blocks. The slices of a head share an
+  // XCD (linear id mod 8 picks the XCD), so its q_nope rows come from one L2.
+  // With H a multiple of 64 the 8 heads h = 8k .. 8k + 7 also share one (XCD
+  // k mod 8): their pieces of q^ in operand order fill whole 128-byte lines,
+  // which that XCD's L2 then writes back whole. Otherwise head h goes to XCD
+  // h mod 8.
   const int x = blockIdx.x;
-  const int h = (x / (8 * kAbsorbParts)) * 8 + (x & 7);
-  const int half = (x >> 3) % kAbsorbParts;   // the slice
+  int h, half;   // half: the slice
+  if (H % 64 == 0) {
+    const int t = x >> 3, t2 = t >> 3;
+    h = (t2 / kAbsorbParts) * 64 + (x & 7) * 8 + (t & 7);
+    half = t2 % kAbsorbParts;
+  } else {
+    h = (x / (8 * kAbsorbParts)) * 8 + (x & 7);
+    half = (x >> 3) % kAbsorbParts;
+  }
   const int b0 = blockIdx.y * kAbsorbRows;
   const int nb = min(kAbsorbRows, B - b0);
   const int tid = threadIdx.x;
@@ -152,14 +164,14 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a) {
     const int part = piece / kPieces, c8 = (piece % kPieces) * 8;
     const u32x4_t v = *reinterpret_cast<const LDS u32x4_t*>(st + row * kAbsorbOutB + 2 * (part * kAbsorbCols + c8));
     const int64_t bh = (int64_t)(b0 + row) * H + h;
-    uint16_t* dst = part == 0 ? a.q_hat + bh * kRowE + c0 + c8 : a.q_lo + bh * kDc + c0 + c8;
+    uint16_t* dst = part == 0 ? a.q_hat + qhat_index(a, b0 + row, h, c0 + c8) : a.q_lo + bh * kDc + c0 + c8;
     *reinterpret_cast<u32x4_t*>(dst) = v;
   }
   if (half == 0) {  // q_rope (already rotated) into q^: 8 pieces of 16 B per row
     for (int p = tid; p < nb * 8; p += 256) {
       const int row = p >> 3, ch = p & 7;
       const int64_t bh = (int64_t)(b0 + row) * H + h;
-      *reinterpret_cast<u32x4_t*>(a.q_hat + bh * kRowE + kDc + 8 * ch) =
+      *reinterpret_cast<u32x4_t*>(a.q_hat + qhat_index(a, b0 + row, h, kDc + 8 * ch)) =
           *reinterpret_cast<const u32x4_t*>(a.q_rope + bh * 64 + 8 * ch);
     }
   }
@@ -665,9 +677,10 @@ void mla_attend32_kernel(MlaArgs a) {
   const int h = 32 * w + l32;
   bf16x8_t qb[36];
   {
-    const uint16_t* qp = a.q_hat + ((int64_t)b * H + h) * kRowE + 8 * g;
+    // operand order (H is a multiple of 32 here): one contiguous KiB per step
+    const uint16_t* qp = a.q_hat + qhat_index(a, b, 32 * w, 0) + 8 * lane;
 #pragma unroll
-    for (int ks = 0; ks < 36; ++ks) qb[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + 16 * ks));
+    for (int ks = 0; ks < 36; ++ks) qb[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + 512 * ks));
 #pragma unroll
     for (int ks = 0; ks < 36; ++ks) asm volatile("" ::"v"(qb[ks]));
   }
@@ -1172,7 +1185,7 @@ __global__ __launch_bounds__(512) void mla_merge_project_kernel(MlaArgs a, int n
 }  // namespace
 
 hipError_t launch_mla_absorb(const MlaArgs& a, hipStream_t st) {
-  // H is a multiple of 8: (head, half) pairs in runs of 8 heads per half
+  // H is a multiple of 8: (head, slice) pairs in runs of 8 heads per slice
   hipLaunchKernelGGL(mla_absorb_kernel, dim3(kAbsorbParts * a.num_heads, (a.batch + kAbsorbRows - 1) / kAbsorbRows), dim3(256),
                      0, st, a);
   return hipGetLastError();

@@ -277,10 +277,16 @@ void mla_attend_fp8_kernel(MlaArgs a) {
   // absorbed query of the lane's head as B operands (zero for padding heads)
   bf16x8_t qb[36];
   {
-    const uint16_t* qp = a.q_hat + ((int64_t)b * H + min(h, H - 1)) * kRowE + 8 * g;
+    // operand order when H is a multiple of 32 (one contiguous KiB per step;
+    // a wave past the last head block reads its block's first one), rows
+    // otherwise
+    const bool blocks = H % 32 == 0;
+    const uint16_t* qp = blocks ? a.q_hat + qhat_index(a, b, min(32 * w, H - 32), 0) + 8 * lane
+                                : a.q_hat + ((int64_t)b * H + min(h, H - 1)) * kRowE + 8 * g;
+    const int step = blocks ? 512 : 16;
 #pragma unroll
     for (int ks = 0; ks < 36; ++ks) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qp + 16 * ks);
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qp + step * ks);
       qb[ks] = as_bf16x8(h < H ? v : u32x4_t{0u, 0u, 0u, 0u});
     }
 #pragma unroll

@@ -259,9 +259,14 @@ DA_EXPORT size_t da_noalloc_scratch_bytes(void);
  * section 4, "Absorb"): with q~ = q_nope[b,h] W_UK[h]^T (float32 accumulation),
  * q_hat[b, h, :] = [bf16(q~) | q_rope[b,h]].
  *   q_hat  B*H*(2 d_c + d_rope) bf16 = B*H*1088, contiguous (written): first
- *          the absorbed queries [B, H, d_c + d_rope], then the low parts
+ *          the absorbed queries, B*H*(d_c + d_rope) values, then the low parts
  *          q~_lo [B, H, d_c] = bf16(q~ - bf16(q~)), which stage 3 uses to
- *          correct the lse. */
+ *          correct the lse. The absorbed queries are rows [B, H, d_c + d_rope]
+ *          when H is not a multiple of 32; when it is, they are in the order
+ *          stage 2's matrix ops read them: for each b and block of 32 heads,
+ *          36 steps of 512 values, step ks holding for i < 32 and g < 2 the 8
+ *          values q_hat[b, 32 blk + i, 16 ks + 8 g .. + 7] at 8 (32 g + i).
+ *          Treat the buffer as opaque between the stages. */
 DA_EXPORT da_status_t da_mla_absorb_query(const da_mla_params_t* params,
                                           const void* q_nope, const void* q_rope,
                                           const void* w_uk, void* q_hat, void* hip_stream);
