@@ -144,6 +144,32 @@ def test_stages_compose_to_the_full_call():
     assert torch.equal(out, out_s) and torch.equal(lse, lse_s)
 
 
+@pytest.mark.parametrize("H", [32, 64, 96, 128])   # 1 to 4 waves of 32 heads
+def test_balanced_splits_with_poisoned_partials(H):
+    """Balanced splits over the 32-head-block kernel, with sequences of 2,
+    32, 1, 75, 14 and 125 splits of 5 tiles on 256 workgroups. The partial
+    buffers (and the split table after the lse slots) start as NaN, the
+    attention stage runs twice, and the stages must still equal the one-call
+    path bit for bit and the oracle to the bar: the merge reads only what the
+    latest attention stage wrote."""
+    announce(f"mla balanced splits, poisoned partials H{H}")
+    lens = [300, 5000, 17, 12000, 2100, 20000]
+    inp = W.make_mla(len(lens), H, lens, seed=21, max_seq_len=20000, pad_value=NAN)
+    qn, qr, cache, wuk, wuv, sl = mla_to_device(inp)
+    assert da.mla_num_splits(qn, qr, cache, wuv) == 0
+    absorb, attend, merge, out_s, lse_s, bufs = da.mla_stages(qn, qr, cache, wuk, wuv, sl, inp.scale)
+    bufs["part_out"].fill_(0xFF)                 # bf16 0xFFFF: NaN
+    bufs["part_lse"].fill_(NAN)
+    absorb()
+    attend()
+    attend()
+    merge()
+    out, lse = da.mla_decode_absorbed(qn, qr, cache, wuk, wuv, sl, inp.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_s) and torch.equal(lse, lse_s)
+    print(assert_all(inp, out.cpu().numpy(), lse.cpu().numpy(), what=f"mla balanced poisoned H{H}"))
+
+
 @pytest.mark.parametrize("B", [5, 20])   # one 16-row merge block (two thread groups per row), two blocks
 def test_empty_fixed_splits_are_never_read(B):
     """Fixed splits past a sequence's end write lse -inf and no pieces; the
