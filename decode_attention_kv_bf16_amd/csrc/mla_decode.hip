@@ -35,20 +35,22 @@ namespace {
 // 1. query absorption
 // ---------------------------------------------------------------------------
 // A workgroup of 4 waves serves one head h, one of the kAbsorbParts slices
-// of the 512 latent columns and up to 64 batch rows. W_UK[h] rows of its
-// slice are copied HBM -> LDS by the load-to-LDS path; q_nope rows of its
-// batch block (16 KiB) by ordinary loads into LDS. Wave w computes
+// of the 512 latent columns and up to kAbsorbRows batch rows. W_UK[h] rows of
+// its slice are copied HBM -> LDS by the load-to-LDS path; q_nope rows of its
+// batch block by ordinary loads into LDS. Wave w computes
 // q~^T[c, b] = sum_e W_UK[h, c, e] q_nope[b, h, e] for its kAbsorbCols / 4
 // columns on 16x16x32 matrix ops (both operands read from LDS, 16-byte reads
 // of 16 rows at one chunk, rows XOR-swizzled by row mod 16), then writes
 // bf16(q~) and q~_lo = bf16(q~ - bf16(q~)) into LDS, so that every row of q^
 // and of q~_lo leaves in whole 16-byte pieces. The workgroups of the first
-// slice also copy q_rope into q^. Quarter slices (48 KiB of LDS) let several
-// workgroups share a CU, so one's copies overlap another's stores.
-constexpr int kAbsorbRows = 64;    // batch rows per workgroup
-constexpr int kAbsorbParts = 4;    // column slices per head
+// slice also copy q_rope into q^. Eighth slices and 32-row blocks (24 KiB of
+// LDS) let several workgroups share a CU, so one's copies overlap another's
+// stores (about 1% faster per MLA call than quarter slices of 64 rows).
+constexpr int kAbsorbRows = 32;    // batch rows per workgroup
+constexpr int kAbsorbParts = 8;    // column slices per head
 constexpr int kAbsorbCols = kDc / kAbsorbParts;   // latent columns per workgroup
 constexpr int kAbsorbCB = kAbsorbCols / 64;       // 16-column blocks per wave
+constexpr int kAbsorbBB = kAbsorbRows / 16;       // 16-row batch blocks
 constexpr int kAbsorbOutB = 2 * kAbsorbCols * 2 + 16;   // staged row: hi | lo (bf16) + pad
 
 __device__ __forceinline__ int absorb_chunk(int row, int chunk) { return chunk ^ (row & 15); }
@@ -111,28 +113,28 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a) {
   __syncthreads();
 
   // wave w: columns c0 + 16 (kAbsorbCB w + cb) + (0..15), batch rows 16 bb + (0..15)
-  f32x4_t acc[kAbsorbCB][4];
+  f32x4_t acc[kAbsorbCB][kAbsorbBB];
 #pragma unroll
   for (int cb = 0; cb < kAbsorbCB; ++cb)
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) acc[cb][bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int bb = 0; bb < kAbsorbBB; ++bb) acc[cb][bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    bf16x8_t wa[kAbsorbCB], qb[4];
+    bf16x8_t wa[kAbsorbCB], qb[kAbsorbBB];
 #pragma unroll
     for (int cb = 0; cb < kAbsorbCB; ++cb) {
       const int row = 16 * (kAbsorbCB * w + cb) + l16;
       wa[cb] = as_bf16x8(*reinterpret_cast<const LDS u32x4_t*>(w_lds + row * 256 + 16 * absorb_chunk(row, 4 * ks + q4)));
     }
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
+    for (int bb = 0; bb < kAbsorbBB; ++bb) {
       const int row = 16 * bb + l16;
       qb[bb] = as_bf16x8(*reinterpret_cast<const LDS u32x4_t*>(q_lds + row * 256 + 16 * absorb_chunk(row, 4 * ks + q4)));
     }
 #pragma unroll
     for (int cb = 0; cb < kAbsorbCB; ++cb)
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) acc[cb][bb] = mfma16x16x32(wa[cb], qb[bb], acc[cb][bb]);
+      for (int bb = 0; bb < kAbsorbBB; ++bb) acc[cb][bb] = mfma16x16x32(wa[cb], qb[bb], acc[cb][bb]);
   }
   __syncthreads();   // every wave is done reading W and q: their bytes become the staging area
 
@@ -143,7 +145,7 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a) {
 #pragma unroll
   for (int cb = 0; cb < kAbsorbCB; ++cb)
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
+    for (int bb = 0; bb < kAbsorbBB; ++bb) {
       const f32x4_t v = acc[cb][bb];
       u32x2_t hi, lo;
       hi.x = cvt_bf16x2(v[0], v[1]);
