@@ -72,14 +72,14 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a) {
   // which that XCD's L2 then writes back whole. Otherwise head h goes to XCD
   // h mod 8.
   const int x = blockIdx.x;
-  int h, half;   // half: the slice
+  int h, part;   // the head and its column slice
   if (H % 64 == 0) {
     const int t = x >> 3, t2 = t >> 3;
     h = (t2 / kAbsorbParts) * 64 + (x & 7) * 8 + (t & 7);
-    half = t2 % kAbsorbParts;
+    part = t2 % kAbsorbParts;
   } else {
     h = (x / (8 * kAbsorbParts)) * 8 + (x & 7);
-    half = (x >> 3) % kAbsorbParts;
+    part = (x >> 3) % kAbsorbParts;
   }
   const int b0 = blockIdx.y * kAbsorbRows;
   const int nb = min(kAbsorbRows, B - b0);
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a) {
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int q4 = lane >> 4, l16 = lane & 15;
-  const int c0 = half * kAbsorbCols;
+  const int c0 = part * kAbsorbCols;
 
   {  // W_UK[h, c0 .. c0 + kAbsorbCols - 1, :]: kAbsorbCols / 4 wave-wide 1 KiB
      // copies; lane l of copy k fills LDS chunk 64 k + l (row 4k + l / 16)
@@ -139,8 +139,8 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a) {
   __syncthreads();   // every wave is done reading W and q: their bytes become the staging area
 
   // lane holds q~[b = 16 bb + l16][c = 16 (kAbsorbCB w + cb) + 4 q4 + i], i = 0..3:
-  // bf16(q~) to the row's first half, what the rounding left out (exact in
-  // float32) to its second half
+  // bf16(q~) to the row's first part, what the rounding left out (exact in
+  // float32) to its second part
   LDS uint8_t* st = w_lds;
 #pragma unroll
   for (int cb = 0; cb < kAbsorbCB; ++cb)
@@ -163,13 +163,13 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a) {
   constexpr int kPieces = kAbsorbCols / 8;
   for (int p = tid; p < nb * 2 * kPieces; p += 256) {
     const int row = p / (2 * kPieces), piece = p % (2 * kPieces);
-    const int part = piece / kPieces, c8 = (piece % kPieces) * 8;
-    const u32x4_t v = *reinterpret_cast<const LDS u32x4_t*>(st + row * kAbsorbOutB + 2 * (part * kAbsorbCols + c8));
+    const int is_lo = piece / kPieces, c8 = (piece % kPieces) * 8;   // is_lo: the q~_lo half
+    const u32x4_t v = *reinterpret_cast<const LDS u32x4_t*>(st + row * kAbsorbOutB + 2 * (is_lo * kAbsorbCols + c8));
     const int64_t bh = (int64_t)(b0 + row) * H + h;
-    uint16_t* dst = part == 0 ? a.q_hat + qhat_index(a, b0 + row, h, c0 + c8) : a.q_lo + bh * kDc + c0 + c8;
+    uint16_t* dst = is_lo == 0 ? a.q_hat + qhat_index(a, b0 + row, h, c0 + c8) : a.q_lo + bh * kDc + c0 + c8;
     *reinterpret_cast<u32x4_t*>(dst) = v;
   }
-  if (half == 0) {  // q_rope (already rotated) into q^: 8 pieces of 16 B per row
+  if (part == 0) {  // q_rope (already rotated) into q^: 8 pieces of 16 B per row
     for (int p = tid; p < nb * 8; p += 256) {
       const int row = p >> 3, ch = p & 7;
       const int64_t bh = (int64_t)(b0 + row) * H + h;
