@@ -461,9 +461,28 @@ def setup_mla_paged(cfg):
     return calls, alg, info, (inp, dict(pool=pool_h, table=table_h))
 
 
-def setup_gqa_fp8(cfg):
+def head_major_codes(x):
+    """E4M3 codes [X, T, H, D] (numpy) stored on the GPU head-major, [X, H, T,
+    D], returned as the [X, T, H, D] view of that storage: each KV head's rows
+    are then one contiguous run per sequence (or page)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x.transpose(0, 2, 1, 3))).cuda()
+    return t.permute(0, 2, 1, 3)
+
+
+def clone_view(t):
+    """A copy of `t` with the same strides (a permuted view's storage cloned)."""
+    if t.is_contiguous():
+        return t.clone()
+    base = t.permute(0, 2, 1, 3)
+    return base.clone().permute(0, 2, 1, 3)
+
+
+def setup_gqa_fp8(cfg, layout="head"):
     """The GQA workload of `cfg` with K and V in E4M3 and one fp32 scale per
-    (token, KV head) for each."""
+    (token, KV head) for each. layout "head": codes stored [B, Hkv, L, D]
+    (each KV head's rows contiguous); "token": [B, L, Hkv, D] (a KV head's
+    128-byte rows 1 KiB apart). Scales are token-major [B, L, Hkv] in both."""
     import torch
     import workloads as W
     import decode_attention_kv_bf16_amd as da
@@ -472,12 +491,14 @@ def setup_gqa_fp8(cfg):
     dev = lambda a: torch.from_numpy(a).cuda()
     # scales token-major [B, L, Hkv] (a KV head's scales 32 bytes apart): in
     # one process this layout measured 57.4 us per call against 68.4 us for
-    # head-major scales, whose reads are contiguous (and 1.2x fewer bytes)
-    k0, v0, ks, vs = dev(inp.k), dev(inp.v), dev(inp.k_scale), dev(inp.v_scale)
+    # head-major scales with token-major codes, and 45.3 against 49.1 us with
+    # head-major codes
+    codes = head_major_codes if layout == "head" else dev
+    k0, v0, ks, vs = codes(inp.k), codes(inp.v), dev(inp.k_scale), dev(inp.v_scale)
     sl = torch.from_numpy(inp.seq_lens).cuda()
     fp = k0.numel() * 2
     n_copies = max(1, math.ceil(MALL_GUARD_BYTES / fp)) if fp < MALL_GUARD_BYTES else 1
-    copies = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(n_copies - 1)]
+    copies = [(k0, v0)] + [(clone_view(k0), clone_view(v0)) for _ in range(n_copies - 1)]
     B, Hq, D = q.shape
     out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
@@ -492,6 +513,7 @@ def setup_gqa_fp8(cfg):
     alg["total"] += scale_bytes
     info = dict(batch=B, q_heads=Hq, kv_heads=int(inp.k.shape[2]), head_dim=D,
                 seq_len=int(inp.seq_lens.max()), cache="e4m3 + fp32 scale per (token, KV head)",
+                codes="head-major [B, Hkv, L, D]" if layout == "head" else "token-major [B, L, Hkv, D]",
                 cache_copies=len(copies))
     return calls, alg, info, inp
 
@@ -573,9 +595,11 @@ def setup_append(kind):
     return [[("mla_append_rope", call)]], alg, info, inp
 
 
-def setup_gqa_fp8_paged(cfg):
+def setup_gqa_fp8_paged(cfg, layout="head"):
     """The fp8 workload of `cfg` over paged pools: codes and per-(token, KV
-    head) scales in 32-row pages placed in a seeded random physical order."""
+    head) scales in 32-row pages placed in a seeded random physical order.
+    layout "head": each page's codes stored [Hkv, 32, D]; "token": [32, Hkv,
+    D]. Scales [pages, 32, Hkv] in both."""
     import torch
     import workloads as W
     import decode_attention_kv_bf16_amd as da
@@ -585,10 +609,10 @@ def setup_gqa_fp8_paged(cfg):
     table, n_pages = W.make_block_table(lens, ps, seed=cfg, spare_pages=0)
     pools = [W.paginate(x, lens, table, n_pages, ps, 0) for x in (inp.k, inp.v, inp.k_scale, inp.v_scale)]
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    first = [d(x) for x in pools]
+    first = [head_major_codes(x) if layout == "head" else d(x) for x in pools[:2]] + [d(x) for x in pools[2:]]
     fp = sum(t.numel() * t.element_size() for t in first)
     n_copies = max(1, math.ceil(MALL_GUARD_BYTES / fp))
-    copies = [first] + [[t.clone() for t in first] for _ in range(n_copies - 1)]
+    copies = [first] + [[clone_view(t) if t.dim() == 4 else t.clone() for t in first] for _ in range(n_copies - 1)]
     tab = d(table)
     q = to_dev_bf16(inp.q)
     sl = torch.from_numpy(lens).cuda()
@@ -608,6 +632,8 @@ def setup_gqa_fp8_paged(cfg):
     alg["total"] += scale_bytes + table_bytes
     info = dict(batch=B, q_heads=Hq, kv_heads=int(inp.k.shape[2]), head_dim=D, seq_len=int(lens.max()),
                 page_size=ps, cache="e4m3 + fp32 scale per (token, KV head), paged",
+                codes="head-major pages [pages, Hkv, 32, D]" if layout == "head" else
+                "token-major pages [pages, 32, Hkv, D]",
                 cache_copies=len(copies))
     return calls, alg, info, (inp, dict(pools=pools, table=table))
 
@@ -649,8 +675,12 @@ def run_gpu(args):
         plans.append(("mla-paged", setup_mla_paged(3)))
     if args.workload == "gqa-fp8":
         plans.append(("gqa-fp8", setup_gqa_fp8(2)))
+    if args.workload == "gqa-fp8-token-major":
+        plans.append(("gqa-fp8", setup_gqa_fp8(2, "token")))
     if args.workload == "gqa-fp8-paged":
         plans.append(("gqa-fp8-paged", setup_gqa_fp8_paged(2)))
+    if args.workload == "gqa-fp8-paged-token-major":
+        plans.append(("gqa-fp8-paged", setup_gqa_fp8_paged(2, "token")))
     if args.workload == "mla-fp8":
         plans.append(("mla-fp8", setup_mla_fp8(3)))
     if args.workload == "mla-fp8-paged":
@@ -808,7 +838,9 @@ def run_gpu(args):
         # long-context MLA, ragged MHA, then E4M3 caches of the step's GQA and
         # MLA shapes
         for key, setup in (("mla_long", lambda: setup_mla(4)), ("gqa_ragged", lambda: setup_gqa(5)),
-                           ("gqa_fp8", lambda: setup_gqa_fp8(2)), ("mla_fp8", lambda: setup_mla_fp8(3))):
+                           ("gqa_fp8", lambda: setup_gqa_fp8(2)),
+                           ("gqa_fp8_token_major", lambda: setup_gqa_fp8(2, "token")),
+                           ("mla_fp8", lambda: setup_mla_fp8(3))):
             paths[key] = time_path(key, setup(), args, hev, stream)
             torch.cuda.empty_cache()
     ceiling = hbm_ceiling(hev, stream) if args.hbm_probe else None
@@ -933,9 +965,11 @@ def workload_name(w):
             "gqa-ragged": "llama2-7b-mha-ragged-b64-l1-8192",
             "gqa-paged": "llama3-8b-gqa-b32-l4096-paged16",
             "mla-paged": "deepseek-v3-mla-b64-l4096-paged16",
-            "gqa-fp8": "llama3-8b-gqa-b32-l4096-fp8e4m3",
+            "gqa-fp8": "llama3-8b-gqa-b32-l4096-fp8e4m3-headmajor",
+            "gqa-fp8-token-major": "llama3-8b-gqa-b32-l4096-fp8e4m3-tokenmajor",
             "gqa-window": "mistral-7b-shape-gqa-b32-l8192-window4096",
-            "gqa-fp8-paged": "llama3-8b-gqa-b32-l4096-fp8e4m3-paged32",
+            "gqa-fp8-paged": "llama3-8b-gqa-b32-l4096-fp8e4m3-paged32-headmajor",
+            "gqa-fp8-paged-token-major": "llama3-8b-gqa-b32-l4096-fp8e4m3-paged32-tokenmajor",
             "mla-fp8": "deepseek-v3-mla-b64-l4096-fp8e4m3-nope-rope-scales",
             "mla-fp8-paged": "deepseek-v3-mla-b64-l4096-fp8e4m3-nope-rope-scales-paged16",
             "append-fp8": "cache append + rope into e4m3: llama3-8b-gqa-b32-l4096",
@@ -1110,7 +1144,8 @@ def main():
     ap.add_argument("--workload", default="step",
                     choices=["step", "gqa", "mla", "mla-long", "gqa-ragged", "gqa-paged",
                              "mla-paged", "gqa-fp8", "append", "gqa-window",
-                             "append-fp8", "gqa-fp8-paged", "mla-fp8", "mla-fp8-paged"])
+                             "append-fp8", "gqa-fp8-paged", "mla-fp8", "mla-fp8-paged",
+                             "gqa-fp8-token-major", "gqa-fp8-paged-token-major"])
     ap.add_argument("--cpu-budget", type=float, default=40.0,
                     help="seconds of oracle time for the CPU baseline (0 disables)")
     ap.add_argument("--no-extra-paths", dest="extra_paths", action="store_false",

@@ -496,13 +496,16 @@ template <typename T, int D>
 hipError_t launch_t(const GqaArgs& a, hipStream_t st) {
   const dim3 grid(a.num_splits, a.num_kv_heads * (a.group / a.heads_per_block), a.batch);
   // bf16: 4 waves, each with 3 steps in flight (the LDS holds 4 per wave).
-  // fp8: 6 waves with 2 in flight each (3 slots): the same bytes in flight
-  // per CU on more waves measured 6% faster (51.8 against 55.2 us, Llama-3-8B
-  // GQA at B 32, L 4096), a wave's step work overlapping another's wait. The planner's
-  // 8-wave workgroups run as these shapes with the same grid.
+  // fp8: 6 waves with one step in flight each (2 slots): six waves per CU
+  // measured 6% faster than four (51.8 against 55.2 us, Llama-3-8B GQA at B
+  // 32, L 4096), a wave's step work overlapping another's wait, and two
+  // slots per wave about 1% faster than three, over token-major, head-major
+  // and paged caches alike (A/B in one process: 52.3 against 53.3 us
+  // token-major, 44.7 against 45.2 us head-major). The planner's 8-wave
+  // workgroups run as these shapes with the same grid.
   if (a.waves_per_block == 8 || a.waves_per_block == 4) {
     if constexpr (sizeof(T) == 1)
-      hipLaunchKernelGGL((gqa_mfma_kernel<T, D, 6, 3>), grid, dim3(6 * 64), 0, st, a);
+      hipLaunchKernelGGL((gqa_mfma_kernel<T, D, 6, 2>), grid, dim3(6 * 64), 0, st, a);
     else
       hipLaunchKernelGGL((gqa_mfma_kernel<T, D, 4, 4>), grid, dim3(4 * 64), 0, st, a);
   } else {

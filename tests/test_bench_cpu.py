@@ -22,8 +22,23 @@ def test_more_than_one_gpu_exits_with_a_message():
 
 def test_every_workload_has_a_name():
     for w in ("step", "gqa", "mla", "mla-long", "gqa-ragged", "gqa-paged", "mla-paged", "gqa-fp8",
-              "append", "gqa-window", "append-fp8", "gqa-fp8-paged", "mla-fp8", "mla-fp8-paged"):
+              "append", "gqa-window", "append-fp8", "gqa-fp8-paged", "mla-fp8", "mla-fp8-paged",
+              "gqa-fp8-token-major", "gqa-fp8-paged-token-major"):
         assert bench.workload_name(w)
+
+
+def test_head_major_codes_view_the_same_values():
+    # the head-major storage, seen through the strided view, holds every code
+    # where the token-major array has it (CPU tensors here; the bench puts
+    # them on the GPU)
+    import torch
+    x = np.random.default_rng(3).integers(0, 255, (2, 5, 3, 4), dtype=np.uint8)
+    base = torch.from_numpy(np.ascontiguousarray(x.transpose(0, 2, 1, 3)))
+    view = base.permute(0, 2, 1, 3)
+    assert view.shape == x.shape and view.stride() == (3 * 5 * 4, 4, 5 * 4, 1)
+    assert np.array_equal(view.numpy(), x)
+    c = bench.clone_view(view)
+    assert c.stride() == view.stride() and torch.equal(c, view) and c.data_ptr() != view.data_ptr()
 
 
 def test_paged_pools_hold_every_row_once():

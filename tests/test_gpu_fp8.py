@@ -241,3 +241,74 @@ def test_paged_fp8_per_head_scales():
     vsp = np.broadcast_to(vh, (n_pages, 64, 4))
     ro, rl = gqa_decode_fp8_paged_ref(q64, kp, vp, ksp, vsp, table, 64, inp.seq_lens, inp.scale)
     assert_parity(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, what="fp8 paged per-head scales")
+
+
+# ----------------------------------------------------------------------------
+# head-major code storage: [B, Hkv, L, D] (or [pages, Hkv, page_size, D]),
+# given to the library as a strided [B, L, Hkv, D] view; scales token-major
+# ----------------------------------------------------------------------------
+
+def head_major(x):
+    """Codes [X, T, H, D] stored head-major on the GPU, returned as the
+    [X, T, H, D] view of that storage (strides (H T D, D, T D, 1))."""
+    t = torch.from_numpy(np.ascontiguousarray(x.transpose(0, 2, 1, 3))).cuda()
+    return t.permute(0, 2, 1, 3)
+
+
+def test_head_major_codes_config2_full_size_all_rows():
+    announce("gqa fp8 config2 full B32 L4096, head-major codes, every row")
+    inp = W.make_gqa_fp8_config(2)
+    q, k, v, ks, vs, sl = to_device(inp)
+    kh, vh = head_major(inp.k), head_major(inp.v)
+    assert kh.stride() == (8 * inp.k.shape[1] * 128, 128, inp.k.shape[1] * 128, 1)
+    out, lse = da.gqa_decode_fp8(q, kh, vh, ks, vs, sl, inp.scale)
+    out_t, lse_t = da.gqa_decode_fp8(q, k, v, ks, vs, sl, inp.scale)
+    torch.cuda.synchronize()
+    # the same values through other addresses: the same arithmetic, bit for bit
+    assert torch.equal(out, out_t) and torch.equal(lse, lse_t)
+    ro, rl = oracle_rows(inp, range(32))
+    assert_parity(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, what="fp8 config2 head-major")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,lens,ps,window,splits", [
+    (4, 32, 8, [4096, 700, 33, 0], 32, 0, 0),
+    (3, 16, 2, [3000, 17, 2049], 64, 1000, 0),
+    (3, 16, 4, [2500, 1, 777], 32, 0, 5),
+])
+def test_paged_head_major_pages(B, Hq, Hkv, lens, ps, window, splits):
+    from oracle.fp8 import gqa_decode_fp8_paged_ref
+    announce(f"gqa fp8 paged head-major pages B{B} Hq{Hq} Hkv{Hkv} ps{ps} w{window} S{splits} lens{lens}")
+    inp = W.make_gqa_fp8(B, Hq, Hkv, 128, lens, seed=57)
+    kp, vp, ksp, vsp, table = paged_fp8(inp, ps, seed=58, window=window)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    args = (d(ksp), d(vsp), d(table), ps, d(inp.seq_lens.astype(np.int32)))
+    kw = dict(max_seq_len=inp.k.shape[1], softmax_scale=inp.scale, num_splits=splits, window=window)
+    out, lse = da.gqa_decode_fp8_paged(bf16_tensor(inp.q), head_major(kp), head_major(vp), *args, **kw)
+    out_t, lse_t = da.gqa_decode_fp8_paged(bf16_tensor(inp.q), d(kp), d(vp), *args, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_t) and torch.equal(lse, lse_t)
+    q64 = W.bf16_to_f32(inp.q).astype(np.float64)
+    ro, rl = gqa_decode_fp8_paged_ref(q64, kp, vp, ksp, vsp, table, ps, inp.seq_lens, inp.scale, window=window)
+    assert_parity(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, what="fp8 paged head-major")
+
+
+def test_paged_head_major_pages_config2_full_size_all_rows():
+    from oracle.fp8 import gqa_decode_fp8_paged_ref
+    announce("gqa fp8 paged config2 full B32 L4096 ps32, head-major pages, every row")
+    inp = W.make_gqa_fp8_config(2)
+    kp, vp, ksp, vsp, table = paged_fp8(inp, 32, seed=53)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    out, lse = da.gqa_decode_fp8_paged(bf16_tensor(inp.q), head_major(kp), head_major(vp), d(ksp), d(vsp),
+                                       d(table), 32, d(inp.seq_lens.astype(np.int32)), softmax_scale=inp.scale)
+    torch.cuda.synchronize()
+    ro, rl = [], []
+    for b in range(32):   # one sequence per oracle call, on its own pages (renumbered)
+        pages = table[b, :-(-int(inp.seq_lens[b]) // 32)]
+        tab = np.arange(len(pages), dtype=np.int32)[None]
+        q64 = W.bf16_to_f32(inp.q[b:b + 1]).astype(np.float64)
+        o, l = gqa_decode_fp8_paged_ref(q64, kp[pages], vp[pages], ksp[pages], vsp[pages], tab, 32,
+                                        inp.seq_lens[b:b + 1], inp.scale)
+        ro.append(o[0])
+        rl.append(l[0])
+    assert_parity(out.cpu().numpy(), lse.cpu().numpy(), np.stack(ro), np.stack(rl),
+                  what="fp8 paged config2 head-major")
