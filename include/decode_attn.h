@@ -381,7 +381,13 @@ typedef struct {
  * dtype, a NULL `scales` or scale pointer, a misaligned scale pointer, a
  * negative scale stride or a token stride above 2^24. da_gqa_decode,
  * da_gqa_decode_split_pass and da_gqa_decode_paged reject DA_DTYPE_FP8_E4M3
- * (they have no scales); paged E4M3 pools go through da_gqa_decode_fp8_paged. */
+ * (they have no scales); paged E4M3 pools go through da_gqa_decode_fp8_paged.
+ * Layout: any strides give the same result bit for bit, but the rate differs.
+ * With head_dim 128 a KV head's row is 128 bytes; stored token-major
+ * ([B, L, Hkv, D]) one head's rows lie Hkv * 128 bytes apart, and the call
+ * reads them about 14% slower than when each head's rows are contiguous
+ * (head-major storage, [B, Hkv, L, D], passed as kv_stride_t = D and
+ * kv_stride_h = L * D). Token-major scales ([B, L, Hkv]) read fastest. */
 DA_EXPORT da_status_t da_gqa_decode_fp8(const da_gqa_params_t* params, const da_kv_scales_t* scales,
                                         const void* q, const void* k_cache, const void* v_cache,
                                         const int32_t* seq_lens, float* out, float* lse,
@@ -553,7 +559,9 @@ DA_EXPORT da_status_t da_mla_append_rope(const da_mla_params_t* params, const da
  * multiples of 32 rows. Workspace as da_gqa_decode_workspace_size for the
  * same params. Errors: as da_gqa_decode_fp8 and da_gqa_decode_paged, and
  * UNSUPPORTED for pages of fewer than 32 rows or scales that vary by page
- * only (stride_t = 0 with stride_b != 0). */
+ * only (stride_t = 0 with stride_b != 0). As for da_gqa_decode_fp8, pages
+ * whose codes are stored head-major ([num_pages, Hkv, page_size, D] through
+ * the strides) read faster than token-major ones. */
 DA_EXPORT da_status_t da_gqa_decode_fp8_paged(const da_gqa_params_t* params, const da_paged_kv_t* pages,
                                               const da_kv_scales_t* scales, const void* q,
                                               const void* k_pool, const void* v_pool,
